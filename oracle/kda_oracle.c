@@ -1,0 +1,249 @@
+/*
+ * KDA CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 implementation of what the Kimi Delta Attention (KDA)
+ * forward pass computes, used to check the HIP library.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark may load it; the
+ * product path never does.  It shares no code, header or constant with the
+ * HIP library: it has its own header (kda_oracle.h) and is compiled by gcc.
+ *
+ * Every function restates the pages it follows; nothing here is blocked,
+ * fused or reordered beyond what those pages state.
+ *
+ * Pages cited:
+ *   [recurrent.py]  "K3/kda/ops/reference/recurrent.py", naive_kda_fwd
+ *                   (GQA expansion, scale default, initial state, time loop).
+ *   [sec-01.tex]    "K3/notes/sections/sec-01.tex", section "KDA 递归核心",
+ *                   subsection "逐步公式": the four-step update.
+ *   [kda.rs]        "metrale_model_weights/kimi_k3_host/kda.rs": conv_update,
+ *                   softplus, bounded_gate, l2norm_rows, kda_recurrent_step,
+ *                   kda_decode_token.
+ */
+#include "kda_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* One token of the recurrence for one (batch, value-head) chain, in place on
+ * S[K][V] (V contiguous).  [sec-01.tex] steps 1-4, identical to the body of the
+ * time loop in [recurrent.py] naive_kda_fwd:
+ *   1. S_dec = exp(g) (.) S          (decay broadcast over V, per K channel)
+ *   2. p = k^T S_dec,  r = v - p     (read the old prediction, residual)
+ *   3. S = S_dec + (beta k) (x) r    (rank-1 write)
+ *   4. o = (scale q)^T S             (readout after the write)
+ * q_scaled already carries the readout scale.  r is caller scratch of size V. */
+static void token_step(double *S, const double *q_scaled, const double *k,
+                       const double *v, const double *g, double beta,
+                       double *o, double *r, long K, long V)
+{
+    long i, j;
+    /* step 1: decay */
+    for (i = 0; i < K; ++i) {
+        double d = exp(g[i]);
+        for (j = 0; j < V; ++j) S[i * V + j] *= d;
+    }
+    /* step 2: residual r = v - k^T S_dec */
+    for (j = 0; j < V; ++j) r[j] = 0.0;
+    for (i = 0; i < K; ++i)
+        for (j = 0; j < V; ++j) r[j] += k[i] * S[i * V + j];
+    for (j = 0; j < V; ++j) r[j] = v[j] - r[j];
+    /* step 3: rank-1 write with a = beta k */
+    for (i = 0; i < K; ++i) {
+        double a = beta * k[i];
+        for (j = 0; j < V; ++j) S[i * V + j] += a * r[j];
+    }
+    /* step 4: readout o = q_scaled^T S */
+    for (j = 0; j < V; ++j) o[j] = 0.0;
+    for (i = 0; i < K; ++i)
+        for (j = 0; j < V; ++j) o[j] += q_scaled[i] * S[i * V + j];
+}
+
+int kda_oracle_fwd(const double *q, const double *k, const double *v,
+                   const double *g, const double *beta, const double *S0,
+                   double *o, double *S_out, long B, long T, long H, long HV,
+                   long K, long V, double scale)
+{
+    long bh;
+    int status = 0;
+    if (B < 0 || T < 0 || H <= 0 || HV <= 0 || K <= 0 || V <= 0) return 1;
+    if (HV % H != 0) return 1;
+    /* [recurrent.py]: scale=None means 1/sqrt(K). */
+    if (!(scale > 0.0)) scale = 1.0 / sqrt((double)K);
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (bh = 0; bh < B * HV; ++bh) {
+        const long b = bh / HV, hv = bh % HV;
+        /* [recurrent.py] GQA: q/k are repeat_interleave'd from H to HV heads,
+         * so value head hv reads q/k head hv / (HV/H). */
+        const long h = hv / (HV / H);
+        double *S = (double *)calloc((size_t)(K * V), sizeof(double));
+        double *qs = (double *)malloc((size_t)K * sizeof(double));
+        double *r = (double *)malloc((size_t)V * sizeof(double));
+        long t, i;
+        if (!S || !qs || !r) {
+            status |= 2;
+        } else {
+            /* [recurrent.py]: S = zeros + initial_state. */
+            if (S0) memcpy(S, S0 + bh * K * V, (size_t)(K * V) * sizeof(double));
+            for (t = 0; t < T; ++t) {
+                const long tok = b * T + t;
+                const double *qt = q + (tok * H + h) * K;
+                const double *kt = k + (tok * H + h) * K;
+                const double *vt = v + (tok * HV + hv) * V;
+                const double *gt = g + (tok * HV + hv) * K;
+                const double bt = beta[tok * HV + hv];
+                for (i = 0; i < K; ++i) qs[i] = scale * qt[i];
+                token_step(S, qs, kt, vt, gt, bt, o + (tok * HV + hv) * V, r, K, V);
+            }
+            if (S_out) memcpy(S_out + bh * K * V, S, (size_t)(K * V) * sizeof(double));
+        }
+        free(S);
+        free(qs);
+        free(r);
+    }
+    return status;
+}
+
+/* [kda.rs] sigmoid and softplus (softplus written in its overflow-safe form
+ * max(x,0) + log1p(exp(-|x|)), as on the page). */
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+static double softplus(double x) { return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x))); }
+
+double kda_oracle_sigmoid(double x) { return sigmoid(x); }
+double kda_oracle_softplus(double x) { return softplus(x); }
+
+/* [kda.rs] conv_update for one row of channels: each channel keeps a shift
+ * register of KW values (oldest first, newest in the last slot); the new input
+ * enters the last slot, the output is the dot of the register with that
+ * channel's weights, then SiLU (y = acc * sigmoid(acc)). */
+static void conv_update(double *state, const double *x, const double *w,
+                        double *y, long channels, long KW)
+{
+    long c, j;
+    for (c = 0; c < channels; ++c) {
+        double *row = state + c * KW;
+        const double *wr = w + c * KW;
+        double acc = 0.0;
+        for (j = 0; j + 1 < KW; ++j) row[j] = row[j + 1];
+        row[KW - 1] = x[c];
+        for (j = 0; j < KW; ++j) acc += wr[j] * row[j];
+        y[c] = acc * sigmoid(acc);
+    }
+}
+
+/* [kda.rs] l2norm_rows: x / sqrt(sum(x^2) + eps), eps added inside the root. */
+static void l2norm_row(double *x, long d, double eps)
+{
+    long i;
+    double ss = 0.0, inv;
+    for (i = 0; i < d; ++i) ss += x[i] * x[i];
+    inv = 1.0 / sqrt(ss + eps);
+    for (i = 0; i < d; ++i) x[i] *= inv;
+}
+
+int kda_oracle_decode_step(const double *x, const double *conv_w, double *conv_state,
+                           long KW, int l2norm_qk, double eps,
+                           const double *gate_in, const double *A_log,
+                           const double *dt_bias, int gate_bounded, double lower_bound,
+                           const double *beta_in, int beta_is_logit, double *state,
+                           double *out, long B, long H, long HV, long K, long V,
+                           double scale)
+{
+    const long Cch = 2 * H * K + HV * V; /* channels: q (H*K) | k (H*K) | v (HV*V) */
+    long b;
+    int status = 0;
+    if (B < 0 || H <= 0 || HV <= 0 || K <= 0 || V <= 0 || HV % H != 0) return 1;
+    if (conv_w && (KW < 1 || !conv_state)) return 1;
+    if (A_log && !dt_bias) return 1;
+    if (!(scale > 0.0)) scale = 1.0 / sqrt((double)K);
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (b = 0; b < B; ++b) {
+        double *y = (double *)malloc((size_t)Cch * sizeof(double));
+        double *qs = (double *)malloc((size_t)K * sizeof(double));
+        double *g = (double *)malloc((size_t)K * sizeof(double));
+        double *r = (double *)malloc((size_t)V * sizeof(double));
+        long hv, i;
+        if (!y || !qs || !g || !r) {
+            status |= 2;
+            goto done;
+        }
+        /* [kda.rs] kda_decode_token: the short conv runs first on all channels. */
+        if (conv_w)
+            conv_update(conv_state + b * Cch * KW, x + b * Cch, conv_w, y, Cch, KW);
+        else
+            memcpy(y, x + b * Cch, (size_t)Cch * sizeof(double));
+        /* [kda.rs] kda_recurrent_step: q and k rows are L2-normalised per head. */
+        if (l2norm_qk)
+            for (i = 0; i < 2 * H; ++i) l2norm_row(y + i * K, K, eps);
+        for (hv = 0; hv < HV; ++hv) {
+            const long h = hv / (HV / H);
+            const double *qh = y + h * K;
+            const double *kh = y + H * K + h * K;
+            const double *vh = y + 2 * H * K + hv * V;
+            double bt = beta_in[b * HV + hv];
+            /* [kda.rs] kda_recurrent_step: beta arrives as a logit -> sigmoid. */
+            if (beta_is_logit) bt = sigmoid(bt);
+            for (i = 0; i < K; ++i) {
+                const double gi = gate_in[(b * HV + hv) * K + i];
+                if (A_log) {
+                    /* [kda.rs] bounded_gate: decay = exp(A_log[head]),
+                     * x = z + dt_bias; lower-bounded branch lb*sigmoid(decay*x),
+                     * otherwise -decay*softplus(x). */
+                    const double decay = exp(A_log[hv]);
+                    const double xz = gi + dt_bias[hv * K + i];
+                    g[i] = gate_bounded ? lower_bound * sigmoid(decay * xz)
+                                        : -decay * softplus(xz);
+                } else {
+                    g[i] = gi;
+                }
+                qs[i] = scale * qh[i];
+            }
+            token_step(state + (b * HV + hv) * K * V, qs, kh, vh, g, bt,
+                       out + (b * HV + hv) * V, r, K, V);
+        }
+    done:
+        free(y);
+        free(qs);
+        free(g);
+        free(r);
+    }
+    return status;
+}
+
+int kda_oracle_gate(const double *z, const double *A_log, const double *dt_bias,
+                    int gate_bounded, double lower_bound, double *g, long rows,
+                    long HV, long K)
+{
+    long r, hv, i;
+    for (r = 0; r < rows; ++r)
+        for (hv = 0; hv < HV; ++hv) {
+            const double decay = exp(A_log[hv]);
+            for (i = 0; i < K; ++i) {
+                const long idx = (r * HV + hv) * K + i;
+                const double xz = z[idx] + dt_bias[hv * K + i];
+                g[idx] = gate_bounded ? lower_bound * sigmoid(decay * xz)
+                                      : -decay * softplus(xz);
+            }
+        }
+    return 0;
+}
+
+int kda_oracle_conv_update(double *state, const double *x, const double *w, double *y,
+                           long rows, long channels, long KW)
+{
+    long r;
+    if (KW < 1) return 1;
+    for (r = 0; r < rows; ++r)
+        conv_update(state + r * channels * KW, x + r * channels, w, y + r * channels,
+                    channels, KW);
+    return 0;
+}
+
+int kda_oracle_l2norm_rows(double *x, long rows, long d, double eps)
+{
+    long r;
+    for (r = 0; r < rows; ++r) l2norm_row(x + r * d, d, eps);
+    return 0;
+}
