@@ -1,0 +1,218 @@
+"""KDA (Kimi Delta Attention) forward for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over libkda.so, the HIP library whose C ABI is declared
+in include/kda.h.  This module only marshals arguments (device pointers,
+sizes, the current HIP stream); every step of the computation runs in the
+library's kernels.  torch supplies device memory and streams.
+
+    o, S_T = chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None,
+                       output_final_state=False)
+    out = decode_step(qkv, gate, beta, state, H=..., ...)   # state updated in place
+
+There is no CPU fallback: calling an op without the built library, or with
+tensors that are not on a GPU, raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["chunk_fwd", "decode_step", "abi_version", "library_path", "KDAError",
+           "GATE_DIRECT", "GATE_BOUNDED", "GATE_SOFTPLUS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+_lock = threading.Lock()
+_lib = None
+
+KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EHIP = 0, 1, 2, 3
+DTYPE_F32, DTYPE_BF16 = 0, 1
+GATE_DIRECT, GATE_BOUNDED, GATE_SOFTPLUS = 0, 1, 2
+ABI_VERSION = 1
+
+
+class KDAError(RuntimeError):
+    """A non-zero status from libkda, with the library's message."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("libkda status %d: %s" % (status, message))
+        self.status = status
+
+
+class DecodePrologue(ctypes.Structure):
+    """Mirror of `kda_decode_prologue` in include/kda.h."""
+    _fields_ = [
+        ("conv_weight", ctypes.c_void_p),
+        ("conv_state", ctypes.c_void_p),
+        ("conv_kernel", ctypes.c_int),
+        ("l2norm_qk", ctypes.c_int),
+        ("l2_eps", ctypes.c_float),
+        ("gate_mode", ctypes.c_int),
+        ("A_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
+        ("gate_lower_bound", ctypes.c_float),
+        ("beta_is_logit", ctypes.c_int),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise ImportError(
+                    "libkda.so is not built; run `python -m gated_delta_rule_kda_amd.build` "
+                    "(expected at %s)" % _LIB_PATH)
+            lib = ctypes.CDLL(_LIB_PATH)
+            P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+            lib.kda_abi_version.argtypes = []
+            lib.kda_abi_version.restype = I
+            lib.kda_last_error.argtypes = []
+            lib.kda_last_error.restype = ctypes.c_char_p
+            lib.kda_chunk_fwd.argtypes = [P] * 8 + [I] * 6 + [F, I, I, P]
+            lib.kda_chunk_fwd.restype = I
+            lib.kda_decode_step.argtypes = [P] * 5 + [ctypes.POINTER(DecodePrologue)] + [I] * 5 + [F, I, P]
+            lib.kda_decode_step.restype = I
+            if lib.kda_abi_version() != ABI_VERSION:
+                raise ImportError("libkda ABI %d, binding expects %d" % (lib.kda_abi_version(), ABI_VERSION))
+            _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return _load().kda_abi_version()
+
+
+def _check(status: int):
+    if status != KDA_OK:
+        raise KDAError(status, _load().kda_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return DTYPE_BF16
+    if dt == torch.float32:
+        return DTYPE_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % dt)
+
+
+def _stream_handle(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (libkda has no CPU path)" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
+              *, chunk_size=32, out=None, final_state=None):
+    """Chunk-parallel KDA prefill (``kda_chunk_fwd``).
+
+    q, k [B,T,H,K]; v [B,T,HV,V] (all bf16 or all fp32); g [B,T,HV,K] fp32 with
+    -5 <= g <= 0; beta [B,T,HV] fp32; initial_state [B,HV,K,V] fp32 or None.
+    Returns (o [B,T,HV,V] in v's dtype, final state [B,HV,K,V] fp32 or None).
+    ``final_state`` may be passed (even the initial_state tensor itself, to
+    resume in place); ``out`` may be passed to avoid an allocation.
+    """
+    _need(q, "q")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    dt = q.dtype
+    dev = q.device
+    _need(k, "k", dt, (B, T, H, K), dev)
+    _need(v, "v", dt, (B, T, HV, V), dev)
+    _need(g, "g", torch.float32, (B, T, HV, K), dev)
+    _need(beta, "beta", torch.float32, (B, T, HV), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (B, HV, K, V), dev)
+    if out is None:
+        out = torch.empty(B, T, HV, V, dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (B, T, HV, V), dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty(B, HV, K, V, dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32, (B, HV, K, V), dev)
+    with torch.cuda.device(dev):
+        _check(_load().kda_chunk_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(out),
+            _ptr(final_state), B, T, H, HV, K, V, float(scale) if scale else 0.0,
+            int(chunk_size), _dtype_code(dt), _stream_handle(dev)))
+    return out, final_state
+
+
+def decode_step(qkv, gate, beta, state, *, H, HV, K, V, scale=None, out=None,
+                conv_weight=None, conv_state=None, l2norm_qk=False, l2_eps=1e-6,
+                gate_mode=GATE_DIRECT, A_log=None, dt_bias=None, gate_lower_bound=-5.0,
+                beta_is_logit=False):
+    """One decode token (``kda_decode_step``); ``state`` (and ``conv_state``)
+    are updated in place.  qkv [B, 2HK+HV*V] (bf16 or fp32), gate [B,HV,K] fp32
+    (g, or z for the BOUNDED/SOFTPLUS gate modes), beta [B,HV] fp32.
+    Returns out [B,HV,V] in qkv's dtype."""
+    _need(qkv, "qkv")
+    B = qkv.shape[0]
+    C = 2 * H * K + HV * V
+    dt = qkv.dtype
+    dev = qkv.device
+    if tuple(qkv.shape) != (B, C):
+        raise ValueError("qkv has shape %s, expected %s" % (tuple(qkv.shape), (B, C)))
+    _need(gate, "gate", torch.float32, (B, HV, K), dev)
+    _need(beta, "beta", torch.float32, (B, HV), dev)
+    _need(state, "state", torch.float32, (B, HV, K, V), dev)
+    if out is None:
+        out = torch.empty(B, HV, V, dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (B, HV, V), dev)
+    pro = DecodePrologue()
+    use_pro = False
+    if conv_weight is not None:
+        KW = conv_weight.shape[-1]
+        _need(conv_weight, "conv_weight", torch.float32, (C, KW), dev)
+        _need(conv_state, "conv_state", torch.float32, (B, C, KW), dev)
+        pro.conv_weight = conv_weight.data_ptr()
+        pro.conv_state = conv_state.data_ptr()
+        pro.conv_kernel = KW
+        use_pro = True
+    if l2norm_qk:
+        pro.l2norm_qk = 1
+        pro.l2_eps = float(l2_eps)
+        use_pro = True
+    if gate_mode != GATE_DIRECT:
+        _need(A_log, "A_log", torch.float32, (HV,), dev)
+        _need(dt_bias, "dt_bias", torch.float32, (HV * K,), dev)
+        pro.gate_mode = int(gate_mode)
+        pro.A_log = A_log.data_ptr()
+        pro.dt_bias = dt_bias.data_ptr()
+        pro.gate_lower_bound = float(gate_lower_bound)
+        use_pro = True
+    if beta_is_logit:
+        pro.beta_is_logit = 1
+        use_pro = True
+    with torch.cuda.device(dev):
+        _check(_load().kda_decode_step(
+            _ptr(qkv), _ptr(gate), _ptr(beta), _ptr(state), _ptr(out),
+            ctypes.byref(pro) if use_pro else None, B, H, HV, K, V,
+            float(scale) if scale else 0.0, _dtype_code(dt), _stream_handle(dev)))
+    return out

@@ -1,0 +1,214 @@
+// C ABI of libkda (declared in include/kda.h): host-side validation, then the
+// kernel launches.  Every check runs before anything is enqueued, so a call
+// that returns an error has no side effects and needs no GPU to be tested.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A byte range [p, p + n) of one argument, for the overlap checks.
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;
+};
+
+Range rng(const char *name, const void *p, uint64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + bytes : lo};
+}
+
+bool overlap(const Range &a, const Range &b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;  // empty or absent
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Element count of a product of non-negative sizes; false on overflow past 2^50.
+bool count(uint64_t &out, std::initializer_list<int64_t> dims) {
+    uint64_t n = 1;
+    for (int64_t d : dims) {
+        if (d < 0) return false;
+        if (d != 0 && n > (uint64_t(1) << 50) / static_cast<uint64_t>(d)) return false;
+        n *= static_cast<uint64_t>(d);
+    }
+    out = n;
+    return true;
+}
+
+__global__ void copy_or_zero_kernel(float *dst, const float *src, uint64_t n) {
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_last_error(void) { return g_err; }
+
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                  const float *beta, const float *initial_state, void *out,
+                  float *final_state, int B, int T, int H, int HV, int K, int V,
+                  float scale, int chunk, int dtype, void *stream) {
+    g_err[0] = '\0';
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
+        return fail(KDA_EUNSUPPORTED, "kda_chunk_fwd: dtype %d is not KDA_DTYPE_F32 or KDA_DTYPE_BF16", dtype);
+    if (B < 0 || T < 0) return fail(KDA_EINVAL, "kda_chunk_fwd: B=%d and T=%d must be >= 0", B, T);
+    if (H < 1 || HV < 1) return fail(KDA_EINVAL, "kda_chunk_fwd: H=%d and HV=%d must be >= 1", H, HV);
+    if (HV % H != 0) return fail(KDA_EINVAL, "kda_chunk_fwd: HV=%d is not a multiple of H=%d", HV, H);
+    if (!head_dim_ok(K) || !head_dim_ok(V))
+        return fail(KDA_EUNSUPPORTED, "kda_chunk_fwd: K=%d, V=%d; each must be 32, 64 or 128", K, V);
+    if (chunk < 0) return fail(KDA_EINVAL, "kda_chunk_fwd: chunk=%d must be >= 0", chunk);
+    if (chunk != 0 && chunk != 32)
+        return fail(KDA_EUNSUPPORTED, "kda_chunk_fwd: chunk=%d; only 32 (or 0 for the default) is built", chunk);
+    if (isinf(scale)) return fail(KDA_EINVAL, "kda_chunk_fwd: scale is infinite");
+    if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(K));
+
+    const uint64_t esz = dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    uint64_t nq, nv, ng, nb, ns;
+    if (!count(nq, {B, T, H, K}) || !count(nv, {B, T, HV, V}) || !count(ng, {B, T, HV, K}) ||
+        !count(nb, {B, T, HV}) || !count(ns, {B, HV, K, V}))
+        return fail(KDA_EINVAL, "kda_chunk_fwd: tensor sizes overflow");
+    const bool work = (static_cast<int64_t>(B) * T) > 0;
+    if (work) {
+        if (!q || !k || !v || !g || !beta || !out)
+            return fail(KDA_EINVAL, "kda_chunk_fwd: q, k, v, g, beta and out must be non-NULL");
+    }
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, out, final_state};
+    const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "out", "final_state"};
+    for (int i = 0; i < 8; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(KDA_EINVAL, "kda_chunk_fwd: %s is not 16-byte aligned", names[i]);
+
+    const Range r_in[] = {rng("q", q, nq * esz), rng("k", k, nq * esz), rng("v", v, nv * esz),
+                          rng("g", g, ng * 4), rng("beta", beta, nb * 4),
+                          rng("initial_state", initial_state, ns * 4)};
+    const Range r_out = rng("out", out, nv * esz);
+    const Range r_st = rng("final_state", final_state, ns * 4);
+    for (const Range &r : r_in) {
+        if (work && overlap(r_out, r)) return fail(KDA_EINVAL, "kda_chunk_fwd: out overlaps %s", r.name);
+        if (overlap(r_st, r) && !(&r == &r_in[5] && final_state == initial_state))
+            return fail(KDA_EINVAL, "kda_chunk_fwd: final_state overlaps %s", r.name);
+    }
+    if (work && overlap(r_out, r_st)) return fail(KDA_EINVAL, "kda_chunk_fwd: out overlaps final_state");
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!work) {
+        // No tokens: the final state is the initial state (zeros when absent).
+        if (final_state && final_state != initial_state && ns > 0) {
+            const unsigned blocks = static_cast<unsigned>((ns + 255) / 256);
+            hipLaunchKernelGGL(copy_or_zero_kernel, dim3(blocks), dim3(256), 0, st, final_state,
+                               initial_state, ns);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return fail(KDA_EHIP, "kda_chunk_fwd: launch failed: %s", hipGetErrorString(e));
+        }
+        return KDA_OK;
+    }
+
+    kda::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = initial_state;
+    a.out = out; a.ST = final_state;
+    a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+    a.scale = scale;
+    a.bf16 = dtype == KDA_DTYPE_BF16;
+    const hipError_t e = kda::launch_prefill(a, st);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda_chunk_fwd: launch failed: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+int kda_decode_step(const void *qkv, const float *gate, const float *beta, float *state,
+                    void *out, const kda_decode_prologue *pro, int B, int H, int HV, int K,
+                    int V, float scale, int dtype, void *stream) {
+    g_err[0] = '\0';
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
+        return fail(KDA_EUNSUPPORTED, "kda_decode_step: dtype %d is not KDA_DTYPE_F32 or KDA_DTYPE_BF16", dtype);
+    if (B < 0) return fail(KDA_EINVAL, "kda_decode_step: B=%d must be >= 0", B);
+    if (H < 1 || HV < 1) return fail(KDA_EINVAL, "kda_decode_step: H=%d and HV=%d must be >= 1", H, HV);
+    if (HV % H != 0) return fail(KDA_EINVAL, "kda_decode_step: HV=%d is not a multiple of H=%d", HV, H);
+    if (!head_dim_ok(K) || !head_dim_ok(V))
+        return fail(KDA_EUNSUPPORTED, "kda_decode_step: K=%d, V=%d; each must be 32, 64 or 128", K, V);
+    if (isinf(scale)) return fail(KDA_EINVAL, "kda_decode_step: scale is infinite");
+    if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(K));
+
+    kda_decode_prologue p{};
+    if (pro) p = *pro;
+    const bool conv = p.conv_weight != nullptr;
+    if (conv) {
+        if (!p.conv_state) return fail(KDA_EINVAL, "kda_decode_step: conv_weight given without conv_state");
+        if (p.conv_kernel < 1) return fail(KDA_EINVAL, "kda_decode_step: conv_kernel=%d must be >= 1", p.conv_kernel);
+        if (p.conv_kernel > 8)
+            return fail(KDA_EUNSUPPORTED, "kda_decode_step: conv_kernel=%d; at most 8 is built", p.conv_kernel);
+    }
+    if (p.gate_mode < 0 || p.gate_mode > 2)
+        return fail(KDA_EINVAL, "kda_decode_step: gate_mode=%d is not a kda_gate_mode", p.gate_mode);
+    if (p.gate_mode != KDA_GATE_DIRECT && (!p.A_log || !p.dt_bias))
+        return fail(KDA_EINVAL, "kda_decode_step: gate_mode %d needs A_log and dt_bias", p.gate_mode);
+    if (p.l2norm_qk && !(p.l2_eps >= 0.f && isfinite(p.l2_eps)))
+        return fail(KDA_EINVAL, "kda_decode_step: l2_eps must be finite and >= 0");
+
+    const uint64_t esz = dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const int64_t C = 2 * static_cast<int64_t>(H) * K + static_cast<int64_t>(HV) * V;
+    uint64_t nx, ng, nb, ns, no, ncs, ncw, nal, ndt;
+    if (!count(nx, {B, C}) || !count(ng, {B, HV, K}) || !count(nb, {B, HV}) ||
+        !count(ns, {B, HV, K, V}) || !count(no, {B, HV, V}) ||
+        !count(ncs, {B, C, conv ? p.conv_kernel : 0}) || !count(ncw, {C, conv ? p.conv_kernel : 0}) ||
+        !count(nal, {HV}) || !count(ndt, {HV, K}))
+        return fail(KDA_EINVAL, "kda_decode_step: tensor sizes overflow");
+    if (B == 0) return KDA_OK;
+    if (!qkv || !gate || !beta || !state || !out)
+        return fail(KDA_EINVAL, "kda_decode_step: qkv, gate, beta, state and out must be non-NULL");
+    const void *ptrs[] = {qkv, gate, beta, state, out, p.conv_weight, p.conv_state, p.A_log, p.dt_bias};
+    const char *names[] = {"qkv", "gate", "beta", "state", "out", "conv_weight", "conv_state", "A_log", "dt_bias"};
+    for (int i = 0; i < 9; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(KDA_EINVAL, "kda_decode_step: %s is not 16-byte aligned", names[i]);
+    const bool gp = p.gate_mode != KDA_GATE_DIRECT;
+    const Range rs[] = {rng("qkv", qkv, nx * esz), rng("gate", gate, ng * 4), rng("beta", beta, nb * 4),
+                        rng("state", state, ns * 4), rng("out", out, no * esz),
+                        rng("conv_weight", p.conv_weight, conv ? ncw * 4 : 0),
+                        rng("conv_state", conv ? p.conv_state : nullptr, ncs * 4),
+                        rng("A_log", gp ? p.A_log : nullptr, nal * 4),
+                        rng("dt_bias", gp ? p.dt_bias : nullptr, ndt * 4)};
+    // outputs (state, out, conv_state) may not overlap anything else
+    const int outs[] = {3, 4, 6};
+    for (int o : outs)
+        for (int i = 0; i < 9; ++i)
+            if (i != o && overlap(rs[o], rs[i]))
+                return fail(KDA_EINVAL, "kda_decode_step: %s overlaps %s", rs[o].name, rs[i].name);
+
+    kda::DecodeArgs a{};
+    a.qkv = qkv; a.gate = gate; a.beta = beta; a.state = state; a.out = out;
+    a.conv_w = p.conv_weight; a.conv_state = conv ? p.conv_state : nullptr;
+    a.conv_kernel = conv ? p.conv_kernel : 0;
+    a.l2norm = p.l2norm_qk ? 1 : 0; a.l2_eps = p.l2_eps;
+    a.gate_mode = p.gate_mode; a.A_log = p.A_log; a.dt_bias = p.dt_bias;
+    a.lower_bound = p.gate_lower_bound; a.beta_is_logit = p.beta_is_logit ? 1 : 0;
+    a.B = B; a.H = H; a.HV = HV; a.K = K; a.V = V; a.scale = scale;
+    a.bf16 = dtype == KDA_DTYPE_BF16;
+    const hipError_t e = kda::launch_decode(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda_decode_step: launch failed: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal interface between the C-ABI layer (kda_api.hip) and the kernels.
+// Sizes reaching these launchers have already been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Arguments of one prefill call; pointers are device pointers.
+struct PrefillArgs {
+    const void *q, *k, *v;      // [B,T,H,K], [B,T,H,K], [B,T,HV,V] (dtype)
+    const float *g, *beta;      // [B,T,HV,K], [B,T,HV]
+    const float *S0;            // [B,HV,K,V] or nullptr
+    void *out;                  // [B,T,HV,V] (dtype)
+    float *ST;                  // [B,HV,K,V] or nullptr
+    int B, T, H, HV, K, V;
+    float scale;
+    bool bf16;
+};
+
+// Arguments of one decode step.
+struct DecodeArgs {
+    const void *qkv;            // [B, 2HK + HV V] (dtype)
+    const float *gate;          // [B,HV,K]
+    const float *beta;          // [B,HV]
+    float *state;               // [B,HV,K,V]
+    void *out;                  // [B,HV,V] (dtype)
+    const float *conv_w;        // [C,KW] or nullptr
+    float *conv_state;          // [B,C,KW]
+    int conv_kernel;
+    int l2norm;
+    float l2_eps;
+    int gate_mode;
+    const float *A_log, *dt_bias;
+    float lower_bound;
+    int beta_is_logit;
+    int B, H, HV, K, V;
+    float scale;
+    bool bf16;
+};
+
+// Launch on `stream`; return the hipError_t of the launch.
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float sigmoidf_dev(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace kda

@@ -1,0 +1,135 @@
+/*
+ * libkda -- Kimi Delta Attention (KDA) forward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "K3/notes/sections/sec-01.tex", section "KDA 递归核心",
+ * subsection "逐步公式"; the same loop is naive_kda_fwd on the page
+ * "K3/kda/ops/reference/recurrent.py"), per batch b, value head hv and token t,
+ * with S the [K x V] state of (b, hv) and h = hv / (HV / H) the q/k head that
+ * hv reads (GQA repeat-interleave):
+ *
+ *     S_dec = exp(g_t) (.) S_{t-1}              decay, one factor per K row
+ *     r_t   = v_t - k_t^T S_dec                 delta-rule residual
+ *     S_t   = S_dec + (beta_t k_t) (x) r_t      rank-1 write
+ *     o_t   = (scale q_t)^T S_t                 readout after the write
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees, or keeps them.  Tensors are dense row-major with
+ *    the last dimension contiguous, and every base address must be 16-byte
+ *    aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *    work; they never synchronise.  Results are deterministic: the same inputs
+ *    give bit-identical outputs on every run (no floating-point atomics).
+ *  - Every argument is validated on the host before anything is enqueued; a
+ *    rejected call has no side effects.  The library never aborts or throws.
+ *  - Return codes: KDA_OK, KDA_EINVAL (bad pointer, size, alignment or
+ *    aliasing), KDA_EUNSUPPORTED (valid but not built: head dim, chunk size,
+ *    dtype, conv width), KDA_EHIP (the HIP runtime reported an error at
+ *    launch).  kda_last_error() returns a message for the calling thread's most
+ *    recent non-zero code.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+enum kda_status { KDA_OK = 0, KDA_EINVAL = 1, KDA_EUNSUPPORTED = 2, KDA_EHIP = 3 };
+
+/* Element type of q, k, v (and qkv) and of the output o.  g, beta and the
+ * recurrent state are always fp32. */
+enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 };
+
+/* Gate modes of the decode prologue ("metrale_model_weights/kimi_k3_host/kda.rs",
+ * bounded_gate).  DIRECT: the gate argument is g itself. */
+enum kda_gate_mode { KDA_GATE_DIRECT = 0, KDA_GATE_BOUNDED = 1, KDA_GATE_SOFTPLUS = 2 };
+
+int kda_abi_version(void);
+
+/* Message for the calling thread's last non-zero status ("" if none). */
+const char *kda_last_error(void);
+
+/*
+ * kda_chunk_fwd -- chunk-parallel prefill over T tokens.
+ *
+ * Computes o and the final state of the recurrence above for all b, t, hv,
+ * starting from initial_state (zeros when NULL); the same interface as
+ * naive_kda_fwd(q, k, v, g, beta, scale, initial_state, output_final_state) on
+ * the "K3/kda/ops/reference/recurrent.py" page.  Internally it uses the chunk
+ * form of the page "src/tinycenn_lm/research_layers.py" (delta_recurrence:
+ * chunk-local cumulative decay, a unit-lower-triangular solve inside each
+ * chunk, the state carried from chunk to chunk).
+ *
+ *   q, k          [B, T, H, K]   dtype
+ *   v             [B, T, HV, V]  dtype
+ *   g             [B, T, HV, K]  fp32, log-space decay; PRECONDITION -5 <= g <= 0
+ *                                (the lower bound of the bounded gate).  Values
+ *                                below -5 are not detected and can overflow the
+ *                                in-chunk exponent factorisation.
+ *   beta          [B, T, HV]     fp32, write strength used as given
+ *   initial_state [B, HV, K, V]  fp32 or NULL (zeros)
+ *   out           [B, T, HV, V]  dtype; must not overlap any input
+ *   final_state   [B, HV, K, V]  fp32 or NULL (not written); may be the same
+ *                                pointer as initial_state (in-place resume), may
+ *                                not otherwise overlap an input or out
+ *   B, T >= 0 (either 0: nothing but the final state, which then equals the
+ *   initial state, is written); H, HV >= 1 with HV % H == 0;
+ *   K, V in {32, 64, 128};  scale <= 0 (or NaN) selects 1/sqrt(K);
+ *   chunk 0 selects the default, 32 (the only size built);
+ *   dtype KDA_DTYPE_F32 or KDA_DTYPE_BF16.
+ */
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                  const float *beta, const float *initial_state, void *out,
+                  float *final_state, int B, int T, int H, int HV, int K, int V,
+                  float scale, int chunk, int dtype, void *stream);
+
+/*
+ * Optional stages fused in front of the decode step, as the host decode on the
+ * page "metrale_model_weights/kimi_k3_host/kda.rs" runs them (kda_decode_token:
+ * conv_update, then kda_recurrent_step with l2norm_rows and a sigmoid on beta;
+ * the gate from bounded_gate).  Zero-initialise and set what is wanted.
+ */
+typedef struct kda_decode_prologue {
+    const float *conv_weight; /* [C, conv_kernel], C = 2*H*K + HV*V; NULL: no conv */
+    float *conv_state;        /* [B, C, conv_kernel], oldest value first; updated in place */
+    int conv_kernel;          /* 1..8 when conv_weight != NULL */
+    int l2norm_qk;            /* nonzero: q, k rows become x / sqrt(sum x^2 + l2_eps) */
+    float l2_eps;             /* e.g. 1e-6 */
+    int gate_mode;            /* enum kda_gate_mode */
+    const float *A_log;       /* [HV]      (BOUNDED, SOFTPLUS) */
+    const float *dt_bias;     /* [HV * K]  (BOUNDED, SOFTPLUS) */
+    float gate_lower_bound;   /* BOUNDED: g = lb * sigmoid(exp(A_log) * (z + dt_bias)) */
+    int beta_is_logit;        /* nonzero: beta = sigmoid(beta argument) */
+} kda_decode_prologue;
+
+/*
+ * kda_decode_step -- one token of the recurrence for B sequences, state
+ * updated in place.
+ *
+ *   qkv    [B, 2*H*K + HV*V] dtype: q (H*K) | k (H*K) | v (HV*V) channels of one
+ *          token, before the short conv when the prologue has one
+ *   gate   [B, HV, K] fp32: g (GATE_DIRECT) or the pre-activation z
+ *   beta   [B, HV] fp32: beta, or its logit when pro->beta_is_logit
+ *   state  [B, HV, K, V] fp32, read and written in place
+ *   out    [B, HV, V] dtype; must not overlap any other argument
+ *   pro    NULL for the plain step (g and beta as given, no conv, no L2 norm)
+ *   B >= 0 (0: no-op); H, HV >= 1, HV % H == 0; K, V in {32, 64, 128};
+ *   scale <= 0 (or NaN) selects 1/sqrt(K); dtype as above.
+ * With GATE_DIRECT the caller owns the range of g; the other modes produce
+ * g <= 0.  Calls that share a state or conv_state buffer must be ordered by
+ * the caller (same stream or events).
+ */
+int kda_decode_step(const void *qkv, const float *gate, const float *beta, float *state,
+                    void *out, const kda_decode_prologue *pro, int B, int H, int HV,
+                    int K, int V, float scale, int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

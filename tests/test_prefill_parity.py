@@ -1,0 +1,219 @@
+"""GPU parity of kda_chunk_fwd against the fp64 oracle (token loop)."""
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_delta_rule_kda_amd as kda
+from gated_delta_rule_kda_amd import synth
+from kda_testutil import assert_close, gpu_available, np64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(shape: synth.PrefillShape, seed=0, g_lower=None, label=""):
+    say("prefill case", label, shape, "seed", seed, "g_lower", g_lower)
+    inp = synth.make_prefill_inputs(shape, DEV, seed, g_lower=g_lower)
+    o, S = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                         initial_state=inp["S0"], output_final_state=True)
+    torch.cuda.synchronize()
+    oref, Sref = oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                initial_state=inp["S0"])
+    mo = assert_close(o, oref, shape.dtype, True, "o " + label)
+    ms = assert_close(S, Sref, shape.dtype, False, "S_T " + label)
+    say("   o", mo)
+    say("   S", ms)
+    return inp, o, S
+
+
+def test_tiny_fp32():
+    """The fp32 tiny workload: B1 T64 H=HV=2 K=V=32."""
+    run_case(synth.PREFILL_TINY_F32, label="tiny-fp32")
+
+
+def test_tiny_fp32_long_memory():
+    run_case(synth.PREFILL_TINY_F32, g_lower=-0.05, label="tiny-fp32-long")
+
+
+def test_twin_bf16():
+    """The bf16 twin workload: B4 T2048 H=HV=8 K=V=32, chunk 32."""
+    run_case(synth.PREFILL_TWIN_BF16, label="twin-bf16")
+
+
+def test_twin_bf16_long_memory():
+    """Same shapes with g = -0.05 sigmoid(N(0,1)): the state survives many
+    chunks, so errors in the chunk-to-chunk carry would show."""
+    run_case(synth.PREFILL_TWIN_BF16, g_lower=-0.05, label="twin-bf16-long")
+
+
+RAGGED = [
+    # (B, T, H, HV, K, V, dtype)
+    (1, 1, 1, 1, 32, 32, torch.float32),
+    (2, 3, 1, 2, 64, 32, torch.float32),
+    (1, 31, 2, 4, 128, 64, torch.float32),
+    (1, 33, 1, 1, 32, 128, torch.float32),
+    (2, 65, 2, 2, 128, 128, torch.float32),
+    (1, 2, 1, 1, 128, 128, torch.bfloat16),
+    (2, 63, 2, 4, 64, 64, torch.bfloat16),
+    (1, 64, 1, 2, 128, 32, torch.bfloat16),
+    (1, 100, 1, 4, 32, 128, torch.bfloat16),
+    (3, 97, 2, 2, 128, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "B%dT%dH%dHV%dK%dV%d-%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], str(c[6]).split(".")[-1]))
+@pytest.mark.parametrize("s0", ["none", "normal"])
+def test_ragged_and_gqa(case, s0):
+    B, T, H, HV, K, V, dt = case
+    shape = synth.PrefillShape(B, T, H, HV, K, V, dt, s0, s0_std=0.5)
+    run_case(shape, seed=T + K, label="ragged")
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_long_memory_ragged(dt):
+    shape = synth.PrefillShape(2, 200, 1, 2, 128, 128, dt, "normal", s0_std=0.5)
+    run_case(shape, seed=5, g_lower=-0.05, label="long-ragged")
+
+
+def test_g_at_lower_bound():
+    """g = -5 everywhere: the in-chunk exponent factors reach their extremes
+    (2^-115 .. 2^115) and must stay finite and exact where kept."""
+    shape = synth.PrefillShape(1, 96, 1, 1, 128, 64, torch.float32, "normal", s0_std=0.5)
+    inp = synth.make_prefill_inputs(shape, DEV, 3)
+    inp["g"].fill_(-5.0)
+    o, S = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                         initial_state=inp["S0"], output_final_state=True)
+    oref, Sref = oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                initial_state=inp["S0"])
+    assert_close(o, oref, torch.float32, True, "o g=-5")
+    assert_close(S, Sref, torch.float32, False, "S g=-5")
+
+
+def test_g_zero_unit_key_recall():
+    """g = 0, beta = 1, unit keys, q = sqrt(K) k  =>  o_t = v_t exactly
+    (the delta rule erases the old association before writing)."""
+    shape = synth.PrefillShape(1, 256, 2, 4, 128, 128, torch.float32, "normal")
+    inp = synth.make_prefill_inputs(shape, DEV, 11)
+    inp["g"].zero_()
+    inp["beta"].fill_(1.0)
+    q = inp["k"] * math.sqrt(128)
+    o, _ = kda.chunk_fwd(q, inp["k"], inp["v"], inp["g"], inp["beta"], initial_state=inp["S0"])
+    assert_close(o, inp["v"], torch.float32, True, "recall")
+
+
+def test_beta_zero_pure_decay():
+    shape = synth.PrefillShape(2, 70, 2, 2, 64, 64, torch.bfloat16, "normal", s0_std=1.0)
+    inp = synth.make_prefill_inputs(shape, DEV, 2, g_lower=-0.2)
+    inp["beta"].zero_()
+    _, S = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                         initial_state=inp["S0"], output_final_state=True)
+    G = inp["g"].double().sum(dim=1)                       # [B,HV,K]
+    expect = torch.exp(G)[..., None] * inp["S0"].double()
+    assert_close(S, expect, torch.bfloat16, False, "beta=0 state")
+
+
+def test_empty_sequence_copies_state():
+    B, HV, K, V = 2, 3, 64, 32
+    S0 = torch.randn(B, HV, K, V, device=DEV)
+    e = torch.empty(B, 0, 1, K, device=DEV)
+    ev = torch.empty(B, 0, HV, V, device=DEV)
+    o, S = kda.chunk_fwd(e, e, ev, torch.empty(B, 0, HV, K, device=DEV),
+                         torch.empty(B, 0, HV, device=DEV), initial_state=S0,
+                         output_final_state=True)
+    assert o.shape == (B, 0, HV, V)
+    assert torch.equal(S, S0)
+    _, Sz = kda.chunk_fwd(e, e, ev, torch.empty(B, 0, HV, K, device=DEV),
+                          torch.empty(B, 0, HV, device=DEV), output_final_state=True)
+    assert torch.count_nonzero(Sz) == 0
+
+
+def test_in_place_resume_and_split():
+    """final_state aliasing initial_state; fwd(T1) then fwd(T2, S_T1) matches
+    fwd(T1+T2) within tolerance (chunk boundaries differ between the two)."""
+    shape = synth.PrefillShape(2, 150, 2, 4, 128, 64, torch.bfloat16, "normal", s0_std=0.3)
+    inp = synth.make_prefill_inputs(shape, DEV, 9, g_lower=-0.1)
+    o_full, S_full = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                   initial_state=inp["S0"], output_final_state=True)
+    S = inp["S0"].clone()
+    a = 45
+    sl = lambda x, s: x[:, s].contiguous()
+    o1, _ = kda.chunk_fwd(*(sl(inp[n], slice(0, a)) for n in ("q", "k", "v", "g", "beta")),
+                          initial_state=S, final_state=S)
+    o2, _ = kda.chunk_fwd(*(sl(inp[n], slice(a, None)) for n in ("q", "k", "v", "g", "beta")),
+                          initial_state=S, final_state=S)
+    oref, Sref = oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                initial_state=inp["S0"])
+    assert_close(torch.cat([o1, o2], 1), oref, torch.bfloat16, True, "split o")
+    assert_close(S, Sref, torch.bfloat16, False, "split S")
+    assert_close(o_full, oref, torch.bfloat16, True, "full o")
+
+
+def test_deterministic_bitwise():
+    shape = dataclasses.replace(synth.PREFILL_TWIN_BF16, B=2, T=300, s0="normal")
+    inp = synth.make_prefill_inputs(shape, DEV, 4)
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    o1, S1 = kda.chunk_fwd(*args, initial_state=inp["S0"], output_final_state=True)
+    o2, S2 = kda.chunk_fwd(*args, initial_state=inp["S0"], output_final_state=True)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def _sampled_full_size(shape, chains, g_lower=None, seed=0):
+    """Run a full-size workload on the GPU in the benchmark's launch
+    configuration, then check whole (b, hv) chains against the oracle."""
+    say("full-size", shape, "chains", chains)
+    inp = synth.make_prefill_inputs(shape, DEV, seed, g_lower=g_lower)
+    o, S = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                         initial_state=inp["S0"], output_final_state=True)
+    torch.cuda.synchronize()
+    G = shape.HV // shape.H
+    for (b, hv) in chains:
+        h = hv // G
+        sub = lambda x, head: x[b:b + 1, :, head:head + 1]
+        S0 = inp["S0"][b:b + 1, hv:hv + 1] if inp["S0"] is not None else None
+        oref, Sref = oracle.kda_fwd(sub(inp["q"], h), sub(inp["k"], h), sub(inp["v"], hv),
+                                    sub(inp["g"], hv), inp["beta"][b:b + 1, :, hv:hv + 1],
+                                    initial_state=S0)
+        mo = assert_close(o[b:b + 1, :, hv:hv + 1], oref, shape.dtype, True, "o chain %s" % ((b, hv),))
+        ms = assert_close(S[b:b + 1, hv:hv + 1], Sref, shape.dtype, False, "S chain %s" % ((b, hv),))
+        say("   chain", (b, hv), "o", mo, "S", ms)
+    return inp, o, S
+
+
+def test_full_size_hv96_sampled():
+    """B1 T8192 H=HV=96 K=V=128 bf16, explicit zero S0."""
+    _sampled_full_size(synth.PREFILL_HV96_BF16, [(0, 0), (0, 37), (0, 95)])
+
+
+def test_full_size_hv96_long_memory_sampled():
+    _sampled_full_size(synth.PREFILL_HV96_BF16, [(0, 5), (0, 64)], g_lower=-0.05, seed=1)
+
+
+def test_full_size_gqa_sampled():
+    """B8 T4096 H16 HV64 (G=4) K=V=128 bf16, S0 ~ N(0, 0.02^2)."""
+    _sampled_full_size(synth.PREFILL_GQA_BF16, [(0, 0), (3, 13), (7, 63)])
+
+
+def test_full_length_unit_key_recall():
+    """The unit-key recall identity over the full HV96 length (T = 8192, 256
+    chunks), fp32: after every write o_t = v_t whatever the history, so an
+    error anywhere in the chunk-to-chunk carry would show."""
+    shape = synth.PrefillShape(1, 8192, 4, 4, 128, 128, torch.float32, "normal")
+    inp = synth.make_prefill_inputs(shape, DEV, 0)
+    inp["g"].zero_()
+    inp["beta"].fill_(1.0)
+    q = inp["k"] * math.sqrt(128)
+    o, _ = kda.chunk_fwd(q, inp["k"], inp["v"], inp["g"], inp["beta"], initial_state=inp["S0"])
+    assert_close(o, inp["v"], torch.float32, True, "recall T8192")
