@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""KDA forward benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload (one JSON line on stdout):
+  * prefill: kda_chunk_fwd on B=1, T=8192, H=HV=96, K=V=128, bf16 q/k/v, fp32
+    g/beta, explicit zero fp32 initial state, final state returned, chunk 32.
+    One timed step = one call over that batch.  value = tokens/s.
+  * decode: 1000 kda_decode_step calls on B=256 sequences, H=HV=96, K=V=128,
+    fp32 everywhere, fused short conv (width 4) + SiLU, L2 norm of q/k
+    (eps 1e-6), bounded gate -5*sigmoid(exp(A_log)(z+dt_bias)), beta logits;
+    state resident in HBM and updated in place.  Reported as GB/s against the
+    HBM peak.
+Inputs are seeded synthetic tensors (gated_delta_rule_kda_amd.synth) created on
+the GPU before the timed region.  Kernel durations come from HIP events
+recorded on the stream the kernels are launched on.  The CPU baseline runs the
+fp64 oracle on the host's cores over a bounded sample of the prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_kda_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_alg_bytes(B, T, H, HV, K, V, esz):
+    """Algorithmic HBM bytes of one prefill call: every input read once, every
+    output written once (q,k per q/k head; v,g,beta,o per value head; S0 and S_T)."""
+    per_tok = H * 2 * K * esz + HV * (V * esz + K * 4 + 4 + V * esz)
+    return B * T * per_tok + 2 * B * HV * K * V * 4
+
+
+def prefill_alg_flops(B, T, HV, K, V, C=32):
+    """Algorithmic flops: 6KV + 2C(K+V) per token per value head at C = 32."""
+    return B * T * HV * (6 * K * V + 2 * C * (K + V))
+
+
+def decode_alg_bytes(B, H, HV, K, V, KW):
+    """Algorithmic HBM bytes of one fused decode step: fp32 state read and
+    written once, conv state one 16-byte pass per channel, the token's qkv,
+    z, beta, the output, and the parameters (conv weights, dt_bias, A_log)."""
+    C = 2 * H * K + HV * V
+    per_seq = 2 * HV * K * V * 4 + C * KW * 4 + C * 4 + HV * K * 4 + HV * 4 + HV * V * 4
+    params = C * KW * 4 + HV * K * 4 + HV * 4
+    return B * per_seq + params
+
+
+def load_counters(kernel_key):
+    """HBM traffic per launch from the committed rocprofv3 counter runs, if
+    they were taken on the kernel sources as they are now; else None."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = c.get(kernel_key)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("traffic_bytes")
+
+
+def time_calls(fn, n, stream):
+    """Average event time (ms) of n calls of fn, events on `stream`."""
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    return starts, ends
+
+
+def cpu_baseline(inp, shape, budget_heads=None):
+    """The fp64 oracle on host cores over a bounded sample of the prefill
+    workload: every token of the first `budget_heads` value heads (all heads
+    by default).  Returns the dict for the JSON line."""
+    import numpy as np
+    import oracle
+    import torch
+    B, T, H, HV, K, V = shape.B, shape.T, shape.H, shape.HV, shape.K, shape.V
+    nh = HV if budget_heads is None else min(HV, budget_heads)
+    G = HV // H
+    nq = max(1, nh // G)
+    q = inp["q"][:, :, :nq].to("cpu")
+    k = inp["k"][:, :, :nq].to("cpu")
+    v = inp["v"][:, :, :nh].to("cpu")
+    g = inp["g"][:, :, :nh].to("cpu")
+    beta = inp["beta"][:, :, :nh].to("cpu")
+    S0 = inp["S0"][:, :nh].to("cpu") if inp["S0"] is not None else None
+    args = [oracle.f64(x) for x in (q, k, v, g, beta)]
+    S0 = oracle.f64(S0)
+    threads = oracle.omp_threads()
+    t0 = time.perf_counter()
+    oracle.kda_fwd(*args, initial_state=S0)
+    dt = time.perf_counter() - t0
+    # tokens/s of the whole workload: the sample did nh/HV of every token's work
+    value = B * T * (nh / HV) / dt
+    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 token loop over all %d tokens of %d of the %d value heads "
+                      "(B=%d), %.2f s on the host; value scaled to all %d heads"
+                      % (T, nh, HV, B, dt, HV),
+            "seconds": dt}
+
+
+def bench_prefill(shape, steps, warmup, tag):
+    import torch
+    import gated_delta_rule_kda_amd as kda
+    from gated_delta_rule_kda_amd import synth
+    dev = torch.device("cuda:0")
+    inp = synth.make_prefill_inputs(shape, dev, 0)
+    out = torch.empty(shape.B, shape.T, shape.HV, shape.V, dtype=shape.dtype, device=dev)
+    ST = torch.empty(shape.B, shape.HV, shape.K, shape.V, dtype=torch.float32, device=dev)
+
+    def call():
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                      initial_state=inp["S0"], out=out, final_state=ST)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    t0 = time.perf_counter()
+    starts, ends = time_calls(call, steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    total_ms = starts[0].elapsed_time(ends[-1])
+    esz = 2 if shape.dtype == torch.bfloat16 else 4
+    nbytes = prefill_alg_bytes(shape.B, shape.T, shape.H, shape.HV, shape.K, shape.V, esz)
+    flops = prefill_alg_flops(shape.B, shape.T, shape.HV, shape.K, shape.V)
+    avg_ms = sum(ev_ms) / len(ev_ms)
+    log("[%s] prefill avg %.4f ms (min %.4f, max %.4f), span %.3f ms, wall %.3f s" % (
+        tag, avg_ms, min(ev_ms), max(ev_ms), total_ms, wall))
+    return dict(inp=inp, avg_ms=avg_ms, min_ms=min(ev_ms), span_ms=total_ms,
+                bytes=nbytes, flops=flops, tokens=shape.B * shape.T)
+
+
+def bench_decode(shape, steps, warmup):
+    import torch
+    import gated_delta_rule_kda_amd as kda
+    from gated_delta_rule_kda_amd import synth
+    dev = torch.device("cuda:0")
+    B, H, HV, K, V, KW = shape.B, shape.H, shape.HV, shape.K, shape.V, shape.KW
+    C = 2 * H * K + HV * V
+    prm = synth.make_decode_params(shape, dev, 0)
+    state = torch.zeros(B, HV, K, V, device=dev)
+    conv = torch.zeros(B, C, KW, device=dev)
+    out = torch.empty(B, HV, V, device=dev)
+    pool = [(x, z.view(B, HV, K), bl) for (x, z, bl) in prm["pool"]]
+
+    def call(t):
+        x, z, bl = pool[t % len(pool)]
+        kda.decode_step(x, z, bl, state, H=H, HV=HV, K=K, V=V, out=out,
+                        conv_weight=prm["conv_w"], conv_state=conv, l2norm_qk=True, l2_eps=1e-6,
+                        gate_mode=kda.GATE_BOUNDED, A_log=prm["A_log"], dt_bias=prm["dt_bias"],
+                        gate_lower_bound=shape.lower_bound, beta_is_logit=True)
+
+    for t in range(warmup):
+        call(t)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for t in range(steps):
+        call(t)
+    e.record(stream)
+    torch.cuda.synchronize()
+    span_ms = s.elapsed_time(e)
+    nbytes = decode_alg_bytes(B, H, HV, K, V, KW)
+    per_ms = span_ms / steps
+    gbs = nbytes / (per_ms * 1e-3) / 1e9
+    log("[decode] %d steps: %.3f ms total, %.4f ms/step, %.1f GB/s" % (steps, span_ms, per_ms, gbs))
+    return dict(span_ms=span_ms, per_ms=per_ms, bytes=nbytes, gbs=gbs)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed prefill calls")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gqa", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy"], default=None,
+                    help="run one workload only (for profiler runs); prints no JSON line")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_kda_amd import synth
+
+    if args.only == "copy":
+        # A plain copy of a known size, for scaling the HBM byte counters.
+        n = 256 * 1024 * 1024
+        a = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("[copy] 5 copies of %d bytes" % (n * 4))
+        return
+    if args.only == "prefill":
+        bench_prefill(synth.PREFILL_HV96_BF16, args.steps, args.warmup, "hv96")
+        return
+    if args.only == "gqa":
+        bench_prefill(synth.PREFILL_GQA_BF16, args.steps, args.warmup, "gqa")
+        return
+    if args.only == "decode":
+        bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup)
+        return
+
+    shape = synth.PREFILL_HV96_BF16
+    torch.cuda.synchronize()
+    p = bench_prefill(shape, args.steps, args.warmup, "hv96")
+    ms_per_step = p["span_ms"] / args.steps
+    value = p["tokens"] / (ms_per_step * 1e-3)
+    achieved = p["bytes"] / (p["avg_ms"] * 1e-3) / 1e9
+    traffic = load_counters("prefill_hv96")
+    line = {
+        "metric": "prefill tokens/s (HV=96,K=V=128) + decode GB/s vs HBM peak, 1 GPU",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "KDA chunked prefill B1 T8192 H=HV=96 K=V=128 bf16 q/k/v, "
+                               "fp32 g/beta/state, zero S0, final state returned, chunk 32",
+                   "B": shape.B, "T": shape.T, "H": shape.H, "HV": shape.HV, "K": shape.K,
+                   "V": shape.V, "chunk": 32, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "prefill_kernel<128,64,bf16>",
+                     "alg_bytes_per_launch": p["bytes"], "avg_launch_ms": p["avg_ms"]},
+        "mfma": {"alg_flops_per_launch": p["flops"],
+                 "achieved_tflops": p["flops"] / (p["avg_ms"] * 1e-3) / 1e12,
+                 "peak_tflops": BF16_MFMA_PEAK / 1e12,
+                 "frac": p["flops"] / (p["avg_ms"] * 1e-3) / BF16_MFMA_PEAK},
+    }
+    if not args.no_gqa:
+        gshape = synth.PREFILL_GQA_BF16
+        gq = bench_prefill(gshape, max(3, args.steps // 2), args.warmup, "gqa")
+        line["prefill_gqa"] = {
+            "workload": "KDA chunked prefill with GQA B8 T4096 H16 HV64 K=V=128 bf16, S0~N(0,0.02^2)",
+            "tokens_per_s": gq["tokens"] / (gq["avg_ms"] * 1e-3), "avg_launch_ms": gq["avg_ms"],
+            "achieved_gbs": gq["bytes"] / (gq["avg_ms"] * 1e-3) / 1e9,
+            "frac_hbm": gq["bytes"] / (gq["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "alg_bytes_per_launch": gq["bytes"]}
+        del gq
+    if not args.no_decode:
+        d = bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup)
+        line["decode"] = {
+            "workload": "KDA recurrent decode, %d steps, B256 H=HV=96 K=V=128 fp32, fused conv4+SiLU, "
+                        "L2 norm, bounded gate -5, beta logits" % args.decode_steps,
+            "value": d["gbs"], "unit": "GB/s", "ms_per_token_step": d["per_ms"],
+            "steps": args.decode_steps, "seconds_total": d["span_ms"] * 1e-3, "dtype": "f32",
+            "roofline": {"bound": "hbm", "achieved": d["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": d["gbs"] / HBM_PEAK_GBS, "traffic": load_counters("decode_b256"),
+                         "kernel": "decode_kernel<128,128>", "alg_bytes_per_launch": d["bytes"],
+                         "avg_launch_ms": d["per_ms"]}}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(p["inp"], shape)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

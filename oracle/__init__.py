@@ -49,6 +49,8 @@ def _load():
             L = ctypes.c_long
             D = ctypes.c_double
             I = ctypes.c_int
+            lib.kda_oracle_threads.argtypes = []
+            lib.kda_oracle_threads.restype = I
             lib.kda_oracle_fwd.argtypes = [P] * 8 + [L] * 6 + [D]
             lib.kda_oracle_fwd.restype = I
             lib.kda_oracle_decode_step.argtypes = (
@@ -191,8 +193,5 @@ def softplus(x: float) -> float:
 
 
 def omp_threads() -> int:
-    """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS, else all cores)."""
-    env = os.environ.get("OMP_NUM_THREADS")
-    if env and env.strip().isdigit():
-        return int(env)
-    return os.cpu_count() or 1
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().kda_oracle_threads())

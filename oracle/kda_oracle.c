@@ -24,6 +24,19 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the OpenMP loops below run with (1 without OpenMP). */
+int kda_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* One token of the recurrence for one (batch, value-head) chain, in place on
  * S[K][V] (V contiguous).  [sec-01.tex] steps 1-4, identical to the body of the

@@ -17,6 +17,9 @@
 extern "C" {
 #endif
 
+/* Threads the oracle's OpenMP loops use. */
+int kda_oracle_threads(void);
+
 int kda_oracle_fwd(const double *q, const double *k, const double *v,
                    const double *g, const double *beta, const double *S0,
                    double *o, double *S_out, long B, long T, long H, long HV,
