@@ -42,6 +42,7 @@ struct DecodeArgs {
 
 // Launch on `stream`; return the hipError_t of the launch.
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers

@@ -1,4 +1,5 @@
-// KDA chunk-parallel prefill for gfx950: one fused kernel.
+// KDA chunk-parallel prefill for gfx950, fp32 inputs: one fused kernel.
+// (bf16 inputs use the pipelined kernel in kda_prefill_bf16.hip.)
 //
 // The chunk form follows delta_recurrence on the page
 // "src/tinycenn_lm/research_layers.py" (chunk-local cumulative decay, a
@@ -634,15 +635,10 @@ hipError_t launch_k(const PrefillArgs &a, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     if (a.B == 0 || a.T == 0) return hipSuccess;
-    if (a.bf16) {
-        if (a.K == 32) return launch_k<32, true>(a, stream);
-        if (a.K == 64) return launch_k<64, true>(a, stream);
-        if (a.K == 128) return launch_k<128, true>(a, stream);
-    } else {
-        if (a.K == 32) return launch_k<32, false>(a, stream);
-        if (a.K == 64) return launch_k<64, false>(a, stream);
-        if (a.K == 128) return launch_k<128, false>(a, stream);
-    }
+    if (a.bf16) return launch_prefill_bf16(a, stream);
+    if (a.K == 32) return launch_k<32, false>(a, stream);
+    if (a.K == 64) return launch_k<64, false>(a, stream);
+    if (a.K == 128) return launch_k<128, false>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -82,6 +82,22 @@ def test_ragged_and_gqa(case, s0):
     run_case(shape, seed=T + K, label="ragged")
 
 
+MANY_CHAINS = [
+    # enough (b, hv) chains that each workgroup takes the whole V width
+    (2, 77, 16, 96, 128, 128),
+    (3, 50, 64, 64, 64, 64),
+    (4, 45, 40, 40, 32, 128),
+    (5, 33, 32, 32, 128, 32),
+]
+
+
+@pytest.mark.parametrize("case", MANY_CHAINS, ids=lambda c: "B%dT%dH%dHV%dK%dV%d" % c)
+def test_bf16_full_width_workgroups(case):
+    B, T, H, HV, K, V = case
+    shape = synth.PrefillShape(B, T, H, HV, K, V, torch.bfloat16, "normal", s0_std=0.3)
+    run_case(shape, seed=B * T, g_lower=-1.0, label="full-width")
+
+
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
 def test_long_memory_ragged(dt):
     shape = synth.PrefillShape(2, 200, 1, 2, 128, 128, dt, "normal", s0_std=0.5)
