@@ -1,39 +1,49 @@
 // KDA chunk-parallel prefill for bf16 inputs on gfx950: one fused, pipelined kernel.
 //
-// The algebra is the one of the fp32 kernel (kda_prefill.hip), i.e. the chunk
-// form of delta_recurrence on the page "src/tinycenn_lm/research_layers.py"
-// specialised to KDA and factored so that every exponent is a difference of
-// chunk-local cumulative sums (base 2, reference row r = 15):
+// The chunk form follows delta_recurrence on the page
+// "src/tinycenn_lm/research_layers.py" (chunk-local cumulative decay, a
+// unit-lower-triangular solve inside each chunk, the state carried from chunk
+// to chunk), specialised to KDA (write key k, erase beta*k, value beta*v,
+// readout scale on q).  Every exponent is a difference of chunk-local
+// cumulative sums G (base 2) around a reference row r = 15, so no factor
+// exceeds 2^116 for g >= -5 and every kept product is <= 1:
 //     e1 = 2^{G_i - G_r},  e2 = 2^{G_r - G_i},  Gamma_i = 2^{G_i}
-//     A_kk = diag(beta) (k e1)(k e2)^T   strictly lower
-//     A_qk =            (q e1)(k e2)^T   lower incl. diagonal
-//     T = (I + A_kk)^-1,  T' = T diag(beta)
-//     W = T' (k Gamma),   U0 = T' v,     U = U0 - W M
+//     A_kk = diag(beta) (k e1)(k e2)^T    strictly lower  (the page's tril(., -1))
+//     A_qk =            (q e1)(k e2)^T    lower incl. diagonal
+//     R = diag(beta) (v - (k Gamma) M)    right-hand side of the in-chunk solve
+//     U = (I + A_kk)^-1 R                 (the page's unit-lower-triangular solve)
 //     O = scale ((q Gamma) M + A_qk U)
 //     M <- Gamma_last (.) M + (k 2^{G_last - G})^T U
-// Folding beta into T' and the readout scale into the output keeps beta and
-// the scale out of the per-element operand work.
+// with M the [K x V] state at the chunk start.
 //
-// Organisation (one workgroup of 8 waves per (b, hv, V-tile of VT columns)):
-//  * State: each "carry" wave owns 16 columns of M (all K rows) in MFMA
-//    accumulators for the whole sequence, so U, O and the M update of those
-//    columns never leave the wave.  The accumulator layout of M is used as the
-//    MFMA B operand directly: the reduction index of an MFMA may be permuted
-//    as long as both operands use the same permutation, so lane group g takes
-//    rows {4g..4g+3} of one 16-row tile and {4g..4g+3} of the next; the A
-//    operand (W, q Gamma, A_qk, k_bar^T) is read from LDS with the same row set.
-//  * Pipeline: while the carry waves run chunk n, all waves prepare chunk n+1
-//    (cumulative decay, exponentials and split-bf16 operands on the VALU, the
-//    A matrices on MFMA, T on one wave in fp32, W on MFMA).  Operands shared
-//    across the pipeline boundary are double-buffered in LDS; global loads for
-//    chunk n+2 are issued about two thirds of an iteration ahead.
-//  * Precision: products whose bf16 rounding would cost accuracy use split
-//    operands (hi + lo bf16, multiplied as hi*hi + hi*lo + lo*hi): A_qk,
-//    (q Gamma) M, A_qk U and k_bar^T U; U0 splits T' (v is exact in bf16).
-//    W, W M and A_kk use single bf16 operands.  Emulating this policy against
-//    the fp64 oracle over decay ranges from g ~ -5 to g ~ -0.05 and initial
-//    states up to N(0, 0.3^2) keeps the output within 1e-2 RMS beyond its own
-//    bf16 rounding and the final state within 2e-3 RMS.
+// The solve is blocked on 16 rows: U1 = T11 R1, U2 = T22 (R2 - A21 U1), where
+// T11, T22 are the inverses of the two 16x16 diagonal blocks of I + A_kk
+// (formed in fp32 from 8x8 forward substitutions and one block merge).  It runs
+// in the carry waves on v_mfma_f32_16x16x16_bf16, whose B operand layout (four
+// consecutive reduction rows per lane group) is exactly the accumulator layout
+// of the previous product, so the three products chain without leaving
+// registers.
+//
+// Organisation: one workgroup of 8 waves per (b, hv, V-tile of VT columns).
+//  * State: carry wave w < VT/16 owns 16 columns of M (all K rows) in MFMA
+//    accumulators for the whole sequence.  M is also used directly as the B
+//    operand of the 32-deep MFMAs: the reduction index may be permuted as long
+//    as both operands agree, so lane group g takes rows {4g..4g+3} of one
+//    16-row tile and of the next; A operands are read from LDS in that order.
+//  * Pipeline (per iteration n; four barriers):
+//      A  P = (q Gamma) M for chunk n       | first operand pass of chunk n+1
+//      B  second operand pass of chunk n+1 (exponentials, split operands)
+//      C  A_qk, A_kk of chunk n+1 (MFMA)    | prefetch of chunk n+2
+//      D  T11, T22 of chunk n+1 (one wave)  | rest of the carry of chunk n
+//    Operands produced for chunk n+1 before D and read by the carry of chunk n
+//    in D are double-buffered in LDS.
+//  * Precision: operands whose bf16 rounding would matter are split into
+//    hi + lo bf16 and multiplied as hi*hi + hi*lo + lo*hi: A_qk, (q Gamma) M,
+//    the three solve products, A_qk U and k_bar^T U.  A_kk and (k Gamma) M use
+//    single bf16 operands.  Emulating this policy against the fp64 oracle over
+//    decay ranges from g ~ -5 to g ~ -0.05 and initial states up to
+//    N(0, 0.3^2) keeps the output within 3e-3 RMS beyond its own bf16 rounding
+//    and the final state within 3e-3 RMS.
 
 #include "kda_internal.h"
 
@@ -44,19 +54,21 @@ constexpr int kC = 32;
 constexpr int kNW = 8;
 constexpr int kNT = kNW * 64;
 constexpr int kRef = 15;
-constexpr int kTWave = kNW - 1;    // wave that forms T
+constexpr int kTWave = kNW - 1;    // wave that forms T11, T22
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma16(const bf16x4 &a, const bf16x4 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ __bf16 bf(float x) { return static_cast<__bf16>(x); }
 __device__ __forceinline__ float fl(__bf16 x) { return static_cast<float>(x); }
@@ -64,14 +76,11 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 
 __device__ __forceinline__ bf16x8 ld8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 __device__ __forceinline__ bf16x4 ld4(const __bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
-// rows {p[0..3], p[16..19]} as one fragment (the permuted reduction order)
-__device__ __forceinline__ bf16x8 ld4x2(const __bf16 *p) {
-    const bf16x4 a = ld4(p), b = ld4(p + 16);
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
 __device__ __forceinline__ bf16x8 cat(const bf16x4 &a, const bf16x4 &b) {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
+// rows {p[0..3], p[16..19]} as one fragment (the permuted reduction order)
+__device__ __forceinline__ bf16x8 ld4x2(const __bf16 *p) { return cat(ld4(p), ld4(p + 16)); }
 __device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -81,6 +90,7 @@ __device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 // Raw buffer resource over `bytes` bytes from `p`: out-of-range loads read 0
 // and out-of-range stores are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
@@ -112,41 +122,43 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // Wait for this wave's LDS accesses (cross-lane exchange inside one wave).
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int K, int VT>
+template <int K>
 struct Plan {
     static constexpr int LDK = K + 8;    // bf16 rows over K
     static constexpr int LDC = kC + 8;   // bf16 rows over C
     static constexpr int LDF = kC + 4;   // fp32 C x C
+    static constexpr int L16 = 16 + 8;   // bf16 rows of a 16x16 block
     static constexpr int CP = K / 2;     // column pairs in the operand phase
     static constexpr int NRG = kNT / CP; // row groups
     static constexpr int RPG = kC / NRG; // rows per group
-    // region A: operands of the A matrices (written in the operand phase, read
-    // by the A phase); the T phase later reuses it for its fp32 scratch
+    static constexpr int B16 = 16 * L16 * 2;  // bytes of one 16x16 bf16 block
+    // region A: operands of the A matrices (operand pass -> A phase); the T
+    // phase reuses it for fp32 scratch
     static constexpr int oLk = 0;                                // [C][LDK]
     static constexpr int oLq = oLk + kC * LDK * 2;               // [2][C][LDK] hi, lo
-    static constexpr int oR = oLq + 2 * kC * LDK * 2;            // [2][C][LDK]
+    static constexpr int oR = oLq + 2 * kC * LDK * 2;            // [2][C][LDK] hi, lo
     static constexpr int endA = oR + 2 * kC * LDK * 2;
-    static constexpr int oTf = 0;                                // fp32 [C][LDF] (T phase)
-    static constexpr int oX = oTf + kC * LDF * 4;                // fp32 [C][LDF] (T phase)
+    static constexpr int oTf = 0;                                // fp32 [C][LDF]
+    static constexpr int oX = oTf + kC * LDF * 4;                // fp32 [C][LDF]
     static_assert(oX + kC * LDF * 4 <= endA, "T scratch must fit in region A");
-    static constexpr int oKG = endA;                             // [K][LDC]   k Gamma, transposed
-    static constexpr int oQh = oKG + K * LDC * 2;                // [2][C][LDK]  q Gamma hi, lo
-    static constexpr int oKbarT = oQh + 2 * kC * LDK * 2;        // [2 buf][2][K][LDC]  k_bar^T hi, lo
-    static constexpr int oAqk = oKbarT + 4 * K * LDC * 2;        // [2 buf][2][C][LDC] hi, lo
-    static constexpr int oW = oAqk + 4 * kC * LDC * 2;           // [C][LDK]
-    static constexpr int oTb = oW + kC * LDK * 2;                // [2][C][LDC]  T' hi, lo
-    static constexpr int oAkk = oTb + 2 * kC * LDC * 2;          // fp32 [C][LDF]
+    static constexpr int oQh = endA;                             // [2][C][LDK]  q Gamma hi, lo
+    static constexpr int oKGr = oQh + 2 * kC * LDK * 2;          // [2 buf][C][LDK]  k Gamma
+    static constexpr int oKbarT = oKGr + 2 * kC * LDK * 2;       // [2 buf][2][K][LDC]  k_bar^T hi, lo
+    static constexpr int oAqk = oKbarT + 4 * K * LDC * 2;        // [2 buf][2][C][LDC]  hi, lo
+    static constexpr int oA21 = oAqk + 4 * kC * LDC * 2;         // [2 buf][2][16][L16]  -A21 hi, lo
+    static constexpr int oTi = oA21 + 4 * B16;                   // [2 buf][2 blk][2][16][L16]  T11, T22
+    static constexpr int oAkk = oTi + 8 * B16;                   // fp32 [C][LDF]
     static constexpr int oGam = oAkk + kC * LDF * 4;             // fp32 [2 buf][K]
-    static constexpr int oBeta = oGam + 2 * K * 4;               // fp32 [C]
-    static constexpr int oGtot = oBeta + kC * 4;                 // fp32 [NRG][K]
+    static constexpr int oBeta = oGam + 2 * K * 4;               // fp32 [2 buf][C]
+    static constexpr int oGtot = oBeta + 2 * kC * 4;             // fp32 [NRG][K]
     static constexpr int bytes = oGtot + NRG * K * 4;
 };
 
 template <int K, int VT>
 __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
-    using L = Plan<K, VT>;
+    using L = Plan<K>;
     static_assert(L::bytes <= 160 * 1024, "LDS plan exceeds 160 KB");
-    constexpr int LDK = L::LDK, LDC = L::LDC, LDF = L::LDF;
+    constexpr int LDK = L::LDK, LDC = L::LDC, LDF = L::LDF, L16 = L::L16;
     constexpr int CP = L::CP, NRG = L::NRG, RPG = L::RPG;
     constexpr int KT = K / 16, KS = K / 32;
     constexpr int NCW = VT / 16;                 // carry waves
@@ -157,23 +169,20 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     __bf16 *sLk = reinterpret_cast<__bf16 *>(smem + L::oLk);
     __bf16 *sLq = reinterpret_cast<__bf16 *>(smem + L::oLq);
     __bf16 *sR = reinterpret_cast<__bf16 *>(smem + L::oR);
-    __bf16 *sKG = reinterpret_cast<__bf16 *>(smem + L::oKG);
-    __bf16 *sQh = reinterpret_cast<__bf16 *>(smem + L::oQh);
-    __bf16 *sKbarT = reinterpret_cast<__bf16 *>(smem + L::oKbarT);
-    __bf16 *sAqk = reinterpret_cast<__bf16 *>(smem + L::oAqk);
-    __bf16 *sW = reinterpret_cast<__bf16 *>(smem + L::oW);
-    __bf16 *sTb = reinterpret_cast<__bf16 *>(smem + L::oTb);
-    float *sAkk = reinterpret_cast<float *>(smem + L::oAkk);
     float *sTf = reinterpret_cast<float *>(smem + L::oTf);
     float *sX = reinterpret_cast<float *>(smem + L::oX);
+    __bf16 *sQh = reinterpret_cast<__bf16 *>(smem + L::oQh);
+    __bf16 *sKGr = reinterpret_cast<__bf16 *>(smem + L::oKGr);
+    __bf16 *sKbarT = reinterpret_cast<__bf16 *>(smem + L::oKbarT);
+    __bf16 *sAqk = reinterpret_cast<__bf16 *>(smem + L::oAqk);
+    __bf16 *sA21 = reinterpret_cast<__bf16 *>(smem + L::oA21);
+    __bf16 *sTi = reinterpret_cast<__bf16 *>(smem + L::oTi);
+    float *sAkk = reinterpret_cast<float *>(smem + L::oAkk);
     float *sGam = reinterpret_cast<float *>(smem + L::oGam);
     float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
     float *sGtot = reinterpret_cast<float *>(smem + L::oGtot);
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int lr = lane & 15, lg = lane >> 4;
-
+    const int wave = threadIdx.x >> 6;
     const int nvt = a.V / VT;
     const int vt_idx = blockIdx.x % nvt;
     const int bhv = blockIdx.x / nvt;
@@ -183,6 +192,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     const int T = a.T;
     const int HV = a.HV, V = a.V;
     const int NC = (T + kC - 1) / kC;
+    const bool carry = wave < NCW;
 
     const uint16_t *qg = static_cast<const uint16_t *>(a.q);
     const uint16_t *kg = static_cast<const uint16_t *>(a.k);
@@ -201,28 +211,22 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         return static_cast<uint32_t>(((nv - 1) * stride + rowlen) * esz);
     };
 
-    // operand-phase mapping: thread owns columns f, f+1 of RPG consecutive rows
-    const int cp = tid % CP, rg = tid / CP;
-    const int f0 = 2 * cp;
+    // operand-pass inputs of one chunk: thread owns columns f, f+1 of RPG rows
     float2 pf_g[RPG];
     uint32_t pf_q[RPG], pf_k[RPG];
     float pf_b[RPG];
     auto load_prep = [&](int ch) {
-        const int tid = opaque_tid();
-        const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-        const int cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
-        const int vcol = v0 + 16 * wave + lr;
-        (void)lane; (void)lr; (void)lg; (void)cp; (void)rg; (void)f0; (void)vcol;
+        const int tid = opaque_tid(), rg = tid / CP, f0 = 2 * (tid % CP);
         const int t0 = ch * kC;
         const size_t tb = tok_b + t0;
-        const auto rg_ = make_rsrc(a.g + (tb * HV + hv) * K, rows_bytes(t0, g_stride, K, 4));
+        const auto rgr = make_rsrc(a.g + (tb * HV + hv) * K, rows_bytes(t0, g_stride, K, 4));
         const auto rq = make_rsrc(qg + (tb * a.H + h) * K, rows_bytes(t0, qk_stride, K, 2));
         const auto rk = make_rsrc(kg + (tb * a.H + h) * K, rows_bytes(t0, qk_stride, K, 2));
         const auto rb = make_rsrc(a.beta + tb * HV + hv, rows_bytes(t0, HV, 1, 4));
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
             const int i = rg * RPG + r;
-            const auto gg = __builtin_amdgcn_raw_buffer_load_b64(rg_, (i * g_stride + f0) * 4, 0, 0);
+            const auto gg = __builtin_amdgcn_raw_buffer_load_b64(rgr, (i * g_stride + f0) * 4, 0, 0);
             pf_g[r] = make_float2(__uint_as_float(gg[0]), __uint_as_float(gg[1]));
             pf_q[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, (i * qk_stride + f0) * 2, 0, 0);
             pf_k[r] = __builtin_amdgcn_raw_buffer_load_b32(rk, (i * qk_stride + f0) * 2, 0, 0);
@@ -230,28 +234,26 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         }
     };
 
-    // carry mapping: wave w < NCW owns columns v0 + 16w + lr of all K rows
-    const bool carry = wave < NCW;
-    const int vcol = v0 + 16 * wave + lr;
-    bf16x8 pf_v;
+    // carry inputs: v of the wave's 16 columns, rows in accumulator order
+    // (row tile rt, rows 4*lg + r)
+    uint16_t pf_v[2][4];
     auto load_v = [&](int ch) {
-        const int tid = opaque_tid();
-        const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-        const int cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
+        const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
         const int vcol = v0 + 16 * wave + lr;
-        (void)lane; (void)lr; (void)lg; (void)cp; (void)rg; (void)f0; (void)vcol;
         const int t0 = ch * kC;
         const auto rv = make_rsrc(vg + ((tok_b + t0) * HV + hv) * V, rows_bytes(t0, v_stride, V, 2));
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int j = 8 * lg + jj;
-            const uint16_t x = __builtin_amdgcn_raw_buffer_load_b16(rv, (j * v_stride + vcol) * 2, 0, 0);
-            pf_v[jj] = __builtin_bit_cast(__bf16, x);
-        }
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pf_v[rt][r] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rv, ((rt * 16 + 4 * lg + r) * v_stride + vcol) * 2, 0, 0);
     };
 
     f32x4 m[KT];
     if (carry) {
+        const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+        const int vcol = v0 + 16 * wave + lr;
         const float *S0 = a.S0 ? a.S0 + (static_cast<size_t>(b) * HV + hv) * K * V : nullptr;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
@@ -260,16 +262,12 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 m[kt][r] = S0 ? S0[static_cast<size_t>(kt * 16 + lg * 4 + r) * V + vcol] : 0.f;
     }
 
-    // registers carried from the first to the second operand phase
+    // registers carried from the first to the second operand pass
     float gl[RPG][2], qv[RPG][2], kv[RPG][2];
 
-    // ======================= operand phase, part 1: cumulative decay within groups
-    auto op1 = [&]() {
-        const int tid = opaque_tid();
-        const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-        const int cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
-        const int vcol = v0 + 16 * wave + lr;
-        (void)lane; (void)lr; (void)lg; (void)cp; (void)rg; (void)f0; (void)vcol;
+    // ======================= operand pass 1: cumulative decay within row groups
+    auto op1 = [&](int buf) {
+        const int tid = opaque_tid(), cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
             gl[r][0] = pf_g[r].x * kLog2e;
@@ -287,16 +285,12 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         *reinterpret_cast<float2 *>(sGtot + rg * K + f0) = make_float2(gl[RPG - 1][0], gl[RPG - 1][1]);
         if (cp == 0)
 #pragma unroll
-            for (int r = 0; r < RPG; ++r) sBeta[rg * RPG + r] = pf_b[r];
+            for (int r = 0; r < RPG; ++r) sBeta[buf * kC + rg * RPG + r] = pf_b[r];
     };
 
-    // ======================= operand phase, part 2: exponentials and operands
+    // ======================= operand pass 2: exponentials and MFMA operands
     auto op2 = [&](int buf) {
-        const int tid = opaque_tid();
-        const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-        const int cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
-        const int vcol = v0 + 16 * wave + lr;
-        (void)lane; (void)lr; (void)lg; (void)cp; (void)rg; (void)f0; (void)vcol;
+        const int tid = opaque_tid(), cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
         float off[2] = {0.f, 0.f}, Gr[2] = {0.f, 0.f}, Gl[2] = {0.f, 0.f};
 #pragma unroll
         for (int g2 = 0; g2 < NRG; ++g2) {
@@ -309,31 +303,32 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         float pr[2], pl[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            pr[c] = ex2(Gr[c]);
-            pl[c] = ex2(Gl[c] - Gr[c]);
+            pr[c] = ex2(Gr[c]);             // 2^{G_r}         >= 2^-116
+            pl[c] = ex2(Gl[c] - Gr[c]);     // 2^{G_last - G_r} in [2^-116, 1]
         }
         if (rg == 0)
             *reinterpret_cast<float2 *>(sGam + buf * K + f0) = make_float2(ex2(Gl[0]), ex2(Gl[1]));
-        __bf16 kgT[2][RPG], kbT[2][RPG], kbTl[2][RPG];
+        __bf16 kbT[2][RPG], kbTl[2][RPG];
+        __bf16 *kgr = sKGr + buf * kC * LDK;
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
             const int i = rg * RPG + r;
-            bf16x2 lk, lqh, lql, rh, rl, qh, ql;
+            bf16x2 lk, lqh, lql, rh, rl, qh, ql, kgm;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const float d = off[c] + gl[r][c] - Gr[c];
                 const float e1 = ex2(d), e2 = ex2(-d);
                 const float xlk = kv[r][c] * e1, xlq = qv[r][c] * e1, xr = kv[r][c] * e2;
+                const float xqh = xlq * pr[c];   // q 2^{G_i}
+                const float xkb = xr * pl[c];    // k 2^{G_last - G_i}
                 lk[c] = bf(xlk);
                 lqh[c] = bf(xlq);
                 lql[c] = bf(xlq - fl(lqh[c]));
                 rh[c] = bf(xr);
                 rl[c] = bf(xr - fl(rh[c]));
-                const float xqh = xlq * pr[c];   // q 2^{G_i}
-                const float xkb = xr * pl[c];    // k 2^{G_last - G_i}
                 qh[c] = bf(xqh);
                 ql[c] = bf(xqh - fl(qh[c]));
-                kgT[c][r] = bf(xlk * pr[c]);     // k 2^{G_i}
+                kgm[c] = bf(xlk * pr[c]);        // k 2^{G_i}
                 kbT[c][r] = bf(xkb);
                 kbTl[c][r] = bf(xkb - fl(kbT[c][r]));
             }
@@ -344,11 +339,11 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             *reinterpret_cast<bf16x2 *>(sR + kC * LDK + i * LDK + f0) = rl;
             *reinterpret_cast<bf16x2 *>(sQh + i * LDK + f0) = qh;
             *reinterpret_cast<bf16x2 *>(sQh + kC * LDK + i * LDK + f0) = ql;
+            *reinterpret_cast<bf16x2 *>(kgr + i * LDK + f0) = kgm;
         }
         __bf16 *kb_buf = sKbarT + buf * 2 * K * LDC;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            store_rows<RPG>(sKG + (f0 + c) * LDC + rg * RPG, kgT[c]);
             store_rows<RPG>(kb_buf + (f0 + c) * LDC + rg * RPG, kbT[c]);
             store_rows<RPG>(kb_buf + K * LDC + (f0 + c) * LDC + rg * RPG, kbTl[c]);
         }
@@ -356,13 +351,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
 
     // ======================= A_qk (3-term split) and A_kk on MFMA
     auto phaseA = [&](int buf) {
-        const int tid = opaque_tid();
-        const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-        const int cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
-        const int vcol = v0 + 16 * wave + lr;
-        (void)lane; (void)lr; (void)lg; (void)cp; (void)rg; (void)f0; (void)vcol;
+        const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
         const int rt = (wave % 3) == 0 ? 0 : 1;
         const int ct = (wave % 3) == 2 ? 1 : 0;
+        __bf16 *aq = sAqk + buf * 2 * kC * LDC;
         if (wave < 3) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -376,14 +368,13 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 acc = mfma(ah, bl, acc);
                 acc = mfma(al, bh, acc);
             }
-            __bf16 *dst = sAqk + buf * 2 * kC * LDC;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = rt * 16 + lg * 4 + r, j = ct * 16 + lr;
                 const float x = (j <= i) ? acc[r] : 0.f;
                 const __bf16 hi = bf(x);
-                dst[i * LDC + j] = hi;
-                dst[kC * LDC + i * LDC + j] = bf(x - fl(hi));
+                aq[i * LDC + j] = hi;
+                aq[kC * LDC + i * LDC + j] = bf(x - fl(hi));
             }
         } else if (wave < 6) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -392,33 +383,36 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 const int kk = ks * 32 + lg * 8;
                 acc = mfma(ld8(sLk + (rt * 16 + lr) * LDK + kk), ld8(sR + (ct * 16 + lr) * LDK + kk), acc);
             }
+            __bf16 *a21 = sA21 + buf * 2 * 16 * L16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = rt * 16 + lg * 4 + r, j = ct * 16 + lr;
-                sAkk[i * LDF + j] = (j < i) ? sBeta[i] * acc[r] : 0.f;
+                const float x = (j < i) ? sBeta[buf * kC + i] * acc[r] : 0.f;
+                sAkk[i * LDF + j] = x;
+                if (rt == 1 && ct == 0) {   // -A21, the off-diagonal block of the solve
+                    const __bf16 hi = bf(-x);
+                    a21[(lg * 4 + r) * L16 + lr] = hi;
+                    a21[16 * L16 + (lg * 4 + r) * L16 + lr] = bf(-x - fl(hi));
+                }
             }
         } else if (wave == 6) {
             // the all-upper tile (rows 0-15, cols 16-31) of both matrices is zero
-            __bf16 *dst = sAqk + buf * 2 * kC * LDC;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = lg * 4 + r, j = 16 + lr;
                 sAkk[i * LDF + j] = 0.f;
-                dst[i * LDC + j] = bf(0.f);
-                dst[kC * LDC + i * LDC + j] = bf(0.f);
+                aq[i * LDC + j] = bf(0.f);
+                aq[kC * LDC + i * LDC + j] = bf(0.f);
             }
         }
     };
 
-    // ======================= T = (I + A_kk)^-1 in fp32 on one wave; T' = T diag(beta)
-    auto phaseT = [&]() {
-        const int tid = opaque_tid();
-        const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-        const int cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
-        const int vcol = v0 + 16 * wave + lr;
-        (void)lane; (void)lr; (void)lg; (void)cp; (void)rg; (void)f0; (void)vcol;
-        // (a) 8x8 diagonal blocks by forward substitution (lanes 0-31: block, column);
-        //     lanes 32-63 clear the upper 8x8 block of each 16x16 diagonal block.
+    // ======================= T11, T22: inverses of the 16x16 diagonal blocks of
+    // I + A_kk, in fp32 on one wave (8x8 forward substitutions, one merge each)
+    auto phaseT = [&](int buf) {
+        const int lane = opaque_tid() & 63;
+        // (a) 8x8 diagonal blocks (lanes 0-31: block, column); lanes 32-63 clear
+        //     the upper 8x8 block of each 16x16 block.
         if (lane < 32) {
             const int d = lane >> 3, c = lane & 7, o = d * 8;
             float x[8];
@@ -445,7 +439,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             }
         }
         wave_lds_sync();
-        // (b) 16x16 merges: T21 = -T22 (A21 T11), 8x8 blocks, both 16-blocks at once
+        // (b) merges: lower-left 8x8 block of each 16x16 block, -T22 (A21 T11)
         {
             const int p = lane >> 5, e = lane & 31, r = e >> 2, c0 = (e & 3) * 2, o = p * 16;
             float x0 = 0.f, x1 = 0.f;
@@ -469,65 +463,28 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             sTf[(o + 8 + r) * LDF + o + c0 + 1] = -y1;
         }
         wave_lds_sync();
-        // (c) 32x32 merge on fp32 MFMA: X = A21 T11, T21 = -T22 X (16x16 blocks)
+        // (c) T11, T22 as split bf16: lane = (block, row, half row)
         {
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            const int blk = lane >> 5, i = (lane & 31) >> 1, j0 = (lane & 1) * 8, o = blk * 16;
+            bf16x8 hi, lo;
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                x = mfma_f32(sAkk[(16 + lr) * LDF + 4 * s + lg], sTf[(4 * s + lg) * LDF + lr], x);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sX[(4 * lg + r) * LDF + lr] = x[r];
-            wave_lds_sync();
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                y = mfma_f32(sTf[(16 + lr) * LDF + 16 + 4 * s + lg], sX[(4 * s + lg) * LDF + lr], y);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sTf[(16 + 4 * lg + r) * LDF + lr] = -y[r];
-        }
-        wave_lds_sync();
-        // (d) T' = T diag(beta), lower triangle only, split into bf16 hi/lo
-        {
-            const int i = lane >> 1, j0 = (lane & 1) * 16;
-            bf16x8 hi[2], lo[2];
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int j = j0 + jj;
-                const float x = (j <= i) ? sTf[i * LDF + j] * sBeta[j] : 0.f;
-                const __bf16 xh = bf(x);
-                hi[jj >> 3][jj & 7] = xh;
-                lo[jj >> 3][jj & 7] = bf(x - fl(xh));
+            for (int jj = 0; jj < 8; ++jj) {
+                const float x = sTf[(o + i) * LDF + o + j0 + jj];
+                hi[jj] = bf(x);
+                lo[jj] = bf(x - fl(hi[jj]));
             }
-            *reinterpret_cast<bf16x8 *>(sTb + i * LDC + j0) = hi[0];
-            *reinterpret_cast<bf16x8 *>(sTb + i * LDC + j0 + 8) = hi[1];
-            *reinterpret_cast<bf16x8 *>(sTb + kC * LDC + i * LDC + j0) = lo[0];
-            *reinterpret_cast<bf16x8 *>(sTb + kC * LDC + i * LDC + j0 + 8) = lo[1];
+            __bf16 *dst = sTi + ((buf * 2 + blk) * 2) * 16 * L16 + i * L16 + j0;
+            *reinterpret_cast<bf16x8 *>(dst) = hi;
+            *reinterpret_cast<bf16x8 *>(dst + 16 * L16) = lo;
         }
     };
 
-    // ======================= W = T' (k Gamma) on MFMA -> LDS
-    auto phaseW = [&]() {
-        const int tid = opaque_tid();
-        const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-        const int cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
-        const int vcol = v0 + 16 * wave + lr;
-        (void)lane; (void)lr; (void)lg; (void)cp; (void)rg; (void)f0; (void)vcol;
-        for (int t = wave; t < 2 * KT; t += kNW) {
-            const int rt = t & 1, ft = t >> 1;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(ld8(sTb + (rt * 16 + lr) * LDC + lg * 8), ld8(sKG + (ft * 16 + lr) * LDC + lg * 8), acc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sW[(rt * 16 + lg * 4 + r) * LDK + ft * 16 + lr] = bf(acc[r]);
-        }
-    };
-
-    // ======================= carry, part 1: U = T' v - W M,  P = (q Gamma) M
-    f32x4 u[2], pq[2];
-    bf16x8 ub_hi, ub_lo;
-    auto carry1 = [&]() {
-        const int tid = opaque_tid();
-        const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-        bf16x8 mh[KS], ml[KS];
+    // ======================= carry: state products, solve, output, state update
+    f32x4 pq[2];
+    bf16x8 mh[KS];
+    auto carryP = [&]() {   // P = (q Gamma) M, three terms (M split)
+        const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
+        bf16x8 ml[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             bf16x4 h0, l0, h1, l1;
@@ -538,38 +495,75 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(ld8(sTb + (rt * 16 + lr) * LDC + lg * 8), pf_v, acc);
-            acc = mfma(ld8(sTb + kC * LDC + (rt * 16 + lr) * LDC + lg * 8), pf_v, acc);
-            f32x4 wm = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
             const int base = (rt * 16 + lr) * LDK + lg * 4;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const bf16x8 wf = ld4x2(sW + base + s * 32);
                 const bf16x8 qf = ld4x2(sQh + base + s * 32);
                 const bf16x8 qfl = ld4x2(sQh + kC * LDK + base + s * 32);
-                wm = mfma(wf, mh[s], wm);
                 p = mfma(qf, mh[s], p);
                 p = mfma(qf, ml[s], p);
                 p = mfma(qfl, mh[s], p);
             }
-            u[rt] = acc - wm;
             pq[rt] = p;
         }
-        bf16x4 h0, l0, h1, l1;
-        split4(u[0], h0, l0);
-        split4(u[1], h1, l1);
-        ub_hi = cat(h0, h1);
-        ub_lo = cat(l0, l1);
     };
 
-    // ======================= carry, part 2: O = s (P + A_qk U) -> HBM;  M update
-    auto carry2 = [&](int buf, int t0) {
-        const int tid = opaque_tid();
-        const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-        const int cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
+    auto carryRest = [&](int buf, int t0) {
+        const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
         const int vcol = v0 + 16 * wave + lr;
-        (void)lane; (void)lr; (void)lg; (void)cp; (void)rg; (void)f0; (void)vcol;
+        // R = diag(beta) (v - (k Gamma) M), accumulator layout per 16-row tile
+        const __bf16 *kgr = sKGr + buf * kC * LDK;
+        const float *beta = sBeta + buf * kC;
+        f32x4 rr[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            const int base = (rt * 16 + lr) * LDK + lg * 4;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) x = mfma(ld4x2(kgr + base + s * 32), mh[s], x);
+            const f32x4 bt = *reinterpret_cast<const f32x4 *>(beta + rt * 16 + lg * 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float vv = __uint_as_float(static_cast<uint32_t>(pf_v[rt][r]) << 16);
+                rr[rt][r] = bt[r] * (vv - x[r]);
+            }
+        }
+        // U1 = T11 R1;  Y = R2 - A21 U1;  U2 = T22 Y   (16x16x16 MFMAs, 3 terms each)
+        const __bf16 *t11 = sTi + (buf * 2 + 0) * 2 * 16 * L16 + lr * L16 + lg * 4;
+        const __bf16 *t22 = sTi + (buf * 2 + 1) * 2 * 16 * L16 + lr * L16 + lg * 4;
+        const __bf16 *a21 = sA21 + buf * 2 * 16 * L16 + lr * L16 + lg * 4;
+        f32x4 u[2];
+        bf16x4 xh, xl, uh0, ul0;
+        split4(rr[0], xh, xl);
+        {
+            const bf16x4 th = ld4(t11), tl = ld4(t11 + 16 * L16);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mfma16(th, xh, acc);
+            acc = mfma16(th, xl, acc);
+            acc = mfma16(tl, xh, acc);
+            u[0] = acc;
+        }
+        split4(u[0], uh0, ul0);
+        {
+            const bf16x4 ah = ld4(a21), al = ld4(a21 + 16 * L16);
+            f32x4 y = rr[1];
+            y = mfma16(ah, uh0, y);
+            y = mfma16(ah, ul0, y);
+            y = mfma16(al, uh0, y);
+            split4(y, xh, xl);
+            const bf16x4 th = ld4(t22), tl = ld4(t22 + 16 * L16);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mfma16(th, xh, acc);
+            acc = mfma16(th, xl, acc);
+            acc = mfma16(tl, xh, acc);
+            u[1] = acc;
+        }
+        bf16x4 uh1, ul1;
+        split4(u[1], uh1, ul1);
+        const bf16x8 ub_hi = cat(uh0, uh1), ub_lo = cat(ul0, ul1);
+
+        // O = scale (P + A_qk U) -> HBM
         const __bf16 *aq = sAqk + buf * 2 * kC * LDC;
         const auto ro = make_rsrc(og + ((tok_b + t0) * HV + hv) * V, rows_bytes(t0, v_stride, V, 2));
 #pragma unroll
@@ -587,8 +581,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                                                       (i * v_stride + vcol) * 2, 0, 0);
             }
         }
-        // M update, one 16-row tile at a time with the next tile's operands in
-        // flight (the scheduling barrier bounds how far loads are hoisted).
+        // M <- Gamma_last (.) M + k_bar^T U
         const __bf16 *kb_buf = sKbarT + buf * 2 * K * LDC + lr * LDC + lg * 4;
         const float *gam = sGam + buf * K + lg * 4;
 #pragma unroll
@@ -606,52 +599,46 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
 
     // ---------------------------------------------------------------- prologue: chunk 0
     load_prep(0);
-    op1();
+    op1(0);
     lds_barrier();
     op2(0);
     if (NC > 1) load_prep(1);
     lds_barrier();
     phaseA(0);
     lds_barrier();
-    if (wave == kTWave) phaseT();
-    lds_barrier();
-    phaseW();
+    if (wave == kTWave) phaseT(0);
     if (carry) load_v(0);
     lds_barrier();
 
     // ---------------------------------------------------------------- main loop
-    // Iteration n runs the carry of chunk n and prepares chunk n+1:
-    //   A  U, P of n (carry waves, MFMA) | first operand pass of n+1 (VALU)
-    //   B  second operand pass of n+1 (VALU, exponentials)
-    //   C  A matrices of n+1 (MFMA); prefetch of chunk n+2
-    //   D  T of n+1 (one wave, VALU) | O, M update of n (carry waves, MFMA)
-    //   E  W of n+1 (MFMA)
-    // U and P read q Gamma of chunk n before the operand pass overwrites it;
-    // k_bar, Gamma_last and A_qk are read in D and are double-buffered.
     for (int n = 0; n < NC; ++n) {
         const bool next = n + 1 < NC;
         const int cur = n & 1, nxt = cur ^ 1;
-        if (carry) {
-            carry1();
-            if (next) load_v(n + 1);
-        }
-        if (next) op1();
+        // A: P of chunk n reads (q Gamma) before the operand pass overwrites it
+        if (carry) carryP();
+        if (next) op1(nxt);
         lds_barrier();
+        // B
         if (next) op2(nxt);
         lds_barrier();
+        // C
         if (next) {
             phaseA(nxt);
             if (n + 2 < NC) load_prep(n + 2);
         }
         lds_barrier();
-        if (next && wave == kTWave) phaseT();
-        if (carry) carry2(cur, n * kC);
-        lds_barrier();
-        if (next) phaseW();
+        // D
+        if (next && wave == kTWave) phaseT(nxt);
+        if (carry) {
+            carryRest(cur, n * kC);
+            if (next) load_v(n + 1);
+        }
         lds_barrier();
     }
 
     if (a.ST && carry) {
+        const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+        const int vcol = v0 + 16 * wave + lr;
         float *ST = a.ST + (static_cast<size_t>(b) * HV + hv) * K * V;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
@@ -663,7 +650,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
 
 template <int K, int VT>
 hipError_t launch_kvt(const PrefillArgs &a, hipStream_t stream) {
-    using L = Plan<K, VT>;
+    using L = Plan<K>;
     auto kern = prefill_bf16_kernel<K, VT>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
