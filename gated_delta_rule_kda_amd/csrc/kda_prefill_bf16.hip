@@ -18,25 +18,36 @@
 //
 // The solve is blocked on 16 rows: U1 = T11 R1, U2 = T22 (R2 - A21 U1), where
 // T11, T22 are the inverses of the two 16x16 diagonal blocks of I + A_kk
-// (formed in fp32 from 8x8 forward substitutions and one block merge).  It runs
-// in the carry waves on v_mfma_f32_16x16x16_bf16, whose B operand layout (four
-// consecutive reduction rows per lane group) is exactly the accumulator layout
-// of the previous product, so the three products chain without leaving
-// registers.
+// (fp32 forward substitution, one column per lane).  It runs in the carry
+// waves on v_mfma_f32_16x16x16_bf16, whose B operand layout (four consecutive
+// reduction rows per lane group) is exactly the accumulator layout of the
+// previous product, so the three products chain without leaving registers.
 //
 // Organisation: one workgroup of 8 waves per (b, hv, V-tile of VT columns).
-//  * State: carry wave w < VT/16 owns 16 columns of M (all K rows) in MFMA
-//    accumulators for the whole sequence.  M is also used directly as the B
-//    operand of the 32-deep MFMAs: the reduction index may be permuted as long
-//    as both operands agree, so lane group g takes rows {4g..4g+3} of one
-//    16-row tile and of the next; A operands are read from LDS in that order.
-//  * Pipeline (per iteration n; four barriers):
-//      A  P = (q Gamma) M for chunk n       | first operand pass of chunk n+1
-//      B  second operand pass of chunk n+1 (exponentials, split operands)
-//      C  A_qk, A_kk of chunk n+1 (MFMA)    | prefetch of chunk n+2
-//      D  T11, T22 of chunk n+1 (one wave)  | rest of the carry of chunk n
-//    Operands produced for chunk n+1 before D and read by the carry of chunk n
-//    in D are double-buffered in LDS.
+// Wave w and wave w + 4 share one SIMD; a single wave issues at most one VALU
+// instruction every four cycles, so the VALU-heavy operand pass is spread over
+// all eight waves and the MFMA chains of the carry interleave with it.
+//  * carry waves 0..3 hold the state: carry wave w owns NG blocks of 16
+//    columns of M (all K rows) in MFMA accumulators for the whole sequence.
+//    M is also used directly as the B operand of the 32-deep MFMAs: the
+//    reduction index may be permuted as long as both operands agree, so lane
+//    group g takes rows {4g..4g+3} of one 16-row tile and of the next; A
+//    operands are read from LDS in that order.
+//  * operand pass: each operand wave owns a slice of K columns and all 32 rows
+//    of the chunk (so the cumulative sums never leave the wave) and turns q, k,
+//    g, beta of the next chunk into MFMA operands (exponentials, hi/lo splits).
+//  * waves 4..7 then form A_kk's diagonal-block inverses T11, T22 (fp32
+//    forward substitution, both blocks at once on one wave), A_qk and -A21.
+//  * Pipeline (per chunk n; two barriers):
+//      P1  carry: R, solve, O (-> HBM), M update of chunk n
+//          all:   operand pass of chunk n+1, prefetch of chunk n+2
+//      P2  carry: (q Gamma) M and (k Gamma) M of chunk n+1
+//          waves 4..7: T11, T22, A_qk, -A21 of chunk n+1
+//    Operands written in P1 and read by the carry in the next P1 (k_bar^T,
+//    Gamma_last, beta) are double-buffered in LDS; everything else is single.
+//  * MFMA chains use independent accumulators (hi*hi, hi*lo, lo*hi apart) and
+//    operand fragments are read ahead, so chains run at MFMA throughput
+//    instead of MFMA and LDS latency.
 //  * Precision: operands whose bf16 rounding would matter are split into
 //    hi + lo bf16 and multiplied as hi*hi + hi*lo + lo*hi: A_qk, (q Gamma) M,
 //    the three solve products, A_qk U and k_bar^T U.  A_kk and (k Gamma) M use
@@ -53,8 +64,8 @@ namespace {
 constexpr int kC = 32;
 constexpr int kNW = 8;
 constexpr int kNT = kNW * 64;
+constexpr int kMaxCW = 4;          // carry waves 0..3 at most
 constexpr int kRef = 15;
-constexpr int kTWave = kNW - 1;    // wave that forms T11, T22
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -62,6 +73,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -79,8 +91,6 @@ __device__ __forceinline__ bf16x4 ld4(const __bf16 *p) { return *reinterpret_cas
 __device__ __forceinline__ bf16x8 cat(const bf16x4 &a, const bf16x4 &b) {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-// rows {p[0..3], p[16..19]} as one fragment (the permuted reduction order)
-__device__ __forceinline__ bf16x8 ld4x2(const __bf16 *p) { return cat(ld4(p), ld4(p + 16)); }
 __device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -90,22 +100,32 @@ __device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// (a, b) -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pk(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// hi = bf16(a, b), lo = bf16(a - hi_a, b - hi_b): six instructions per pair
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = pk(a, b);
+    lo = pk(a - bf_lo(hi), b - bf_hi(hi));
+}
+__device__ __forceinline__ void st_word(__bf16 *p, uint32_t w) { *reinterpret_cast<uint32_t *>(p) = w; }
+// NW consecutive packed words as one LDS store (NW in {1, 2, 4})
+template <int NW>
+__device__ __forceinline__ void st_words(__bf16 *p, const uint32_t (&w)[NW]) {
+    if constexpr (NW == 4) {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if constexpr (NW == 2) {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+    } else {
+        *reinterpret_cast<uint32_t *>(p) = w[0];
+    }
+}
 
 // Raw buffer resource over `bytes` bytes from `p`: out-of-range loads read 0
 // and out-of-range stores are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes), 0x00020000);
-}
-// RPG consecutive bf16 values as one LDS store (RPG in {1, 2, 4}).
-template <int RPG>
-__device__ __forceinline__ void store_rows(__bf16 *dst, const __bf16 (&x)[RPG]) {
-    if constexpr (RPG == 4) {
-        *reinterpret_cast<bf16x4 *>(dst) = bf16x4{x[0], x[1], x[2], x[3]};
-    } else if constexpr (RPG == 2) {
-        *reinterpret_cast<bf16x2 *>(dst) = bf16x2{x[0], x[1]};
-    } else {
-        dst[0] = x[0];
-    }
 }
 // The thread index behind an empty asm: values derived from it inside the
 // chunk loop are recomputed per use instead of being hoisted out of the loop
@@ -119,70 +139,77 @@ __device__ __forceinline__ int opaque_tid() {
 // wait for outstanding global loads, so prefetches stay in flight across it
 // (each register is waited for at its first use).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Wait for this wave's LDS accesses (cross-lane exchange inside one wave).
+// Wait for this wave's LDS accesses (exchange between lanes of one wave).
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int K>
 struct Plan {
     static constexpr int LDK = K + 8;    // bf16 rows over K
     static constexpr int LDC = kC + 8;   // bf16 rows over C
-    static constexpr int LDF = kC + 4;   // fp32 C x C
     static constexpr int L16 = 16 + 8;   // bf16 rows of a 16x16 block
-    static constexpr int CP = K / 2;     // column pairs in the operand phase
-    static constexpr int NRG = kNT / CP; // row groups
-    static constexpr int RPG = kC / NRG; // rows per group
-    static constexpr int B16 = 16 * L16 * 2;  // bytes of one 16x16 bf16 block
-    // region A: operands of the A matrices (operand pass -> A phase); the T
-    // phase reuses it for fp32 scratch
-    static constexpr int oLk = 0;                                // [C][LDK]
-    static constexpr int oLq = oLk + kC * LDK * 2;               // [2][C][LDK] hi, lo
-    static constexpr int oR = oLq + 2 * kC * LDK * 2;            // [2][C][LDK] hi, lo
-    static constexpr int endA = oR + 2 * kC * LDK * 2;
-    static constexpr int oTf = 0;                                // fp32 [C][LDF]
-    static constexpr int oX = oTf + kC * LDF * 4;                // fp32 [C][LDF]
-    static_assert(oX + kC * LDF * 4 <= endA, "T scratch must fit in region A");
-    static constexpr int oQh = endA;                             // [2][C][LDK]  q Gamma hi, lo
-    static constexpr int oKGr = oQh + 2 * kC * LDK * 2;          // [2 buf][C][LDK]  k Gamma
-    static constexpr int oKbarT = oKGr + 2 * kC * LDK * 2;       // [2 buf][2][K][LDC]  k_bar^T hi, lo
-    static constexpr int oAqk = oKbarT + 4 * K * LDC * 2;        // [2 buf][2][C][LDC]  hi, lo
-    static constexpr int oA21 = oAqk + 4 * kC * LDC * 2;         // [2 buf][2][16][L16]  -A21 hi, lo
-    static constexpr int oTi = oA21 + 4 * B16;                   // [2 buf][2 blk][2][16][L16]  T11, T22
-    static constexpr int oAkk = oTi + 8 * B16;                   // fp32 [C][LDF]
-    static constexpr int oGam = oAkk + kC * LDF * 4;             // fp32 [2 buf][K]
+    static constexpr int LDT = 20;       // fp32 rows of a 16x16 block
+    static constexpr int CPW = K / 16 > 4 ? K / 16 : 4;   // column pairs per operand wave
+    static constexpr int NOW = K / (2 * CPW);             // operand waves (the last NOW waves)
+    static constexpr int NRG = 64 / CPW;                  // row groups per operand wave
+    static constexpr int RPG = kC / NRG;                  // rows per group
+    static constexpr int oLk = 0;                                // [C][LDK]  k e1
+    static constexpr int oLq = oLk + kC * LDK * 2;               // [2][C][LDK]  q e1 hi, lo
+    static constexpr int oR = oLq + 2 * kC * LDK * 2;            // [2][C][LDK]  k e2 hi, lo
+    static constexpr int oQh = oR + 2 * kC * LDK * 2;            // [2][C][LDK]  q Gamma hi, lo
+    static constexpr int oKGr = oQh + 2 * kC * LDK * 2;          // [C][LDK]  k Gamma
+    static constexpr int oKbarT = oKGr + kC * LDK * 2;           // [2 buf][2][K][LDC]  k_bar^T hi, lo
+    static constexpr int oAqk = oKbarT + 4 * K * LDC * 2;        // [2][C][LDC]  A_qk hi, lo
+    static constexpr int oA21 = oAqk + 2 * kC * LDC * 2;         // [2][16][L16]  -A21 hi, lo
+    static constexpr int oTi = oA21 + 2 * 16 * L16 * 2;          // [2 blk][2][16][L16]  T11, T22
+    static constexpr int oGam = oTi + 4 * 16 * L16 * 2;          // fp32 [2 buf][K]  Gamma_last
     static constexpr int oBeta = oGam + 2 * K * 4;               // fp32 [2 buf][C]
-    static constexpr int oGtot = oBeta + 2 * kC * 4;             // fp32 [NRG][K]
-    static constexpr int bytes = oGtot + NRG * K * 4;
+    static constexpr int oGx = oBeta + 2 * kC * 4;               // fp32 [NOW][NRG][2 CPW]  row-group sums
+    static constexpr int oTs = oGx + NOW * NRG * 2 * CPW * 4;    // fp32 [2 blk][2][16][LDT]  A^T, T
+    static constexpr int bytes = oTs + 4 * 16 * LDT * 4;
 };
 
 template <int K, int VT>
 __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     using L = Plan<K>;
     static_assert(L::bytes <= 160 * 1024, "LDS plan exceeds 160 KB");
-    constexpr int LDK = L::LDK, LDC = L::LDC, LDF = L::LDF, L16 = L::L16;
-    constexpr int CP = L::CP, NRG = L::NRG, RPG = L::RPG;
+    constexpr int LDK = L::LDK, LDC = L::LDC, L16 = L::L16, LDT = L::LDT;
+    constexpr int CPW = L::CPW, NOW = L::NOW, NRG = L::NRG, RPG = L::RPG;
     constexpr int KT = K / 16, KS = K / 32;
-    constexpr int NCW = VT / 16;                 // carry waves
-    static_assert(RPG >= 1 && (kRef + 1) % RPG == 0, "row groups must align with the reference row");
-    static_assert(NCW <= kNW, "too many V columns per workgroup");
+    constexpr int NCW = VT / 16 < kMaxCW ? VT / 16 : kMaxCW;   // carry waves
+    constexpr int NG = VT / (16 * NCW);                          // 16-column blocks per carry wave
+    static_assert(NG * NCW * 16 == VT, "V tile must split evenly over the carry waves");
+    static_assert(NOW * 2 * CPW == K && NOW <= kNW && NOW >= 4, "operand waves must cover K");
+    static_assert(RPG >= 2 && RPG % 2 == 0 && (kRef + 1) % RPG == 0,
+                  "row groups must pair rows and align with the reference row");
+
+    // [C][LDK] operand arrays: element (i, c) sits in 8-column group (c / 8) XOR
+    // (XS if i >= 16).  With the K + 8 row pitch this keeps both the operand
+    // pass's stores (64 lanes over 8..16 rows) and the MFMA fragment reads
+    // (16 consecutive rows) free of LDS bank conflicts.
+    constexpr int XS = K == 128 ? 2 : 1;
+    auto sw = [](int i, int c) { return i * LDK + ((((c >> 3) ^ (((i >> 4) & 1) * XS)) << 3) | (c & 7)); };
+    // Within every block of 32 reduction indices (K columns, or tokens of a
+    // chunk) the operands are stored in the MFMA's permuted order: index
+    // 16h + 4g + e goes to 8g + 4h + e, so lane group g's fragment (rows
+    // {4g..4g+3} of two 16-row tiles) is 16 contiguous bytes, one LDS read.
+    auto perm = [](int c) { return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3); };
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __bf16 *sLk = reinterpret_cast<__bf16 *>(smem + L::oLk);
     __bf16 *sLq = reinterpret_cast<__bf16 *>(smem + L::oLq);
     __bf16 *sR = reinterpret_cast<__bf16 *>(smem + L::oR);
-    float *sTf = reinterpret_cast<float *>(smem + L::oTf);
-    float *sX = reinterpret_cast<float *>(smem + L::oX);
     __bf16 *sQh = reinterpret_cast<__bf16 *>(smem + L::oQh);
     __bf16 *sKGr = reinterpret_cast<__bf16 *>(smem + L::oKGr);
     __bf16 *sKbarT = reinterpret_cast<__bf16 *>(smem + L::oKbarT);
     __bf16 *sAqk = reinterpret_cast<__bf16 *>(smem + L::oAqk);
     __bf16 *sA21 = reinterpret_cast<__bf16 *>(smem + L::oA21);
     __bf16 *sTi = reinterpret_cast<__bf16 *>(smem + L::oTi);
-    float *sAkk = reinterpret_cast<float *>(smem + L::oAkk);
     float *sGam = reinterpret_cast<float *>(smem + L::oGam);
     float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
-    float *sGtot = reinterpret_cast<float *>(smem + L::oGtot);
+    float *sGx = reinterpret_cast<float *>(smem + L::oGx);
+    float *sTs = reinterpret_cast<float *>(smem + L::oTs);
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int nvt = a.V / VT;
     const int vt_idx = blockIdx.x % nvt;
     const int bhv = blockIdx.x / nvt;
@@ -193,6 +220,8 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     const int HV = a.HV, V = a.V;
     const int NC = (T + kC - 1) / kC;
     const bool carry = wave < NCW;
+    const bool opw = NOW == kNW || wave >= kNW - NOW;
+    const int ow = wave - (kNW - NOW);   // operand wave index (valid when opw)
 
     const uint16_t *qg = static_cast<const uint16_t *>(a.q);
     const uint16_t *kg = static_cast<const uint16_t *>(a.k);
@@ -201,28 +230,32 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
 
     // ---- global memory: per-chunk buffer resources (base in SGPRs, 32-bit lane
     // offsets).  A resource covers exactly the valid rows of the chunk, so rows
-    // past the end of the sequence load as zero and their stores are dropped.
+    // past the end of the sequence load as zero and their stores are dropped; a
+    // chunk past the end has an empty resource.  Prefetches are therefore issued
+    // unconditionally, which keeps their registers out of loop-carried copies
+    // that would wait for the loads.
     const size_t tok_b = static_cast<size_t>(b) * T;
     const int g_stride = HV * K;             // elements per token
     const int qk_stride = a.H * K;
     const int v_stride = HV * V;
     auto rows_bytes = [&](int t0, int stride, int rowlen, int esz) -> uint32_t {
         const int nv = min(kC, T - t0);
-        return static_cast<uint32_t>(((nv - 1) * stride + rowlen) * esz);
+        return nv > 0 ? static_cast<uint32_t>(((nv - 1) * stride + rowlen) * esz) : 0u;
     };
 
-    // operand-pass inputs of one chunk: thread owns columns f, f+1 of RPG rows
+    // ======================= operand pass.  Lane = (row group rg, column pair
+    // cp): columns f0, f0 + 1 of rows rg*RPG .. rg*RPG + RPG - 1.
     float2 pf_g[RPG];
     uint32_t pf_q[RPG], pf_k[RPG];
-    float pf_b[RPG];
+    float pf_b;
     auto load_prep = [&](int ch) {
-        const int tid = opaque_tid(), rg = tid / CP, f0 = 2 * (tid % CP);
+        const int lane = opaque_tid() & 63, cp = lane % CPW, rg = lane / CPW;
+        const int f0 = ow * 2 * CPW + 2 * cp;
         const int t0 = ch * kC;
         const size_t tb = tok_b + t0;
         const auto rgr = make_rsrc(a.g + (tb * HV + hv) * K, rows_bytes(t0, g_stride, K, 4));
         const auto rq = make_rsrc(qg + (tb * a.H + h) * K, rows_bytes(t0, qk_stride, K, 2));
         const auto rk = make_rsrc(kg + (tb * a.H + h) * K, rows_bytes(t0, qk_stride, K, 2));
-        const auto rb = make_rsrc(a.beta + tb * HV + hv, rows_bytes(t0, HV, 1, 4));
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
             const int i = rg * RPG + r;
@@ -230,421 +263,491 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             pf_g[r] = make_float2(__uint_as_float(gg[0]), __uint_as_float(gg[1]));
             pf_q[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, (i * qk_stride + f0) * 2, 0, 0);
             pf_k[r] = __builtin_amdgcn_raw_buffer_load_b32(rk, (i * qk_stride + f0) * 2, 0, 0);
-            pf_b[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, i * HV * 4, 0, 0));
+        }
+        if (wave == kNW - 1) {
+            const auto rb = make_rsrc(a.beta + tb * HV + hv, rows_bytes(t0, HV, 1, 4));
+            pf_b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (lane & (kC - 1)) * HV * 4, 0, 0));
         }
     };
 
-    // carry inputs: v of the wave's 16 columns, rows in accumulator order
-    // (row tile rt, rows 4*lg + r)
-    uint16_t pf_v[2][4];
-    auto load_v = [&](int ch) {
-        const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
-        const int vcol = v0 + 16 * wave + lr;
-        const int t0 = ch * kC;
-        const auto rv = make_rsrc(vg + ((tok_b + t0) * HV + hv) * V, rows_bytes(t0, v_stride, V, 2));
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                pf_v[rt][r] = __builtin_amdgcn_raw_buffer_load_b16(
-                    rv, ((rt * 16 + 4 * lg + r) * v_stride + vcol) * 2, 0, 0);
-    };
-
-    f32x4 m[KT];
-    if (carry) {
-        const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-        const int vcol = v0 + 16 * wave + lr;
-        const float *S0 = a.S0 ? a.S0 + (static_cast<size_t>(b) * HV + hv) * K * V : nullptr;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                m[kt][r] = S0 ? S0[static_cast<size_t>(kt * 16 + lg * 4 + r) * V + vcol] : 0.f;
-    }
-
-    // registers carried from the first to the second operand pass
-    float gl[RPG][2], qv[RPG][2], kv[RPG][2];
-
-    // ======================= operand pass 1: cumulative decay within row groups
+    // operand pass 1: cumulative sums of g (natural log units) within the row group
+    float gl[RPG][2];
+    uint32_t qw[RPG], kw[RPG];
     auto op1 = [&](int buf) {
-        const int tid = opaque_tid(), cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
+        const int lane = opaque_tid() & 63, cp = lane % CPW, rg = lane / CPW;
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
-            gl[r][0] = pf_g[r].x * kLog2e;
-            gl[r][1] = pf_g[r].y * kLog2e;
-            qv[r][0] = bf_lo(pf_q[r]);
-            qv[r][1] = bf_hi(pf_q[r]);
-            kv[r][0] = bf_lo(pf_k[r]);
-            kv[r][1] = bf_hi(pf_k[r]);
+            gl[r][0] = pf_g[r].x;
+            gl[r][1] = pf_g[r].y;
+            qw[r] = pf_q[r];
+            kw[r] = pf_k[r];
         }
 #pragma unroll
         for (int r = 1; r < RPG; ++r) {
             gl[r][0] += gl[r - 1][0];
             gl[r][1] += gl[r - 1][1];
         }
-        *reinterpret_cast<float2 *>(sGtot + rg * K + f0) = make_float2(gl[RPG - 1][0], gl[RPG - 1][1]);
-        if (cp == 0)
-#pragma unroll
-            for (int r = 0; r < RPG; ++r) sBeta[buf * kC + rg * RPG + r] = pf_b[r];
+        *reinterpret_cast<float2 *>(sGx + (ow * NRG + rg) * 2 * CPW + 2 * cp) =
+            make_float2(gl[RPG - 1][0], gl[RPG - 1][1]);
+        if (wave == kNW - 1 && lane < kC) sBeta[buf * kC + lane] = pf_b;
     };
 
-    // ======================= operand pass 2: exponentials and MFMA operands
+    // operand pass 2: exponentials (base 2) and MFMA operands of one chunk
     auto op2 = [&](int buf) {
-        const int tid = opaque_tid(), cp = tid % CP, rg = tid / CP, f0 = 2 * cp;
+        const int lane = opaque_tid() & 63, cp = lane % CPW, rg = lane / CPW;
+        const int f0 = ow * 2 * CPW + 2 * cp;
+        wave_lds_sync();
+        const float *gx = sGx + ow * NRG * 2 * CPW + 2 * cp;
         float off[2] = {0.f, 0.f}, Gr[2] = {0.f, 0.f}, Gl[2] = {0.f, 0.f};
 #pragma unroll
         for (int g2 = 0; g2 < NRG; ++g2) {
-            const float2 t = *reinterpret_cast<const float2 *>(sGtot + g2 * K + f0);
+            const float2 t = *reinterpret_cast<const float2 *>(gx + g2 * 2 * CPW);
             if (g2 < rg) { off[0] += t.x; off[1] += t.y; }
             if (g2 * RPG <= kRef) { Gr[0] += t.x; Gr[1] += t.y; }
             Gl[0] += t.x;
             Gl[1] += t.y;
         }
-        float pr[2], pl[2];
+        float pr[2], pl[2], og2[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            pr[c] = ex2(Gr[c]);             // 2^{G_r}         >= 2^-116
-            pl[c] = ex2(Gl[c] - Gr[c]);     // 2^{G_last - G_r} in [2^-116, 1]
+            pr[c] = ex2(Gr[c] * kLog2e);              // 2^{G_r}         >= 2^-116
+            pl[c] = ex2((Gl[c] - Gr[c]) * kLog2e);    // 2^{G_last - G_r} in [2^-116, 1]
+            og2[c] = (off[c] - Gr[c]) * kLog2e;
         }
         if (rg == 0)
-            *reinterpret_cast<float2 *>(sGam + buf * K + f0) = make_float2(ex2(Gl[0]), ex2(Gl[1]));
-        __bf16 kbT[2][RPG], kbTl[2][RPG];
-        __bf16 *kgr = sKGr + buf * kC * LDK;
+            *reinterpret_cast<float2 *>(sGam + buf * K + f0) =
+                make_float2(ex2(Gl[0] * kLog2e), ex2(Gl[1] * kLog2e));
+        uint32_t kbh[2][RPG / 2], kbl[2][RPG / 2];
+        float kbp[2] = {0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
             const int i = rg * RPG + r;
-            bf16x2 lk, lqh, lql, rh, rl, qh, ql, kgm;
+            const float qf[2] = {bf_lo(qw[r]), bf_hi(qw[r])};
+            const float kf[2] = {bf_lo(kw[r]), bf_hi(kw[r])};
+            float xlk[2], xlq[2], xr[2], xqh[2], xkg[2], xkb[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const float d = off[c] + gl[r][c] - Gr[c];
+                const float d = __builtin_fmaf(gl[r][c], kLog2e, og2[c]);   // G_i - G_r
                 const float e1 = ex2(d), e2 = ex2(-d);
-                const float xlk = kv[r][c] * e1, xlq = qv[r][c] * e1, xr = kv[r][c] * e2;
-                const float xqh = xlq * pr[c];   // q 2^{G_i}
-                const float xkb = xr * pl[c];    // k 2^{G_last - G_i}
-                lk[c] = bf(xlk);
-                lqh[c] = bf(xlq);
-                lql[c] = bf(xlq - fl(lqh[c]));
-                rh[c] = bf(xr);
-                rl[c] = bf(xr - fl(rh[c]));
-                qh[c] = bf(xqh);
-                ql[c] = bf(xqh - fl(qh[c]));
-                kgm[c] = bf(xlk * pr[c]);        // k 2^{G_i}
-                kbT[c][r] = bf(xkb);
-                kbTl[c][r] = bf(xkb - fl(kbT[c][r]));
+                xlk[c] = kf[c] * e1;
+                xlq[c] = qf[c] * e1;
+                xr[c] = kf[c] * e2;
+                xqh[c] = xlq[c] * pr[c];       // q 2^{G_i}
+                xkg[c] = xlk[c] * pr[c];       // k 2^{G_i}
+                xkb[c] = xr[c] * pl[c];        // k 2^{G_last - G_i}
             }
-            *reinterpret_cast<bf16x2 *>(sLk + i * LDK + f0) = lk;
-            *reinterpret_cast<bf16x2 *>(sLq + i * LDK + f0) = lqh;
-            *reinterpret_cast<bf16x2 *>(sLq + kC * LDK + i * LDK + f0) = lql;
-            *reinterpret_cast<bf16x2 *>(sR + i * LDK + f0) = rh;
-            *reinterpret_cast<bf16x2 *>(sR + kC * LDK + i * LDK + f0) = rl;
-            *reinterpret_cast<bf16x2 *>(sQh + i * LDK + f0) = qh;
-            *reinterpret_cast<bf16x2 *>(sQh + kC * LDK + i * LDK + f0) = ql;
-            *reinterpret_cast<bf16x2 *>(kgr + i * LDK + f0) = kgm;
+            uint32_t hi, lo;
+            const int at = sw(i, perm(f0));
+            st_word(sLk + at, pk(xlk[0], xlk[1]));
+            split2(xlq[0], xlq[1], hi, lo);
+            st_word(sLq + at, hi);
+            st_word(sLq + kC * LDK + at, lo);
+            split2(xr[0], xr[1], hi, lo);
+            st_word(sR + at, hi);
+            st_word(sR + kC * LDK + at, lo);
+            split2(xqh[0], xqh[1], hi, lo);
+            st_word(sQh + at, hi);
+            st_word(sQh + kC * LDK + at, lo);
+            st_word(sKGr + at, pk(xkg[0], xkg[1]));
+            if (r & 1) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) split2(kbp[c], xkb[c], kbh[c][r / 2], kbl[c][r / 2]);
+            } else {
+                kbp[0] = xkb[0];
+                kbp[1] = xkb[1];
+            }
         }
         __bf16 *kb_buf = sKbarT + buf * 2 * K * LDC;
+        // runs of four tokens stay contiguous under the permutation
+        constexpr int RUN = RPG < 4 ? RPG : 4;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            store_rows<RPG>(kb_buf + (f0 + c) * LDC + rg * RPG, kbT[c]);
-            store_rows<RPG>(kb_buf + K * LDC + (f0 + c) * LDC + rg * RPG, kbTl[c]);
-        }
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int q = 0; q < RPG / RUN; ++q) {
+                const int at = (f0 + c) * LDC + perm(rg * RPG + q * RUN);
+                uint32_t wh[RUN / 2], wl[RUN / 2];
+#pragma unroll
+                for (int w = 0; w < RUN / 2; ++w) {
+                    wh[w] = kbh[c][q * RUN / 2 + w];
+                    wl[w] = kbl[c][q * RUN / 2 + w];
+                }
+                st_words<RUN / 2>(kb_buf + at, wh);
+                st_words<RUN / 2>(kb_buf + K * LDC + at, wl);
+            }
     };
 
-    // ======================= A_qk (3-term split) and A_kk on MFMA
-    auto phaseA = [&](int buf) {
+    // ======================= waves 4..7: A_qk (3-term), -A21, T11, T22
+    // A_qk tile (rt, ct): independent accumulators for the three terms
+    auto aqk_tile = [&](int rt, int ct) {
         const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
-        const int rt = (wave % 3) == 0 ? 0 : 1;
-        const int ct = (wave % 3) == 2 ? 1 : 0;
-        __bf16 *aq = sAqk + buf * 2 * kC * LDC;
-        if (wave < 3) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 hh = {0.f, 0.f, 0.f, 0.f}, hl = hh, lh = hh;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int kk = ks * 32 + lg * 8;
-                const bf16x8 ah = ld8(sLq + (rt * 16 + lr) * LDK + kk);
-                const bf16x8 al = ld8(sLq + kC * LDK + (rt * 16 + lr) * LDK + kk);
-                const bf16x8 bh = ld8(sR + (ct * 16 + lr) * LDK + kk);
-                const bf16x8 bl = ld8(sR + kC * LDK + (ct * 16 + lr) * LDK + kk);
-                acc = mfma(ah, bh, acc);
-                acc = mfma(ah, bl, acc);
-                acc = mfma(al, bh, acc);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            const int kk = ks * 32 + lg * 8;
+            const int pa = sw(rt * 16 + lr, kk), pb = sw(ct * 16 + lr, kk);
+            const bf16x8 ah = ld8(sLq + pa);
+            const bf16x8 al = ld8(sLq + kC * LDK + pa);
+            const bf16x8 bh = ld8(sR + pb);
+            const bf16x8 bl = ld8(sR + kC * LDK + pb);
+            hh = mfma(ah, bh, hh);
+            hl = mfma(ah, bl, hl);
+            lh = mfma(al, bh, lh);
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = rt * 16 + lg * 4 + r, j = ct * 16 + lr;
-                const float x = (j <= i) ? acc[r] : 0.f;
-                const __bf16 hi = bf(x);
-                aq[i * LDC + j] = hi;
-                aq[kC * LDC + i * LDC + j] = bf(x - fl(hi));
-            }
-        } else if (wave < 6) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int kk = ks * 32 + lg * 8;
-                acc = mfma(ld8(sLk + (rt * 16 + lr) * LDK + kk), ld8(sR + (ct * 16 + lr) * LDK + kk), acc);
-            }
-            __bf16 *a21 = sA21 + buf * 2 * 16 * L16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = rt * 16 + lg * 4 + r, j = ct * 16 + lr;
-                const float x = (j < i) ? sBeta[buf * kC + i] * acc[r] : 0.f;
-                sAkk[i * LDF + j] = x;
-                if (rt == 1 && ct == 0) {   // -A21, the off-diagonal block of the solve
-                    const __bf16 hi = bf(-x);
-                    a21[(lg * 4 + r) * L16 + lr] = hi;
-                    a21[16 * L16 + (lg * 4 + r) * L16 + lr] = bf(-x - fl(hi));
-                }
-            }
-        } else if (wave == 6) {
-            // the all-upper tile (rows 0-15, cols 16-31) of both matrices is zero
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = lg * 4 + r, j = 16 + lr;
-                sAkk[i * LDF + j] = 0.f;
-                aq[i * LDC + j] = bf(0.f);
-                aq[kC * LDC + i * LDC + j] = bf(0.f);
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int i = rt * 16 + lg * 4 + r, j = ct * 16 + lr;
+            const float x = (j <= i) ? (hh[r] + (hl[r] + lh[r])) : 0.f;
+            const __bf16 hi = bf(x);
+            sAqk[i * LDC + perm(j)] = hi;
+            sAqk[kC * LDC + i * LDC + perm(j)] = bf(x - fl(hi));
         }
     };
-
-    // ======================= T11, T22: inverses of the 16x16 diagonal blocks of
-    // I + A_kk, in fp32 on one wave (8x8 forward substitutions, one merge each)
-    auto phaseT = [&](int buf) {
-        const int lane = opaque_tid() & 63;
-        // (a) 8x8 diagonal blocks (lanes 0-31: block, column); lanes 32-63 clear
-        //     the upper 8x8 block of each 16x16 block.
-        if (lane < 32) {
-            const int d = lane >> 3, c = lane & 7, o = d * 8;
-            float x[8];
+    // raw A_kk tile (rt, ct) = (k e1)(k e2)^T with single bf16 operands (beta not applied)
+    auto akk_tile = [&](int rt, int ct) {
+        const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                float acc = (r == c) ? 1.f : 0.f;
-                if (r > 0) {
-                    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(sAkk + (o + r) * LDF + o);
-                    const f32x4 a1 = *reinterpret_cast<const f32x4 *>(sAkk + (o + r) * LDF + o + 4);
-                    const float ar[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-#pragma unroll
-                    for (int j = 0; j < r; ++j) acc -= ar[j] * x[j];
-                }
-                x[r] = (r < c) ? 0.f : acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 8; ++r) sTf[(o + r) * LDF + o + c] = x[r];
-        } else {
-            const int e = lane - 32;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int idx = e * 4 + qq, p = idx >> 6, w = idx & 63;
-                sTf[(p * 16 + (w >> 3)) * LDF + p * 16 + 8 + (w & 7)] = 0.f;
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            const int kk = ks * 32 + lg * 8;
+            const bf16x8 x = ld8(sLk + sw(rt * 16 + lr, kk)), y = ld8(sR + sw(ct * 16 + lr, kk));
+            if (ks & 1) acc1 = mfma(x, y, acc1);
+            else acc0 = mfma(x, y, acc0);
         }
-        wave_lds_sync();
-        // (b) merges: lower-left 8x8 block of each 16x16 block, -T22 (A21 T11)
-        {
-            const int p = lane >> 5, e = lane & 31, r = e >> 2, c0 = (e & 3) * 2, o = p * 16;
-            float x0 = 0.f, x1 = 0.f;
+        return acc0 + acc1;
+    };
+    auto phaseAT = [&](int buf) {
+        const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
+        const float *beta = sBeta + buf * kC;
+        if (wave == 4) {
+            // T_blk = (I + A_blk)^-1 for both diagonal blocks of A_kk, in fp32.
+            // A_blk^T goes to LDS; lane (blk = bit 4, c = low 4 bits) solves
+            // (I + A_blk) x = e_c column-wise: once x_j is final it is removed
+            // from every later row, so each step waits on one FMA only.
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float av = sAkk[(o + 8 + r) * LDF + o + j];
-                x0 += av * sTf[(o + j) * LDF + o + c0];
-                x1 += av * sTf[(o + j) * LDF + o + c0 + 1];
+            for (int blk = 0; blk < 2; ++blk) {
+                const f32x4 acc = akk_tile(blk, blk);
+                f32x4 at;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = lg * 4 + r;
+                    at[r] = (lr < i) ? beta[16 * blk + i] * acc[r] : 0.f;
+                }
+                // A^T[j = lr][i = 4 lg + r]
+                *reinterpret_cast<f32x4 *>(sTs + blk * 2 * 16 * LDT + lr * LDT + lg * 4) = at;
             }
-            sX[(o + r) * LDF + c0] = x0;
-            sX[(o + r) * LDF + c0 + 1] = x1;
             wave_lds_sync();
-            float y0 = 0.f, y1 = 0.f;
+            const int blk = (lane >> 4) & 1, c = lane & 15;
+            const float *sAT = sTs + blk * 2 * 16 * LDT;
+            float x[16];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float tv = sTf[(o + 8 + r) * LDF + o + 8 + j];
-                y0 += tv * sX[(o + j) * LDF + c0];
-                y1 += tv * sX[(o + j) * LDF + c0 + 1];
-            }
-            sTf[(o + 8 + r) * LDF + o + c0] = -y0;
-            sTf[(o + 8 + r) * LDF + o + c0 + 1] = -y1;
-        }
-        wave_lds_sync();
-        // (c) T11, T22 as split bf16: lane = (block, row, half row)
-        {
-            const int blk = lane >> 5, i = (lane & 31) >> 1, j0 = (lane & 1) * 8, o = blk * 16;
-            bf16x8 hi, lo;
+            for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const float x = sTf[(o + i) * LDF + o + j0 + jj];
-                hi[jj] = bf(x);
-                lo[jj] = bf(x - fl(hi[jj]));
+            for (int j = 0; j < 15; ++j) {
+#pragma unroll
+                for (int q4 = (j + 1) / 4; q4 < 4; ++q4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4 *>(sAT + j * LDT + 4 * q4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * q4 + e > j) x[4 * q4 + e] -= av[e] * x[j];
+                }
             }
-            __bf16 *dst = sTi + ((buf * 2 + blk) * 2) * 16 * L16 + i * L16 + j0;
-            *reinterpret_cast<bf16x8 *>(dst) = hi;
-            *reinterpret_cast<bf16x8 *>(dst + 16 * L16) = lo;
+            float *sT = sTs + blk * 2 * 16 * LDT + 16 * LDT;
+            if (lane < 32)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sT[r * LDT + c] = x[r];
+            wave_lds_sync();
+            // split bf16 rows: lane = (blk, row i, half row)
+            const int ob = lane >> 5, i = (lane >> 1) & 15, j0 = (lane & 1) * 8;
+            const float *src = sTs + ob * 2 * 16 * LDT + 16 * LDT + i * LDT + j0;
+            bf16x4 h0, l0, h1, l1;
+            split4(*reinterpret_cast<const f32x4 *>(src), h0, l0);
+            split4(*reinterpret_cast<const f32x4 *>(src + 4), h1, l1);
+            __bf16 *dst = sTi + ob * 2 * 16 * L16 + i * L16 + j0;
+            *reinterpret_cast<bf16x8 *>(dst) = cat(h0, h1);
+            *reinterpret_cast<bf16x8 *>(dst + 16 * L16) = cat(l0, l1);
+        } else if (wave == 5) {
+            aqk_tile(0, 0);
+        } else if (wave == 6) {
+            aqk_tile(1, 1);
+        } else if (wave == 7) {
+            aqk_tile(1, 0);
+            // -A21: the off-diagonal block of the solve (rows 16-31, columns 0-15)
+            const f32x4 acc = akk_tile(1, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = lg * 4 + r;
+                const float x = -beta[16 + i] * acc[r];
+                const __bf16 hi = bf(x);
+                sA21[i * L16 + lr] = hi;
+                sA21[16 * L16 + i * L16 + lr] = bf(x - fl(hi));
+            }
         }
     };
 
-    // ======================= carry: state products, solve, output, state update
-    f32x4 pq[2];
-    bf16x8 mh[KS];
-    auto carryP = [&]() {   // P = (q Gamma) M, three terms (M split)
+    // ======================= carry waves
+    // v of the wave's column blocks, rows in accumulator order (row tile rt, rows 4*lg + r)
+    uint16_t pf_v[NG][2][4];
+    auto load_v = [&](int ch) {
         const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
-        bf16x8 ml[KS];
+        const int t0 = ch * kC;
+        const auto rv = make_rsrc(vg + ((tok_b + t0) * HV + hv) * V, rows_bytes(t0, v_stride, V, 2));
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            bf16x4 h0, l0, h1, l1;
-            split4(m[2 * s], h0, l0);
-            split4(m[2 * s + 1], h1, l1);
-            mh[s] = cat(h0, h1);
-            ml[s] = cat(l0, l1);
+        for (int gi = 0; gi < NG; ++gi) {
+            const int vcol = v0 + 16 * (wave * NG + gi) + lr;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    pf_v[gi][rt][r] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rv, ((rt * 16 + 4 * lg + r) * v_stride + vcol) * 2, 0, 0);
         }
+    };
+
+    f32x4 m[NG][KT];
+    f32x4 pq[NG][2], xq[NG][2];
+    // P = (q Gamma) M (three terms, M split) and X = (k Gamma) M of the next chunk
+    auto carryPX = [&]() {
+        const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
+        bf16x8 mh[NG][KS], ml[NG][KS];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            f32x4 p = {0.f, 0.f, 0.f, 0.f};
-            const int base = (rt * 16 + lr) * LDK + lg * 4;
+        for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const bf16x8 qf = ld4x2(sQh + base + s * 32);
-                const bf16x8 qfl = ld4x2(sQh + kC * LDK + base + s * 32);
-                p = mfma(qf, mh[s], p);
-                p = mfma(qf, ml[s], p);
-                p = mfma(qfl, mh[s], p);
+                bf16x4 h0, l0, h1, l1;
+                split4(m[gi][2 * s], h0, l0);
+                split4(m[gi][2 * s + 1], h1, l1);
+                mh[gi][s] = cat(h0, h1);
+                ml[gi][s] = cat(l0, l1);
             }
-            pq[rt] = p;
+        f32x4 phh[NG][2], phl[NG][2], plh[NG][2], x[NG][2];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                phh[gi][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                phl[gi][rt] = phh[gi][rt];
+                plh[gi][rt] = phh[gi][rt];
+                x[gi][rt] = phh[gi][rt];
+            }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            bf16x8 qf[2], qfl[2], kf[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int p0 = sw(rt * 16 + lr, s * 32 + lg * 8);
+                qf[rt] = ld8(sQh + p0);
+                qfl[rt] = ld8(sQh + kC * LDK + p0);
+                kf[rt] = ld8(sKGr + p0);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    phh[gi][rt] = mfma(qf[rt], mh[gi][s], phh[gi][rt]);
+                    x[gi][rt] = mfma(kf[rt], mh[gi][s], x[gi][rt]);
+                    phl[gi][rt] = mfma(qf[rt], ml[gi][s], phl[gi][rt]);
+                    plh[gi][rt] = mfma(qfl[rt], mh[gi][s], plh[gi][rt]);
+                }
         }
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                pq[gi][rt] = phh[gi][rt] + (phl[gi][rt] + plh[gi][rt]);
+                xq[gi][rt] = x[gi][rt];
+            }
     };
 
-    auto carryRest = [&](int buf, int t0) {
+    // R, solve, output and state update of chunk n
+    auto carryMain = [&](int n) {
         const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
-        const int vcol = v0 + 16 * wave + lr;
-        // R = diag(beta) (v - (k Gamma) M), accumulator layout per 16-row tile
-        const __bf16 *kgr = sKGr + buf * kC * LDK;
-        const float *beta = sBeta + buf * kC;
-        f32x4 rr[2];
+        const int cbuf = n & 1, t0 = n * kC;
+        // operand fragments that do not depend on this chunk's products
+        const __bf16 *t11 = sTi + lr * L16 + lg * 4;
+        const __bf16 *t22 = sTi + 2 * 16 * L16 + lr * L16 + lg * 4;
+        const __bf16 *a21 = sA21 + lr * L16 + lg * 4;
+        const bf16x4 t11h = ld4(t11), t11l = ld4(t11 + 16 * L16);
+        const bf16x4 t22h = ld4(t22), t22l = ld4(t22 + 16 * L16);
+        const bf16x4 a21h = ld4(a21), a21l = ld4(a21 + 16 * L16);
+        bf16x8 aqh[2], aql[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            const int base = (rt * 16 + lr) * LDK + lg * 4;
+            const int off = (rt * 16 + lr) * LDC + lg * 8;
+            aqh[rt] = ld8(sAqk + off);
+            aql[rt] = ld8(sAqk + kC * LDC + off);
+        }
+        // R = diag(beta) (v - (k Gamma) M), accumulator layout per 16-row tile
+        const float *beta = sBeta + cbuf * kC;
+        f32x4 rr[NG][2];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) x = mfma(ld4x2(kgr + base + s * 32), mh[s], x);
+        for (int rt = 0; rt < 2; ++rt) {
             const f32x4 bt = *reinterpret_cast<const f32x4 *>(beta + rt * 16 + lg * 4);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float vv = __uint_as_float(static_cast<uint32_t>(pf_v[rt][r]) << 16);
-                rr[rt][r] = bt[r] * (vv - x[r]);
-            }
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float vv = __uint_as_float(static_cast<uint32_t>(pf_v[gi][rt][r]) << 16);
+                    rr[gi][rt][r] = bt[r] * (vv - xq[gi][rt][r]);
+                }
         }
+        load_v(n + 1);
         // U1 = T11 R1;  Y = R2 - A21 U1;  U2 = T22 Y   (16x16x16 MFMAs, 3 terms each)
-        const __bf16 *t11 = sTi + (buf * 2 + 0) * 2 * 16 * L16 + lr * L16 + lg * 4;
-        const __bf16 *t22 = sTi + (buf * 2 + 1) * 2 * 16 * L16 + lr * L16 + lg * 4;
-        const __bf16 *a21 = sA21 + buf * 2 * 16 * L16 + lr * L16 + lg * 4;
-        f32x4 u[2];
-        bf16x4 xh, xl, uh0, ul0;
-        split4(rr[0], xh, xl);
-        {
-            const bf16x4 th = ld4(t11), tl = ld4(t11 + 16 * L16);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma16(th, xh, acc);
-            acc = mfma16(th, xl, acc);
-            acc = mfma16(tl, xh, acc);
-            u[0] = acc;
+        bf16x4 uh0[NG], ul0[NG], uh1[NG], ul1[NG];
+        f32x4 acc[NG], acc2[NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            bf16x4 xh, xl;
+            split4(rr[gi][0], xh, xl);
+            acc[gi] = mfma16(t11h, xh, f32x4{0.f, 0.f, 0.f, 0.f});
+            acc2[gi] = mfma16(t11h, xl, f32x4{0.f, 0.f, 0.f, 0.f});
+            acc2[gi] = mfma16(t11l, xh, acc2[gi]);
         }
-        split4(u[0], uh0, ul0);
-        {
-            const bf16x4 ah = ld4(a21), al = ld4(a21 + 16 * L16);
-            f32x4 y = rr[1];
-            y = mfma16(ah, uh0, y);
-            y = mfma16(ah, ul0, y);
-            y = mfma16(al, uh0, y);
-            split4(y, xh, xl);
-            const bf16x4 th = ld4(t22), tl = ld4(t22 + 16 * L16);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma16(th, xh, acc);
-            acc = mfma16(th, xl, acc);
-            acc = mfma16(tl, xh, acc);
-            u[1] = acc;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            split4(acc[gi] + acc2[gi], uh0[gi], ul0[gi]);
+            acc[gi] = mfma16(a21h, uh0[gi], rr[gi][1]);
+            acc2[gi] = mfma16(a21h, ul0[gi], f32x4{0.f, 0.f, 0.f, 0.f});
+            acc2[gi] = mfma16(a21l, uh0[gi], acc2[gi]);
         }
-        bf16x4 uh1, ul1;
-        split4(u[1], uh1, ul1);
-        const bf16x8 ub_hi = cat(uh0, uh1), ub_lo = cat(ul0, ul1);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            bf16x4 xh, xl;
+            split4(acc[gi] + acc2[gi], xh, xl);
+            acc[gi] = mfma16(t22h, xh, f32x4{0.f, 0.f, 0.f, 0.f});
+            acc2[gi] = mfma16(t22h, xl, f32x4{0.f, 0.f, 0.f, 0.f});
+            acc2[gi] = mfma16(t22l, xh, acc2[gi]);
+        }
+        bf16x8 ubh[NG], ubl[NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            split4(acc[gi] + acc2[gi], uh1[gi], ul1[gi]);
+            ubh[gi] = cat(uh0[gi], uh1[gi]);
+            ubl[gi] = cat(ul0[gi], ul1[gi]);
+        }
 
         // O = scale (P + A_qk U) -> HBM
-        const __bf16 *aq = sAqk + buf * 2 * kC * LDC;
         const auto ro = make_rsrc(og + ((tok_b + t0) * HV + hv) * V, rows_bytes(t0, v_stride, V, 2));
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int off = (rt * 16 + lr) * LDC + lg * 4;
-            const bf16x8 ah = ld4x2(aq + off), al = ld4x2(aq + kC * LDC + off);
-            f32x4 o = pq[rt];
-            o = mfma(ah, ub_hi, o);
-            o = mfma(ah, ub_lo, o);
-            o = mfma(al, ub_hi, o);
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = rt * 16 + lg * 4 + r;
-                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, bf(o[r] * a.scale)), ro,
-                                                      (i * v_stride + vcol) * 2, 0, 0);
+            for (int gi = 0; gi < NG; ++gi) {
+                const int vcol = v0 + 16 * (wave * NG + gi) + lr;
+                f32x4 o = mfma(aqh[rt], ubh[gi], pq[gi][rt]);
+                f32x4 o2 = mfma(aqh[rt], ubl[gi], f32x4{0.f, 0.f, 0.f, 0.f});
+                o2 = mfma(aql[rt], ubh[gi], o2);
+                o += o2;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = rt * 16 + lg * 4 + r;
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, bf(o[r] * a.scale)), ro,
+                                                          (i * v_stride + vcol) * 2, 0, 0);
+                }
             }
-        }
-        // M <- Gamma_last (.) M + k_bar^T U
-        const __bf16 *kb_buf = sKbarT + buf * 2 * K * LDC + lr * LDC + lg * 4;
-        const float *gam = sGam + buf * K + lg * 4;
+        // M <- Gamma_last (.) M + k_bar^T U, four row tiles at a time: the three
+        // terms of each tile go to separate accumulators
+        const __bf16 *kb_buf = sKbarT + cbuf * 2 * K * LDC + lr * LDC + lg * 8;
+        const float *gam = sGam + cbuf * K + lg * 4;
+        constexpr int KB = KT < 4 ? KT : 4;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            const f32x4 gm = *reinterpret_cast<const f32x4 *>(gam + kt * 16);
-            const bf16x8 kf = ld4x2(kb_buf + kt * 16 * LDC);
-            const bf16x8 kfl = ld4x2(kb_buf + K * LDC + kt * 16 * LDC);
-            f32x4 x = m[kt] * gm;
-            x = mfma(kf, ub_hi, x);
-            x = mfma(kf, ub_lo, x);
-            x = mfma(kfl, ub_hi, x);
-            m[kt] = x;
+        for (int k0 = 0; k0 < KT; k0 += KB) {
+            bf16x8 kf[KB], kfl[KB];
+            f32x4 gm[KB];
+#pragma unroll
+            for (int u = 0; u < KB; ++u) {
+                kf[u] = ld8(kb_buf + (k0 + u) * 16 * LDC);
+                kfl[u] = ld8(kb_buf + K * LDC + (k0 + u) * 16 * LDC);
+                gm[u] = *reinterpret_cast<const f32x4 *>(gam + (k0 + u) * 16);
+            }
+            f32x4 t2[NG][KB];
+#pragma unroll
+            for (int u = 0; u < KB; ++u)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    m[gi][k0 + u] = mfma(kf[u], ubh[gi], m[gi][k0 + u] * gm[u]);
+                    t2[gi][u] = mfma(kf[u], ubl[gi], f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+#pragma unroll
+            for (int u = 0; u < KB; ++u)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    t2[gi][u] = mfma(kfl[u], ubh[gi], t2[gi][u]);
+                    m[gi][k0 + u] += t2[gi][u];
+                }
         }
     };
 
     // ---------------------------------------------------------------- prologue: chunk 0
-    load_prep(0);
-    op1(0);
+    if (carry) {
+        const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+        if (a.S0) {
+            const float *S0 = a.S0 + (static_cast<size_t>(b) * HV + hv) * K * V;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const int vcol = v0 + 16 * (wave * NG + gi) + lr;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        m[gi][kt][r] = S0[static_cast<size_t>(kt * 16 + lg * 4 + r) * V + vcol];
+            }
+        } else {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) m[gi][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        load_v(0);
+        if (wave == 0) {
+            // rows 0-15 x columns 16-31 of A_qk lie above the diagonal: zero for every chunk
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = lg * 4 + r, j = perm(16 + lr);
+                sAqk[i * LDC + j] = bf(0.f);
+                sAqk[kC * LDC + i * LDC + j] = bf(0.f);
+            }
+        }
+    }
+    if (opw) {
+        load_prep(0);
+        op1(0);
+        load_prep(1);
+        op2(0);
+    }
     lds_barrier();
-    op2(0);
-    if (NC > 1) load_prep(1);
-    lds_barrier();
-    phaseA(0);
-    lds_barrier();
-    if (wave == kTWave) phaseT(0);
-    if (carry) load_v(0);
+    if (wave >= 4) phaseAT(0);
+    if (carry) carryPX();
     lds_barrier();
 
     // ---------------------------------------------------------------- main loop
-    for (int n = 0; n < NC; ++n) {
-        const bool next = n + 1 < NC;
-        const int cur = n & 1, nxt = cur ^ 1;
-        // A: P of chunk n reads (q Gamma) before the operand pass overwrites it
-        if (carry) carryP();
-        if (next) op1(nxt);
-        lds_barrier();
-        // B
-        if (next) op2(nxt);
-        lds_barrier();
-        // C
-        if (next) {
-            phaseA(nxt);
-            if (n + 2 < NC) load_prep(n + 2);
+    for (int n = 0; n + 1 < NC; ++n) {
+        const int nb = (n + 1) & 1;
+        // P1
+        if (opw) {
+            op1(nb);
+            load_prep(n + 2);
         }
+        if (carry) carryMain(n);
+        if (opw) op2(nb);
         lds_barrier();
-        // D
-        if (next && wave == kTWave) phaseT(nxt);
-        if (carry) {
-            carryRest(cur, n * kC);
-            if (next) load_v(n + 1);
-        }
+        // P2
+        if (wave >= 4) phaseAT(nb);
+        if (carry) carryPX();
         lds_barrier();
     }
+    if (carry) carryMain(NC - 1);
 
     if (a.ST && carry) {
         const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-        const int vcol = v0 + 16 * wave + lr;
         float *ST = a.ST + (static_cast<size_t>(b) * HV + hv) * K * V;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+        for (int gi = 0; gi < NG; ++gi) {
+            const int vcol = v0 + 16 * (wave * NG + gi) + lr;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                ST[static_cast<size_t>(kt * 16 + lg * 4 + r) * V + vcol] = m[kt][r];
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    ST[static_cast<size_t>(kt * 16 + lg * 4 + r) * V + vcol] = m[gi][kt][r];
+        }
     }
 }
 
