@@ -269,7 +269,7 @@ def main():
                    "V": shape.V, "chunk": 32, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "prefill_kernel<128,64,bf16>",
+                     "kernel": "prefill_bf16_kernel<128,64>",
                      "alg_bytes_per_launch": p["bytes"], "avg_launch_ms": p["avg_ms"]},
         "mfma": {"alg_flops_per_launch": p["flops"],
                  "achieved_tflops": p["flops"] / (p["avg_ms"] * 1e-3) / 1e12,

@@ -211,8 +211,16 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
 
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int nvt = a.V / VT;
-    const int vt_idx = blockIdx.x % nvt;
-    const int bhv = blockIdx.x / nvt;
+    // Workgroups are handed to the 8 XCDs round-robin (block i -> XCD i % 8),
+    // each with its own L2.  Give every XCD a contiguous range of the logical
+    // order (b, q/k head, value head, V tile), so the V tiles of one value head
+    // (same q, k, g) and the value heads of one q/k head (same q, k) run on one
+    // XCD at about the same time and share its L2.
+    const int nblk = static_cast<int>(gridDim.x);
+    const int blk = (nblk & 7) == 0 ? (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3)
+                                    : static_cast<int>(blockIdx.x);
+    const int vt_idx = blk % nvt;
+    const int bhv = blk / nvt;
     const int b = bhv / a.HV, hv = bhv % a.HV;
     const int h = hv / (a.HV / a.H);
     const int v0 = vt_idx * VT;
