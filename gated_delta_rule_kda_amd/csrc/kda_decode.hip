@@ -27,6 +27,17 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxConv = 8;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// The state is streamed: each 16-byte segment is read once and written once
+// per step, so both go through the non-temporal path and do not displace
+// reusable lines (conv weights, dt_bias) from the caches.
+__device__ __forceinline__ float4 ld_stream(const float4 *p) {
+    return __builtin_bit_cast(float4, __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p)));
+}
+__device__ __forceinline__ void st_stream(float4 *p, const float4 &x) {
+    __builtin_nontemporal_store(__builtin_bit_cast(f32x4, x), reinterpret_cast<f32x4 *>(p));
+}
+
 __device__ __forceinline__ float load_io(const void *p, size_t i, bool bf16) {
     return bf16 ? bf16_bits_to_float(static_cast<const uint16_t *>(p)[i])
                 : static_cast<const float *>(p)[i];
@@ -48,6 +59,15 @@ __device__ __forceinline__ float channel_value(const DecodeArgs &a, int b, int c
     const int KW = a.conv_kernel;
     float *st = a.conv_state + (static_cast<size_t>(b) * C + c) * KW;
     const float *w = a.conv_w + static_cast<size_t>(c) * KW;
+    if (KW == 4) {
+        // the common width: one 16-byte load and store of the channel's register
+        const float4 o = *reinterpret_cast<const float4 *>(st);
+        const float4 wv = *reinterpret_cast<const float4 *>(w);
+        const float4 n = make_float4(o.y, o.z, o.w, x);
+        *reinterpret_cast<float4 *>(st) = n;
+        const float acc = fmaf(wv.w, n.w, fmaf(wv.z, n.z, fmaf(wv.y, n.y, wv.x * n.x)));
+        return acc * sigmoid_acc(acc);
+    }
     float reg[kMaxConv];
 #pragma unroll
     for (int j = 0; j < kMaxConv; ++j)
@@ -93,6 +113,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int c4 = tid % TPR;
     const int r0 = tid / TPR;
 
+    // The state of the first value head streams in while the prologue runs.
+    float4 st[NP];
+    {
+        const float4 *S0 = reinterpret_cast<const float4 *>(
+            a.state + (static_cast<size_t>(b) * a.HV + h * G) * K * V);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) st[p] = ld_stream(&S0[(p * RPP + r0) * TPR + c4]);
+    }
+
     // ---- q/k channels of head h (conv + SiLU when enabled)
     for (int i = tid; i < 2 * K; i += kThreads) {
         const int c = (i < K) ? h * K + i : a.H * K + h * K + (i - K);
@@ -131,10 +160,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const size_t bhv = static_cast<size_t>(b) * a.HV + hv;
         float4 *S = reinterpret_cast<float4 *>(a.state + bhv * K * V);
 
-        // Issue the state loads first; the prologue below hides their latency.
-        float4 st[NP];
+        // Later value heads issue their state loads first; the value channels
+        // and the gate below hide part of the latency.
+        if (gi > 0)
 #pragma unroll
-        for (int p = 0; p < NP; ++p) st[p] = S[(p * RPP + r0) * TPR + c4];
+            for (int p = 0; p < NP; ++p) st[p] = ld_stream(&S[(p * RPP + r0) * TPR + c4]);
 
         for (int j = tid; j < V; j += kThreads)
             s_v[j] = channel_value(a, b, 2 * a.H * K + hv * V + j, C);
@@ -206,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             n.y = fmaf(kr, u4[1], e * st[p].y);
             n.z = fmaf(kr, u4[2], e * st[p].z);
             n.w = fmaf(kr, u4[3], e * st[p].w);
-            S[(p * RPP + r0) * TPR + c4] = n;
+            st_stream(&S[(p * RPP + r0) * TPR + c4], n);
         }
         __syncthreads();  // s_v / s_eg / s_u are reused by the next value head
     }
