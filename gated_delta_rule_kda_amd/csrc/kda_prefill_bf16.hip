@@ -738,13 +738,20 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     // ---------------------------------------------------------------- main loop
     for (int n = 0; n + 1 < NC; ++n) {
         const int nb = (n + 1) & 1;
-        // P1
-        if (opw) {
+        // P1 (carry waves get their carry work and their share of the operand
+        // pass in one block, so the scheduler can fill MFMA latency with VALU)
+        if (carry) {
+            if (opw) {
+                op1(nb);
+                load_prep(n + 2);
+            }
+            carryMain(n);
+            if (opw) op2(nb);
+        } else if (opw) {
             op1(nb);
             load_prep(n + 2);
+            op2(nb);
         }
-        if (carry) carryMain(n);
-        if (opw) op2(nb);
         lds_barrier();
         // P2
         if (wave >= 4) phaseAT(nb);
