@@ -16,15 +16,18 @@
 //
 // Layout: each thread owns one float4 column group (4 consecutive V columns)
 // of K / RPP state rows, so a wave's loads and stores cover whole 16-byte
-// segments of consecutive rows.  Handling all G value heads of a q/k head in
-// one workgroup means the q/k conv channels are shifted exactly once.
+// segments of consecutive rows.  At K = V = 128 a workgroup has 512 threads
+// holding 8 float4 each: smaller per-thread footprints keep more workgroups
+// resident, which streams the read-modify-write of the state faster than
+// fewer, fatter threads.  Handling all G value heads of a q/k head in one
+// workgroup means the q/k conv channels are shifted exactly once.
 
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kMaxThreads = 512;   // threads per workgroup for the largest state tiles
 constexpr int kMaxConv = 8;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -83,7 +86,9 @@ __device__ __forceinline__ float channel_value(const DecodeArgs &a, int b, int c
     return acc * sigmoid_acc(acc);
 }
 
-// Sum over the 256 threads; every thread gets the result.  `red` holds 4 floats.
+// Sum over the workgroup of NW waves; every thread gets the result (fixed
+// order, so the result is reproducible).  `red` holds NW floats.
+template <int NW>
 __device__ __forceinline__ float block_sum(float x, float *red) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
@@ -91,19 +96,29 @@ __device__ __forceinline__ float block_sum(float x, float *red) {
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[wave] = x;
     __syncthreads();
-    return (red[0] + red[1]) + (red[2] + red[3]);
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += red[w];
+    return t;
 }
 
+// Threads of a workgroup: one float4 column group of at least 4 state rows each,
+// capped at kMaxThreads.
 template <int K, int V>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+constexpr int decode_threads() { return K * V / 16 < kMaxThreads ? K * V / 16 : kMaxThreads; }
+
+template <int K, int V>
+__global__ __launch_bounds__((decode_threads<K, V>())) void decode_kernel(DecodeArgs a) {
+    constexpr int kThreads = decode_threads<K, V>();
+    constexpr int kWaves = kThreads / 64;
     constexpr int TPR = V / 4;          // threads per state row (one float4 each)
     constexpr int RPP = kThreads / TPR; // state rows per pass of the workgroup
     constexpr int NP = K / RPP;         // passes; each thread holds NP float4
     static_assert(K % RPP == 0, "state rows must tile the workgroup");
 
     __shared__ float s_q[K], s_k[K], s_v[V], s_eg[K], s_u[V];
-    __shared__ float s_red[4][2][V];
-    __shared__ float s_tmp[4];
+    __shared__ float s_red[kWaves][2][V];
+    __shared__ float s_tmp[kWaves];
 
     const int tid = threadIdx.x;
     const int b = blockIdx.x / a.H;
@@ -139,8 +154,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         }
         float inv_q = 1.f, inv_k = 1.f;
         if (a.l2norm) {
-            sq = block_sum(sq, s_tmp);
-            sk = block_sum(sk, s_tmp);
+            sq = block_sum<kWaves>(sq, s_tmp);
+            sk = block_sum<kWaves>(sk, s_tmp);
             inv_q = 1.0f / sqrtf(sq + a.l2_eps);
             inv_k = 1.0f / sqrtf(sk + a.l2_eps);
         }
@@ -152,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             s_k[f] = kn;
             d += qn * kn;
         }
-        qk = block_sum(d, s_tmp);
+        qk = block_sum<kWaves>(d, s_tmp);
     }
 
     for (int gi = 0; gi < G; ++gi) {
@@ -217,8 +232,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             }
         __syncthreads();
         for (int j = tid; j < V; j += kThreads) {
-            const float pkv = (s_red[0][0][j] + s_red[1][0][j]) + (s_red[2][0][j] + s_red[3][0][j]);
-            const float pqv = (s_red[0][1][j] + s_red[1][1][j]) + (s_red[2][1][j] + s_red[3][1][j]);
+            float pkv = 0.f, pqv = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                pkv += s_red[w][0][j];
+                pqv += s_red[w][1][j];
+            }
             const float u = beta * (s_v[j] - pkv);
             s_u[j] = u;
             store_io(a.out, bhv * V + j, fmaf(qk, u, pqv), a.bf16);
@@ -244,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
 template <int K, int V>
 hipError_t launch_kv(const DecodeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_kernel<K, V>), dim3(a.B * a.H), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<K, V>), dim3(a.B * a.H), dim3(decode_threads<K, V>()), 0, stream, a);
     return hipGetLastError();
 }
 
