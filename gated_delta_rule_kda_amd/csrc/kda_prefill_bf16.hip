@@ -95,23 +95,40 @@ __device__ __forceinline__ bf16x4 ld4(const __bf16 *p) { return *reinterpret_cas
 __device__ __forceinline__ bf16x8 cat(const bf16x4 &a, const bf16x4 &b) {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        hi[r] = bf(x[r]);
-        lo[r] = bf(x[r] - fl(hi[r]));
-    }
-}
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 // (a, b) -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pk(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
-// hi = bf16(a, b), lo = bf16(a - hi_a, b - hi_b): six instructions per pair
+// A 32-bit constant the compiler cannot see through, kept in an SGPR.  The bf16
+// pairs below go to v_dot2c_f32_bf16 this way: as an inline constant the pair
+// (-1, 0) is encoded as the fp32 constant -1.0, whose bits the instruction reads
+// as the pair (0, -1).
+__device__ __forceinline__ bf16x2 sgpr_pair(uint32_t bits) {
+    asm("" : "+s"(bits));
+    return __builtin_bit_cast(bf16x2, bits);
+}
+// a - (low bf16 of w), b - (high bf16 of w) in one v_dot2c_f32_bf16 each: the
+// products with -1 and 0 are exact and the difference of a and its own bf16
+// rounding is representable, so the result is exact.
+__device__ __forceinline__ float minus_lo(uint32_t w, float a) {
+    return __builtin_amdgcn_fdot2_f32_bf16(sgpr_pair(0x0000bf80u), __builtin_bit_cast(bf16x2, w), a, false);
+}
+__device__ __forceinline__ float minus_hi(uint32_t w, float b) {
+    return __builtin_amdgcn_fdot2_f32_bf16(sgpr_pair(0xbf800000u), __builtin_bit_cast(bf16x2, w), b, false);
+}
+// hi = bf16(a, b), lo = bf16(a - hi_a, b - hi_b): four instructions per pair
 __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
     hi = pk(a, b);
-    lo = pk(a - bf_lo(hi), b - bf_hi(hi));
+    lo = pk(minus_lo(hi, a), minus_hi(hi, b));
+}
+__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
+    uint32_t h[2], l[2];
+    split2(x[0], x[1], h[0], l[0]);
+    split2(x[2], x[3], h[1], l[1]);
+    hi = __builtin_bit_cast(bf16x4, h);
+    lo = __builtin_bit_cast(bf16x4, l);
 }
 __device__ __forceinline__ void st_word(__bf16 *p, uint32_t w) { *reinterpret_cast<uint32_t *>(p) = w; }
 // NW consecutive packed words as one LDS store (NW in {1, 2, 4})
@@ -425,6 +442,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
         const float *beta = sBeta + buf * kC;
         if (wave == 4) {
+            // the inverses are the longest path of this phase: this wave's
+            // LDS and VALU instructions go ahead of the others' while it runs
+            __builtin_amdgcn_s_setprio(3);
             // T_blk = (I + A_blk)^-1 for both diagonal blocks of A_kk, in fp32.
             // A_blk^T goes to LDS; lane (blk = bit 4, c = low 4 bits) solves
             // (I + A_blk) x = e_c column-wise: once x_j is final it is removed
@@ -471,6 +491,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             __bf16 *dst = sTi + ob * 2 * 16 * L16 + i * L16 + j0;
             *reinterpret_cast<bf16x8 *>(dst) = cat(h0, h1);
             *reinterpret_cast<bf16x8 *>(dst + 16 * L16) = cat(l0, l1);
+            __builtin_amdgcn_s_setprio(0);
         } else if (wave == 5) {
             aqk_tile(0, 0);
         } else if (wave == 6) {
