@@ -131,6 +131,10 @@ __device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
     lo = __builtin_bit_cast(bf16x4, l);
 }
 __device__ __forceinline__ void st_word(__bf16 *p, uint32_t w) { *reinterpret_cast<uint32_t *>(p) = w; }
+// x of lane `src` (0..63) of the wave (ds_bpermute)
+__device__ __forceinline__ float lane_value(int src, float x) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
 // NW consecutive packed words as one LDS store (NW in {1, 2, 4})
 template <int NW>
 __device__ __forceinline__ void st_words(__bf16 *p, const uint32_t (&w)[NW]) {
@@ -183,8 +187,7 @@ struct Plan {
     static constexpr int oGam = oTi + 4 * 16 * L16 * 2;          // fp32 [2 buf][K]  Gamma_last
     static constexpr int oPr = oGam + 2 * K * 4;                 // fp32 [K]  2^{G_r}
     static constexpr int oBeta = oPr + K * 4;                    // fp32 [2 buf][C]
-    static constexpr int oGx = oBeta + 2 * kC * 4;               // fp32 [NOW][NRG][2 CPW]  row-group sums
-    static constexpr int oTs = oGx + NOW * NRG * 2 * CPW * 4;    // fp32 [2 blk][2][16][LDT]  A^T, T
+    static constexpr int oTs = oBeta + 2 * kC * 4;               // fp32 [2 blk][2][16][LDT]  A^T, T
     static constexpr int bytes = oTs + 4 * 16 * LDT * 4;
 };
 
@@ -225,7 +228,6 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     float *sGam = reinterpret_cast<float *>(smem + L::oGam);
     float *sPr = reinterpret_cast<float *>(smem + L::oPr);
     float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
-    float *sGx = reinterpret_cast<float *>(smem + L::oGx);
     float *sTs = reinterpret_cast<float *>(smem + L::oTs);
 
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -314,8 +316,6 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             gl[r][0] += gl[r - 1][0];
             gl[r][1] += gl[r - 1][1];
         }
-        *reinterpret_cast<float2 *>(sGx + (ow * NRG + rg) * 2 * CPW + 2 * cp) =
-            make_float2(gl[RPG - 1][0], gl[RPG - 1][1]);
         if (wave == kNW - 1 && lane < kC) sBeta[buf * kC + lane] = pf_b;
     };
 
@@ -323,16 +323,26 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     auto op2 = [&](int buf) {
         const int lane = opaque_tid() & 63, cp = lane % CPW, rg = lane / CPW;
         const int f0 = ow * 2 * CPW + 2 * cp;
-        wave_lds_sync();
-        const float *gx = sGx + ow * NRG * 2 * CPW + 2 * cp;
-        float off[2] = {0.f, 0.f}, Gr[2] = {0.f, 0.f}, Gl[2] = {0.f, 0.f};
+        // inclusive scan of the row-group sums across the lanes of one column pair
+        // (lanes cp, cp + CPW, ..): log2(NRG) steps of ds_bpermute; then the sums
+        // through the reference row and through the last row from the groups
+        // that end them
+        float sc[2] = {gl[RPG - 1][0], gl[RPG - 1][1]};
 #pragma unroll
-        for (int g2 = 0; g2 < NRG; ++g2) {
-            const float2 t = *reinterpret_cast<const float2 *>(gx + g2 * 2 * CPW);
-            if (g2 < rg) { off[0] += t.x; off[1] += t.y; }
-            if (g2 * RPG <= kRef) { Gr[0] += t.x; Gr[1] += t.y; }
-            Gl[0] += t.x;
-            Gl[1] += t.y;
+        for (int st = 1; st < NRG; st <<= 1) {
+            const int src = (lane - st * CPW) & 63;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const float y = lane_value(src, sc[c]);
+                sc[c] += rg >= st ? y : 0.f;
+            }
+        }
+        float off[2], Gr[2], Gl[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            Gr[c] = lane_value((kRef / RPG) * CPW + cp, sc[c]);
+            Gl[c] = lane_value((NRG - 1) * CPW + cp, sc[c]);
+            off[c] = sc[c] - gl[RPG - 1][c];    // rows before the group
         }
         float pr[2], pl[2], og2[2];
 #pragma unroll
@@ -342,8 +352,8 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             og2[c] = (off[c] - Gr[c]) * kLog2e;
         }
         if (rg == 0) {
-            *reinterpret_cast<float2 *>(sGam + buf * K + f0) =
-                make_float2(ex2(Gl[0] * kLog2e), ex2(Gl[1] * kLog2e));
+            // Gamma_last = 2^{G_r} 2^{G_last - G_r}
+            *reinterpret_cast<float2 *>(sGam + buf * K + f0) = make_float2(pr[0] * pl[0], pr[1] * pl[1]);
             *reinterpret_cast<float2 *>(sPr + f0) = make_float2(pr[0], pr[1]);
         }
         uint32_t kbh[2][RPG / 2], kbl[2][RPG / 2];
