@@ -451,16 +451,16 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     auto phaseAT = [&](int buf) {
         const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
         const float *beta = sBeta + buf * kC;
-        if (wave == 4) {
+        if (wave == 4 || wave == 5) {
             // the inverses are the longest path of this phase: this wave's
             // LDS and VALU instructions go ahead of the others' while it runs
             __builtin_amdgcn_s_setprio(3);
-            // T_blk = (I + A_blk)^-1 for both diagonal blocks of A_kk, in fp32.
-            // A_blk^T goes to LDS; lane (blk = bit 4, c = low 4 bits) solves
-            // (I + A_blk) x = e_c column-wise: once x_j is final it is removed
-            // from every later row, so each step waits on one FMA only.
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
+            // T_blk = (I + A_blk)^-1 for diagonal block blk = wave - 4 of A_kk, in
+            // fp32.  A_blk^T goes to LDS; lane c < 16 solves (I + A_blk) x = e_c
+            // column-wise: once x_j is final it is removed from every later row,
+            // so each step waits on one FMA only.
+            const int blk = wave - 4;
+            {
                 const f32x4 acc = akk_tile(blk, blk);
                 f32x4 at;
 #pragma unroll
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 *reinterpret_cast<f32x4 *>(sTs + blk * 2 * 16 * LDT + lr * LDT + lg * 4) = at;
             }
             wave_lds_sync();
-            const int blk = (lane >> 4) & 1, c = lane & 15;
+            const int c = lane & 15;
             const float *sAT = sTs + blk * 2 * 16 * LDT;
             float x[16];
 #pragma unroll
@@ -488,23 +488,24 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 }
             }
             float *sT = sTs + blk * 2 * 16 * LDT + 16 * LDT;
-            if (lane < 32)
+            if (lane < 16)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sT[r * LDT + c] = x[r];
             wave_lds_sync();
-            // split bf16 rows: lane = (blk, row i, half row)
-            const int ob = lane >> 5, i = (lane >> 1) & 15, j0 = (lane & 1) * 8;
-            const float *src = sTs + ob * 2 * 16 * LDT + 16 * LDT + i * LDT + j0;
-            bf16x4 h0, l0, h1, l1;
-            split4(*reinterpret_cast<const f32x4 *>(src), h0, l0);
-            split4(*reinterpret_cast<const f32x4 *>(src + 4), h1, l1);
-            __bf16 *dst = sTi + ob * 2 * 16 * L16 + i * L16 + j0;
-            *reinterpret_cast<bf16x8 *>(dst) = cat(h0, h1);
-            *reinterpret_cast<bf16x8 *>(dst + 16 * L16) = cat(l0, l1);
+            // split bf16 rows: lane = (row i, half row)
+            if (lane < 32) {
+                const int i = lane >> 1, j0 = (lane & 1) * 8;
+                const float *src = sT + i * LDT + j0;
+                bf16x4 h0, l0, h1, l1;
+                split4(*reinterpret_cast<const f32x4 *>(src), h0, l0);
+                split4(*reinterpret_cast<const f32x4 *>(src + 4), h1, l1);
+                __bf16 *dst = sTi + blk * 2 * 16 * L16 + i * L16 + j0;
+                *reinterpret_cast<bf16x8 *>(dst) = cat(h0, h1);
+                *reinterpret_cast<bf16x8 *>(dst + 16 * L16) = cat(l0, l1);
+            }
             __builtin_amdgcn_s_setprio(0);
-        } else if (wave == 5) {
-            aqk_tile(0, 0);
         } else if (wave == 6) {
+            aqk_tile(0, 0);
             aqk_tile(1, 1);
         } else if (wave == 7) {
             aqk_tile(1, 0);
