@@ -187,8 +187,8 @@ struct Plan {
     static constexpr int oGam = oTi + 4 * 16 * L16 * 2;          // fp32 [2 buf][K]  Gamma_last
     static constexpr int oPr = oGam + 2 * K * 4;                 // fp32 [K]  2^{G_r}
     static constexpr int oBeta = oPr + K * 4;                    // fp32 [2 buf][C]
-    static constexpr int oTs = oBeta + 2 * kC * 4;               // fp32 [2 blk][2][16][LDT]  A^T, T
-    static constexpr int bytes = oTs + 4 * 16 * LDT * 4;
+    static constexpr int oTs = oBeta + 2 * kC * 4;               // fp32 [2 blk][16][LDT]  A_blk
+    static constexpr int bytes = oTs + 2 * 16 * LDT * 4;
 };
 
 template <int K, int VT>
@@ -299,11 +299,16 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         }
     };
 
-    // operand pass 1: cumulative sums of g (natural log units) within the row group
+    // operand pass 1: cumulative sums of g (natural log units) within the row
+    // group, then across the row groups, and the chunk's exponent offsets.  This
+    // runs before the prefetch and the carry work of the phase, whose issue
+    // covers the latency of the cross-lane steps.
     float gl[RPG][2];
     uint32_t qw[RPG], kw[RPG];
+    float pl[2], og2[2];
     auto op1 = [&](int buf) {
         const int lane = opaque_tid() & 63, cp = lane % CPW, rg = lane / CPW;
+        const int f0 = ow * 2 * CPW + 2 * cp;
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
             gl[r][0] = pf_g[r].x;
@@ -317,12 +322,6 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             gl[r][1] += gl[r - 1][1];
         }
         if (wave == kNW - 1 && lane < kC) sBeta[buf * kC + lane] = pf_b;
-    };
-
-    // operand pass 2: exponentials (base 2) and MFMA operands of one chunk
-    auto op2 = [&](int buf) {
-        const int lane = opaque_tid() & 63, cp = lane % CPW, rg = lane / CPW;
-        const int f0 = ow * 2 * CPW + 2 * cp;
         // inclusive scan of the row-group sums across the lanes of one column pair
         // (lanes cp, cp + CPW, ..): log2(NRG) steps of ds_bpermute; then the sums
         // through the reference row and through the last row from the groups
@@ -337,25 +336,27 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 sc[c] += rg >= st ? y : 0.f;
             }
         }
-        float off[2], Gr[2], Gl[2];
+        float pr[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            Gr[c] = lane_value((kRef / RPG) * CPW + cp, sc[c]);
-            Gl[c] = lane_value((NRG - 1) * CPW + cp, sc[c]);
-            off[c] = sc[c] - gl[RPG - 1][c];    // rows before the group
-        }
-        float pr[2], pl[2], og2[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            pr[c] = ex2(Gr[c] * kLog2e);              // 2^{G_r}         >= 2^-116
-            pl[c] = ex2((Gl[c] - Gr[c]) * kLog2e);    // 2^{G_last - G_r} in [2^-116, 1]
-            og2[c] = (off[c] - Gr[c]) * kLog2e;
+            const float Gr = lane_value((kRef / RPG) * CPW + cp, sc[c]);
+            const float Gl = lane_value((NRG - 1) * CPW + cp, sc[c]);
+            const float off = sc[c] - gl[RPG - 1][c];    // rows before the group
+            pr[c] = ex2(Gr * kLog2e);              // 2^{G_r}         >= 2^-116
+            pl[c] = ex2((Gl - Gr) * kLog2e);       // 2^{G_last - G_r} in [2^-116, 1]
+            og2[c] = (off - Gr) * kLog2e;
         }
         if (rg == 0) {
             // Gamma_last = 2^{G_r} 2^{G_last - G_r}
             *reinterpret_cast<float2 *>(sGam + buf * K + f0) = make_float2(pr[0] * pl[0], pr[1] * pl[1]);
             *reinterpret_cast<float2 *>(sPr + f0) = make_float2(pr[0], pr[1]);
         }
+    };
+
+    // operand pass 2: exponentials (base 2) and MFMA operands of one chunk
+    auto op2 = [&](int buf) {
+        const int lane = opaque_tid() & 63, cp = lane % CPW, rg = lane / CPW;
+        const int f0 = ow * 2 * CPW + 2 * cp;
         uint32_t kbh[2][RPG / 2], kbl[2][RPG / 2];
         float kbp[2] = {0.f, 0.f};
 #pragma unroll
@@ -456,52 +457,44 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             // LDS and VALU instructions go ahead of the others' while it runs
             __builtin_amdgcn_s_setprio(3);
             // T_blk = (I + A_blk)^-1 for diagonal block blk = wave - 4 of A_kk, in
-            // fp32.  A_blk^T goes to LDS; lane c < 16 solves (I + A_blk) x = e_c
-            // column-wise: once x_j is final it is removed from every later row,
-            // so each step waits on one FMA only.
+            // fp32.  A_blk goes to LDS row-major; lane i < 16 finds row i of T from
+            // x^T (I + A_blk) = e_i^T, sweeping k = 15 .. 1: once x_k is final it is
+            // removed from every earlier column (one FMA per step on the chain),
+            // and the finished row is split and stored as it stands.
             const int blk = wave - 4;
+            float *sA = sTs + blk * 16 * LDT;
             {
                 const f32x4 acc = akk_tile(blk, blk);
-                f32x4 at;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = lg * 4 + r;
-                    at[r] = (lr < i) ? beta[16 * blk + i] * acc[r] : 0.f;
+                    sA[i * LDT + lr] = (lr < i) ? beta[16 * blk + i] * acc[r] : 0.f;
                 }
-                // A^T[j = lr][i = 4 lg + r]
-                *reinterpret_cast<f32x4 *>(sTs + blk * 2 * 16 * LDT + lr * LDT + lg * 4) = at;
             }
             wave_lds_sync();
-            const int c = lane & 15;
-            const float *sAT = sTs + blk * 2 * 16 * LDT;
+            const int i = lane & 15;
             float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) x[r] = (r == i) ? 1.f : 0.f;
 #pragma unroll
-            for (int j = 0; j < 15; ++j) {
+            for (int k = 15; k >= 1; --k) {
 #pragma unroll
-                for (int q4 = (j + 1) / 4; q4 < 4; ++q4) {
-                    const f32x4 av = *reinterpret_cast<const f32x4 *>(sAT + j * LDT + 4 * q4);
+                for (int q4 = 0; 4 * q4 < k; ++q4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4 *>(sA + k * LDT + 4 * q4);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (4 * q4 + e > j) x[4 * q4 + e] -= av[e] * x[j];
+                        if (4 * q4 + e < k) x[4 * q4 + e] -= av[e] * x[k];
                 }
             }
-            float *sT = sTs + blk * 2 * 16 * LDT + 16 * LDT;
-            if (lane < 16)
+            if (lane < 16) {
+                uint32_t hw[8], lw[8];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sT[r * LDT + c] = x[r];
-            wave_lds_sync();
-            // split bf16 rows: lane = (row i, half row)
-            if (lane < 32) {
-                const int i = lane >> 1, j0 = (lane & 1) * 8;
-                const float *src = sT + i * LDT + j0;
-                bf16x4 h0, l0, h1, l1;
-                split4(*reinterpret_cast<const f32x4 *>(src), h0, l0);
-                split4(*reinterpret_cast<const f32x4 *>(src + 4), h1, l1);
-                __bf16 *dst = sTi + blk * 2 * 16 * L16 + i * L16 + j0;
-                *reinterpret_cast<bf16x8 *>(dst) = cat(h0, h1);
-                *reinterpret_cast<bf16x8 *>(dst + 16 * L16) = cat(l0, l1);
+                for (int p2 = 0; p2 < 8; ++p2) split2(x[2 * p2], x[2 * p2 + 1], hw[p2], lw[p2]);
+                __bf16 *dst = sTi + blk * 2 * 16 * L16 + i * L16;
+                *reinterpret_cast<uint4 *>(dst) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                *reinterpret_cast<uint4 *>(dst + 8) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+                *reinterpret_cast<uint4 *>(dst + 16 * L16) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+                *reinterpret_cast<uint4 *>(dst + 16 * L16 + 8) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
             }
             __builtin_amdgcn_s_setprio(0);
         } else if (wave == 6) {
