@@ -557,15 +557,12 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 ml[gi][s] = cat(l0, l1);
             }
         }
-        f32x4 phh[NG][2], phl[NG][2], plh[NG][2], x[NG][2];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                phh[gi][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                phl[gi][rt] = phh[gi][rt];
-                plh[gi][rt] = phh[gi][rt];
-                x[gi][rt] = phh[gi][rt];
+                pq[gi][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                xq[gi][rt] = pq[gi][rt];
             }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -577,23 +574,24 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 qfl[rt] = ld8(sLq + kC * LDK + p0);
                 kf[rt] = ld8(sLk + p0);
             }
+            // the three terms of P accumulate in place (accumulator forwarding
+            // between MFMAs of one shape); independent products sit between them
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
-                    phh[gi][rt] = mfma(qf[rt], mh[gi][s], phh[gi][rt]);
-                    x[gi][rt] = mfma(kf[rt], mh[gi][s], x[gi][rt]);
-                    phl[gi][rt] = mfma(qf[rt], ml[gi][s], phl[gi][rt]);
-                    plh[gi][rt] = mfma(qfl[rt], mh[gi][s], plh[gi][rt]);
+                    pq[gi][rt] = mfma(qf[rt], mh[gi][s], pq[gi][rt]);
+                    xq[gi][rt] = mfma(kf[rt], mh[gi][s], xq[gi][rt]);
                 }
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) pq[gi][rt] = mfma(qf[rt], ml[gi][s], pq[gi][rt]);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) pq[gi][rt] = mfma(qfl[rt], mh[gi][s], pq[gi][rt]);
         }
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi)
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                pq[gi][rt] = phh[gi][rt] + (phl[gi][rt] + plh[gi][rt]);
-                xq[gi][rt] = x[gi][rt];
-            }
     };
 
     // R, solve and output of chunk n (U stays in registers for the state update)
@@ -664,26 +662,35 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
 
         // O = scale (P + A_qk U) -> HBM
         const auto ro = make_rsrc(og + ((tok_b + t0) * HV + hv) * V, rows_bytes(t0, v_stride, V, 2));
+        f32x4 o[2][NG];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) o[rt][gi] = mfma(aqh[rt], ubh[gi], pq[gi][rt]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) o[rt][gi] = mfma(aqh[rt], ubl[gi], o[rt][gi]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) o[rt][gi] = mfma(aql[rt], ubh[gi], o[rt][gi]);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const int vcol = v0 + 16 * (wave * NG + gi) + lr;
-                f32x4 o = mfma(aqh[rt], ubh[gi], pq[gi][rt]);
-                f32x4 o2 = mfma(aqh[rt], ubl[gi], f32x4{0.f, 0.f, 0.f, 0.f});
-                o2 = mfma(aql[rt], ubh[gi], o2);
-                o += o2;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = rt * 16 + lg * 4 + r;
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, bf(o[r] * a.scale)), ro,
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, bf(o[rt][gi][r] * a.scale)), ro,
                                                           (i * v_stride + vcol) * 2, 0, 0);
                 }
             }
     };
 
-    // M <- Gamma_last (.) M + k_bar^T U of chunk n, four row tiles at a time:
-    // the three terms of each tile go to separate accumulators
+    // M <- Gamma_last (.) M + k_bar^T U of chunk n, four row tiles at a time;
+    // the three terms accumulate into M in turn, the tiles of a batch between them
     auto carryUpdate = [&](int n) {
         const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
         const int cbuf = n & 1;
@@ -700,21 +707,18 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 kfl[u] = ld8(kb_buf + K * LDC + (k0 + u) * 16 * LDC);
                 gm[u] = *reinterpret_cast<const f32x4 *>(gam + (k0 + u) * 16);
             }
-            f32x4 t2[NG][KB];
 #pragma unroll
             for (int u = 0; u < KB; ++u)
 #pragma unroll
-                for (int gi = 0; gi < NG; ++gi) {
-                    m[gi][k0 + u] = mfma(kf[u], ubh[gi], m[gi][k0 + u] * gm[u]);
-                    t2[gi][u] = mfma(kf[u], ubl[gi], f32x4{0.f, 0.f, 0.f, 0.f});
-                }
+                for (int gi = 0; gi < NG; ++gi) m[gi][k0 + u] = mfma(kf[u], ubh[gi], m[gi][k0 + u] * gm[u]);
 #pragma unroll
             for (int u = 0; u < KB; ++u)
 #pragma unroll
-                for (int gi = 0; gi < NG; ++gi) {
-                    t2[gi][u] = mfma(kfl[u], ubh[gi], t2[gi][u]);
-                    m[gi][k0 + u] += t2[gi][u];
-                }
+                for (int gi = 0; gi < NG; ++gi) m[gi][k0 + u] = mfma(kf[u], ubl[gi], m[gi][k0 + u]);
+#pragma unroll
+            for (int u = 0; u < KB; ++u)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) m[gi][k0 + u] = mfma(kfl[u], ubh[gi], m[gi][k0 + u]);
         }
     };
 
