@@ -304,16 +304,13 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         }
     };
 
-    // operand pass 1: cumulative sums of g (natural log units) within the row
-    // group, then across the row groups, and the chunk's exponent offsets.  This
-    // runs before the prefetch and the carry work of the phase, whose issue
-    // covers the latency of the cross-lane steps.
+    // operand pass 1a: take the prefetched registers, so that the next prefetch
+    // can be issued into them before the cross-lane steps of pass 1b
     float gl[RPG][2];
     uint32_t qw[RPG], kw[RPG];
     float pl[2], og2[2];
-    auto op1 = [&](int buf) {
-        const int lane = opaque_tid() & 63, cp = lane % CPW, rg = lane / CPW;
-        const int f0 = ow * 2 * CPW + 2 * cp;
+    auto op1a = [&](int buf) {
+        const int lane = opaque_tid() & 63;
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
             gl[r][0] = pf_g[r].x;
@@ -321,12 +318,19 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             qw[r] = pf_q[r];
             kw[r] = pf_k[r];
         }
+        if (wave == kNW - 1 && lane < kC) sBeta[buf * kC + lane] = pf_b;
+    };
+    // operand pass 1b: cumulative sums of g (natural log units) within the row
+    // group, then across the row groups, and the chunk's exponent offsets; the
+    // prefetch and the carry work of the phase cover the cross-lane latency
+    auto op1b = [&](int buf) {
+        const int lane = opaque_tid() & 63, cp = lane % CPW, rg = lane / CPW;
+        const int f0 = ow * 2 * CPW + 2 * cp;
 #pragma unroll
         for (int r = 1; r < RPG; ++r) {
             gl[r][0] += gl[r - 1][0];
             gl[r][1] += gl[r - 1][1];
         }
-        if (wave == kNW - 1 && lane < kC) sBeta[buf * kC + lane] = pf_b;
         // inclusive scan of the row-group sums across the lanes of one column pair
         // (lanes cp, cp + CPW, ..): log2(NRG) steps of ds_bpermute; then the sums
         // through the reference row and through the last row from the groups
@@ -784,8 +788,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     }
     if (opw) {
         load_prep(0);
-        op1(0);
+        op1a(0);
         load_prep(1);
+        op1b(0);
         op2(0);
     }
     lds_barrier();
@@ -803,14 +808,16 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         // pass in one block, so the scheduler can fill MFMA latency with VALU)
         if (carry) {
             if (opw) {
-                op1(nb);
+                op1a(nb);
                 load_prep(n + 2);
+                op1b(nb);
             }
             carryMain(n);
             if (opw) op2(nb);
         } else if (opw) {
-            op1(nb);
+            op1a(nb);
             load_prep(n + 2);
+            op1b(nb);
             op2(nb);
         }
         lds_barrier();
