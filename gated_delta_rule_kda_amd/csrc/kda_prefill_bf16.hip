@@ -136,6 +136,17 @@ __device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
     lo = __builtin_bit_cast(bf16x4, l);
 }
 __device__ __forceinline__ void st_word(__bf16 *p, uint32_t w) { *reinterpret_cast<uint32_t *>(p) = w; }
+// x of lane p of the lane's group of four (DPP quad_perm broadcast; p must
+// fold to a constant)
+__device__ __forceinline__ float quad_bcast(float x, int p) {
+    const int v = __float_as_int(x);
+    switch (p) {
+    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x00, 0xf, 0xf, false));
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x55, 0xf, 0xf, false));
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xaa, 0xf, 0xf, false));
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xff, 0xf, 0xf, false));
+    }
+}
 // x of lane `src` (0..63) of the wave (ds_bpermute)
 __device__ __forceinline__ float lane_value(int src, float x) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
@@ -466,10 +477,12 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             // LDS and VALU instructions go ahead of the others' while it runs
             __builtin_amdgcn_s_setprio(3);
             // T_blk = (I + A_blk)^-1 for diagonal block blk = wave - 4 of A_kk, in
-            // fp32.  A_blk goes to LDS row-major; lane i < 16 finds row i of T from
-            // x^T (I + A_blk) = e_i^T, sweeping k = 15 .. 1: once x_k is final it is
-            // removed from every earlier column (one FMA per step on the chain),
-            // and the finished row is split and stored as it stands.
+            // fp32.  A_blk goes to LDS row-major; row i of T solves
+            // x^T (I + A_blk) = e_i^T, swept k = 15 .. 1: once x_k is final it is
+            // removed from every earlier column.  Lane = (row i, quarter q) holds
+            // x_{4q..4q+3}; x_k comes from its row's lane k / 4 by DPP, and the
+            // strictly lower A_blk (zero for j >= k) makes the update uniform.
+            // The finished quarter rows are split and stored as they stand.
             const int blk = wave - 4;
             float *sA = sTs + blk * 16 * LDT;
             {
@@ -481,30 +494,23 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 }
             }
             wave_lds_sync();
-            const int i = lane & 15;
-            float x[16];
+            const int i = lane >> 2, q = lane & 3;
+            float x[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == i) ? 1.f : 0.f;
+            for (int e = 0; e < 4; ++e) x[e] = (4 * q + e == i) ? 1.f : 0.f;
 #pragma unroll
             for (int k = 15; k >= 1; --k) {
+                const f32x4 av = *reinterpret_cast<const f32x4 *>(sA + k * LDT + 4 * q);
+                const float xk = quad_bcast(x[k % 4], k / 4);
 #pragma unroll
-                for (int q4 = 0; 4 * q4 < k; ++q4) {
-                    const f32x4 av = *reinterpret_cast<const f32x4 *>(sA + k * LDT + 4 * q4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * q4 + e < k) x[4 * q4 + e] -= av[e] * x[k];
-                }
+                for (int e = 0; e < 4; ++e) x[e] -= av[e] * xk;
             }
-            if (lane < 16) {
-                uint32_t hw[8], lw[8];
-#pragma unroll
-                for (int p2 = 0; p2 < 8; ++p2) split2(x[2 * p2], x[2 * p2 + 1], hw[p2], lw[p2]);
-                __bf16 *dst = sTi + blk * 2 * 16 * L16 + i * L16;
-                *reinterpret_cast<uint4 *>(dst) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-                *reinterpret_cast<uint4 *>(dst + 8) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-                *reinterpret_cast<uint4 *>(dst + 16 * L16) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-                *reinterpret_cast<uint4 *>(dst + 16 * L16 + 8) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-            }
+            uint32_t hw[2], lw[2];
+            split2(x[0], x[1], hw[0], lw[0]);
+            split2(x[2], x[3], hw[1], lw[1]);
+            __bf16 *dst = sTi + blk * 2 * 16 * L16 + i * L16 + 4 * q;
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(hw[0], hw[1]);
+            *reinterpret_cast<uint2 *>(dst + 16 * L16) = make_uint2(lw[0], lw[1]);
             __builtin_amdgcn_s_setprio(0);
         } else if (wave == 6) {
             aqk_tile(0, 0);
