@@ -136,6 +136,11 @@ __device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
     lo = __builtin_bit_cast(bf16x4, l);
 }
 __device__ __forceinline__ void st_word(__bf16 *p, uint32_t w) { *reinterpret_cast<uint32_t *>(p) = w; }
+// x of lane l - N within the lane's row of 16 (DPP row_shr:N), 0 for l % 16 < N
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, false));
+}
 // x of lane p of the lane's group of four (DPP quad_perm broadcast; p must
 // fold to a constant)
 __device__ __forceinline__ float quad_bcast(float x, int p) {
@@ -342,26 +347,26 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             gl[r][0] += gl[r - 1][0];
             gl[r][1] += gl[r - 1][1];
         }
-        // inclusive scan of the row-group sums across the lanes of one column pair
-        // (lanes cp, cp + CPW, ..): log2(NRG) steps of ds_bpermute; then the sums
-        // through the reference row and through the last row from the groups
-        // that end them
-        float sc[2] = {gl[RPG - 1][0], gl[RPG - 1][1]};
-#pragma unroll
-        for (int st = 1; st < NRG; st <<= 1) {
-            const int src = (lane - st * CPW) & 63;
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const float y = lane_value(src, sc[c]);
-                sc[c] += rg >= st ? y : 0.f;
-            }
-        }
+        // sums over the row groups of one column pair (lanes cp, cp + CPW, ..):
+        // an inclusive scan within each DPP row of 16 lanes (row_shr by CPW,
+        // 2 CPW, ..), then the four row totals in one round of ds_bpermute.
+        // Rows 0..15 of the chunk are the first two DPP rows.
+        const int drow = lane >> 4;
         float pr[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const float Gr = lane_value((kRef / RPG) * CPW + cp, sc[c]);
-            const float Gl = lane_value((NRG - 1) * CPW + cp, sc[c]);
-            const float off = sc[c] - gl[RPG - 1][c];    // rows before the group
+            float sc = gl[RPG - 1][c];
+            if constexpr (CPW <= 1) sc += row_shr<1>(sc);
+            if constexpr (CPW <= 2) sc += row_shr<2>(sc);
+            if constexpr (CPW <= 4) sc += row_shr<4>(sc);
+            if constexpr (CPW <= 8) sc += row_shr<8>(sc);
+            float rt[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rt[j] = lane_value(16 * j + 16 - CPW + cp, sc);
+            const float Gr = rt[0] + rt[1];
+            const float Gl = Gr + (rt[2] + rt[3]);
+            const float before = drow == 0 ? 0.f : drow == 1 ? rt[0] : drow == 2 ? Gr : Gr + rt[2];
+            const float off = before + (sc - gl[RPG - 1][c]);    // rows before the group
             pr[c] = ex2(Gr * kLog2e);              // 2^{G_r}         >= 2^-116
             pl[c] = ex2((Gl - Gr) * kLog2e);       // 2^{G_last - G_r} in [2^-116, 1]
             og2[c] = (off - Gr) * kLog2e;
