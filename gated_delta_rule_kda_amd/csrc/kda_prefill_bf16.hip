@@ -190,7 +190,7 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 
 template <int K>
 struct Plan {
-    static constexpr int LDK = K + 8;    // bf16 rows over K
+    static constexpr int LDK = K + 16;   // bf16 rows over K
     static constexpr int LDC = kC + 8;   // bf16 rows over C
     static constexpr int L16 = 16 + 8;   // bf16 rows of a 16x16 block
     static constexpr int LDT = 20;       // fp32 rows of a 16x16 block
@@ -227,16 +227,26 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                   "row groups must pair rows and align with the reference row");
 
     // [C][LDK] operand arrays: element (i, c) sits in 8-column group (c / 8) XOR
-    // (XS if i >= 16).  With the K + 8 row pitch this keeps both the operand
-    // pass's stores (64 lanes over 8..16 rows) and the MFMA fragment reads
-    // (16 consecutive rows) free of LDS bank conflicts.
-    constexpr int XS = K == 128 ? 2 : 1;
+    // (XS if i >= 16).  With the K + 16 row pitch the MFMA fragment reads (16
+    // consecutive rows x 4 groups) are free of LDS bank conflicts, and the
+    // operand pass's 32-bit stores -- whose 32-lane halves hold row groups of
+    // both 16-row halves of the chunk, see row_base -- conflict only pairwise,
+    // the least their column pattern allows (each measured on the device).
+    constexpr int XS = K >= 64 ? 4 : 2;
     auto sw = [](int i, int c) { return i * LDK + ((((c >> 3) ^ (((i >> 4) & 1) * XS)) << 3) | (c & 7)); };
     // Within every block of 32 reduction indices (K columns, or tokens of a
     // chunk) the operands are stored in the MFMA's permuted order: index
     // 16h + 4g + e goes to 8g + 4h + e, so lane group g's fragment (rows
     // {4g..4g+3} of two 16-row tiles) is 16 contiguous bytes, one LDS read.
     auto perm = [](int c) { return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3); };
+    // First row of operand-pass row group q: the groups' two top index bits are
+    // swapped, so that each 32-lane half of a wave (q < NRG / 2, q >= NRG / 2)
+    // holds groups from both 16-row halves of the chunk, while the two or four
+    // groups of one DPP row of 16 lanes stay consecutive rows.
+    auto row_base = [](int q) {
+        constexpr int hb = NRG / 2, nb = NRG / 4;
+        return RPG * ((q & ~(hb | nb)) | ((q & hb) ? nb : 0) | ((q & nb) ? hb : 0));
+    };
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __bf16 *sLk = reinterpret_cast<__bf16 *>(smem + L::oLk);
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         const auto rk = make_rsrc(kg + (tb * a.H + h) * K, rows_bytes(t0, qk_stride, K, 2));
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
-            const int i = rg * RPG + r;
+            const int i = row_base(rg) + r;
             const auto gg = __builtin_amdgcn_raw_buffer_load_b64(rgr, (i * g_stride + f0) * 4, 0, 0);
             pf_g[r] = make_float2(__uint_as_float(gg[0]), __uint_as_float(gg[1]));
             pf_q[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, (i * qk_stride + f0) * 2, 0, 0);
@@ -349,8 +359,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         }
         // sums over the row groups of one column pair (lanes cp, cp + CPW, ..):
         // an inclusive scan within each DPP row of 16 lanes (row_shr by CPW,
-        // 2 CPW, ..), then the four row totals in one round of ds_bpermute.
-        // Rows 0..15 of the chunk are the first two DPP rows.
+        // 2 CPW, ..; its row groups are consecutive rows), then the four row
+        // totals in one round of ds_bpermute.  In row order the DPP rows come
+        // 0, 2, 1, 3 (row_base); rows 0..15 of the chunk are DPP rows 0 and 2.
         const int drow = lane >> 4;
         float pr[2];
 #pragma unroll
@@ -363,9 +374,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             float rt[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) rt[j] = lane_value(16 * j + 16 - CPW + cp, sc);
-            const float Gr = rt[0] + rt[1];
-            const float Gl = Gr + (rt[2] + rt[3]);
-            const float before = drow == 0 ? 0.f : drow == 1 ? rt[0] : drow == 2 ? Gr : Gr + rt[2];
+            const float Gr = rt[0] + rt[2];
+            const float Gl = Gr + (rt[1] + rt[3]);
+            const float before = drow == 0 ? 0.f : drow == 2 ? rt[0] : drow == 1 ? Gr : Gr + rt[1];
             const float off = before + (sc - gl[RPG - 1][c]);    // rows before the group
             pr[c] = ex2(Gr * kLog2e);              // 2^{G_r}         >= 2^-116
             pl[c] = ex2((Gl - Gr) * kLog2e);       // 2^{G_last - G_r} in [2^-116, 1]
@@ -384,7 +395,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         uint32_t rh[RPG], rl[RPG];   // k e2 of the lane's rows, packed bf16 pairs (hi, lo)
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
-            const int i = rg * RPG + r;
+            const int i = row_base(rg) + r;
             const float qf[2] = {bf_lo(qw[r]), bf_hi(qw[r])};
             const float kf[2] = {bf_lo(kw[r]), bf_hi(kw[r])};
             float xlk[2], xlq[2], xr[2];
@@ -423,7 +434,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int q = 0; q < RPG / RUN; ++q) {
-                const int at = (f0 + c) * LDC + perm(rg * RPG + q * RUN);
+                const int at = (f0 + c) * LDC + perm(row_base(rg) + q * RUN);
                 uint32_t wh[RUN / 2], wl[RUN / 2];
 #pragma unroll
                 for (int w = 0; w < RUN / 2; ++w) {
