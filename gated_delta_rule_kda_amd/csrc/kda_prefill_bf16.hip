@@ -191,7 +191,7 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 template <int K>
 struct Plan {
     static constexpr int LDK = K + 16;   // bf16 rows over K
-    static constexpr int LDC = kC + 8;   // bf16 rows over C
+    static constexpr int LDC = kC + 16;  // bf16 rows over C
     static constexpr int L16 = 16 + 8;   // bf16 rows of a 16x16 block
     static constexpr int LDT = 20;       // fp32 rows of a 16x16 block
     static constexpr int CPW = K / 16 > 4 ? K / 16 : 4;   // column pairs per operand wave
@@ -239,6 +239,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     // 16h + 4g + e goes to 8g + 4h + e, so lane group g's fragment (rows
     // {4g..4g+3} of two 16-row tiles) is 16 contiguous bytes, one LDS read.
     auto perm = [](int c) { return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3); };
+    // (k e2)^T [K][LDC]: token position p of row kr sits in 8-token group
+    // (p / 8) XOR ((kr / 4) % 4); with the C + 16 pitch the update's fragment
+    // reads (16 rows x 4 groups) are then free of bank conflicts (measured).
+    auto kb_at = [](int kr, int p) { return kr * LDC + ((((p >> 3) ^ ((kr >> 2) & 3)) << 3) | (p & 7)); };
     // First row of operand-pass row group q: the groups' two top index bits are
     // swapped, so that each 32-lane half of a wave (q < NRG / 2, q >= NRG / 2)
     // holds groups from both 16-row halves of the chunk, while the two or four
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int q = 0; q < RPG / RUN; ++q) {
-                const int at = (f0 + c) * LDC + perm(row_base(rg) + q * RUN);
+                const int at = kb_at(f0 + c, perm(row_base(rg) + q * RUN));
                 uint32_t wh[RUN / 2], wl[RUN / 2];
 #pragma unroll
                 for (int w = 0; w < RUN / 2; ++w) {
@@ -730,7 +734,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     auto carryUpdate = [&](int n, bool last) {
         const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
         const int cbuf = n & 1;
-        const __bf16 *kb_buf = sKbarT + cbuf * 2 * K * LDC + lr * LDC + lg * 8;
+        const __bf16 *kb_buf = sKbarT + cbuf * 2 * K * LDC + kb_at(lr, lg * 8);
         const float *plp = sPl + cbuf * K + lg * 4;
         const float *prp = sPr + lg * 4;
         constexpr int KB = KT < 4 ? KT : 4;
