@@ -83,6 +83,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -209,13 +210,16 @@ struct Plan {
     static constexpr int oPr = oPl + 2 * K * 4;                  // fp32 [K]  2^{G_r}
     static constexpr int oBeta = oPr + K * 4;                    // fp32 [2 buf][C]
     static constexpr int oTs = oBeta + 2 * kC * 4;               // fp32 [2 blk][16][LDT]  A_blk
-    static constexpr int bytes = oTs + 2 * 16 * LDT * 4;
+    static constexpr int oStage = oTs + 2 * 16 * LDT * 4;        // bf16 [C][VT + 8]  o of the chunk
+    static constexpr int bytes = oStage;                         // plus stage_bytes(VT)
+    static constexpr int stage_bytes(int VT) { return kC * (VT + 8) * 2; }
 };
 
 template <int K, int VT>
 __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     using L = Plan<K>;
-    static_assert(L::bytes <= 160 * 1024, "LDS plan exceeds 160 KB");
+    static_assert(L::bytes + L::stage_bytes(VT) <= 160 * 1024, "LDS plan exceeds 160 KB");
+    constexpr int LDO = VT + 8;   // bf16 rows of the o staging tile
     constexpr int LDK = L::LDK, LDC = L::LDC, L16 = L::L16, LDT = L::LDT;
     constexpr int CPW = L::CPW, NOW = L::NOW, NRG = L::NRG, RPG = L::RPG;
     constexpr int KT = K / 16, KS = K / 32;
@@ -264,6 +268,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     float *sPr = reinterpret_cast<float *>(smem + L::oPr);
     float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
     float *sTs = reinterpret_cast<float *>(smem + L::oTs);
+    __bf16 *sO = reinterpret_cast<__bf16 *>(smem + L::oStage);
 
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int nvt = a.V / VT;
@@ -693,8 +698,8 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             ubl[gi] = cat(ul0[gi], ul1[gi]);
         }
 
-        // O = scale (P + A_qk U) -> HBM
-        const auto ro = make_rsrc(og + ((tok_b + t0) * HV + hv) * V, rows_bytes(t0, v_stride, V, 2));
+        // O = scale (P + A_qk U) -> the LDS staging tile (row-major); waves 4..7
+        // store it to HBM in whole rows in the next phase
         f32x4 o[2][NG];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -712,14 +717,29 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
-                const int vcol = v0 + 16 * (wave * NG + gi) + lr;
+                const int col = 16 * (wave * NG + gi) + lr;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = rt * 16 + lg * 4 + r;
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, bf(o[rt][gi][r] * a.scale)), ro,
-                                                          (i * v_stride + vcol) * 2, 0, 0);
-                }
+                for (int r = 0; r < 4; ++r) sO[(rt * 16 + lg * 4 + r) * LDO + col] = bf(o[rt][gi][r] * a.scale);
             }
+    };
+
+    // o of chunk n from the staging tile to HBM, 16 bytes per lane and whole
+    // rows of the V tile per lane group (waves 4..7, a quarter of the rows each)
+    auto storeO = [&](int n) {
+        const int lane = opaque_tid() & 63;
+        const int t0 = n * kC;
+        const auto ro = make_rsrc(og + ((tok_b + t0) * HV + hv) * V + v0, rows_bytes(t0, v_stride, VT, 2));
+        constexpr int UPR = VT / 8;                 // 16-byte units per row
+        constexpr int UPW = kC * UPR / 4;           // units per wave
+#pragma unroll
+        for (int u0 = 0; u0 < UPW; u0 += 64) {
+            const int u = (wave - 4) * UPW + u0 + lane;
+            if (UPW % 64 == 0 || u0 + lane < UPW) {
+                const int row = u / UPR, c8 = (u % UPR) * 8;
+                const uint4 w = *reinterpret_cast<const uint4 *>(sO + row * LDO + c8);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, (row * v_stride + c8) * 2, 0, 0);
+            }
+        }
     };
 
     // State update of chunk n.  The carried state is N = 2^{G_r} (.) M (per K
@@ -848,7 +868,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         }
         lds_barrier();
         // P2
-        if (wave >= 4) phaseAT(nb);
+        if (wave >= 4) {
+            phaseAT(nb);
+            storeO(n);
+        }
         if (carry) {
             carryUpdate(n, false);
             carryPX();
@@ -859,6 +882,8 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         carryMain(NC - 1);
         carryUpdate(NC - 1, true);
     }
+    lds_barrier();
+    if (wave >= 4) storeO(NC - 1);
 
     if (a.ST && carry) {
         const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
@@ -879,11 +904,12 @@ template <int K, int VT>
 hipError_t launch_kvt(const PrefillArgs &a, hipStream_t stream) {
     using L = Plan<K>;
     auto kern = prefill_bf16_kernel<K, VT>;
+    constexpr int lds = L::bytes + L::stage_bytes(VT);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     const unsigned grid = static_cast<unsigned>(a.B) * a.HV * (a.V / VT);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kNT), L::bytes, stream, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kNT), lds, stream, a);
     return hipGetLastError();
 }
 
