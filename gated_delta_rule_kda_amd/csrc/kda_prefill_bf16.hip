@@ -210,9 +210,9 @@ struct Plan {
     static constexpr int oPr = oPl + 2 * K * 4;                  // fp32 [K]  2^{G_r}
     static constexpr int oBeta = oPr + K * 4;                    // fp32 [2 buf][C]
     static constexpr int oTs = oBeta + 2 * kC * 4;               // fp32 [2 blk][16][LDT]  A_blk
-    static constexpr int oStage = oTs + 2 * 16 * LDT * 4;        // bf16 [C][VT + 8]  o of the chunk
+    static constexpr int oStage = oTs + 2 * 16 * LDT * 4;        // bf16 [2][C][VT + 8]  o, v of a chunk
     static constexpr int bytes = oStage;                         // plus stage_bytes(VT)
-    static constexpr int stage_bytes(int VT) { return kC * (VT + 8) * 2; }
+    static constexpr int stage_bytes(int VT) { return 2 * kC * (VT + 8) * 2; }
 };
 
 template <int K, int VT>
@@ -269,6 +269,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
     float *sTs = reinterpret_cast<float *>(smem + L::oTs);
     __bf16 *sO = reinterpret_cast<__bf16 *>(smem + L::oStage);
+    __bf16 *sV = sO + kC * LDO;
 
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int nvt = a.V / VT;
@@ -556,22 +557,50 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     };
 
     // ======================= carry waves
-    // v of the wave's column blocks, rows in accumulator order (row tile rt, rows 4*lg + r)
-    uint16_t pf_v[NG][2][4];
-    auto load_v = [&](int ch) {
-        const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
+    // v of a chunk: waves 4..7 load whole rows of the V tile (16 bytes per lane)
+    // one chunk ahead and write them to the staging tile sV; the carry waves read
+    // their accumulator-layout fragments (column lr, rows 4 lg .. 4 lg + 3) with
+    // ds_read_b64_tr_b16: in each 16-lane group g, lane 4a + b gets element b
+    // of the 8-byte pieces addressed by lanes 16 g + 4 e + a, e = 0..3.
+    // The staging work of the o and v tiles goes to waves 4, 5 and 7 (wave 6
+    // has the longest list of its own in that phase): helper index sh.
+    constexpr int VUPR = VT / 8;                // 16-byte units per row of the V tile
+    constexpr int VU = kC * VUPR;               // units of the tile
+    constexpr int VUPW = (VU / 3 + 63) / 64 * 64;   // units per helper wave
+    constexpr int VPL = VUPW / 64;              // units per lane
+    const int sh = wave == 4 ? 0 : wave == 5 ? 1 : 2;
+    uint4 pfv[VPL];
+    auto loadV = [&](int ch) {
+        const int lane = opaque_tid() & 63;
         const int t0 = ch * kC;
-        const auto rv = make_rsrc(vg + ((tok_b + t0) * HV + hv) * V, rows_bytes(t0, v_stride, V, 2));
+        const auto rv = make_rsrc(vg + ((tok_b + t0) * HV + hv) * V + v0, rows_bytes(t0, v_stride, VT, 2));
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            const int vcol = v0 + 16 * (wave * NG + gi) + lr;
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    pf_v[gi][rt][r] = __builtin_amdgcn_raw_buffer_load_b16(
-                        rv, ((rt * 16 + 4 * lg + r) * v_stride + vcol) * 2, 0, 0);
+        for (int j = 0; j < VPL; ++j) {
+            const int u = sh * VUPW + j * 64 + lane;   // past the tile: rows >= C, dropped by the resource
+            const int row = u / VUPR, c8 = (u % VUPR) * 8;
+            const auto w = __builtin_amdgcn_raw_buffer_load_b128(rv, (row * v_stride + c8) * 2, 0, 0);
+            pfv[j] = make_uint4(w[0], w[1], w[2], w[3]);
         }
+    };
+    auto writeV = [&]() {
+        const int lane = opaque_tid() & 63;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            const int u = sh * VUPW + j * 64 + lane;
+            if (u < VU) {
+                const int row = u / VUPR, c8 = (u % VUPR) * 8;
+                *reinterpret_cast<uint4 *>(sV + row * LDO + c8) = pfv[j];
+            }
+        }
+    };
+    // v fragment of row tile rt, column block gi of this carry wave: rows
+    // rt*16 + 4 lg + e (e = 0..3) of column 16 (wave NG + gi) + lr
+    auto readV = [&](int rt, int gi) {
+        const int lane = opaque_tid() & 63;
+        const int row = rt * 16 + 4 * (lane >> 4) + ((lane >> 2) & 3);
+        const int col = 16 * (wave * NG + gi) + 4 * (lane & 3);
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4 *)(sV + row * LDO + col));
     };
 
     f32x4 m[NG][KT];
@@ -652,6 +681,11 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         }
         // R = diag(beta) (v - (k Gamma) M), accumulator layout per 16-row tile
         const float *beta = sBeta + cbuf * kC;
+        bf16x4 vf[NG][2];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) vf[gi][rt] = readV(rt, gi);
         f32x4 rr[NG][2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -660,11 +694,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float vv = __uint_as_float(static_cast<uint32_t>(pf_v[gi][rt][r]) << 16);
-                    rr[gi][rt][r] = bt[r] * (vv - xq[gi][rt][r]);
+                    rr[gi][rt][r] = bt[r] * (fl(vf[gi][rt][r]) - xq[gi][rt][r]);
                 }
         }
-        load_v(n + 1);
         // U1 = T11 R1;  Y = R2 - A21 U1;  U2 = T22 Y   (16x16x16 MFMAs, 3 terms each)
         bf16x4 uh0[NG], ul0[NG], uh1[NG], ul1[NG];
         f32x4 acc[NG], acc2[NG];
@@ -724,18 +756,16 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     };
 
     // o of chunk n from the staging tile to HBM, 16 bytes per lane and whole
-    // rows of the V tile per lane group (waves 4..7, a quarter of the rows each)
+    // rows of the V tile per lane group (the helper waves, a third each)
     auto storeO = [&](int n) {
         const int lane = opaque_tid() & 63;
         const int t0 = n * kC;
         const auto ro = make_rsrc(og + ((tok_b + t0) * HV + hv) * V + v0, rows_bytes(t0, v_stride, VT, 2));
-        constexpr int UPR = VT / 8;                 // 16-byte units per row
-        constexpr int UPW = kC * UPR / 4;           // units per wave
 #pragma unroll
-        for (int u0 = 0; u0 < UPW; u0 += 64) {
-            const int u = (wave - 4) * UPW + u0 + lane;
-            if (UPW % 64 == 0 || u0 + lane < UPW) {
-                const int row = u / UPR, c8 = (u % UPR) * 8;
+        for (int j = 0; j < VPL; ++j) {
+            const int u = sh * VUPW + j * 64 + lane;
+            if (u < VU) {
+                const int row = u / VUPR, c8 = (u % VUPR) * 8;
                 const uint4 w = *reinterpret_cast<const uint4 *>(sO + row * LDO + c8);
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, (row * v_stride + c8) * 2, 0, 0);
             }
@@ -821,7 +851,6 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) m[gi][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        load_v(0);
         if (wave == 0) {
             // rows 0-15 x columns 16-31 of A_qk lie above the diagonal: zero for every chunk
 #pragma unroll
@@ -831,6 +860,11 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 sAqk[kC * LDC + i * LDC + j] = bf(0.f);
             }
         }
+    }
+    if (wave >= 4 && wave != 6) {
+        loadV(0);
+        writeV();
+        loadV(1);
     }
     if (opw) {
         load_prep(0);
@@ -870,7 +904,11 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         // P2
         if (wave >= 4) {
             phaseAT(nb);
-            storeO(n);
+            if (wave != 6) {
+                storeO(n);
+                writeV();        // v of chunk n+1 for the next phase's carry
+                loadV(n + 2);
+            }
         }
         if (carry) {
             carryUpdate(n, false);
@@ -883,7 +921,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         carryUpdate(NC - 1, true);
     }
     lds_barrier();
-    if (wave >= 4) storeO(NC - 1);
+    if (wave >= 4 && wave != 6) storeO(NC - 1);
 
     if (a.ST && carry) {
         const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
