@@ -562,13 +562,13 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     // their accumulator-layout fragments (column lr, rows 4 lg .. 4 lg + 3) with
     // ds_read_b64_tr_b16: in each 16-lane group g, lane 4a + b gets element b
     // of the 8-byte pieces addressed by lanes 16 g + 4 e + a, e = 0..3.
-    // The staging work of the o and v tiles goes to waves 4, 5 and 7 (wave 6
-    // has the longest list of its own in that phase): helper index sh.
+    // The staging work of the o and v tiles goes to waves 7, 4 and 5 (wave 6
+    // has the longest list of its own in that phase; 4 and 5 the next): groups
+    // of 64 units round-robin, helper index sh.
     constexpr int VUPR = VT / 8;                // 16-byte units per row of the V tile
     constexpr int VU = kC * VUPR;               // units of the tile
-    constexpr int VUPW = (VU / 3 + 63) / 64 * 64;   // units per helper wave
-    constexpr int VPL = VUPW / 64;              // units per lane
-    const int sh = wave == 4 ? 0 : wave == 5 ? 1 : 2;
+    constexpr int VPL = (VU / 64 + 2) / 3;      // unit groups per helper wave (at most)
+    const int sh = wave == 7 ? 0 : wave == 4 ? 1 : 2;
     uint4 pfv[VPL];
     auto loadV = [&](int ch) {
         const int lane = opaque_tid() & 63;
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         const auto rv = make_rsrc(vg + ((tok_b + t0) * HV + hv) * V + v0, rows_bytes(t0, v_stride, VT, 2));
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
-            const int u = sh * VUPW + j * 64 + lane;   // past the tile: rows >= C, dropped by the resource
+            const int u = (3 * j + sh) * 64 + lane;   // past the tile: rows >= C, dropped by the resource
             const int row = u / VUPR, c8 = (u % VUPR) * 8;
             const auto w = __builtin_amdgcn_raw_buffer_load_b128(rv, (row * v_stride + c8) * 2, 0, 0);
             pfv[j] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         const int lane = opaque_tid() & 63;
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
-            const int u = sh * VUPW + j * 64 + lane;
+            const int u = (3 * j + sh) * 64 + lane;
             if (u < VU) {
                 const int row = u / VUPR, c8 = (u % VUPR) * 8;
                 *reinterpret_cast<uint4 *>(sV + row * LDO + c8) = pfv[j];
@@ -763,7 +763,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         const auto ro = make_rsrc(og + ((tok_b + t0) * HV + hv) * V + v0, rows_bytes(t0, v_stride, VT, 2));
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
-            const int u = sh * VUPW + j * 64 + lane;
+            const int u = (3 * j + sh) * 64 + lane;
             if (u < VU) {
                 const int row = u / VUPR, c8 = (u % VUPR) * 8;
                 const uint4 w = *reinterpret_cast<const uint4 *>(sO + row * LDO + c8);
