@@ -53,6 +53,8 @@ def _load():
             lib.kda_oracle_threads.restype = I
             lib.kda_oracle_fwd.argtypes = [P] * 8 + [L] * 6 + [D]
             lib.kda_oracle_fwd.restype = I
+            lib.kda_oracle_fwd_snapshots.argtypes = [P] * 9 + [L] * 7 + [D]
+            lib.kda_oracle_fwd_snapshots.restype = I
             lib.kda_oracle_decode_step.argtypes = (
                 [P, P, P, L, I, D, P, P, P, I, D, P, I, P, P] + [L] * 5 + [D])
             lib.kda_oracle_decode_step.restype = I
@@ -85,12 +87,17 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def kda_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True):
+def kda_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
+            snapshot_every=None):
     """Token-by-token KDA forward in fp64.
 
     Follows naive_kda_fwd on the "K3/kda/ops/reference/recurrent.py" page:
     q, k [B,T,H,K]; v [B,T,HV,V]; g [B,T,HV,K]; beta [B,T,HV];
-    initial_state [B,HV,K,V] or None.  Returns (o [B,T,HV,V], S_T or None).
+    initial_state [B,HV,K,V] or None.  Returns (o [B,T,HV,V], S_T or None),
+    and with ``snapshot_every`` a third array [B, T // every, HV, K, V]: the
+    state after each whole multiple of ``every`` tokens (the prefix snapshots
+    that the prefix-cache test on the "metrale_model_weights/kimi_k3_host/kda.rs"
+    page resumes decoding from).
     """
     q, k, v, g, beta = (f64(a) for a in (q, k, v, g, beta))
     S0 = f64(initial_state)
@@ -104,10 +111,18 @@ def kda_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state
         scale = 1.0 / math.sqrt(K)
     o = np.zeros((B, T, HV, V), dtype=np.float64)
     S = np.zeros((B, HV, K, V), dtype=np.float64)
-    rc = _load().kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
-                                _ptr(o), _ptr(S), B, T, H, HV, K, V, float(scale))
+    snaps, every = None, 0
+    if snapshot_every is not None:
+        every = int(snapshot_every)
+        assert every >= 1
+        snaps = np.zeros((B, T // every, HV, K, V), dtype=np.float64)
+    rc = _load().kda_oracle_fwd_snapshots(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S),
+        _ptr(snaps), every, B, T, H, HV, K, V, float(scale))
     if rc != 0:
         raise RuntimeError("kda_oracle_fwd failed with status %d" % rc)
+    if snapshot_every is not None:
+        return o, (S if output_final_state else None), snaps
     return o, (S if output_final_state else None)
 
 

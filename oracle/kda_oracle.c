@@ -77,10 +77,27 @@ int kda_oracle_fwd(const double *q, const double *k, const double *v,
                    double *o, double *S_out, long B, long T, long H, long HV,
                    long K, long V, double scale)
 {
+    return kda_oracle_fwd_snapshots(q, k, v, g, beta, S0, o, S_out, NULL, 0,
+                                    B, T, H, HV, K, V, scale);
+}
+
+/* The time loop of [recurrent.py] naive_kda_fwd, which can also keep copies of
+ * the state along the way: the prefix-cache test of [kda.rs]
+ * (prefix_hit_wrong_slot_diverges) clones the whole state after each token and
+ * resumes decoding from such a clone.  Here snapshot j, for j < T / every, is
+ * the state after the first (j + 1) * every tokens, written to
+ * snaps[b][j][hv] ([B, T / every, HV, K, V]).  snaps == NULL keeps none. */
+int kda_oracle_fwd_snapshots(const double *q, const double *k, const double *v,
+                             const double *g, const double *beta, const double *S0,
+                             double *o, double *S_out, double *snaps, long every,
+                             long B, long T, long H, long HV, long K, long V,
+                             double scale)
+{
     long bh;
     int status = 0;
     if (B < 0 || T < 0 || H <= 0 || HV <= 0 || K <= 0 || V <= 0) return 1;
     if (HV % H != 0) return 1;
+    if (snaps && every <= 0) return 1;
     /* [recurrent.py]: scale=None means 1/sqrt(K). */
     if (!(scale > 0.0)) scale = 1.0 / sqrt((double)K);
 
@@ -108,6 +125,11 @@ int kda_oracle_fwd(const double *q, const double *k, const double *v,
                 const double bt = beta[tok * HV + hv];
                 for (i = 0; i < K; ++i) qs[i] = scale * qt[i];
                 token_step(S, qs, kt, vt, gt, bt, o + (tok * HV + hv) * V, r, K, V);
+                if (snaps && (t + 1) % every == 0) {
+                    const long j = (t + 1) / every - 1, ns = T / every;
+                    memcpy(snaps + ((b * ns + j) * HV + hv) * K * V, S,
+                           (size_t)(K * V) * sizeof(double));
+                }
             }
             if (S_out) memcpy(S_out + bh * K * V, S, (size_t)(K * V) * sizeof(double));
         }

@@ -25,6 +25,16 @@ int kda_oracle_fwd(const double *q, const double *k, const double *v,
                    double *o, double *S_out, long B, long T, long H, long HV,
                    long K, long V, double scale);
 
+/* kda_oracle_fwd that also keeps snapshots of the state: snapshot j
+ * (j < T / every) is the state after the first (j + 1) * every tokens, stored
+ * at snaps[b][j][hv] ([B, T / every, HV, K, V]).  snaps == NULL keeps none;
+ * otherwise every must be >= 1. */
+int kda_oracle_fwd_snapshots(const double *q, const double *k, const double *v,
+                             const double *g, const double *beta, const double *S0,
+                             double *o, double *S_out, double *snaps, long every,
+                             long B, long T, long H, long HV, long K, long V,
+                             double scale);
+
 /* One decode token for B sequences ("metrale_model_weights/kimi_k3_host/kda.rs",
  * kda_decode_token / kda_recurrent_step), with every prologue stage optional:
  *   x          [B, 2*H*K + HV*V]  packed q | k | v channels (before the conv)

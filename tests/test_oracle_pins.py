@@ -200,6 +200,78 @@ def test_split_resume():
     np.testing.assert_allclose(Sb, S, rtol=1e-13, atol=1e-15)
 
 
+def _fraction_states(q, k, v, d, beta, S0):
+    """All states S_1..S_T of the projection form of the recurrence, exactly."""
+    T = len(q)
+    K, V = len(S0), len(S0[0])
+    S = [row[:] for row in S0]
+    states = []
+    for t in range(T):
+        DS = [[d[t][i] * S[i][j] for j in range(V)] for i in range(K)]
+        S = [[DS[i][j] - beta[t] * k[t][i] * sum(k[t][m] * DS[m][j] for m in range(K))
+              + beta[t] * k[t][i] * v[t][j] for j in range(V)] for i in range(K)]
+        states.append(S)
+    return states
+
+
+@pytest.mark.parametrize("T,every", [(8, 2), (7, 3), (6, 6), (5, 8)])
+def test_snapshots_brute_force_rational(T, every):
+    """Prefix snapshots (the state clones that kda.rs prefix_hit_wrong_slot_diverges
+    resumes from) against exact rationals: snapshot j is S after token
+    (j+1)*every, T // every of them.  Catches an off-by-one token, a snapshot
+    taken before the write, a wrong count."""
+    K, V = 3, 2
+    rng = np.random.default_rng(T * 10 + every)
+    fr = lambda lo, hi: Fraction(int(rng.integers(lo, hi)), 8)
+    q = [[fr(-8, 9) for _ in range(K)] for _ in range(T)]
+    k = [[fr(-8, 9) for _ in range(K)] for _ in range(T)]
+    v = [[fr(-16, 17) for _ in range(V)] for _ in range(T)]
+    d = [[Fraction(int(rng.integers(1, 9)), 8) for _ in range(K)] for _ in range(T)]
+    beta = [Fraction(int(rng.integers(0, 9)), 8) for _ in range(T)]
+    S0 = [[fr(-8, 9) for _ in range(V)] for _ in range(K)]
+    states = _fraction_states(q, k, v, d, beta, S0)
+    A = lambda x: np.array([[float(e) for e in row] for row in x])
+    _, _, snaps = oracle.kda_fwd(
+        A(q)[None, :, None], A(k)[None, :, None], A(v)[None, :, None],
+        np.log(A(d))[None, :, None], np.array([float(b) for b in beta])[None, :, None],
+        scale=0.5, initial_state=A(S0)[None, None], snapshot_every=every)
+    assert snaps.shape == (1, T // every, 1, K, V)
+    for j in range(T // every):
+        np.testing.assert_allclose(snaps[0, j, 0], A(states[(j + 1) * every - 1]),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_snapshots_beta_zero_closed_form():
+    """beta = 0: snapshot j = exp(G_{(j+1)e}) (.) S0 for every (b, hv), laid out
+    [B, T // e, HV, K, V].  Catches a transposed (b, j, hv) layout."""
+    B, T, H, HV, K, V, e = 2, 20, 1, 3, 4, 5, 6
+    q, k, v, g, beta, S0 = rand_inputs(B, T, H, HV, K, V, g_scale=0.5)
+    beta[:] = 0.0
+    _, S, snaps = oracle.kda_fwd(q, k, v, g, beta, initial_state=S0, snapshot_every=e)
+    G = np.cumsum(g, axis=1)
+    assert snaps.shape == (B, 3, HV, K, V)
+    for j in range(3):
+        np.testing.assert_allclose(snaps[:, j], np.exp(G[:, (j + 1) * e - 1])[..., None] * S0,
+                                   rtol=1e-13, atol=1e-15)
+
+
+def test_snapshot_resume_equals_full_run():
+    """Resuming from snapshot j over the rest of the tokens gives the full run's
+    later outputs and final state; resuming from snapshot j-1 does not."""
+    B, T, H, HV, K, V, e = 2, 40, 1, 2, 8, 4, 8
+    q, k, v, g, beta, S0 = rand_inputs(B, T, H, HV, K, V)
+    o, S, snaps = oracle.kda_fwd(q, k, v, g, beta, initial_state=S0, snapshot_every=e)
+    j = 2
+    a = (j + 1) * e
+    ob, Sb = oracle.kda_fwd(q[:, a:], k[:, a:], v[:, a:], g[:, a:], beta[:, a:],
+                            initial_state=snaps[:, j])
+    np.testing.assert_allclose(ob, o[:, a:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(Sb, S, rtol=1e-12, atol=1e-14)
+    ow, _ = oracle.kda_fwd(q[:, a:], k[:, a:], v[:, a:], g[:, a:], beta[:, a:],
+                           initial_state=snaps[:, j - 1])
+    assert np.max(np.abs(ow - o[:, a:])) > 1e-4
+
+
 def test_default_scale_and_zero_state():
     """scale=None means 1/sqrt(K); initial_state=None means zeros."""
     B, T, H, HV, K, V = 1, 5, 1, 1, 16, 4
