@@ -7,6 +7,7 @@ library's kernels.  torch supplies device memory and streams.
 
     o, S_T = chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                        output_final_state=False)
+    o, S_T, snaps = chunk_fwd_snapshots(q, k, v, g, beta, snapshot_every, ...)
     out = decode_step(qkv, gate, beta, state, H=..., ...)   # state updated in place
 
 There is no CPU fallback: calling an op without the built library, or with
@@ -20,7 +21,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "abi_version", "library_path", "KDAError",
+__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "decode_step", "abi_version", "library_path", "KDAError",
            "GATE_DIRECT", "GATE_BOUNDED", "GATE_SOFTPLUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +79,8 @@ def _load():
             lib.kda_last_error.restype = ctypes.c_char_p
             lib.kda_chunk_fwd.argtypes = [P] * 8 + [I] * 6 + [F, I, I, P]
             lib.kda_chunk_fwd.restype = I
+            lib.kda_chunk_fwd_snapshots.argtypes = [P] * 9 + [I] * 7 + [F, I, I, P]
+            lib.kda_chunk_fwd_snapshots.restype = I
             lib.kda_decode_step.argtypes = [P] * 5 + [ctypes.POINTER(DecodePrologue)] + [I] * 5 + [F, I, P]
             lib.kda_decode_step.restype = I
             if lib.kda_abi_version() != ABI_VERSION:
@@ -126,16 +129,7 @@ def _need(t, name, dtype=None, shape=None, device=None):
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
 
 
-def chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
-              *, chunk_size=32, out=None, final_state=None):
-    """Chunk-parallel KDA prefill (``kda_chunk_fwd``).
-
-    q, k [B,T,H,K]; v [B,T,HV,V] (all bf16 or all fp32); g [B,T,HV,K] fp32 with
-    -5 <= g <= 0; beta [B,T,HV] fp32; initial_state [B,HV,K,V] fp32 or None.
-    Returns (o [B,T,HV,V] in v's dtype, final state [B,HV,K,V] fp32 or None).
-    ``final_state`` may be passed (even the initial_state tensor itself, to
-    resume in place); ``out`` may be passed to avoid an allocation.
-    """
+def _prefill_args(q, k, v, g, beta, initial_state, output_final_state, out, final_state):
     _need(q, "q")
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
@@ -155,11 +149,54 @@ def chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
         final_state = torch.empty(B, HV, K, V, dtype=torch.float32, device=dev)
     elif final_state is not None:
         _need(final_state, "final_state", torch.float32, (B, HV, K, V), dev)
+    return (B, T, H, HV, K, V), out, final_state
+
+
+def chunk_fwd_snapshots(q, k, v, g, beta, snapshot_every, scale=None, initial_state=None,
+                        output_final_state=False, *, chunk_size=32, out=None,
+                        final_state=None, snapshots=None):
+    """``kda_chunk_fwd_snapshots``: :func:`chunk_fwd` that also returns prefix
+    snapshots [B, T // snapshot_every, HV, K, V] fp32, snapshot j being the
+    state after the first (j+1)*snapshot_every tokens (a positive multiple of
+    32).  Returns (o, final state or None, snapshots)."""
+    (B, T, H, HV, K, V), out, final_state = _prefill_args(
+        q, k, v, g, beta, initial_state, output_final_state, out, final_state)
+    dev = q.device
+    every = int(snapshot_every)
+    if every < 32 or every % 32 != 0:
+        raise ValueError("snapshot_every=%d must be a positive multiple of the chunk size 32" % every)
+    NS = T // every
+    if snapshots is None:
+        snapshots = torch.empty(B, NS, HV, K, V, dtype=torch.float32, device=dev)
+    else:
+        _need(snapshots, "snapshots", torch.float32, (B, NS, HV, K, V), dev)
+    with torch.cuda.device(dev):
+        _check(_load().kda_chunk_fwd_snapshots(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(out),
+            _ptr(final_state), _ptr(snapshots), every, B, T, H, HV, K, V,
+            float(scale) if scale else 0.0, int(chunk_size), _dtype_code(q.dtype),
+            _stream_handle(dev)))
+    return out, final_state, snapshots
+
+
+def chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
+              *, chunk_size=32, out=None, final_state=None):
+    """Chunk-parallel KDA prefill (``kda_chunk_fwd``).
+
+    q, k [B,T,H,K]; v [B,T,HV,V] (all bf16 or all fp32); g [B,T,HV,K] fp32 with
+    -5 <= g <= 0; beta [B,T,HV] fp32; initial_state [B,HV,K,V] fp32 or None.
+    Returns (o [B,T,HV,V] in v's dtype, final state [B,HV,K,V] fp32 or None).
+    ``final_state`` may be passed (even the initial_state tensor itself, to
+    resume in place); ``out`` may be passed to avoid an allocation.
+    """
+    (B, T, H, HV, K, V), out, final_state = _prefill_args(
+        q, k, v, g, beta, initial_state, output_final_state, out, final_state)
+    dev = q.device
     with torch.cuda.device(dev):
         _check(_load().kda_chunk_fwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(out),
             _ptr(final_state), B, T, H, HV, K, V, float(scale) if scale else 0.0,
-            int(chunk_size), _dtype_code(dt), _stream_handle(dev)))
+            int(chunk_size), _dtype_code(q.dtype), _stream_handle(dev)))
     return out, final_state
 
 

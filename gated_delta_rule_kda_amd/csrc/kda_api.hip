@@ -67,39 +67,49 @@ int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
 const char *kda_last_error(void) { return g_err; }
 
-int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
-                  const float *beta, const float *initial_state, void *out,
-                  float *final_state, int B, int T, int H, int HV, int K, int V,
-                  float scale, int chunk, int dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of kda_chunk_fwd and kda_chunk_fwd_snapshots; `fn` names the
+// entry point in error messages.
+int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, const float *g,
+                   const float *beta, const float *initial_state, void *out, float *final_state,
+                   float *snapshots, int snapshot_every, int B, int T, int H, int HV, int K,
+                   int V, float scale, int chunk, int dtype, void *stream) {
     g_err[0] = '\0';
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
-        return fail(KDA_EUNSUPPORTED, "kda_chunk_fwd: dtype %d is not KDA_DTYPE_F32 or KDA_DTYPE_BF16", dtype);
-    if (B < 0 || T < 0) return fail(KDA_EINVAL, "kda_chunk_fwd: B=%d and T=%d must be >= 0", B, T);
-    if (H < 1 || HV < 1) return fail(KDA_EINVAL, "kda_chunk_fwd: H=%d and HV=%d must be >= 1", H, HV);
-    if (HV % H != 0) return fail(KDA_EINVAL, "kda_chunk_fwd: HV=%d is not a multiple of H=%d", HV, H);
+        return fail(KDA_EUNSUPPORTED, "%s: dtype %d is not KDA_DTYPE_F32 or KDA_DTYPE_BF16", fn, dtype);
+    if (B < 0 || T < 0) return fail(KDA_EINVAL, "%s: B=%d and T=%d must be >= 0", fn, B, T);
+    if (H < 1 || HV < 1) return fail(KDA_EINVAL, "%s: H=%d and HV=%d must be >= 1", fn, H, HV);
+    if (HV % H != 0) return fail(KDA_EINVAL, "%s: HV=%d is not a multiple of H=%d", fn, HV, H);
     if (!head_dim_ok(K) || !head_dim_ok(V))
-        return fail(KDA_EUNSUPPORTED, "kda_chunk_fwd: K=%d, V=%d; each must be 32, 64 or 128", K, V);
-    if (chunk < 0) return fail(KDA_EINVAL, "kda_chunk_fwd: chunk=%d must be >= 0", chunk);
+        return fail(KDA_EUNSUPPORTED, "%s: K=%d, V=%d; each must be 32, 64 or 128", fn, K, V);
+    if (chunk < 0) return fail(KDA_EINVAL, "%s: chunk=%d must be >= 0", fn, chunk);
     if (chunk != 0 && chunk != 32)
-        return fail(KDA_EUNSUPPORTED, "kda_chunk_fwd: chunk=%d; only 32 (or 0 for the default) is built", chunk);
-    if (isinf(scale)) return fail(KDA_EINVAL, "kda_chunk_fwd: scale is infinite");
+        return fail(KDA_EUNSUPPORTED, "%s: chunk=%d; only 32 (or 0 for the default) is built", fn, chunk);
+    if (snapshots && (snapshot_every < 32 || snapshot_every % 32 != 0))
+        return fail(KDA_EINVAL, "%s: snapshot_every=%d must be a positive multiple of the chunk size 32",
+                    fn, snapshot_every);
+    if (isinf(scale)) return fail(KDA_EINVAL, "%s: scale is infinite", fn);
     if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(K));
 
     const uint64_t esz = dtype == KDA_DTYPE_BF16 ? 2 : 4;
-    uint64_t nq, nv, ng, nb, ns;
+    const int NS = snapshots ? T / snapshot_every : 0;
+    uint64_t nq, nv, ng, nb, ns, nsn;
     if (!count(nq, {B, T, H, K}) || !count(nv, {B, T, HV, V}) || !count(ng, {B, T, HV, K}) ||
-        !count(nb, {B, T, HV}) || !count(ns, {B, HV, K, V}))
-        return fail(KDA_EINVAL, "kda_chunk_fwd: tensor sizes overflow");
+        !count(nb, {B, T, HV}) || !count(ns, {B, HV, K, V}) || !count(nsn, {B, NS, HV, K, V}))
+        return fail(KDA_EINVAL, "%s: tensor sizes overflow", fn);
     const bool work = (static_cast<int64_t>(B) * T) > 0;
     if (work) {
         if (!q || !k || !v || !g || !beta || !out)
-            return fail(KDA_EINVAL, "kda_chunk_fwd: q, k, v, g, beta and out must be non-NULL");
+            return fail(KDA_EINVAL, "%s: q, k, v, g, beta and out must be non-NULL", fn);
     }
-    const void *ptrs[] = {q, k, v, g, beta, initial_state, out, final_state};
-    const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "out", "final_state"};
-    for (int i = 0; i < 8; ++i)
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, out, final_state, snapshots};
+    const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "out", "final_state", "snapshots"};
+    for (int i = 0; i < 9; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
-            return fail(KDA_EINVAL, "kda_chunk_fwd: %s is not 16-byte aligned", names[i]);
+            return fail(KDA_EINVAL, "%s: %s is not 16-byte aligned", fn, names[i]);
 
     const Range r_in[] = {rng("q", q, nq * esz), rng("k", k, nq * esz), rng("v", v, nv * esz),
                           rng("g", g, ng * 4), rng("beta", beta, nb * 4),
@@ -107,11 +117,16 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
     const Range r_out = rng("out", out, nv * esz);
     const Range r_st = rng("final_state", final_state, ns * 4);
     for (const Range &r : r_in) {
-        if (work && overlap(r_out, r)) return fail(KDA_EINVAL, "kda_chunk_fwd: out overlaps %s", r.name);
+        if (work && overlap(r_out, r)) return fail(KDA_EINVAL, "%s: out overlaps %s", fn, r.name);
         if (overlap(r_st, r) && !(&r == &r_in[5] && final_state == initial_state))
-            return fail(KDA_EINVAL, "kda_chunk_fwd: final_state overlaps %s", r.name);
+            return fail(KDA_EINVAL, "%s: final_state overlaps %s", fn, r.name);
     }
-    if (work && overlap(r_out, r_st)) return fail(KDA_EINVAL, "kda_chunk_fwd: out overlaps final_state");
+    if (work && overlap(r_out, r_st)) return fail(KDA_EINVAL, "%s: out overlaps final_state", fn);
+    const Range r_sn = rng("snapshots", snapshots, nsn * 4);
+    for (const Range &r : r_in)
+        if (overlap(r_sn, r)) return fail(KDA_EINVAL, "%s: snapshots overlap %s", fn, r.name);
+    if (overlap(r_sn, r_out) || overlap(r_sn, r_st))
+        return fail(KDA_EINVAL, "%s: snapshots overlap %s", fn, overlap(r_sn, r_out) ? "out" : "final_state");
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!work) {
@@ -121,7 +136,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
             hipLaunchKernelGGL(copy_or_zero_kernel, dim3(blocks), dim3(256), 0, st, final_state,
                                initial_state, ns);
             const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return fail(KDA_EHIP, "kda_chunk_fwd: launch failed: %s", hipGetErrorString(e));
+            if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
         }
         return KDA_OK;
     }
@@ -129,12 +144,37 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
     kda::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = initial_state;
     a.out = out; a.ST = final_state;
+    a.snap = NS > 0 ? snapshots : nullptr;
+    a.snap_chunks = NS > 0 ? snapshot_every / 32 : 1;
+    a.NS = NS;
     a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
     a.scale = scale;
     a.bf16 = dtype == KDA_DTYPE_BF16;
     const hipError_t e = kda::launch_prefill(a, st);
-    if (e != hipSuccess) return fail(KDA_EHIP, "kda_chunk_fwd: launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                  const float *beta, const float *initial_state, void *out,
+                  float *final_state, int B, int T, int H, int HV, int K, int V,
+                  float scale, int chunk, int dtype, void *stream) {
+    return chunk_fwd_impl("kda_chunk_fwd", q, k, v, g, beta, initial_state, out, final_state,
+                          nullptr, 0, B, T, H, HV, K, V, scale, chunk, dtype, stream);
+}
+
+int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *initial_state, void *out,
+                            float *final_state, float *snapshots, int snapshot_every,
+                            int B, int T, int H, int HV, int K, int V, float scale,
+                            int chunk, int dtype, void *stream) {
+    return chunk_fwd_impl("kda_chunk_fwd_snapshots", q, k, v, g, beta, initial_state, out,
+                          final_state, snapshots, snapshot_every, B, T, H, HV, K, V, scale,
+                          chunk, dtype, stream);
 }
 
 int kda_decode_step(const void *qkv, const float *gate, const float *beta, float *state,

@@ -14,6 +14,9 @@ struct PrefillArgs {
     const float *S0;            // [B,HV,K,V] or nullptr
     void *out;                  // [B,T,HV,V] (dtype)
     float *ST;                  // [B,HV,K,V] or nullptr
+    float *snap;                // [B,NS,HV,K,V] prefix snapshots or nullptr
+    int snap_chunks;            // chunks between snapshots (>= 1 when snap is set)
+    int NS;                     // snapshots per sequence, T / (32 * snap_chunks)
     int B, T, H, HV, K, V;
     float scale;
     bool bf16;

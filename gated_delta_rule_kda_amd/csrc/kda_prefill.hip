@@ -198,6 +198,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         }
     };
     store_MT();
+    // M -> dst[K][V] (the state slice of this workgroup's columns)
+    auto store_state = [&](float *dst) {
+#pragma unroll
+        for (int s = 0; s < NMT; ++s) {
+            const int t = wave * NMT + s;
+            const int kt = t / VTT, vtt = t % VTT;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int f = kt * 16 + lg * 4 + r, v = vtt * 16 + lr;
+                dst[static_cast<size_t>(f) * a.V + v0 + v] = macc[s][r];
+            }
+        }
+    };
+    // prefix snapshots: the state after every snap_chunks whole chunks
+    int snap_left = a.snap_chunks, snap_j = 0;
 
     const int nchunks = (a.T + kC - 1) / kC;
     for (int ch = 0; ch < nchunks; ++ch) {
@@ -565,6 +580,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             }
         }
         store_MT();
+        if (a.snap && --snap_left == 0) {
+            snap_left = a.snap_chunks;
+            if (snap_j < a.NS)
+                store_state(a.snap + ((static_cast<size_t>(b) * a.NS + snap_j) * a.HV + hv) * K * a.V);
+            ++snap_j;
+        }
         __syncthreads();
 
         // ============ output: staging -> global, 16-byte stores along V
@@ -593,19 +614,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     }
 
     // ---------------------------------------------------------------- final state
-    if (a.ST) {
-        float *ST = a.ST + (static_cast<size_t>(b) * a.HV + hv) * K * a.V;
-#pragma unroll
-        for (int s = 0; s < NMT; ++s) {
-            const int t = wave * NMT + s;
-            const int kt = t / VTT, vtt = t % VTT;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int f = kt * 16 + lg * 4 + r, v = vtt * 16 + lr;
-                ST[static_cast<size_t>(f) * a.V + v0 + v] = macc[s][r];
-            }
-        }
-    }
+    if (a.ST) store_state(a.ST + (static_cast<size_t>(b) * a.HV + hv) * K * a.V);
 }
 
 template <int K, int VT, bool BF16IO>

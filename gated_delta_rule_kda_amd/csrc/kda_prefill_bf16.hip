@@ -215,7 +215,9 @@ struct Plan {
     static constexpr int stage_bytes(int VT) { return 2 * kC * (VT + 8) * 2; }
 };
 
-template <int K, int VT>
+// SNAP: the variant that also writes prefix snapshots of the state (a
+// separate instantiation, so that the plain path carries none of its code).
+template <int K, int VT, bool SNAP>
 __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     using L = Plan<K>;
     static_assert(L::bytes + L::stage_bytes(VT) <= 160 * 1024, "LDS plan exceeds 160 KB");
@@ -831,6 +833,59 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         }
     };
 
+    // rowscale(kt) (.) M -> dst[K][V], the columns of this wave (the carry's
+    // own layout).  A buffer resource and an opaque lane index keep the
+    // addresses from being hoisted into registers that live across the whole
+    // chunk loop.
+    auto carryStoreScaled = [&](float *dst, auto rowscale) {
+        const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
+        int row_bytes = V * 4;
+        asm volatile("" : "+s"(row_bytes));
+        const auto rs = make_rsrc(dst, static_cast<uint32_t>(K) * V * 4);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            const f32x4 sc = rowscale(kt, lg);
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const int vo = lg * 4 * row_bytes + (v0 + 16 * (wave * NG + gi) + lr) * 4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // the element is copied out first: __builtin_bit_cast applied to a
+                    // vector element directly compiles to element 0 for every r
+                    const float x = m[gi][kt][r] * sc[r];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, vo,
+                                                          (kt * 16 + r) * row_bytes, 0);
+                }
+            }
+        }
+    };
+    auto carryStore = [&](float *dst) {
+        carryStoreScaled(dst, [](int, int) { return f32x4{1.f, 1.f, 1.f, 1.f}; });
+    };
+    // Prefix snapshots (SNAP only): the state after chunks snap_chunks,
+    // 2 snap_chunks, ..., NS snap_chunks; snap_ptr is the next one's [K][V]
+    // slice, null when none is left.
+    float *snap_ptr = SNAP ? a.snap + ((static_cast<size_t>(b) * a.NS) * HV + hv) * K * V : nullptr;
+    int snap_at = a.snap_chunks;
+    // Snapshot after chunk snap_at - 1.  exact: m holds M (after the last
+    // chunk).  Otherwise m holds the next chunk's N (end of P2, off the carry's
+    // critical block) and M = N / 2^{G_r}, the reciprocal exact to 1 ulp.
+    auto carrySnapshot = [&](bool exact) {
+        if (exact) {
+            carryStore(snap_ptr);
+        } else {
+            carryStoreScaled(snap_ptr, [&](int kt, int lg) {
+                const f32x4 prv = *reinterpret_cast<const f32x4 *>(sPr + kt * 16 + lg * 4);
+                f32x4 inv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) inv[r] = __builtin_amdgcn_rcpf(prv[r]);
+                return inv;
+            });
+        }
+        snap_at += a.snap_chunks;
+        snap_ptr = snap_at <= a.NS * a.snap_chunks ? snap_ptr + static_cast<size_t>(HV) * K * V : nullptr;
+    };
+
     // ---------------------------------------------------------------- prologue: chunk 0
     if (carry) {
         const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
@@ -913,35 +968,27 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         if (carry) {
             carryUpdate(n, false);
             carryPX();
+            if constexpr (SNAP)
+                if (snap_ptr && n + 1 == snap_at) carrySnapshot(false);
         }
         lds_barrier();
     }
     if (carry) {
         carryMain(NC - 1);
         carryUpdate(NC - 1, true);
+        if constexpr (SNAP)
+            if (snap_ptr && NC == snap_at) carrySnapshot(true);
     }
     lds_barrier();
     if (wave >= 4 && wave != 6) storeO(NC - 1);
 
-    if (a.ST && carry) {
-        const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-        float *ST = a.ST + (static_cast<size_t>(b) * HV + hv) * K * V;
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            const int vcol = v0 + 16 * (wave * NG + gi) + lr;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    ST[static_cast<size_t>(kt * 16 + lg * 4 + r) * V + vcol] = m[gi][kt][r];
-        }
-    }
+    if (a.ST && carry) carryStore(a.ST + (static_cast<size_t>(b) * HV + hv) * K * V);
 }
 
-template <int K, int VT>
-hipError_t launch_kvt(const PrefillArgs &a, hipStream_t stream) {
+template <int K, int VT, bool SNAP>
+hipError_t launch_kvt_s(const PrefillArgs &a, hipStream_t stream) {
     using L = Plan<K>;
-    auto kern = prefill_bf16_kernel<K, VT>;
+    auto kern = prefill_bf16_kernel<K, VT, SNAP>;
     constexpr int lds = L::bytes + L::stage_bytes(VT);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -949,6 +996,11 @@ hipError_t launch_kvt(const PrefillArgs &a, hipStream_t stream) {
     const unsigned grid = static_cast<unsigned>(a.B) * a.HV * (a.V / VT);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kNT), lds, stream, a);
     return hipGetLastError();
+}
+
+template <int K, int VT>
+hipError_t launch_kvt(const PrefillArgs &a, hipStream_t stream) {
+    return a.snap ? launch_kvt_s<K, VT, true>(a, stream) : launch_kvt_s<K, VT, false>(a, stream);
 }
 
 template <int K>

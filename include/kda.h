@@ -89,6 +89,37 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                   float scale, int chunk, int dtype, void *stream);
 
 /*
+ * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also writes prefix snapshots
+ * of the state, so that decoding can later resume from any whole multiple of
+ * snapshot_every tokens (the prefix cache of the page
+ * "metrale_model_weights/kimi_k3_host/kda.rs": its test
+ * prefix_hit_wrong_slot_diverges keeps a clone of the state after each token
+ * and resumes decoding from one; a resumed decode must equal the sequential
+ * one).
+ *
+ *   snapshots       [B, NS, HV, K, V] fp32 with NS = T / snapshot_every
+ *                   (rounded down); snapshot j of sequence b holds, for each
+ *                   value head, the state after the first
+ *                   (j + 1) * snapshot_every tokens, i.e. exactly what
+ *                   final_state would hold for a call on that prefix.  So
+ *                   snapshots[b][j] is laid out as the initial_state of one
+ *                   sequence.  NULL: none are written (the call is then
+ *                   kda_chunk_fwd).  Must not overlap any other argument.
+ *   snapshot_every  tokens between snapshots; when snapshots is not NULL it
+ *                   must be a positive multiple of the chunk size (32), else
+ *                   KDA_EINVAL.
+ * All other arguments, their layouts and the error behaviour are those of
+ * kda_chunk_fwd.  When T is a multiple of snapshot_every the last snapshot
+ * equals the final state.  Writing snapshots adds B*NS*HV*K*V*4 bytes of
+ * stores to the call.
+ */
+int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *initial_state, void *out,
+                            float *final_state, float *snapshots, int snapshot_every,
+                            int B, int T, int H, int HV, int K, int V, float scale,
+                            int chunk, int dtype, void *stream);
+
+/*
  * Optional stages fused in front of the decode step, as the host decode on the
  * page "metrale_model_weights/kimi_k3_host/kda.rs" runs them (kda_decode_token:
  * conv_update, then kda_recurrent_step with l2norm_rows and a sigmoid on beta;

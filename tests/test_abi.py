@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) == {"kda_abi_version", "kda_last_error", "kda_chunk_fwd", "kda_decode_step"}
+    assert set(names) == {"kda_abi_version", "kda_last_error", "kda_chunk_fwd",
+                          "kda_chunk_fwd_snapshots", "kda_decode_step"}
     L = ctypes.CDLL(kda.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -100,6 +101,44 @@ def test_chunk_fwd_rejects(over, code, msg):
     rc, err = chunk(**over)
     assert rc == code, err
     assert msg in err, err
+
+
+def snap_call(snaps, every, **over):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, s0=None, out=FAKE * 6,
+             st=None, B=1, T=64, H=2, HV=4, K=32, V=32, scale=0.0, chunk=0, dtype=1)
+    a.update(over)
+    L = lib()
+    rc = L.kda_chunk_fwd_snapshots(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["out"],
+                                   a["st"], snaps, every, a["B"], a["T"], a["H"], a["HV"], a["K"],
+                                   a["V"], a["scale"], a["chunk"], a["dtype"], None)
+    return rc, L.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("snaps,every,over,code,msg", [
+    (FAKE * 7, 0, {}, 1, "snapshot_every=0"),
+    (FAKE * 7, 48, {}, 1, "multiple of the chunk size"),
+    (FAKE * 7, -32, {}, 1, "snapshot_every"),
+    (FAKE * 7 + 8, 32, {}, 1, "snapshots is not 16-byte aligned"),
+    (3 * BIG + 256, 32, dict(q=BIG, k=2 * BIG, v=3 * BIG, g=4 * BIG, beta=5 * BIG, out=6 * BIG),
+     1, "snapshots overlap v"),
+    (6 * BIG - 64, 32, dict(q=BIG, k=2 * BIG, v=3 * BIG, g=4 * BIG, beta=5 * BIG, out=6 * BIG),
+     1, "snapshots overlap out"),
+    (7 * BIG + 64, 32, dict(q=BIG, k=2 * BIG, v=3 * BIG, g=4 * BIG, beta=5 * BIG, out=6 * BIG,
+                            st=7 * BIG), 1, "snapshots overlap final_state"),
+    (FAKE * 7, 32, dict(HV=3), 1, "kda_chunk_fwd_snapshots: HV=3"),
+])
+def test_chunk_fwd_snapshots_rejects(snaps, every, over, code, msg):
+    rc, err = snap_call(snaps, every, **over)
+    assert rc == code, err
+    assert msg in err, err
+
+
+def test_chunk_fwd_snapshots_empty_is_noop():
+    # NULL snapshots ignore snapshot_every; no tokens means no HIP call
+    rc, err = snap_call(None, 0, T=0, q=None, k=None, v=None, g=None, beta=None, out=None)
+    assert rc == 0, err
+    rc, err = snap_call(FAKE * 7, 32, B=0, q=None, k=None, v=None, g=None, beta=None, out=None)
+    assert rc == 0, err
 
 
 def test_chunk_fwd_empty_is_noop():
