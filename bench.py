@@ -12,6 +12,9 @@ Headline workload (one JSON line on stdout):
     (eps 1e-6), bounded gate -5*sigmoid(exp(A_log)(z+dt_bias)), beta logits;
     state resident in HBM and updated in place.  Reported as GB/s against the
     HBM peak.
+  * secondary lines: the GQA prefill (B8 T4096 H16 HV64), and the HV96 prefill
+    with prefix snapshots of the state every 1024 and every 32 tokens
+    (kda_chunk_fwd_snapshots; the snapshot stores count in the bytes).
 Inputs are seeded synthetic tensors (gated_delta_rule_kda_amd.synth) created on
 the GPU before the timed region.  Kernel durations come from HIP events
 recorded on the stream the kernels are launched on.  The CPU baseline runs the
@@ -130,18 +133,29 @@ def cpu_baseline(inp, shape, budget_heads=None):
             "seconds": dt}
 
 
-def bench_prefill(shape, steps, warmup, tag):
+def bench_prefill(shape, steps, warmup, tag, snapshot_every=None, inp=None):
     import torch
     import gated_delta_rule_kda_amd as kda
     from gated_delta_rule_kda_amd import synth
     dev = torch.device("cuda:0")
-    inp = synth.make_prefill_inputs(shape, dev, 0)
+    if inp is None:
+        inp = synth.make_prefill_inputs(shape, dev, 0)
     out = torch.empty(shape.B, shape.T, shape.HV, shape.V, dtype=shape.dtype, device=dev)
     ST = torch.empty(shape.B, shape.HV, shape.K, shape.V, dtype=torch.float32, device=dev)
+    snap_bytes = 0
+    if snapshot_every:
+        snaps = torch.empty(shape.B, shape.T // snapshot_every, shape.HV, shape.K, shape.V,
+                            dtype=torch.float32, device=dev)
+        snap_bytes = snaps.numel() * 4
 
-    def call():
-        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
-                      initial_state=inp["S0"], out=out, final_state=ST)
+        def call():
+            kda.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                    snapshot_every, initial_state=inp["S0"], out=out,
+                                    final_state=ST, snapshots=snaps)
+    else:
+        def call():
+            kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                          initial_state=inp["S0"], out=out, final_state=ST)
 
     for _ in range(warmup):
         call()
@@ -154,7 +168,7 @@ def bench_prefill(shape, steps, warmup, tag):
     ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     total_ms = starts[0].elapsed_time(ends[-1])
     esz = 2 if shape.dtype == torch.bfloat16 else 4
-    nbytes = prefill_alg_bytes(shape.B, shape.T, shape.H, shape.HV, shape.K, shape.V, esz)
+    nbytes = prefill_alg_bytes(shape.B, shape.T, shape.H, shape.HV, shape.K, shape.V, esz) + snap_bytes
     flops = prefill_alg_flops(shape.B, shape.T, shape.HV, shape.K, shape.V)
     avg_ms = sum(ev_ms) / len(ev_ms)
     log("[%s] prefill avg %.4f ms (min %.4f, max %.4f), span %.3f ms, wall %.3f s" % (
@@ -206,12 +220,13 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20, help="timed prefill calls")
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gqa", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy"], default=None,
+    ap.add_argument("--no-snapshots", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy", "snap"], default=None,
                     help="run one workload only (for profiler runs); prints no JSON line")
     args = ap.parse_args()
 
@@ -241,6 +256,9 @@ def main():
         return
     if args.only == "decode":
         bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup)
+        return
+    if args.only == "snap":
+        bench_prefill(synth.PREFILL_HV96_BF16, args.steps, args.warmup, "hv96 snapshots/1024", 1024)
         return
 
     shape = synth.PREFILL_HV96_BF16
@@ -286,6 +304,20 @@ def main():
             "frac_hbm": gq["bytes"] / (gq["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "alg_bytes_per_launch": gq["bytes"]}
         del gq
+    if not args.no_snapshots:
+        line["prefill_snapshots"] = []
+        for every in (1024, 32):
+            sp = bench_prefill(shape, max(3, args.steps // 2), args.warmup,
+                               "hv96 snapshots/%d" % every, every, inp=p["inp"])
+            line["prefill_snapshots"].append({
+                "workload": "kda_chunk_fwd_snapshots on the HV96 workload, a state snapshot "
+                            "every %d tokens" % every,
+                "snapshot_every": every, "tokens_per_s": sp["tokens"] / (sp["avg_ms"] * 1e-3),
+                "avg_launch_ms": sp["avg_ms"],
+                "alg_bytes_per_launch": sp["bytes"],
+                "achieved_gbs": sp["bytes"] / (sp["avg_ms"] * 1e-3) / 1e9,
+                "frac_hbm": sp["bytes"] / (sp["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS})
+            del sp
     if not args.no_decode:
         d = bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup)
         line["decode"] = {
