@@ -58,6 +58,11 @@ def _load():
             lib.kda_oracle_decode_step.argtypes = (
                 [P, P, P, L, I, D, P, P, P, I, D, P, I, P, P] + [L] * 5 + [D])
             lib.kda_oracle_decode_step.restype = I
+            lib.kda_oracle_prefill_prologue.argtypes = (
+                [P, P, P, L, I, D, P, P, P, I, D, P, I, P, P, P, P, P] + [L] * 6)
+            lib.kda_oracle_prefill_prologue.restype = I
+            lib.kda_oracle_output_gate.argtypes = [P, P, P, L, L, D]
+            lib.kda_oracle_output_gate.restype = I
             lib.kda_oracle_gate.argtypes = [P, P, P, I, D, P, L, L, L]
             lib.kda_oracle_gate.restype = I
             lib.kda_oracle_conv_update.argtypes = [P, P, P, P, L, L, L]
@@ -166,6 +171,59 @@ def kda_decode_step(x, state, H, HV, K, V, *, conv_w=None, conv_state=None,
     if rc != 0:
         raise RuntimeError("kda_oracle_decode_step failed with status %d" % rc)
     return out
+
+
+def prefill_prologue(x, H, HV, K, V, *, conv_w=None, conv_state=None, l2norm_qk=False,
+                     eps=1e-6, gate_in=None, A_log=None, dt_bias=None, gate_bounded=True,
+                     lower_bound=-5.0, beta=None, beta_is_logit=False):
+    """The decode prologue's stages over T tokens of each sequence, in fp64
+    (conv_update, l2norm_rows, bounded_gate and the beta sigmoid of the
+    "metrale_model_weights/kimi_k3_host/kda.rs" page, token after token).
+
+    x [B,T,2HK+HV*V]; gate_in [B,T,HV,K]; beta [B,T,HV]; ``conv_state``
+    (float64 [B,C,KW]) is updated in place.  Returns (q [B,T,H,K], k, v
+    [B,T,HV,V], g [B,T,HV,K], beta [B,T,HV]).
+    """
+    x = f64(x)
+    B, T, Cch = x.shape
+    assert Cch == 2 * H * K + HV * V
+    gate_in = f64(gate_in).reshape(B, T, HV, K)
+    beta = f64(beta).reshape(B, T, HV)
+    KW = 0
+    cw = None
+    if conv_w is not None:
+        cw = f64(conv_w)
+        KW = cw.shape[-1]
+        assert cw.shape == (Cch, KW)
+        assert isinstance(conv_state, np.ndarray) and conv_state.dtype == np.float64
+        assert conv_state.flags.c_contiguous and conv_state.shape == (B, Cch, KW)
+    q = np.zeros((B, T, H, K))
+    k = np.zeros((B, T, H, K))
+    v = np.zeros((B, T, HV, V))
+    g = np.zeros((B, T, HV, K))
+    bo = np.zeros((B, T, HV))
+    rc = _load().kda_oracle_prefill_prologue(
+        _ptr(x), _ptr(cw), _ptr(conv_state if cw is not None else None), KW,
+        int(bool(l2norm_qk)), float(eps), _ptr(gate_in), _ptr(f64(A_log)), _ptr(f64(dt_bias)),
+        int(bool(gate_bounded)), float(lower_bound), _ptr(beta), int(bool(beta_is_logit)),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bo), B, T, H, HV, K, V)
+    if rc != 0:
+        raise RuntimeError("kda_oracle_prefill_prologue failed with status %d" % rc)
+    return q, k, v, g, bo
+
+
+def output_gate(o, gate_in, eps):
+    """full_rank_output_gate ("kda.rs"): rows of the last dimension,
+    y = sigmoid(gate) * o / sqrt(mean(o^2) + eps)."""
+    o = f64(o)
+    gi = f64(gate_in)
+    assert gi.shape == o.shape
+    d = o.shape[-1]
+    y = np.zeros_like(o)
+    rc = _load().kda_oracle_output_gate(_ptr(o), _ptr(gi), _ptr(y), o.size // d, d, float(eps))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_output_gate failed")
+    return y
 
 
 def gate(z, A_log, dt_bias, HV, K, bounded=True, lower_bound=-5.0):

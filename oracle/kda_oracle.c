@@ -282,3 +282,87 @@ int kda_oracle_l2norm_rows(double *x, long rows, long d, double eps)
     for (r = 0; r < rows; ++r) l2norm_row(x + r * d, d, eps);
     return 0;
 }
+
+/* The stages [kda.rs] kda_decode_token runs in front of the recurrence
+ * (conv_update on the packed q | k | v channels, then in kda_recurrent_step
+ * l2norm_rows on q and k, the gate from bounded_gate, a sigmoid on beta),
+ * applied to the T tokens of each sequence in order: the per-token inputs of a
+ * whole prefill.  The conv register of each channel is carried from token to
+ * token and left in conv_state, as T decode steps would leave it.
+ *   x [B,T,C] (C = 2HK + HV V), conv_state [B,C,KW] (in/out; unused without
+ *   conv_w), gate_in [B,T,HV,K] (g itself when A_log == NULL, else z),
+ *   beta_in [B,T,HV];  outputs q, k [B,T,H,K], v [B,T,HV,V], g [B,T,HV,K],
+ *   beta_out [B,T,HV]. */
+int kda_oracle_prefill_prologue(const double *x, const double *conv_w, double *conv_state,
+                                long KW, int l2norm_qk, double eps,
+                                const double *gate_in, const double *A_log,
+                                const double *dt_bias, int gate_bounded, double lower_bound,
+                                const double *beta_in, int beta_is_logit,
+                                double *q, double *k, double *v, double *g, double *beta_out,
+                                long B, long T, long H, long HV, long K, long V)
+{
+    const long Cch = 2 * H * K + HV * V;
+    long b;
+    int status = 0;
+    if (B < 0 || T < 0 || H <= 0 || HV <= 0 || K <= 0 || V <= 0 || HV % H != 0) return 1;
+    if (conv_w && (KW < 1 || !conv_state)) return 1;
+    if (A_log && !dt_bias) return 1;
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (b = 0; b < B; ++b) {
+        double *y = (double *)malloc((size_t)Cch * sizeof(double));
+        long t, i, hv;
+        if (!y) {
+            status |= 2;
+            continue;
+        }
+        for (t = 0; t < T; ++t) {
+            const long bt = b * T + t;
+            if (conv_w)
+                conv_update(conv_state + b * Cch * KW, x + bt * Cch, conv_w, y, Cch, KW);
+            else
+                memcpy(y, x + bt * Cch, (size_t)Cch * sizeof(double));
+            if (l2norm_qk)
+                for (i = 0; i < 2 * H; ++i) l2norm_row(y + i * K, K, eps);
+            memcpy(q + bt * H * K, y, (size_t)(H * K) * sizeof(double));
+            memcpy(k + bt * H * K, y + H * K, (size_t)(H * K) * sizeof(double));
+            memcpy(v + bt * HV * V, y + 2 * H * K, (size_t)(HV * V) * sizeof(double));
+            for (hv = 0; hv < HV; ++hv) {
+                const double bl = beta_in[bt * HV + hv];
+                beta_out[bt * HV + hv] = beta_is_logit ? sigmoid(bl) : bl;
+                for (i = 0; i < K; ++i) {
+                    const long idx = (bt * HV + hv) * K + i;
+                    if (A_log) {
+                        const double decay = exp(A_log[hv]);
+                        const double xz = gate_in[idx] + dt_bias[hv * K + i];
+                        g[idx] = gate_bounded ? lower_bound * sigmoid(decay * xz)
+                                              : -decay * softplus(xz);
+                    } else {
+                        g[idx] = gate_in[idx];
+                    }
+                }
+            }
+        }
+        free(y);
+    }
+    return status;
+}
+
+/* [kda.rs] full_rank_output_gate: for each row of d values,
+ * y = sigmoid(gate) * o / sqrt(mean(o^2) + eps)  (an RMS norm of o without a
+ * learned scale, gated elementwise). */
+int kda_oracle_output_gate(const double *o, const double *gate, double *y, long rows,
+                           long d, double eps)
+{
+    long r, i;
+    if (rows < 0 || d <= 0) return 1;
+    for (r = 0; r < rows; ++r) {
+        const double *orow = o + r * d, *grow = gate + r * d;
+        double ms = 0.0, inv;
+        for (i = 0; i < d; ++i) ms += orow[i] * orow[i];
+        ms /= (double)d;
+        inv = 1.0 / sqrt(ms + eps);
+        for (i = 0; i < d; ++i) y[r * d + i] = sigmoid(grow[i]) * orow[i] * inv;
+    }
+    return 0;
+}

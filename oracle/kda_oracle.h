@@ -54,6 +54,24 @@ int kda_oracle_decode_step(const double *x, const double *conv_w, double *conv_s
                            double *out, long B, long H, long HV, long K, long V,
                            double scale);
 
+/* The decode prologue's stages applied to T tokens of each sequence in order
+ * (a prefill's per-token inputs from the raw projections):
+ *   x [B,T,2HK+HV*V]; conv_state [B,2HK+HV*V,KW] in/out; gate_in [B,T,HV,K];
+ *   beta_in [B,T,HV];  q, k [B,T,H,K], v [B,T,HV,V], g [B,T,HV,K], beta_out [B,T,HV]
+ * with the options of kda_oracle_decode_step. */
+int kda_oracle_prefill_prologue(const double *x, const double *conv_w, double *conv_state,
+                                long KW, int l2norm_qk, double eps,
+                                const double *gate_in, const double *A_log,
+                                const double *dt_bias, int gate_bounded, double lower_bound,
+                                const double *beta_in, int beta_is_logit,
+                                double *q, double *k, double *v, double *g, double *beta_out,
+                                long B, long T, long H, long HV, long K, long V);
+
+/* full_rank_output_gate ("metrale_model_weights/kimi_k3_host/kda.rs"):
+ * y = sigmoid(gate) * o / sqrt(mean(o^2) + eps) per row of d values. */
+int kda_oracle_output_gate(const double *o, const double *gate, double *y, long rows,
+                           long d, double eps);
+
 /* The decode prologue stages on their own, for pinning them separately. */
 int kda_oracle_gate(const double *z, const double *A_log, const double *dt_bias,
                     int gate_bounded, double lower_bound, double *g, long rows,

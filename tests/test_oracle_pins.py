@@ -462,3 +462,87 @@ def test_decode_prologue_composition():
         np.testing.assert_allclose(o_a, o_b, rtol=1e-13, atol=1e-15)
         np.testing.assert_allclose(st_a, st_b, rtol=1e-13, atol=1e-15)
         np.testing.assert_array_equal(cs_a, cs_b)
+
+
+# ---------------------------------------------------------------- prefill prologue, output gate
+
+def test_prefill_prologue_conv_page_example():
+    """kda.rs conv_kernel_4_state_advances over T = 4 tokens of one prefill:
+    w = 1, x_t = t + 1 on every channel; the outputs are SiLU of the running
+    sums 1, 3, 6, 10 and the register ends as [1, 2, 3, 4].  Catches a window
+    that does not carry from token to token, or runs the wrong way in time."""
+    d = json.load(open(os.path.join(GOLDEN, "kda_rs_unit_examples.json")))["conv"]
+    H = HV = d["heads"]
+    K = V = d["head_dim"]
+    KW = d["kernel"]
+    ch = 2 * H * K + HV * V
+    T = len(d["x_per_step"])
+    x = np.repeat(np.array(d["x_per_step"])[None, :, None], ch, axis=2)
+    cs = np.zeros((1, ch, KW))
+    q, k, v, _, _ = oracle.prefill_prologue(
+        x, H, HV, K, V, conv_w=np.full((ch, KW), d["weight"]), conv_state=cs,
+        gate_in=np.zeros((1, T, HV, K)), beta=np.zeros((1, T, HV)))
+    sums = np.cumsum(d["x_per_step"])
+    for t in range(T):
+        for arr in (q, k, v):
+            np.testing.assert_allclose(arr[0, t].ravel(), _silu(sums[t]), rtol=1e-15)
+    assert np.all(cs[0] == np.array(d["page_final_state_row"]))
+
+
+@pytest.mark.parametrize("bounded", [True, False])
+def test_prefill_prologue_then_fwd_equals_decode_loop(bounded):
+    """T decode steps with the full prologue (conv + SiLU, L2 norm, gate, beta
+    logits) from zero state equal the prologue over the T tokens followed by
+    the token loop: same outputs, same recurrent state, same conv register.
+    The decode step is pinned separately against the kda.rs examples."""
+    rng = np.random.default_rng(7)
+    B, T, H, HV, K, V, KW = 2, 9, 1, 2, 4, 3, 4
+    ch = 2 * H * K + HV * V
+    x = rng.standard_normal((B, T, ch))
+    w = rng.standard_normal((ch, KW))
+    z = rng.standard_normal((B, T, HV, K))
+    A_log = rng.standard_normal(HV) * 0.5
+    dt = rng.standard_normal(HV * K) * 0.5
+    bl = rng.standard_normal((B, T, HV))
+    cs0 = rng.standard_normal((B, ch, KW)) * 0.5
+    kw = dict(l2norm_qk=True, eps=1e-6, A_log=A_log, dt_bias=dt, gate_bounded=bounded,
+              lower_bound=-5.0, beta_is_logit=True)
+    st = np.zeros((B, HV, K, V))
+    cs = cs0.copy()
+    outs = []
+    for t in range(T):
+        outs.append(oracle.kda_decode_step(x[:, t], st, H, HV, K, V, conv_w=w, conv_state=cs,
+                                           gate_in=z[:, t], beta=bl[:, t], **kw))
+    cs2 = cs0.copy()
+    q, k, v, g, beta = oracle.prefill_prologue(x, H, HV, K, V, conv_w=w, conv_state=cs2,
+                                               gate_in=z, beta=bl, **kw)
+    o, S = oracle.kda_fwd(q, k, v, g, beta)
+    np.testing.assert_allclose(o, np.stack(outs, 1), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S, st, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(cs2, cs)
+
+
+def test_output_gate_closed_forms():
+    """kda.rs full_rank_output_gate: y = sigmoid(g) o / sqrt(mean(o^2) + eps).
+    o = [3, -4], g = 0, eps = 0: mean square 12.5, so y = [3, -4] / (2 sqrt 12.5);
+    g = log 3 gives sigmoid = 3/4 exactly; an all-zero row stays zero (eps > 0);
+    with eps = 0, y is invariant to scaling o by c > 0 and flips sign for c < 0.
+    Catches sum in place of mean, a missing root, tanh in place of sigmoid."""
+    o = np.array([[3.0, -4.0]])
+    y = oracle.output_gate(o, np.zeros_like(o), 0.0)
+    np.testing.assert_allclose(y, o / (2 * math.sqrt(12.5)), rtol=1e-15)
+    y = oracle.output_gate(o, np.full_like(o, math.log(3.0)), 0.0)
+    np.testing.assert_allclose(y, 0.75 * o / math.sqrt(12.5), rtol=1e-14)
+    z = oracle.output_gate(np.zeros((2, 8)), np.ones((2, 8)), 1e-6)
+    assert np.all(z == 0.0)
+    rng = np.random.default_rng(3)
+    o = rng.standard_normal((5, 16))
+    gt = rng.standard_normal((5, 16))
+    y = oracle.output_gate(o, gt, 0.0)
+    np.testing.assert_allclose(oracle.output_gate(7.5 * o, gt, 0.0), y, rtol=1e-13)
+    np.testing.assert_allclose(oracle.output_gate(-0.25 * o, gt, 0.0), -y, rtol=1e-13)
+    # with the gate saturated, every row has mean square ms / (ms + eps)
+    eps = 0.3
+    y = oracle.output_gate(o, np.full_like(o, 60.0), eps)
+    ms = np.mean(o * o, axis=1)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), ms / (ms + eps), rtol=1e-13)
