@@ -21,7 +21,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "decode_step", "abi_version", "library_path", "KDAError",
+__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
            "GATE_DIRECT", "GATE_BOUNDED", "GATE_SOFTPLUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +81,11 @@ def _load():
             lib.kda_chunk_fwd.restype = I
             lib.kda_chunk_fwd_snapshots.argtypes = [P] * 9 + [I] * 7 + [F, I, I, P]
             lib.kda_chunk_fwd_snapshots.restype = I
+            lib.kda_prefill_prologue.argtypes = ([P, P, P, ctypes.POINTER(DecodePrologue)] + [P] * 5
+                                                 + [I] * 6 + [I, P])
+            lib.kda_prefill_prologue.restype = I
+            lib.kda_output_gate.argtypes = [P, P, P, ctypes.c_longlong, I, F, I, P]
+            lib.kda_output_gate.restype = I
             lib.kda_decode_step.argtypes = [P] * 5 + [ctypes.POINTER(DecodePrologue)] + [I] * 5 + [F, I, P]
             lib.kda_decode_step.restype = I
             if lib.kda_abi_version() != ABI_VERSION:
@@ -198,6 +203,95 @@ def chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
             _ptr(final_state), B, T, H, HV, K, V, float(scale) if scale else 0.0,
             int(chunk_size), _dtype_code(q.dtype), _stream_handle(dev)))
     return out, final_state
+
+
+def _prologue_struct(C, dev, conv_weight, conv_state, l2norm_qk, l2_eps, gate_mode, A_log,
+                     dt_bias, gate_lower_bound, beta_is_logit, HV, K, B):
+    pro = DecodePrologue()
+    use = False
+    if conv_weight is not None:
+        KW = conv_weight.shape[-1]
+        _need(conv_weight, "conv_weight", torch.float32, (C, KW), dev)
+        pro.conv_weight = conv_weight.data_ptr()
+        if conv_state is not None:
+            _need(conv_state, "conv_state", torch.float32, (B, C, KW), dev)
+            pro.conv_state = conv_state.data_ptr()
+        pro.conv_kernel = KW
+        use = True
+    if l2norm_qk:
+        pro.l2norm_qk = 1
+        pro.l2_eps = float(l2_eps)
+        use = True
+    if gate_mode != GATE_DIRECT:
+        _need(A_log, "A_log", torch.float32, (HV,), dev)
+        _need(dt_bias, "dt_bias", torch.float32, (HV * K,), dev)
+        pro.gate_mode = int(gate_mode)
+        pro.A_log = A_log.data_ptr()
+        pro.dt_bias = dt_bias.data_ptr()
+        pro.gate_lower_bound = float(gate_lower_bound)
+        use = True
+    if beta_is_logit:
+        pro.beta_is_logit = 1
+        use = True
+    return pro, use
+
+
+def prefill_prologue(x, gate, beta, *, H, HV, K, V, conv_weight=None, conv_state=None,
+                     l2norm_qk=False, l2_eps=1e-6, gate_mode=GATE_DIRECT, A_log=None,
+                     dt_bias=None, gate_lower_bound=-5.0, beta_is_logit=False, out=None):
+    """``kda_prefill_prologue``: the decode prologue's stages over all T tokens.
+
+    x [B,T,2HK+HV*V] (bf16 or fp32), gate [B,T,HV,K] fp32 (g or z), beta
+    [B,T,HV] fp32 (or logits); ``conv_state`` [B,C,KW] fp32 is read and then
+    overwritten with the registers after the last token.  Returns
+    (q [B,T,H,K], k, v [B,T,HV,V] in x's dtype, g [B,T,HV,K] fp32, beta [B,T,HV] fp32)
+    -- the inputs of :func:`chunk_fwd`.  ``out`` may supply those five tensors.
+    """
+    _need(x, "x")
+    B, T = x.shape[0], x.shape[1]
+    C = 2 * H * K + HV * V
+    dt = x.dtype
+    dev = x.device
+    if tuple(x.shape) != (B, T, C):
+        raise ValueError("x has shape %s, expected %s" % (tuple(x.shape), (B, T, C)))
+    _need(gate, "gate", torch.float32, (B, T, HV, K), dev)
+    _need(beta, "beta", torch.float32, (B, T, HV), dev)
+    if out is None:
+        out = (torch.empty(B, T, H, K, dtype=dt, device=dev), torch.empty(B, T, H, K, dtype=dt, device=dev),
+               torch.empty(B, T, HV, V, dtype=dt, device=dev),
+               torch.empty(B, T, HV, K, dtype=torch.float32, device=dev),
+               torch.empty(B, T, HV, dtype=torch.float32, device=dev))
+    q, k, v, g, bo = out
+    _need(q, "q", dt, (B, T, H, K), dev)
+    _need(k, "k", dt, (B, T, H, K), dev)
+    _need(v, "v", dt, (B, T, HV, V), dev)
+    _need(g, "g", torch.float32, (B, T, HV, K), dev)
+    _need(bo, "beta_out", torch.float32, (B, T, HV), dev)
+    pro, use = _prologue_struct(C, dev, conv_weight, conv_state, l2norm_qk, l2_eps, gate_mode,
+                                A_log, dt_bias, gate_lower_bound, beta_is_logit, HV, K, B)
+    with torch.cuda.device(dev):
+        _check(_load().kda_prefill_prologue(
+            _ptr(x), _ptr(gate), _ptr(beta), ctypes.byref(pro) if use else None,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bo), B, T, H, HV, K, V,
+            _dtype_code(dt), _stream_handle(dev)))
+    return q, k, v, g, bo
+
+
+def output_gate(o, gate, eps=1e-6, *, out=None):
+    """``kda_output_gate``: y = sigmoid(gate) * o / sqrt(mean(o^2) + eps) over
+    the last dimension (the head dimension).  ``out`` may be ``o`` (in place)."""
+    _need(o, "o")
+    dev = o.device
+    D = o.shape[-1]
+    _need(gate, "gate", o.dtype, tuple(o.shape), dev)
+    if out is None:
+        out = torch.empty_like(o)
+    else:
+        _need(out, "out", o.dtype, tuple(o.shape), dev)
+    with torch.cuda.device(dev):
+        _check(_load().kda_output_gate(_ptr(o), _ptr(gate), _ptr(out), o.numel() // D, D,
+                                       float(eps), _dtype_code(o.dtype), _stream_handle(dev)))
+    return out
 
 
 def decode_step(qkv, gate, beta, state, *, H, HV, K, V, scale=None, out=None,

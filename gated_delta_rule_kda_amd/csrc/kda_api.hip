@@ -177,6 +177,113 @@ int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const f
                           chunk, dtype, stream);
 }
 
+int kda_prefill_prologue(const void *x, const float *gate, const float *beta,
+                         const kda_decode_prologue *pro, void *q, void *k, void *v,
+                         float *g, float *beta_out, int B, int T, int H, int HV, int K,
+                         int V, int dtype, void *stream) {
+    g_err[0] = '\0';
+    const char *fn = "kda_prefill_prologue";
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
+        return fail(KDA_EUNSUPPORTED, "%s: dtype %d is not KDA_DTYPE_F32 or KDA_DTYPE_BF16", fn, dtype);
+    if (B < 0 || T < 0) return fail(KDA_EINVAL, "%s: B=%d and T=%d must be >= 0", fn, B, T);
+    if (H < 1 || HV < 1) return fail(KDA_EINVAL, "%s: H=%d and HV=%d must be >= 1", fn, H, HV);
+    if (HV % H != 0) return fail(KDA_EINVAL, "%s: HV=%d is not a multiple of H=%d", fn, HV, H);
+    if (!head_dim_ok(K) || !head_dim_ok(V))
+        return fail(KDA_EUNSUPPORTED, "%s: K=%d, V=%d; each must be 32, 64 or 128", fn, K, V);
+    if (B > 65535 || 2 * static_cast<int64_t>(H) > 65535 || HV > 65535)
+        return fail(KDA_EUNSUPPORTED, "%s: B=%d, 2H=%lld and HV=%d must each be <= 65535", fn, B,
+                    2 * static_cast<long long>(H), HV);
+    kda_decode_prologue p{};
+    if (pro) p = *pro;
+    const bool conv = p.conv_weight != nullptr;
+    if (conv) {
+        if (p.conv_kernel < 1) return fail(KDA_EINVAL, "%s: conv_kernel=%d must be >= 1", fn, p.conv_kernel);
+        if (p.conv_kernel > 8)
+            return fail(KDA_EUNSUPPORTED, "%s: conv_kernel=%d; at most 8 is built", fn, p.conv_kernel);
+    }
+    if (p.gate_mode < 0 || p.gate_mode > 2)
+        return fail(KDA_EINVAL, "%s: gate_mode=%d is not a kda_gate_mode", fn, p.gate_mode);
+    if (p.gate_mode != KDA_GATE_DIRECT && (!p.A_log || !p.dt_bias))
+        return fail(KDA_EINVAL, "%s: gate_mode %d needs A_log and dt_bias", fn, p.gate_mode);
+    if (p.l2norm_qk && !(p.l2_eps >= 0.f && isfinite(p.l2_eps)))
+        return fail(KDA_EINVAL, "%s: l2_eps must be finite and >= 0", fn);
+
+    const uint64_t esz = dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const int64_t C = 2 * static_cast<int64_t>(H) * K + static_cast<int64_t>(HV) * V;
+    const int KW = conv ? p.conv_kernel : 0;
+    uint64_t nx, nq, nv, ng, nb, ncs, ncw, nal, ndt;
+    if (!count(nx, {B, T, C}) || !count(nq, {B, T, H, K}) || !count(nv, {B, T, HV, V}) ||
+        !count(ng, {B, T, HV, K}) || !count(nb, {B, T, HV}) || !count(ncs, {B, C, KW}) ||
+        !count(ncw, {C, KW}) || !count(nal, {HV}) || !count(ndt, {HV, K}) || nx >= (uint64_t(1) << 40))
+        return fail(KDA_EINVAL, "%s: tensor sizes overflow", fn);
+    if (static_cast<int64_t>(B) * T == 0) return KDA_OK;
+    if (!x || !gate || !beta || !q || !k || !v || !g || !beta_out)
+        return fail(KDA_EINVAL, "%s: x, gate, beta, q, k, v, g and beta_out must be non-NULL", fn);
+    const void *ptrs[] = {x, gate, beta, q, k, v, g, beta_out, p.conv_weight, p.conv_state, p.A_log, p.dt_bias};
+    const char *names[] = {"x", "gate", "beta", "q", "k", "v", "g", "beta_out", "conv_weight", "conv_state",
+                           "A_log", "dt_bias"};
+    for (int i = 0; i < 12; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(KDA_EINVAL, "%s: %s is not 16-byte aligned", fn, names[i]);
+    const bool gp = p.gate_mode != KDA_GATE_DIRECT;
+    const Range rs[] = {rng("x", x, nx * esz), rng("gate", gate, ng * 4), rng("beta", beta, nb * 4),
+                        rng("q", q, nq * esz), rng("k", k, nq * esz), rng("v", v, nv * esz),
+                        rng("g", g, ng * 4), rng("beta_out", beta_out, nb * 4),
+                        rng("conv_weight", p.conv_weight, ncw * 4),
+                        rng("conv_state", conv ? p.conv_state : nullptr, ncs * 4),
+                        rng("A_log", gp ? p.A_log : nullptr, nal * 4),
+                        rng("dt_bias", gp ? p.dt_bias : nullptr, ndt * 4)};
+    const int outs[] = {3, 4, 5, 6, 7, 9};
+    for (int o : outs)
+        for (int i = 0; i < 12; ++i)
+            if (i != o && overlap(rs[o], rs[i]))
+                return fail(KDA_EINVAL, "%s: %s overlaps %s", fn, rs[o].name, rs[i].name);
+
+    kda::PrologueArgs a{};
+    a.x = x; a.conv_w = conv ? p.conv_weight : nullptr;
+    a.conv_state = conv ? p.conv_state : nullptr;
+    a.conv_state_out = conv ? p.conv_state : nullptr;
+    a.KW = KW; a.l2norm = p.l2norm_qk ? 1 : 0; a.l2_eps = p.l2_eps;
+    a.gate = gate; a.gate_mode = p.gate_mode; a.A_log = p.A_log; a.dt_bias = p.dt_bias;
+    a.lower_bound = p.gate_lower_bound; a.beta_in = beta; a.beta_is_logit = p.beta_is_logit ? 1 : 0;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta_out = beta_out;
+    a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+    a.bf16 = dtype == KDA_DTYPE_BF16;
+    const hipError_t e = kda::launch_prologue(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
+int kda_output_gate(const void *o, const void *gate, void *y, long long rows, int head_dim,
+                    float eps, int dtype, void *stream) {
+    g_err[0] = '\0';
+    const char *fn = "kda_output_gate";
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
+        return fail(KDA_EUNSUPPORTED, "%s: dtype %d is not KDA_DTYPE_F32 or KDA_DTYPE_BF16", fn, dtype);
+    if (rows < 0) return fail(KDA_EINVAL, "%s: rows=%lld must be >= 0", fn, rows);
+    if (!head_dim_ok(head_dim))
+        return fail(KDA_EUNSUPPORTED, "%s: head_dim=%d must be 32, 64 or 128", fn, head_dim);
+    if (!(eps >= 0.f && isfinite(eps))) return fail(KDA_EINVAL, "%s: eps must be finite and >= 0", fn);
+    if (rows > (int64_t(1) << 40) / head_dim) return fail(KDA_EINVAL, "%s: tensor sizes overflow", fn);
+    if (rows == 0) return KDA_OK;
+    if (!o || !gate || !y) return fail(KDA_EINVAL, "%s: o, gate and y must be non-NULL", fn);
+    const void *ptrs[] = {o, gate, y};
+    const char *names[] = {"o", "gate", "y"};
+    for (int i = 0; i < 3; ++i)
+        if (!aligned16(ptrs[i])) return fail(KDA_EINVAL, "%s: %s is not 16-byte aligned", fn, names[i]);
+    const uint64_t n = static_cast<uint64_t>(rows) * head_dim * (dtype == KDA_DTYPE_BF16 ? 2 : 4);
+    const Range ro = rng("o", o, n), rg = rng("gate", gate, n), ry = rng("y", y, n);
+    if (overlap(ry, rg)) return fail(KDA_EINVAL, "%s: y overlaps gate", fn);
+    if (y != o && overlap(ry, ro)) return fail(KDA_EINVAL, "%s: y overlaps o (only y == o is allowed)", fn);
+
+    kda::OutputGateArgs a{};
+    a.o = o; a.gate = gate; a.y = y; a.rows = static_cast<long>(rows); a.D = head_dim; a.eps = eps;
+    a.bf16 = dtype == KDA_DTYPE_BF16;
+    const hipError_t e = kda::launch_output_gate(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
+}
+
 int kda_decode_step(const void *qkv, const float *gate, const float *beta, float *state,
                     void *out, const kda_decode_prologue *pro, int B, int H, int HV, int K,
                     int V, float scale, int dtype, void *stream) {

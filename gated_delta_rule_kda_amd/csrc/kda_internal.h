@@ -43,7 +43,42 @@ struct DecodeArgs {
     bool bf16;
 };
 
+// Arguments of the prefill prologue (the decode prologue's stages over T tokens).
+struct PrologueArgs {
+    const void *x;              // [B,T,C] (dtype), C = 2HK + HV V
+    const float *conv_w;        // [C,KW] or nullptr (no conv)
+    const float *conv_state;    // [B,C,KW] registers before token 0, or nullptr (zeros)
+    float *conv_state_out;      // [B,C,KW] registers after token T-1, or nullptr
+    int KW;
+    int l2norm;
+    float l2_eps;
+    const float *gate;          // [B,T,HV,K]: g, or z for the gate modes
+    int gate_mode;              // 0 direct, 1 bounded, 2 softplus
+    const float *A_log, *dt_bias;
+    float lower_bound;
+    const float *beta_in;       // [B,T,HV]
+    int beta_is_logit;
+    void *q, *k, *v;            // [B,T,H,K], [B,T,H,K], [B,T,HV,V] (dtype)
+    float *g, *beta_out;        // [B,T,HV,K], [B,T,HV]
+    int B, T, H, HV, K, V;
+    bool bf16;
+};
+
+// Arguments of the output gate: rows of D values.
+struct OutputGateArgs {
+    const void *o, *gate;       // [rows, D] (dtype)
+    void *y;                    // [rows, D] (dtype), may be o
+    long rows;
+    int D;
+    float eps;
+    bool bf16;
+};
+
+constexpr int kMaxConvKernel = 8;
+
 // Launch on `stream`; return the hipError_t of the launch.
+hipError_t launch_prologue(const PrologueArgs &a, hipStream_t stream);
+hipError_t launch_output_gate(const OutputGateArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

@@ -139,6 +139,50 @@ typedef struct kda_decode_prologue {
 } kda_decode_prologue;
 
 /*
+ * kda_prefill_prologue -- the stages of the decode prologue applied to all T
+ * tokens of a prefill at once, producing the inputs of kda_chunk_fwd from the
+ * raw projections.  Per token, in the order of kda_decode_token on the page
+ * "metrale_model_weights/kimi_k3_host/kda.rs": conv_update (causal depthwise
+ * short conv over the packed q | k | v channels, then SiLU), l2norm_rows on
+ * the q and k head rows, the gate of bounded_gate, a sigmoid on beta -- each
+ * stage as selected in `pro` (NULL: none; q, k, v are then the channels of x
+ * and g, beta pass through).
+ *
+ *   x        [B, T, 2*H*K + HV*V] dtype: q | k | v channels of every token
+ *   gate     [B, T, HV, K] fp32: g (GATE_DIRECT) or the pre-activation z
+ *   beta     [B, T, HV] fp32: beta, or its logit when pro->beta_is_logit
+ *   pro->conv_state  [B, 2*H*K + HV*V, conv_kernel] fp32 or NULL: the conv
+ *            registers before token 0 (oldest first), overwritten with those
+ *            after token T-1, so that kda_decode_step continues the sequence;
+ *            NULL means zero registers and none written
+ *   q, k     [B, T, H, K] dtype;  v [B, T, HV, V] dtype
+ *   g        [B, T, HV, K] fp32;  beta_out [B, T, HV] fp32
+ *   B, T >= 0 (either 0: no-op); H, HV >= 1, HV % H == 0; K, V in {32, 64, 128};
+ *   conv_kernel 1..8; dtype as above.
+ * Outputs may not overlap each other or any input.  The SOFTPLUS gate mode can
+ * produce g < -5, which kda_chunk_fwd does not accept (see its precondition).
+ */
+int kda_prefill_prologue(const void *x, const float *gate, const float *beta,
+                         const kda_decode_prologue *pro, void *q, void *k, void *v,
+                         float *g, float *beta_out, int B, int T, int H, int HV, int K,
+                         int V, int dtype, void *stream);
+
+/*
+ * kda_output_gate -- full_rank_output_gate of the page
+ * "metrale_model_weights/kimi_k3_host/kda.rs": for each row of head_dim values,
+ *     y = sigmoid(gate) * o / sqrt(mean(o^2) + eps)
+ * (an RMS norm of the attention output without a learned scale, gated
+ * elementwise).
+ *
+ *   o, gate, y  [rows, head_dim] dtype; y may be o itself (in place) but may
+ *               not otherwise overlap o or gate
+ *   rows >= 0 (0: no-op); head_dim in {32, 64, 128}; eps >= 0 and finite
+ *   (with eps = 0 an all-zero row gives NaN).
+ */
+int kda_output_gate(const void *o, const void *gate, void *y, long long rows, int head_dim,
+                    float eps, int dtype, void *stream);
+
+/*
  * kda_decode_step -- one token of the recurrence for B sequences, state
  * updated in place.
  *

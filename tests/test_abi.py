@@ -28,7 +28,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"kda_abi_version", "kda_last_error", "kda_chunk_fwd",
-                          "kda_chunk_fwd_snapshots", "kda_decode_step"}
+                          "kda_chunk_fwd_snapshots", "kda_prefill_prologue", "kda_output_gate",
+                          "kda_decode_step"}
     L = ctypes.CDLL(kda.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -205,3 +206,74 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 4, 1, 32)
     with pytest.raises(ValueError, match="GPU"):
         kda.chunk_fwd(q, q, q, q, torch.zeros(1, 4, 1))
+
+
+def prologue_call(pro=None, **over):
+    a = dict(x=FAKE, gate=FAKE * 2, beta=FAKE * 3, q=FAKE * 4, k=FAKE * 5, v=FAKE * 6, g=FAKE * 7,
+             bo=FAKE * 8, B=1, T=8, H=2, HV=4, K=32, V=32, dtype=1)
+    a.update(over)
+    L = lib()
+    rc = L.kda_prefill_prologue(a["x"], a["gate"], a["beta"], ctypes.byref(pro) if pro else None,
+                                a["q"], a["k"], a["v"], a["g"], a["bo"], a["B"], a["T"], a["H"],
+                                a["HV"], a["K"], a["V"], a["dtype"], None)
+    return rc, L.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(HV=3), 1, "multiple"),
+    (dict(K=48), 2, "32, 64 or 128"),
+    (dict(dtype=5), 2, "dtype"),
+    (dict(T=-1), 1, ">= 0"),
+    (dict(x=None), 1, "non-NULL"),
+    (dict(g=FAKE * 7 + 4), 1, "g is not 16-byte aligned"),
+    (dict(x=BIG, gate=2 * BIG, beta=3 * BIG, q=4 * BIG, k=5 * BIG, v=6 * BIG, g=7 * BIG,
+          bo=2 * BIG + 64), 1, "beta_out overlaps gate"),
+    (dict(x=BIG, gate=2 * BIG, beta=3 * BIG, q=4 * BIG, k=4 * BIG + 256, v=6 * BIG, g=7 * BIG,
+          bo=8 * BIG), 1, "q overlaps k"),
+])
+def test_prefill_prologue_rejects(over, code, msg):
+    rc, err = prologue_call(**over)
+    assert rc == code, err
+    assert msg in err, err
+
+
+@pytest.mark.parametrize("pro,code,msg", [
+    (dict(conv_weight=FAKE * 9, conv_kernel=0), 1, "conv_kernel=0"),
+    (dict(conv_weight=FAKE * 9, conv_kernel=9), 2, "at most 8"),
+    (dict(gate_mode=1), 1, "needs A_log"),
+    (dict(gate_mode=4), 1, "kda_gate_mode"),
+    (dict(l2norm_qk=1, l2_eps=-1.0), 1, "l2_eps"),
+])
+def test_prefill_prologue_struct_rejects(pro, code, msg):
+    p = kda.DecodePrologue()
+    for kk, vv in pro.items():
+        setattr(p, kk, vv)
+    rc, err = prologue_call(pro=p)
+    assert rc == code, err
+    assert msg in err, err
+
+
+def test_prefill_prologue_empty_is_noop():
+    rc, err = prologue_call(T=0, x=None, gate=None, beta=None, q=None, k=None, v=None, g=None, bo=None)
+    assert rc == 0, err
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    (dict(D=48), 2, "head_dim"),
+    (dict(rows=-1), 1, "rows"),
+    (dict(eps=float("nan")), 1, "eps"),
+    (dict(eps=-1.0), 1, "eps"),
+    (dict(dtype=3), 2, "dtype"),
+    (dict(o=None), 1, "non-NULL"),
+    (dict(y=FAKE * 3 + 8), 1, "y is not 16-byte aligned"),
+    (dict(y=FAKE * 2 + 64), 1, "y overlaps gate"),
+    (dict(y=FAKE + 64), 1, "y overlaps o"),
+])
+def test_output_gate_rejects(args, code, msg):
+    a = dict(o=FAKE, gate=FAKE * 2, y=FAKE * 3, rows=4, D=32, eps=1e-6, dtype=1)
+    a.update(args)
+    L = lib()
+    rc = L.kda_output_gate(a["o"], a["gate"], a["y"], a["rows"], a["D"], a["eps"], a["dtype"], None)
+    err = L.kda_last_error().decode()
+    assert rc == code, err
+    assert msg in err, err
