@@ -14,7 +14,9 @@ Headline workload (one JSON line on stdout):
     HBM peak.
   * secondary lines: the GQA prefill (B8 T4096 H16 HV64), and the HV96 prefill
     with prefix snapshots of the state every 1024 and every 32 tokens
-    (kda_chunk_fwd_snapshots; the snapshot stores count in the bytes).
+    (kda_chunk_fwd_snapshots; the snapshot stores count in the bytes), and the
+    layer's per-token stages on the HV96 shape (kda_prefill_prologue,
+    kda_output_gate) against the HBM peak.
 Inputs are seeded synthetic tensors (gated_delta_rule_kda_amd.synth) created on
 the GPU before the timed region.  Kernel durations come from HIP events
 recorded on the stream the kernels are launched on.  The CPU baseline runs the
@@ -216,6 +218,59 @@ def bench_decode(shape, steps, warmup):
     return dict(span_ms=span_ms, per_ms=per_ms, bytes=nbytes, gbs=gbs)
 
 
+def prologue_alg_bytes(B, T, H, HV, K, V, KW, esz):
+    """Bytes of kda_prefill_prologue read or written once: x, z, beta in; q, k,
+    v, g, beta out; conv weights, conv registers in and out, A_log, dt_bias."""
+    C = 2 * H * K + HV * V
+    return (B * T * C * esz * 2 + B * T * HV * K * 4 * 2 + B * T * HV * 4 * 2
+            + C * KW * 4 + B * C * KW * 4 * 2 + HV * 4 + HV * K * 4)
+
+
+def bench_layer_stages(steps, warmup):
+    """kda_prefill_prologue and kda_output_gate on the HV96 layer shape."""
+    import torch
+    import gated_delta_rule_kda_amd as kda
+    dev = torch.device("cuda:0")
+    B, T, H, HV, K, V, KW = 1, 8192, 96, 96, 128, 128, 4
+    C = 2 * H * K + HV * V
+    gen = torch.Generator(device=dev).manual_seed(0)
+    r = lambda *s_: torch.randn(*s_, generator=gen, device=dev)
+    x = r(B, T, C).to(torch.bfloat16)
+    conv_w, conv_state = r(C, KW) * 0.5, r(B, C, KW)
+    z, A_log, dt_bias, bl = r(B, T, HV, K), r(HV) * 0.5, r(HV * K) * 0.5, r(B, T, HV)
+    outs = (torch.empty(B, T, H, K, dtype=torch.bfloat16, device=dev),
+            torch.empty(B, T, H, K, dtype=torch.bfloat16, device=dev),
+            torch.empty(B, T, HV, V, dtype=torch.bfloat16, device=dev),
+            torch.empty(B, T, HV, K, device=dev), torch.empty(B, T, HV, device=dev))
+    o = r(B, T, HV, V).to(torch.bfloat16)
+    og = r(B, T, HV, V).to(torch.bfloat16)
+    y = torch.empty_like(o)
+
+    def pro():
+        kda.prefill_prologue(x, z, bl, H=H, HV=HV, K=K, V=V, conv_weight=conv_w,
+                             conv_state=conv_state, l2norm_qk=True, l2_eps=1e-6,
+                             gate_mode=kda.GATE_BOUNDED, A_log=A_log, dt_bias=dt_bias,
+                             gate_lower_bound=-5.0, beta_is_logit=True, out=outs)
+
+    def gate():
+        kda.output_gate(o, og, 1e-6, out=y)
+
+    res = {}
+    stream = torch.cuda.current_stream(dev)
+    for name, fn, nbytes in (("prologue", pro, prologue_alg_bytes(B, T, H, HV, K, V, KW, 2)),
+                             ("output_gate", gate, 3 * o.numel() * 2)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        starts, ends = time_calls(fn, steps, stream)
+        torch.cuda.synchronize()
+        ms = sum(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)) / steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log("[%s] avg %.4f ms, %.1f GB/s" % (name, ms, gbs))
+        res[name] = dict(avg_ms=ms, bytes=nbytes, gbs=gbs)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,7 +281,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gqa", action="store_true")
     ap.add_argument("--no-snapshots", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy", "snap"], default=None,
+    ap.add_argument("--no-layer-stages", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy", "snap", "stages"], default=None,
                     help="run one workload only (for profiler runs); prints no JSON line")
     args = ap.parse_args()
 
@@ -256,6 +312,9 @@ def main():
         return
     if args.only == "decode":
         bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup)
+        return
+    if args.only == "stages":
+        bench_layer_stages(args.steps, args.warmup)
         return
     if args.only == "snap":
         bench_prefill(synth.PREFILL_HV96_BF16, args.steps, args.warmup, "hv96 snapshots/1024", 1024)
@@ -318,6 +377,20 @@ def main():
                 "achieved_gbs": sp["bytes"] / (sp["avg_ms"] * 1e-3) / 1e9,
                 "frac_hbm": sp["bytes"] / (sp["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS})
             del sp
+    if not args.no_layer_stages:
+        st = bench_layer_stages(args.steps, args.warmup)
+        line["layer_stages"] = {
+            "workload": "the HV96 layer's per-token stages, B1 T8192 H=HV=96 K=V=128 bf16: "
+                        "kda_prefill_prologue (conv width 4 + SiLU, L2 norm, bounded gate, beta "
+                        "logits, conv registers in and out) and kda_output_gate on o",
+            "prologue": {"avg_launch_ms": st["prologue"]["avg_ms"],
+                         "alg_bytes_per_launch": st["prologue"]["bytes"],
+                         "achieved_gbs": st["prologue"]["gbs"],
+                         "frac_hbm": st["prologue"]["gbs"] / HBM_PEAK_GBS},
+            "output_gate": {"avg_launch_ms": st["output_gate"]["avg_ms"],
+                            "alg_bytes_per_launch": st["output_gate"]["bytes"],
+                            "achieved_gbs": st["output_gate"]["gbs"],
+                            "frac_hbm": st["output_gate"]["gbs"] / HBM_PEAK_GBS}}
     if not args.no_decode:
         d = bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup)
         line["decode"] = {

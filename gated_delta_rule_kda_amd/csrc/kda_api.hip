@@ -190,9 +190,8 @@ int kda_prefill_prologue(const void *x, const float *gate, const float *beta,
     if (HV % H != 0) return fail(KDA_EINVAL, "%s: HV=%d is not a multiple of H=%d", fn, HV, H);
     if (!head_dim_ok(K) || !head_dim_ok(V))
         return fail(KDA_EUNSUPPORTED, "%s: K=%d, V=%d; each must be 32, 64 or 128", fn, K, V);
-    if (B > 65535 || 2 * static_cast<int64_t>(H) > 65535 || HV > 65535)
-        return fail(KDA_EUNSUPPORTED, "%s: B=%d, 2H=%lld and HV=%d must each be <= 65535", fn, B,
-                    2 * static_cast<long long>(H), HV);
+    if (B > 65535 || T > 65535 * 256)
+        return fail(KDA_EUNSUPPORTED, "%s: B=%d must be <= 65535 and T=%d <= 16776960", fn, B, T);
     kda_decode_prologue p{};
     if (pro) p = *pro;
     const bool conv = p.conv_weight != nullptr;

@@ -45,14 +45,20 @@ __device__ __forceinline__ void load8(const void *base, size_t i, float (&x)[8])
     }
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// (a, b) -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 template <bool BF16>
 __device__ __forceinline__ void store8(void *base, size_t i, const float (&y)[8]) {
     if constexpr (BF16) {
         uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            w[e] = static_cast<uint32_t>(float_to_bf16_bits(y[2 * e])) |
-                   (static_cast<uint32_t>(float_to_bf16_bits(y[2 * e + 1])) << 16);
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16(y[2 * e], y[2 * e + 1]);
         *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + i) = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
         *reinterpret_cast<float4 *>(static_cast<float *>(base) + i) = make_float4(y[0], y[1], y[2], y[3]);
@@ -61,18 +67,32 @@ __device__ __forceinline__ void store8(void *base, size_t i, const float (&y)[8]
 }
 
 __device__ __forceinline__ float sigmoid_acc(float x) { return 1.0f / (1.0f + expf(-x)); }
+// x * sigmoid(x) from the hardware exponential and reciprocal (a few ulp;
+// 0 for x -> -inf, x for x -> +inf)
+__device__ __forceinline__ float silu_fast(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
-// Sum over the LPR consecutive lanes that hold one row (LPR a power of two <= 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// Sum over the LPR consecutive lanes that hold one row (LPR 4, 8 or 16; the
+// groups are aligned within the 16-lane DPP rows): xor 1 and xor 2 inside
+// each quad, then the mirrored quad of the half row, then the mirrored half.
 template <int LPR>
 __device__ __forceinline__ float row_sum(float s) {
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o, 64);
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16, "row of 4, 8 or 16 lanes");
+    s += dpp<0xb1>(s);                        // quad_perm [1,0,3,2]
+    s += dpp<0x4e>(s);                        // quad_perm [2,3,0,1]
+    if constexpr (LPR >= 8) s += dpp<0x141>(s);   // row_half_mirror
+    if constexpr (LPR >= 16) s += dpp<0x140>(s);  // row_mirror
     return s;
 }
 
 // One launch covers `nseg` head rows of D channels each, starting at channel
 // c_base of x: rows s < split go to out0 (head s of `heads0`), the others to
-// out1 (head s - split).  Grid: (token tiles, nseg, B).
+// out1 (head s - split).  Grid: (nseg, token tiles, B): workgroups that run
+// together cover neighbouring head rows of the same tokens, so their 256-byte
+// row pieces fill whole DRAM pages.
 struct RowLaunch {
     int c_base, nseg, split, heads0, heads1;
     void *out0, *out1;
@@ -87,8 +107,8 @@ __global__ __launch_bounds__(kRowThreads) void prologue_rows_kernel(PrologueArgs
     static_assert(R >= 1 && kTile % RUNS == 0, "tile must split into runs");
     const int C = 2 * a.H * a.K + a.HV * a.V;
     const int lr = threadIdx.x % LPR, run = threadIdx.x / LPR;
-    const int s = blockIdx.y, b = blockIdx.z;
-    const int t0 = blockIdx.x * kTile + run * R;
+    const int s = blockIdx.x, b = blockIdx.z;
+    const int t0 = blockIdx.y * kTile + run * R;
     if (t0 >= a.T) return;
     const int c = L.c_base + s * D + lr * 8;         // first of this lane's 8 channels
     void *out = s < L.split ? L.out0 : L.out1;
@@ -96,56 +116,61 @@ __global__ __launch_bounds__(kRowThreads) void prologue_rows_kernel(PrologueArgs
     const int heads = s < L.split ? L.heads0 : L.heads1;
     const bool conv = a.conv_w != nullptr;
 
-    float w[8][KW], win[8][KW];
+    // h[i] holds token t0 - (KW - 1) + i: KW - 1 rows of history, then the R
+    // rows of the run, all loaded up front (rows past the end re-read the last
+    // row and are not stored), so every load of the run is in flight at once
+    // and the conv reads fixed registers (no window shifts)
+    constexpr int NH = KW - 1;
+    float h[NH + R][8];
+    float w[8][KW];
     if (conv) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
 #pragma unroll
             for (int j = 0; j < KW; ++j) w[e][j] = a.conv_w[static_cast<size_t>(c + e) * KW + j];
-        // window before token t0: slot i holds x_{t0 - KW + i} (slot 0 is shifted
-        // out by the first token); tokens before 0 come from the conv state, whose
-        // slot KW + t holds x_t for t = -1 .. -(KW - 1)
+        // tokens before 0 come from the conv registers, whose slot KW + t holds
+        // x_t for t = -1 .. -(KW - 1)
 #pragma unroll
-        for (int i = 1; i < KW; ++i) {
-            const int t = t0 - KW + i;
-            float xv[8];
+        for (int i = 0; i < NH; ++i) {
+            const int t = t0 - NH + i;
             if (t >= 0) {
-                load8<BF16>(a.x, (static_cast<size_t>(b) * a.T + t) * C + c, xv);
+                load8<BF16>(a.x, (static_cast<size_t>(b) * a.T + t) * C + c, h[i]);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    xv[e] = a.conv_state ? a.conv_state[(static_cast<size_t>(b) * C + c + e) * KW + KW + t] : 0.f;
+                    h[i][e] = a.conv_state ? a.conv_state[(static_cast<size_t>(b) * C + c + e) * KW + KW + t] : 0.f;
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) win[e][i] = xv[e];
         }
     }
-    const int tend = min(t0 + R, a.T);
-    for (int t = t0; t < tend; ++t) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        load8<BF16>(a.x, (static_cast<size_t>(b) * a.T + min(t0 + r, a.T - 1)) * C + c, h[NH + r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int t = t0 + r;
         float y[8];
-        load8<BF16>(a.x, (static_cast<size_t>(b) * a.T + t) * C + c, y);
         if (conv) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-#pragma unroll
-                for (int j = 0; j + 1 < KW; ++j) win[e][j] = win[e][j + 1];
-                win[e][KW - 1] = y[e];
                 float acc = 0.f;
 #pragma unroll
-                for (int j = 0; j < KW; ++j) acc = fmaf(w[e][j], win[e][j], acc);
-                y[e] = acc * sigmoid_acc(acc);
+                for (int j = 0; j < KW; ++j) acc = fmaf(w[e][j], h[r + j][e], acc);
+                y[e] = silu_fast(acc);
             }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = h[NH + r][e];
         }
         if (L.l2) {
             float ss = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
             ss = row_sum<LPR>(ss);
-            const float inv = 1.0f / sqrtf(ss + a.l2_eps);
+            const float inv = __frsqrt_rn(ss + a.l2_eps);
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] *= inv;
         }
-        store8<BF16>(out, ((static_cast<size_t>(b) * a.T + t) * heads + head) * D + lr * 8, y);
+        if (t < a.T) store8<BF16>(out, ((static_cast<size_t>(b) * a.T + t) * heads + head) * D + lr * 8, y);
     }
 }
 
@@ -164,9 +189,11 @@ __global__ __launch_bounds__(kRowThreads) void prologue_gate_kernel(PrologueArgs
             for (int e = 0; e < 4; ++e) g[e] = zz[e];
         } else {
             const float decay = expf(a.A_log[hv]);
+            const float4 db = *reinterpret_cast<const float4 *>(a.dt_bias + hv * a.K + f0);
+            const float dd[4] = {db.x, db.y, db.z, db.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float xz = zz[e] + a.dt_bias[hv * a.K + f0 + e];
+                const float xz = zz[e] + dd[e];
                 if (a.gate_mode == 1)
                     g[e] = a.lower_bound * sigmoid_acc(decay * xz);
                 else   // -decay * softplus(xz), softplus in its overflow-safe form
@@ -231,7 +258,7 @@ __global__ __launch_bounds__(kRowThreads) void output_gate_kernel(OutputGateArgs
 
 template <int D, bool BF16>
 hipError_t launch_rows_d(const PrologueArgs &a, const RowLaunch &L, hipStream_t stream) {
-    const dim3 grid((a.T + kTile - 1) / kTile, L.nseg, a.B);
+    const dim3 grid(L.nseg, (a.T + kTile - 1) / kTile, a.B);
     switch (a.conv_w ? a.KW : 1) {
 #define KDA_KW(n) case n: hipLaunchKernelGGL((prologue_rows_kernel<D, n, BF16>), grid, dim3(kRowThreads), 0, stream, a, L); break;
         KDA_KW(1) KDA_KW(2) KDA_KW(3) KDA_KW(4) KDA_KW(5) KDA_KW(6) KDA_KW(7) KDA_KW(8)
