@@ -21,7 +21,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
+__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "recurrent_fwd", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
            "GATE_DIRECT", "GATE_BOUNDED", "GATE_SOFTPLUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +79,8 @@ def _load():
             lib.kda_last_error.restype = ctypes.c_char_p
             lib.kda_chunk_fwd.argtypes = [P] * 8 + [I] * 6 + [F, I, I, P]
             lib.kda_chunk_fwd.restype = I
+            lib.kda_recurrent_fwd.argtypes = [P] * 8 + [I] * 6 + [F, I, P]
+            lib.kda_recurrent_fwd.restype = I
             lib.kda_chunk_fwd_snapshots.argtypes = [P] * 9 + [I] * 7 + [F, I, I, P]
             lib.kda_chunk_fwd_snapshots.restype = I
             lib.kda_prefill_prologue.argtypes = ([P, P, P, ctypes.POINTER(DecodePrologue)] + [P] * 5
@@ -182,6 +184,21 @@ def chunk_fwd_snapshots(q, k, v, g, beta, snapshot_every, scale=None, initial_st
             float(scale) if scale else 0.0, int(chunk_size), _dtype_code(q.dtype),
             _stream_handle(dev)))
     return out, final_state, snapshots
+
+
+def recurrent_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
+                  *, out=None, final_state=None):
+    """``kda_recurrent_fwd``: :func:`chunk_fwd`'s computation for gates without
+    a lower bound (any finite g), token by token with the state on chip."""
+    (B, T, H, HV, K, V), out, final_state = _prefill_args(
+        q, k, v, g, beta, initial_state, output_final_state, out, final_state)
+    dev = q.device
+    with torch.cuda.device(dev):
+        _check(_load().kda_recurrent_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(out),
+            _ptr(final_state), B, T, H, HV, K, V, float(scale) if scale else 0.0,
+            _dtype_code(q.dtype), _stream_handle(dev)))
+    return out, final_state
 
 
 def chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,

@@ -76,7 +76,7 @@ namespace {
 int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, const float *g,
                    const float *beta, const float *initial_state, void *out, float *final_state,
                    float *snapshots, int snapshot_every, int B, int T, int H, int HV, int K,
-                   int V, float scale, int chunk, int dtype, void *stream) {
+                   int V, float scale, int chunk, int dtype, void *stream, bool recurrent = false) {
     g_err[0] = '\0';
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
         return fail(KDA_EUNSUPPORTED, "%s: dtype %d is not KDA_DTYPE_F32 or KDA_DTYPE_BF16", fn, dtype);
@@ -150,7 +150,7 @@ int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, 
     a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
     a.scale = scale;
     a.bf16 = dtype == KDA_DTYPE_BF16;
-    const hipError_t e = kda::launch_prefill(a, st);
+    const hipError_t e = recurrent ? kda::launch_recurrent(a, st) : kda::launch_prefill(a, st);
     if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KDA_OK;
 }
@@ -175,6 +175,14 @@ int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const f
     return chunk_fwd_impl("kda_chunk_fwd_snapshots", q, k, v, g, beta, initial_state, out,
                           final_state, snapshots, snapshot_every, B, T, H, HV, K, V, scale,
                           chunk, dtype, stream);
+}
+
+int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const float *initial_state, void *out,
+                      float *final_state, int B, int T, int H, int HV, int K, int V,
+                      float scale, int dtype, void *stream) {
+    return chunk_fwd_impl("kda_recurrent_fwd", q, k, v, g, beta, initial_state, out, final_state,
+                          nullptr, 0, B, T, H, HV, K, V, scale, 0, dtype, stream, true);
 }
 
 int kda_prefill_prologue(const void *x, const float *gate, const float *beta,

@@ -78,6 +78,7 @@ constexpr int kMaxConvKernel = 8;
 
 // Launch on `stream`; return the hipError_t of the launch.
 hipError_t launch_prologue(const PrologueArgs &a, hipStream_t stream);
+hipError_t launch_recurrent(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_output_gate(const OutputGateArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream);

@@ -1,0 +1,300 @@
+// KDA forward as the token recurrence itself, for gfx950: the prefill path for
+// gates without a lower bound.
+//
+// The chunked kernels factor every within-chunk decay product around a
+// reference row, which needs g >= -5 (the bounded gate) to stay inside fp32.
+// A gate such as -exp(A_log) * softplus(z + dt_bias) (the page
+// "metrale_model_weights/kimi_k3_host/kda.rs", bounded_gate without a lower
+// bound) has no such bound.  This kernel runs the four-step update of the page
+// "K3/notes/sections/sec-01.tex" (section "KDA 递归核心") token by token --
+//     S_dec = exp(g) (.) S,  r = v - k^T S_dec,  S = S_dec + (beta k) (x) r,
+//     o = scale q^T S
+// -- with the state on chip for the whole sequence, so only exp(g) of single
+// tokens is ever formed and any finite g is exact.  The readout uses
+// q^T S = q^T S_dec + (q.k) beta r, so one reduction per token gives both
+// k^T S_dec and q^T S_dec.
+//
+// Work decomposition: one workgroup of 4 waves per (b, hv, 32 state columns);
+// lane = (column, row group), 8 row groups of K/8 rows.  The 8 lanes of a
+// column are half a DPP row, so the per-token column sums are three DPP steps.
+// Tokens are staged 16 at a time in LDS (k, scale q, exp(g) as fp32 rows, v of
+// the workgroup's columns, beta, q.k), shared by the 8 waves, and the next
+// round's inputs are loaded into registers while the current round runs.
+
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kTC = 16;        // tokens staged per round
+constexpr int kRG = 8;         // lanes (row groups) per state column
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kWGCols = kThreads / kRG;   // state columns per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// sum over the 8 lanes of one half DPP row (the lanes of one state column)
+__device__ __forceinline__ float col_sum8(float s) {
+    s += dpp<0xb1>(s);    // quad_perm [1,0,3,2]
+    s += dpp<0x4e>(s);    // quad_perm [2,3,0,1]
+    s += dpp<0x141>(s);   // row_half_mirror
+    return s;
+}
+// sum over the 16 lanes of one DPP row
+__device__ __forceinline__ float row_sum16(float s) {
+    s = col_sum8(s);
+    s += dpp<0x140>(s);   // row_mirror
+    return s;
+}
+
+__device__ __forceinline__ float load_io(const void *p, size_t i, bool bf16) {
+    return bf16 ? bf16_bits_to_float(static_cast<const uint16_t *>(p)[i]) : static_cast<const float *>(p)[i];
+}
+// 4 consecutive elements as loaded (bf16: two packed words; fp32: a float4)
+template <bool BF16> struct Raw4;
+template <> struct Raw4<true> { uint2 u; };
+template <> struct Raw4<false> { float4 f; };
+// Raw buffer resource over `bytes` bytes from `p`: out-of-range loads read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+template <bool BF16>
+__device__ __forceinline__ Raw4<BF16> load_raw4(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+    if constexpr (BF16) {
+        const auto u = __builtin_amdgcn_raw_buffer_load_b64(rs, byte_off, 0, 0);
+        return Raw4<true>{make_uint2(u[0], u[1])};
+    } else {
+        const auto u = __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0);
+        return Raw4<false>{make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]),
+                                       __uint_as_float(u[2]), __uint_as_float(u[3]))};
+    }
+}
+template <bool BF16>
+__device__ __forceinline__ Raw4<BF16> zero_raw4() {
+    if constexpr (BF16)
+        return Raw4<true>{make_uint2(0u, 0u)};
+    else
+        return Raw4<false>{make_float4(0.f, 0.f, 0.f, 0.f)};
+}
+template <bool BF16>
+__device__ __forceinline__ float4 widen(const Raw4<BF16> &r) {
+    if constexpr (BF16)
+        return make_float4(__uint_as_float(r.u.x << 16), __uint_as_float(r.u.x & 0xffff0000u),
+                           __uint_as_float(r.u.y << 16), __uint_as_float(r.u.y & 0xffff0000u));
+    else
+        return r.f;
+}
+
+template <int K, bool BF16>
+__global__ __launch_bounds__(kThreads) void recurrent_kernel(PrefillArgs a) {
+    constexpr int RPL = K / kRG;                // state rows per lane
+    constexpr int LD = K + 4;                   // padded fp32 rows of the staged tokens
+    constexpr int NP = kTC * K / 4;             // 4-element pieces of one staged [kTC][K] array
+    static_assert(NP % kThreads == 0 || NP < kThreads, "pieces split over the threads");
+    constexpr int NPT = NP < kThreads ? 1 : NP / kThreads;     // pieces per thread
+    constexpr int NVT = kTC * kWGCols / kThreads;               // v values per thread
+    static_assert(NVT * kThreads == kTC * kWGCols, "v values split over the threads");
+    __shared__ __attribute__((aligned(16))) float sK[kTC][LD];
+    __shared__ __attribute__((aligned(16))) float sQ[kTC][LD];
+    __shared__ __attribute__((aligned(16))) float sD[kTC][LD];
+    __shared__ float sV[kTC][kWGCols], sB[kTC], sQK[kTC], sO[kTC][kWGCols];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = wave * (64 / kRG) + lane / kRG;     // this lane's column within the workgroup
+    const int rg = lane % kRG;
+    const int ncb = a.V / kWGCols;
+    const int cb = blockIdx.x % ncb, bhv = blockIdx.x / ncb;
+    const int b = bhv / a.HV, hv = bhv % a.HV;
+    const int h = hv / (a.HV / a.H);
+    const int c0 = cb * kWGCols;
+    const int r0 = rg * RPL;
+    const size_t tok_b = static_cast<size_t>(b) * a.T;
+
+    float S[RPL];
+    const size_t st_off = (static_cast<size_t>(b) * a.HV + hv) * K * a.V;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) S[r] = a.S0 ? a.S0[st_off + static_cast<size_t>(r0 + r) * a.V + c0 + c] : 0.f;
+
+    // ---- the next round's inputs (one 4-element piece of q, k and g, one v
+    // and one beta per thread), prefetched into registers while the current
+    // round runs; tokens past the end are a no-op step (k = q = 0, g = 0,
+    // v = beta = 0)
+    Raw4<BF16> pk[NPT], pq[NPT];
+    float4 pg[NPT];
+    uint32_t pv[NVT];
+    float pb = 0.f;
+    constexpr int ESZ = BF16 ? 2 : 4;
+    // Loads go through buffer resources that cover exactly the round's valid
+    // tokens: tokens past the end read 0 (k = q = 0, g = 0 so exp(g) = 1,
+    // v = beta = 0: a no-op step) with no branches around the loads, so no
+    // register copy has to wait for them.
+    auto load_round = [&](int t0) {
+        const int nv = min(kTC, a.T - t0);
+        const size_t tb = tok_b + t0;
+        auto span = [&](int stride, int rowlen, int esz) -> uint32_t {
+            return nv > 0 ? static_cast<uint32_t>(((nv - 1) * stride + rowlen) * esz) : 0u;
+        };
+        const auto rk = make_rsrc(static_cast<const char *>(a.k) + ((tb * a.H + h) * K) * ESZ, span(a.H * K, K, ESZ));
+        const auto rq = make_rsrc(static_cast<const char *>(a.q) + ((tb * a.H + h) * K) * ESZ, span(a.H * K, K, ESZ));
+        const auto rgr = make_rsrc(a.g + (tb * a.HV + hv) * K, span(a.HV * K, K, 4));
+        const auto rv = make_rsrc(static_cast<const char *>(a.v) + ((tb * a.HV + hv) * a.V + c0) * ESZ,
+                                  span(a.HV * a.V, kWGCols, ESZ));
+        const auto rb = make_rsrc(a.beta + tb * a.HV + hv, span(a.HV, 1, 4));
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int e = min(tid + i * kThreads, NP - 1);
+            const int t = e / (K / 4), f = (e % (K / 4)) * 4;
+            pk[i] = load_raw4<BF16>(rk, (t * a.H * K + f) * ESZ);
+            pq[i] = load_raw4<BF16>(rq, (t * a.H * K + f) * ESZ);
+            const auto gg = __builtin_amdgcn_raw_buffer_load_b128(rgr, (t * a.HV * K + f) * 4, 0, 0);
+            pg[i] = make_float4(__uint_as_float(gg[0]), __uint_as_float(gg[1]), __uint_as_float(gg[2]),
+                                __uint_as_float(gg[3]));
+        }
+#pragma unroll
+        for (int i = 0; i < NVT; ++i) {
+            const int e = tid + i * kThreads, t = e / kWGCols, cc = e % kWGCols;
+            if constexpr (BF16)
+                pv[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, (t * a.HV * a.V + cc) * 2, 0, 0);
+            else
+                pv[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, (t * a.HV * a.V + cc) * 4, 0, 0);
+        }
+        pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (tid & (kTC - 1)) * a.HV * 4, 0, 0));
+    };
+    // registers -> LDS (q scaled, exp(g) from the hardware exponential), then q.k per token
+    auto store_round = [&]() {
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int e = tid + i * kThreads;
+            if (e < NP) {
+                const int t = e / (K / 4), f = (e % (K / 4)) * 4;
+                const float4 q = widen<BF16>(pq[i]), g = pg[i];
+                *reinterpret_cast<float4 *>(&sK[t][f]) = widen<BF16>(pk[i]);
+                *reinterpret_cast<float4 *>(&sQ[t][f]) = make_float4(a.scale * q.x, a.scale * q.y, a.scale * q.z, a.scale * q.w);
+                *reinterpret_cast<float4 *>(&sD[t][f]) = make_float4(exp2f(g.x * kLog2e), exp2f(g.y * kLog2e),
+                                                                    exp2f(g.z * kLog2e), exp2f(g.w * kLog2e));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NVT; ++i) {
+            const int e = tid + i * kThreads;
+            sV[e / kWGCols][e % kWGCols] = BF16 ? __uint_as_float(pv[i] << 16) : __uint_as_float(pv[i]);
+        }
+        if (tid < kTC) sB[tid] = pb;
+        __syncthreads();
+        // q.k of each staged token: 16 lanes per token
+        if (tid < 16 * kTC) {
+            const int t = tid / 16, part = tid % 16;
+            float s = 0.f;
+#pragma unroll
+            for (int f = part; f < K; f += 16) s = fmaf(sQ[t][f], sK[t][f], s);
+            s = row_sum16(s);
+            if (part == 0) sQK[t] = s;
+        }
+        __syncthreads();
+    };
+    // one token's operands, read from LDS a token ahead of their use so that
+    // the LDS latency is off the token-to-token dependency chain
+    struct Tok {
+        float d[RPL], k[RPL], q[RPL];
+        float v, b, qk;
+    };
+    auto read_tok = [&](int t, Tok &x) {
+        if constexpr (RPL >= 4) {
+#pragma unroll
+            for (int r = 0; r < RPL; r += 4) {
+                const float4 d4 = *reinterpret_cast<const float4 *>(&sD[t][r0 + r]);
+                const float4 k4 = *reinterpret_cast<const float4 *>(&sK[t][r0 + r]);
+                const float4 q4 = *reinterpret_cast<const float4 *>(&sQ[t][r0 + r]);
+                x.d[r] = d4.x; x.d[r + 1] = d4.y; x.d[r + 2] = d4.z; x.d[r + 3] = d4.w;
+                x.k[r] = k4.x; x.k[r + 1] = k4.y; x.k[r + 2] = k4.z; x.k[r + 3] = k4.w;
+                x.q[r] = q4.x; x.q[r + 1] = q4.y; x.q[r + 2] = q4.z; x.q[r + 3] = q4.w;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                x.d[r] = sD[t][r0 + r];
+                x.k[r] = sK[t][r0 + r];
+                x.q[r] = sQ[t][r0 + r];
+            }
+        }
+        x.v = sV[t][c];
+        x.b = sB[t];
+        x.qk = sQK[t];
+    };
+    // one token: decay, k^T S_dec and q^T S_dec (over the column's 8 lanes),
+    // the rank-1 write, and the readout
+    auto step = [&](int t, const Tok &x) {
+        float p0 = 0.f, p1 = 0.f, w0 = 0.f, w1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            S[r] *= x.d[r];                                          // decay
+            if (r & 1) { p1 = fmaf(x.k[r], S[r], p1); w1 = fmaf(x.q[r], S[r], w1); }
+            else       { p0 = fmaf(x.k[r], S[r], p0); w0 = fmaf(x.q[r], S[r], w0); }
+        }
+        const float p = col_sum8(p0 + p1), w = col_sum8(w0 + w1);
+        const float u = x.b * (x.v - p);                             // beta r
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) S[r] = fmaf(x.k[r], u, S[r]);  // rank-1 write
+        if (rg == 0) sO[t][c] = fmaf(x.qk, u, w);                    // q^T S = q^T S_dec + (q.k) beta r
+    };
+
+    load_round(0);
+    store_round();
+    for (int t0 = 0; t0 < a.T; t0 += kTC) {
+        load_round(t0 + kTC);                              // in flight during this round
+        const int nt = min(kTC, a.T - t0);
+        // two operand sets alternate (even and odd tokens), so no copies
+        Tok x0, x1;
+        read_tok(0, x0);
+        for (int t = 0; t < nt; t += 2) {
+            if (t + 1 < nt) read_tok(t + 1, x1);
+            step(t, x0);
+            if (t + 1 < nt) {
+                if (t + 2 < nt) read_tok(t + 2, x0);
+                step(t + 1, x1);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NVT; ++i) {
+            const int e = tid + i * kThreads, t = e / kWGCols, cc = e % kWGCols;
+            if (t < nt) {
+                const size_t oi = ((tok_b + t0 + t) * a.HV + hv) * a.V + c0 + cc;
+                if (BF16)
+                    static_cast<uint16_t *>(a.out)[oi] = float_to_bf16_bits(sO[t][cc]);
+                else
+                    static_cast<float *>(a.out)[oi] = sO[t][cc];
+            }
+        }
+        if (t0 + kTC < a.T) store_round();                 // the prefetched round to LDS
+    }
+    if (a.ST) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) a.ST[st_off + static_cast<size_t>(r0 + r) * a.V + c0 + c] = S[r];
+    }
+}
+
+template <int K>
+hipError_t launch_k(const PrefillArgs &a, hipStream_t stream) {
+    const unsigned grid = static_cast<unsigned>(a.B) * a.HV * (a.V / kWGCols);
+    if (a.bf16)
+        hipLaunchKernelGGL((recurrent_kernel<K, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((recurrent_kernel<K, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_recurrent(const PrefillArgs &a, hipStream_t stream) {
+    if (a.B == 0 || a.T == 0) return hipSuccess;
+    if (a.K == 32) return launch_k<32>(a, stream);
+    if (a.K == 64) return launch_k<64>(a, stream);
+    if (a.K == 128) return launch_k<128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

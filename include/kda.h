@@ -89,6 +89,24 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                   float scale, int chunk, int dtype, void *stream);
 
 /*
+ * kda_recurrent_fwd -- the same computation and interface as kda_chunk_fwd
+ * (without the chunk size), for gates with no lower bound.
+ *
+ * It runs the recurrence of the page "K3/notes/sections/sec-01.tex" (section
+ * "KDA 递归核心") one token at a time with the state kept on chip, so it takes
+ * exp(g) of single tokens only and is exact for any finite g -- for instance
+ * the unbounded gate -exp(A_log) * softplus(z + dt_bias) of bounded_gate on
+ * the page "metrale_model_weights/kimi_k3_host/kda.rs" (no lower bound),
+ * which kda_chunk_fwd's -5 <= g <= 0 precondition excludes.  Slower than
+ * kda_chunk_fwd where both apply.  Arguments, layouts, aliasing rules and
+ * return codes are those of kda_chunk_fwd.
+ */
+int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const float *initial_state, void *out,
+                      float *final_state, int B, int T, int H, int HV, int K, int V,
+                      float scale, int dtype, void *stream);
+
+/*
  * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also writes prefix snapshots
  * of the state, so that decoding can later resume from any whole multiple of
  * snapshot_every tokens (the prefix cache of the page

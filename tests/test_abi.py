@@ -28,8 +28,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"kda_abi_version", "kda_last_error", "kda_chunk_fwd",
-                          "kda_chunk_fwd_snapshots", "kda_prefill_prologue", "kda_output_gate",
-                          "kda_decode_step"}
+                          "kda_chunk_fwd_snapshots", "kda_recurrent_fwd", "kda_prefill_prologue",
+                          "kda_output_gate", "kda_decode_step"}
     L = ctypes.CDLL(kda.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -274,6 +274,24 @@ def test_output_gate_rejects(args, code, msg):
     a.update(args)
     L = lib()
     rc = L.kda_output_gate(a["o"], a["gate"], a["y"], a["rows"], a["D"], a["eps"], a["dtype"], None)
+    err = L.kda_last_error().decode()
+    assert rc == code, err
+    assert msg in err, err
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(HV=3), 1, "kda_recurrent_fwd: HV=3"),
+    (dict(K=16), 2, "32, 64 or 128"),
+    (dict(q=None), 1, "non-NULL"),
+    (dict(q=BIG, k=2 * BIG, v=3 * BIG, g=4 * BIG, beta=5 * BIG, out=3 * BIG + 64), 1, "out overlaps v"),
+])
+def test_recurrent_fwd_rejects(over, code, msg):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, s0=None, out=FAKE * 6,
+             st=None, B=1, T=8, H=2, HV=4, K=32, V=32, scale=0.0, dtype=1)
+    a.update(over)
+    L = lib()
+    rc = L.kda_recurrent_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["out"], a["st"],
+                             a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["scale"], a["dtype"], None)
     err = L.kda_last_error().decode()
     assert rc == code, err
     assert msg in err, err
