@@ -16,7 +16,8 @@ Headline workload (one JSON line on stdout):
     with prefix snapshots of the state every 1024 and every 32 tokens
     (kda_chunk_fwd_snapshots; the snapshot stores count in the bytes), and the
     layer's per-token stages on the HV96 shape (kda_prefill_prologue,
-    kda_output_gate) against the HBM peak.
+    kda_output_gate) against the HBM peak, and kda_recurrent_fwd on the HV96
+    workload with an unbounded gate (against the fp32 vector peak).
 Inputs are seeded synthetic tensors (gated_delta_rule_kda_amd.synth) created on
 the GPU before the timed region.  Kernel durations come from HIP events
 recorded on the stream the kernels are launched on.  The CPU baseline runs the
@@ -39,6 +40,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
+FP32_VALU_PEAK = 157.3e12      # MI355X fp32 vector, FLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
@@ -135,7 +137,7 @@ def cpu_baseline(inp, shape, budget_heads=None):
             "seconds": dt}
 
 
-def bench_prefill(shape, steps, warmup, tag, snapshot_every=None, inp=None):
+def bench_prefill(shape, steps, warmup, tag, snapshot_every=None, inp=None, recurrent=False):
     import torch
     import gated_delta_rule_kda_amd as kda
     from gated_delta_rule_kda_amd import synth
@@ -154,6 +156,10 @@ def bench_prefill(shape, steps, warmup, tag, snapshot_every=None, inp=None):
             kda.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                                     snapshot_every, initial_state=inp["S0"], out=out,
                                     final_state=ST, snapshots=snaps)
+    elif recurrent:
+        def call():
+            kda.recurrent_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                              initial_state=inp["S0"], out=out, final_state=ST)
     else:
         def call():
             kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
@@ -282,7 +288,9 @@ def main():
     ap.add_argument("--no-gqa", action="store_true")
     ap.add_argument("--no-snapshots", action="store_true")
     ap.add_argument("--no-layer-stages", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy", "snap", "stages"], default=None,
+    ap.add_argument("--no-unbounded", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy", "snap", "stages", "unbounded"],
+                    default=None,
                     help="run one workload only (for profiler runs); prints no JSON line")
     args = ap.parse_args()
 
@@ -312,6 +320,11 @@ def main():
         return
     if args.only == "decode":
         bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup)
+        return
+    if args.only == "unbounded":
+        sh = synth.PREFILL_HV96_BF16
+        bench_prefill(sh, args.steps, args.warmup, "hv96 unbounded gate, recurrent",
+                      inp=synth.make_prefill_inputs(sh, "cuda:0", 0, g_heavy=True), recurrent=True)
         return
     if args.only == "stages":
         bench_layer_stages(args.steps, args.warmup)
@@ -377,6 +390,21 @@ def main():
                 "achieved_gbs": sp["bytes"] / (sp["avg_ms"] * 1e-3) / 1e9,
                 "frac_hbm": sp["bytes"] / (sp["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS})
             del sp
+    if not args.no_unbounded:
+        uinp = dict(p["inp"])
+        uinp["g"] = synth.make_prefill_inputs(shape, "cuda:0", 0, g_heavy=True)["g"]
+        ub = bench_prefill(shape, max(3, args.steps // 4), min(args.warmup, 3), "hv96 unbounded gate, recurrent",
+                           inp=uinp, recurrent=True)
+        del uinp
+        tf = ub["flops"] / (ub["avg_ms"] * 1e-3) / 1e12
+        line["prefill_unbounded_gate"] = {
+            "workload": "kda_recurrent_fwd on the HV96 workload with g = -exp(1.5 N(0,1)) (no lower bound; "
+                        "outside kda_chunk_fwd's -5 <= g <= 0)",
+            "tokens_per_s": ub["tokens"] / (ub["avg_ms"] * 1e-3), "avg_launch_ms": ub["avg_ms"],
+            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": tf * 1e12 / FP32_VALU_PEAK,
+                         "flops_per_launch": ub["flops"]}}
+        del ub
     if not args.no_layer_stages:
         st = bench_layer_stages(args.steps, args.warmup)
         line["layer_stages"] = {

@@ -66,8 +66,10 @@ def _gen(device, seed):
 
 
 def make_prefill_inputs(shape: PrefillShape, device="cpu", seed: int = 0,
-                        g_lower: float | None = None):
-    """Return dict(q, k, v, g, beta, S0) on ``device`` following the recipe above."""
+                        g_lower: float | None = None, g_heavy: bool = False):
+    """Return dict(q, k, v, g, beta, S0) on ``device`` following the recipe above.
+    ``g_heavy`` draws g = -exp(1.5 N(0,1)) instead (no lower bound: median -1,
+    about 5 % below -12, 0.1 % below -100), the range of an unbounded gate."""
     B, T, H, HV, K, V = shape.B, shape.T, shape.H, shape.HV, shape.K, shape.V
     lower = shape.g_lower if g_lower is None else g_lower
     gen = _gen(device, seed)
@@ -76,6 +78,8 @@ def make_prefill_inputs(shape: PrefillShape, device="cpu", seed: int = 0,
     k = F.normalize(torch.randn(B, T, H, K, **f32), dim=-1)
     v = torch.randn(B, T, HV, V, **f32)
     g = lower * torch.sigmoid(torch.randn(B, T, HV, K, **f32))
+    if g_heavy:
+        g = -torch.exp(1.5 * torch.randn(B, T, HV, K, **f32))
     beta = torch.sigmoid(torch.randn(B, T, HV, **f32))
     if shape.s0 == "normal":
         S0 = shape.s0_std * torch.randn(B, HV, K, V, **f32)
