@@ -8,6 +8,9 @@ library's kernels.  torch supplies device memory and streams.
     o, S_T = chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                        output_final_state=False)
     o, S_T, snaps = chunk_fwd_snapshots(q, k, v, g, beta, snapshot_every, ...)
+    o, S_T = recurrent_fwd(q, k, v, g, beta, ...)        # any g (unbounded gate)
+    q, k, v, g, beta = prefill_prologue(x, z, beta_logits, H=..., ...)
+    y = output_gate(o, gate, eps)
     out = decode_step(qkv, gate, beta, state, H=..., ...)   # state updated in place
 
 There is no CPU fallback: calling an op without the built library, or with

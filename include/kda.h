@@ -70,7 +70,8 @@ const char *kda_last_error(void);
  *   g             [B, T, HV, K]  fp32, log-space decay; PRECONDITION -5 <= g <= 0
  *                                (the lower bound of the bounded gate).  Values
  *                                below -5 are not detected and can overflow the
- *                                in-chunk exponent factorisation.
+ *                                in-chunk exponent factorisation; gates without
+ *                                that bound go to kda_recurrent_fwd.
  *   beta          [B, T, HV]     fp32, write strength used as given
  *   initial_state [B, HV, K, V]  fp32 or NULL (zeros)
  *   out           [B, T, HV, V]  dtype; must not overlap any input
