@@ -71,9 +71,11 @@ __device__ __forceinline__ float sigmoid_acc(float x) { return 1.0f / (1.0f + ex
 // 0 for x -> -inf, x for x -> +inf)
 __device__ __forceinline__ float silu_fast(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
+// x of another lane (DPP); the 0 that stands for lanes without a source lets
+// the compiler fold the move into the add that consumes it
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 // Sum over the LPR consecutive lanes that hold one row (LPR 4, 8 or 16; the
 // groups are aligned within the 16-lane DPP rows): xor 1 and xor 2 inside
