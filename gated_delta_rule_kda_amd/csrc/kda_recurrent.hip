@@ -37,6 +37,10 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kWGCols = kThreads / kRG;   // state columns per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
+// 2^x by the hardware exponential alone, without the library's rescaling for
+// results below the normal range (1 ulp; such a result may come out as 0, an
+// absolute change of less than 2^-126 in a decay factor)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 // x of another lane (DPP); the 0 that stands for lanes without a source lets the
 // compiler fold the move into the add that consumes it
 template <int CTRL>
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(PrefillArgs a) {
         }
         pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (tid & (kTC - 1)) * a.HV * 4, 0, 0));
     };
-    // registers -> LDS: k, scale q, exp(g) (hardware exponential), v, beta,
+    // registers -> LDS: k, scale q, exp(g), v, beta,
     // and the partial sums of (scale q).k
     auto store_round = [&]() {
 #pragma unroll
@@ -200,8 +204,8 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(PrefillArgs a) {
                 const float4 qs = make_float4(a.scale * q.x, a.scale * q.y, a.scale * q.z, a.scale * q.w);
                 *reinterpret_cast<float4 *>(&sK[t][f]) = k;
                 *reinterpret_cast<float4 *>(&sQ[t][f]) = qs;
-                *reinterpret_cast<float4 *>(&sD[t][f]) = make_float4(exp2f(g.x * kLog2e), exp2f(g.y * kLog2e),
-                                                                    exp2f(g.z * kLog2e), exp2f(g.w * kLog2e));
+                *reinterpret_cast<float4 *>(&sD[t][f]) = make_float4(ex2(g.x * kLog2e), ex2(g.y * kLog2e),
+                                                                    ex2(g.z * kLog2e), ex2(g.w * kLog2e));
                 float s = fmaf(qs.x, k.x, fmaf(qs.y, k.y, fmaf(qs.z, k.z, qs.w * k.w)));
                 s += dpp<0xb1>(s);    // quad_perm [1,0,3,2]
                 s += dpp<0x4e>(s);    // quad_perm [2,3,0,1]
