@@ -122,3 +122,28 @@ def test_full_size_hv96_unbounded_sampled():
         assert_close(o[:, :, hv:hv + 1], oref, torch.bfloat16, True, "HV96 unbounded o head %d" % hv)
         assert_close(S[:, hv:hv + 1], Sref, torch.bfloat16, False, "HV96 unbounded S head %d" % hv)
         say("   head", hv, "ok")
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_recurrent_prefix_and_resume_bitwise(dt):
+    """Each token's step depends on earlier tokens only, and tokens past the
+    end of a sequence are exact no-ops, so (a) the outputs of a prefix do not
+    change when later tokens are appended, and (b) running a sequence in two
+    calls, the second resuming from the first one's final state, reproduces
+    the single call bit for bit (outputs and final state), whatever the split
+    point."""
+    shape = synth.PrefillShape(2, 53, 2, 4, 64, 32, dt, "normal", s0_std=0.3)
+    inp = synth.make_prefill_inputs(shape, DEV, 11)
+    inp["g"] = unbounded_gate(shape.B, shape.T, shape.HV, shape.K, 12).to(DEV)
+    sl = lambda x, a, b: x[:, a:b].contiguous()
+    args = lambda a, b: (sl(inp["q"], a, b), sl(inp["k"], a, b), sl(inp["v"], a, b),
+                         sl(inp["g"], a, b), sl(inp["beta"], a, b))
+    o_full, S_full = kda.recurrent_fwd(*args(0, 53), initial_state=inp["S0"], output_final_state=True)
+    for split in (1, 16, 21, 32, 52):
+        say("   split at", split)
+        o1, S1 = kda.recurrent_fwd(*args(0, split), initial_state=inp["S0"], output_final_state=True)
+        o2, S2 = kda.recurrent_fwd(*args(split, 53), initial_state=S1, output_final_state=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o_full[:, :split]), "prefix outputs changed (split %d)" % split
+        assert torch.equal(o2, o_full[:, split:]), "resumed outputs differ (split %d)" % split
+        assert torch.equal(S2, S_full), "resumed final state differs (split %d)" % split
