@@ -55,6 +55,8 @@ def _load():
             lib.kda_oracle_fwd.restype = I
             lib.kda_oracle_fwd_snapshots.argtypes = [P] * 9 + [L] * 7 + [D]
             lib.kda_oracle_fwd_snapshots.restype = I
+            lib.kda_oracle_bwd.argtypes = [P] * 14 + [L] * 6 + [D]
+            lib.kda_oracle_bwd.restype = I
             lib.kda_oracle_decode_step.argtypes = (
                 [P, P, P, L, I, D, P, P, P, I, D, P, I, P, P] + [L] * 5 + [D])
             lib.kda_oracle_decode_step.restype = I
@@ -129,6 +131,40 @@ def kda_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state
     if snapshot_every is not None:
         return o, (S if output_final_state else None), snaps
     return o, (S if output_final_state else None)
+
+
+def kda_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initial_state=None):
+    """Gradients of kda_fwd in fp64 by back-propagation through time, as the
+    backward of KDAFunction on the "K3/kda/ops/reference/recurrent.py" page
+    derives them, with the gradient of the initial state kept.
+
+    dout [B,T,HV,V] is dL/do, d_final_state [B,HV,K,V] (or None = 0) is
+    dL/dS_T.  Returns (dq, dk [B,T,H,K], dv [B,T,HV,V], dg [B,T,HV,K],
+    dbeta [B,T,HV], dS0 [B,HV,K,V]).
+    """
+    q, k, v, g, beta, do = (f64(a) for a in (q, k, v, g, beta, dout))
+    S0, dST = f64(initial_state), f64(d_final_state)
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    assert k.shape == q.shape and v.shape[:2] == (B, T) and do.shape == v.shape
+    assert g.shape == (B, T, HV, K) and beta.shape == (B, T, HV)
+    for st in (S0, dST):
+        if st is not None:
+            assert st.shape == (B, HV, K, V)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    dq = np.zeros((B, T, H, K))
+    dk = np.zeros((B, T, H, K))
+    dv = np.zeros((B, T, HV, V))
+    dg = np.zeros((B, T, HV, K))
+    db = np.zeros((B, T, HV))
+    dS0 = np.zeros((B, HV, K, V))
+    rc = _load().kda_oracle_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(do), _ptr(dST),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dS0), B, T, H, HV, K, V, float(scale))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_bwd failed with status %d" % rc)
+    return dq, dk, dv, dg, db, dS0
 
 
 def kda_decode_step(x, state, H, HV, K, V, *, conv_w=None, conv_state=None,

@@ -140,6 +140,147 @@ int kda_oracle_fwd_snapshots(const double *q, const double *k, const double *v,
     return status;
 }
 
+/* Gradients of the forward pass: back-propagation through time over the time
+ * loop of [recurrent.py], the backward its docstring derives (KDAFunction in
+ * [recurrent.py]), with the gradient of the initial state kept (the page's
+ * backward drops it).  For a loss L with dL/do = dout ([B,T,HV,V]) and
+ * dL/dS_T = dS_T ([B,HV,K,V], NULL = 0):
+ *   forward, per (b, hv) chain: S_dec_t = exp(g_t) (.) S_{t-1},
+ *     r_t = v_t - k_t^T S_dec_t,  a_t = beta_t k_t,  S_t = S_dec_t + a_t (x) r_t,
+ *     o_t = qs_t^T S_t with qs_t = scale q_t;
+ *   backward, t = T-1 .. 0, with D (= dL/dS_t, starting at dS_T):
+ *     D += qs_t (x) dout_t             (the readout)
+ *     dqs_t = S_t dout_t               (dq_t = scale dqs_t)
+ *     da_t = D r_t,  dr_t = a_t^T D    (the rank-1 write)
+ *     dbeta_t = k_t . da_t,  dk_t = beta_t da_t - S_dec_t dr_t,  dv_t = dr_t
+ *     D_dec = D - k_t (x) dr_t         (r_t = v_t - k_t^T S_dec_t)
+ *     dg_t = sum over V of S_dec_t (.) D_dec
+ *     D = exp(g_t) (.) D_dec           (the decay)
+ *   dS0 = D after t = 0.
+ * GQA: q/k head h serves value heads h*G .. h*G+G-1 (G = HV/H), so dq and dk
+ * of head h sum over them (the repeat_interleave of [recurrent.py] reversed).
+ * Every array is row-major as in kda_oracle_fwd; dS_out may be NULL.  The
+ * forward states of a chain are kept (T*K*V doubles per chain at a time). */
+int kda_oracle_bwd(const double *q, const double *k, const double *v,
+                   const double *g, const double *beta, const double *S0,
+                   const double *dout, const double *dST,
+                   double *dq, double *dk, double *dv, double *dg, double *dbeta,
+                   double *dS_out, long B, long T, long H, long HV, long K, long V,
+                   double scale)
+{
+    long bh;
+    int status = 0;
+    const long G = (H > 0 && HV % H == 0) ? HV / H : 0;
+    if (B < 0 || T < 0 || H <= 0 || HV <= 0 || K <= 0 || V <= 0 || G == 0) return 1;
+    if (!(scale > 0.0)) scale = 1.0 / sqrt((double)K);
+    memset(dq, 0, (size_t)(B * T * H * K) * sizeof(double));
+    memset(dk, 0, (size_t)(B * T * H * K) * sizeof(double));
+
+    /* one q/k head (and its G value heads, one after another) per iteration,
+     * so that the GQA sums into dq and dk need no synchronisation */
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (bh = 0; bh < B * H; ++bh) {
+        const long b = bh / H, h = bh % H;
+        const long KV = K * V;
+        double *Sdec = (double *)malloc((size_t)(T > 0 ? T : 1) * KV * sizeof(double));
+        double *R = (double *)malloc((size_t)(T > 0 ? T : 1) * V * sizeof(double));
+        double *S = (double *)malloc((size_t)KV * sizeof(double));
+        double *D = (double *)malloc((size_t)KV * sizeof(double));
+        double *da = (double *)malloc((size_t)K * sizeof(double));
+        double *dr = (double *)malloc((size_t)V * sizeof(double));
+        long j, t, i, c;
+        if (!Sdec || !R || !S || !D || !da || !dr) {
+            status |= 2;
+        } else {
+            for (j = 0; j < G; ++j) {
+                const long hv = h * G + j, chain = b * HV + hv;
+                /* forward, keeping S_dec_t and r_t */
+                if (S0) memcpy(S, S0 + chain * KV, (size_t)KV * sizeof(double));
+                else memset(S, 0, (size_t)KV * sizeof(double));
+                for (t = 0; t < T; ++t) {
+                    const long tok = b * T + t;
+                    const double *kt = k + (tok * H + h) * K;
+                    const double *vt = v + (tok * HV + hv) * V;
+                    const double *gt = g + (tok * HV + hv) * K;
+                    const double bt = beta[tok * HV + hv];
+                    double *Sd = Sdec + t * KV, *rt = R + t * V;
+                    for (i = 0; i < K; ++i) {
+                        const double d = exp(gt[i]);
+                        for (c = 0; c < V; ++c) Sd[i * V + c] = d * S[i * V + c];
+                    }
+                    for (c = 0; c < V; ++c) {
+                        double p = 0.0;
+                        for (i = 0; i < K; ++i) p += kt[i] * Sd[i * V + c];
+                        rt[c] = vt[c] - p;
+                    }
+                    for (i = 0; i < K; ++i)
+                        for (c = 0; c < V; ++c) S[i * V + c] = Sd[i * V + c] + bt * kt[i] * rt[c];
+                }
+                /* backward */
+                if (dST) memcpy(D, dST + chain * KV, (size_t)KV * sizeof(double));
+                else memset(D, 0, (size_t)KV * sizeof(double));
+                for (t = T - 1; t >= 0; --t) {
+                    const long tok = b * T + t;
+                    const double *qt = q + (tok * H + h) * K;
+                    const double *kt = k + (tok * H + h) * K;
+                    const double *gt = g + (tok * HV + hv) * K;
+                    const double *dot = dout + (tok * HV + hv) * V;
+                    const double bt = beta[tok * HV + hv];
+                    const double *Sd = Sdec + t * KV, *rt = R + t * V;
+                    double *dqt = dq + (tok * H + h) * K, *dkt = dk + (tok * H + h) * K;
+                    double db = 0.0;
+                    /* the readout: D += qs (x) dout, dqs = S_t dout */
+                    for (i = 0; i < K; ++i) {
+                        const double qs = scale * qt[i];
+                        double acc = 0.0;
+                        for (c = 0; c < V; ++c) {
+                            const double St = Sd[i * V + c] + bt * kt[i] * rt[c];
+                            D[i * V + c] += qs * dot[c];
+                            acc += St * dot[c];
+                        }
+                        dqt[i] += scale * acc;
+                    }
+                    /* the write S_t = S_dec + a (x) r: da = D r, dr = a^T D */
+                    for (i = 0; i < K; ++i) {
+                        double acc = 0.0;
+                        for (c = 0; c < V; ++c) acc += D[i * V + c] * rt[c];
+                        da[i] = acc;
+                        db += kt[i] * acc;
+                    }
+                    for (c = 0; c < V; ++c) {
+                        double acc = 0.0;
+                        for (i = 0; i < K; ++i) acc += bt * kt[i] * D[i * V + c];
+                        dr[c] = acc;
+                        dv[(tok * HV + hv) * V + c] = acc;
+                    }
+                    dbeta[tok * HV + hv] = db;
+                    /* the residual r = v - k^T S_dec, then the decay */
+                    for (i = 0; i < K; ++i) {
+                        const double e = exp(gt[i]);
+                        double acc_k = 0.0, acc_g = 0.0;
+                        for (c = 0; c < V; ++c) {
+                            const double Dd = D[i * V + c] - kt[i] * dr[c];
+                            acc_k += Sd[i * V + c] * dr[c];
+                            acc_g += Sd[i * V + c] * Dd;
+                            D[i * V + c] = e * Dd;
+                        }
+                        dkt[i] += bt * da[i] - acc_k;
+                        dg[(tok * HV + hv) * K + i] = acc_g;
+                    }
+                }
+                if (dS_out) memcpy(dS_out + chain * KV, D, (size_t)KV * sizeof(double));
+            }
+        }
+        free(Sdec);
+        free(R);
+        free(S);
+        free(D);
+        free(da);
+        free(dr);
+    }
+    return status;
+}
+
 /* [kda.rs] sigmoid and softplus (softplus written in its overflow-safe form
  * max(x,0) + log1p(exp(-|x|)), as on the page). */
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }

@@ -35,6 +35,18 @@ int kda_oracle_fwd_snapshots(const double *q, const double *k, const double *v,
                              long B, long T, long H, long HV, long K, long V,
                              double scale);
 
+/* Gradients of kda_oracle_fwd by back-propagation through time: from dL/do
+ * (dout [B,T,HV,V]) and dL/dS_T (dST [B,HV,K,V], NULL = 0) to dq, dk
+ * [B,T,H,K], dv [B,T,HV,V], dg [B,T,HV,K], dbeta [B,T,HV] and dS_out
+ * [B,HV,K,V] (NULL = not written).  Keeps the T forward states of one chain
+ * at a time. */
+int kda_oracle_bwd(const double *q, const double *k, const double *v,
+                   const double *g, const double *beta, const double *S0,
+                   const double *dout, const double *dST,
+                   double *dq, double *dk, double *dv, double *dg, double *dbeta,
+                   double *dS_out, long B, long T, long H, long HV, long K, long V,
+                   double scale);
+
 /* One decode token for B sequences ("metrale_model_weights/kimi_k3_host/kda.rs",
  * kda_decode_token / kda_recurrent_step), with every prologue stage optional:
  *   x          [B, 2*H*K + HV*V]  packed q | k | v channels (before the conv)

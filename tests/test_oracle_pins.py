@@ -546,3 +546,103 @@ def test_output_gate_closed_forms():
     y = oracle.output_gate(o, np.full_like(o, 60.0), eps)
     ms = np.mean(o * o, axis=1)
     np.testing.assert_allclose(np.mean(y * y, axis=1), ms / (ms + eps), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- backward
+
+def _loss(inp, Wo, WS, scale=None):
+    """L = sum(o * Wo) + sum(S_T * WS), by the forward oracle."""
+    o, S = oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                          scale=scale, initial_state=inp["S0"])
+    return float((o * Wo).sum() + (S * WS).sum())
+
+
+@pytest.mark.parametrize("with_dST", [True, False])
+def test_backward_matches_finite_differences(with_dST):
+    """Every gradient of kda_bwd against central differences of the forward
+    oracle, entry by entry (GQA, nonzero S0, unnormalised q and k)."""
+    B, T, H, HV, K, V = 2, 5, 1, 2, 3, 2
+    rng = np.random.default_rng(7)
+    inp = dict(q=rng.standard_normal((B, T, H, K)), k=rng.standard_normal((B, T, H, K)),
+               v=rng.standard_normal((B, T, HV, V)), g=-2.0 * rng.random((B, T, HV, K)),
+               beta=rng.random((B, T, HV)), S0=rng.standard_normal((B, HV, K, V)))
+    Wo = rng.standard_normal((B, T, HV, V))
+    WS = rng.standard_normal((B, HV, K, V)) if with_dST else np.zeros((B, HV, K, V))
+    grads = oracle.kda_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], Wo,
+                           WS if with_dST else None, initial_state=inp["S0"])
+    h = 1e-6
+    for name, grad in zip(("q", "k", "v", "g", "beta", "S0"), grads):
+        x = inp[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = _loss(inp, Wo, WS)
+            x[idx] = keep - h
+            lm = _loss(inp, Wo, WS)
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7, err_msg="d" + name)
+
+
+def test_backward_explicit_scale():
+    """A given scale enters dq linearly and the other gradients through o."""
+    B, T, H, HV, K, V = 1, 4, 2, 2, 3, 3
+    rng = np.random.default_rng(8)
+    inp = dict(q=rng.standard_normal((B, T, H, K)), k=rng.standard_normal((B, T, H, K)),
+               v=rng.standard_normal((B, T, HV, V)), g=-rng.random((B, T, HV, K)),
+               beta=rng.random((B, T, HV)), S0=None)
+    Wo = rng.standard_normal((B, T, HV, V))
+    WS = np.zeros((B, HV, K, V))
+    dq = oracle.kda_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], Wo, scale=0.7)[0]
+    h = 1e-6
+    idx = (0, 2, 1, 2)
+    inp["q"][idx] += h
+    lp = _loss(inp, Wo, WS, scale=0.7)
+    inp["q"][idx] -= 2 * h
+    lm = _loss(inp, Wo, WS, scale=0.7)
+    assert abs(dq[idx] - (lp - lm) / (2 * h)) < 1e-7
+
+
+def test_backward_empty_sequence_and_beta_zero():
+    """T = 0: dS0 = dS_T and nothing else.  beta = 0: nothing is written, so
+    dL/dv = 0 exactly, and dS0 = exp(sum of g) (.) dS_T + sum over t of
+    exp(G_t) (.) (s q_t (x) dout_t)  (the state only decays)."""
+    rng = np.random.default_rng(9)
+    B, H, HV, K, V = 1, 1, 1, 3, 2
+    dST = rng.standard_normal((B, HV, K, V))
+    z = lambda *s: np.zeros(s)
+    dq, dk, dv, dg, db, dS0 = oracle.kda_bwd(z(B, 0, H, K), z(B, 0, H, K), z(B, 0, HV, V), z(B, 0, HV, K),
+                                             z(B, 0, HV), z(B, 0, HV, V), dST, initial_state=z(B, HV, K, V))
+    assert dq.size == 0 and dv.size == 0 and dg.size == 0 and db.size == 0
+    np.testing.assert_array_equal(dS0, dST)
+    T = 4
+    q, k = rng.standard_normal((B, T, H, K)), rng.standard_normal((B, T, H, K))
+    v, g = rng.standard_normal((B, T, HV, V)), -rng.random((B, T, HV, K))
+    do = rng.standard_normal((B, T, HV, V))
+    dq, dk, dv, dg, db, dS0 = oracle.kda_bwd(q, k, v, g, np.zeros((B, T, HV)), do, dST,
+                                             initial_state=rng.standard_normal((B, HV, K, V)))
+    assert np.all(dv == 0.0)
+    s = 1 / math.sqrt(K)
+    G = np.cumsum(g[0, :, 0], axis=0)                    # [T, K]
+    want = np.exp(G[-1])[:, None] * dST[0, 0]
+    for t in range(T):
+        want += np.exp(G[t])[:, None] * np.outer(s * q[0, t, 0], do[0, t, 0])
+    np.testing.assert_allclose(dS0[0, 0], want, rtol=1e-12, atol=1e-14)
+
+
+def test_backward_gqa_equals_explicit_repeat():
+    """dq and dk of a q/k head are the sums over the value heads it serves
+    (the repeat_interleave reversed)."""
+    B, T, H, HV, K, V = 1, 6, 2, 4, 3, 2
+    rng = np.random.default_rng(10)
+    q, k = rng.standard_normal((B, T, H, K)), rng.standard_normal((B, T, H, K))
+    v, g = rng.standard_normal((B, T, HV, V)), -rng.random((B, T, HV, K))
+    beta, do = rng.random((B, T, HV)), rng.standard_normal((B, T, HV, V))
+    a = oracle.kda_bwd(q, k, v, g, beta, do)
+    qr, kr = np.repeat(q, HV // H, axis=2), np.repeat(k, HV // H, axis=2)
+    r = oracle.kda_bwd(qr, kr, v, g, beta, do)
+    np.testing.assert_allclose(a[0], r[0].reshape(B, T, H, HV // H, K).sum(3), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(a[1], r[1].reshape(B, T, H, HV // H, K).sum(3), rtol=1e-13, atol=1e-14)
+    for i in range(2, 6):
+        np.testing.assert_allclose(a[i], r[i], rtol=1e-13, atol=1e-14)
