@@ -84,6 +84,10 @@ def _load():
             lib.kda_chunk_fwd.restype = I
             lib.kda_recurrent_fwd.argtypes = [P] * 8 + [I] * 6 + [F, I, P]
             lib.kda_recurrent_fwd.restype = I
+            lib.kda_recurrent_bwd_workspace_size.argtypes = [I] * 6
+            lib.kda_recurrent_bwd_workspace_size.restype = ctypes.c_longlong
+            lib.kda_recurrent_bwd.argtypes = ([P] * 14 + [I] * 6 + [F, I, P, ctypes.c_longlong, P])
+            lib.kda_recurrent_bwd.restype = I
             lib.kda_chunk_fwd_snapshots.argtypes = [P] * 9 + [I] * 7 + [F, I, I, P]
             lib.kda_chunk_fwd_snapshots.restype = I
             lib.kda_prefill_prologue.argtypes = ([P, P, P, ctypes.POINTER(DecodePrologue)] + [P] * 5
@@ -202,6 +206,55 @@ def recurrent_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final
             _ptr(final_state), B, T, H, HV, K, V, float(scale) if scale else 0.0,
             _dtype_code(q.dtype), _stream_handle(dev)))
     return out, final_state
+
+
+def recurrent_bwd_workspace_size(B, T, H, HV, K, V) -> int:
+    """Bytes of workspace ``kda_recurrent_bwd`` needs for these sizes."""
+    n = _load().kda_recurrent_bwd_workspace_size(B, T, H, HV, K, V)
+    if n < 0:
+        raise KDAError(KDA_EINVAL, _load().kda_last_error().decode(errors="replace"))
+    return n
+
+
+def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initial_state=None,
+                  *, workspace=None, need_d_initial_state=True):
+    """``kda_recurrent_bwd``: gradients of the forward pass with the same
+    inputs (any finite g).  dout [B,T,HV,V] is dL/do (v's dtype),
+    d_final_state [B,HV,K,V] fp32 (or None) is dL/dS_T.  Returns (dq, dk
+    [B,T,H,K] and dv [B,T,HV,V] in q's dtype, dg [B,T,HV,K], dbeta [B,T,HV],
+    dS0 [B,HV,K,V] fp32 or None).  ``workspace`` (a uint8 GPU tensor of at
+    least :func:`recurrent_bwd_workspace_size` bytes) may be passed to avoid
+    an allocation."""
+    _need(q, "q")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    dt, dev = q.dtype, q.device
+    _need(k, "k", dt, (B, T, H, K), dev)
+    _need(v, "v", dt, (B, T, HV, V), dev)
+    _need(g, "g", torch.float32, (B, T, HV, K), dev)
+    _need(beta, "beta", torch.float32, (B, T, HV), dev)
+    _need(dout, "dout", dt, (B, T, HV, V), dev)
+    for t_, n_ in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
+        if t_ is not None:
+            _need(t_, n_, torch.float32, (B, HV, K, V), dev)
+    nbytes = recurrent_bwd_workspace_size(B, T, H, HV, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, None, dev)
+    dq = torch.empty(B, T, H, K, dtype=dt, device=dev)
+    dk = torch.empty(B, T, H, K, dtype=dt, device=dev)
+    dv = torch.empty(B, T, HV, V, dtype=dt, device=dev)
+    dg = torch.empty(B, T, HV, K, dtype=torch.float32, device=dev)
+    db = torch.empty(B, T, HV, dtype=torch.float32, device=dev)
+    dS0 = torch.empty(B, HV, K, V, dtype=torch.float32, device=dev) if need_d_initial_state else None
+    with torch.cuda.device(dev):
+        _check(_load().kda_recurrent_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dout),
+            _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dS0),
+            B, T, H, HV, K, V, float(scale) if scale else 0.0, _dtype_code(dt), _ptr(workspace),
+            workspace.numel(), _stream_handle(dev)))
+    return dq, dk, dv, dg, db, dS0
 
 
 def chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,

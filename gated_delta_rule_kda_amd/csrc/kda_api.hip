@@ -157,6 +157,37 @@ int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, 
 
 }  // namespace
 
+namespace {
+
+// Workspace of kda_recurrent_bwd: fp32 regions, each 256-byte aligned (offsets
+// in bytes).
+struct BwdLayout {
+    uint64_t r, dr, st, daP, dqP, dkrP, e, bs, total;
+    int NCB, NB;
+};
+
+bool bwd_layout(BwdLayout &L, int B, int T, int HV, int K, int V) {
+    L.NCB = V / kda::kBwdCols;
+    L.NB = (T + kda::kDgBlock - 1) / kda::kDgBlock;
+    uint64_t nv, ns, np, ne, nbs;
+    if (!count(nv, {B, T, HV, V}) || !count(ns, {B, HV, K, V}) || !count(np, {L.NCB, B, T, HV, K}) ||
+        !count(ne, {B, T, HV, K}) || !count(nbs, {B, HV, K, L.NB}))
+        return false;
+    uint64_t off = 0;
+    auto take = [&](uint64_t floats) {
+        const uint64_t at = off;
+        off += (floats * 4 + 255) / 256 * 256;
+        return at;
+    };
+    L.r = take(nv); L.dr = take(nv); L.st = take(ns);
+    L.daP = take(np); L.dqP = take(np); L.dkrP = take(np);
+    L.e = take(ne); L.bs = take(nbs);
+    L.total = off;
+    return true;
+}
+
+}  // namespace
+
 extern "C" {
 
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
@@ -183,6 +214,117 @@ int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *
                       float scale, int dtype, void *stream) {
     return chunk_fwd_impl("kda_recurrent_fwd", q, k, v, g, beta, initial_state, out, final_state,
                           nullptr, 0, B, T, H, HV, K, V, scale, 0, dtype, stream, true);
+}
+
+long long kda_recurrent_bwd_workspace_size(int B, int T, int H, int HV, int K, int V) {
+    g_err[0] = '\0';
+    if (B < 0 || T < 0 || H < 1 || HV < 1 || HV % H != 0) {
+        fail(KDA_EINVAL, "kda_recurrent_bwd_workspace_size: B=%d, T=%d, H=%d, HV=%d are not valid sizes",
+             B, T, H, HV);
+        return -1;
+    }
+    if (!head_dim_ok(K) || !head_dim_ok(V)) {
+        fail(KDA_EUNSUPPORTED, "kda_recurrent_bwd_workspace_size: K=%d, V=%d; each must be 32, 64 or 128", K, V);
+        return -1;
+    }
+    BwdLayout L;
+    if (!bwd_layout(L, B, T, HV, K, V)) {
+        fail(KDA_EINVAL, "kda_recurrent_bwd_workspace_size: tensor sizes overflow");
+        return -1;
+    }
+    return static_cast<long long>(L.total);
+}
+
+int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const float *initial_state, const void *dout,
+                      const float *dfinal_state, void *dq, void *dk, void *dv, float *dg,
+                      float *dbeta, float *dinitial_state, int B, int T, int H, int HV, int K,
+                      int V, float scale, int dtype, void *workspace, long long workspace_bytes,
+                      void *stream) {
+    const char *fn = "kda_recurrent_bwd";
+    g_err[0] = '\0';
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
+        return fail(KDA_EUNSUPPORTED, "%s: dtype %d is not KDA_DTYPE_F32 or KDA_DTYPE_BF16", fn, dtype);
+    if (B < 0 || T < 0) return fail(KDA_EINVAL, "%s: B=%d and T=%d must be >= 0", fn, B, T);
+    if (H < 1 || HV < 1) return fail(KDA_EINVAL, "%s: H=%d and HV=%d must be >= 1", fn, H, HV);
+    if (HV % H != 0) return fail(KDA_EINVAL, "%s: HV=%d is not a multiple of H=%d", fn, HV, H);
+    if (!head_dim_ok(K) || !head_dim_ok(V))
+        return fail(KDA_EUNSUPPORTED, "%s: K=%d, V=%d; each must be 32, 64 or 128", fn, K, V);
+    if (isinf(scale)) return fail(KDA_EINVAL, "%s: scale is infinite", fn);
+    if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(K));
+    BwdLayout L;
+    uint64_t nq, nv, ng, nb, ns;
+    if (!bwd_layout(L, B, T, HV, K, V) || !count(nq, {B, T, H, K}) || !count(nv, {B, T, HV, V}) ||
+        !count(ng, {B, T, HV, K}) || !count(nb, {B, T, HV}) || !count(ns, {B, HV, K, V}))
+        return fail(KDA_EINVAL, "%s: tensor sizes overflow", fn);
+    const uint64_t esz = dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const bool work = static_cast<int64_t>(B) * T > 0;
+    if (work) {
+        if (!q || !k || !v || !g || !beta || !dout)
+            return fail(KDA_EINVAL, "%s: q, k, v, g, beta and dout must be non-NULL", fn);
+        if (!dq || !dk || !dv || !dg || !dbeta)
+            return fail(KDA_EINVAL, "%s: dq, dk, dv, dg and dbeta must be non-NULL", fn);
+        if (!workspace) return fail(KDA_EINVAL, "%s: workspace is NULL", fn);
+        if (workspace_bytes < 0 || static_cast<uint64_t>(workspace_bytes) < L.total)
+            return fail(KDA_EINVAL, "%s: workspace of %lld bytes, %llu needed", fn, workspace_bytes,
+                        static_cast<unsigned long long>(L.total));
+    }
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, dout, dfinal_state,
+                          dq, dk, dv, dg, dbeta, dinitial_state, workspace};
+    const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "dout", "dfinal_state",
+                           "dq", "dk", "dv", "dg", "dbeta", "dinitial_state", "workspace"};
+    for (int i = 0; i < 15; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(KDA_EINVAL, "%s: %s is not 16-byte aligned", fn, names[i]);
+    // every output (and the workspace) is disjoint from every other argument
+    const Range rs[] = {rng("q", q, nq * esz), rng("k", k, nq * esz), rng("v", v, nv * esz),
+                        rng("g", g, ng * 4), rng("beta", beta, nb * 4),
+                        rng("initial_state", initial_state, ns * 4), rng("dout", dout, nv * esz),
+                        rng("dfinal_state", dfinal_state, ns * 4),
+                        rng("dq", dq, nq * esz), rng("dk", dk, nq * esz), rng("dv", dv, nv * esz),
+                        rng("dg", dg, ng * 4), rng("dbeta", dbeta, nb * 4),
+                        rng("dinitial_state", dinitial_state, ns * 4),
+                        rng("workspace", work ? workspace : nullptr, L.total)};
+    for (int o = 8; o < 15; ++o)
+        for (int i = 0; i < 15; ++i)
+            if (i != o && overlap(rs[o], rs[i]))
+                return fail(KDA_EINVAL, "%s: %s overlaps %s", fn, rs[o].name, rs[i].name);
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    kda::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = initial_state;
+    a.dout = dout; a.dST = dfinal_state;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dS0 = dinitial_state;
+    if (work) {
+        a.r = reinterpret_cast<float *>(ws + L.r);
+        a.dr = reinterpret_cast<float *>(ws + L.dr);
+        a.ST = reinterpret_cast<float *>(ws + L.st);
+        a.daP = reinterpret_cast<float *>(ws + L.daP);
+        a.dqP = reinterpret_cast<float *>(ws + L.dqP);
+        a.dkrP = reinterpret_cast<float *>(ws + L.dkrP);
+        a.e = reinterpret_cast<float *>(ws + L.e);
+        a.bs = reinterpret_cast<float *>(ws + L.bs);
+    }
+    a.NCB = L.NCB; a.NB = L.NB;
+    a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+    a.scale = scale;
+    a.bf16 = dtype == KDA_DTYPE_BF16;
+    if (work) {
+        // the forward pass, keeping the residuals and the final state
+        kda::PrefillArgs f{};
+        f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.S0 = initial_state;
+        f.out = nullptr; f.ST = a.ST; f.aux = a.r;
+        f.B = B; f.T = T; f.H = H; f.HV = HV; f.K = K; f.V = V;
+        f.scale = scale; f.bf16 = a.bf16;
+        const hipError_t e = kda::launch_recurrent(f, st);
+        if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    } else if (!dinitial_state || B == 0) {
+        return KDA_OK;
+    }
+    const hipError_t e = kda::launch_backward(a, st);
+    if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
 }
 
 int kda_prefill_prologue(const void *x, const float *gate, const float *beta,

@@ -17,6 +17,9 @@ struct PrefillArgs {
     float *snap;                // [B,NS,HV,K,V] prefix snapshots or nullptr
     int snap_chunks;            // chunks between snapshots (>= 1 when snap is set)
     int NS;                     // snapshots per sequence, T / (32 * snap_chunks)
+    float *aux;                 // token-recurrent kernel only: when set, the
+                                // residuals r_t = v_t - k_t^T S_dec ([B,T,HV,V]
+                                // fp32) are written here instead of out
     int B, T, H, HV, K, V;
     float scale;
     bool bf16;
@@ -74,11 +77,38 @@ struct OutputGateArgs {
     bool bf16;
 };
 
+// Arguments of the backward of the token recurrence (kda_recurrent_bwd).
+struct BwdArgs {
+    const void *q, *k, *v;      // [B,T,H,K], [B,T,H,K], [B,T,HV,V] (dtype)
+    const float *g, *beta;      // [B,T,HV,K], [B,T,HV]
+    const float *S0;            // [B,HV,K,V] or nullptr
+    const void *dout;           // [B,T,HV,V] (dtype): dL/do
+    const float *dST;           // [B,HV,K,V] or nullptr: dL/dS_T
+    void *dq, *dk, *dv;         // [B,T,H,K], [B,T,H,K], [B,T,HV,V] (dtype)
+    float *dg, *dbeta;          // [B,T,HV,K], [B,T,HV]
+    float *dS0;                 // [B,HV,K,V] or nullptr
+    // workspace, fp32
+    float *r, *dr;              // [B,T,HV,V]: forward residuals, their gradients
+    float *ST;                  // [B,HV,K,V]: forward final state
+    float *daP, *dqP, *dkrP;    // [NCB,B,T,HV,K]: per column-block partial sums
+    float *e;                   // [B,T,HV,K]: per-token terms of dg
+    float *bs;                  // [B,HV,K,NB]: sums of e over blocks of kDgBlock tokens
+    int NCB, NB;
+    int B, T, H, HV, K, V;
+    float scale;
+    bool bf16;
+};
+constexpr int kBwdCols = 32;    // state columns per workgroup of the backward passes
+constexpr int kDgBlock = 64;    // tokens per block of the reverse sum that forms dg
 constexpr int kMaxConvKernel = 8;
 
 // Launch on `stream`; return the hipError_t of the launch.
 hipError_t launch_prologue(const PrologueArgs &a, hipStream_t stream);
 hipError_t launch_recurrent(const PrefillArgs &a, hipStream_t stream);
+// the backward after the forward residuals and final state are in the
+// workspace: the reverse state-gradient pass, the forward gradient pass and
+// the reductions
+hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_output_gate(const OutputGateArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream);

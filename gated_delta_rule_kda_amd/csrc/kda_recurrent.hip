@@ -25,7 +25,7 @@
 // loaded into registers while the current round runs.  96 value heads of
 // K = V = 128 give 768 workgroups, 3072 waves: three per SIMD.
 
-#include "kda_internal.h"
+#include "kda_lanes.h"
 
 namespace kda {
 namespace {
@@ -35,65 +35,14 @@ constexpr int kRG = 16;        // lanes (row groups) per state column: 8 or 16
 static_assert(kRG == 8 || kRG == 16, "a column's lanes are a half or a whole DPP row");
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWGCols = kThreads / kRG;   // state columns per workgroup
-constexpr float kLog2e = 1.4426950408889634f;
+using namespace lanes;
 
-// 2^x by the hardware exponential alone, without the library's rescaling for
-// results below the normal range (1 ulp; such a result may come out as 0, an
-// absolute change of less than 2^-126 in a decay factor)
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-// x of another lane (DPP); the 0 that stands for lanes without a source lets the
-// compiler fold the move into the add that consumes it
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
 // sum over the kRG lanes of one state column (a half or a whole DPP row)
-__device__ __forceinline__ float col_sum(float s) {
-    s += dpp<0xb1>(s);    // quad_perm [1,0,3,2]
-    s += dpp<0x4e>(s);    // quad_perm [2,3,0,1]
-    s += dpp<0x141>(s);   // row_half_mirror
-    if constexpr (kRG == 16) s += dpp<0x140>(s);   // row_mirror
-    return s;
-}
-__device__ __forceinline__ float load_io(const void *p, size_t i, bool bf16) {
-    return bf16 ? bf16_bits_to_float(static_cast<const uint16_t *>(p)[i]) : static_cast<const float *>(p)[i];
-}
-// 4 consecutive elements as loaded (bf16: two packed words; fp32: a float4)
-template <bool BF16> struct Raw4;
-template <> struct Raw4<true> { uint2 u; };
-template <> struct Raw4<false> { float4 f; };
-// Raw buffer resource over `bytes` bytes from `p`: out-of-range loads read 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes), 0x00020000);
-}
-template <bool BF16>
-__device__ __forceinline__ Raw4<BF16> load_raw4(__amdgpu_buffer_rsrc_t rs, int byte_off) {
-    if constexpr (BF16) {
-        const auto u = __builtin_amdgcn_raw_buffer_load_b64(rs, byte_off, 0, 0);
-        return Raw4<true>{make_uint2(u[0], u[1])};
-    } else {
-        const auto u = __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0);
-        return Raw4<false>{make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]),
-                                       __uint_as_float(u[2]), __uint_as_float(u[3]))};
-    }
-}
-template <bool BF16>
-__device__ __forceinline__ Raw4<BF16> zero_raw4() {
-    if constexpr (BF16)
-        return Raw4<true>{make_uint2(0u, 0u)};
-    else
-        return Raw4<false>{make_float4(0.f, 0.f, 0.f, 0.f)};
-}
-template <bool BF16>
-__device__ __forceinline__ float4 widen(const Raw4<BF16> &r) {
-    if constexpr (BF16)
-        return make_float4(__uint_as_float(r.u.x << 16), __uint_as_float(r.u.x & 0xffff0000u),
-                           __uint_as_float(r.u.y << 16), __uint_as_float(r.u.y & 0xffff0000u));
-    else
-        return r.f;
-}
+__device__ __forceinline__ float col_sum(float s) { return group_sum<kRG>(s); }
 
-template <int K, bool BF16>
+// RES: the variant that writes the residuals r_t (a.aux) in place of the
+// outputs, the forward half of the backward pass
+template <int K, bool BF16, bool RES>
 __global__ __launch_bounds__(kThreads) void recurrent_kernel(PrefillArgs a) {
     constexpr int RPL = K / kRG;                // state rows per lane
     constexpr int NP = kTC * K / 4;             // 4-element pieces of one staged [kTC][K] array
@@ -120,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(PrefillArgs a) {
     // group j reads entry j, so the (q.k) beta r term of the readout lands in
     // the first QKN row groups' parts and nowhere else
     __shared__ float sQKz[kTC][kRG];
-    __shared__ float sV[kTC][kWGCols], sB[kTC];
+    __shared__ float sV[kTC][kWGCols], sB[kTC], sRes[RES ? kTC : 1][kWGCols];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = wave * (64 / kRG) + lane / kRG;     // this lane's column within the workgroup
@@ -270,7 +219,11 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(PrefillArgs a) {
         const float u = x.b * (x.v - p);                             // beta r
 #pragma unroll
         for (int r = 0; r < RPL; ++r) S[r] = fmaf(x.k[r], u, S[r]);  // rank-1 write
-        sW[t][c][rg] = fmaf(x.qk, u, w0 + w1);                       // q^T S = q^T S_dec + (q.k) beta r
+        if constexpr (RES) {
+            if (rg == 0) sRes[t][c] = x.v - p;
+        } else {
+            sW[t][c][rg] = fmaf(x.qk, u, w0 + w1);                   // q^T S = q^T S_dec + (q.k) beta r
+        }
     };
 
     load_round(0);
@@ -298,7 +251,9 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < NVT; ++i) {
             const int e = tid + i * kThreads, t = e / kWGCols, cc = e % kWGCols;
-            if (t < nt) {
+            if (RES && t < nt) {
+                a.aux[((tok_b + t0 + t) * a.HV + hv) * a.V + c0 + cc] = sRes[t][cc];
+            } else if (t < nt) {
                 float o = 0.f;
 #pragma unroll
                 for (int j = 0; j < kRG; j += 4) {
@@ -326,10 +281,17 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(PrefillArgs a) {
 template <int K>
 hipError_t launch_k(const PrefillArgs &a, hipStream_t stream) {
     const unsigned grid = static_cast<unsigned>(a.B) * a.HV * (a.V / kWGCols);
-    if (a.bf16)
-        hipLaunchKernelGGL((recurrent_kernel<K, true>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((recurrent_kernel<K, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    if (a.aux) {
+        if (a.bf16)
+            hipLaunchKernelGGL((recurrent_kernel<K, true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((recurrent_kernel<K, false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    } else {
+        if (a.bf16)
+            hipLaunchKernelGGL((recurrent_kernel<K, true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((recurrent_kernel<K, false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

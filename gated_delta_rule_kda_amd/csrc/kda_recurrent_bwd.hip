@@ -1,0 +1,496 @@
+// Backward of the KDA forward, for gfx950: back-propagation through time over
+// the token recurrence.
+//
+// The backward that the page "K3/kda/ops/reference/recurrent.py" derives in
+// its module docstring (KDAFunction.backward: BPTT from t = T-1 to 0), with
+// the gradient of the initial state kept.  With D = dL/dS_t carried backwards
+// (D_T = dL/dS_T), per token and value head:
+//     D~ = D + qs (x) dout               (qs = scale q: the readout)
+//     dr = (beta k)^T D~,  dv = dr,  da = D~ r      (the rank-1 write, r its residual)
+//     D  = exp(g) (.) (D~ - k (x) dr)    (the residual's read and the decay)
+//     dq = scale S_t dout,  dk = beta da - S_dec dr,  dbeta = k . da
+// and dS0 = D after token 0.  The per-token dg = sum over V of S_dec (.) D_dec
+// needs both states at the same token; it is taken instead from the identity
+//     dg_u = sum over t >= u of (qs_t (.) dqs_t - k_t (.) (S_dec,t dr_t)
+//                                - k_t (.) beta_t da_t)  +  sum over V of S_T (.) dL/dS_T,
+// which holds because adding eps to g_u[f] multiplies, in channel f, every
+// product of a read (q_t, or k_t where it reads S_dec,t) at t >= u with a write
+// (k_s as written, or S0) at s < u by e^eps, as scaling all reads at t >= u by
+// e^eps and all writes at s >= u by e^-eps does; the tests compare the result
+// with the oracle's direct sum (itself checked against finite differences).
+//
+// So the state gradient D never meets the forward state S: three passes over
+// the sequence, each holding one K x 32 slice of one of them in registers --
+//   1. forward (kda_recurrent.hip, residual variant): r_t and S_T;
+//   2. reverse, this file: D, giving dv, dr, the partial sums of da, and dS0;
+//   3. forward, this file: S again, giving the partial sums of S_t dout and
+//      S_dec dr;
+// then the partial sums are added (one per 32 state columns), dq and dk summed
+// over the value heads of a q/k head (GQA), and dg formed by a blocked reverse
+// sum over the tokens.
+//
+// Lanes as in the forward kernel: lane = (state column, row group), 16 row
+// groups of K/16 rows (runs of four at stride 64), a column's 16 lanes one DPP
+// row, so sums over K are four DPP steps.  Sums over V (da, S_t dout,
+// S_dec dr: one K-vector per token) go over the four columns of a wave by the
+// gfx950 lane swaps, then over the waves of the workgroup through LDS, once
+// per round of kTB tokens.
+
+#include "kda_lanes.h"
+
+namespace kda {
+namespace {
+
+using namespace lanes;
+
+constexpr int kTB = 4;                          // tokens staged per round
+constexpr int kRG = 16;                         // lanes per state column
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCols = kWaves * (64 / kRG);      // state columns per workgroup
+static_assert(kCols == kBwdCols, "column blocks as the workspace is laid out");
+
+// row of the lane's r-th state row (runs of four, or fewer for small K)
+template <int K>
+__device__ __forceinline__ int row_of(int r, int rg) {
+    constexpr int RPL = K / kRG, RUN = RPL < 4 ? RPL : 4;
+    return (r / RUN) * (RUN * kRG) + rg * RUN + r % RUN;
+}
+// RPL consecutive-in-runs values of one [K] row of LDS into registers
+template <int K>
+__device__ __forceinline__ void read_rows(const float *row, int rg, float (&x)[K / kRG]) {
+    constexpr int RPL = K / kRG;
+    if constexpr (RPL >= 4) {
+#pragma unroll
+        for (int r = 0; r < RPL; r += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(row + row_of<K>(r, rg));
+            x[r] = v.x; x[r + 1] = v.y; x[r + 2] = v.z; x[r + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) x[r] = row[row_of<K>(r, rg)];
+    }
+}
+// this lane's RPL values into one [K] row of LDS
+template <int K>
+__device__ __forceinline__ void write_rows(float *row, int rg, const float (&x)[K / kRG]) {
+    constexpr int RPL = K / kRG;
+    if constexpr (RPL >= 4) {
+#pragma unroll
+        for (int r = 0; r < RPL; r += 4)
+            *reinterpret_cast<float4 *>(row + row_of<K>(r, rg)) = make_float4(x[r], x[r + 1], x[r + 2], x[r + 3]);
+    } else {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) row[row_of<K>(r, rg)] = x[r];
+    }
+}
+
+// Bytes of kTB tokens' rows from token t0 on, for a buffer resource: rows past
+// the end of the sequence are not covered and read as 0.
+__device__ __forceinline__ uint32_t span_bytes(int T, int t0, int stride, int rowlen, int esz) {
+    const int nv = min(kTB, T - t0);
+    return nv > 0 ? static_cast<uint32_t>(((nv - 1) * stride + rowlen) * esz) : 0u;
+}
+
+// ----------------------------------------------------------------------------
+// Pass 2: the state gradient D, tokens in reverse.  Tokens past the end of the
+// sequence (only in the first round processed) stage as q = k = 0, exp(g) = 1,
+// beta = dout = r = 0: D passes through unchanged.
+template <int K, bool BF16>
+__global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
+    constexpr int RPL = K / kRG;
+    constexpr int NP = kTB * K / 4;              // 4-element pieces of a [kTB][K] array
+    static_assert(NP <= kThreads, "one piece per thread at most");
+    constexpr int NCV = kTB * kCols;             // column values per round
+    static_assert(NCV <= kThreads, "one column value per thread at most");
+    constexpr int ESZ = BF16 ? 2 : 4;
+    __shared__ __attribute__((aligned(16))) float sQ[kTB][K], sK[kTB][K], sA[kTB][K], sD[kTB][K];
+    __shared__ float sDo[kTB][kCols], sR[kTB][kCols], sDr[kTB][kCols];
+    __shared__ __attribute__((aligned(16))) float sDa[kTB][kWaves][K];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = wave * (64 / kRG) + lane / kRG, rg = lane % kRG;
+    const int ncb = a.V / kCols;
+    const int cb = blockIdx.x % ncb, bhv = blockIdx.x / ncb;
+    const int b = bhv / a.HV, hv = bhv % a.HV, h = hv / (a.HV / a.H);
+    const int c0 = cb * kCols;
+    const size_t tok_b = static_cast<size_t>(b) * a.T;
+    const size_t st_off = (static_cast<size_t>(b) * a.HV + hv) * K * a.V;
+
+    float D[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+        D[r] = a.dST ? a.dST[st_off + static_cast<size_t>(row_of<K>(r, rg)) * a.V + c0 + c] : 0.f;
+
+    // ---- a round's inputs, prefetched into registers
+    Raw4<BF16> pq, pk;
+    float4 pg;
+    float pb = 0.f, pdo = 0.f, pr = 0.f;
+    auto load_round = [&](int t0) {
+        const size_t tb = tok_b + t0;
+        const int e = min(tid, NP - 1);
+        const int t = e / (K / 4), f = (e % (K / 4)) * 4;
+        const auto rq = make_rsrc(static_cast<const char *>(a.q) + (tb * a.H + h) * K * ESZ,
+                                  span_bytes(a.T, t0, a.H * K, K, ESZ));
+        const auto rk = make_rsrc(static_cast<const char *>(a.k) + (tb * a.H + h) * K * ESZ,
+                                  span_bytes(a.T, t0, a.H * K, K, ESZ));
+        const auto rgr = make_rsrc(a.g + (tb * a.HV + hv) * K, span_bytes(a.T, t0, a.HV * K, K, 4));
+        const auto rb = make_rsrc(a.beta + tb * a.HV + hv, span_bytes(a.T, t0, a.HV, 1, 4));
+        pq = load_raw4<BF16>(rq, (t * a.H * K + f) * ESZ);
+        pk = load_raw4<BF16>(rk, (t * a.H * K + f) * ESZ);
+        pg = load_f4(rgr, (t * a.HV * K + f) * 4);
+        pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * a.HV * 4, 0, 0));
+        const int ec = min(tid, NCV - 1), tc = ec / kCols, cc = ec % kCols;
+        const auto rdo = make_rsrc(static_cast<const char *>(a.dout) + ((tb * a.HV + hv) * a.V + c0) * ESZ,
+                                   span_bytes(a.T, t0, a.HV * a.V, kCols, ESZ));
+        const auto rr = make_rsrc(a.r + (tb * a.HV + hv) * a.V + c0, span_bytes(a.T, t0, a.HV * a.V, kCols, 4));
+        pdo = load1<BF16>(rdo, tc * a.HV * a.V + cc);
+        pr = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, (tc * a.HV * a.V + cc) * 4, 0, 0));
+    };
+    auto store_round = [&]() {
+        if (tid < NP) {
+            const int t = tid / (K / 4), f = (tid % (K / 4)) * 4;
+            const float4 q = widen<BF16>(pq), k = widen<BF16>(pk), g = pg;
+            *reinterpret_cast<float4 *>(&sQ[t][f]) = make_float4(a.scale * q.x, a.scale * q.y, a.scale * q.z, a.scale * q.w);
+            *reinterpret_cast<float4 *>(&sK[t][f]) = k;
+            *reinterpret_cast<float4 *>(&sA[t][f]) = make_float4(pb * k.x, pb * k.y, pb * k.z, pb * k.w);
+            *reinterpret_cast<float4 *>(&sD[t][f]) = make_float4(ex2(g.x * kLog2e), ex2(g.y * kLog2e),
+                                                                 ex2(g.z * kLog2e), ex2(g.w * kLog2e));
+        }
+        if (tid < NCV) {
+            sDo[tid / kCols][tid % kCols] = pdo;
+            sR[tid / kCols][tid % kCols] = pr;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): every prefetched register consumed
+    };
+
+    const int last0 = a.T > 0 ? ((a.T - 1) / kTB) * kTB : -kTB;
+    if (last0 >= 0) {
+        load_round(last0);
+        store_round();
+    }
+    __syncthreads();
+    for (int t0 = last0; t0 >= 0; t0 -= kTB) {
+        if (t0 >= kTB) load_round(t0 - kTB);               // in flight during this round
+#pragma unroll
+        for (int t = kTB - 1; t >= 0; --t) {
+            float q[RPL], k[RPL], av[RPL], d[RPL], Dt[RPL];
+            read_rows<K>(sQ[t], rg, q);
+            read_rows<K>(sK[t], rg, k);
+            read_rows<K>(sA[t], rg, av);
+            read_rows<K>(sD[t], rg, d);
+            const float dout = sDo[t][c], rr = sR[t][c];
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                Dt[r] = fmaf(q[r], dout, D[r]);                      // D~ = D + qs (x) dout
+                if (r & 1) s1 = fmaf(av[r], Dt[r], s1); else s0 = fmaf(av[r], Dt[r], s0);
+            }
+            const float dr = group_sum<kRG>(s0 + s1);               // (beta k)^T D~
+            if (rg == 0) sDr[t][c] = dr;
+            float pa[RPL];
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) pa[r] = across_rows_sum(Dt[r] * rr);   // da over the wave's columns
+            if (lane < kRG) write_rows<K>(sDa[t][wave], rg, pa);
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) D[r] = d[r] * fmaf(-k[r], dr, Dt[r]);
+        }
+        __syncthreads();
+        // the next round to LDS (its loads are waited for here, before this
+        // round's stores are issued), then the round's dv, dr and da partial sums
+        if (t0 >= kTB) store_round();
+        if (tid < NCV) {
+            const int t = tid / kCols, cc = tid % kCols;
+            if (t0 + t < a.T) {
+                const size_t i = ((tok_b + t0 + t) * a.HV + hv) * a.V + c0 + cc;
+                store1<BF16>(a.dv, i, sDr[t][cc]);
+                a.dr[i] = sDr[t][cc];
+            }
+        }
+        for (int i = tid; i < kTB * K; i += kThreads) {
+            const int t = i / K, kk = i % K;
+            if (t0 + t < a.T) {
+                float s = 0.f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) s += sDa[t][w][kk];
+                a.daP[((static_cast<size_t>(cb) * a.B * a.T + tok_b + t0 + t) * a.HV + hv) * K + kk] = s;
+            }
+        }
+        __syncthreads();
+    }
+    if (a.dS0) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) a.dS0[st_off + static_cast<size_t>(row_of<K>(r, rg)) * a.V + c0 + c] = D[r];
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Pass 3: the forward state again, tokens in order, with the partial sums of
+// S_t dout (for dq) and S_dec dr (for dk).  Tokens past the end stage as
+// k = 0, exp(g) = 1, v = beta = dout = dr = 0: no-ops.
+template <int K, bool BF16>
+__global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
+    constexpr int RPL = K / kRG;
+    constexpr int NP = kTB * K / 4;
+    static_assert(NP <= kThreads, "one piece per thread at most");
+    constexpr int NCV = kTB * kCols;
+    static_assert(NCV <= kThreads, "one column value per thread at most");
+    constexpr int ESZ = BF16 ? 2 : 4;
+    __shared__ __attribute__((aligned(16))) float sK[kTB][K], sD[kTB][K];
+    __shared__ float sV[kTB][kCols], sDo[kTB][kCols], sDr[kTB][kCols], sB[kTB];
+    __shared__ __attribute__((aligned(16))) float sDq[kTB][kWaves][K], sDk[kTB][kWaves][K];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = wave * (64 / kRG) + lane / kRG, rg = lane % kRG;
+    const int ncb = a.V / kCols;
+    const int cb = blockIdx.x % ncb, bhv = blockIdx.x / ncb;
+    const int b = bhv / a.HV, hv = bhv % a.HV, h = hv / (a.HV / a.H);
+    const int c0 = cb * kCols;
+    const size_t tok_b = static_cast<size_t>(b) * a.T;
+    const size_t st_off = (static_cast<size_t>(b) * a.HV + hv) * K * a.V;
+
+    float S[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+        S[r] = a.S0 ? a.S0[st_off + static_cast<size_t>(row_of<K>(r, rg)) * a.V + c0 + c] : 0.f;
+
+    Raw4<BF16> pk;
+    float4 pg;
+    float pb = 0.f, pv = 0.f, pdo = 0.f, pdr = 0.f;
+    auto load_round = [&](int t0) {
+        const size_t tb = tok_b + t0;
+        const int e = min(tid, NP - 1);
+        const int t = e / (K / 4), f = (e % (K / 4)) * 4;
+        const auto rk = make_rsrc(static_cast<const char *>(a.k) + (tb * a.H + h) * K * ESZ,
+                                  span_bytes(a.T, t0, a.H * K, K, ESZ));
+        const auto rgr = make_rsrc(a.g + (tb * a.HV + hv) * K, span_bytes(a.T, t0, a.HV * K, K, 4));
+        const auto rb = make_rsrc(a.beta + tb * a.HV + hv, span_bytes(a.T, t0, a.HV, 1, 4));
+        pk = load_raw4<BF16>(rk, (t * a.H * K + f) * ESZ);
+        pg = load_f4(rgr, (t * a.HV * K + f) * 4);
+        pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (tid & (kTB - 1)) * a.HV * 4, 0, 0));
+        const int ec = min(tid, NCV - 1), tc = ec / kCols, cc = ec % kCols;
+        const size_t cbase = (tb * a.HV + hv) * a.V + c0;
+        const uint32_t cspan_d = span_bytes(a.T, t0, a.HV * a.V, kCols, ESZ);
+        const uint32_t cspan_f = span_bytes(a.T, t0, a.HV * a.V, kCols, 4);
+        const auto rv = make_rsrc(static_cast<const char *>(a.v) + cbase * ESZ, cspan_d);
+        const auto rdo = make_rsrc(static_cast<const char *>(a.dout) + cbase * ESZ, cspan_d);
+        const auto rdr = make_rsrc(a.dr + cbase, cspan_f);
+        pv = load1<BF16>(rv, tc * a.HV * a.V + cc);
+        pdo = load1<BF16>(rdo, tc * a.HV * a.V + cc);
+        pdr = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdr, (tc * a.HV * a.V + cc) * 4, 0, 0));
+    };
+    auto store_round = [&]() {
+        if (tid < NP) {
+            const int t = tid / (K / 4), f = (tid % (K / 4)) * 4;
+            const float4 g = pg;
+            *reinterpret_cast<float4 *>(&sK[t][f]) = widen<BF16>(pk);
+            *reinterpret_cast<float4 *>(&sD[t][f]) = make_float4(ex2(g.x * kLog2e), ex2(g.y * kLog2e),
+                                                                 ex2(g.z * kLog2e), ex2(g.w * kLog2e));
+        }
+        if (tid < NCV) {
+            sV[tid / kCols][tid % kCols] = pv;
+            sDo[tid / kCols][tid % kCols] = pdo;
+            sDr[tid / kCols][tid % kCols] = pdr;
+        }
+        if (tid < kTB) sB[tid] = pb;
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): every prefetched register consumed
+    };
+
+    if (a.T > 0) {
+        load_round(0);
+        store_round();
+    }
+    __syncthreads();
+    for (int t0 = 0; t0 < a.T; t0 += kTB) {
+        if (t0 + kTB < a.T) load_round(t0 + kTB);
+#pragma unroll
+        for (int t = 0; t < kTB; ++t) {
+            float k[RPL], d[RPL];
+            read_rows<K>(sK[t], rg, k);
+            read_rows<K>(sD[t], rg, d);
+            const float v = sV[t][c], dout = sDo[t][c], dr = sDr[t][c], beta = sB[t];
+            float pk_[RPL], s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                S[r] *= d[r];                                        // S_dec
+                if (r & 1) s1 = fmaf(k[r], S[r], s1); else s0 = fmaf(k[r], S[r], s0);
+            }
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) pk_[r] = across_rows_sum(S[r] * dr);    // S_dec dr
+            if (lane < kRG) write_rows<K>(sDk[t][wave], rg, pk_);
+            const float u = beta * (v - group_sum<kRG>(s0 + s1));
+            float pq_[RPL];
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                S[r] = fmaf(k[r], u, S[r]);                          // S_t
+                pq_[r] = across_rows_sum(S[r] * dout);               // S_t dout
+            }
+            if (lane < kRG) write_rows<K>(sDq[t][wave], rg, pq_);
+        }
+        __syncthreads();
+        if (t0 + kTB < a.T) store_round();                 // the next round (see the reverse pass)
+        for (int i = tid; i < kTB * K; i += kThreads) {
+            const int t = i / K, kk = i % K;
+            if (t0 + t < a.T) {
+                float sq = 0.f, sk = 0.f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    sq += sDq[t][w][kk];
+                    sk += sDk[t][w][kk];
+                }
+                const size_t o = ((static_cast<size_t>(cb) * a.B * a.T + tok_b + t0 + t) * a.HV + hv) * K + kk;
+                a.dqP[o] = sq;
+                a.dkrP[o] = sk;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Partial sums over the column blocks, the per-token dg terms and dbeta.  One
+// row (b, t, hv) of K values per K threads.
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_sum_kernel(BwdArgs a) {
+    __shared__ float sRed[256];
+    const int K = a.K, rows_per_block = 256 / K;
+    const int tid = threadIdx.x, rl = tid / K, kk = tid % K;
+    const long nrows = static_cast<long>(a.B) * a.T * a.HV;
+    const long row = static_cast<long>(blockIdx.x) * rows_per_block + rl;
+    const bool live = rl < rows_per_block && row < nrows;
+    float prod = 0.f;
+    if (live) {
+        const size_t plane = static_cast<size_t>(nrows) * K, i = static_cast<size_t>(row) * K + kk;
+        float da = 0.f, dkr = 0.f, dqs = 0.f;
+        for (int cb = 0; cb < a.NCB; ++cb) {
+            da += a.daP[cb * plane + i];
+            dkr += a.dkrP[cb * plane + i];
+            dqs += a.dqP[cb * plane + i];
+        }
+        a.daP[i] = da;
+        a.dkrP[i] = dkr;
+        a.dqP[i] = dqs;
+        const long tok = row / a.HV;
+        const int hv = static_cast<int>(row % a.HV), h = hv / (a.HV / a.H);
+        const size_t qi = (static_cast<size_t>(tok) * a.H + h) * K + kk;
+        const float q = BF16 ? bf16_bits_to_float(static_cast<const uint16_t *>(a.q)[qi]) : static_cast<const float *>(a.q)[qi];
+        const float k = BF16 ? bf16_bits_to_float(static_cast<const uint16_t *>(a.k)[qi]) : static_cast<const float *>(a.k)[qi];
+        const float beta = a.beta[row];
+        a.e[i] = a.scale * q * dqs - k * (dkr + beta * da);
+        prod = k * da;
+    }
+    sRed[tid] = prod;
+    __syncthreads();
+    if (live && kk == 0) {
+        float s = 0.f;
+        for (int j = 0; j < K; ++j) s += sRed[rl * K + j];
+        a.dbeta[row] = s;                                          // k . da
+    }
+}
+
+// dq = scale * sum over the q/k head's value heads of S_t dout; dk = sum of
+// beta da - S_dec dr.  One element of [B,T,H,K] per thread.
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_qk_kernel(BwdArgs a) {
+    const long n = static_cast<long>(a.B) * a.T * a.H * a.K;
+    const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int kk = static_cast<int>(i % a.K);
+    const long th = i / a.K, tok = th / a.H;
+    const int h = static_cast<int>(th % a.H), G = a.HV / a.H;
+    float dq = 0.f, dk = 0.f;
+    for (int j = 0; j < G; ++j) {
+        const long row = tok * a.HV + h * G + j;
+        const size_t ri = static_cast<size_t>(row) * a.K + kk;
+        dq += a.dqP[ri];
+        dk += a.beta[row] * a.daP[ri] - a.dkrP[ri];
+    }
+    store1<BF16>(a.dq, i, a.scale * dq);
+    store1<BF16>(a.dk, i, dk);
+}
+
+// Sums of e over blocks of kDgBlock tokens: bs[b, hv, k, block].
+__global__ __launch_bounds__(256) void bwd_dg_blocks_kernel(BwdArgs a) {
+    const long n = static_cast<long>(a.B) * a.HV * a.NB * a.K;
+    const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int kk = static_cast<int>(i % a.K);
+    const long r = i / a.K;
+    const int jb = static_cast<int>(r % a.NB);
+    const long bhv = r / a.NB;
+    const int b = static_cast<int>(bhv / a.HV), hv = static_cast<int>(bhv % a.HV);
+    const int t1 = min(a.T, (jb + 1) * kDgBlock);
+    float s = 0.f;
+    for (int t = jb * kDgBlock; t < t1; ++t)
+        s += a.e[((static_cast<size_t>(b) * a.T + t) * a.HV + hv) * a.K + kk];
+    a.bs[(bhv * a.K + kk) * a.NB + jb] = s;
+}
+
+// dg_u = sum over V of S_T (.) dL/dS_T + sum over t >= u of e_t: each thread
+// one block of tokens of one (b, hv, k), starting from the later blocks' sums.
+__global__ __launch_bounds__(256) void bwd_dg_kernel(BwdArgs a) {
+    const long n = static_cast<long>(a.B) * a.HV * a.NB * a.K;
+    const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int kk = static_cast<int>(i % a.K);
+    const long r = i / a.K;
+    const int jb = static_cast<int>(r % a.NB);
+    const long bhv = r / a.NB;
+    const int b = static_cast<int>(bhv / a.HV), hv = static_cast<int>(bhv % a.HV);
+    float acc = 0.f;
+    if (a.dST) {
+        const size_t s0 = (static_cast<size_t>(bhv) * a.K + kk) * a.V;
+        for (int v = 0; v < a.V; ++v) acc += a.ST[s0 + v] * a.dST[s0 + v];
+    }
+    for (int j = a.NB - 1; j > jb; --j) acc += a.bs[(bhv * a.K + kk) * a.NB + j];
+    const int t1 = min(a.T, (jb + 1) * kDgBlock);
+    for (int t = t1 - 1; t >= jb * kDgBlock; --t) {
+        const size_t ei = ((static_cast<size_t>(b) * a.T + t) * a.HV + hv) * a.K + kk;
+        acc += a.e[ei];
+        a.dg[ei] = acc;
+    }
+}
+
+template <int K>
+hipError_t launch_passes(const BwdArgs &a, hipStream_t stream) {
+    const unsigned grid = static_cast<unsigned>(a.B) * a.HV * (a.V / kCols);
+    if (a.bf16)
+        hipLaunchKernelGGL((bwd_state_kernel<K, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((bwd_state_kernel<K, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.T == 0) return e;
+    if (a.bf16)
+        hipLaunchKernelGGL((bwd_grad_kernel<K, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((bwd_grad_kernel<K, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+unsigned blocks_of(long n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
+    if (a.B == 0) return hipSuccess;
+    hipError_t e = a.K == 32 ? launch_passes<32>(a, stream)
+                 : a.K == 64 ? launch_passes<64>(a, stream)
+                 : a.K == 128 ? launch_passes<128>(a, stream) : hipErrorInvalidValue;
+    if (e != hipSuccess || a.T == 0) return e;
+    const long rows = static_cast<long>(a.B) * a.T * a.HV;
+    if (a.bf16) {
+        hipLaunchKernelGGL(bwd_sum_kernel<true>, dim3(blocks_of(rows, 256 / a.K)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(bwd_qk_kernel<true>, dim3(blocks_of(static_cast<long>(a.B) * a.T * a.H * a.K, 256)),
+                           dim3(256), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(bwd_sum_kernel<false>, dim3(blocks_of(rows, 256 / a.K)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(bwd_qk_kernel<false>, dim3(blocks_of(static_cast<long>(a.B) * a.T * a.H * a.K, 256)),
+                           dim3(256), 0, stream, a);
+    }
+    const long nb = static_cast<long>(a.B) * a.HV * a.NB * a.K;
+    hipLaunchKernelGGL(bwd_dg_blocks_kernel, dim3(blocks_of(nb, 256)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dg_kernel, dim3(blocks_of(nb, 256)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace kda

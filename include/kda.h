@@ -108,6 +108,49 @@ int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *
                       float scale, int dtype, void *stream);
 
 /*
+ * kda_recurrent_bwd -- gradients of the forward pass (kda_recurrent_fwd, or
+ * kda_chunk_fwd where it applies: both compute the same function).
+ *
+ * Back-propagation through time over the recurrence, as the backward of
+ * KDAFunction on the page "K3/kda/ops/reference/recurrent.py" derives it
+ * (module docstring, "backward (BPTT, T -> 0)"), with the gradient of the
+ * initial state returned as well.  Given dL/do and dL/dS_T it returns
+ * dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta and dL/dS0 for the same inputs and
+ * scale as the forward call.  Exact for any finite g (no lower bound).
+ *
+ *   q, k, v, g, beta, initial_state, B, T, H, HV, K, V, scale, dtype
+ *                   as for kda_recurrent_fwd (the forward inputs)
+ *   dout          [B, T, HV, V]  dtype, dL/do
+ *   dfinal_state  [B, HV, K, V]  fp32 or NULL (0): dL/dS_T
+ *   dq, dk        [B, T, H, K]   dtype outputs (GQA: summed over the value
+ *                                heads of each q/k head)
+ *   dv            [B, T, HV, V]  dtype output
+ *   dg            [B, T, HV, K]  fp32 output
+ *   dbeta         [B, T, HV]     fp32 output
+ *   dinitial_state [B, HV, K, V] fp32 output, or NULL (not written)
+ *   workspace     device memory of at least
+ *                 kda_recurrent_bwd_workspace_size(B, T, H, HV, K, V) bytes,
+ *                 16-byte aligned, owned by the caller; its contents are
+ *                 scratch (nothing carries over between calls).  May be NULL
+ *                 when B * T == 0.
+ * Outputs and the workspace may not overlap each other or any input.  With
+ * T = 0 only dinitial_state is written (= dfinal_state, or zeros).
+ * kda_recurrent_bwd_workspace_size returns the workspace size in bytes, or -1
+ * (message in kda_last_error) for sizes kda_recurrent_bwd rejects.
+ * Runs the forward recurrence once more (keeping its residuals and final
+ * state in the workspace), then a reverse pass for the state gradient and a
+ * forward pass for the gradients that need the state; all asynchronous on
+ * `stream`.
+ */
+long long kda_recurrent_bwd_workspace_size(int B, int T, int H, int HV, int K, int V);
+int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const float *initial_state, const void *dout,
+                      const float *dfinal_state, void *dq, void *dk, void *dv, float *dg,
+                      float *dbeta, float *dinitial_state, int B, int T, int H, int HV, int K,
+                      int V, float scale, int dtype, void *workspace, long long workspace_bytes,
+                      void *stream);
+
+/*
  * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also writes prefix snapshots
  * of the state, so that decoding can later resume from any whole multiple of
  * snapshot_every tokens (the prefix cache of the page

@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"kda_abi_version", "kda_last_error", "kda_chunk_fwd",
                           "kda_chunk_fwd_snapshots", "kda_recurrent_fwd", "kda_prefill_prologue",
-                          "kda_output_gate", "kda_decode_step"}
+                          "kda_output_gate", "kda_decode_step", "kda_recurrent_bwd",
+                          "kda_recurrent_bwd_workspace_size"}
     L = ctypes.CDLL(kda.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -295,3 +296,57 @@ def test_recurrent_fwd_rejects(over, code, msg):
     err = L.kda_last_error().decode()
     assert rc == code, err
     assert msg in err, err
+
+
+def bwd_call(**over):
+    """kda_recurrent_bwd with fake, disjoint pointers (each BIG apart)."""
+    a = dict(q=BIG, k=2 * BIG, v=3 * BIG, g=4 * BIG, beta=5 * BIG, s0=None, do=6 * BIG, dst=None,
+             dq=7 * BIG, dk=8 * BIG, dv=9 * BIG, dg=10 * BIG, db=11 * BIG, ds0=None, ws=12 * BIG,
+             wsb=1 << 40, B=1, T=8, H=2, HV=4, K=32, V=32, scale=0.0, dtype=1)
+    a.update(over)
+    L = lib()
+    rc = L.kda_recurrent_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["do"], a["dst"],
+                             a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["ds0"], a["B"], a["T"],
+                             a["H"], a["HV"], a["K"], a["V"], a["scale"], a["dtype"], a["ws"], a["wsb"],
+                             None)
+    return rc, L.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(HV=3), 1, "kda_recurrent_bwd: HV=3"),
+    (dict(K=16), 2, "32, 64 or 128"),
+    (dict(dtype=5), 2, "dtype"),
+    (dict(do=None), 1, "dout must be non-NULL"),
+    (dict(dg=None), 1, "dbeta must be non-NULL"),
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(wsb=1000), 1, "needed"),
+    (dict(dq=FAKE + 8), 1, "dq is not 16-byte aligned"),
+    (dict(dv=3 * BIG + 32), 1, "dv overlaps v"),
+    (dict(ws=7 * BIG + 512), 1, "dq overlaps workspace"),
+    (dict(ds0=6 * BIG), 1, "dinitial_state overlaps dout"),
+    (dict(scale=float("inf")), 1, "infinite"),
+])
+def test_recurrent_bwd_rejects(over, code, msg):
+    rc, err = bwd_call(**over)
+    assert rc == code, err
+    assert msg in err, err
+
+
+def test_recurrent_bwd_workspace_size():
+    L = lib()
+    n = L.kda_recurrent_bwd_workspace_size(2, 100, 2, 4, 64, 128)
+    # r, dr [B,T,HV,V]; S_T [B,HV,K,V]; 3 x partials [V/32,B,T,HV,K]; e [B,T,HV,K];
+    # block sums [B,HV,K,ceil(T/64)] -- fp32, each region rounded up to 256 bytes
+    up = lambda floats: (floats * 4 + 255) // 256 * 256
+    want = (2 * up(2 * 100 * 4 * 128) + up(2 * 4 * 64 * 128) + 3 * up(4 * 2 * 100 * 4 * 64)
+            + up(2 * 100 * 4 * 64) + up(2 * 4 * 64 * 2))
+    assert n == want
+    assert L.kda_recurrent_bwd_workspace_size(1, 8, 2, 3, 32, 32) == -1
+    assert "HV=3" in L.kda_last_error().decode()
+    assert L.kda_recurrent_bwd_workspace_size(1, 8, 2, 4, 32, 48) == -1
+
+
+def test_recurrent_bwd_empty_batch_is_noop():
+    rc, err = bwd_call(B=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None, dk=None,
+                       dv=None, dg=None, db=None, ws=None)
+    assert rc == 0, err

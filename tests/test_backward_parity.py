@@ -1,0 +1,131 @@
+"""GPU parity of kda_recurrent_bwd (the backward of the forward pass) against
+the fp64 oracle's back-propagation through time, which the CPU suite checks
+against finite differences."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_delta_rule_kda_amd as kda
+from gated_delta_rule_kda_amd import synth
+from kda_testutil import assert_close, gpu_available, np64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def unbounded_gate(B, T, HV, K, seed):
+    """g = -exp(A_log) * softplus(z + dt_bias), no lower bound (the kda.rs
+    page's bounded_gate without its bound), A_log, dt_bias, z ~ N(0,1)."""
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    A_log = torch.randn(HV, generator=gen)
+    dt = torch.randn(HV * K, generator=gen)
+    z = torch.randn(B, T, HV * K, generator=gen) * 2.0
+    g = -torch.exp(A_log).repeat_interleave(K) * torch.nn.functional.softplus(z + dt)
+    return g.view(B, T, HV, K).contiguous()
+
+
+def run(shape, seed, gate="bounded", with_dst=True, label=""):
+    say("backward case", label, shape, "seed", seed, "gate", gate, "dS_T", with_dst)
+    inp = synth.make_prefill_inputs(shape, DEV, seed)
+    if gate == "unbounded":
+        inp["g"] = unbounded_gate(shape.B, shape.T, shape.HV, shape.K, seed + 1).to(DEV)
+    gen = torch.Generator(device="cpu").manual_seed(seed + 2)
+    dout = torch.randn(shape.B, shape.T, shape.HV, shape.V, generator=gen).to(shape.dtype).to(DEV)
+    dST = (torch.randn(shape.B, shape.HV, shape.K, shape.V, generator=gen) * 0.1).to(DEV) if with_dst else None
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    got = kda.recurrent_bwd(*args, dout, dST, initial_state=inp["S0"])
+    torch.cuda.synchronize()
+    ref = oracle.kda_bwd(*args, dout, dST, initial_state=inp["S0"])
+    stored = (True, True, True, False, False, False)
+    for name, gpu, want, st in zip(NAMES, got, ref, stored):
+        m = assert_close(gpu, want, shape.dtype, st, "%s %s" % (name, label))
+        say("   %-6s max_rel %.2e  excess/rms %.2e" % (name, m["max_rel"], m["excess_over_rms"]))
+    return inp, dout, dST, got
+
+
+CASES = [
+    # B, T, H, HV, K, V, dtype
+    (2, 37, 1, 2, 32, 32, torch.float32),
+    (1, 70, 2, 4, 64, 64, torch.bfloat16),
+    (2, 100, 2, 2, 128, 128, torch.float32),
+    (1, 45, 1, 3, 128, 64, torch.bfloat16),
+    (1, 1, 1, 1, 32, 32, torch.float32),
+    (3, 9, 2, 2, 64, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dT%dH%dHV%dK%dV%d-%s" % (
+    c[:6] + (str(c[6]).split(".")[-1],)))
+@pytest.mark.parametrize("gate,with_dst", [("bounded", True), ("unbounded", False)])
+def test_backward_matches_oracle(case, gate, with_dst):
+    B, T, H, HV, K, V, dt = case
+    shape = synth.PrefillShape(B, T, H, HV, K, V, dt, "normal", s0_std=0.3)
+    run(shape, seed=T + K + V, gate=gate, with_dst=with_dst, label=str(case))
+
+
+def test_backward_empty_sequence():
+    """T = 0: dS0 = dL/dS_T, and nothing else is written."""
+    B, H, HV, K, V = 2, 1, 2, 64, 32
+    z = lambda *s, dt=torch.float32: torch.zeros(*s, dtype=dt, device=DEV)
+    dST = torch.randn(B, HV, K, V, device=DEV)
+    got = kda.recurrent_bwd(z(B, 0, H, K), z(B, 0, H, K), z(B, 0, HV, V), z(B, 0, HV, K), z(B, 0, HV),
+                            z(B, 0, HV, V), dST)
+    torch.cuda.synchronize()
+    assert torch.equal(got[5], dST)
+    got = kda.recurrent_bwd(z(B, 0, H, K), z(B, 0, H, K), z(B, 0, HV, V), z(B, 0, HV, K), z(B, 0, HV),
+                            z(B, 0, HV, V), None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(got[5]) == 0
+
+
+def test_backward_workspace_reuse_and_determinism():
+    """The same call twice through one workspace (with other sizes in between)
+    gives bitwise equal gradients."""
+    shape = synth.PrefillShape(2, 50, 2, 4, 64, 64, torch.bfloat16, "normal", s0_std=0.3)
+    inp = synth.make_prefill_inputs(shape, DEV, 5)
+    dout = torch.randn(2, 50, 4, 64, device=DEV).to(torch.bfloat16)
+    nbytes = kda.recurrent_bwd_workspace_size(2, 50, 2, 4, 64, 64)
+    ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device=DEV)
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dout)
+    a = kda.recurrent_bwd(*args, initial_state=inp["S0"], workspace=ws)
+    small = synth.make_prefill_inputs(synth.PrefillShape(1, 7, 1, 1, 32, 32, torch.bfloat16, "normal"), DEV, 6)
+    kda.recurrent_bwd(small["q"], small["k"], small["v"], small["g"], small["beta"],
+                      torch.ones(1, 7, 1, 32, device=DEV, dtype=torch.bfloat16), workspace=ws)
+    b = kda.recurrent_bwd(*args, initial_state=inp["S0"], workspace=ws)
+    torch.cuda.synchronize()
+    for name, x, y in zip(NAMES, a, b):
+        assert torch.equal(x, y), name
+
+
+def test_full_size_hv96_backward_sampled():
+    """The HV96 shape cut to T = 1024 (B1 H=HV=96 K=V=128 bf16, bounded gate,
+    dL/dS_T given): heads 0 and 95 against the oracle run on just those
+    heads."""
+    shape = synth.PrefillShape(1, 1024, 96, 96, 128, 128, torch.bfloat16, "none")
+    say("full-width backward", shape)
+    inp = synth.make_prefill_inputs(shape, DEV, 0)
+    gen = torch.Generator(device="cpu").manual_seed(3)
+    dout = torch.randn(1, 1024, 96, 128, generator=gen).to(torch.bfloat16).to(DEV)
+    dST = (torch.randn(1, 96, 128, 128, generator=gen) * 0.1).to(DEV)
+    got = kda.recurrent_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dout, dST)
+    torch.cuda.synchronize()
+    for hv in (0, 95):
+        sub = lambda x: x[:, :, hv:hv + 1]
+        ref = oracle.kda_bwd(sub(inp["q"]), sub(inp["k"]), sub(inp["v"]), sub(inp["g"]),
+                             inp["beta"][:, :, hv:hv + 1], sub(dout), dST[:, hv:hv + 1])
+        part = (got[0][:, :, hv:hv + 1], got[1][:, :, hv:hv + 1], got[2][:, :, hv:hv + 1],
+                got[3][:, :, hv:hv + 1], got[4][:, :, hv:hv + 1], got[5][:, hv:hv + 1])
+        for name, gpu, want, st in zip(NAMES, part, ref, (True, True, True, False, False, False)):
+            assert_close(gpu, want, torch.bfloat16, st, "HV96 %s head %d" % (name, hv))
+        say("   head", hv, "ok")
