@@ -171,7 +171,7 @@ bool bwd_layout(BwdLayout &L, int B, int T, int HV, int K, int V) {
     L.NB = (T + kda::kDgBlock - 1) / kda::kDgBlock;
     uint64_t nv, ns, np, ne, nbs;
     if (!count(nv, {B, T, HV, V}) || !count(ns, {B, HV, K, V}) || !count(np, {L.NCB, B, T, HV, K}) ||
-        !count(ne, {B, T, HV, K}) || !count(nbs, {B, HV, K, L.NB}))
+        !count(ne, {B, T, HV, K}) || !count(nbs, {B, HV, K, L.NB + 1}))
         return false;
     uint64_t off = 0;
     auto take = [&](uint64_t floats) {

@@ -41,6 +41,45 @@ __device__ __forceinline__ float across_rows_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Sums over the four DPP rows of a wave (lane positions l % 16 equal) of N
+// values per lane, N in {2, 4, 8}, spread over the result so that every lane
+// keeps some: swapping two different values at each step needs no copies and
+// halves the instructions of summing each value by itself.  After the call,
+// lane l (DPP row j = l / 16) holds in out[i] the sum of value
+// across_index<N>(i, j) -- see below -- over the four rows.
+//   Step 1 (lane swap of the wave's halves) on pairs (x[2m], x[2m+1]):
+//     rows 0,1 keep x[2m] (rows 0+2, 1+3 summed), rows 2,3 x[2m+1].
+//   Step 2 (swap of neighbouring rows) on pairs of those: the four rows of
+//     out[i] end up with values 4i, 4i+2, 4i+1, 4i+3 (N = 2: 0, 0, 1, 1).
+template <int N>
+__device__ __forceinline__ void across_rows_sums(const float (&x)[N], float (&out)[N < 4 ? 1 : N / 4]) {
+    static_assert(N == 2 || N == 4 || N == 8, "2, 4 or 8 values");
+    float h[N / 2];
+#pragma unroll
+    for (int m = 0; m < N / 2; ++m) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[2 * m]), __float_as_uint(x[2 * m + 1]),
+                                                         false, false);
+        h[m] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if constexpr (N == 2) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h[0]), __float_as_uint(h[0]), false, false);
+        out[0] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h[2 * i]), __float_as_uint(h[2 * i + 1]),
+                                                             false, false);
+            out[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+    }
+}
+// which of the N values out[i] of DPP row j holds the sum of
+template <int N>
+__device__ __forceinline__ int across_index(int i, int j) {
+    if constexpr (N == 2) return j >> 1;
+    else return 4 * i + ((j & 1) << 1) + (j >> 1);
+}
+
 // 4 consecutive elements as loaded (bf16: two packed words; fp32: a float4)
 template <bool BF16> struct Raw4;
 template <> struct Raw4<true> { uint2 u; };

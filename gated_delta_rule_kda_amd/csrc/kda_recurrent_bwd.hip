@@ -34,7 +34,7 @@
 // row, so sums over K are four DPP steps.  Sums over V (da, S_t dout,
 // S_dec dr: one K-vector per token) go over the four columns of a wave by the
 // gfx950 lane swaps, then over the waves of the workgroup through LDS, once
-// per round of kTB tokens.
+// per round of staged tokens.
 
 #include "kda_lanes.h"
 
@@ -43,7 +43,8 @@ namespace {
 
 using namespace lanes;
 
-constexpr int kTB = 4;                          // tokens staged per round
+constexpr int kTA = 8;                          // tokens staged per round: reverse pass
+constexpr int kTG = 4;                          // tokens staged per round: forward gradient pass
 constexpr int kRG = 16;                         // lanes per state column
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -71,24 +72,27 @@ __device__ __forceinline__ void read_rows(const float *row, int rg, float (&x)[K
         for (int r = 0; r < RPL; ++r) x[r] = row[row_of<K>(r, rg)];
     }
 }
-// this lane's RPL values into one [K] row of LDS
+// The lane's RPL per-row values summed over the wave's four columns, into
+// one [K] row of LDS: after across_rows_sums every lane holds some of the
+// sums (RPL / 4 of them; with RPL = 2 the rows of the wave's halves hold the
+// same ones, and one half writes).
 template <int K>
-__device__ __forceinline__ void write_rows(float *row, int rg, const float (&x)[K / kRG]) {
+__device__ __forceinline__ void put_column_sums(float *row, int lane, const float (&x)[K / kRG]) {
     constexpr int RPL = K / kRG;
-    if constexpr (RPL >= 4) {
+    float sums[RPL < 4 ? 1 : RPL / 4];
+    across_rows_sums<RPL>(x, sums);
+    const int j = lane / kRG, rg = lane % kRG;
+    if (RPL > 2 || (j & 1) == 0) {
 #pragma unroll
-        for (int r = 0; r < RPL; r += 4)
-            *reinterpret_cast<float4 *>(row + row_of<K>(r, rg)) = make_float4(x[r], x[r + 1], x[r + 2], x[r + 3]);
-    } else {
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) row[row_of<K>(r, rg)] = x[r];
+        for (int i = 0; i < (RPL < 4 ? 1 : RPL / 4); ++i) row[row_of<K>(across_index<RPL>(i, j), rg)] = sums[i];
     }
 }
 
-// Bytes of kTB tokens' rows from token t0 on, for a buffer resource: rows past
+// Bytes of TB tokens' rows from token t0 on, for a buffer resource: rows past
 // the end of the sequence are not covered and read as 0.
+template <int TB>
 __device__ __forceinline__ uint32_t span_bytes(int T, int t0, int stride, int rowlen, int esz) {
-    const int nv = min(kTB, T - t0);
+    const int nv = min(TB, T - t0);
     return nv > 0 ? static_cast<uint32_t>(((nv - 1) * stride + rowlen) * esz) : 0u;
 }
 
@@ -99,14 +103,16 @@ __device__ __forceinline__ uint32_t span_bytes(int T, int t0, int stride, int ro
 template <int K, bool BF16>
 __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
     constexpr int RPL = K / kRG;
-    constexpr int NP = kTB * K / 4;              // 4-element pieces of a [kTB][K] array
+    constexpr int TB = kTA;
+    static_assert(TB % 2 == 0, "tokens go in pairs");
+    constexpr int NP = TB * K / 4;              // 4-element pieces of a [TB][K] array
     static_assert(NP <= kThreads, "one piece per thread at most");
-    constexpr int NCV = kTB * kCols;             // column values per round
+    constexpr int NCV = TB * kCols;             // column values per round
     static_assert(NCV <= kThreads, "one column value per thread at most");
     constexpr int ESZ = BF16 ? 2 : 4;
-    __shared__ __attribute__((aligned(16))) float sQ[kTB][K], sK[kTB][K], sA[kTB][K], sD[kTB][K];
-    __shared__ float sDo[kTB][kCols], sR[kTB][kCols], sDr[kTB][kCols];
-    __shared__ __attribute__((aligned(16))) float sDa[kTB][kWaves][K];
+    __shared__ __attribute__((aligned(16))) float sQ[TB][K], sK[TB][K], sA[TB][K], sD[TB][K];
+    __shared__ float sDo[TB][kCols], sR[TB][kCols], sDr[TB][kCols];
+    __shared__ __attribute__((aligned(16))) float sDa[TB][kWaves][K];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = wave * (64 / kRG) + lane / kRG, rg = lane % kRG;
@@ -131,19 +137,19 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
         const int e = min(tid, NP - 1);
         const int t = e / (K / 4), f = (e % (K / 4)) * 4;
         const auto rq = make_rsrc(static_cast<const char *>(a.q) + (tb * a.H + h) * K * ESZ,
-                                  span_bytes(a.T, t0, a.H * K, K, ESZ));
+                                  span_bytes<TB>(a.T, t0, a.H * K, K, ESZ));
         const auto rk = make_rsrc(static_cast<const char *>(a.k) + (tb * a.H + h) * K * ESZ,
-                                  span_bytes(a.T, t0, a.H * K, K, ESZ));
-        const auto rgr = make_rsrc(a.g + (tb * a.HV + hv) * K, span_bytes(a.T, t0, a.HV * K, K, 4));
-        const auto rb = make_rsrc(a.beta + tb * a.HV + hv, span_bytes(a.T, t0, a.HV, 1, 4));
+                                  span_bytes<TB>(a.T, t0, a.H * K, K, ESZ));
+        const auto rgr = make_rsrc(a.g + (tb * a.HV + hv) * K, span_bytes<TB>(a.T, t0, a.HV * K, K, 4));
+        const auto rb = make_rsrc(a.beta + tb * a.HV + hv, span_bytes<TB>(a.T, t0, a.HV, 1, 4));
         pq = load_raw4<BF16>(rq, (t * a.H * K + f) * ESZ);
         pk = load_raw4<BF16>(rk, (t * a.H * K + f) * ESZ);
         pg = load_f4(rgr, (t * a.HV * K + f) * 4);
         pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * a.HV * 4, 0, 0));
         const int ec = min(tid, NCV - 1), tc = ec / kCols, cc = ec % kCols;
         const auto rdo = make_rsrc(static_cast<const char *>(a.dout) + ((tb * a.HV + hv) * a.V + c0) * ESZ,
-                                   span_bytes(a.T, t0, a.HV * a.V, kCols, ESZ));
-        const auto rr = make_rsrc(a.r + (tb * a.HV + hv) * a.V + c0, span_bytes(a.T, t0, a.HV * a.V, kCols, 4));
+                                   span_bytes<TB>(a.T, t0, a.HV * a.V, kCols, ESZ));
+        const auto rr = make_rsrc(a.r + (tb * a.HV + hv) * a.V + c0, span_bytes<TB>(a.T, t0, a.HV * a.V, kCols, 4));
         pdo = load1<BF16>(rdo, tc * a.HV * a.V + cc);
         pr = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, (tc * a.HV * a.V + cc) * 4, 0, 0));
     };
@@ -164,41 +170,57 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): every prefetched register consumed
     };
 
-    const int last0 = a.T > 0 ? ((a.T - 1) / kTB) * kTB : -kTB;
+    const int last0 = a.T > 0 ? ((a.T - 1) / TB) * TB : -TB;
     if (last0 >= 0) {
         load_round(last0);
         store_round();
     }
     __syncthreads();
-    for (int t0 = last0; t0 >= 0; t0 -= kTB) {
-        if (t0 >= kTB) load_round(t0 - kTB);               // in flight during this round
-#pragma unroll
-        for (int t = kTB - 1; t >= 0; --t) {
-            float q[RPL], k[RPL], av[RPL], d[RPL], Dt[RPL];
-            read_rows<K>(sQ[t], rg, q);
-            read_rows<K>(sK[t], rg, k);
-            read_rows<K>(sA[t], rg, av);
-            read_rows<K>(sD[t], rg, d);
-            const float dout = sDo[t][c], rr = sR[t][c];
-            float s0 = 0.f, s1 = 0.f;
+    for (int t0 = last0; t0 >= 0; t0 -= TB) {
+        if (t0 >= TB) load_round(t0 - TB);               // in flight during this round
+        // a token's operands are read a token ahead of their use (two
+        // alternating register sets), off the token-to-token chain
+        struct Tok {
+            float q[RPL], k[RPL], a[RPL], d[RPL];
+            float dout, r;
+        };
+        auto read_tok = [&](int t, Tok &x) {
+            read_rows<K>(sQ[t], rg, x.q);
+            read_rows<K>(sK[t], rg, x.k);
+            read_rows<K>(sA[t], rg, x.a);
+            read_rows<K>(sD[t], rg, x.d);
+            x.dout = sDo[t][c];
+            x.r = sR[t][c];
+        };
+        auto step = [&](int t, const Tok &x) {
+            float Dt[RPL], s0 = 0.f, s1 = 0.f;
 #pragma unroll
             for (int r = 0; r < RPL; ++r) {
-                Dt[r] = fmaf(q[r], dout, D[r]);                      // D~ = D + qs (x) dout
-                if (r & 1) s1 = fmaf(av[r], Dt[r], s1); else s0 = fmaf(av[r], Dt[r], s0);
+                Dt[r] = fmaf(x.q[r], x.dout, D[r]);                  // D~ = D + qs (x) dout
+                if (r & 1) s1 = fmaf(x.a[r], Dt[r], s1); else s0 = fmaf(x.a[r], Dt[r], s0);
             }
             const float dr = group_sum<kRG>(s0 + s1);               // (beta k)^T D~
             if (rg == 0) sDr[t][c] = dr;
             float pa[RPL];
 #pragma unroll
-            for (int r = 0; r < RPL; ++r) pa[r] = across_rows_sum(Dt[r] * rr);   // da over the wave's columns
-            if (lane < kRG) write_rows<K>(sDa[t][wave], rg, pa);
+            for (int r = 0; r < RPL; ++r) pa[r] = Dt[r] * x.r;
+            put_column_sums<K>(sDa[t][wave], lane, pa);          // da over the wave's columns
 #pragma unroll
-            for (int r = 0; r < RPL; ++r) D[r] = d[r] * fmaf(-k[r], dr, Dt[r]);
+            for (int r = 0; r < RPL; ++r) D[r] = x.d[r] * fmaf(-x.k[r], dr, Dt[r]);
+        };
+        Tok x0, x1;
+        read_tok(TB - 1, x0);
+#pragma unroll
+        for (int t = TB - 1; t > 0; t -= 2) {
+            read_tok(t - 1, x1);
+            step(t, x0);
+            if (t >= 2) read_tok(t - 2, x0);
+            step(t - 1, x1);
         }
         __syncthreads();
         // the next round to LDS (its loads are waited for here, before this
         // round's stores are issued), then the round's dv, dr and da partial sums
-        if (t0 >= kTB) store_round();
+        if (t0 >= TB) store_round();
         if (tid < NCV) {
             const int t = tid / kCols, cc = tid % kCols;
             if (t0 + t < a.T) {
@@ -207,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
                 a.dr[i] = sDr[t][cc];
             }
         }
-        for (int i = tid; i < kTB * K; i += kThreads) {
+        for (int i = tid; i < TB * K; i += kThreads) {
             const int t = i / K, kk = i % K;
             if (t0 + t < a.T) {
                 float s = 0.f;
@@ -231,14 +253,16 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
 template <int K, bool BF16>
 __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
     constexpr int RPL = K / kRG;
-    constexpr int NP = kTB * K / 4;
+    constexpr int TB = kTG;
+    static_assert(TB % 2 == 0, "tokens go in pairs");
+    constexpr int NP = TB * K / 4;
     static_assert(NP <= kThreads, "one piece per thread at most");
-    constexpr int NCV = kTB * kCols;
+    constexpr int NCV = TB * kCols;
     static_assert(NCV <= kThreads, "one column value per thread at most");
     constexpr int ESZ = BF16 ? 2 : 4;
-    __shared__ __attribute__((aligned(16))) float sK[kTB][K], sD[kTB][K];
-    __shared__ float sV[kTB][kCols], sDo[kTB][kCols], sDr[kTB][kCols], sB[kTB];
-    __shared__ __attribute__((aligned(16))) float sDq[kTB][kWaves][K], sDk[kTB][kWaves][K];
+    __shared__ __attribute__((aligned(16))) float sK[TB][K], sD[TB][K];
+    __shared__ float sV[TB][kCols], sDo[TB][kCols], sDr[TB][kCols], sB[TB];
+    __shared__ __attribute__((aligned(16))) float sDq[TB][kWaves][K], sDk[TB][kWaves][K];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = wave * (64 / kRG) + lane / kRG, rg = lane % kRG;
@@ -262,16 +286,16 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
         const int e = min(tid, NP - 1);
         const int t = e / (K / 4), f = (e % (K / 4)) * 4;
         const auto rk = make_rsrc(static_cast<const char *>(a.k) + (tb * a.H + h) * K * ESZ,
-                                  span_bytes(a.T, t0, a.H * K, K, ESZ));
-        const auto rgr = make_rsrc(a.g + (tb * a.HV + hv) * K, span_bytes(a.T, t0, a.HV * K, K, 4));
-        const auto rb = make_rsrc(a.beta + tb * a.HV + hv, span_bytes(a.T, t0, a.HV, 1, 4));
+                                  span_bytes<TB>(a.T, t0, a.H * K, K, ESZ));
+        const auto rgr = make_rsrc(a.g + (tb * a.HV + hv) * K, span_bytes<TB>(a.T, t0, a.HV * K, K, 4));
+        const auto rb = make_rsrc(a.beta + tb * a.HV + hv, span_bytes<TB>(a.T, t0, a.HV, 1, 4));
         pk = load_raw4<BF16>(rk, (t * a.H * K + f) * ESZ);
         pg = load_f4(rgr, (t * a.HV * K + f) * 4);
-        pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (tid & (kTB - 1)) * a.HV * 4, 0, 0));
+        pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (tid & (TB - 1)) * a.HV * 4, 0, 0));
         const int ec = min(tid, NCV - 1), tc = ec / kCols, cc = ec % kCols;
         const size_t cbase = (tb * a.HV + hv) * a.V + c0;
-        const uint32_t cspan_d = span_bytes(a.T, t0, a.HV * a.V, kCols, ESZ);
-        const uint32_t cspan_f = span_bytes(a.T, t0, a.HV * a.V, kCols, 4);
+        const uint32_t cspan_d = span_bytes<TB>(a.T, t0, a.HV * a.V, kCols, ESZ);
+        const uint32_t cspan_f = span_bytes<TB>(a.T, t0, a.HV * a.V, kCols, 4);
         const auto rv = make_rsrc(static_cast<const char *>(a.v) + cbase * ESZ, cspan_d);
         const auto rdo = make_rsrc(static_cast<const char *>(a.dout) + cbase * ESZ, cspan_d);
         const auto rdr = make_rsrc(a.dr + cbase, cspan_f);
@@ -292,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
             sDo[tid / kCols][tid % kCols] = pdo;
             sDr[tid / kCols][tid % kCols] = pdr;
         }
-        if (tid < kTB) sB[tid] = pb;
+        if (tid < TB) sB[tid] = pb;
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): every prefetched register consumed
     };
 
@@ -301,35 +325,51 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
         store_round();
     }
     __syncthreads();
-    for (int t0 = 0; t0 < a.T; t0 += kTB) {
-        if (t0 + kTB < a.T) load_round(t0 + kTB);
-#pragma unroll
-        for (int t = 0; t < kTB; ++t) {
+    for (int t0 = 0; t0 < a.T; t0 += TB) {
+        if (t0 + TB < a.T) load_round(t0 + TB);
+        struct Tok {
             float k[RPL], d[RPL];
-            read_rows<K>(sK[t], rg, k);
-            read_rows<K>(sD[t], rg, d);
-            const float v = sV[t][c], dout = sDo[t][c], dr = sDr[t][c], beta = sB[t];
+            float v, dout, dr, beta;
+        };
+        auto read_tok = [&](int t, Tok &x) {
+            read_rows<K>(sK[t], rg, x.k);
+            read_rows<K>(sD[t], rg, x.d);
+            x.v = sV[t][c];
+            x.dout = sDo[t][c];
+            x.dr = sDr[t][c];
+            x.beta = sB[t];
+        };
+        auto step = [&](int t, const Tok &x) {
             float pk_[RPL], s0 = 0.f, s1 = 0.f;
 #pragma unroll
             for (int r = 0; r < RPL; ++r) {
-                S[r] *= d[r];                                        // S_dec
-                if (r & 1) s1 = fmaf(k[r], S[r], s1); else s0 = fmaf(k[r], S[r], s0);
+                S[r] *= x.d[r];                                      // S_dec
+                if (r & 1) s1 = fmaf(x.k[r], S[r], s1); else s0 = fmaf(x.k[r], S[r], s0);
             }
 #pragma unroll
-            for (int r = 0; r < RPL; ++r) pk_[r] = across_rows_sum(S[r] * dr);    // S_dec dr
-            if (lane < kRG) write_rows<K>(sDk[t][wave], rg, pk_);
-            const float u = beta * (v - group_sum<kRG>(s0 + s1));
+            for (int r = 0; r < RPL; ++r) pk_[r] = S[r] * x.dr;
+            put_column_sums<K>(sDk[t][wave], lane, pk_);         // S_dec dr over the wave's columns
+            const float u = x.beta * (x.v - group_sum<kRG>(s0 + s1));
             float pq_[RPL];
 #pragma unroll
             for (int r = 0; r < RPL; ++r) {
-                S[r] = fmaf(k[r], u, S[r]);                          // S_t
-                pq_[r] = across_rows_sum(S[r] * dout);               // S_t dout
+                S[r] = fmaf(x.k[r], u, S[r]);                        // S_t
+                pq_[r] = S[r] * x.dout;
             }
-            if (lane < kRG) write_rows<K>(sDq[t][wave], rg, pq_);
+            put_column_sums<K>(sDq[t][wave], lane, pq_);         // S_t dout over the wave's columns
+        };
+        Tok x0, x1;
+        read_tok(0, x0);
+#pragma unroll
+        for (int t = 0; t < TB; t += 2) {
+            read_tok(t + 1, x1);
+            step(t, x0);
+            if (t + 2 < TB) read_tok(t + 2, x0);
+            step(t + 1, x1);
         }
         __syncthreads();
-        if (t0 + kTB < a.T) store_round();                 // the next round (see the reverse pass)
-        for (int i = tid; i < kTB * K; i += kThreads) {
+        if (t0 + TB < a.T) store_round();                 // the next round (see the reverse pass)
+        for (int i = tid; i < TB * K; i += kThreads) {
             const int t = i / K, kk = i % K;
             if (t0 + t < a.T) {
                 float sq = 0.f, sk = 0.f;
@@ -409,7 +449,9 @@ __global__ __launch_bounds__(256) void bwd_qk_kernel(BwdArgs a) {
     store1<BF16>(a.dk, i, dk);
 }
 
-// Sums of e over blocks of kDgBlock tokens: bs[b, hv, k, block].
+// Sums of e over blocks of kDgBlock tokens: bs[b, hv, k, block], and in the
+// entry after the last block the final-state term sum over V of
+// S_T (.) dL/dS_T (0 without dL/dS_T).
 __global__ __launch_bounds__(256) void bwd_dg_blocks_kernel(BwdArgs a) {
     const long n = static_cast<long>(a.B) * a.HV * a.NB * a.K;
     const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
@@ -423,11 +465,21 @@ __global__ __launch_bounds__(256) void bwd_dg_blocks_kernel(BwdArgs a) {
     float s = 0.f;
     for (int t = jb * kDgBlock; t < t1; ++t)
         s += a.e[((static_cast<size_t>(b) * a.T + t) * a.HV + hv) * a.K + kk];
-    a.bs[(bhv * a.K + kk) * a.NB + jb] = s;
+    float *row = a.bs + (bhv * a.K + kk) * (a.NB + 1);
+    row[jb] = s;
+    if (jb == a.NB - 1) {
+        float c = 0.f;
+        if (a.dST) {
+            const size_t s0 = (static_cast<size_t>(bhv) * a.K + kk) * a.V;
+            for (int v = 0; v < a.V; ++v) c += a.ST[s0 + v] * a.dST[s0 + v];
+        }
+        row[a.NB] = c;
+    }
 }
 
 // dg_u = sum over V of S_T (.) dL/dS_T + sum over t >= u of e_t: each thread
-// one block of tokens of one (b, hv, k), starting from the later blocks' sums.
+// one block of tokens of one (b, hv, k), starting from the final-state term
+// and the later blocks' sums.
 __global__ __launch_bounds__(256) void bwd_dg_kernel(BwdArgs a) {
     const long n = static_cast<long>(a.B) * a.HV * a.NB * a.K;
     const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
@@ -437,12 +489,9 @@ __global__ __launch_bounds__(256) void bwd_dg_kernel(BwdArgs a) {
     const int jb = static_cast<int>(r % a.NB);
     const long bhv = r / a.NB;
     const int b = static_cast<int>(bhv / a.HV), hv = static_cast<int>(bhv % a.HV);
-    float acc = 0.f;
-    if (a.dST) {
-        const size_t s0 = (static_cast<size_t>(bhv) * a.K + kk) * a.V;
-        for (int v = 0; v < a.V; ++v) acc += a.ST[s0 + v] * a.dST[s0 + v];
-    }
-    for (int j = a.NB - 1; j > jb; --j) acc += a.bs[(bhv * a.K + kk) * a.NB + j];
+    const float *row = a.bs + (bhv * a.K + kk) * (a.NB + 1);
+    float acc = row[a.NB];
+    for (int j = a.NB - 1; j > jb; --j) acc += row[j];
     const int t1 = min(a.T, (jb + 1) * kDgBlock);
     for (int t = t1 - 1; t >= jb * kDgBlock; --t) {
         const size_t ei = ((static_cast<size_t>(b) * a.T + t) * a.HV + hv) * a.K + kk;

@@ -336,10 +336,11 @@ def test_recurrent_bwd_workspace_size():
     L = lib()
     n = L.kda_recurrent_bwd_workspace_size(2, 100, 2, 4, 64, 128)
     # r, dr [B,T,HV,V]; S_T [B,HV,K,V]; 3 x partials [V/32,B,T,HV,K]; e [B,T,HV,K];
-    # block sums [B,HV,K,ceil(T/64)] -- fp32, each region rounded up to 256 bytes
+    # block sums and the final-state term [B,HV,K,ceil(T/64)+1] -- fp32, each
+    # region rounded up to 256 bytes
     up = lambda floats: (floats * 4 + 255) // 256 * 256
     want = (2 * up(2 * 100 * 4 * 128) + up(2 * 4 * 64 * 128) + 3 * up(4 * 2 * 100 * 4 * 64)
-            + up(2 * 100 * 4 * 64) + up(2 * 4 * 64 * 2))
+            + up(2 * 100 * 4 * 64) + up(2 * 4 * 64 * 3))
     assert n == want
     assert L.kda_recurrent_bwd_workspace_size(1, 8, 2, 3, 32, 32) == -1
     assert "HV=3" in L.kda_last_error().decode()
