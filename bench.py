@@ -16,8 +16,9 @@ Headline workload (one JSON line on stdout):
     with prefix snapshots of the state every 1024 and every 32 tokens
     (kda_chunk_fwd_snapshots; the snapshot stores count in the bytes), and the
     layer's per-token stages on the HV96 shape (kda_prefill_prologue,
-    kda_output_gate) against the HBM peak, and kda_recurrent_fwd on the HV96
-    workload with an unbounded gate (against the fp32 vector peak).
+    kda_output_gate) against the HBM peak, kda_recurrent_fwd on the HV96
+    workload with an unbounded gate, and kda_recurrent_bwd (the backward) on
+    the HV96 workload (both against the fp32 vector peak).
 Inputs are seeded synthetic tensors (gated_delta_rule_kda_amd.synth) created on
 the GPU before the timed region.  Kernel durations come from HIP events
 recorded on the stream the kernels are launched on.  The CPU baseline runs the
@@ -277,6 +278,51 @@ def bench_layer_stages(steps, warmup):
     return res
 
 
+def backward_alg_flops(B, T, HV, K, V):
+    """The gradient's own arithmetic per token and value head, as the
+    back-propagation through time forms it: D += qs dout^T, S_t dout, D r,
+    a^T D, D - k dr^T, S_dec dr, rowsum(S_dec * D_dec) (2KV each) and the
+    decay (KV): 15KV (the forward recompute not counted)."""
+    return 15 * K * V * B * T * HV
+
+
+def bench_backward(shape, steps, warmup, inp=None):
+    """kda_recurrent_bwd on `shape` with dL/do ~ N(0,1) and dL/dS_T ~ 0.1 N(0,1);
+    workspace and outputs allocated before the timed region."""
+    import torch
+    import gated_delta_rule_kda_amd as kda
+    from gated_delta_rule_kda_amd import synth
+    dev = torch.device("cuda:0")
+    if inp is None:
+        inp = synth.make_prefill_inputs(shape, dev, 0)
+    B, T, H, HV, K, V = shape.B, shape.T, shape.H, shape.HV, shape.K, shape.V
+    gen = torch.Generator(device=dev).manual_seed(1)
+    dout = torch.randn(B, T, HV, V, generator=gen, device=dev).to(shape.dtype)
+    dST = torch.randn(B, HV, K, V, generator=gen, device=dev) * 0.1
+    ws = torch.empty(kda.recurrent_bwd_workspace_size(B, T, H, HV, K, V), dtype=torch.uint8, device=dev)
+    outs = (torch.empty(B, T, H, K, dtype=shape.dtype, device=dev),
+            torch.empty(B, T, H, K, dtype=shape.dtype, device=dev),
+            torch.empty(B, T, HV, V, dtype=shape.dtype, device=dev),
+            torch.empty(B, T, HV, K, device=dev), torch.empty(B, T, HV, device=dev),
+            torch.empty(B, HV, K, V, device=dev))
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dout, dST)
+
+    def call():
+        kda.recurrent_bwd(*args, initial_state=inp["S0"], workspace=ws, out=outs)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts, ends = time_calls(call, steps, stream)
+    torch.cuda.synchronize()
+    ms = sum(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)) / steps
+    flops = backward_alg_flops(B, T, HV, K, V)
+    log("[backward] avg %.3f ms, %.1f TFLOP/s (15KV per token-head), workspace %.2f GB"
+        % (ms, flops / (ms * 1e-3) / 1e12, ws.numel() / 1e9))
+    return dict(avg_ms=ms, flops=flops, tokens=B * T, workspace=ws.numel())
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,7 +335,9 @@ def main():
     ap.add_argument("--no-snapshots", action="store_true")
     ap.add_argument("--no-layer-stages", action="store_true")
     ap.add_argument("--no-unbounded", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy", "snap", "stages", "unbounded"],
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy", "snap", "stages", "unbounded",
+                                       "backward"],
                     default=None,
                     help="run one workload only (for profiler runs); prints no JSON line")
     args = ap.parse_args()
@@ -328,6 +376,9 @@ def main():
         return
     if args.only == "stages":
         bench_layer_stages(args.steps, args.warmup)
+        return
+    if args.only == "backward":
+        bench_backward(synth.PREFILL_HV96_BF16, args.steps, args.warmup)
         return
     if args.only == "snap":
         bench_prefill(synth.PREFILL_HV96_BF16, args.steps, args.warmup, "hv96 snapshots/1024", 1024)
@@ -405,6 +456,17 @@ def main():
                          "frac": tf * 1e12 / FP32_VALU_PEAK,
                          "flops_per_launch": ub["flops"]}}
         del ub
+    if not args.no_backward:
+        bw = bench_backward(shape, max(3, args.steps // 4), min(args.warmup, 3), inp=p["inp"])
+        tf = bw["flops"] / (bw["avg_ms"] * 1e-3) / 1e12
+        line["backward"] = {
+            "workload": "kda_recurrent_bwd on the HV96 workload (B1 T8192 H=HV=96 K=V=128 bf16, bounded "
+                        "gate), dL/do ~ N(0,1), dL/dS_T ~ 0.1 N(0,1): dq, dk, dv, dg, dbeta, dS0",
+            "tokens_per_s": bw["tokens"] / (bw["avg_ms"] * 1e-3), "avg_call_ms": bw["avg_ms"],
+            "workspace_bytes": bw["workspace"],
+            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": tf * 1e12 / FP32_VALU_PEAK, "flops_per_call": bw["flops"]}}
+        del bw
     if not args.no_layer_stages:
         st = bench_layer_stages(args.steps, args.warmup)
         line["layer_stages"] = {

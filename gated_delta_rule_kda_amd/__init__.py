@@ -217,14 +217,15 @@ def recurrent_bwd_workspace_size(B, T, H, HV, K, V) -> int:
 
 
 def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initial_state=None,
-                  *, workspace=None, need_d_initial_state=True):
+                  *, workspace=None, need_d_initial_state=True, out=None):
     """``kda_recurrent_bwd``: gradients of the forward pass with the same
     inputs (any finite g).  dout [B,T,HV,V] is dL/do (v's dtype),
     d_final_state [B,HV,K,V] fp32 (or None) is dL/dS_T.  Returns (dq, dk
     [B,T,H,K] and dv [B,T,HV,V] in q's dtype, dg [B,T,HV,K], dbeta [B,T,HV],
     dS0 [B,HV,K,V] fp32 or None).  ``workspace`` (a uint8 GPU tensor of at
     least :func:`recurrent_bwd_workspace_size` bytes) may be passed to avoid
-    an allocation."""
+    an allocation, and ``out`` (the six result tensors, dS0 may be None) to
+    write into."""
     _need(q, "q")
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
@@ -242,12 +243,21 @@ def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initia
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", torch.uint8, None, dev)
-    dq = torch.empty(B, T, H, K, dtype=dt, device=dev)
-    dk = torch.empty(B, T, H, K, dtype=dt, device=dev)
-    dv = torch.empty(B, T, HV, V, dtype=dt, device=dev)
-    dg = torch.empty(B, T, HV, K, dtype=torch.float32, device=dev)
-    db = torch.empty(B, T, HV, dtype=torch.float32, device=dev)
-    dS0 = torch.empty(B, HV, K, V, dtype=torch.float32, device=dev) if need_d_initial_state else None
+    if out is None:
+        dq = torch.empty(B, T, H, K, dtype=dt, device=dev)
+        dk = torch.empty(B, T, H, K, dtype=dt, device=dev)
+        dv = torch.empty(B, T, HV, V, dtype=dt, device=dev)
+        dg = torch.empty(B, T, HV, K, dtype=torch.float32, device=dev)
+        db = torch.empty(B, T, HV, dtype=torch.float32, device=dev)
+        dS0 = torch.empty(B, HV, K, V, dtype=torch.float32, device=dev) if need_d_initial_state else None
+    else:
+        dq, dk, dv, dg, db, dS0 = out
+        for t_, n_, d_, s_ in ((dq, "dq", dt, (B, T, H, K)), (dk, "dk", dt, (B, T, H, K)),
+                               (dv, "dv", dt, (B, T, HV, V)), (dg, "dg", torch.float32, (B, T, HV, K)),
+                               (db, "dbeta", torch.float32, (B, T, HV))):
+            _need(t_, n_, d_, s_, dev)
+        if dS0 is not None:
+            _need(dS0, "dS0", torch.float32, (B, HV, K, V), dev)
     with torch.cuda.device(dev):
         _check(_load().kda_recurrent_bwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dout),
