@@ -407,9 +407,6 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(BwdArgs a) {
             dkr += a.dkrP[cb * plane + i];
             dqs += a.dqP[cb * plane + i];
         }
-        a.daP[i] = da;
-        a.dkrP[i] = dkr;
-        a.dqP[i] = dqs;
         const long tok = row / a.HV;
         const int hv = static_cast<int>(row % a.HV), h = hv / (a.HV / a.H);
         const size_t qi = (static_cast<size_t>(tok) * a.H + h) * K + kk;
@@ -418,6 +415,16 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(BwdArgs a) {
         const float beta = a.beta[row];
         a.e[i] = a.scale * q * dqs - k * (dkr + beta * da);
         prod = k * da;
+        if (a.H == a.HV) {
+            // one value head per q/k head: dq and dk are this row's own
+            store1<BF16>(a.dq, qi, a.scale * dqs);
+            store1<BF16>(a.dk, qi, beta * da - dkr);
+        } else {
+            // kept for the sums over the value heads of a q/k head
+            a.daP[i] = da;
+            a.dkrP[i] = dkr;
+            a.dqP[i] = dqs;
+        }
     }
     sRed[tid] = prod;
     __syncthreads();
@@ -428,8 +435,9 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(BwdArgs a) {
     }
 }
 
-// dq = scale * sum over the q/k head's value heads of S_t dout; dk = sum of
-// beta da - S_dec dr.  One element of [B,T,H,K] per thread.
+// With GQA (HV > H): dq = scale * sum over the q/k head's value heads of
+// S_t dout; dk = sum of beta da - S_dec dr.  One element of [B,T,H,K] per
+// thread.
 template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_qk_kernel(BwdArgs a) {
     const long n = static_cast<long>(a.B) * a.T * a.H * a.K;
@@ -461,17 +469,25 @@ __global__ __launch_bounds__(256) void bwd_dg_blocks_kernel(BwdArgs a) {
     const int jb = static_cast<int>(r % a.NB);
     const long bhv = r / a.NB;
     const int b = static_cast<int>(bhv / a.HV), hv = static_cast<int>(bhv % a.HV);
-    const int t1 = min(a.T, (jb + 1) * kDgBlock);
+    const int tb = jb * kDgBlock;
+    const size_t step = static_cast<size_t>(a.HV) * a.K;
+    const float *e = a.e + ((static_cast<size_t>(b) * a.T + tb) * a.HV + hv) * a.K + kk;
     float s = 0.f;
-    for (int t = jb * kDgBlock; t < t1; ++t)
-        s += a.e[((static_cast<size_t>(b) * a.T + t) * a.HV + hv) * a.K + kk];
+#pragma unroll 16
+    for (int t = 0; t < kDgBlock; ++t)
+        if (tb + t < a.T) s += e[t * step];
     float *row = a.bs + (bhv * a.K + kk) * (a.NB + 1);
     row[jb] = s;
     if (jb == a.NB - 1) {
         float c = 0.f;
         if (a.dST) {
-            const size_t s0 = (static_cast<size_t>(bhv) * a.K + kk) * a.V;
-            for (int v = 0; v < a.V; ++v) c += a.ST[s0 + v] * a.dST[s0 + v];
+            const float4 *st = reinterpret_cast<const float4 *>(a.ST + (static_cast<size_t>(bhv) * a.K + kk) * a.V);
+            const float4 *ds = reinterpret_cast<const float4 *>(a.dST + (static_cast<size_t>(bhv) * a.K + kk) * a.V);
+#pragma unroll 8
+            for (int v = 0; v < a.V / 4; ++v) {
+                const float4 x = st[v], y = ds[v];
+                c += (x.x * y.x + x.y * y.y) + (x.z * y.z + x.w * y.w);
+            }
         }
         row[a.NB] = c;
     }
@@ -527,14 +543,13 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
                  : a.K == 128 ? launch_passes<128>(a, stream) : hipErrorInvalidValue;
     if (e != hipSuccess || a.T == 0) return e;
     const long rows = static_cast<long>(a.B) * a.T * a.HV;
+    const unsigned qk_blocks = blocks_of(static_cast<long>(a.B) * a.T * a.H * a.K, 256);
     if (a.bf16) {
         hipLaunchKernelGGL(bwd_sum_kernel<true>, dim3(blocks_of(rows, 256 / a.K)), dim3(256), 0, stream, a);
-        hipLaunchKernelGGL(bwd_qk_kernel<true>, dim3(blocks_of(static_cast<long>(a.B) * a.T * a.H * a.K, 256)),
-                           dim3(256), 0, stream, a);
+        if (a.H != a.HV) hipLaunchKernelGGL(bwd_qk_kernel<true>, dim3(qk_blocks), dim3(256), 0, stream, a);
     } else {
         hipLaunchKernelGGL(bwd_sum_kernel<false>, dim3(blocks_of(rows, 256 / a.K)), dim3(256), 0, stream, a);
-        hipLaunchKernelGGL(bwd_qk_kernel<false>, dim3(blocks_of(static_cast<long>(a.B) * a.T * a.H * a.K, 256)),
-                           dim3(256), 0, stream, a);
+        if (a.H != a.HV) hipLaunchKernelGGL(bwd_qk_kernel<false>, dim3(qk_blocks), dim3(256), 0, stream, a);
     }
     const long nb = static_cast<long>(a.B) * a.HV * a.NB * a.K;
     hipLaunchKernelGGL(bwd_dg_blocks_kernel, dim3(blocks_of(nb, 256)), dim3(256), 0, stream, a);
