@@ -1,6 +1,6 @@
 // Lane-level helpers shared by the token-recurrent kernels (forward and
-// backward): buffer-resource loads, bf16 widening, DPP sums, the hardware
-// exponential.
+// backward): buffer-resource loads, bf16 widening, DPP sums, sums across the
+// DPP rows of a wave, the hardware exponential.
 #pragma once
 #include "kda_internal.h"
 
@@ -31,16 +31,6 @@ __device__ __forceinline__ float group_sum(float s) {
     if constexpr (N == 16) s += dpp<0x140>(s);   // row_mirror
     return s;
 }
-// Sum of the four lanes l % 16 + 16 j (j = 0..3: the same position in each DPP
-// row), in every lane: the gfx950 lane swaps exchange the wave's halves
-// (lanes l and l + 32), then neighbouring rows (l and l + 16).
-__device__ __forceinline__ float across_rows_sum(float x) {
-    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float y = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // Sums over the four DPP rows of a wave (lane positions l % 16 equal) of N
 // values per lane, N in {2, 4, 8}, spread over the result so that every lane
 // keeps some: swapping two different values at each step needs no copies and
