@@ -112,9 +112,9 @@ int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *
  * kda_chunk_fwd where it applies: both compute the same function).
  *
  * Back-propagation through time over the recurrence, as the backward of
- * KDAFunction on the page "K3/kda/ops/reference/recurrent.py" derives it
- * (module docstring, "backward (BPTT, T -> 0)"), with the gradient of the
- * initial state returned as well.  Given dL/do and dL/dS_T it returns
+ * KDAFunction on the page "K3/kda/ops/reference/recurrent.py" derives it (the
+ * derivation in its module docstring), with the gradient of the initial state
+ * returned as well.  Given dL/do and dL/dS_T it returns
  * dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta and dL/dS0 for the same inputs and
  * scale as the forward call.  Exact for any finite g (no lower bound).
  *
