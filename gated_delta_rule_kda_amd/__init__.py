@@ -24,7 +24,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "recurrent_fwd", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
+__all__ = ["kda", "chunk_fwd", "recurrent_bwd", "recurrent_bwd_workspace_size", "chunk_fwd_snapshots", "recurrent_fwd", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
            "GATE_DIRECT", "GATE_BOUNDED", "GATE_SOFTPLUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -286,6 +286,38 @@ def chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
             _ptr(final_state), B, T, H, HV, K, V, float(scale) if scale else 0.0,
             int(chunk_size), _dtype_code(q.dtype), _stream_handle(dev)))
     return out, final_state
+
+
+class _KDA(torch.autograd.Function):
+    """Forward by kda_chunk_fwd (chunked) or kda_recurrent_fwd, backward by
+    kda_recurrent_bwd: the two forward kernels compute the same function."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, initial_state, scale, chunked):
+        fwd = chunk_fwd if chunked else recurrent_fwd
+        o, S = fwd(q, k, v, g, beta, scale=scale, initial_state=initial_state, output_final_state=True)
+        ctx.save_for_backward(q, k, v, g, beta, initial_state)
+        ctx.scale = scale
+        return o, S
+
+    @staticmethod
+    def backward(ctx, do, dS):
+        q, k, v, g, beta, S0 = ctx.saved_tensors
+        do = torch.zeros_like(v) if do is None else do.contiguous()
+        dS = None if dS is None else dS.contiguous()
+        dq, dk, dv, dg, db, dS0 = recurrent_bwd(q, k, v, g, beta, do, dS, scale=ctx.scale, initial_state=S0,
+                                                need_d_initial_state=S0 is not None)
+        return dq, dk, dv, dg, db, dS0, None, None
+
+
+def kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False, *, chunked=True):
+    """KDA forward with autograd: the interface of naive_kda on the
+    "K3/kda/ops/reference/recurrent.py" page.  Returns (o, final state or
+    None); gradients reach q, k, v, g, beta and initial_state.  ``chunked``
+    picks kda_chunk_fwd (needs -5 <= g <= 0) or kda_recurrent_fwd (any g)
+    for the forward; the backward is kda_recurrent_bwd either way."""
+    o, S = _KDA.apply(q, k, v, g, beta, initial_state, scale, chunked)
+    return o, (S if output_final_state else None)
 
 
 def _prologue_struct(C, dev, conv_weight, conv_state, l2norm_qk, l2_eps, gate_mode, A_log,

@@ -129,3 +129,24 @@ def test_full_size_hv96_backward_sampled():
         for name, gpu, want, st in zip(NAMES, part, ref, (True, True, True, False, False, False)):
             assert_close(gpu, want, torch.bfloat16, st, "HV96 %s head %d" % (name, hv))
         say("   head", hv, "ok")
+
+
+@pytest.mark.parametrize("chunked,dt", [(True, torch.bfloat16), (False, torch.float32)])
+def test_autograd_function_matches_oracle(chunked, dt):
+    """kda.kda (forward kernel + kda_recurrent_bwd under torch.autograd): the
+    gradients of L = sum(o * Wo) + sum(S_T * WS) reach every input and equal
+    the oracle's."""
+    shape = synth.PrefillShape(2, 41, 1, 2, 64, 64, dt, "normal", s0_std=0.3)
+    inp = synth.make_prefill_inputs(shape, DEV, 17)
+    gen = torch.Generator(device="cpu").manual_seed(18)
+    Wo = torch.randn(2, 41, 2, 64, generator=gen).to(dt).to(DEV)
+    WS = (torch.randn(2, 2, 64, 64, generator=gen) * 0.1).to(DEV)
+    leaves = {n: inp[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g", "beta", "S0")}
+    o, S = kda.kda(leaves["q"], leaves["k"], leaves["v"], leaves["g"], leaves["beta"],
+                   initial_state=leaves["S0"], output_final_state=True, chunked=chunked)
+    ((o.float() * Wo.float()).sum() + (S * WS).sum()).backward()
+    torch.cuda.synchronize()
+    ref = oracle.kda_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], Wo, WS, initial_state=inp["S0"])
+    for name, want, st in zip(("q", "k", "v", "g", "beta", "S0"), ref, (True, True, True, False, False, False)):
+        assert leaves[name].grad is not None, name
+        assert_close(leaves[name].grad, want, dt, st, "autograd d%s" % name)
