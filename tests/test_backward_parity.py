@@ -62,6 +62,9 @@ CASES = [
     (1, 45, 1, 3, 128, 64, torch.bfloat16),
     (1, 1, 1, 1, 32, 32, torch.float32),
     (3, 9, 2, 2, 64, 128, torch.bfloat16),
+    (2, 33, 2, 2, 64, 128, torch.float32),
+    (1, 24, 1, 4, 32, 128, torch.bfloat16),
+    (1, 19, 1, 1, 128, 32, torch.float32),
 ]
 
 
