@@ -44,7 +44,7 @@ namespace {
 using namespace lanes;
 
 constexpr int kTA = 8;                          // tokens staged per round: reverse pass
-constexpr int kTG = 4;                          // tokens staged per round: forward gradient pass
+constexpr int kTG = 8;                          // tokens staged per round: forward gradient pass
 constexpr int kRG = 16;                         // lanes per state column
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -260,9 +260,18 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
     constexpr int NCV = TB * kCols;
     static_assert(NCV <= kThreads, "one column value per thread at most");
     constexpr int ESZ = BF16 ? 2 : 4;
-    __shared__ __attribute__((aligned(16))) float sK[TB][K], sD[TB][K];
-    __shared__ float sV[TB][kCols], sDo[TB][kCols], sDr[TB][kCols], sB[TB];
-    __shared__ __attribute__((aligned(16))) float sDq[TB][kWaves][K], sDk[TB][kWaves][K];
+    // LDS (dynamic: more than the 64 KB of static shared memory), carved as
+    // sK, sD [TB][K]; sDq, sDk [TB][kWaves][K]; sV, sDo, sDr [TB][kCols]; sB [TB]
+    extern __shared__ __attribute__((aligned(16))) float grad_lds[];
+    float (*sK)[K] = reinterpret_cast<float (*)[K]>(grad_lds);
+    float (*sD)[K] = reinterpret_cast<float (*)[K]>(grad_lds + TB * K);
+    float (*sDq)[kWaves][K] = reinterpret_cast<float (*)[kWaves][K]>(grad_lds + 2 * TB * K);
+    float (*sDk)[kWaves][K] = reinterpret_cast<float (*)[kWaves][K]>(grad_lds + 2 * TB * K + TB * kWaves * K);
+    float *cols = grad_lds + 2 * TB * K + 2 * TB * kWaves * K;
+    float (*sV)[kCols] = reinterpret_cast<float (*)[kCols]>(cols);
+    float (*sDo)[kCols] = reinterpret_cast<float (*)[kCols]>(cols + TB * kCols);
+    float (*sDr)[kCols] = reinterpret_cast<float (*)[kCols]>(cols + 2 * TB * kCols);
+    float *sB = cols + 3 * TB * kCols;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = wave * (64 / kRG) + lane / kRG, rg = lane % kRG;
@@ -525,10 +534,16 @@ hipError_t launch_passes(const BwdArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((bwd_state_kernel<K, false>), dim3(grid), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.T == 0) return e;
+    // the forward gradient pass's LDS (see bwd_grad_kernel)
+    constexpr int grad_lds = (2 * kTG * K + 2 * kTG * kWaves * K + 3 * kTG * kCols + kTG) * 4;
+    const void *kern = a.bf16 ? reinterpret_cast<const void *>(bwd_grad_kernel<K, true>)
+                              : reinterpret_cast<const void *>(bwd_grad_kernel<K, false>);
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, grad_lds);
+    if (e != hipSuccess) return e;
     if (a.bf16)
-        hipLaunchKernelGGL((bwd_grad_kernel<K, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((bwd_grad_kernel<K, true>), dim3(grid), dim3(kThreads), grad_lds, stream, a);
     else
-        hipLaunchKernelGGL((bwd_grad_kernel<K, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((bwd_grad_kernel<K, false>), dim3(grid), dim3(kThreads), grad_lds, stream, a);
     return hipGetLastError();
 }
 
