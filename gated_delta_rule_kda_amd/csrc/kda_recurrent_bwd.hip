@@ -517,11 +517,15 @@ __global__ __launch_bounds__(256) void bwd_dg_kernel(BwdArgs a) {
     const float *row = a.bs + (bhv * a.K + kk) * (a.NB + 1);
     float acc = row[a.NB];
     for (int j = a.NB - 1; j > jb; --j) acc += row[j];
-    const int t1 = min(a.T, (jb + 1) * kDgBlock);
-    for (int t = t1 - 1; t >= jb * kDgBlock; --t) {
-        const size_t ei = ((static_cast<size_t>(b) * a.T + t) * a.HV + hv) * a.K + kk;
-        acc += a.e[ei];
-        a.dg[ei] = acc;
+    const int tb = jb * kDgBlock;
+    const size_t step = static_cast<size_t>(a.HV) * a.K;
+    const size_t base = ((static_cast<size_t>(b) * a.T + tb) * a.HV + hv) * a.K + kk;
+#pragma unroll 16
+    for (int t = kDgBlock - 1; t >= 0; --t) {
+        if (tb + t < a.T) {
+            acc += a.e[base + t * step];
+            a.dg[base + t * step] = acc;
+        }
     }
 }
 
