@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(PrefillArgs a) {
             const int e = min(tid + i * kThreads, NP - 1);
             const int t = e / (K / 4), f = (e % (K / 4)) * 4;
             pk[i] = load_raw4<BF16>(rk, (t * a.H * K + f) * ESZ);
-            pq[i] = load_raw4<BF16>(rq, (t * a.H * K + f) * ESZ);
+            if constexpr (!RES) pq[i] = load_raw4<BF16>(rq, (t * a.H * K + f) * ESZ);   // no readout in RES
             const auto gg = __builtin_amdgcn_raw_buffer_load_b128(rgr, (t * a.HV * K + f) * 4, 0, 0);
             pg[i] = make_float4(__uint_as_float(gg[0]), __uint_as_float(gg[1]), __uint_as_float(gg[2]),
                                 __uint_as_float(gg[3]));
@@ -149,18 +149,21 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(PrefillArgs a) {
             // reads only lanes that took part
             if (e < NP) {
                 const int t = e / (K / 4), f = (e % (K / 4)) * 4;
-                const float4 q = widen<BF16>(pq[i]), k = widen<BF16>(pk[i]), g = pg[i];
-                const float4 qs = make_float4(a.scale * q.x, a.scale * q.y, a.scale * q.z, a.scale * q.w);
+                const float4 k = widen<BF16>(pk[i]), g = pg[i];
                 *reinterpret_cast<float4 *>(&sK[t][f]) = k;
-                *reinterpret_cast<float4 *>(&sQ[t][f]) = qs;
                 *reinterpret_cast<float4 *>(&sD[t][f]) = make_float4(ex2(g.x * kLog2e), ex2(g.y * kLog2e),
                                                                     ex2(g.z * kLog2e), ex2(g.w * kLog2e));
-                float s = fmaf(qs.x, k.x, fmaf(qs.y, k.y, fmaf(qs.z, k.z, qs.w * k.w)));
-                s += dpp<0xb1>(s);    // quad_perm [1,0,3,2]
-                s += dpp<0x4e>(s);    // quad_perm [2,3,0,1]
-                s += dpp<0x141>(s);   // row_half_mirror
-                if constexpr (QKR == 16) s += dpp<0x140>(s);   // row_mirror
-                if (e % QKR == 0) sQKz[t][(e % (K / 4)) / QKR] = s;
+                if constexpr (!RES) {
+                    const float4 q = widen<BF16>(pq[i]);
+                    const float4 qs = make_float4(a.scale * q.x, a.scale * q.y, a.scale * q.z, a.scale * q.w);
+                    *reinterpret_cast<float4 *>(&sQ[t][f]) = qs;
+                    float s = fmaf(qs.x, k.x, fmaf(qs.y, k.y, fmaf(qs.z, k.z, qs.w * k.w)));
+                    s += dpp<0xb1>(s);    // quad_perm [1,0,3,2]
+                    s += dpp<0x4e>(s);    // quad_perm [2,3,0,1]
+                    s += dpp<0x141>(s);   // row_half_mirror
+                    if constexpr (QKR == 16) s += dpp<0x140>(s);   // row_mirror
+                    if (e % QKR == 0) sQKz[t][(e % (K / 4)) / QKR] = s;
+                }
             }
         }
 #pragma unroll
