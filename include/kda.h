@@ -1,5 +1,6 @@
 /*
- * libkda -- Kimi Delta Attention (KDA) forward on AMD Instinct MI355X (gfx950).
+ * libkda -- Kimi Delta Attention (KDA) forward and backward on AMD Instinct
+ * MI355X (gfx950).
  *
  * The operation (page "K3/notes/sections/sec-01.tex", section "KDA 递归核心",
  * subsection "逐步公式"; the same loop is naive_kda_fwd on the page
@@ -14,7 +15,8 @@
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *    never allocates, frees, or keeps them.  Tensors are dense row-major with
+ *    never allocates, frees, or keeps them; the one entry point that needs
+ *    scratch memory (kda_recurrent_bwd) takes it as a workspace argument.  Tensors are dense row-major with
  *    the last dimension contiguous, and every base address must be 16-byte
  *    aligned.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
