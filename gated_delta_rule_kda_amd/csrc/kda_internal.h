@@ -92,7 +92,7 @@ struct BwdArgs {
     float *ST;                  // [B,HV,K,V]: forward final state
     float *daP, *dqP, *dkrP;    // [NCB,B,T,HV,K]: per column-block partial sums
     float *e;                   // [B,T,HV,K]: per-token terms of dg
-    float *bs;                  // [B,HV,K,NB+1]: sums of e over blocks of kDgBlock
+    float *bs;                  // [B,HV,NB+1,K]: sums of e over blocks of kDgBlock
                                 // tokens, then the final-state term of dg
     int NCB, NB;
     int B, T, H, HV, K, V;

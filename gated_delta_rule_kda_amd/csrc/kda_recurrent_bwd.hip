@@ -466,7 +466,7 @@ __global__ __launch_bounds__(256) void bwd_qk_kernel(BwdArgs a) {
     store1<BF16>(a.dk, i, dk);
 }
 
-// Sums of e over blocks of kDgBlock tokens: bs[b, hv, k, block], and in the
+// Sums of e over blocks of kDgBlock tokens: bs[b, hv, block, k], and in the
 // entry after the last block the final-state term sum over V of
 // S_T (.) dL/dS_T (0 without dL/dS_T).
 __global__ __launch_bounds__(256) void bwd_dg_blocks_kernel(BwdArgs a) {
@@ -485,8 +485,9 @@ __global__ __launch_bounds__(256) void bwd_dg_blocks_kernel(BwdArgs a) {
 #pragma unroll 16
     for (int t = 0; t < kDgBlock; ++t)
         if (tb + t < a.T) s += e[t * step];
-    float *row = a.bs + (bhv * a.K + kk) * (a.NB + 1);
-    row[jb] = s;
+    // bs[b, hv, block, k]: the threads of one block read it k-contiguous
+    float *col = a.bs + bhv * (a.NB + 1) * a.K + kk;
+    col[static_cast<size_t>(jb) * a.K] = s;
     if (jb == a.NB - 1) {
         float c = 0.f;
         if (a.dST) {
@@ -498,7 +499,7 @@ __global__ __launch_bounds__(256) void bwd_dg_blocks_kernel(BwdArgs a) {
                 c += (x.x * y.x + x.y * y.y) + (x.z * y.z + x.w * y.w);
             }
         }
-        row[a.NB] = c;
+        col[static_cast<size_t>(a.NB) * a.K] = c;
     }
 }
 
@@ -514,9 +515,9 @@ __global__ __launch_bounds__(256) void bwd_dg_kernel(BwdArgs a) {
     const int jb = static_cast<int>(r % a.NB);
     const long bhv = r / a.NB;
     const int b = static_cast<int>(bhv / a.HV), hv = static_cast<int>(bhv % a.HV);
-    const float *row = a.bs + (bhv * a.K + kk) * (a.NB + 1);
-    float acc = row[a.NB];
-    for (int j = a.NB - 1; j > jb; --j) acc += row[j];
+    const float *col = a.bs + bhv * (a.NB + 1) * a.K + kk;
+    float acc = col[static_cast<size_t>(a.NB) * a.K];
+    for (int j = a.NB - 1; j > jb; --j) acc += col[static_cast<size_t>(j) * a.K];
     const int tb = jb * kDgBlock;
     const size_t step = static_cast<size_t>(a.HV) * a.K;
     const size_t base = ((static_cast<size_t>(b) * a.T + tb) * a.HV + hv) * a.K + kk;
