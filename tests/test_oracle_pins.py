@@ -646,3 +646,39 @@ def test_backward_gqa_equals_explicit_repeat():
     np.testing.assert_allclose(a[1], r[1].reshape(B, T, H, HV // H, K).sum(3), rtol=1e-13, atol=1e-14)
     for i in range(2, 6):
         np.testing.assert_allclose(a[i], r[i], rtol=1e-13, atol=1e-14)
+
+
+def test_dg_from_read_write_rescaling():
+    """The identity the GPU backward forms dg from: adding eps to g_u scales
+    every read at t >= u against every write at s < u by e^eps, so
+    dg_u = sum_{t>=u} (qs_t*dqs_t - k_t*(S_dec,t dr_t) - beta_t k_t*da_t)
+           + sum_V S_T * dL/dS_T.
+    Its terms come from a plain numpy pass here; the sum must equal the
+    oracle's dg (pinned by finite differences above)."""
+    B, T, H, HV, K, V = 1, 9, 1, 1, 4, 3
+    rng = np.random.default_rng(21)
+    q, k = rng.standard_normal((T, K)), rng.standard_normal((T, K))
+    v, g = rng.standard_normal((T, V)), -3.0 * rng.random((T, K))
+    beta, S0 = rng.random(T), rng.standard_normal((K, V))
+    do, dST = rng.standard_normal((T, V)), rng.standard_normal((K, V))
+    s = 1 / math.sqrt(K)
+    S, Sdec, St, r = S0.copy(), [], [], []
+    for t in range(T):
+        Sd = np.exp(g[t])[:, None] * S
+        rt = v[t] - k[t] @ Sd
+        S = Sd + np.outer(beta[t] * k[t], rt)
+        Sdec.append(Sd); St.append(S.copy()); r.append(rt)
+    D = dST.copy()
+    e = np.zeros((T, K))
+    for t in range(T - 1, -1, -1):
+        D = D + np.outer(s * q[t], do[t])
+        dqs = St[t] @ do[t]
+        da = D @ r[t]
+        dr = (beta[t] * k[t]) @ D
+        e[t] = s * q[t] * dqs - k[t] * (Sdec[t] @ dr) - beta[t] * k[t] * da
+        D = np.exp(g[t])[:, None] * (D - np.outer(k[t], dr))
+    dg_identity = np.cumsum(e[::-1], axis=0)[::-1] + (S * dST).sum(axis=1)
+    ref = oracle.kda_bwd(q[None, :, None], k[None, :, None], v[None, :, None], g[None, :, None],
+                         beta[None, :, None], do[None, :, None], dST[None, None],
+                         initial_state=S0[None, None])[3][0, :, 0]
+    np.testing.assert_allclose(dg_identity, ref, rtol=1e-11, atol=1e-12)
