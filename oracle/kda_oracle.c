@@ -289,33 +289,53 @@ static double softplus(double x) { return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(
 double kda_oracle_sigmoid(double x) { return sigmoid(x); }
 double kda_oracle_softplus(double x) { return softplus(x); }
 
-/* [kda.rs] conv_update for one row of channels: each channel keeps a shift
- * register of KW values (oldest first, newest in the last slot); the new input
- * enters the last slot, the output is the dot of the register with that
- * channel's weights, then SiLU (y = acc * sigmoid(acc)). */
+/* [kda.rs] bounded_gate, for one channel: with d = exp(A_log[head]) and
+ * x = z + dt_bias[channel], the gate is lb * sigmoid(d * x) when a lower bound
+ * lb is given, and -d * softplus(x) when it is not.  The only statement of the
+ * gate in this file: the gate entry point, the decode step and the prefill
+ * prologue all call it. */
+static double gate_value(double z, double dt_bias, double A_log_head, int bounded,
+                         double lower_bound)
+{
+    const double d = exp(A_log_head);
+    const double x = z + dt_bias;
+    if (bounded) return lower_bound * sigmoid(d * x);
+    return -(d * softplus(x));
+}
+
+/* [kda.rs] conv_update, for one row of channels, from its definition: channel
+ * c keeps a register of its last KW inputs (oldest first).  The window of this
+ * step is the register's newest KW - 1 values followed by the new input; the
+ * output is the SiLU of the window's dot product with the channel's KW weights
+ * (weight j on window position j), and the window becomes the register. */
 static void conv_update(double *state, const double *x, const double *w,
                         double *y, long channels, long KW)
 {
+    double *win = (double *)malloc((size_t)KW * sizeof(double));
     long c, j;
+    if (!win) abort();
     for (c = 0; c < channels; ++c) {
-        double *row = state + c * KW;
-        const double *wr = w + c * KW;
-        double acc = 0.0;
-        for (j = 0; j + 1 < KW; ++j) row[j] = row[j + 1];
-        row[KW - 1] = x[c];
-        for (j = 0; j < KW; ++j) acc += wr[j] * row[j];
-        y[c] = acc * sigmoid(acc);
+        double *reg = state + c * KW; /* KW slots; slot 0 is the oldest */
+        double pre = 0.0;
+        /* the window: the register's newest KW - 1 values, then x[c] */
+        for (j = 0; j < KW - 1; ++j) win[j] = reg[j + 1];
+        win[KW - 1] = x[c];
+        for (j = 0; j < KW; ++j) pre += w[c * KW + j] * win[j];
+        y[c] = pre / (1.0 + exp(-pre)); /* SiLU(pre) = pre * sigmoid(pre) */
+        memcpy(reg, win, (size_t)KW * sizeof(double));
     }
+    free(win);
 }
 
-/* [kda.rs] l2norm_rows: x / sqrt(sum(x^2) + eps), eps added inside the root. */
+/* [kda.rs] l2norm_rows: each row divided by its norm sqrt(sum x^2 + eps), the
+ * eps inside the root. */
 static void l2norm_row(double *x, long d, double eps)
 {
     long i;
-    double ss = 0.0, inv;
+    double ss = 0.0, norm;
     for (i = 0; i < d; ++i) ss += x[i] * x[i];
-    inv = 1.0 / sqrt(ss + eps);
-    for (i = 0; i < d; ++i) x[i] *= inv;
+    norm = sqrt(ss + eps);
+    for (i = 0; i < d; ++i) x[i] = x[i] / norm;
 }
 
 int kda_oracle_decode_step(const double *x, const double *conv_w, double *conv_state,
@@ -364,13 +384,8 @@ int kda_oracle_decode_step(const double *x, const double *conv_w, double *conv_s
             for (i = 0; i < K; ++i) {
                 const double gi = gate_in[(b * HV + hv) * K + i];
                 if (A_log) {
-                    /* [kda.rs] bounded_gate: decay = exp(A_log[head]),
-                     * x = z + dt_bias; lower-bounded branch lb*sigmoid(decay*x),
-                     * otherwise -decay*softplus(x). */
-                    const double decay = exp(A_log[hv]);
-                    const double xz = gi + dt_bias[hv * K + i];
-                    g[i] = gate_bounded ? lower_bound * sigmoid(decay * xz)
-                                        : -decay * softplus(xz);
+                    g[i] = gate_value(gi, dt_bias[hv * K + i], A_log[hv], gate_bounded,
+                                      lower_bound);
                 } else {
                     g[i] = gi;
                 }
@@ -394,15 +409,12 @@ int kda_oracle_gate(const double *z, const double *A_log, const double *dt_bias,
 {
     long r, hv, i;
     for (r = 0; r < rows; ++r)
-        for (hv = 0; hv < HV; ++hv) {
-            const double decay = exp(A_log[hv]);
+        for (hv = 0; hv < HV; ++hv)
             for (i = 0; i < K; ++i) {
                 const long idx = (r * HV + hv) * K + i;
-                const double xz = z[idx] + dt_bias[hv * K + i];
-                g[idx] = gate_bounded ? lower_bound * sigmoid(decay * xz)
-                                      : -decay * softplus(xz);
+                g[idx] = gate_value(z[idx], dt_bias[hv * K + i], A_log[hv], gate_bounded,
+                                    lower_bound);
             }
-        }
     return 0;
 }
 
@@ -474,10 +486,8 @@ int kda_oracle_prefill_prologue(const double *x, const double *conv_w, double *c
                 for (i = 0; i < K; ++i) {
                     const long idx = (bt * HV + hv) * K + i;
                     if (A_log) {
-                        const double decay = exp(A_log[hv]);
-                        const double xz = gate_in[idx] + dt_bias[hv * K + i];
-                        g[idx] = gate_bounded ? lower_bound * sigmoid(decay * xz)
-                                              : -decay * softplus(xz);
+                        g[idx] = gate_value(gate_in[idx], dt_bias[hv * K + i], A_log[hv],
+                                            gate_bounded, lower_bound);
                     } else {
                         g[idx] = gate_in[idx];
                     }

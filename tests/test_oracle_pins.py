@@ -378,6 +378,74 @@ def test_gate_closed_forms():
     np.testing.assert_allclose(g2[0, 0], -5.0 / (1 + math.exp(-3.0 * xs[0])), rtol=1e-14)
 
 
+def _gate_cases():
+    """Closed forms of "kda.rs" bounded_gate at A_log = ln 3 (decay factor 3),
+    chosen so that the value is exact: softplus(ln 3) = ln 4, so the unbounded
+    gate is -3 ln 4 = -6 ln 2; at x = ln(3)/3 the lower-bounded gate is
+    -5 sigmoid(ln 3) = -5 * 3/4.  Misplacing the factor (-softplus(3x) gives
+    -ln 28; -5 sigmoid(x) gives -3.0) fails them."""
+    ln3 = math.log(3.0)
+    return [
+        # (bounded, z + dt_bias, expected g)
+        (False, ln3, -6.0 * math.log(2.0)),
+        (False, 0.0, -3.0 * math.log(2.0)),
+        (True, ln3 / 3.0, -3.75),
+        (True, 0.0, -2.5),
+    ]
+
+
+def test_gate_exp_alog_factor():
+    """The gate entry point: exp(A_log) multiplies softplus(x) on the
+    unbounded branch and x inside the sigmoid on the bounded one."""
+    for bounded, x, want in _gate_cases():
+        z = np.array([[x - 0.25, x + 0.5]])           # z + dt_bias = x on both channels
+        g = oracle.gate(z, [math.log(3.0)], [0.25, -0.5], HV=1, K=2, bounded=bounded)
+        np.testing.assert_allclose(g[0], [want, want], rtol=1e-14)
+
+
+def test_gate_exp_alog_factor_in_decode_step():
+    """The same gate inside the decode step: one head, K = V = 1, no conv or
+    L2 norm, beta = 0 and state 1.  The step only decays, so the new state and
+    the readout (q = 1, scale 1) are both exp(g): 1/64 on the unbounded case
+    with x = ln 3."""
+    for bounded, x, want in _gate_cases():
+        state = np.ones((1, 1, 1, 1))
+        xq = np.array([[1.0, 0.5, 2.0]])               # q | k | v
+        o = oracle.kda_decode_step(xq, state, 1, 1, 1, 1, gate_in=np.array([[x - 0.1]]),
+                                   A_log=[math.log(3.0)], dt_bias=[0.1], gate_bounded=bounded,
+                                   beta=np.array([[0.0]]), beta_is_logit=False, scale=1.0)
+        np.testing.assert_allclose(o[0, 0, 0], math.exp(want), rtol=1e-13)
+        np.testing.assert_allclose(state[0, 0, 0, 0], math.exp(want), rtol=1e-13)
+    # the unbounded case at x = ln 3 is exactly 2^-6
+    state = np.ones((1, 1, 1, 1))
+    o = oracle.kda_decode_step(np.array([[1.0, 0.5, 2.0]]), state, 1, 1, 1, 1,
+                               gate_in=np.array([[math.log(3.0)]]), A_log=[math.log(3.0)],
+                               dt_bias=[0.0], gate_bounded=False, beta=np.array([[0.0]]),
+                               beta_is_logit=False, scale=1.0)
+    assert abs(o[0, 0, 0] - 1.0 / 64.0) < 1e-15
+
+
+def test_gate_exp_alog_factor_in_prefill_prologue():
+    """The same gate inside the prefill prologue, on every token and head:
+    two value heads with A_log = ln 3 and 0 (decay factors 3 and 1)."""
+    for bounded, x, want in _gate_cases():
+        H = HV = 2
+        K = V = 1
+        T = 3
+        xin = np.zeros((1, T, 2 * H * K + HV * V))
+        dt = np.array([0.2, -0.3])
+        z = np.empty((1, T, HV, K))
+        z[..., 0, 0] = x - dt[0]
+        z[..., 1, 0] = 0.0 - dt[1]                       # head 1: x = 0, factor 1
+        _, _, _, g, _ = oracle.prefill_prologue(xin, H, HV, K, V, gate_in=z,
+                                                A_log=[math.log(3.0), 0.0], dt_bias=dt,
+                                                gate_bounded=bounded, beta=np.zeros((1, T, HV)))
+        np.testing.assert_allclose(g[0, :, 0, 0], [want] * T, rtol=1e-14)
+        # factor 1 at x = 0: -ln 2 unbounded, -5/2 bounded
+        np.testing.assert_allclose(g[0, :, 1, 0], [-2.5 if bounded else -math.log(2.0)] * T,
+                                   rtol=1e-14)
+
+
 def test_l2norm_eps_inside_root():
     """kda.rs l2norm_rows: x / sqrt(sum x^2 + eps)."""
     x = np.array([[3.0, 4.0], [0.0, 0.0]])
