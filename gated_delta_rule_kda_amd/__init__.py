@@ -24,7 +24,7 @@ import threading
 
 import torch
 
-__all__ = ["kda", "chunk_fwd", "recurrent_bwd", "recurrent_bwd_workspace_size", "chunk_fwd_snapshots", "recurrent_fwd", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
+__all__ = ["kda", "chunk_fwd", "chunk_fwd_workspace_size", "recurrent_bwd", "recurrent_bwd_workspace_size", "chunk_fwd_snapshots", "recurrent_fwd", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
            "GATE_DIRECT", "GATE_BOUNDED", "GATE_SOFTPLUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +35,7 @@ _lib = None
 KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EHIP = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_DIRECT, GATE_BOUNDED, GATE_SOFTPLUS = 0, 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class KDAError(RuntimeError):
@@ -80,7 +80,9 @@ def _load():
             lib.kda_abi_version.restype = I
             lib.kda_last_error.argtypes = []
             lib.kda_last_error.restype = ctypes.c_char_p
-            lib.kda_chunk_fwd.argtypes = [P] * 8 + [I] * 6 + [F, I, I, P]
+            lib.kda_chunk_fwd_workspace_size.argtypes = [I] * 8
+            lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_longlong
+            lib.kda_chunk_fwd.argtypes = [P] * 8 + [I] * 6 + [F, I, I, P, ctypes.c_longlong, P]
             lib.kda_chunk_fwd.restype = I
             lib.kda_recurrent_fwd.argtypes = [P] * 8 + [I] * 6 + [F, I, P]
             lib.kda_recurrent_fwd.restype = I
@@ -88,7 +90,7 @@ def _load():
             lib.kda_recurrent_bwd_workspace_size.restype = ctypes.c_longlong
             lib.kda_recurrent_bwd.argtypes = ([P] * 14 + [I] * 6 + [F, I, P, ctypes.c_longlong, P])
             lib.kda_recurrent_bwd.restype = I
-            lib.kda_chunk_fwd_snapshots.argtypes = [P] * 9 + [I] * 7 + [F, I, I, P]
+            lib.kda_chunk_fwd_snapshots.argtypes = [P] * 9 + [I] * 7 + [F, I, I, P, ctypes.c_longlong, P]
             lib.kda_chunk_fwd_snapshots.restype = I
             lib.kda_prefill_prologue.argtypes = ([P, P, P, ctypes.POINTER(DecodePrologue)] + [P] * 5
                                                  + [I] * 6 + [I, P])
@@ -166,9 +168,29 @@ def _prefill_args(q, k, v, g, beta, initial_state, output_final_state, out, fina
     return (B, T, H, HV, K, V), out, final_state
 
 
+def chunk_fwd_workspace_size(B, T, H, HV, K, V, chunk_size=32, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace ``kda_chunk_fwd`` (and ``kda_chunk_fwd_snapshots``)
+    needs for these sizes (0 for the fused kernels built here)."""
+    n = _load().kda_chunk_fwd_workspace_size(B, T, H, HV, K, V, int(chunk_size), _dtype_code(dtype))
+    if n < 0:
+        raise KDAError(KDA_EINVAL, _load().kda_last_error().decode(errors="replace"))
+    return n
+
+
+def _prefill_workspace(workspace, shape, chunk_size, dtype, dev):
+    """The caller's workspace (a uint8 GPU tensor), or one of the size the
+    library asks for (None when it needs none)."""
+    B, T, H, HV, K, V = shape
+    nbytes = chunk_fwd_workspace_size(B, T, H, HV, K, V, chunk_size, dtype)
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes > 0 else None
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    return workspace
+
+
 def chunk_fwd_snapshots(q, k, v, g, beta, snapshot_every, scale=None, initial_state=None,
                         output_final_state=False, *, chunk_size=32, out=None,
-                        final_state=None, snapshots=None):
+                        final_state=None, snapshots=None, workspace=None):
     """``kda_chunk_fwd_snapshots``: :func:`chunk_fwd` that also returns prefix
     snapshots [B, T // snapshot_every, HV, K, V] fp32, snapshot j being the
     state after the first (j+1)*snapshot_every tokens (a positive multiple of
@@ -184,12 +206,13 @@ def chunk_fwd_snapshots(q, k, v, g, beta, snapshot_every, scale=None, initial_st
         snapshots = torch.empty(B, NS, HV, K, V, dtype=torch.float32, device=dev)
     else:
         _need(snapshots, "snapshots", torch.float32, (B, NS, HV, K, V), dev)
+    ws = _prefill_workspace(workspace, (B, T, H, HV, K, V), chunk_size, q.dtype, dev)
     with torch.cuda.device(dev):
         _check(_load().kda_chunk_fwd_snapshots(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(out),
             _ptr(final_state), _ptr(snapshots), every, B, T, H, HV, K, V,
             float(scale) if scale else 0.0, int(chunk_size), _dtype_code(q.dtype),
-            _stream_handle(dev)))
+            _ptr(ws), ws.numel() if ws is not None else 0, _stream_handle(dev)))
     return out, final_state, snapshots
 
 
@@ -268,23 +291,27 @@ def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initia
 
 
 def chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
-              *, chunk_size=32, out=None, final_state=None):
+              *, chunk_size=32, out=None, final_state=None, workspace=None):
     """Chunk-parallel KDA prefill (``kda_chunk_fwd``).
 
     q, k [B,T,H,K]; v [B,T,HV,V] (all bf16 or all fp32); g [B,T,HV,K] fp32 with
     -5 <= g <= 0; beta [B,T,HV] fp32; initial_state [B,HV,K,V] fp32 or None.
     Returns (o [B,T,HV,V] in v's dtype, final state [B,HV,K,V] fp32 or None).
     ``final_state`` may be passed (even the initial_state tensor itself, to
-    resume in place); ``out`` may be passed to avoid an allocation.
+    resume in place); ``out`` may be passed to avoid an allocation, and
+    ``workspace`` (a uint8 GPU tensor of at least
+    :func:`chunk_fwd_workspace_size` bytes) to avoid one for scratch.
     """
     (B, T, H, HV, K, V), out, final_state = _prefill_args(
         q, k, v, g, beta, initial_state, output_final_state, out, final_state)
     dev = q.device
+    ws = _prefill_workspace(workspace, (B, T, H, HV, K, V), chunk_size, q.dtype, dev)
     with torch.cuda.device(dev):
         _check(_load().kda_chunk_fwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(out),
             _ptr(final_state), B, T, H, HV, K, V, float(scale) if scale else 0.0,
-            int(chunk_size), _dtype_code(q.dtype), _stream_handle(dev)))
+            int(chunk_size), _dtype_code(q.dtype), _ptr(ws), ws.numel() if ws is not None else 0,
+            _stream_handle(dev)))
     return out, final_state
 
 

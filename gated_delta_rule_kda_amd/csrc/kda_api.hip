@@ -73,11 +73,10 @@ namespace {
 
 // Shared body of kda_chunk_fwd and kda_chunk_fwd_snapshots; `fn` names the
 // entry point in error messages.
-int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, const float *g,
-                   const float *beta, const float *initial_state, void *out, float *final_state,
-                   float *snapshots, int snapshot_every, int B, int T, int H, int HV, int K,
-                   int V, float scale, int chunk, int dtype, void *stream, bool recurrent = false) {
-    g_err[0] = '\0';
+// The size checks shared by the prefill entry points and their workspace
+// query: KDA_OK, or the code with the message set.
+int prefill_sizes_ok(const char *fn, int B, int T, int H, int HV, int K, int V, int chunk,
+                     int dtype) {
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
         return fail(KDA_EUNSUPPORTED, "%s: dtype %d is not KDA_DTYPE_F32 or KDA_DTYPE_BF16", fn, dtype);
     if (B < 0 || T < 0) return fail(KDA_EINVAL, "%s: B=%d and T=%d must be >= 0", fn, B, T);
@@ -88,6 +87,22 @@ int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, 
     if (chunk < 0) return fail(KDA_EINVAL, "%s: chunk=%d must be >= 0", fn, chunk);
     if (chunk != 0 && chunk != 32)
         return fail(KDA_EUNSUPPORTED, "%s: chunk=%d; only 32 (or 0 for the default) is built", fn, chunk);
+    return KDA_OK;
+}
+
+// Workspace bytes of a prefill call: the fused kernels keep every
+// intermediate in registers and LDS, so none of the built paths needs any.
+uint64_t prefill_workspace_bytes(int, int, int, int, int, int, int, int) { return 0; }
+
+int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, const float *g,
+                   const float *beta, const float *initial_state, void *out, float *final_state,
+                   float *snapshots, int snapshot_every, int B, int T, int H, int HV, int K,
+                   int V, float scale, int chunk, int dtype, void *workspace,
+                   long long workspace_bytes, void *stream, bool recurrent = false) {
+    g_err[0] = '\0';
+    if (const int rc = prefill_sizes_ok(fn, B, T, H, HV, K, V, chunk, dtype)) return rc;
+    if (workspace_bytes < 0)
+        return fail(KDA_EINVAL, "%s: workspace_bytes=%lld must be >= 0", fn, workspace_bytes);
     if (snapshots && (snapshot_every < 32 || snapshot_every % 32 != 0))
         return fail(KDA_EINVAL, "%s: snapshot_every=%d must be a positive multiple of the chunk size 32",
                     fn, snapshot_every);
@@ -101,13 +116,20 @@ int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, 
         !count(nb, {B, T, HV}) || !count(ns, {B, HV, K, V}) || !count(nsn, {B, NS, HV, K, V}))
         return fail(KDA_EINVAL, "%s: tensor sizes overflow", fn);
     const bool work = (static_cast<int64_t>(B) * T) > 0;
+    const uint64_t ws_need = recurrent ? 0 : prefill_workspace_bytes(B, T, H, HV, K, V, chunk, dtype);
     if (work) {
         if (!q || !k || !v || !g || !beta || !out)
             return fail(KDA_EINVAL, "%s: q, k, v, g, beta and out must be non-NULL", fn);
+        if (ws_need > 0 && (!workspace || static_cast<uint64_t>(workspace_bytes) < ws_need))
+            return fail(KDA_EINVAL, "%s: workspace of %lld bytes at %p, %llu needed", fn, workspace_bytes,
+                        workspace, static_cast<unsigned long long>(ws_need));
     }
-    const void *ptrs[] = {q, k, v, g, beta, initial_state, out, final_state, snapshots};
-    const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "out", "final_state", "snapshots"};
-    for (int i = 0; i < 9; ++i)
+    // the workspace is only looked at when the call uses it
+    const void *ws = work && ws_need > 0 ? workspace : nullptr;
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, out, final_state, snapshots, ws};
+    const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "out", "final_state", "snapshots",
+                           "workspace"};
+    for (int i = 0; i < 10; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(KDA_EINVAL, "%s: %s is not 16-byte aligned", fn, names[i]);
 
@@ -127,6 +149,11 @@ int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, 
         if (overlap(r_sn, r)) return fail(KDA_EINVAL, "%s: snapshots overlap %s", fn, r.name);
     if (overlap(r_sn, r_out) || overlap(r_sn, r_st))
         return fail(KDA_EINVAL, "%s: snapshots overlap %s", fn, overlap(r_sn, r_out) ? "out" : "final_state");
+    const Range r_ws = rng("workspace", ws, ws_need);
+    for (const Range &r : r_in)
+        if (overlap(r_ws, r)) return fail(KDA_EINVAL, "%s: workspace overlaps %s", fn, r.name);
+    if (overlap(r_ws, r_out) || overlap(r_ws, r_st) || overlap(r_ws, r_sn))
+        return fail(KDA_EINVAL, "%s: workspace overlaps an output", fn);
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!work) {
@@ -190,22 +217,38 @@ bool bwd_layout(BwdLayout &L, int B, int T, int HV, int K, int V) {
 
 extern "C" {
 
+long long kda_chunk_fwd_workspace_size(int B, int T, int H, int HV, int K, int V, int chunk,
+                                       int dtype) {
+    g_err[0] = '\0';
+    if (prefill_sizes_ok("kda_chunk_fwd_workspace_size", B, T, H, HV, K, V, chunk, dtype) != KDA_OK)
+        return -1;
+    uint64_t n;
+    if (!count(n, {B, T, HV, K}) || !count(n, {B, T, HV, V})) {
+        fail(KDA_EINVAL, "kda_chunk_fwd_workspace_size: tensor sizes overflow");
+        return -1;
+    }
+    return static_cast<long long>(prefill_workspace_bytes(B, T, H, HV, K, V, chunk, dtype));
+}
+
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                   const float *beta, const float *initial_state, void *out,
                   float *final_state, int B, int T, int H, int HV, int K, int V,
-                  float scale, int chunk, int dtype, void *stream) {
+                  float scale, int chunk, int dtype, void *workspace,
+                  long long workspace_bytes, void *stream) {
     return chunk_fwd_impl("kda_chunk_fwd", q, k, v, g, beta, initial_state, out, final_state,
-                          nullptr, 0, B, T, H, HV, K, V, scale, chunk, dtype, stream);
+                          nullptr, 0, B, T, H, HV, K, V, scale, chunk, dtype, workspace,
+                          workspace_bytes, stream);
 }
 
 int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const float *g,
                             const float *beta, const float *initial_state, void *out,
                             float *final_state, float *snapshots, int snapshot_every,
                             int B, int T, int H, int HV, int K, int V, float scale,
-                            int chunk, int dtype, void *stream) {
+                            int chunk, int dtype, void *workspace, long long workspace_bytes,
+                            void *stream) {
     return chunk_fwd_impl("kda_chunk_fwd_snapshots", q, k, v, g, beta, initial_state, out,
                           final_state, snapshots, snapshot_every, B, T, H, HV, K, V, scale,
-                          chunk, dtype, stream);
+                          chunk, dtype, workspace, workspace_bytes, stream);
 }
 
 int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *g,
@@ -213,7 +256,7 @@ int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *
                       float *final_state, int B, int T, int H, int HV, int K, int V,
                       float scale, int dtype, void *stream) {
     return chunk_fwd_impl("kda_recurrent_fwd", q, k, v, g, beta, initial_state, out, final_state,
-                          nullptr, 0, B, T, H, HV, K, V, scale, 0, dtype, stream, true);
+                          nullptr, 0, B, T, H, HV, K, V, scale, 0, dtype, nullptr, 0, stream, true);
 }
 
 long long kda_recurrent_bwd_workspace_size(int B, int T, int H, int HV, int K, int V) {

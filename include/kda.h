@@ -15,9 +15,10 @@
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *    never allocates, frees, or keeps them; the one entry point that needs
- *    scratch memory (kda_recurrent_bwd) takes it as a workspace argument.  Tensors are dense row-major with
- *    the last dimension contiguous, and every base address must be 16-byte
+ *    never allocates, frees, or keeps them; entry points that may need
+ *    scratch memory take it as a workspace argument whose size a
+ *    *_workspace_size query returns.  Tensors are dense row-major with the
+ *    last dimension contiguous, and every base address must be 16-byte
  *    aligned.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *    work; they never synchronise.  Results are deterministic: the same inputs
@@ -39,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 enum kda_status { KDA_OK = 0, KDA_EINVAL = 1, KDA_EUNSUPPORTED = 2, KDA_EHIP = 3 };
 
@@ -83,17 +84,34 @@ const char *kda_last_error(void);
  *   B, T >= 0 (either 0: nothing but the final state, which then equals the
  *   initial state, is written); H, HV >= 1 with HV % H == 0;
  *   K, V in {32, 64, 128};  scale <= 0 (or NaN) selects 1/sqrt(K);
- *   chunk 0 selects the default, 32 (the only size built);
- *   dtype KDA_DTYPE_F32 or KDA_DTYPE_BF16.
+ *   chunk 0 selects the default, 32 (the only size built; the chunk bounds
+ *   of delta_recurrence on "src/tinycenn_lm/research_layers.py" are checked
+ *   the same way: other sizes return KDA_EUNSUPPORTED);
+ *   dtype KDA_DTYPE_F32 or KDA_DTYPE_BF16;
+ *   workspace     device scratch of workspace_bytes bytes, owned by the
+ *                 caller, 16-byte aligned, disjoint from every other
+ *                 argument; its contents carry nothing between calls.  It
+ *                 must hold at least kda_chunk_fwd_workspace_size(...) bytes
+ *                 for the same sizes (else KDA_EINVAL); when that is 0 it may
+ *                 be NULL and is not touched.  workspace_bytes < 0: KDA_EINVAL.
+ *
+ * kda_chunk_fwd_workspace_size returns the workspace bytes kda_chunk_fwd (and
+ * kda_chunk_fwd_snapshots) needs for these sizes, chunk and dtype, or -1 with
+ * a message in kda_last_error for arguments those calls reject.  The fused
+ * kernels built here keep every intermediate on chip, so it is 0 for all of
+ * them; callers that query it stay correct for builds that need scratch.
  */
+long long kda_chunk_fwd_workspace_size(int B, int T, int H, int HV, int K, int V, int chunk,
+                                       int dtype);
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                   const float *beta, const float *initial_state, void *out,
                   float *final_state, int B, int T, int H, int HV, int K, int V,
-                  float scale, int chunk, int dtype, void *stream);
+                  float scale, int chunk, int dtype, void *workspace,
+                  long long workspace_bytes, void *stream);
 
 /*
  * kda_recurrent_fwd -- the same computation and interface as kda_chunk_fwd
- * (without the chunk size), for gates with no lower bound.
+ * (without the chunk size and the workspace), for gates with no lower bound.
  *
  * It runs the recurrence of the page "K3/notes/sections/sec-01.tex" (section
  * "KDA 递归核心") one token at a time with the state kept on chip, so it takes
@@ -172,8 +190,9 @@ int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *
  *   snapshot_every  tokens between snapshots; when snapshots is not NULL it
  *                   must be a positive multiple of the chunk size (32), else
  *                   KDA_EINVAL.
- * All other arguments, their layouts and the error behaviour are those of
- * kda_chunk_fwd.  When T is a multiple of snapshot_every the last snapshot
+ * All other arguments (the workspace included: its size is
+ * kda_chunk_fwd_workspace_size), their layouts and the error behaviour are
+ * those of kda_chunk_fwd.  When T is a multiple of snapshot_every the last snapshot
  * equals the final state.  Writing snapshots adds B*NS*HV*K*V*4 bytes of
  * stores to the call.
  */
@@ -181,7 +200,8 @@ int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const f
                             const float *beta, const float *initial_state, void *out,
                             float *final_state, float *snapshots, int snapshot_every,
                             int B, int T, int H, int HV, int K, int V, float scale,
-                            int chunk, int dtype, void *stream);
+                            int chunk, int dtype, void *workspace, long long workspace_bytes,
+                            void *stream);
 
 /*
  * Optional stages fused in front of the decode step, as the host decode on the
@@ -248,7 +268,14 @@ int kda_output_gate(const void *o, const void *gate, void *y, long long rows, in
 
 /*
  * kda_decode_step -- one token of the recurrence for B sequences, state
- * updated in place.
+ * updated in place: the host decode of the page
+ * "metrale_model_weights/kimi_k3_host/kda.rs" (kda_decode_token: conv_update
+ * on the packed channels, then kda_recurrent_step: l2norm_rows on q and k, a
+ * sigmoid on the beta logit, the gate from bounded_gate, and the step of the
+ * recurrence above on the in-place recurrent state, readout after the write
+ * with scale 1/sqrt(K)), the stages selected by `pro`.  The step itself is
+ * the four-step update of "K3/notes/sections/sec-01.tex" (section "KDA 递归核心")
+ * for T = 1.
  *
  *   qkv    [B, 2*H*K + HV*V] dtype: q (H*K) | k (H*K) | v (HV*V) channels of one
  *          token, before the short conv when the prologue has one

@@ -28,6 +28,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"kda_abi_version", "kda_last_error", "kda_chunk_fwd",
+                          "kda_chunk_fwd_workspace_size",
                           "kda_chunk_fwd_snapshots", "kda_recurrent_fwd", "kda_prefill_prologue",
                           "kda_output_gate", "kda_decode_step", "kda_recurrent_bwd",
                           "kda_recurrent_bwd_workspace_size"}
@@ -65,12 +66,13 @@ FAKE = 0x100000   # never dereferenced: every call below fails validation first
 
 def chunk(**over):
     a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, s0=None, out=FAKE * 6,
-             st=None, B=1, T=8, H=2, HV=4, K=32, V=32, scale=0.0, chunk=0, dtype=1)
+             st=None, B=1, T=8, H=2, HV=4, K=32, V=32, scale=0.0, chunk=0, dtype=1, ws=None,
+             ws_bytes=0)
     a.update(over)
     L = lib()
     rc = L.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["out"], a["st"],
                          a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["scale"], a["chunk"],
-                         a["dtype"], None)
+                         a["dtype"], a["ws"], a["ws_bytes"], None)
     return rc, L.kda_last_error().decode()
 
 
@@ -98,11 +100,39 @@ BIG = 1 << 36
     (dict(q=BIG, k=2 * BIG, v=3 * BIG, g=4 * BIG, beta=5 * BIG, out=6 * BIG, s0=7 * BIG,
           st=7 * BIG + 64), 1, "final_state overlaps initial_state"),
     (dict(B=1 << 20, T=1 << 20, H=128, HV=128), 1, "overflow"),
+    (dict(ws_bytes=-1), 1, "workspace_bytes=-1"),
+    (dict(ws=FAKE * 7, ws_bytes=-8), 1, "workspace_bytes"),
 ])
 def test_chunk_fwd_rejects(over, code, msg):
     rc, err = chunk(**over)
     assert rc == code, err
     assert msg in err, err
+
+
+def test_chunk_fwd_workspace_size():
+    """kda_chunk_fwd_workspace_size: 0 bytes for every size the fused kernels
+    take (chunk 0 or 32, both dtypes, GQA, empty), -1 with the same message
+    kda_chunk_fwd gives for sizes it rejects."""
+    L = lib()
+    for args in [(1, 8192, 96, 96, 128, 128, 0, 1), (8, 4096, 16, 64, 128, 128, 32, 1),
+                 (1, 64, 2, 2, 32, 32, 0, 0), (0, 0, 1, 1, 64, 32, 32, 0), (3, 97, 2, 4, 64, 128, 0, 1)]:
+        assert L.kda_chunk_fwd_workspace_size(*args) == 0, args
+    for args, msg in [((1, 8, 2, 3, 32, 32, 0, 1), "multiple"), ((1, 8, 2, 2, 16, 32, 0, 1), "32, 64 or 128"),
+                      ((1, 8, 2, 2, 32, 32, 64, 1), "only 32"), ((1, 8, 2, 2, 32, 32, 0, 9), "dtype"),
+                      ((-1, 8, 2, 2, 32, 32, 0, 1), ">= 0"), ((1 << 20, 1 << 20, 128, 128, 128, 128, 0, 1),
+                                                             "overflow")]:
+        assert L.kda_chunk_fwd_workspace_size(*args) == -1, args
+        assert msg in L.kda_last_error().decode(), (args, L.kda_last_error())
+
+
+def test_chunk_fwd_unused_workspace_is_not_checked():
+    """With a size of 0 the workspace argument is not looked at: an unaligned
+    or overlapping pointer passes validation (the call then fails on the
+    deliberately misaligned g, proving validation got past the workspace)."""
+    rc, err = chunk(ws=FAKE + 3, ws_bytes=5, g=FAKE * 4 + 4)
+    assert rc == 1 and "g is not 16-byte aligned" in err, err
+    rc, err = chunk(ws=FAKE, ws_bytes=1 << 20, g=FAKE * 4 + 4)
+    assert rc == 1 and "g is not 16-byte aligned" in err, err
 
 
 def snap_call(snaps, every, **over):
@@ -112,7 +142,7 @@ def snap_call(snaps, every, **over):
     L = lib()
     rc = L.kda_chunk_fwd_snapshots(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["out"],
                                    a["st"], snaps, every, a["B"], a["T"], a["H"], a["HV"], a["K"],
-                                   a["V"], a["scale"], a["chunk"], a["dtype"], None)
+                                   a["V"], a["scale"], a["chunk"], a["dtype"], None, 0, None)
     return rc, L.kda_last_error().decode()
 
 

@@ -196,6 +196,20 @@ def test_deterministic_bitwise():
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
+def test_workspace_argument():
+    """A caller's workspace (here larger than the 0 bytes the fused kernel
+    asks for) changes nothing: bitwise the same outputs as without one."""
+    shape = synth.PrefillShape(1, 70, 2, 4, 128, 64, torch.bfloat16, "normal", s0_std=0.3)
+    inp = synth.make_prefill_inputs(shape, DEV, 12)
+    assert kda.chunk_fwd_workspace_size(1, 70, 2, 4, 128, 64) == 0
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    o1, S1 = kda.chunk_fwd(*args, initial_state=inp["S0"], output_final_state=True)
+    ws = torch.full((4096,), 0xAB, dtype=torch.uint8, device=DEV)
+    o2, S2 = kda.chunk_fwd(*args, initial_state=inp["S0"], output_final_state=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
 def _sampled_full_size(shape, chains, g_lower=None, seed=0):
     """Run a full-size workload on the GPU in the benchmark's launch
     configuration, then check whole (b, hv) chains against the oracle."""
