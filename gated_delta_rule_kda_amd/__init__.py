@@ -24,7 +24,7 @@ import threading
 
 import torch
 
-__all__ = ["kda", "chunk_fwd", "chunk_fwd_workspace_size", "recurrent_bwd", "recurrent_bwd_workspace_size", "chunk_fwd_snapshots", "recurrent_fwd", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
+__all__ = ["kda", "chunk_fwd", "chunk_fwd_workspace_size", "recurrent_bwd", "recurrent_bwd_noalloc", "recurrent_bwd_workspace_size", "chunk_fwd_snapshots", "recurrent_fwd", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
            "GATE_DIRECT", "GATE_BOUNDED", "GATE_SOFTPLUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -90,6 +90,8 @@ def _load():
             lib.kda_recurrent_bwd_workspace_size.restype = ctypes.c_longlong
             lib.kda_recurrent_bwd.argtypes = ([P] * 14 + [I] * 6 + [F, I, P, ctypes.c_longlong, P])
             lib.kda_recurrent_bwd.restype = I
+            lib.kda_recurrent_bwd_noalloc.argtypes = ([P] * 14 + [I] * 6 + [F, I, P])
+            lib.kda_recurrent_bwd_noalloc.restype = I
             lib.kda_chunk_fwd_snapshots.argtypes = [P] * 9 + [I] * 7 + [F, I, I, P, ctypes.c_longlong, P]
             lib.kda_chunk_fwd_snapshots.restype = I
             lib.kda_prefill_prologue.argtypes = ([P, P, P, ctypes.POINTER(DecodePrologue)] + [P] * 5
@@ -239,8 +241,23 @@ def recurrent_bwd_workspace_size(B, T, H, HV, K, V) -> int:
     return n
 
 
+NOALLOC_SCRATCH_BYTES = 128 << 20   # KDA_NOALLOC_SCRATCH_BYTES of include/kda.h
+
+
+def recurrent_bwd_noalloc(q, k, v, g, beta, dout, d_final_state=None, scale=None,
+                          initial_state=None, *, need_d_initial_state=True, out=None):
+    """``kda_recurrent_bwd_noalloc``: :func:`recurrent_bwd` without a
+    workspace, for callers that cannot allocate: the library's own scratch
+    array (``NOALLOC_SCRATCH_BYTES`` per GPU) serves instead, so sizes whose
+    :func:`recurrent_bwd_workspace_size` exceeds it are rejected.  Calls that
+    overlap in time on one GPU race on that array.  Pass ``out`` (the six
+    result tensors) to allocate nothing on this side either."""
+    return recurrent_bwd(q, k, v, g, beta, dout, d_final_state, scale, initial_state,
+                         need_d_initial_state=need_d_initial_state, out=out, _noalloc=True)
+
+
 def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initial_state=None,
-                  *, workspace=None, need_d_initial_state=True, out=None):
+                  *, workspace=None, need_d_initial_state=True, out=None, _noalloc=False):
     """``kda_recurrent_bwd``: gradients of the forward pass with the same
     inputs (any finite g).  dout [B,T,HV,V] is dL/do (v's dtype),
     d_final_state [B,HV,K,V] fp32 (or None) is dL/dS_T.  Returns (dq, dk
@@ -261,11 +278,12 @@ def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initia
     for t_, n_ in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
         if t_ is not None:
             _need(t_, n_, torch.float32, (B, HV, K, V), dev)
-    nbytes = recurrent_bwd_workspace_size(B, T, H, HV, K, V)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    else:
-        _need(workspace, "workspace", torch.uint8, None, dev)
+    if not _noalloc:
+        nbytes = recurrent_bwd_workspace_size(B, T, H, HV, K, V)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        else:
+            _need(workspace, "workspace", torch.uint8, None, dev)
     if out is None:
         dq = torch.empty(B, T, H, K, dtype=dt, device=dev)
         dk = torch.empty(B, T, H, K, dtype=dt, device=dev)
@@ -282,11 +300,17 @@ def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initia
         if dS0 is not None:
             _need(dS0, "dS0", torch.float32, (B, HV, K, V), dev)
     with torch.cuda.device(dev):
-        _check(_load().kda_recurrent_bwd(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dout),
-            _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dS0),
-            B, T, H, HV, K, V, float(scale) if scale else 0.0, _dtype_code(dt), _ptr(workspace),
-            workspace.numel(), _stream_handle(dev)))
+        if _noalloc:
+            _check(_load().kda_recurrent_bwd_noalloc(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dout),
+                _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dS0),
+                B, T, H, HV, K, V, float(scale) if scale else 0.0, _dtype_code(dt), _stream_handle(dev)))
+        else:
+            _check(_load().kda_recurrent_bwd(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dout),
+                _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dS0),
+                B, T, H, HV, K, V, float(scale) if scale else 0.0, _dtype_code(dt), _ptr(workspace),
+                workspace.numel(), _stream_handle(dev)))
     return dq, dk, dv, dg, db, dS0
 
 

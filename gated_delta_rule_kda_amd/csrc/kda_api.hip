@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "kda.h"
 #include "kda_internal.h"
 
@@ -278,13 +280,61 @@ long long kda_recurrent_bwd_workspace_size(int B, int T, int H, int HV, int K, i
     return static_cast<long long>(L.total);
 }
 
-int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *g,
-                      const float *beta, const float *initial_state, const void *dout,
-                      const float *dfinal_state, void *dq, void *dk, void *dv, float *dg,
-                      float *dbeta, float *dinitial_state, int B, int T, int H, int HV, int K,
-                      int V, float scale, int dtype, void *workspace, long long workspace_bytes,
-                      void *stream) {
-    const char *fn = "kda_recurrent_bwd";
+}  // extern "C"
+
+// Scratch for kda_recurrent_bwd_noalloc: in the code object's device memory,
+// one copy per GPU the library runs on, held until the process ends.  Host
+// code never uses this name as an address (on the host it is a stand-in
+// symbol); the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the GPU `stream` runs on (the current
+// device for the NULL stream), looked up once per device with that device
+// current.
+int scratch_for_stream(const char *fn, hipStream_t stream, void **out) {
+    int cur = -1, dev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(KDA_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    dev = cur;
+    if (stream) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return fail(KDA_EHIP, "%s: hipStreamGetDevice: %s", fn, hipGetErrorString(e));
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KDA_EUNSUPPORTED, "%s: device %d; devices 0..%d are supported", fn, dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(KDA_EHIP, "%s: hipSetDevice(%d): %s", fn, dev, hipGetErrorString(e));
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e2 = dev != cur ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess)
+            return fail(KDA_EHIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                        hipGetErrorString(e));
+        if (e2 != hipSuccess) return fail(KDA_EHIP, "%s: hipSetDevice(%d): %s", fn, cur, hipGetErrorString(e2));
+        if (!p || !aligned16(p)) return fail(KDA_EHIP, "%s: scratch address %p on device %d", fn, p, dev);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KDA_OK;
+}
+
+// Shared body of kda_recurrent_bwd and kda_recurrent_bwd_noalloc (noalloc:
+// the workspace arguments are ignored and the device's scratch array serves
+// instead, once the arguments have passed validation).
+int recurrent_bwd_impl(const char *fn, const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const float *initial_state, const void *dout,
+                       const float *dfinal_state, void *dq, void *dk, void *dv, float *dg,
+                       float *dbeta, float *dinitial_state, int B, int T, int H, int HV, int K,
+                       int V, float scale, int dtype, void *workspace, long long workspace_bytes,
+                       void *stream, bool noalloc) {
     g_err[0] = '\0';
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
         return fail(KDA_EUNSUPPORTED, "%s: dtype %d is not KDA_DTYPE_F32 or KDA_DTYPE_BF16", fn, dtype);
@@ -307,10 +357,20 @@ int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *
             return fail(KDA_EINVAL, "%s: q, k, v, g, beta and dout must be non-NULL", fn);
         if (!dq || !dk || !dv || !dg || !dbeta)
             return fail(KDA_EINVAL, "%s: dq, dk, dv, dg and dbeta must be non-NULL", fn);
-        if (!workspace) return fail(KDA_EINVAL, "%s: workspace is NULL", fn);
-        if (workspace_bytes < 0 || static_cast<uint64_t>(workspace_bytes) < L.total)
-            return fail(KDA_EINVAL, "%s: workspace of %lld bytes, %llu needed", fn, workspace_bytes,
-                        static_cast<unsigned long long>(L.total));
+        if (noalloc) {
+            if (L.total > KDA_NOALLOC_SCRATCH_BYTES)
+                return fail(KDA_EUNSUPPORTED,
+                            "%s: these sizes need %llu bytes of scratch, more than the %llu bytes of the "
+                            "library's array (use kda_recurrent_bwd with a workspace)",
+                            fn, static_cast<unsigned long long>(L.total),
+                            static_cast<unsigned long long>(KDA_NOALLOC_SCRATCH_BYTES));
+            workspace = nullptr;   // not a caller buffer: set below, after validation
+        } else {
+            if (!workspace) return fail(KDA_EINVAL, "%s: workspace is NULL", fn);
+            if (workspace_bytes < 0 || static_cast<uint64_t>(workspace_bytes) < L.total)
+                return fail(KDA_EINVAL, "%s: workspace of %lld bytes, %llu needed", fn, workspace_bytes,
+                            static_cast<unsigned long long>(L.total));
+        }
     }
     const void *ptrs[] = {q, k, v, g, beta, initial_state, dout, dfinal_state,
                           dq, dk, dv, dg, dbeta, dinitial_state, workspace};
@@ -334,6 +394,9 @@ int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *
                 return fail(KDA_EINVAL, "%s: %s overlaps %s", fn, rs[o].name, rs[i].name);
 
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (noalloc && work) {
+        if (const int rc = scratch_for_stream(fn, st, &workspace)) return rc;
+    }
     char *ws = static_cast<char *>(workspace);
     kda::BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = initial_state;
@@ -368,6 +431,31 @@ int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *
     const hipError_t e = kda::launch_backward(a, st);
     if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const float *initial_state, const void *dout,
+                      const float *dfinal_state, void *dq, void *dk, void *dv, float *dg,
+                      float *dbeta, float *dinitial_state, int B, int T, int H, int HV, int K,
+                      int V, float scale, int dtype, void *workspace, long long workspace_bytes,
+                      void *stream) {
+    return recurrent_bwd_impl("kda_recurrent_bwd", q, k, v, g, beta, initial_state, dout, dfinal_state,
+                              dq, dk, dv, dg, dbeta, dinitial_state, B, T, H, HV, K, V, scale, dtype,
+                              workspace, workspace_bytes, stream, false);
+}
+
+int kda_recurrent_bwd_noalloc(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, const float *initial_state, const void *dout,
+                              const float *dfinal_state, void *dq, void *dk, void *dv, float *dg,
+                              float *dbeta, float *dinitial_state, int B, int T, int H, int HV,
+                              int K, int V, float scale, int dtype, void *stream) {
+    return recurrent_bwd_impl("kda_recurrent_bwd_noalloc", q, k, v, g, beta, initial_state, dout,
+                              dfinal_state, dq, dk, dv, dg, dbeta, dinitial_state, B, T, H, HV, K, V,
+                              scale, dtype, nullptr, 0, stream, true);
 }
 
 int kda_prefill_prologue(const void *x, const float *gate, const float *beta,

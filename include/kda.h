@@ -171,6 +171,34 @@ int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *
                       void *stream);
 
 /*
+ * kda_recurrent_bwd_noalloc -- kda_recurrent_bwd for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same arguments, results, validation
+ * and return codes as kda_recurrent_bwd, without the workspace: a scratch
+ * array of KDA_NOALLOC_SCRATCH_BYTES (128 MiB) in the library's own device
+ * memory takes its place, one per GPU, held from the first call on that GPU
+ * until the process ends.  Nothing is allocated or freed by the call.
+ *  - Sizes whose kda_recurrent_bwd_workspace_size exceeds the array return
+ *    KDA_EUNSUPPORTED (for K = V = 128 that is about 17,000 token-value-head
+ *    pairs, e.g. B = 1, T = 1024, HV = 16), with no side effects.
+ *  - The array serves the GPU `stream` runs on (the current device for the
+ *    NULL stream).  Every call on that GPU shares it and leaves its last
+ *    contents there; nothing in it needs clearing, since each call writes
+ *    every scratch value before reading it.  Calls that overlap in time on
+ *    one GPU (on different streams, or from several host threads without
+ *    ordering) RACE on the array and give wrong gradients: order them on one
+ *    stream or with events.
+ *  - The first call on a GPU looks up the array's device address
+ *    (hipGetSymbolAddress); a failure there returns KDA_EHIP.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (128ull << 20)
+int kda_recurrent_bwd_noalloc(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, const float *initial_state, const void *dout,
+                              const float *dfinal_state, void *dq, void *dk, void *dv, float *dg,
+                              float *dbeta, float *dinitial_state, int B, int T, int H, int HV,
+                              int K, int V, float scale, int dtype, void *stream);
+
+/*
  * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also writes prefix snapshots
  * of the state, so that decoding can later resume from any whole multiple of
  * snapshot_every tokens (the prefix cache of the page

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
                           "kda_chunk_fwd_workspace_size",
                           "kda_chunk_fwd_snapshots", "kda_recurrent_fwd", "kda_prefill_prologue",
                           "kda_output_gate", "kda_decode_step", "kda_recurrent_bwd",
-                          "kda_recurrent_bwd_workspace_size"}
+                          "kda_recurrent_bwd_workspace_size", "kda_recurrent_bwd_noalloc"}
     L = ctypes.CDLL(kda.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -381,3 +381,32 @@ def test_recurrent_bwd_empty_batch_is_noop():
     rc, err = bwd_call(B=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None, dk=None,
                        dv=None, dg=None, db=None, ws=None)
     assert rc == 0, err
+
+
+def test_noalloc_backward_scratch_limit():
+    """kda_recurrent_bwd_noalloc rejects, before any HIP call, sizes whose
+    workspace exceeds the library's scratch array (KDA_NOALLOC_SCRATCH_BYTES,
+    the binding's mirror checked against the header); sizes that fit pass
+    validation up to the first bad argument."""
+    text = open(HEADER).read()
+    m = re.search(r"#define KDA_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == kda.NOALLOC_SCRATCH_BYTES
+    L = lib()
+    def call(B, T, H, HV, K, V, **over):
+        a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, dout=FAKE * 6,
+                 dq=FAKE * 7, dk=FAKE * 8, dv=FAKE * 9, dg=FAKE * 10, db=FAKE * 11)
+        a.update(over)
+        rc = L.kda_recurrent_bwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], None, a["dout"],
+                                         None, a["dq"], a["dk"], a["dv"], a["dg"], a["db"], None,
+                                         B, T, H, HV, K, V, 0.0, 1, None)
+        return rc, L.kda_last_error().decode()
+    big = (1, 8192, 96, 96, 128, 128)
+    assert L.kda_recurrent_bwd_workspace_size(*big) > kda.NOALLOC_SCRATCH_BYTES
+    rc, err = call(*big)
+    assert rc == 2 and "scratch" in err, err
+    fits = (1, 1024, 16, 16, 128, 128)
+    assert 0 < L.kda_recurrent_bwd_workspace_size(*fits) <= kda.NOALLOC_SCRATCH_BYTES
+    rc, err = call(*fits, dg=FAKE * 10 + 4)
+    assert rc == 1 and "dg is not 16-byte aligned" in err, err
+    rc, err = call(1, 8, 2, 3, 32, 32)
+    assert rc == 1 and "multiple" in err, err
