@@ -41,17 +41,36 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
-FP32_VALU_PEAK = 157.3e12      # MI355X fp32 vector, FLOP/s
+FP32_VALU_PEAK = 157.3e12      # MI355X fp32 vector, FLOP/s, counting packed (2-wide) FP32
+# The same without packed FP32 (256 CU x 4 SIMD x 16 lanes x 2 flops x 2.4 GHz):
+# the ceiling for code built, as this library is, without packed FP32 instructions.
+FP32_VALU_PEAK_NONPACKED = 78.6e12
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+N_CU = 256                     # MI355X compute units, 4 SIMDs each
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# The sources each profiled kernel is built from: its counters stay valid
+# while these files are unchanged.
+KERNEL_SOURCES = {
+    "prefill_hv96": ["kda_prefill_bf16.hip", "kda_internal.h"],
+    "prefill_gqa": ["kda_prefill_bf16.hip", "kda_internal.h"],
+    "decode_b256": ["kda_decode.hip", "kda_internal.h"],
+}
+
+
+def kernel_source_hash(kernel_key=None) -> str:
+    """sha256 (first 16 hex digits) of the kernel's source files, or of every
+    file under csrc/ when the kernel is not listed."""
+    csrc = os.path.join(ROOT, "gated_delta_rule_kda_amd", "csrc")
+    names = KERNEL_SOURCES.get(kernel_key)
+    paths = ([os.path.join(csrc, n) for n in names] if names
+             else sorted(glob.glob(os.path.join(csrc, "*"))))
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_kda_amd", "csrc", "*"))):
+    for p in paths:
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -80,18 +99,75 @@ def decode_alg_bytes(B, H, HV, K, V, KW):
     return B * per_seq + params
 
 
-def load_counters(kernel_key):
-    """HBM traffic per launch from the committed rocprofv3 counter runs, if
-    they were taken on the kernel sources as they are now; else None."""
+def counter_entry(kernel_key):
+    """The committed rocprofv3 counter record of a kernel, if it was taken on
+    the kernel sources as they are now; else None."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
     e = c.get(kernel_key)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash(kernel_key):
         return None
-    return e.get("traffic_bytes")
+    return e
+
+
+def load_counters(kernel_key):
+    """HBM traffic per launch from the committed counter runs (see
+    counter_entry), or None."""
+    e = counter_entry(kernel_key)
+    return e.get("traffic_bytes") if e else None
+
+
+def mfma_busy(kernel_key, avg_launch_ms):
+    """The matrix cores' busy fraction from the committed SQ counters of one
+    launch: SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) over the SIMD-cycles
+    of the CUs the kernel kept busy (4 x SQ_BUSY_CU_CYCLES), and over the
+    SIMD-cycles of the whole GPU for the launch (4 x 256 CUs x duration x the
+    clock those counters imply).  The cross-check: SQ_INSTS_VALU_MFMA_MOPS_BF16
+    (units of 512 flops) at 1024 bf16 flops per SIMD-cycle gives the busy
+    cycles the instructions alone need.  None without counters."""
+    e = counter_entry(kernel_key)
+    if not e or "sq_valu_mfma_busy_cycles" not in e:
+        return None
+    busy, cu = e["sq_valu_mfma_busy_cycles"], e["sq_busy_cu_cycles"]
+    clock_hz = cu / (e["busy_cus"] * e["kernel_avg_ns"] * 1e-9)
+    gpu_simd_cycles = 4 * N_CU * avg_launch_ms * 1e-3 * clock_hz
+    return {"busy_frac": busy / (4.0 * cu), "busy_frac_whole_gpu": busy / gpu_simd_cycles,
+            "mfma_busy_cycles": busy, "busy_cu_cycles": cu, "busy_cus": e["busy_cus"],
+            "implied_clock_ghz": clock_hz / 1e9,
+            "mops_bf16": e["sq_insts_valu_mfma_mops_bf16"],
+            "cycles_from_mops": e["sq_insts_valu_mfma_mops_bf16"] * 512 / 1024.0,
+            "executed_bf16_flops": e["sq_insts_valu_mfma_mops_bf16"] * 512,
+            "source": "profiles/counters.json (rocprofv3 --pmc on the current kernel sources)"}
+
+
+def measure_copy_bandwidth(nbytes=1 << 30, reps=10):
+    """HBM bandwidth a plain device copy (torch copy_) and an in-place
+    read-modify-write (mul_) reach on this GPU, in GB/s counting every byte
+    read and written once: the practical ceilings beside the 8 TB/s peak."""
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    res = {}
+    for name, fn in (("copy", lambda: b.copy_(a)), ("rmw_in_place", lambda: a.mul_(1.0000001))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s_ = torch.cuda.Event(enable_timing=True)
+        e_ = torch.cuda.Event(enable_timing=True)
+        s_.record()
+        for _ in range(reps):
+            fn()
+        e_.record()
+        torch.cuda.synchronize()
+        ms = s_.elapsed_time(e_) / reps
+        res[name] = 2 * n * 4 / (ms * 1e-3) / 1e9
+        log("[%s] %.1f GB/s (%d MiB each way)" % (name, res[name], nbytes >> 20))
+    del a, b
+    return res
 
 
 def time_calls(fn, n, stream):
@@ -337,7 +413,7 @@ def main():
     ap.add_argument("--no-unbounded", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy", "snap", "stages", "unbounded",
-                                       "backward"],
+                                       "backward", "bandwidth"],
                     default=None,
                     help="run one workload only (for profiler runs); prints no JSON line")
     args = ap.parse_args()
@@ -350,6 +426,9 @@ def main():
     import torch
     from gated_delta_rule_kda_amd import synth
 
+    if args.only == "bandwidth":
+        measure_copy_bandwidth()
+        return
     if args.only == "copy":
         # A plain copy of a known size, for scaling the HBM byte counters.
         n = 256 * 1024 * 1024
@@ -415,7 +494,8 @@ def main():
         "mfma": {"alg_flops_per_launch": p["flops"],
                  "achieved_tflops": p["flops"] / (p["avg_ms"] * 1e-3) / 1e12,
                  "peak_tflops": BF16_MFMA_PEAK / 1e12,
-                 "frac": p["flops"] / (p["avg_ms"] * 1e-3) / BF16_MFMA_PEAK},
+                 "frac": p["flops"] / (p["avg_ms"] * 1e-3) / BF16_MFMA_PEAK,
+                 "counters": mfma_busy("prefill_hv96", p["avg_ms"])},
     }
     if not args.no_gqa:
         gshape = synth.PREFILL_GQA_BF16
@@ -454,6 +534,8 @@ def main():
             "tokens_per_s": ub["tokens"] / (ub["avg_ms"] * 1e-3), "avg_launch_ms": ub["avg_ms"],
             "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
                          "frac": tf * 1e12 / FP32_VALU_PEAK,
+                         "peak_nonpacked": FP32_VALU_PEAK_NONPACKED / 1e12,
+                         "frac_nonpacked": tf * 1e12 / FP32_VALU_PEAK_NONPACKED,
                          "flops_per_launch": ub["flops"]}}
         del ub
     if not args.no_backward:
@@ -465,7 +547,10 @@ def main():
             "tokens_per_s": bw["tokens"] / (bw["avg_ms"] * 1e-3), "avg_call_ms": bw["avg_ms"],
             "workspace_bytes": bw["workspace"],
             "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
-                         "frac": tf * 1e12 / FP32_VALU_PEAK, "flops_per_call": bw["flops"]}}
+                         "frac": tf * 1e12 / FP32_VALU_PEAK,
+                         "peak_nonpacked": FP32_VALU_PEAK_NONPACKED / 1e12,
+                         "frac_nonpacked": tf * 1e12 / FP32_VALU_PEAK_NONPACKED,
+                         "flops_per_call": bw["flops"]}}
         del bw
     if not args.no_layer_stages:
         st = bench_layer_stages(args.steps, args.warmup)
@@ -483,6 +568,7 @@ def main():
                             "frac_hbm": st["output_gate"]["gbs"] / HBM_PEAK_GBS}}
     if not args.no_decode:
         d = bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup)
+        bw_meas = measure_copy_bandwidth()
         line["decode"] = {
             "workload": "KDA recurrent decode, %d steps, B256 H=HV=96 K=V=128 fp32, fused conv4+SiLU, "
                         "L2 norm, bounded gate -5, beta logits" % args.decode_steps,
@@ -491,7 +577,12 @@ def main():
             "roofline": {"bound": "hbm", "achieved": d["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": d["gbs"] / HBM_PEAK_GBS, "traffic": load_counters("decode_b256"),
                          "kernel": "decode_kernel<128,128>", "alg_bytes_per_launch": d["bytes"],
-                         "avg_launch_ms": d["per_ms"]}}
+                         "avg_launch_ms": d["per_ms"]},
+            "measured_ceilings": {"copy_gbs": bw_meas["copy"], "rmw_in_place_gbs": bw_meas["rmw_in_place"],
+                                  "frac_of_copy": d["gbs"] / bw_meas["copy"],
+                                  "frac_of_rmw_in_place": d["gbs"] / bw_meas["rmw_in_place"],
+                                  "what": "torch copy_ and in-place mul_ over 1 GiB fp32, bytes read + "
+                                          "written per second on this GPU"}}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p["inp"], shape)
     print(json.dumps(line), flush=True)
