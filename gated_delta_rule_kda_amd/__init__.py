@@ -24,7 +24,7 @@ import threading
 
 import torch
 
-__all__ = ["kda", "chunk_fwd", "chunk_fwd_workspace_size", "recurrent_bwd", "recurrent_bwd_noalloc", "recurrent_bwd_workspace_size", "chunk_fwd_snapshots", "recurrent_fwd", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
+__all__ = ["kda", "chunk_fwd", "chunk_fwd_gated", "chunk_fwd_workspace_size", "recurrent_bwd", "recurrent_bwd_noalloc", "recurrent_bwd_workspace_size", "chunk_fwd_snapshots", "recurrent_fwd", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
            "GATE_DIRECT", "GATE_BOUNDED", "GATE_SOFTPLUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +84,9 @@ def _load():
             lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_longlong
             lib.kda_chunk_fwd.argtypes = [P] * 8 + [I] * 6 + [F, I, I, P, ctypes.c_longlong, P]
             lib.kda_chunk_fwd.restype = I
+            lib.kda_chunk_fwd_gated.argtypes = ([P] * 7 + [F, P, P, F, P, P] + [I] * 6 + [F, I, I, P,
+                                                ctypes.c_longlong, P])
+            lib.kda_chunk_fwd_gated.restype = I
             lib.kda_recurrent_fwd.argtypes = [P] * 8 + [I] * 6 + [F, I, P]
             lib.kda_recurrent_fwd.restype = I
             lib.kda_recurrent_bwd_workspace_size.argtypes = [I] * 6
@@ -339,6 +342,33 @@ def chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
     return out, final_state
 
 
+def chunk_fwd_gated(q, k, v, z, beta_logit, A_log, dt_bias, gate_lower_bound=-5.0, scale=None,
+                    initial_state=None, output_final_state=False, *, out_gate=None,
+                    out_gate_eps=1e-6, chunk_size=32, out=None, final_state=None, workspace=None):
+    """``kda_chunk_fwd_gated``: :func:`chunk_fwd` with the gate
+    g = lb * sigmoid(exp(A_log) (z + dt_bias)) and beta = sigmoid(beta_logit)
+    formed in the kernel, and, with ``out_gate``, the output gate
+    y = sigmoid(out_gate) * o / sqrt(mean(o^2) + eps) applied to o.  bf16 only.
+    z [B,T,HV,K] fp32; beta_logit [B,T,HV] fp32; A_log [HV]; dt_bias [HV*K];
+    out_gate [B,T,HV,V] bf16 or None.  Returns (y or o, final state or None)."""
+    (B, T, H, HV, K, V), out, final_state = _prefill_args(
+        q, k, v, z, beta_logit, initial_state, output_final_state, out, final_state)
+    dev = q.device
+    _need(A_log, "A_log", torch.float32, (HV,), dev)
+    _need(dt_bias, "dt_bias", torch.float32, (HV * K,), dev)
+    if out_gate is not None:
+        _need(out_gate, "out_gate", q.dtype, (B, T, HV, V), dev)
+    ws = _prefill_workspace(workspace, (B, T, H, HV, K, V), chunk_size, q.dtype, dev)
+    with torch.cuda.device(dev):
+        _check(_load().kda_chunk_fwd_gated(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta_logit), _ptr(A_log), _ptr(dt_bias),
+            float(gate_lower_bound), _ptr(initial_state), _ptr(out_gate), float(out_gate_eps),
+            _ptr(out), _ptr(final_state), B, T, H, HV, K, V, float(scale) if scale else 0.0,
+            int(chunk_size), _dtype_code(q.dtype), _ptr(ws), ws.numel() if ws is not None else 0,
+            _stream_handle(dev)))
+    return out, final_state
+
+
 class _KDA(torch.autograd.Function):
     """Forward by kda_chunk_fwd (chunked) or kda_recurrent_fwd, backward by
     kda_recurrent_bwd: the two forward kernels compute the same function."""
@@ -412,6 +442,9 @@ def prefill_prologue(x, gate, beta, *, H, HV, K, V, conv_weight=None, conv_state
     overwritten with the registers after the last token.  Returns
     (q [B,T,H,K], k, v [B,T,HV,V] in x's dtype, g [B,T,HV,K] fp32, beta [B,T,HV] fp32)
     -- the inputs of :func:`chunk_fwd`.  ``out`` may supply those five tensors.
+    With ``gate`` and ``beta`` both None the gate and beta stages are skipped
+    (g and beta come back as None): the inputs of :func:`chunk_fwd_gated`,
+    which forms them itself.
     """
     _need(x, "x")
     B, T = x.shape[0], x.shape[1]
@@ -420,19 +453,24 @@ def prefill_prologue(x, gate, beta, *, H, HV, K, V, conv_weight=None, conv_state
     dev = x.device
     if tuple(x.shape) != (B, T, C):
         raise ValueError("x has shape %s, expected %s" % (tuple(x.shape), (B, T, C)))
-    _need(gate, "gate", torch.float32, (B, T, HV, K), dev)
-    _need(beta, "beta", torch.float32, (B, T, HV), dev)
+    gate_stage = gate is not None or beta is not None
+    if gate_stage:
+        _need(gate, "gate", torch.float32, (B, T, HV, K), dev)
+        _need(beta, "beta", torch.float32, (B, T, HV), dev)
     if out is None:
         out = (torch.empty(B, T, H, K, dtype=dt, device=dev), torch.empty(B, T, H, K, dtype=dt, device=dev),
                torch.empty(B, T, HV, V, dtype=dt, device=dev),
-               torch.empty(B, T, HV, K, dtype=torch.float32, device=dev),
-               torch.empty(B, T, HV, dtype=torch.float32, device=dev))
+               torch.empty(B, T, HV, K, dtype=torch.float32, device=dev) if gate_stage else None,
+               torch.empty(B, T, HV, dtype=torch.float32, device=dev) if gate_stage else None)
     q, k, v, g, bo = out
     _need(q, "q", dt, (B, T, H, K), dev)
     _need(k, "k", dt, (B, T, H, K), dev)
     _need(v, "v", dt, (B, T, HV, V), dev)
-    _need(g, "g", torch.float32, (B, T, HV, K), dev)
-    _need(bo, "beta_out", torch.float32, (B, T, HV), dev)
+    if gate_stage:
+        _need(g, "g", torch.float32, (B, T, HV, K), dev)
+        _need(bo, "beta_out", torch.float32, (B, T, HV), dev)
+    else:
+        g = bo = None
     pro, use = _prologue_struct(C, dev, conv_weight, conv_state, l2norm_qk, l2_eps, gate_mode,
                                 A_log, dt_bias, gate_lower_bound, beta_is_logit, HV, K, B)
     with torch.cuda.device(dev):

@@ -96,13 +96,32 @@ int prefill_sizes_ok(const char *fn, int B, int T, int H, int HV, int K, int V, 
 // intermediate in registers and LDS, so none of the built paths needs any.
 uint64_t prefill_workspace_bytes(int, int, int, int, int, int, int, int) { return 0; }
 
+// The fused layer stages of kda_chunk_fwd_gated (none when A_log is NULL).
+struct FusedStages {
+    bool on = false;
+    const float *A_log = nullptr, *dt_bias = nullptr;
+    float lower_bound = 0.f;
+    const void *ogate = nullptr;
+    float og_eps = 0.f;
+};
+
 int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, const float *g,
                    const float *beta, const float *initial_state, void *out, float *final_state,
                    float *snapshots, int snapshot_every, int B, int T, int H, int HV, int K,
                    int V, float scale, int chunk, int dtype, void *workspace,
-                   long long workspace_bytes, void *stream, bool recurrent = false) {
+                   long long workspace_bytes, void *stream, bool recurrent = false,
+                   const FusedStages &fs = FusedStages()) {
     g_err[0] = '\0';
     if (const int rc = prefill_sizes_ok(fn, B, T, H, HV, K, V, chunk, dtype)) return rc;
+    const bool fused = fs.on;
+    if (fused) {
+        if (dtype != KDA_DTYPE_BF16)
+            return fail(KDA_EUNSUPPORTED, "%s: the fused stages are built for KDA_DTYPE_BF16 only", fn);
+        if (!(fs.lower_bound >= -5.f && fs.lower_bound <= 0.f))
+            return fail(KDA_EINVAL, "%s: gate_lower_bound=%g must lie in [-5, 0]", fn, fs.lower_bound);
+        if (fs.ogate && !(fs.og_eps >= 0.f && isfinite(fs.og_eps)))
+            return fail(KDA_EINVAL, "%s: out_gate_eps must be finite and >= 0", fn);
+    }
     if (workspace_bytes < 0)
         return fail(KDA_EINVAL, "%s: workspace_bytes=%lld must be >= 0", fn, workspace_bytes);
     if (snapshots && (snapshot_every < 32 || snapshot_every % 32 != 0))
@@ -121,23 +140,30 @@ int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, 
     const uint64_t ws_need = recurrent ? 0 : prefill_workspace_bytes(B, T, H, HV, K, V, chunk, dtype);
     if (work) {
         if (!q || !k || !v || !g || !beta || !out)
-            return fail(KDA_EINVAL, "%s: q, k, v, g, beta and out must be non-NULL", fn);
+            return fail(KDA_EINVAL, "%s: q, k, v, %s, %s and out must be non-NULL", fn, fused ? "z" : "g",
+                        fused ? "beta_logit" : "beta");
+        if (fused && (!fs.A_log || !fs.dt_bias))
+            return fail(KDA_EINVAL, "%s: A_log and dt_bias must be non-NULL", fn);
         if (ws_need > 0 && (!workspace || static_cast<uint64_t>(workspace_bytes) < ws_need))
             return fail(KDA_EINVAL, "%s: workspace of %lld bytes at %p, %llu needed", fn, workspace_bytes,
                         workspace, static_cast<unsigned long long>(ws_need));
     }
     // the workspace is only looked at when the call uses it
     const void *ws = work && ws_need > 0 ? workspace : nullptr;
-    const void *ptrs[] = {q, k, v, g, beta, initial_state, out, final_state, snapshots, ws};
-    const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "out", "final_state", "snapshots",
-                           "workspace"};
-    for (int i = 0; i < 10; ++i)
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, out, final_state, snapshots, ws,
+                          fs.A_log, fs.dt_bias, fs.ogate};
+    const char *names[] = {"q", "k", "v", fused ? "z" : "g", fused ? "beta_logit" : "beta", "initial_state",
+                           "out", "final_state", "snapshots", "workspace", "A_log", "dt_bias", "out_gate"};
+    for (int i = 0; i < 13; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(KDA_EINVAL, "%s: %s is not 16-byte aligned", fn, names[i]);
 
     const Range r_in[] = {rng("q", q, nq * esz), rng("k", k, nq * esz), rng("v", v, nv * esz),
-                          rng("g", g, ng * 4), rng("beta", beta, nb * 4),
-                          rng("initial_state", initial_state, ns * 4)};
+                          rng(fused ? "z" : "g", g, ng * 4), rng(fused ? "beta_logit" : "beta", beta, nb * 4),
+                          rng("initial_state", initial_state, ns * 4),
+                          rng("A_log", fs.A_log, static_cast<uint64_t>(HV) * 4),
+                          rng("dt_bias", fs.dt_bias, static_cast<uint64_t>(HV) * K * 4),
+                          rng("out_gate", fs.ogate, nv * esz)};
     const Range r_out = rng("out", out, nv * esz);
     const Range r_st = rng("final_state", final_state, ns * 4);
     for (const Range &r : r_in) {
@@ -179,6 +205,8 @@ int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, 
     a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
     a.scale = scale;
     a.bf16 = dtype == KDA_DTYPE_BF16;
+    a.A_log = fs.A_log; a.dt_bias = fs.dt_bias; a.lower_bound = fs.lower_bound;
+    a.ogate = fs.ogate; a.og_eps = fs.og_eps;
     const hipError_t e = recurrent ? kda::launch_recurrent(a, st) : kda::launch_prefill(a, st);
     if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KDA_OK;
@@ -251,6 +279,21 @@ int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const f
     return chunk_fwd_impl("kda_chunk_fwd_snapshots", q, k, v, g, beta, initial_state, out,
                           final_state, snapshots, snapshot_every, B, T, H, HV, K, V, scale,
                           chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const float *z,
+                        const float *beta_logit, const float *A_log, const float *dt_bias,
+                        float gate_lower_bound, const float *initial_state, const void *out_gate,
+                        float out_gate_eps, void *out, float *final_state, int B, int T, int H,
+                        int HV, int K, int V, float scale, int chunk, int dtype, void *workspace,
+                        long long workspace_bytes, void *stream) {
+    FusedStages fs;
+    fs.on = true;
+    fs.A_log = A_log; fs.dt_bias = dt_bias; fs.lower_bound = gate_lower_bound;
+    fs.ogate = out_gate; fs.og_eps = out_gate_eps;
+    return chunk_fwd_impl("kda_chunk_fwd_gated", q, k, v, z, beta_logit, initial_state, out, final_state,
+                          nullptr, 0, B, T, H, HV, K, V, scale, chunk, dtype, workspace, workspace_bytes,
+                          stream, false, fs);
 }
 
 int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *g,
@@ -483,7 +526,7 @@ int kda_prefill_prologue(const void *x, const float *gate, const float *beta,
     }
     if (p.gate_mode < 0 || p.gate_mode > 2)
         return fail(KDA_EINVAL, "%s: gate_mode=%d is not a kda_gate_mode", fn, p.gate_mode);
-    if (p.gate_mode != KDA_GATE_DIRECT && (!p.A_log || !p.dt_bias))
+    if (p.gate_mode != KDA_GATE_DIRECT && (g || beta_out) && (!p.A_log || !p.dt_bias))
         return fail(KDA_EINVAL, "%s: gate_mode %d needs A_log and dt_bias", fn, p.gate_mode);
     if (p.l2norm_qk && !(p.l2_eps >= 0.f && isfinite(p.l2_eps)))
         return fail(KDA_EINVAL, "%s: l2_eps must be finite and >= 0", fn);
@@ -497,15 +540,23 @@ int kda_prefill_prologue(const void *x, const float *gate, const float *beta,
         !count(ncw, {C, KW}) || !count(nal, {HV}) || !count(ndt, {HV, K}) || nx >= (uint64_t(1) << 40))
         return fail(KDA_EINVAL, "%s: tensor sizes overflow", fn);
     if (static_cast<int64_t>(B) * T == 0) return KDA_OK;
-    if (!x || !gate || !beta || !q || !k || !v || !g || !beta_out)
-        return fail(KDA_EINVAL, "%s: x, gate, beta, q, k, v, g and beta_out must be non-NULL", fn);
+    // g and beta_out both NULL: no gate or beta stage (kda_chunk_fwd_gated
+    // forms them itself); gate and beta are then not read
+    const bool gate_stage = g || beta_out;
+    if (!x || !q || !k || !v) return fail(KDA_EINVAL, "%s: x, q, k and v must be non-NULL", fn);
+    if (gate_stage && (!gate || !beta || !g || !beta_out))
+        return fail(KDA_EINVAL, "%s: gate, beta, g and beta_out must be non-NULL (or g and beta_out both NULL)", fn);
+    if (!gate_stage) {
+        gate = nullptr;
+        beta = nullptr;
+    }
     const void *ptrs[] = {x, gate, beta, q, k, v, g, beta_out, p.conv_weight, p.conv_state, p.A_log, p.dt_bias};
     const char *names[] = {"x", "gate", "beta", "q", "k", "v", "g", "beta_out", "conv_weight", "conv_state",
                            "A_log", "dt_bias"};
     for (int i = 0; i < 12; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(KDA_EINVAL, "%s: %s is not 16-byte aligned", fn, names[i]);
-    const bool gp = p.gate_mode != KDA_GATE_DIRECT;
+    const bool gp = gate_stage && p.gate_mode != KDA_GATE_DIRECT;
     const Range rs[] = {rng("x", x, nx * esz), rng("gate", gate, ng * 4), rng("beta", beta, nb * 4),
                         rng("q", q, nq * esz), rng("k", k, nq * esz), rng("v", v, nv * esz),
                         rng("g", g, ng * 4), rng("beta_out", beta_out, nb * 4),

@@ -23,6 +23,16 @@ struct PrefillArgs {
     int B, T, H, HV, K, V;
     float scale;
     bool bf16;
+    // Fused layer stages (kda_chunk_fwd_gated; bf16 chunk kernel only).
+    // A_log set: g holds the pre-activation z and beta the logits, and the
+    // kernel forms g = lower_bound * sigmoid(exp(A_log[hv]) (z + dt_bias[hv K + f]))
+    // and beta = sigmoid(logit) itself.
+    const float *A_log, *dt_bias;   // [HV], [HV*K] or nullptr
+    float lower_bound;
+    // ogate set: out receives y = sigmoid(ogate) * o / sqrt(mean(o^2) + og_eps)
+    // per row of V values, o rounded to the output dtype first.
+    const void *ogate;              // [B,T,HV,V] (dtype) or nullptr
+    float og_eps;
 };
 
 // Arguments of one decode step.

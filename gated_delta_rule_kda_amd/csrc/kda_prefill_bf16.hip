@@ -65,6 +65,16 @@
 //    N(0, 0.3^2) keeps the output within 3e-3 RMS beyond its own bf16 rounding
 //    and the final state within 3e-3 RMS.
 
+//  * Fused layer stages (GATED, OG instantiations, for kda_chunk_fwd_gated):
+//    GATED reads the gate pre-activation z where g would be and beta logits,
+//    and the operand pass forms g = lb sigmoid(exp(A_log)(z + dt_bias)) (the
+//    bounded_gate of the page "metrale_model_weights/kimi_k3_host/kda.rs") and
+//    beta = sigmoid(logit) before the cumulative sums, so g never goes through
+//    HBM.  OG (one workgroup per whole V row) applies full_rank_output_gate of
+//    the same page, y = sigmoid(gate) o / sqrt(mean(o^2) + eps), to the bf16
+//    rows of o as the helper waves store them: the 16 lanes holding a row of
+//    128 values sum its squares by DPP within their row of lanes.
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -142,6 +152,25 @@ template <int N>
 __device__ __forceinline__ float row_shr(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, false));
 }
+// Sum of x over aligned groups of N lanes (N = 2, 4, 8 or 16), in every lane
+// of the group: swap neighbours, then pairs, then the two quads of each half
+// row, then the halves (DPP; a fixed order, the same result on every run).
+template <int N>
+__device__ __forceinline__ float rowN_sum(float x) {
+    static_assert(N == 2 || N == 4 || N == 8 || N == 16, "DPP groups");
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+    if constexpr (N >= 4)
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, false));  // quad_perm 2,3,0,1
+    if constexpr (N >= 8)
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false)); // row_half_mirror
+    if constexpr (N >= 16)
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false)); // row_mirror
+    return x;
+}
+// 1 / (1 + 2^t): the logistic function of -t ln 2 (hardware exponential and
+// reciprocal; 0 for t -> +inf, 1 for t -> -inf)
+__device__ __forceinline__ float inv1p_exp2(float t) { return __builtin_amdgcn_rcpf(1.0f + ex2(t)); }
+
 // x of lane p of the lane's group of four (DPP quad_perm broadcast; p must
 // fold to a constant)
 __device__ __forceinline__ float quad_bcast(float x, int p) {
@@ -217,8 +246,9 @@ struct Plan {
 
 // SNAP: the variant that also writes prefix snapshots of the state (a
 // separate instantiation, so that the plain path carries none of its code).
-template <int K, int VT, bool SNAP>
+template <int K, int VT, bool SNAP, bool GATED, bool OG>
 __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
+    static_assert(!OG || !SNAP, "the output gate is built for the plain prefill only");
     using L = Plan<K>;
     static_assert(L::bytes + L::stage_bytes(VT) <= 160 * 1024, "LDS plan exceeds 160 KB");
     constexpr int LDO = VT + 8;   // bf16 rows of the o staging tile
@@ -294,6 +324,17 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     const bool carry = wave < NCW;
     const bool opw = NOW == kNW || wave >= kNW - NOW;
     const int ow = wave - (kNW - NOW);   // operand wave index (valid when opw)
+    // GATED: the gate of the lane's two columns as a base-2 exponent,
+    // exp(-decay (z + dt_bias)) = 2^(gsl z + gof[c]) with decay = exp(A_log[hv])
+    float gsl = 0.f, gof[2] = {0.f, 0.f};
+    if constexpr (GATED) {
+        if (opw) {
+            const int f0 = ow * 2 * CPW + 2 * ((threadIdx.x & 63) % CPW);
+            gsl = -expf(a.A_log[hv]) * kLog2e;
+            gof[0] = gsl * a.dt_bias[hv * K + f0];
+            gof[1] = gsl * a.dt_bias[hv * K + f0 + 1];
+        }
+    }
 
     const uint16_t *qg = static_cast<const uint16_t *>(a.q);
     const uint16_t *kg = static_cast<const uint16_t *>(a.k);
@@ -347,7 +388,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     float gl[RPG][2];
     uint32_t qw[RPG], kw[RPG];
     float pl[2], og2[2];
-    auto op1a = [&](int buf) {
+    auto op1a = [&](int buf, int ch) {
         const int lane = opaque_tid() & 63;
 #pragma unroll
         for (int r = 0; r < RPG; ++r) {
@@ -356,14 +397,29 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             qw[r] = pf_q[r];
             kw[r] = pf_k[r];
         }
-        if (wave == kNW - 1 && lane < kC) sBeta[buf * kC + lane] = pf_b;
+        if (wave == kNW - 1 && lane < kC) {
+            float bt = pf_b;
+            // GATED: beta = sigmoid(logit); tokens past the end write nothing
+            if constexpr (GATED) bt = ch * kC + lane < T ? inv1p_exp2(-bt * kLog2e) : 0.f;
+            sBeta[buf * kC + lane] = bt;
+        }
     };
     // operand pass 1b: cumulative sums of g (natural log units) within the row
     // group, then across the row groups, and the chunk's exponent offsets; the
     // prefetch and the carry work of the phase cover the cross-lane latency
-    auto op1b = [&](int buf) {
+    auto op1b = [&](int buf, int ch) {
         const int lane = opaque_tid() & 63, cp = lane % CPW, rg = lane / CPW;
         const int f0 = ow * 2 * CPW + 2 * cp;
+        if constexpr (GATED) {
+            // g = lb sigmoid(decay (z + dt_bias)); 0 (no decay) past the end
+#pragma unroll
+            for (int r = 0; r < RPG; ++r)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    gl[r][c] = ch * kC + row_base(rg) + r < T
+                                   ? a.lower_bound * inv1p_exp2(__builtin_fmaf(gl[r][c], gsl, gof[c]))
+                                   : 0.f;
+        }
 #pragma unroll
         for (int r = 1; r < RPG; ++r) {
             gl[r][0] += gl[r - 1][0];
@@ -584,6 +640,24 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             pfv[j] = make_uint4(w[0], w[1], w[2], w[3]);
         }
     };
+    // OG: the output gate's values for the o tile the helper waves store
+    // next, loaded a phase ahead (the same addressing as the o stores)
+    uint4 pfog[OG ? VPL : 1];
+    auto loadOG = [&](int ch) {
+        if constexpr (OG) {
+            const int lane = opaque_tid() & 63;
+            const int t0 = ch * kC;
+            const auto rg_ = make_rsrc(static_cast<const uint16_t *>(a.ogate) + ((tok_b + t0) * HV + hv) * V + v0,
+                                       rows_bytes(t0, v_stride, VT, 2));
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                const int u = (3 * j + sh) * 64 + lane;
+                const int row = u / VUPR, c8 = (u % VUPR) * 8;
+                const auto w = __builtin_amdgcn_raw_buffer_load_b128(rg_, (row * v_stride + c8) * 2, 0, 0);
+                pfog[j] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    };
     auto writeV = [&]() {
         const int lane = opaque_tid() & 63;
 #pragma unroll
@@ -768,7 +842,30 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             const int u = (3 * j + sh) * 64 + lane;
             if (u < VU) {
                 const int row = u / VUPR, c8 = (u % VUPR) * 8;
-                const uint4 w = *reinterpret_cast<const uint4 *>(sO + row * LDO + c8);
+                uint4 w = *reinterpret_cast<const uint4 *>(sO + row * LDO + c8);
+                if constexpr (OG) {
+                    // y = sigmoid(gate) o / sqrt(mean(o^2) + eps) over the row's
+                    // VT = V values, held by VUPR consecutive lanes (u < VU is the
+                    // same for all of them: VU is a multiple of 64)
+                    const uint32_t ow_[4] = {w.x, w.y, w.z, w.w};
+                    const uint32_t gw[4] = {pfog[j].x, pfog[j].y, pfog[j].z, pfog[j].w};
+                    float o[8], ss = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        o[2 * e] = bf_lo(ow_[e]);
+                        o[2 * e + 1] = bf_hi(ow_[e]);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(o[e], o[e], ss);
+                    ss = rowN_sum<VUPR>(ss);
+                    const float inv = 1.0f / sqrtf(ss * (1.0f / VT) + a.og_eps);
+                    uint32_t yw[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        yw[e] = pk(inv1p_exp2(-bf_lo(gw[e]) * kLog2e) * o[2 * e] * inv,
+                                   inv1p_exp2(-bf_hi(gw[e]) * kLog2e) * o[2 * e + 1] * inv);
+                    w = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+                }
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, (row * v_stride + c8) * 2, 0, 0);
             }
         }
@@ -920,12 +1017,13 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         loadV(0);
         writeV();
         loadV(1);
+        loadOG(0);
     }
     if (opw) {
         load_prep(0);
-        op1a(0);
+        op1a(0, 0);
         load_prep(1);
-        op1b(0);
+        op1b(0, 0);
         op2(0);
     }
     lds_barrier();
@@ -943,16 +1041,16 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         // pass in one block, so the scheduler can fill MFMA latency with VALU)
         if (carry) {
             if (opw) {
-                op1a(nb);
+                op1a(nb, n + 1);
                 load_prep(n + 2);
-                op1b(nb);
+                op1b(nb, n + 1);
             }
             carryMain(n);
             if (opw) op2(nb);
         } else if (opw) {
-            op1a(nb);
+            op1a(nb, n + 1);
             load_prep(n + 2);
-            op1b(nb);
+            op1b(nb, n + 1);
             op2(nb);
         }
         lds_barrier();
@@ -963,6 +1061,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 storeO(n);
                 writeV();        // v of chunk n+1 for the next phase's carry
                 loadV(n + 2);
+                loadOG(n + 1);
             }
         }
         if (carry) {
@@ -985,10 +1084,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     if (a.ST && carry) carryStore(a.ST + (static_cast<size_t>(b) * HV + hv) * K * V);
 }
 
-template <int K, int VT, bool SNAP>
+template <int K, int VT, bool SNAP, bool GATED, bool OG>
 hipError_t launch_kvt_s(const PrefillArgs &a, hipStream_t stream) {
     using L = Plan<K>;
-    auto kern = prefill_bf16_kernel<K, VT, SNAP>;
+    auto kern = prefill_bf16_kernel<K, VT, SNAP, GATED, OG>;
     constexpr int lds = L::bytes + L::stage_bytes(VT);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1000,7 +1099,17 @@ hipError_t launch_kvt_s(const PrefillArgs &a, hipStream_t stream) {
 
 template <int K, int VT>
 hipError_t launch_kvt(const PrefillArgs &a, hipStream_t stream) {
-    return a.snap ? launch_kvt_s<K, VT, true>(a, stream) : launch_kvt_s<K, VT, false>(a, stream);
+    if (a.snap) return launch_kvt_s<K, VT, true, false, false>(a, stream);
+    if (!a.A_log) return launch_kvt_s<K, VT, false, false, false>(a, stream);
+    // the fused gate; the output gate in the o stores when the workgroup
+    // holds whole rows of V, else as its own pass over out afterwards
+    if (a.ogate && VT == a.V) return launch_kvt_s<K, VT, false, true, true>(a, stream);
+    hipError_t e = launch_kvt_s<K, VT, false, true, false>(a, stream);
+    if (e != hipSuccess || !a.ogate) return e;
+    OutputGateArgs og{};
+    og.o = a.out; og.gate = a.ogate; og.y = a.out;
+    og.rows = static_cast<long>(a.B) * a.T * a.HV; og.D = a.V; og.eps = a.og_eps; og.bf16 = true;
+    return launch_output_gate(og, stream);
 }
 
 template <int K>

@@ -289,11 +289,13 @@ hipError_t launch_prologue(const PrologueArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     e = a.bf16 ? launch_rows<true>(a, a.V, vv, stream) : launch_rows<false>(a, a.V, vv, stream);
     if (e != hipSuccess) return e;
-    const size_t n = static_cast<size_t>(a.B) * a.T * a.HV * (a.K / 4 + 1);
-    hipLaunchKernelGGL(prologue_gate_kernel, dim3(static_cast<unsigned>((n + kRowThreads - 1) / kRowThreads)),
-                       dim3(kRowThreads), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (a.g) {   // the gate and beta stage (skipped when the chunk kernel forms them)
+        const size_t n = static_cast<size_t>(a.B) * a.T * a.HV * (a.K / 4 + 1);
+        hipLaunchKernelGGL(prologue_gate_kernel, dim3(static_cast<unsigned>((n + kRowThreads - 1) / kRowThreads)),
+                           dim3(kRowThreads), 0, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (a.conv_w && a.conv_state_out) {
         const size_t nc = static_cast<size_t>(a.B) * (2 * a.H * a.K + a.HV * a.V);
         hipLaunchKernelGGL(prologue_conv_state_kernel, dim3(static_cast<unsigned>((nc + kRowThreads - 1) / kRowThreads)),

@@ -110,6 +110,42 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                   long long workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_fwd_gated -- kda_chunk_fwd with the layer stages on either side
+ * fused in: the gate and beta are formed inside the chunk kernel from their
+ * pre-activations, and the output gate is applied to o, as the host layer on
+ * the page "metrale_model_weights/kimi_k3_host/kda.rs" computes them
+ * (bounded_gate with a lower bound, a sigmoid on the beta logit,
+ * full_rank_output_gate).  Per token, value head hv and key channel f:
+ *     g    = gate_lower_bound * sigmoid(exp(A_log[hv]) * (z + dt_bias[hv*K + f]))
+ *     beta = sigmoid(beta_logit)
+ * then o as kda_chunk_fwd computes it from q, k, v, g, beta, and, when
+ * out_gate is given, per row of V values (o rounded to dtype first)
+ *     y = sigmoid(out_gate) * o / sqrt(mean(o^2) + out_gate_eps).
+ * g never goes to memory.  The output gate runs in the chunk kernel's o
+ * stores when one workgroup holds whole rows of V (the launch splits V over
+ * workgroups only when B * HV < 160), else as a pass over out after it.
+ *
+ *   z             [B, T, HV, K]  fp32 gate pre-activation (read where g would be)
+ *   beta_logit    [B, T, HV]     fp32
+ *   A_log         [HV] fp32;  dt_bias [HV * K] fp32
+ *   gate_lower_bound  in [-5, 0] (so -5 <= g <= 0, kda_chunk_fwd's precondition)
+ *   out_gate      [B, T, HV, V]  dtype, or NULL: out holds o itself
+ *   out_gate_eps  finite, >= 0 (used when out_gate is given)
+ *   out           [B, T, HV, V]  dtype: y (or o); may not overlap any input
+ * q, k, v, initial_state, final_state, sizes, scale, chunk, the workspace
+ * (kda_chunk_fwd_workspace_size gives its size here too) and the errors are
+ * those of kda_chunk_fwd.  Built for KDA_DTYPE_BF16 only (KDA_EUNSUPPORTED
+ * for KDA_DTYPE_F32).  kda_prefill_prologue with g and beta_out NULL gives
+ * its q, k, v inputs without writing g.
+ */
+int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const float *z,
+                        const float *beta_logit, const float *A_log, const float *dt_bias,
+                        float gate_lower_bound, const float *initial_state, const void *out_gate,
+                        float out_gate_eps, void *out, float *final_state, int B, int T, int H,
+                        int HV, int K, int V, float scale, int chunk, int dtype, void *workspace,
+                        long long workspace_bytes, void *stream);
+
+/*
  * kda_recurrent_fwd -- the same computation and interface as kda_chunk_fwd
  * (without the chunk size and the workspace), for gates with no lower bound.
  *
@@ -271,6 +307,8 @@ typedef struct kda_decode_prologue {
  *   g        [B, T, HV, K] fp32;  beta_out [B, T, HV] fp32
  *   B, T >= 0 (either 0: no-op); H, HV >= 1, HV % H == 0; K, V in {32, 64, 128};
  *   conv_kernel 1..8; dtype as above.
+ * g and beta_out may both be NULL: the gate and beta stages are then skipped
+ * and gate and beta are not read (kda_chunk_fwd_gated forms them itself).
  * Outputs may not overlap each other or any input.  The SOFTPLUS gate mode can
  * produce g < -5, which kda_chunk_fwd does not accept (see its precondition).
  */

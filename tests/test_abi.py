@@ -28,7 +28,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"kda_abi_version", "kda_last_error", "kda_chunk_fwd",
-                          "kda_chunk_fwd_workspace_size",
+                          "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_gated",
                           "kda_chunk_fwd_snapshots", "kda_recurrent_fwd", "kda_prefill_prologue",
                           "kda_output_gate", "kda_decode_step", "kda_recurrent_bwd",
                           "kda_recurrent_bwd_workspace_size", "kda_recurrent_bwd_noalloc"}
@@ -264,6 +264,47 @@ def prologue_call(pro=None, **over):
 ])
 def test_prefill_prologue_rejects(over, code, msg):
     rc, err = prologue_call(**over)
+    assert rc == code, err
+    assert msg in err, err
+
+
+def test_prefill_prologue_without_gate_stage():
+    """g and beta_out both NULL skip the gate stage (gate and beta are then
+    not needed); only one of them NULL is an error."""
+    rc, err = prologue_call(g=None, bo=FAKE * 8)
+    assert rc == 1 and "both NULL" in err, err
+    rc, err = prologue_call(g=None, bo=None, gate=None, beta=None, v=FAKE * 6 + 4)
+    assert rc == 1 and "v is not 16-byte aligned" in err, err
+
+
+def gated(**over):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, z=FAKE * 4, bl=FAKE * 5, al=FAKE * 6, dt=FAKE * 7, lb=-5.0,
+             s0=None, og=None, oge=1e-6, out=FAKE * 9, st=None, B=1, T=8, H=2, HV=4, K=32, V=32,
+             scale=0.0, chunk=0, dtype=1)
+    a.update(over)
+    L = lib()
+    rc = L.kda_chunk_fwd_gated(a["q"], a["k"], a["v"], a["z"], a["bl"], a["al"], a["dt"], a["lb"], a["s0"],
+                               a["og"], a["oge"], a["out"], a["st"], a["B"], a["T"], a["H"], a["HV"],
+                               a["K"], a["V"], a["scale"], a["chunk"], a["dtype"], None, 0, None)
+    return rc, L.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(dtype=0), 2, "KDA_DTYPE_BF16 only"),
+    (dict(lb=-5.5), 1, "[-5, 0]"),
+    (dict(lb=0.5), 1, "[-5, 0]"),
+    (dict(lb=float("nan")), 1, "[-5, 0]"),
+    (dict(al=None), 1, "A_log and dt_bias"),
+    (dict(dt=None), 1, "A_log and dt_bias"),
+    (dict(z=None), 1, "z, beta_logit and out"),
+    (dict(og=FAKE * 8, oge=-1.0), 1, "out_gate_eps"),
+    (dict(og=FAKE * 8 + 2), 1, "out_gate is not 16-byte aligned"),
+    (dict(q=BIG, k=2 * BIG, v=3 * BIG, z=4 * BIG, bl=5 * BIG, al=6 * BIG, dt=7 * BIG, og=8 * BIG,
+          out=8 * BIG + 32), 1, "out overlaps out_gate"),
+    (dict(HV=3), 1, "multiple"),
+])
+def test_chunk_fwd_gated_rejects(over, code, msg):
+    rc, err = gated(**over)
     assert rc == code, err
     assert msg in err, err
 
