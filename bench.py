@@ -354,6 +354,56 @@ def bench_layer_stages(steps, warmup):
     return res
 
 
+def bench_layer_path(shape, steps, warmup, tag):
+    """The layer around the prefill, end to end, two ways on the same inputs:
+    unfused = kda_prefill_prologue (conv width 4 + SiLU, L2 norm, bounded gate
+    into g, beta logits) -> kda_chunk_fwd -> kda_output_gate; fused =
+    kda_prefill_prologue without its gate stage -> kda_chunk_fwd_gated (gate,
+    beta and output gate in the chunk kernel).  Outputs preallocated; each
+    timed step is the whole sequence of calls."""
+    import torch
+    import gated_delta_rule_kda_amd as kda
+    dev = torch.device("cuda:0")
+    B, T, H, HV, K, V, KW = shape.B, shape.T, shape.H, shape.HV, shape.K, shape.V, 4
+    C = 2 * H * K + HV * V
+    gen = torch.Generator(device=dev).manual_seed(0)
+    r = lambda *s_: torch.randn(*s_, generator=gen, device=dev)
+    x = r(B, T, C).to(torch.bfloat16)
+    conv_w, conv_state = r(C, KW) * 0.5, torch.zeros(B, C, KW, device=dev)
+    z, A_log, dt_bias, bl = r(B, T, HV, K), r(HV) * 0.5, r(HV * K) * 0.5, r(B, T, HV)
+    ogate = r(B, T, HV, V).to(torch.bfloat16)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    q, k, v = torch.empty(B, T, H, K, **bf), torch.empty(B, T, H, K, **bf), torch.empty(B, T, HV, V, **bf)
+    g, beta = torch.empty(B, T, HV, K, device=dev), torch.empty(B, T, HV, device=dev)
+    o, y = torch.empty(B, T, HV, V, **bf), torch.empty(B, T, HV, V, **bf)
+    ST = torch.empty(B, HV, K, V, device=dev)
+    pro = dict(H=H, HV=HV, K=K, V=V, conv_weight=conv_w, conv_state=conv_state, l2norm_qk=True, l2_eps=1e-6)
+
+    def unfused():
+        kda.prefill_prologue(x, z, bl, gate_mode=kda.GATE_BOUNDED, A_log=A_log, dt_bias=dt_bias,
+                             gate_lower_bound=-5.0, beta_is_logit=True, out=(q, k, v, g, beta), **pro)
+        kda.chunk_fwd(q, k, v, g, beta, out=o, final_state=ST)
+        kda.output_gate(o, ogate, 1e-6, out=y)
+
+    def fused():
+        kda.prefill_prologue(x, None, None, out=(q, k, v, None, None), **pro)
+        kda.chunk_fwd_gated(q, k, v, z, bl, A_log, dt_bias, -5.0, out_gate=ogate, out_gate_eps=1e-6,
+                            out=y, final_state=ST)
+
+    res = {}
+    stream = torch.cuda.current_stream(dev)
+    for name, fn in (("unfused", unfused), ("fused", fused)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        starts, ends = time_calls(fn, steps, stream)
+        torch.cuda.synchronize()
+        ms = sum(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)) / steps
+        log("[layer %s %s] %.4f ms" % (tag, name, ms))
+        res[name + "_ms"] = ms
+    return res
+
+
 def backward_alg_flops(B, T, HV, K, V):
     """The gradient's own arithmetic per token and value head, as the
     back-propagation through time forms it: D += qs dout^T, S_t dout, D r,
@@ -413,7 +463,7 @@ def main():
     ap.add_argument("--no-unbounded", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy", "snap", "stages", "unbounded",
-                                       "backward", "bandwidth"],
+                                       "backward", "bandwidth", "layer"],
                     default=None,
                     help="run one workload only (for profiler runs); prints no JSON line")
     args = ap.parse_args()
@@ -455,6 +505,10 @@ def main():
         return
     if args.only == "stages":
         bench_layer_stages(args.steps, args.warmup)
+        return
+    if args.only == "layer":
+        bench_layer_path(synth.PREFILL_HV96_BF16, args.steps, args.warmup, "hv96")
+        bench_layer_path(synth.PREFILL_GQA_BF16, args.steps, args.warmup, "gqa")
         return
     if args.only == "backward":
         bench_backward(synth.PREFILL_HV96_BF16, args.steps, args.warmup)
@@ -566,6 +620,17 @@ def main():
                             "alg_bytes_per_launch": st["output_gate"]["bytes"],
                             "achieved_gbs": st["output_gate"]["gbs"],
                             "frac_hbm": st["output_gate"]["gbs"] / HBM_PEAK_GBS}}
+    if not args.no_layer_stages:
+        lp = {}
+        for tag, sh in (("hv96", synth.PREFILL_HV96_BF16), ("gqa", synth.PREFILL_GQA_BF16)):
+            r_ = bench_layer_path(sh, max(3, args.steps // 2), min(args.warmup, 5), tag)
+            lp[tag] = {"unfused_ms": r_["unfused_ms"], "fused_ms": r_["fused_ms"],
+                       "fused_speedup": r_["unfused_ms"] / r_["fused_ms"]}
+        line["layer_path"] = {
+            "workload": "prologue (conv width 4 + SiLU, L2 norm) + gate/beta + chunked prefill + output gate, "
+                        "end to end: unfused = kda_prefill_prologue -> kda_chunk_fwd -> kda_output_gate, "
+                        "fused = kda_prefill_prologue (no gate stage) -> kda_chunk_fwd_gated",
+            **lp}
     if not args.no_decode:
         d = bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup)
         bw_meas = measure_copy_bandwidth()
