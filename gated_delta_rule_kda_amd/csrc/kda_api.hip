@@ -217,18 +217,24 @@ int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, 
 namespace {
 
 // Workspace of kda_recurrent_bwd: fp32 regions, each 256-byte aligned (offsets
-// in bytes).
+// in bytes).  The passes after the forward one run over slabs of Ls tokens
+// (kBwdSlab, or all of T when shorter), so dr, the partial sums and the dg
+// terms hold one slab; the forward residuals r cover the whole sequence, and
+// the forward pass leaves the state at each later slab's start in snap.
 struct BwdLayout {
-    uint64_t r, dr, st, daP, dqP, dkrP, e, bs, total;
-    int NCB, NB;
+    uint64_t r, dr, st, snap, Dc, daP, dqP, dkrP, e, bs, gc, total;
+    int NCB, NB, Ls, NS;
 };
 
 bool bwd_layout(BwdLayout &L, int B, int T, int HV, int K, int V) {
     L.NCB = V / kda::kBwdCols;
-    L.NB = (T + kda::kDgBlock - 1) / kda::kDgBlock;
-    uint64_t nv, ns, np, ne, nbs;
-    if (!count(nv, {B, T, HV, V}) || !count(ns, {B, HV, K, V}) || !count(np, {L.NCB, B, T, HV, K}) ||
-        !count(ne, {B, T, HV, K}) || !count(nbs, {B, HV, K, L.NB + 1}))
+    L.Ls = T < kda::kBwdSlab ? (T > 0 ? T : 1) : kda::kBwdSlab;
+    L.NS = T > 0 ? (T - 1) / kda::kBwdSlab : 0;
+    L.NB = (L.Ls + kda::kDgBlock - 1) / kda::kDgBlock;
+    uint64_t nv, nvs, ns, nsn, np, ne, nbs, ngc;
+    if (!count(nv, {B, T, HV, V}) || !count(nvs, {B, L.Ls, HV, V}) || !count(ns, {B, HV, K, V}) ||
+        !count(nsn, {B, L.NS, HV, K, V}) || !count(np, {L.NCB, B, L.Ls, HV, K}) ||
+        !count(ne, {B, L.Ls, HV, K}) || !count(nbs, {B, HV, L.NB, K}) || !count(ngc, {2, B, HV, K}))
         return false;
     uint64_t off = 0;
     auto take = [&](uint64_t floats) {
@@ -236,9 +242,9 @@ bool bwd_layout(BwdLayout &L, int B, int T, int HV, int K, int V) {
         off += (floats * 4 + 255) / 256 * 256;
         return at;
     };
-    L.r = take(nv); L.dr = take(nv); L.st = take(ns);
+    L.r = take(nv); L.dr = take(nvs); L.st = take(ns); L.snap = take(nsn); L.Dc = take(ns);
     L.daP = take(np); L.dqP = take(np); L.dkrP = take(np);
-    L.e = take(ne); L.bs = take(nbs);
+    L.e = take(ne); L.bs = take(nbs); L.gc = take(ngc);
     L.total = off;
     return true;
 }
@@ -454,8 +460,12 @@ int recurrent_bwd_impl(const char *fn, const void *q, const void *k, const void 
         a.dkrP = reinterpret_cast<float *>(ws + L.dkrP);
         a.e = reinterpret_cast<float *>(ws + L.e);
         a.bs = reinterpret_cast<float *>(ws + L.bs);
+        a.snap = reinterpret_cast<float *>(ws + L.snap);
+        a.Dc = reinterpret_cast<float *>(ws + L.Dc);
+        a.gc_in = reinterpret_cast<float *>(ws + L.gc);
+        a.gc_out = reinterpret_cast<float *>(ws + L.gc) + static_cast<size_t>(B) * HV * K;
     }
-    a.NCB = L.NCB; a.NB = L.NB;
+    a.NCB = L.NCB; a.NB = L.NB; a.Ls = L.Ls; a.NS = L.NS;
     a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
     a.scale = scale;
     a.bf16 = dtype == KDA_DTYPE_BF16;
@@ -464,6 +474,9 @@ int recurrent_bwd_impl(const char *fn, const void *q, const void *k, const void 
         kda::PrefillArgs f{};
         f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.S0 = initial_state;
         f.out = nullptr; f.ST = a.ST; f.aux = a.r;
+        // the states at the later slabs' starts, for the forward gradient pass
+        f.snap = L.NS > 0 ? const_cast<float *>(a.snap) : nullptr;
+        f.snap_chunks = kda::kBwdSlab / 32; f.NS = L.NS;
         f.B = B; f.T = T; f.H = H; f.HV = HV; f.K = K; f.V = V;
         f.scale = scale; f.bf16 = a.bf16;
         const hipError_t e = kda::launch_recurrent(f, st);

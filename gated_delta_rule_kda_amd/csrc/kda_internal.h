@@ -14,8 +14,10 @@ struct PrefillArgs {
     const float *S0;            // [B,HV,K,V] or nullptr
     void *out;                  // [B,T,HV,V] (dtype)
     float *ST;                  // [B,HV,K,V] or nullptr
-    float *snap;                // [B,NS,HV,K,V] prefix snapshots or nullptr
-    int snap_chunks;            // chunks between snapshots (>= 1 when snap is set)
+    float *snap;                // [B,NS,HV,K,V] prefix snapshots or nullptr (also
+                                // the residual variant of the token-recurrent
+                                // kernel: the states at the backward's slab starts)
+    int snap_chunks;            // chunks of 32 tokens between snapshots (>= 1 when snap is set)
     int NS;                     // snapshots per sequence, T / (32 * snap_chunks)
     float *aux;                 // token-recurrent kernel only: when set, the
                                 // residuals r_t = v_t - k_t^T S_dec ([B,T,HV,V]
@@ -101,16 +103,26 @@ struct BwdArgs {
     float *r, *dr;              // [B,T,HV,V]: forward residuals, their gradients
     float *ST;                  // [B,HV,K,V]: forward final state
     float *daP, *dqP, *dkrP;    // [NCB,B,T,HV,K]: per column-block partial sums
-    float *e;                   // [B,T,HV,K]: per-token terms of dg
-    float *bs;                  // [B,HV,NB+1,K]: sums of e over blocks of kDgBlock
-                                // tokens, then the final-state term of dg
-    int NCB, NB;
+    float *e;                   // [B,Ls,HV,K]: per-token terms of dg
+    float *bs;                  // [B,HV,NB,K]: sums of e over blocks of kDgBlock tokens
+    int NCB, NB;                // column blocks; dg blocks per slab (Ls / kDgBlock)
+    // The passes after the forward one run slab by slab, the last slab first:
+    // tokens [t_begin, t_end) of every sequence per launch.  dr, the partial
+    // sums and e hold one slab (slab-local token index, Ls tokens per
+    // sequence); the state gradient D and the dg carry go from slab to slab.
+    int t_begin, t_end, Ls;
+    float *Dc;                  // [B,HV,K,V]: D at the start of the slab just done
+    const float *snap;          // [B,NS,HV,K,V]: forward state after (j+1) Ls tokens
+    int NS;
+    const float *gc_in;         // [B,HV,K]: dg carried in (later tokens, the final-state term)
+    float *gc_out;              // [B,HV,K]: dg carried to the slab before
     int B, T, H, HV, K, V;
     float scale;
     bool bf16;
 };
 constexpr int kBwdCols = 32;    // state columns per workgroup of the backward passes
 constexpr int kDgBlock = 64;    // tokens per block of the reverse sum that forms dg
+constexpr int kBwdSlab = 1024;  // tokens per slab of the backward passes (a multiple of kDgBlock)
 constexpr int kMaxConvKernel = 8;
 
 // Launch on `stream`; return the hipError_t of the launch.

@@ -270,6 +270,17 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(PrefillArgs a) {
                     static_cast<float *>(a.out)[oi] = o;
             }
         }
+        // RES: the state at the start of each later slab of the backward
+        // (after every snap_chunks * 32 tokens, strictly inside the sequence)
+        if constexpr (RES) {
+            const int te = t0 + kTC;
+            if (a.snap && te < a.T && te % (a.snap_chunks * 32) == 0) {
+                const int j = te / (a.snap_chunks * 32) - 1;
+                float *sn = a.snap + ((static_cast<size_t>(b) * a.NS + j) * a.HV + hv) * K * a.V;
+#pragma unroll
+                for (int r = 0; r < RPL; ++r) sn[static_cast<size_t>(row_of(r)) * a.V + c0 + c] = S[r];
+            }
+        }
         if (t0 + kTC < a.T) {
             store_round();                                 // the prefetched round to LDS
             __syncthreads();

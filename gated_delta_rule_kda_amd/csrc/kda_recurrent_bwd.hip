@@ -100,8 +100,9 @@ __device__ __forceinline__ uint32_t span_bytes(int T, int t0, int stride, int ro
 // Pass 2: the state gradient D, tokens in reverse.  Tokens past the end of the
 // sequence (only in the first round processed) stage as q = k = 0, exp(g) = 1,
 // beta = dout = r = 0: D passes through unchanged.
+// (at most 128 VGPRs, so that two workgroups share a CU: 4 waves per SIMD)
 template <int K, bool BF16>
-__global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void bwd_state_kernel(BwdArgs a) {
     constexpr int RPL = K / kRG;
     constexpr int TB = kTA;
     static_assert(TB % 2 == 0, "tokens go in pairs");
@@ -122,11 +123,17 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
     const int c0 = cb * kCols;
     const size_t tok_b = static_cast<size_t>(b) * a.T;
     const size_t st_off = (static_cast<size_t>(b) * a.HV + hv) * K * a.V;
+    // slab-local rows of dr and the partial sums: (b, t - t_begin, hv)
+    const size_t loc_b = static_cast<size_t>(b) * a.Ls - a.t_begin;
 
+    // D at the end of the slab: dL/dS_T for the last slab, else what the
+    // slab after this one left in Dc
+    const bool last_slab = a.t_end == a.T;
+    const float *D_in = last_slab ? a.dST : a.Dc;
     float D[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
-        D[r] = a.dST ? a.dST[st_off + static_cast<size_t>(row_of<K>(r, rg)) * a.V + c0 + c] : 0.f;
+        D[r] = D_in ? D_in[st_off + static_cast<size_t>(row_of<K>(r, rg)) * a.V + c0 + c] : 0.f;
 
     // ---- a round's inputs, prefetched into registers
     Raw4<BF16> pq, pk;
@@ -170,14 +177,15 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): every prefetched register consumed
     };
 
-    const int last0 = a.T > 0 ? ((a.T - 1) / TB) * TB : -TB;
-    if (last0 >= 0) {
+    // rounds of TB tokens from the slab start (slabs start at multiples of TB)
+    const int last0 = a.t_end > a.t_begin ? a.t_begin + ((a.t_end - 1 - a.t_begin) / TB) * TB : a.t_begin - TB;
+    if (last0 >= a.t_begin) {
         load_round(last0);
         store_round();
     }
     __syncthreads();
-    for (int t0 = last0; t0 >= 0; t0 -= TB) {
-        if (t0 >= TB) load_round(t0 - TB);               // in flight during this round
+    for (int t0 = last0; t0 >= a.t_begin; t0 -= TB) {
+        if (t0 >= a.t_begin + TB) load_round(t0 - TB);   // in flight during this round
         // a token's operands are read a token ahead of their use (two
         // alternating register sets), off the token-to-token chain
         struct Tok {
@@ -220,13 +228,12 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
         __syncthreads();
         // the next round to LDS (its loads are waited for here, before this
         // round's stores are issued), then the round's dv, dr and da partial sums
-        if (t0 >= TB) store_round();
+        if (t0 >= a.t_begin + TB) store_round();
         if (tid < NCV) {
             const int t = tid / kCols, cc = tid % kCols;
             if (t0 + t < a.T) {
-                const size_t i = ((tok_b + t0 + t) * a.HV + hv) * a.V + c0 + cc;
-                store1<BF16>(a.dv, i, sDr[t][cc]);
-                a.dr[i] = sDr[t][cc];
+                store1<BF16>(a.dv, ((tok_b + t0 + t) * a.HV + hv) * a.V + c0 + cc, sDr[t][cc]);
+                a.dr[((loc_b + t0 + t) * a.HV + hv) * a.V + c0 + cc] = sDr[t][cc];
             }
         }
         for (int i = tid; i < TB * K; i += kThreads) {
@@ -235,14 +242,16 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
                 float s = 0.f;
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) s += sDa[t][w][kk];
-                a.daP[((static_cast<size_t>(cb) * a.B * a.T + tok_b + t0 + t) * a.HV + hv) * K + kk] = s;
+                a.daP[((static_cast<size_t>(cb) * a.B * a.Ls + loc_b + t0 + t) * a.HV + hv) * K + kk] = s;
             }
         }
         __syncthreads();
     }
-    if (a.dS0) {
+    // D at the slab start: dS0 after the first slab, else for the slab before
+    float *D_out = a.t_begin == 0 ? a.dS0 : a.Dc;
+    if (D_out) {
 #pragma unroll
-        for (int r = 0; r < RPL; ++r) a.dS0[st_off + static_cast<size_t>(row_of<K>(r, rg)) * a.V + c0 + c] = D[r];
+        for (int r = 0; r < RPL; ++r) D_out[st_off + static_cast<size_t>(row_of<K>(r, rg)) * a.V + c0 + c] = D[r];
     }
 }
 
@@ -281,11 +290,17 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
     const int c0 = cb * kCols;
     const size_t tok_b = static_cast<size_t>(b) * a.T;
     const size_t st_off = (static_cast<size_t>(b) * a.HV + hv) * K * a.V;
+    const size_t loc_b = static_cast<size_t>(b) * a.Ls - a.t_begin;
 
+    // S at the slab start: S0 for the first slab, else the forward pass's
+    // snapshot after t_begin tokens
+    const float *S_in = a.t_begin == 0
+                            ? (a.S0 ? a.S0 + st_off : nullptr)
+                            : a.snap + ((static_cast<size_t>(b) * a.NS + a.t_begin / a.Ls - 1) * a.HV + hv) * K * a.V;
     float S[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
-        S[r] = a.S0 ? a.S0[st_off + static_cast<size_t>(row_of<K>(r, rg)) * a.V + c0 + c] : 0.f;
+        S[r] = S_in ? S_in[static_cast<size_t>(row_of<K>(r, rg)) * a.V + c0 + c] : 0.f;
 
     Raw4<BF16> pk;
     float4 pg;
@@ -307,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
         const uint32_t cspan_f = span_bytes<TB>(a.T, t0, a.HV * a.V, kCols, 4);
         const auto rv = make_rsrc(static_cast<const char *>(a.v) + cbase * ESZ, cspan_d);
         const auto rdo = make_rsrc(static_cast<const char *>(a.dout) + cbase * ESZ, cspan_d);
-        const auto rdr = make_rsrc(a.dr + cbase, cspan_f);
+        const auto rdr = make_rsrc(a.dr + (((loc_b + t0) * a.HV + hv) * a.V + c0), cspan_f);
         pv = load1<BF16>(rv, tc * a.HV * a.V + cc);
         pdo = load1<BF16>(rdo, tc * a.HV * a.V + cc);
         pdr = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdr, (tc * a.HV * a.V + cc) * 4, 0, 0));
@@ -329,13 +344,13 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): every prefetched register consumed
     };
 
-    if (a.T > 0) {
-        load_round(0);
+    if (a.t_end > a.t_begin) {
+        load_round(a.t_begin);
         store_round();
     }
     __syncthreads();
-    for (int t0 = 0; t0 < a.T; t0 += TB) {
-        if (t0 + TB < a.T) load_round(t0 + TB);
+    for (int t0 = a.t_begin; t0 < a.t_end; t0 += TB) {
+        if (t0 + TB < a.t_end) load_round(t0 + TB);
         struct Tok {
             float k[RPL], d[RPL];
             float v, dout, dr, beta;
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
             step(t + 1, x1);
         }
         __syncthreads();
-        if (t0 + TB < a.T) store_round();                 // the next round (see the reverse pass)
+        if (t0 + TB < a.t_end) store_round();             // the next round (see the reverse pass)
         for (int i = tid; i < TB * K; i += kThreads) {
             const int t = i / K, kk = i % K;
             if (t0 + t < a.T) {
@@ -387,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
                     sq += sDq[t][w][kk];
                     sk += sDk[t][w][kk];
                 }
-                const size_t o = ((static_cast<size_t>(cb) * a.B * a.T + tok_b + t0 + t) * a.HV + hv) * K + kk;
+                const size_t o = ((static_cast<size_t>(cb) * a.B * a.Ls + loc_b + t0 + t) * a.HV + hv) * K + kk;
                 a.dqP[o] = sq;
                 a.dkrP[o] = sk;
             }
@@ -397,31 +412,39 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Partial sums over the column blocks, the per-token dg terms and dbeta.  One
-// row (b, t, hv) of K values per K threads.
+// Partial sums over the column blocks, the per-token dg terms and dbeta, for
+// the tokens of one slab.  One row (b, t, hv) of K values per K threads; the
+// partial sums and e are indexed by the slab-local token, the inputs and
+// outputs by the token itself.
 template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_sum_kernel(BwdArgs a) {
     __shared__ float sRed[256];
     const int K = a.K, rows_per_block = 256 / K;
     const int tid = threadIdx.x, rl = tid / K, kk = tid % K;
-    const long nrows = static_cast<long>(a.B) * a.T * a.HV;
+    const int len = a.t_end - a.t_begin;
+    const long nrows = static_cast<long>(a.B) * len * a.HV;
     const long row = static_cast<long>(blockIdx.x) * rows_per_block + rl;
     const bool live = rl < rows_per_block && row < nrows;
     float prod = 0.f;
+    long grow = 0;
     if (live) {
-        const size_t plane = static_cast<size_t>(nrows) * K, i = static_cast<size_t>(row) * K + kk;
+        const int hv = static_cast<int>(row % a.HV), h = hv / (a.HV / a.H);
+        const long bt = row / a.HV;
+        const int b = static_cast<int>(bt / len), lt = static_cast<int>(bt % len);
+        const long tok = static_cast<long>(b) * a.T + a.t_begin + lt;     // b T + t
+        grow = tok * a.HV + hv;
+        const size_t plane = static_cast<size_t>(a.B) * a.Ls * a.HV * K;
+        const size_t i = ((static_cast<size_t>(b) * a.Ls + lt) * a.HV + hv) * K + kk;
         float da = 0.f, dkr = 0.f, dqs = 0.f;
         for (int cb = 0; cb < a.NCB; ++cb) {
             da += a.daP[cb * plane + i];
             dkr += a.dkrP[cb * plane + i];
             dqs += a.dqP[cb * plane + i];
         }
-        const long tok = row / a.HV;
-        const int hv = static_cast<int>(row % a.HV), h = hv / (a.HV / a.H);
         const size_t qi = (static_cast<size_t>(tok) * a.H + h) * K + kk;
         const float q = BF16 ? bf16_bits_to_float(static_cast<const uint16_t *>(a.q)[qi]) : static_cast<const float *>(a.q)[qi];
         const float k = BF16 ? bf16_bits_to_float(static_cast<const uint16_t *>(a.k)[qi]) : static_cast<const float *>(a.k)[qi];
-        const float beta = a.beta[row];
+        const float beta = a.beta[grow];
         a.e[i] = a.scale * q * dqs - k * (dkr + beta * da);
         prod = k * da;
         if (a.H == a.HV) {
@@ -440,55 +463,60 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(BwdArgs a) {
     if (live && kk == 0) {
         float s = 0.f;
         for (int j = 0; j < K; ++j) s += sRed[rl * K + j];
-        a.dbeta[row] = s;                                          // k . da
+        a.dbeta[grow] = s;                                         // k . da
     }
 }
 
 // With GQA (HV > H): dq = scale * sum over the q/k head's value heads of
-// S_t dout; dk = sum of beta da - S_dec dr.  One element of [B,T,H,K] per
-// thread.
+// S_t dout; dk = sum of beta da - S_dec dr.  One element of [B,T,H,K] of the
+// slab per thread.
 template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_qk_kernel(BwdArgs a) {
-    const long n = static_cast<long>(a.B) * a.T * a.H * a.K;
+    const int len = a.t_end - a.t_begin;
+    const long n = static_cast<long>(a.B) * len * a.H * a.K;
     const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= n) return;
     const int kk = static_cast<int>(i % a.K);
-    const long th = i / a.K, tok = th / a.H;
+    const long th = i / a.K, bt = th / a.H;
     const int h = static_cast<int>(th % a.H), G = a.HV / a.H;
+    const int b = static_cast<int>(bt / len), lt = static_cast<int>(bt % len);
+    const long tok = static_cast<long>(b) * a.T + a.t_begin + lt;
     float dq = 0.f, dk = 0.f;
     for (int j = 0; j < G; ++j) {
-        const long row = tok * a.HV + h * G + j;
-        const size_t ri = static_cast<size_t>(row) * a.K + kk;
+        const int hv = h * G + j;
+        const size_t ri = ((static_cast<size_t>(b) * a.Ls + lt) * a.HV + hv) * a.K + kk;
         dq += a.dqP[ri];
-        dk += a.beta[row] * a.daP[ri] - a.dkrP[ri];
+        dk += a.beta[tok * a.HV + hv] * a.daP[ri] - a.dkrP[ri];
     }
-    store1<BF16>(a.dq, i, a.scale * dq);
-    store1<BF16>(a.dk, i, dk);
+    const size_t o = (static_cast<size_t>(tok) * a.H + h) * a.K + kk;
+    store1<BF16>(a.dq, o, a.scale * dq);
+    store1<BF16>(a.dk, o, dk);
 }
 
-// Sums of e over blocks of kDgBlock tokens: bs[b, hv, block, k], and in the
-// entry after the last block the final-state term sum over V of
-// S_T (.) dL/dS_T (0 without dL/dS_T).
+// Sums of e over the slab's blocks of kDgBlock tokens: bs[b, hv, block, k].
+// In the last slab the same threads also start the dg carry with the
+// final-state term sum over V of S_T (.) dL/dS_T (0 without dL/dS_T).
 __global__ __launch_bounds__(256) void bwd_dg_blocks_kernel(BwdArgs a) {
-    const long n = static_cast<long>(a.B) * a.HV * a.NB * a.K;
+    const int len = a.t_end - a.t_begin;
+    const int nbs = (len + kDgBlock - 1) / kDgBlock;
+    const long n = static_cast<long>(a.B) * a.HV * nbs * a.K;
     const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= n) return;
     const int kk = static_cast<int>(i % a.K);
     const long r = i / a.K;
-    const int jb = static_cast<int>(r % a.NB);
-    const long bhv = r / a.NB;
+    const int jb = static_cast<int>(r % nbs);
+    const long bhv = r / nbs;
     const int b = static_cast<int>(bhv / a.HV), hv = static_cast<int>(bhv % a.HV);
     const int tb = jb * kDgBlock;
     const size_t step = static_cast<size_t>(a.HV) * a.K;
-    const float *e = a.e + ((static_cast<size_t>(b) * a.T + tb) * a.HV + hv) * a.K + kk;
+    const float *e = a.e + ((static_cast<size_t>(b) * a.Ls + tb) * a.HV + hv) * a.K + kk;
     float s = 0.f;
 #pragma unroll 16
     for (int t = 0; t < kDgBlock; ++t)
-        if (tb + t < a.T) s += e[t * step];
+        if (tb + t < len) s += e[t * step];
     // bs[b, hv, block, k]: the threads of one block read it k-contiguous
-    float *col = a.bs + bhv * (a.NB + 1) * a.K + kk;
-    col[static_cast<size_t>(jb) * a.K] = s;
-    if (jb == a.NB - 1) {
+    a.bs[(bhv * a.NB + jb) * a.K + kk] = s;
+    if (jb == nbs - 1 && a.t_end == a.T) {
         float c = 0.f;
         if (a.dST) {
             const float4 *st = reinterpret_cast<const float4 *>(a.ST + (static_cast<size_t>(bhv) * a.K + kk) * a.V);
@@ -499,35 +527,40 @@ __global__ __launch_bounds__(256) void bwd_dg_blocks_kernel(BwdArgs a) {
                 c += (x.x * y.x + x.y * y.y) + (x.z * y.z + x.w * y.w);
             }
         }
-        col[static_cast<size_t>(a.NB) * a.K] = c;
+        const_cast<float *>(a.gc_in)[bhv * a.K + kk] = c;
     }
 }
 
 // dg_u = sum over V of S_T (.) dL/dS_T + sum over t >= u of e_t: each thread
-// one block of tokens of one (b, hv, k), starting from the final-state term
-// and the later blocks' sums.
+// one block of tokens of one (b, hv, k) in the slab, starting from the carry
+// (the final-state term and every later slab's e) and the slab's later
+// blocks; the thread of the slab's first block leaves the carry for the slab
+// before.
 __global__ __launch_bounds__(256) void bwd_dg_kernel(BwdArgs a) {
-    const long n = static_cast<long>(a.B) * a.HV * a.NB * a.K;
+    const int len = a.t_end - a.t_begin;
+    const int nbs = (len + kDgBlock - 1) / kDgBlock;
+    const long n = static_cast<long>(a.B) * a.HV * nbs * a.K;
     const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= n) return;
     const int kk = static_cast<int>(i % a.K);
     const long r = i / a.K;
-    const int jb = static_cast<int>(r % a.NB);
-    const long bhv = r / a.NB;
+    const int jb = static_cast<int>(r % nbs);
+    const long bhv = r / nbs;
     const int b = static_cast<int>(bhv / a.HV), hv = static_cast<int>(bhv % a.HV);
-    const float *col = a.bs + bhv * (a.NB + 1) * a.K + kk;
-    float acc = col[static_cast<size_t>(a.NB) * a.K];
-    for (int j = a.NB - 1; j > jb; --j) acc += col[static_cast<size_t>(j) * a.K];
+    float acc = a.gc_in[bhv * a.K + kk];
+    for (int j = nbs - 1; j > jb; --j) acc += a.bs[(bhv * a.NB + j) * a.K + kk];
     const int tb = jb * kDgBlock;
     const size_t step = static_cast<size_t>(a.HV) * a.K;
-    const size_t base = ((static_cast<size_t>(b) * a.T + tb) * a.HV + hv) * a.K + kk;
+    const size_t lbase = ((static_cast<size_t>(b) * a.Ls + tb) * a.HV + hv) * a.K + kk;
+    const size_t gbase = ((static_cast<size_t>(b) * a.T + a.t_begin + tb) * a.HV + hv) * a.K + kk;
 #pragma unroll 16
     for (int t = kDgBlock - 1; t >= 0; --t) {
-        if (tb + t < a.T) {
-            acc += a.e[base + t * step];
-            a.dg[base + t * step] = acc;
+        if (tb + t < len) {
+            acc += a.e[lbase + t * step];
+            a.dg[gbase + t * step] = acc;
         }
     }
+    if (jb == 0) a.gc_out[bhv * a.K + kk] = acc;
 }
 
 template <int K>
@@ -554,16 +587,16 @@ hipError_t launch_passes(const BwdArgs &a, hipStream_t stream) {
 
 unsigned blocks_of(long n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
 
-}  // namespace
-
-hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
-    if (a.B == 0) return hipSuccess;
+// One slab: the reverse and forward gradient passes over its tokens, then
+// its reductions.
+hipError_t launch_slab(const BwdArgs &a, hipStream_t stream) {
     hipError_t e = a.K == 32 ? launch_passes<32>(a, stream)
                  : a.K == 64 ? launch_passes<64>(a, stream)
                  : a.K == 128 ? launch_passes<128>(a, stream) : hipErrorInvalidValue;
     if (e != hipSuccess || a.T == 0) return e;
-    const long rows = static_cast<long>(a.B) * a.T * a.HV;
-    const unsigned qk_blocks = blocks_of(static_cast<long>(a.B) * a.T * a.H * a.K, 256);
+    const int len = a.t_end - a.t_begin;
+    const long rows = static_cast<long>(a.B) * len * a.HV;
+    const unsigned qk_blocks = blocks_of(static_cast<long>(a.B) * len * a.H * a.K, 256);
     if (a.bf16) {
         hipLaunchKernelGGL(bwd_sum_kernel<true>, dim3(blocks_of(rows, 256 / a.K)), dim3(256), 0, stream, a);
         if (a.H != a.HV) hipLaunchKernelGGL(bwd_qk_kernel<true>, dim3(qk_blocks), dim3(256), 0, stream, a);
@@ -571,10 +604,37 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL(bwd_sum_kernel<false>, dim3(blocks_of(rows, 256 / a.K)), dim3(256), 0, stream, a);
         if (a.H != a.HV) hipLaunchKernelGGL(bwd_qk_kernel<false>, dim3(qk_blocks), dim3(256), 0, stream, a);
     }
-    const long nb = static_cast<long>(a.B) * a.HV * a.NB * a.K;
+    const long nb = static_cast<long>(a.B) * a.HV * ((len + kDgBlock - 1) / kDgBlock) * a.K;
     hipLaunchKernelGGL(bwd_dg_blocks_kernel, dim3(blocks_of(nb, 256)), dim3(256), 0, stream, a);
     hipLaunchKernelGGL(bwd_dg_kernel, dim3(blocks_of(nb, 256)), dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs &a0, hipStream_t stream) {
+    if (a0.B == 0) return hipSuccess;
+    if (a0.T == 0) {   // only dS0 = dL/dS_T (or zeros): the reverse pass over no tokens
+        BwdArgs a = a0;
+        a.t_begin = a.t_end = 0;
+        return a.K == 32 ? launch_passes<32>(a, stream)
+             : a.K == 64 ? launch_passes<64>(a, stream)
+             : a.K == 128 ? launch_passes<128>(a, stream) : hipErrorInvalidValue;
+    }
+    // slabs of Ls tokens, the last one first; the dg carry alternates between
+    // the two halves of gc (gc_out of one slab is gc_in of the next)
+    const int ns = (a0.T + a0.Ls - 1) / a0.Ls;
+    float *gc[2] = {const_cast<float *>(a0.gc_in), a0.gc_out};
+    for (int s = ns - 1, j = 0; s >= 0; --s, ++j) {
+        BwdArgs a = a0;
+        a.t_begin = s * a0.Ls;
+        a.t_end = min(a0.T, a.t_begin + a0.Ls);
+        a.gc_in = gc[j & 1];
+        a.gc_out = gc[(j + 1) & 1];
+        const hipError_t e = launch_slab(a, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kda

@@ -193,10 +193,13 @@ int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *
  * T = 0 only dinitial_state is written (= dfinal_state, or zeros).
  * kda_recurrent_bwd_workspace_size returns the workspace size in bytes, or -1
  * (message in kda_last_error) for sizes kda_recurrent_bwd rejects.
- * Runs the forward recurrence once more (keeping its residuals and final
- * state in the workspace), then a reverse pass for the state gradient and a
- * forward pass for the gradients that need the state; all asynchronous on
- * `stream`.
+ * Runs the forward recurrence once more (keeping its residuals, its final
+ * state and the state every 1024 tokens in the workspace), then, one slab of
+ * 1024 tokens at a time from the last, a reverse pass for the state gradient,
+ * a forward pass for the gradients that need the state and the sums that
+ * finish them; all asynchronous on `stream`.  The workspace therefore grows
+ * with T only by the residuals (4 V bytes per token and value head): 1.16 GB
+ * at B = 1, T = 8192, HV = 96, K = V = 128.
  */
 long long kda_recurrent_bwd_workspace_size(int B, int T, int H, int HV, int K, int V);
 int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *g,
@@ -215,8 +218,8 @@ int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *
  * memory takes its place, one per GPU, held from the first call on that GPU
  * until the process ends.  Nothing is allocated or freed by the call.
  *  - Sizes whose kda_recurrent_bwd_workspace_size exceeds the array return
- *    KDA_EUNSUPPORTED (for K = V = 128 that is about 17,000 token-value-head
- *    pairs, e.g. B = 1, T = 1024, HV = 16), with no side effects.
+ *    KDA_EUNSUPPORTED, with no side effects (at K = V = 128, B = 1, T = 1024,
+ *    HV = 16 fits; the HV96 shape at T = 8192 needs 1.16 GB and does not).
  *  - The array serves the GPU `stream` runs on (the current device for the
  *    NULL stream).  Every call on that GPU shares it and leaves its last
  *    contents there; nothing in it needs clearing, since each call writes

@@ -405,14 +405,25 @@ def test_recurrent_bwd_rejects(over, code, msg):
 
 def test_recurrent_bwd_workspace_size():
     L = lib()
-    n = L.kda_recurrent_bwd_workspace_size(2, 100, 2, 4, 64, 128)
-    # r, dr [B,T,HV,V]; S_T [B,HV,K,V]; 3 x partials [V/32,B,T,HV,K]; e [B,T,HV,K];
-    # block sums and the final-state term [B,HV,K,ceil(T/64)+1] -- fp32, each
-    # region rounded up to 256 bytes
     up = lambda floats: (floats * 4 + 255) // 256 * 256
-    want = (2 * up(2 * 100 * 4 * 128) + up(2 * 4 * 64 * 128) + 3 * up(4 * 2 * 100 * 4 * 64)
-            + up(2 * 100 * 4 * 64) + up(2 * 4 * 64 * 3))
-    assert n == want
+
+    def want(B, T, HV, K, V, slab=1024):
+        # r [B,T,HV,V]; per slab of Ls = min(T, 1024) tokens: dr [B,Ls,HV,V];
+        # S_T and the carried state gradient [B,HV,K,V]; the states at the
+        # later slabs' starts [B,(T-1)//1024,HV,K,V]; 3 x partials
+        # [V/32,B,Ls,HV,K]; e [B,Ls,HV,K]; block sums [B,HV,ceil(Ls/64),K];
+        # the dg carry [2,B,HV,K] -- fp32, each region rounded up to 256 bytes
+        Ls = min(T, slab)
+        NS = (T - 1) // slab
+        return (up(B * T * HV * V) + up(B * Ls * HV * V) + 2 * up(B * HV * K * V) + up(B * NS * HV * K * V)
+                + 3 * up(V // 32 * B * Ls * HV * K) + up(B * Ls * HV * K) + up(B * HV * -(-Ls // 64) * K)
+                + up(2 * B * HV * K))
+    for args in [(2, 100, 2, 4, 64, 128), (1, 8192, 96, 96, 128, 128), (3, 2500, 1, 2, 32, 64),
+                 (1, 1024, 1, 1, 128, 128), (1, 1025, 1, 1, 128, 128)]:
+        B, T, H, HV, K, V = args
+        assert L.kda_recurrent_bwd_workspace_size(*args) == want(B, T, HV, K, V), args
+    # the HV96 workload: about 1.16 GB (6.05 GB with whole-sequence partial sums)
+    assert L.kda_recurrent_bwd_workspace_size(1, 8192, 96, 96, 128, 128) < 1.2e9
     assert L.kda_recurrent_bwd_workspace_size(1, 8, 2, 3, 32, 32) == -1
     assert "HV=3" in L.kda_last_error().decode()
     assert L.kda_recurrent_bwd_workspace_size(1, 8, 2, 4, 32, 48) == -1

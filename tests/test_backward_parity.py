@@ -154,6 +154,25 @@ def test_backward_long_memory(case):
     run(shape, seed=T + 1, gate="bounded", with_dst=True, label="long memory " + str(case))
 
 
+SLABS = [
+    # B, T, H, HV, K, V, dtype: sequences longer than one slab of 1024 tokens,
+    # so the state gradient, the forward states and the dg sum cross slab
+    # boundaries (a last slab of 76 tokens; of 1 token; three slabs with GQA)
+    (2, 1100, 1, 2, 64, 64, torch.bfloat16),
+    (1, 1025, 2, 2, 32, 32, torch.float32),
+    (1, 2100, 1, 4, 128, 32, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", SLABS, ids=lambda c: "B%dT%dH%dHV%dK%dV%d-%s" % (
+    c[:6] + (str(c[6]).split(".")[-1],)))
+@pytest.mark.parametrize("gate", ["bounded", "unbounded"])
+def test_backward_across_slabs(case, gate):
+    B, T, H, HV, K, V, dt = case
+    shape = synth.PrefillShape(B, T, H, HV, K, V, dt, "normal", s0_std=0.3, g_lower=-1.0)
+    run(shape, seed=T + 7, gate=gate, with_dst=True, label="slabs " + str(case))
+
+
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
 def test_backward_beta_zero(dt):
     """beta = 0: nothing is written, so dL/dv = 0 exactly and
