@@ -740,7 +740,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     // R, solve and output of chunk n (U stays in registers for the state update)
     auto carryMain = [&](int n) {
         const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
-        const int cbuf = n & 1, t0 = n * kC;
+        const int cbuf = n & 1;
         // operand fragments that do not depend on this chunk's products
         const __bf16 *t11 = sTi + lr * L16 + lg * 4;
         const __bf16 *t22 = sTi + 2 * 16 * L16 + lr * L16 + lg * 4;
