@@ -17,8 +17,9 @@ Headline workload (one JSON line on stdout):
     (kda_chunk_fwd_snapshots; the snapshot stores count in the bytes), and the
     layer's per-token stages on the HV96 shape (kda_prefill_prologue,
     kda_output_gate) against the HBM peak, kda_recurrent_fwd on the HV96
-    workload with an unbounded gate, and kda_recurrent_bwd (the backward) on
-    the HV96 workload (both against the fp32 vector peak).
+    workload with an unbounded gate (against the fp32 vector peak), and the
+    backward on the HV96 workload: kda_chunk_bwd (fp32 matrix cores) and
+    kda_recurrent_bwd (fp32 vector ALUs).
 Inputs are seeded synthetic tensors (gated_delta_rule_kda_amd.synth) created on
 the GPU before the timed region.  Kernel durations come from HIP events
 recorded on the stream the kernels are launched on.  The CPU baseline runs the
@@ -45,6 +46,7 @@ FP32_VALU_PEAK = 157.3e12      # MI355X fp32 vector, FLOP/s, counting packed (2-
 # The same without packed FP32 (256 CU x 4 SIMD x 16 lanes x 2 flops x 2.4 GHz):
 # the ceiling for code built, as this library is, without packed FP32 instructions.
 FP32_VALU_PEAK_NONPACKED = 78.6e12
+FP32_MFMA_PEAK = 157.3e12      # MI355X dense fp32 matrix cores, FLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 N_CU = 256                     # MI355X compute units, 4 SIMDs each
 
@@ -412,9 +414,10 @@ def backward_alg_flops(B, T, HV, K, V):
     return 15 * K * V * B * T * HV
 
 
-def bench_backward(shape, steps, warmup, inp=None):
-    """kda_recurrent_bwd on `shape` with dL/do ~ N(0,1) and dL/dS_T ~ 0.1 N(0,1);
-    workspace and outputs allocated before the timed region."""
+def bench_backward(shape, steps, warmup, inp=None, chunked=True):
+    """kda_chunk_bwd (chunked) or kda_recurrent_bwd on `shape` with dL/do ~
+    N(0,1) and dL/dS_T ~ 0.1 N(0,1); workspace and outputs allocated before the
+    timed region."""
     import torch
     import gated_delta_rule_kda_amd as kda
     from gated_delta_rule_kda_amd import synth
@@ -425,7 +428,10 @@ def bench_backward(shape, steps, warmup, inp=None):
     gen = torch.Generator(device=dev).manual_seed(1)
     dout = torch.randn(B, T, HV, V, generator=gen, device=dev).to(shape.dtype)
     dST = torch.randn(B, HV, K, V, generator=gen, device=dev) * 0.1
-    ws = torch.empty(kda.recurrent_bwd_workspace_size(B, T, H, HV, K, V), dtype=torch.uint8, device=dev)
+    nbytes = (kda.chunk_bwd_workspace_size(B, T, H, HV, K, V, shape.dtype) if chunked
+              else kda.recurrent_bwd_workspace_size(B, T, H, HV, K, V))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    bwd = kda.chunk_bwd if chunked else kda.recurrent_bwd
     outs = (torch.empty(B, T, H, K, dtype=shape.dtype, device=dev),
             torch.empty(B, T, H, K, dtype=shape.dtype, device=dev),
             torch.empty(B, T, HV, V, dtype=shape.dtype, device=dev),
@@ -434,7 +440,7 @@ def bench_backward(shape, steps, warmup, inp=None):
     args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dout, dST)
 
     def call():
-        kda.recurrent_bwd(*args, initial_state=inp["S0"], workspace=ws, out=outs)
+        bwd(*args, initial_state=inp["S0"], workspace=ws, out=outs)
 
     for _ in range(warmup):
         call()
@@ -444,8 +450,8 @@ def bench_backward(shape, steps, warmup, inp=None):
     torch.cuda.synchronize()
     ms = sum(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)) / steps
     flops = backward_alg_flops(B, T, HV, K, V)
-    log("[backward] avg %.3f ms, %.1f TFLOP/s (15KV per token-head), workspace %.2f GB"
-        % (ms, flops / (ms * 1e-3) / 1e12, ws.numel() / 1e9))
+    log("[backward %s] avg %.3f ms, %.1f TFLOP/s (15KV per token-head), workspace %.2f GB"
+        % ("chunked" if chunked else "recurrent", ms, flops / (ms * 1e-3) / 1e12, ws.numel() / 1e9))
     return dict(avg_ms=ms, flops=flops, tokens=B * T, workspace=ws.numel())
 
 
@@ -511,7 +517,8 @@ def main():
         bench_layer_path(synth.PREFILL_GQA_BF16, args.steps, args.warmup, "gqa")
         return
     if args.only == "backward":
-        bench_backward(synth.PREFILL_HV96_BF16, args.steps, args.warmup)
+        bench_backward(synth.PREFILL_HV96_BF16, args.steps, args.warmup, chunked=True)
+        bench_backward(synth.PREFILL_HV96_BF16, args.steps, args.warmup, chunked=False)
         return
     if args.only == "snap":
         bench_prefill(synth.PREFILL_HV96_BF16, args.steps, args.warmup, "hv96 snapshots/1024", 1024)
@@ -593,19 +600,29 @@ def main():
                          "flops_per_launch": ub["flops"]}}
         del ub
     if not args.no_backward:
-        bw = bench_backward(shape, max(3, args.steps // 4), min(args.warmup, 3), inp=p["inp"])
+        bw = bench_backward(shape, max(3, args.steps // 4), min(args.warmup, 3), inp=p["inp"], chunked=True)
         tf = bw["flops"] / (bw["avg_ms"] * 1e-3) / 1e12
+        br = bench_backward(shape, max(3, args.steps // 4), min(args.warmup, 3), inp=p["inp"], chunked=False)
+        tr = br["flops"] / (br["avg_ms"] * 1e-3) / 1e12
         line["backward"] = {
-            "workload": "kda_recurrent_bwd on the HV96 workload (B1 T8192 H=HV=96 K=V=128 bf16, bounded "
+            "workload": "kda_chunk_bwd on the HV96 workload (B1 T8192 H=HV=96 K=V=128 bf16, bounded "
                         "gate), dL/do ~ N(0,1), dL/dS_T ~ 0.1 N(0,1): dq, dk, dv, dg, dbeta, dS0",
             "tokens_per_s": bw["tokens"] / (bw["avg_ms"] * 1e-3), "avg_call_ms": bw["avg_ms"],
             "workspace_bytes": bw["workspace"],
-            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
-                         "frac": tf * 1e12 / FP32_VALU_PEAK,
-                         "peak_nonpacked": FP32_VALU_PEAK_NONPACKED / 1e12,
-                         "frac_nonpacked": tf * 1e12 / FP32_VALU_PEAK_NONPACKED,
-                         "flops_per_call": bw["flops"]}}
-        del bw
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": FP32_MFMA_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": tf * 1e12 / FP32_MFMA_PEAK, "flops_per_call": bw["flops"],
+                         "what": "the gradient's own arithmetic (15KV per token and value head) against "
+                                 "the fp32 matrix-core peak its products run on"},
+            "recurrent": {
+                "workload": "kda_recurrent_bwd (token recurrence on the vector ALUs, any finite g) on the "
+                            "same inputs",
+                "avg_call_ms": br["avg_ms"], "workspace_bytes": br["workspace"],
+                "roofline": {"bound": "alu", "achieved": tr, "peak": FP32_VALU_PEAK / 1e12,
+                             "unit": "TFLOP/s", "frac": tr * 1e12 / FP32_VALU_PEAK,
+                             "peak_nonpacked": FP32_VALU_PEAK_NONPACKED / 1e12,
+                             "frac_nonpacked": tr * 1e12 / FP32_VALU_PEAK_NONPACKED,
+                             "flops_per_call": br["flops"]}}}
+        del bw, br
     if not args.no_layer_stages:
         st = bench_layer_stages(args.steps, args.warmup)
         line["layer_stages"] = {

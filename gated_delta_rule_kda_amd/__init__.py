@@ -24,7 +24,7 @@ import threading
 
 import torch
 
-__all__ = ["kda", "chunk_fwd", "chunk_fwd_gated", "chunk_fwd_workspace_size", "recurrent_bwd", "recurrent_bwd_noalloc", "recurrent_bwd_workspace_size", "chunk_fwd_snapshots", "recurrent_fwd", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
+__all__ = ["kda", "chunk_fwd", "chunk_fwd_gated", "chunk_fwd_workspace_size", "recurrent_bwd", "recurrent_bwd_noalloc", "recurrent_bwd_workspace_size", "chunk_bwd", "chunk_bwd_workspace_size", "chunk_fwd_snapshots", "recurrent_fwd", "prefill_prologue", "output_gate", "decode_step", "abi_version", "library_path", "KDAError",
            "GATE_DIRECT", "GATE_BOUNDED", "GATE_SOFTPLUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +35,7 @@ _lib = None
 KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EHIP = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_DIRECT, GATE_BOUNDED, GATE_SOFTPLUS = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class KDAError(RuntimeError):
@@ -95,6 +95,10 @@ def _load():
             lib.kda_recurrent_bwd.restype = I
             lib.kda_recurrent_bwd_noalloc.argtypes = ([P] * 14 + [I] * 6 + [F, I, P])
             lib.kda_recurrent_bwd_noalloc.restype = I
+            lib.kda_chunk_bwd_workspace_size.argtypes = [I] * 7
+            lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_longlong
+            lib.kda_chunk_bwd.argtypes = ([P] * 14 + [I] * 6 + [F, I, P, ctypes.c_longlong, P])
+            lib.kda_chunk_bwd.restype = I
             lib.kda_chunk_fwd_snapshots.argtypes = [P] * 9 + [I] * 7 + [F, I, I, P, ctypes.c_longlong, P]
             lib.kda_chunk_fwd_snapshots.restype = I
             lib.kda_prefill_prologue.argtypes = ([P, P, P, ctypes.POINTER(DecodePrologue)] + [P] * 5
@@ -259,8 +263,28 @@ def recurrent_bwd_noalloc(q, k, v, g, beta, dout, d_final_state=None, scale=None
                          need_d_initial_state=need_d_initial_state, out=out, _noalloc=True)
 
 
+def chunk_bwd_workspace_size(B, T, H, HV, K, V, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace ``kda_chunk_bwd`` needs for these sizes."""
+    n = _load().kda_chunk_bwd_workspace_size(B, T, H, HV, K, V, _dtype_code(dtype))
+    if n < 0:
+        raise KDAError(KDA_EINVAL, _load().kda_last_error().decode(errors="replace"))
+    return n
+
+
+def chunk_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initial_state=None,
+              *, workspace=None, need_d_initial_state=True, out=None):
+    """``kda_chunk_bwd``: :func:`recurrent_bwd` in the chunk form on the
+    matrix cores, for bf16 inputs with -5 <= g <= 0 (the inputs of
+    :func:`chunk_fwd`).  Same arguments and results; ``workspace`` of at
+    least :func:`chunk_bwd_workspace_size` bytes."""
+    return recurrent_bwd(q, k, v, g, beta, dout, d_final_state, scale, initial_state,
+                         workspace=workspace, need_d_initial_state=need_d_initial_state,
+                         out=out, _chunked=True)
+
+
 def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initial_state=None,
-                  *, workspace=None, need_d_initial_state=True, out=None, _noalloc=False):
+                  *, workspace=None, need_d_initial_state=True, out=None, _noalloc=False,
+                  _chunked=False):
     """``kda_recurrent_bwd``: gradients of the forward pass with the same
     inputs (any finite g).  dout [B,T,HV,V] is dL/do (v's dtype),
     d_final_state [B,HV,K,V] fp32 (or None) is dL/dS_T.  Returns (dq, dk
@@ -282,7 +306,8 @@ def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initia
         if t_ is not None:
             _need(t_, n_, torch.float32, (B, HV, K, V), dev)
     if not _noalloc:
-        nbytes = recurrent_bwd_workspace_size(B, T, H, HV, K, V)
+        nbytes = (chunk_bwd_workspace_size(B, T, H, HV, K, V, dt) if _chunked
+                  else recurrent_bwd_workspace_size(B, T, H, HV, K, V))
         if workspace is None:
             workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         else:
@@ -309,7 +334,8 @@ def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initia
                 _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dS0),
                 B, T, H, HV, K, V, float(scale) if scale else 0.0, _dtype_code(dt), _stream_handle(dev)))
         else:
-            _check(_load().kda_recurrent_bwd(
+            entry = _load().kda_chunk_bwd if _chunked else _load().kda_recurrent_bwd
+            _check(entry(
                 _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dout),
                 _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dS0),
                 B, T, H, HV, K, V, float(scale) if scale else 0.0, _dtype_code(dt), _ptr(workspace),
@@ -371,7 +397,8 @@ def chunk_fwd_gated(q, k, v, z, beta_logit, A_log, dt_bias, gate_lower_bound=-5.
 
 class _KDA(torch.autograd.Function):
     """Forward by kda_chunk_fwd (chunked) or kda_recurrent_fwd, backward by
-    kda_recurrent_bwd: the two forward kernels compute the same function."""
+    kda_chunk_bwd (chunked forward, bf16) or kda_recurrent_bwd: all compute
+    the same function and its gradients."""
 
     @staticmethod
     def forward(ctx, q, k, v, g, beta, initial_state, scale, chunked):
@@ -379,6 +406,7 @@ class _KDA(torch.autograd.Function):
         o, S = fwd(q, k, v, g, beta, scale=scale, initial_state=initial_state, output_final_state=True)
         ctx.save_for_backward(q, k, v, g, beta, initial_state)
         ctx.scale = scale
+        ctx.chunked = chunked and q.dtype == torch.bfloat16
         return o, S
 
     @staticmethod
@@ -386,8 +414,9 @@ class _KDA(torch.autograd.Function):
         q, k, v, g, beta, S0 = ctx.saved_tensors
         do = torch.zeros_like(v) if do is None else do.contiguous()
         dS = None if dS is None else dS.contiguous()
-        dq, dk, dv, dg, db, dS0 = recurrent_bwd(q, k, v, g, beta, do, dS, scale=ctx.scale, initial_state=S0,
-                                                need_d_initial_state=S0 is not None)
+        bwd = chunk_bwd if ctx.chunked else recurrent_bwd
+        dq, dk, dv, dg, db, dS0 = bwd(q, k, v, g, beta, do, dS, scale=ctx.scale, initial_state=S0,
+                                      need_d_initial_state=S0 is not None)
         return dq, dk, dv, dg, db, dS0, None, None
 
 
@@ -396,7 +425,8 @@ def kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=Fal
     "K3/kda/ops/reference/recurrent.py" page.  Returns (o, final state or
     None); gradients reach q, k, v, g, beta and initial_state.  ``chunked``
     picks kda_chunk_fwd (needs -5 <= g <= 0) or kda_recurrent_fwd (any g)
-    for the forward; the backward is kda_recurrent_bwd either way."""
+    for the forward; the backward is kda_chunk_bwd after a chunked bf16
+    forward, else kda_recurrent_bwd."""
     o, S = _KDA.apply(q, k, v, g, beta, initial_state, scale, chunked)
     return o, (S if output_final_state else None)
 

@@ -249,6 +249,40 @@ bool bwd_layout(BwdLayout &L, int B, int T, int HV, int K, int V) {
     return true;
 }
 
+// Workspace of kda_chunk_bwd: fp32 regions, each 256-byte aligned (offsets in
+// bytes).  Slabs of Ls tokens (1024, or T rounded up to the chunk when
+// shorter); everything but the final state and the slab-start states holds one
+// slab.
+struct ChunkBwdLayout {
+    uint64_t st, snap1, Dc, snapc, W, U, img, dR, dMs, e, bs, gc, total;
+    int Ls, NS1, NCs, NB;
+};
+
+bool chunk_bwd_layout(ChunkBwdLayout &L, int B, int T, int HV, int K, int V) {
+    L.Ls = T > kda::kBwdSlab ? kda::kBwdSlab : (T > 0 ? (T + 31) / 32 * 32 : 32);
+    L.NS1 = T > 0 ? (T + L.Ls - 1) / L.Ls - 1 : 0;
+    L.NCs = L.Ls / 32;
+    L.NB = (L.Ls + kda::kDgBlock - 1) / kda::kDgBlock;
+    const int imf = kda::chunk_bwd_image_floats(K);
+    uint64_t ns, nsn, nsc, nv, nimg, nms, ne, nbs, ngc;
+    if (imf <= 0 || !count(ns, {B, HV, K, V}) || !count(nsn, {B, L.NS1, HV, K, V}) ||
+        !count(nsc, {B, L.NCs - 1, HV, K, V}) || !count(nv, {B, L.Ls, HV, V}) ||
+        !count(nimg, {B, L.NCs, HV, imf}) || !count(nms, {B, L.NCs, HV, K, V}) ||
+        !count(ne, {B, L.Ls, HV, K}) || !count(nbs, {B, HV, L.NB, K}) || !count(ngc, {2, B, HV, K}))
+        return false;
+    uint64_t off = 0;
+    auto take = [&](uint64_t floats) {
+        const uint64_t at = off;
+        off += (floats * 4 + 255) / 256 * 256;
+        return at;
+    };
+    L.st = take(ns); L.snap1 = take(nsn); L.Dc = take(ns); L.snapc = take(nsc);
+    L.W = take(nv); L.U = take(nv); L.img = take(nimg); L.dR = take(nv); L.dMs = take(nms);
+    L.e = take(ne); L.bs = take(nbs); L.gc = take(ngc);
+    L.total = off;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -327,6 +361,102 @@ long long kda_recurrent_bwd_workspace_size(int B, int T, int H, int HV, int K, i
         return -1;
     }
     return static_cast<long long>(L.total);
+}
+
+long long kda_chunk_bwd_workspace_size(int B, int T, int H, int HV, int K, int V, int dtype) {
+    g_err[0] = '\0';
+    const char *fn = "kda_chunk_bwd_workspace_size";
+    if (dtype != KDA_DTYPE_BF16) {
+        fail(KDA_EUNSUPPORTED, "%s: dtype %d; the chunked backward takes KDA_DTYPE_BF16 (use kda_recurrent_bwd)", fn, dtype);
+        return -1;
+    }
+    if (B < 0 || T < 0 || H < 1 || HV < 1 || HV % H != 0) {
+        fail(KDA_EINVAL, "%s: B=%d, T=%d, H=%d, HV=%d are not valid sizes", fn, B, T, H, HV);
+        return -1;
+    }
+    if (!head_dim_ok(K) || !head_dim_ok(V)) {
+        fail(KDA_EUNSUPPORTED, "%s: K=%d, V=%d; each must be 32, 64 or 128", fn, K, V);
+        return -1;
+    }
+    ChunkBwdLayout L;
+    if (!chunk_bwd_layout(L, B, T, HV, K, V)) {
+        fail(KDA_EINVAL, "%s: tensor sizes overflow", fn);
+        return -1;
+    }
+    return static_cast<long long>(L.total);
+}
+
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  const float *initial_state, const void *dout, const float *dfinal_state, void *dq,
+                  void *dk, void *dv, float *dg, float *dbeta, float *dinitial_state, int B, int T,
+                  int H, int HV, int K, int V, float scale, int dtype, void *workspace,
+                  long long workspace_bytes, void *stream) {
+    g_err[0] = '\0';
+    const char *fn = "kda_chunk_bwd";
+    if (dtype != KDA_DTYPE_BF16)
+        return fail(KDA_EUNSUPPORTED, "%s: dtype %d; the chunked backward takes KDA_DTYPE_BF16 (use kda_recurrent_bwd)", fn, dtype);
+    if (B < 0 || T < 0) return fail(KDA_EINVAL, "%s: B=%d and T=%d must be >= 0", fn, B, T);
+    if (H < 1 || HV < 1) return fail(KDA_EINVAL, "%s: H=%d and HV=%d must be >= 1", fn, H, HV);
+    if (HV % H != 0) return fail(KDA_EINVAL, "%s: HV=%d is not a multiple of H=%d", fn, HV, H);
+    if (!head_dim_ok(K) || !head_dim_ok(V))
+        return fail(KDA_EUNSUPPORTED, "%s: K=%d, V=%d; each must be 32, 64 or 128", fn, K, V);
+    if (static_cast<int64_t>(B) * HV * 32 > 0x7fffffffLL)
+        return fail(KDA_EUNSUPPORTED, "%s: B=%d, HV=%d exceed the launch grid", fn, B, HV);
+    if (isinf(scale)) return fail(KDA_EINVAL, "%s: scale is infinite", fn);
+    if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(K));
+    ChunkBwdLayout L;
+    uint64_t nq, nv, ng, nb, ns;
+    if (!chunk_bwd_layout(L, B, T, HV, K, V) || !count(nq, {B, T, H, K}) || !count(nv, {B, T, HV, V}) ||
+        !count(ng, {B, T, HV, K}) || !count(nb, {B, T, HV}) || !count(ns, {B, HV, K, V}))
+        return fail(KDA_EINVAL, "%s: tensor sizes overflow", fn);
+    const bool work = static_cast<int64_t>(B) * T > 0;
+    if (work) {
+        if (!q || !k || !v || !g || !beta || !dout)
+            return fail(KDA_EINVAL, "%s: q, k, v, g, beta and dout must be non-NULL", fn);
+        if (!dq || !dk || !dv || !dg || !dbeta)
+            return fail(KDA_EINVAL, "%s: dq, dk, dv, dg and dbeta must be non-NULL", fn);
+        if (!workspace) return fail(KDA_EINVAL, "%s: workspace is NULL", fn);
+        if (workspace_bytes < 0 || static_cast<uint64_t>(workspace_bytes) < L.total)
+            return fail(KDA_EINVAL, "%s: workspace of %lld bytes, %llu needed", fn, workspace_bytes,
+                        static_cast<unsigned long long>(L.total));
+    }
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, dout, dfinal_state,
+                          dq, dk, dv, dg, dbeta, dinitial_state, workspace};
+    const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "dout", "dfinal_state",
+                           "dq", "dk", "dv", "dg", "dbeta", "dinitial_state", "workspace"};
+    for (int i = 0; i < 15; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(KDA_EINVAL, "%s: %s is not 16-byte aligned", fn, names[i]);
+    const Range rs[] = {rng("q", q, nq * 2), rng("k", k, nq * 2), rng("v", v, nv * 2),
+                        rng("g", g, ng * 4), rng("beta", beta, nb * 4),
+                        rng("initial_state", initial_state, ns * 4), rng("dout", dout, nv * 2),
+                        rng("dfinal_state", dfinal_state, ns * 4),
+                        rng("dq", dq, nq * 2), rng("dk", dk, nq * 2), rng("dv", dv, nv * 2),
+                        rng("dg", dg, ng * 4), rng("dbeta", dbeta, nb * 4),
+                        rng("dinitial_state", dinitial_state, ns * 4),
+                        rng("workspace", work ? workspace : nullptr, L.total)};
+    for (int o = 8; o < 15; ++o)
+        for (int i = 0; i < 15; ++i)
+            if (i != o && overlap(rs[o], rs[i]))
+                return fail(KDA_EINVAL, "%s: %s overlaps %s", fn, rs[o].name, rs[i].name);
+
+    char *ws = static_cast<char *>(workspace);
+    kda::ChunkBwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = initial_state;
+    a.dout = dout; a.dST = dfinal_state;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dS0 = dinitial_state;
+    if (work) {
+        auto at = [&](uint64_t off) { return reinterpret_cast<float *>(ws + off); };
+        a.ST = at(L.st); a.snap1 = at(L.snap1); a.Dc = at(L.Dc); a.snapc = at(L.snapc);
+        a.W = at(L.W); a.U = at(L.U); a.img = at(L.img); a.dR = at(L.dR); a.dMs = at(L.dMs);
+        a.e = at(L.e); a.bs = at(L.bs); a.gc = at(L.gc);
+    }
+    a.Ls = L.Ls; a.NS1 = L.NS1; a.NB = L.NB;
+    a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
+    a.scale = scale;
+    const hipError_t e = kda::launch_chunk_backward(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KDA_OK;
 }
 
 }  // extern "C"

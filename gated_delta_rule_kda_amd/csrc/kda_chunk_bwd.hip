@@ -1,0 +1,903 @@
+// KDA chunked backward for bf16 inputs on gfx950 (kda_chunk_bwd).
+//
+// The gradients of the chunk form of the bf16 prefill (kda_prefill_bf16.hip:
+// chunk-local cumulative decay G in base 2 around reference row r = 15, the
+// unit-lower-triangular in-chunk solve, the carried state M), derived chunk by
+// chunk in reverse.  With, per chunk,
+//     e1 = 2^{G_i - G_r}, e2 = 2^{G_r - G_i}, Gamma_i = 2^{G_i},
+//     Lambda'_i = 2^{G_last - G_i}, Pq = q e1, Pk = k e1, Rk = k e2,
+//     A_qk = L(Pq Rk^T), A_kk = diag(beta) SL(Pk Rk^T), T = (I + A_kk)^-1,
+//     W = v - (k Gamma) M, U = T diag(beta) W,
+//     O = s ((q Gamma) M + A_qk U),  M' = Gamma_last (.) M + (k Lambda')^T U,
+// and dM' = dL/dM' entering from the chunk after (dL/dS_T for the last):
+//     dU = (k Lambda') dM' + s A_qk^T dO
+//     dR = T^T dU                      (blocked: dR2 = T22^T dU2,
+//                                       dR1 = T11^T (dU1 - A21^T dR2))
+//     dM = Gamma_last (.) dM' + s (q Gamma)^T dO - (beta k Gamma)^T dR
+//     dA_qk = s L(dO U^T),  dA_kk = -SL(dR U^T)
+//     dq       = s Gamma (.) (dO M^T) + e1 (.) (dA_qk Rk)
+//     dk_read  = beta (.) (-Gamma (.) (dR M^T) + e1 (.) (dA_kk Rk))
+//     dk_write = Lambda' (.) (U dM'^T) + e2 (.) (dA_qk^T Pq + (beta dA_kk)^T Pk)
+//     dk = dk_read + dk_write,  dv = beta dR,
+//     dbeta = rowsum(dR (.) W) + rowsum(dA_kk (.) SL(Pk Rk^T))
+// and dg from the same identity the token-recurrent backward uses: a change
+// of g_u scales every read at t >= u against every write before u, so
+//     dg_u = sum_{t >= u} (q (.) dq + k (.) dk_read - k (.) dk_write)_t
+//            + sum_V S_T (.) dL/dS_T.
+// This is the backward of KDAFunction on the "K3/kda/ops/reference/recurrent.py"
+// page restated for the chunk form of delta_recurrence on the
+// "src/tinycenn_lm/research_layers.py" page (its forward quantities as the
+// prefill computes them).
+//
+// Passes, one slab of Ls tokens at a time from the last (the state gradient
+// and the dg sum carried between slabs):
+//  0. a forward pass over the whole sequence keeps S_T and the states at the
+//     slab starts; per slab, the forward kernel's backward instantiation runs
+//     the slab again from its start state, keeping the state at every chunk
+//     start, W and U (kda_prefill_bf16.hip);
+//  1. prep (chunk-parallel): every chunk's operands of the reverse chain --
+//     k Lambda', s (q Gamma)^T, -(beta k Gamma)^T, s A_qk^T, T11^T, T22^T,
+//     -A21^T, Gamma_last -- as the exact LDS image the chain kernel reads;
+//  2. chain (one workgroup per (b, hv, V tile), chunks in reverse): dU, dR,
+//     the dM update, on the matrix cores; keeps dR and every chunk's dM';
+//  3. grad (chunk-parallel, one workgroup per (b, q/k head, chunk), summing
+//     over the head's value heads): the rest of the formulas above;
+//  4. dg: the blocked reverse sum of the token-recurrent backward.
+// Every product is an fp32 MFMA (v_mfma_f32_16x16x4_f32): no operand is
+// rounded below fp32 in the backward itself.
+//
+// fp32 16x16x4 MFMA lane layout (lane l, x = l % 16, kq = l / 16): A[x][kq],
+// B[kq][x]; the result holds D[4 kq + j][x] in element j.  Every product
+// D[m][n] = sum_k X[m][k] Y[n][k] below reads, for reduction block k0, the
+// float4 X[m0 + x][k0 + 4 kq .. + 3] and Y[n0 + x][k0 + 4 kq .. + 3] and issues
+// four MFMAs (element j of both): the reduction index inside a block of 16 is
+// permuted (step j takes k0 + 4 kq + j), which both operands share.  A result
+// used as the B operand of the next product (dm, dU, dR) is already in that
+// order: its element j is row 4 kq + j.
+
+#include "kda_internal.h"
+#include "kda_lanes.h"
+
+namespace kda {
+namespace {
+
+using lanes::ex2;
+using lanes::group_sum;
+using lanes::kLog2e;
+using lanes::make_rsrc;
+
+constexpr int kC = 32;     // tokens per chunk
+constexpr int kR = 15;     // reference row
+constexpr int kThr = 512;  // threads per workgroup of the prep and chain kernels (8 waves)
+constexpr int kThrG = 512;  // of the grad kernel
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mma4(float a, float b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+// x of lane 4 (lane / 4) + p (DPP quad broadcast)
+template <int P>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), P | (P << 2) | (P << 4) | (P << 6), 0xf, 0xf, false));
+}
+__device__ __forceinline__ float quad_bcast(float x, int p) {
+    switch (p) {
+    case 0: return quad_bcast<0>(x);
+    case 1: return quad_bcast<1>(x);
+    case 2: return quad_bcast<2>(x);
+    default: return quad_bcast<3>(x);
+    }
+}
+// a 16x16 tile product over reduction length L (a multiple of 16):
+// D[m][n] += sum_k X[m][k] Y[n][k], X and Y row pointers of this lane's row x
+template <int L>
+__device__ __forceinline__ void tile_nt(const float *xrow, const float *yrow, int kq, f32x4 &acc) {
+#pragma unroll
+    for (int k0 = 0; k0 < L; k0 += 16) {
+        const f32x4 xa = ld4(xrow + k0 + 4 * kq), yb = ld4(yrow + k0 + 4 * kq);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mma4(xa[j], yb[j], acc);
+    }
+}
+
+// ---------------------------------------------------------------- operand image
+// Floats of one chunk's operands of the reverse chain, as the chain kernel's
+// LDS holds them (row pitches padded by 4 floats).
+template <int K>
+struct Img {
+    static constexpr int LK = K + 4;     // [C][K] rows
+    static constexpr int LC = kC + 4;    // [K][C], [C][C] rows
+    static constexpr int L16 = 20;       // [16][16] rows
+    static constexpr int oKb = 0;                    // [C][LK]  k Lambda'
+    static constexpr int oA1 = oKb + kC * LK;         // [K][LC]  s (q Gamma)^T
+    static constexpr int oA2 = oA1 + K * LC;         // [K][LC]  -(beta k Gamma)^T
+    static constexpr int oAq = oA2 + K * LC;         // [C][LC]  s A_qk^T
+    static constexpr int oT1 = oAq + kC * LC;        // [16][L16] T11^T
+    static constexpr int oT2 = oT1 + 16 * L16;       // [16][L16] T22^T
+    static constexpr int oNA = oT2 + 16 * L16;       // [16][L16] -A21^T
+    static constexpr int oGl = oNA + 16 * L16;       // [K] Gamma_last
+    static constexpr int used = oGl + K;
+    // floats per chunk in HBM and per LDS buffer: whole rounds of the
+    // chain kernel's copy (256 lanes x 16 bytes)
+    static constexpr int floats = (used + 1023) / 1024 * 1024;
+};
+
+// Per-slab arguments of the three kernels.
+struct SlabArgs {
+    ChunkBwdArgs a;
+    int t_begin, len, NCs;      // tokens [t_begin, t_begin + len), NCs chunks
+    const float *Sstart;        // state at the slab start for (b, hv): Sstart + b * s_bstride + hv K V; null = 0
+    long long s_bstride;
+    const float *dm_in;         // [B,HV,K,V] dL/dS at the slab end, or null (0)
+    float *dm_out;              // [B,HV,K,V] dL/dS at the slab start, or null
+};
+
+// Base-2 cumulative sums of g over the chunk (per column), for rows < nv
+// (rows past the end get g = 0): sG[i][c] = log2(e) sum_{t <= i} g_t[c].
+// All 512 threads: column c = tid % K, a run of kC / (512 / K) rows each.
+template <int K, int NTHR>
+__device__ __forceinline__ void chunk_cumsum(const float *g, int nv, int row_stride, float *sG, int LK,
+                                             float *sTot) {
+    constexpr int NP = NTHR / K, RP = kC / NP;
+    static_assert(RP >= 1, "at least one row per thread");
+    const int tid = threadIdx.x, c = tid % K, p = tid / K;
+    float acc = 0.f, gv[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+        const int i = p * RP + r;
+        acc += i < nv ? g[static_cast<size_t>(i) * row_stride + c] : 0.f;
+        gv[r] = acc;
+    }
+    sTot[p * K + c] = acc;
+    __syncthreads();
+    float off = 0.f;
+    for (int pp = 0; pp < p; ++pp) off += sTot[pp * K + c];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) sG[(p * RP + r) * LK + c] = (gv[r] + off) * kLog2e;
+}
+
+// ---------------------------------------------------------------- 1. prep
+// One workgroup per (b, hv, chunk of the slab).
+template <int K>
+__global__ __launch_bounds__(kThr) void cbwd_prep_kernel(SlabArgs s) {
+    using I = Img<K>;
+    constexpr int LK = I::LK, LC = I::LC, L16 = I::L16;
+    const ChunkBwdArgs &a = s.a;
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    float *img = sm;                        // [I::floats]
+    float *sPq = img + I::floats;           // [C][LK] q e1, k e1, k e2
+    float *sPk = sPq + kC * LK;
+    float *sRk = sPk + kC * LK;
+    float *sG = sRk + kC * LK;              // [C][LK]
+    float *sTot = sG + kC * LK;             // [kThr] partial column sums
+    float *sB = sTot + kThr;                // [C] beta
+    float *sAb = sB + kC;                   // [2][16][L16] diagonal blocks of A_kk
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int n = blockIdx.x % s.NCs;
+    const int bhv = blockIdx.x / s.NCs;
+    const int b = bhv / a.HV, hv = bhv % a.HV, h = hv / (a.HV / a.H);
+    const int t0 = s.t_begin + n * kC;
+    const int nv = min(kC, s.t_begin + s.len - t0);
+    const size_t tok = static_cast<size_t>(b) * a.T + t0;
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q);
+    const uint16_t *kg = static_cast<const uint16_t *>(a.k);
+
+    chunk_cumsum<K, kThr>(a.g + (tok * a.HV + hv) * K, nv, a.HV * K, sG, LK, sTot);
+    if (tid < kC) sB[tid] = tid < nv ? a.beta[(tok + tid) * a.HV + hv] : 0.f;
+    __syncthreads();
+
+    // element-wise operands: 8 columns of one row per thread (16-byte loads of q, k)
+    for (int u = tid; u < kC * K / 8; u += kThr) {
+        const int i = u / (K / 8), c0 = (u % (K / 8)) * 8;
+        uint4 wq = make_uint4(0u, 0u, 0u, 0u), wk = wq;
+        if (i < nv) {
+            const size_t qi = ((tok + i) * a.H + h) * K + c0;
+            wq = *reinterpret_cast<const uint4 *>(qg + qi);
+            wk = *reinterpret_cast<const uint4 *>(kg + qi);
+        }
+        const uint32_t q8[4] = {wq.x, wq.y, wq.z, wq.w}, k8[4] = {wk.x, wk.y, wk.z, wk.w};
+        const float bi = sB[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = c0 + e;
+            const float qv = __uint_as_float(e & 1 ? q8[e >> 1] & 0xffff0000u : q8[e >> 1] << 16);
+            const float kv = __uint_as_float(e & 1 ? k8[e >> 1] & 0xffff0000u : k8[e >> 1] << 16);
+            const float Gi = sG[i * LK + c], Gr = sG[kR * LK + c], Gl = sG[(kC - 1) * LK + c];
+            const float e1 = ex2(Gi - Gr), e2 = ex2(Gr - Gi), gam = ex2(Gi), lam = ex2(Gl - Gi);
+            sPq[i * LK + c] = qv * e1;
+            sPk[i * LK + c] = kv * e1;
+            sRk[i * LK + c] = kv * e2;
+            img[I::oKb + i * LK + c] = kv * lam;
+            img[I::oA1 + c * LC + i] = a.scale * qv * gam;
+            img[I::oA2 + c * LC + i] = -bi * kv * gam;
+            if (i == kC - 1) img[I::oGl + c] = ex2(Gl);
+        }
+    }
+    __syncthreads();
+
+    // A_qk (waves 0-2) and Pk Rk^T (waves 3-5), lower tiles (0,0), (1,0), (1,1)
+    if (wave < 6) {
+        const int t = wave % 3, rt = t == 0 ? 0 : 1, ct = t == 2 ? 1 : 0;
+        const float *X = wave < 3 ? sPq : sPk;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        tile_nt<K>(X + (rt * 16 + lr) * LK, sRk + (ct * 16 + lr) * LK, lg, acc);
+        if (wave < 3) {
+            // s A_qk^T: element (col, row) of A_qk, lower including the diagonal
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = rt * 16 + 4 * lg + j, col = ct * 16 + lr;
+                img[I::oAq + col * LC + row] = col <= row ? a.scale * acc[j] : 0.f;
+            }
+            if (wave == 0) {
+                // rows 16-31 of A_qk^T, columns 0-15: above A_qk's diagonal
+#pragma unroll
+                for (int j = 0; j < 4; ++j) img[I::oAq + (16 + lr) * LC + 4 * lg + j] = 0.f;
+            }
+        } else if (t != 1) {
+            // diagonal block of A_kk = diag(beta) SL(Pk Rk^T)
+            const int blk = rt;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 4 * lg + j;
+                sAb[blk * 16 * L16 + i * L16 + lr] = lr < i ? sB[16 * blk + i] * acc[j] : 0.f;
+            }
+        } else {
+            // -A21^T: element (m, j) = -beta_{16+j} (Pk Rk^T)[16 + j][m]
+#pragma unroll
+            for (int j = 0; j < 4; ++j) img[I::oNA + lr * L16 + 4 * lg + j] = -sB[16 + 4 * lg + j] * acc[j];
+        }
+    }
+    __syncthreads();
+    // T_blk = (I + A_blk)^-1 by rows: row i solves x^T (I + A_blk) = e_i^T,
+    // swept k = 15 .. 1 (x_k final, removed from every earlier column; the
+    // strictly lower A_blk makes the update uniform).  Lane = (row i, quarter
+    // q) holds x_{4q..4q+3}.  Stored transposed: T^T[m][i] = x_m.
+    if (wave < 2) {
+        const int blk = wave;
+        const float *A = sAb + blk * 16 * L16;
+        const int i = lane >> 2, q = lane & 3;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (4 * q + e == i) ? 1.f : 0.f;
+#pragma unroll
+        for (int k = 15; k >= 1; --k) {
+            const f32x4 av = ld4(A + k * L16 + 4 * q);
+            const float xk = quad_bcast(x[k % 4], k / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] -= av[e] * xk;
+        }
+        float *TT = img + (blk == 0 ? I::oT1 : I::oT2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) TT[(4 * q + e) * L16 + i] = x[e];
+    }
+    __syncthreads();
+    // the image to HBM, 16 bytes per thread
+    float4 *dst = reinterpret_cast<float4 *>(a.img + ((static_cast<size_t>(b) * s.NCs + n) * a.HV + hv) * I::floats);
+    const float4 *src = reinterpret_cast<const float4 *>(img);
+    for (int u = tid; u < I::floats / 4; u += kThr) dst[u] = src[u];
+}
+
+// ---------------------------------------------------------------- 2. chain
+// One workgroup per (b, hv, V tile of VT columns); chunks of the slab in
+// reverse.  Waves 0 .. NCW-1 hold dM (NG blocks of 16 columns each, all K rows,
+// in MFMA accumulators); waves 4-7 bring the next chunk's operand image and dO
+// tile into the other LDS buffer.
+template <int K, int VT>
+__global__ __launch_bounds__(kThr, 1) void cbwd_chain_kernel(SlabArgs s) {
+    using I = Img<K>;
+    constexpr int LK = I::LK, LC = I::LC, L16 = I::L16;
+    constexpr int KT = K / 16;
+    constexpr int NCW = VT / 16 < 4 ? VT / 16 : 4;
+    constexpr int NG = VT / (16 * NCW);
+    constexpr int LDO = VT + 8;                                  // bf16 pitch of the dO tile
+    constexpr int BUF = I::floats + (kC * LDO * 2 + 15) / 16 * 4;   // floats per buffer
+    const ChunkBwdArgs &a = s.a;
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int nvt = a.V / VT;
+    const int vt = blockIdx.x % nvt, bhv = blockIdx.x / nvt;
+    const int b = bhv / a.HV, hv = bhv % a.HV;
+    const int v0 = vt * VT;
+    const int HV = a.HV, V = a.V;
+    const bool carry = wave < NCW;
+    const uint16_t *dog = static_cast<const uint16_t *>(a.dout);
+
+    // operand image and dO tile of chunk n into buffer n & 1 (waves 4-7)
+    auto load = [&](int n) {
+        const int hl = tid - 256;
+        float *buf = sm + (n & 1) * BUF;
+        const float4 *src = reinterpret_cast<const float4 *>(a.img + ((static_cast<size_t>(b) * s.NCs + n) * HV + hv) * I::floats);
+        float4 *dst = reinterpret_cast<float4 *>(buf);
+        // every load in flight before the first LDS store: one round trip
+        constexpr int NJ = I::floats / 1024;
+        constexpr int UPR = VT / 8, NUO = kC * UPR, NJO = (NUO + 255) / 256;   // dO: 8 bf16 per unit
+        const int t0 = s.t_begin + n * kC;
+        const int nv = min(kC, s.t_begin + s.len - t0);
+        float4 t[NJ];
+        uint4 w[NJO];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) t[j] = src[hl + 256 * j];
+#pragma unroll
+        for (int j = 0; j < NJO; ++j) {
+            const int u = hl + 256 * j, row = u / UPR, c8 = (u % UPR) * 8;
+            w[j] = make_uint4(0u, 0u, 0u, 0u);
+            if (u < NUO && row < nv)
+                w[j] = *reinterpret_cast<const uint4 *>(dog + ((static_cast<size_t>(b) * a.T + t0 + row) * HV + hv) * V + v0 + c8);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) dst[hl + 256 * j] = t[j];
+        __bf16 *sdo = reinterpret_cast<__bf16 *>(buf + I::floats);
+#pragma unroll
+        for (int j = 0; j < NJO; ++j) {
+            const int u = hl + 256 * j, row = u / UPR, c8 = (u % UPR) * 8;
+            if (u < NUO) *reinterpret_cast<uint4 *>(sdo + row * LDO + c8) = w[j];
+        }
+    };
+
+    f32x4 dm[NG][KT];
+    if (carry) {
+        const float *src = s.dm_in ? s.dm_in + (static_cast<size_t>(b) * HV + hv) * K * V : nullptr;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            const int col = v0 + 16 * (wave * NG + gi) + lr;
+#pragma unroll
+            for (int kb = 0; kb < KT; ++kb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dm[gi][kb][j] = src ? src[static_cast<size_t>(kb * 16 + 4 * lg + j) * V + col] : 0.f;
+        }
+    }
+    if (wave >= 4) load(s.NCs - 1);
+    __syncthreads();
+
+    for (int n = s.NCs - 1; n >= 0; --n) {
+        if (wave >= 4 && n > 0) load(n - 1);
+        if (carry) {
+            const float *img = sm + (n & 1) * BUF;
+            const __bf16 *sdo = reinterpret_cast<const __bf16 *>(img + I::floats);
+            const int t0 = s.t_begin + n * kC;
+            const int nv = min(kC, s.t_begin + s.len - t0);
+            // dM' (the gradient at the end of chunk n) for the gradient kernel
+            float *dms = a.dMs + ((static_cast<size_t>(b) * s.NCs + n) * HV + hv) * K * V;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const int col = v0 + 16 * (wave * NG + gi) + lr;
+#pragma unroll
+                for (int kb = 0; kb < KT; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) dms[static_cast<size_t>(kb * 16 + 4 * lg + j) * V + col] = dm[gi][kb][j];
+            }
+            // dO fragments: rows 16 b2 + 4 lg + j of the block's column lr
+            f32x4 dof[NG][2];
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int b2 = 0; b2 < 2; ++b2) {
+                    const int row = b2 * 16 + 4 * (lane >> 4) + ((lane >> 2) & 3);
+                    const int col = 16 * (wave * NG + gi) + 4 * (lane & 3);
+                    const bf16x4 f = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (__attribute__((address_space(3))) bf16x4 *)(sdo + row * LDO + col));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) dof[gi][b2][j] = static_cast<float>(f[j]);
+                }
+            // dU = (k Lambda') dM' + s A_qk^T dO
+            f32x4 du[NG][2];
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) du[gi][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KT; ++kb) {
+                f32x4 kk[2];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) kk[rt] = ld4(img + I::oKb + (rt * 16 + lr) * LK + kb * 16 + 4 * lg);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                        for (int gi = 0; gi < NG; ++gi) du[gi][rt] = mma4(kk[rt][j], dm[gi][kb][j], du[gi][rt]);
+            }
+#pragma unroll
+            for (int b2 = 0; b2 < 2; ++b2) {
+                f32x4 aq[2];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) aq[rt] = ld4(img + I::oAq + (rt * 16 + lr) * LC + b2 * 16 + 4 * lg);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                        for (int gi = 0; gi < NG; ++gi) du[gi][rt] = mma4(aq[rt][j], dof[gi][b2][j], du[gi][rt]);
+            }
+            // dR2 = T22^T dU2;  Y = dU1 - A21^T dR2;  dR1 = T11^T Y
+            const f32x4 t1 = ld4(img + I::oT1 + lr * L16 + 4 * lg);
+            const f32x4 t2 = ld4(img + I::oT2 + lr * L16 + 4 * lg);
+            const f32x4 na = ld4(img + I::oNA + lr * L16 + 4 * lg);
+            f32x4 dr[NG][2];
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x = mma4(t2[j], du[gi][1][j], x);
+                dr[gi][1] = x;
+                f32x4 y = du[gi][0];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) y = mma4(na[j], x[j], y);
+                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) z = mma4(t1[j], y[j], z);
+                dr[gi][0] = z;
+            }
+            // dR (rows of the chunk inside the sequence) for the gradient kernel
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const int col = v0 + 16 * (wave * NG + gi) + lr;
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int row = rt * 16 + 4 * lg + j;
+                        if (row < nv)
+                            a.dR[((static_cast<size_t>(b) * a.Ls + n * kC + row) * HV + hv) * V + col] = dr[gi][rt][j];
+                    }
+            }
+            // dM = Gamma_last (.) dM' + s (q Gamma)^T dO - (beta k Gamma)^T dR
+#pragma unroll
+            for (int kb = 0; kb < KT; ++kb) {
+                const f32x4 gl = ld4(img + I::oGl + kb * 16 + 4 * lg);
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) dm[gi][kb] *= gl;
+#pragma unroll
+                for (int b2 = 0; b2 < 2; ++b2) {
+                    const f32x4 a1 = ld4(img + I::oA1 + (kb * 16 + lr) * LC + b2 * 16 + 4 * lg);
+                    const f32x4 a2 = ld4(img + I::oA2 + (kb * 16 + lr) * LC + b2 * 16 + 4 * lg);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int gi = 0; gi < NG; ++gi) {
+                            dm[gi][kb] = mma4(a1[j], dof[gi][b2][j], dm[gi][kb]);
+                            dm[gi][kb] = mma4(a2[j], dr[gi][b2][j], dm[gi][kb]);
+                        }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (carry && s.dm_out) {
+        float *dst = s.dm_out + (static_cast<size_t>(b) * HV + hv) * K * V;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            const int col = v0 + 16 * (wave * NG + gi) + lr;
+#pragma unroll
+            for (int kb = 0; kb < KT; ++kb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[static_cast<size_t>(kb * 16 + 4 * lg + j) * V + col] = dm[gi][kb][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- 3. grad
+// One workgroup per (b, q/k head h, chunk of the slab); the value heads of h
+// one after another, dq and dk summed over them in registers.
+template <int K, int V>
+__global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
+    constexpr int LK = K + 4, LC = kC + 4;
+    constexpr int KT = K / 16;
+    constexpr int NT = 2 * KT;              // 16x16 tiles of a [C][K] result
+    constexpr int TPW = (NT + 7) / 8;       // tiles per wave
+    const ChunkBwdArgs &a = s.a;
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    float *sQ = sm;                         // [C][LK] q, k of the chunk (fp32)
+    float *sK = sQ + kC * LK;
+    float *sG = sK + kC * LK;               // [C][LK] base-2 cumulative sums
+    float *sPqT = sG + kC * LK;             // [K][LC] (q e1)^T, (k e1)^T, (k e2)^T
+    float *sPkT = sPqT + K * LC;
+    float *sRkT = sPkT + K * LC;
+    float *sDq = sRkT + K * LC;             // [C][LC] dA_qk, dA_qk^T, dA_kk, (beta dA_kk)^T
+    float *sDqT = sDq + kC * LC;
+    float *sDk = sDqT + kC * LC;
+    float *sDkbT = sDk + kC * LC;
+    float *sTot = sDkbT + kC * LC;          // [kThrG] partial column sums
+    float *sB = sTot + kThrG;               // [C] beta
+    float *sDb = sB + kC;                   // [4][C] partial dbeta
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int n = blockIdx.x % s.NCs;
+    const int bh = blockIdx.x / s.NCs;
+    const int b = bh / a.H, h = bh % a.H;
+    const int G = a.HV / a.H;
+    const int HV = a.HV;
+    const int t0 = s.t_begin + n * kC;
+    const int nv = min(kC, s.t_begin + s.len - t0);
+    const size_t tok = static_cast<size_t>(b) * a.T + t0;
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q);
+    const uint16_t *kg = static_cast<const uint16_t *>(a.k);
+    const uint16_t *dog = static_cast<const uint16_t *>(a.dout);
+    const float scale = a.scale;
+
+    // q, k of the chunk: 8 bf16 (16 bytes) per thread and row piece
+    for (int u = tid; u < kC * K / 8; u += kThrG) {
+        const int i = u / (K / 8), c = (u % (K / 8)) * 8;
+        uint4 wq = make_uint4(0u, 0u, 0u, 0u), wk = wq;
+        if (i < nv) {
+            const size_t qi = ((tok + i) * a.H + h) * K + c;
+            wq = *reinterpret_cast<const uint4 *>(qg + qi);
+            wk = *reinterpret_cast<const uint4 *>(kg + qi);
+        }
+        const uint32_t q8[4] = {wq.x, wq.y, wq.z, wq.w}, k8[4] = {wk.x, wk.y, wk.z, wk.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sQ[i * LK + c + 2 * e] = __uint_as_float(q8[e] << 16);
+            sQ[i * LK + c + 2 * e + 1] = __uint_as_float(q8[e] & 0xffff0000u);
+            sK[i * LK + c + 2 * e] = __uint_as_float(k8[e] << 16);
+            sK[i * LK + c + 2 * e + 1] = __uint_as_float(k8[e] & 0xffff0000u);
+        }
+    }
+
+    f32x4 dqa[TPW], dka[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) dqa[u] = dka[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int gv = 0; gv < G; ++gv) {
+        const int hv = h * G + gv;
+        __syncthreads();   // the previous head's LDS reads are done
+        chunk_cumsum<K, kThrG>(a.g + (tok * HV + hv) * K, nv, HV * K, sG, LK, sTot);
+        if (tid < kC) sB[tid] = tid < nv ? a.beta[(tok + tid) * HV + hv] : 0.f;
+        __syncthreads();
+        for (int e = tid; e < kC * K; e += kThrG) {
+            const int c = e / kC, i = e % kC;   // consecutive threads: consecutive rows of one column
+            const float Gi = sG[i * LK + c], Gr = sG[kR * LK + c];
+            const float e1 = ex2(Gi - Gr), e2 = ex2(Gr - Gi);
+            sPqT[c * LC + i] = sQ[i * LK + c] * e1;
+            sPkT[c * LC + i] = sK[i * LK + c] * e1;
+            sRkT[c * LC + i] = sK[i * LK + c] * e2;
+        }
+        __syncthreads();
+
+        // slab-local rows of this chunk in the [B, Ls, HV, V] arrays
+        const size_t lrow0 = static_cast<size_t>(b) * a.Ls + n * kC;
+        const float *Ug = a.U + (lrow0 * HV + hv) * V;
+        const float *Wg = a.W + (lrow0 * HV + hv) * V;
+        const float *dRg = a.dR + (lrow0 * HV + hv) * V;
+        const uint16_t *dOg = dog + (tok * HV + hv) * V;
+        const size_t rs = static_cast<size_t>(HV) * V;   // row stride of those arrays
+        // A operand of an [C x C] or [C x K] product from a row of dO (bf16,
+        // rows past the end read as 0)
+        auto dO4 = [&](int row, int col) -> f32x4 {
+            if (row >= nv) return f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint2 w = *reinterpret_cast<const uint2 *>(dOg + row * rs + col);
+            return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                         __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+        };
+        auto row4 = [&](const float *base, int row, int col) -> f32x4 {
+            if (row >= nv) return f32x4{0.f, 0.f, 0.f, 0.f};
+            return ld4(base + row * rs + col);
+        };
+
+        if (wave < 6) {
+            // dA_qk = s L(dO U^T) (waves 0-2), dA_kk = -SL(dR U^T) and the
+            // dbeta term with SL(Pk Rk^T) (waves 3-5); lower tiles (0,0), (1,0), (1,1)
+            const int t = wave % 3, rt = t == 0 ? 0 : 1, ct = t == 2 ? 1 : 0;
+            const int xr = rt * 16 + lr, yr = ct * 16 + lr;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            // the loads of four steps first, then their products
+            constexpr int SA = V / 16 > 4 ? 4 : V / 16;
+#pragma unroll
+            for (int s0 = 0; s0 < V / 16; s0 += SA) {
+                f32x4 xa[SA], yb[SA];
+#pragma unroll
+                for (int st = 0; st < SA; ++st) {
+                    const int c = (s0 + st) * 16 + 4 * lg;
+                    xa[st] = wave < 3 ? dO4(xr, c) : row4(dRg, xr, c);
+                    yb[st] = row4(Ug, yr, c);
+                }
+#pragma unroll
+                for (int st = 0; st < SA; ++st)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc = mma4(xa[st][j], yb[st][j], acc);
+            }
+            if (wave < 3) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = rt * 16 + 4 * lg + j, col = ct * 16 + lr;
+                    const float x = col <= row ? scale * acc[j] : 0.f;
+                    sDq[row * LC + col] = x;
+                    sDqT[col * LC + row] = x;
+                }
+                if (wave == 0) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        sDq[(4 * lg + j) * LC + 16 + lr] = 0.f;
+                        sDqT[(16 + lr) * LC + 4 * lg + j] = 0.f;
+                    }
+                }
+            } else {
+                // Pk Rk^T of the tile, from the transposed operands
+                f32x4 ar = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+                for (int k0 = 0; k0 < K; k0 += 16)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int kk = k0 + 4 * lg + j;
+                        ar = mma4(sPkT[kk * LC + xr], sRkT[kk * LC + yr], ar);
+                    }
+                float part[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = rt * 16 + 4 * lg + j, col = ct * 16 + lr;
+                    const float x = col < row ? -acc[j] : 0.f;
+                    sDk[row * LC + col] = x;
+                    sDkbT[col * LC + row] = sB[row] * x;
+                    part[j] = x * ar[j];
+                }
+                if (wave == 3) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        sDk[(4 * lg + j) * LC + 16 + lr] = 0.f;
+                        sDkbT[(16 + lr) * LC + 4 * lg + j] = 0.f;
+                    }
+                }
+                // row sums over the tile's 16 columns (one DPP row of lanes)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) part[j] = group_sum<16>(part[j]);
+                if (lr == 0) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sDb[(t == 2 ? 1 : 0) * kC + rt * 16 + 4 * lg + j] = part[j];
+                }
+            }
+        } else if (wave < 8) {
+            // waves 6-7: dv = beta dR, and rowsum(dR (.) W); lane = (row, quarter of V)
+            const int l = tid - 384, row = l >> 2, qv = l & 3;
+            float dot = 0.f;
+            if (row < nv) {
+                uint16_t *dvg = static_cast<uint16_t *>(a.dv) + ((tok + row) * HV + hv) * V;
+                const float bt = sB[row];
+                constexpr int SD = V / 16 > 4 ? 4 : V / 16;
+#pragma unroll
+                for (int s0 = 0; s0 < V / 16; s0 += SD) {
+                f32x4 dd[SD], ww[SD];
+#pragma unroll
+                for (int st = 0; st < SD; ++st) {
+                    dd[st] = ld4(dRg + row * rs + (s0 + st) * 16 + qv * 4);
+                    ww[st] = ld4(Wg + row * rs + (s0 + st) * 16 + qv * 4);
+                }
+#pragma unroll
+                for (int st = 0; st < SD; ++st) {
+                    const int c = (s0 + st) * 16 + qv * 4;
+                    const f32x4 d = dd[st], w = ww[st];
+                    dot += d[0] * w[0] + d[1] * w[1] + d[2] * w[2] + d[3] * w[3];
+                    uint2 o;
+                    o.x = static_cast<uint32_t>(float_to_bf16_bits(bt * d[0])) | (static_cast<uint32_t>(float_to_bf16_bits(bt * d[1])) << 16);
+                    o.y = static_cast<uint32_t>(float_to_bf16_bits(bt * d[2])) | (static_cast<uint32_t>(float_to_bf16_bits(bt * d[3])) << 16);
+                    *reinterpret_cast<uint2 *>(dvg + c) = o;
+                }
+                }
+            }
+            dot += lanes::dpp<0xb1>(dot);
+            dot += lanes::dpp<0x4e>(dot);
+            if (qv == 0) sDb[2 * kC + row] = dot;
+        }
+        __syncthreads();
+        if (tid < nv) {
+            // rows 0-15 have one A_kk tile term, rows 16-31 two
+            const float dA = sDb[tid] + (tid >= 16 ? sDb[kC + tid] : 0.f);
+            a.dbeta[(tok + tid) * HV + hv] = sDb[2 * kC + tid] + dA;
+        }
+
+        // [C x K] results, tile (rt, ct) per wave
+        const float *Mn = n == 0 ? (s.Sstart ? s.Sstart + b * s.s_bstride + static_cast<size_t>(hv) * K * V : nullptr)
+                                 : a.snapc + ((static_cast<size_t>(b) * (s.NCs - 1) + n - 1) * HV + hv) * K * V;
+        const float *dMn = a.dMs + ((static_cast<size_t>(b) * s.NCs + n) * HV + hv) * K * V;
+        float *eg = a.e + ((static_cast<size_t>(b) * a.Ls + n * kC) * HV + hv) * K;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int tile = wave + 8 * u;
+            if (tile < NT) {
+                const int rt = tile / KT, ct = tile % KT;
+                const int xr = rt * 16 + lr, yr = ct * 16 + lr;
+                f32x4 x1 = {0.f, 0.f, 0.f, 0.f}, x2 = x1, x3 = x1, y1 = x1, y2 = x1, y3 = x1;
+                // dO M^T and dR M^T over V (every step's loads first), then U dM'^T
+                constexpr int SB = V / 16 > 4 ? 4 : V / 16;   // steps per batch of loads
+#pragma unroll
+                for (int s0 = 0; s0 < V / 16; s0 += SB) {
+                    f32x4 o4[SB], r4[SB], m4[SB];
+#pragma unroll
+                    for (int st = 0; st < SB; ++st) {
+                        const int c = (s0 + st) * 16 + 4 * lg;
+                        o4[st] = dO4(xr, c);
+                        r4[st] = row4(dRg, xr, c);
+                        m4[st] = Mn ? ld4(Mn + static_cast<size_t>(yr) * V + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+#pragma unroll
+                    for (int st = 0; st < SB; ++st)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            x1 = mma4(o4[st][j], m4[st][j], x1);
+                            x2 = mma4(r4[st][j], m4[st][j], x2);
+                        }
+                }
+#pragma unroll
+                for (int s0 = 0; s0 < V / 16; s0 += SB) {
+                    f32x4 u4[SB], dm4[SB];
+#pragma unroll
+                    for (int st = 0; st < SB; ++st) {
+                        const int c = (s0 + st) * 16 + 4 * lg;
+                        u4[st] = row4(Ug, xr, c);
+                        dm4[st] = ld4(dMn + static_cast<size_t>(yr) * V + c);
+                    }
+#pragma unroll
+                    for (int st = 0; st < SB; ++st)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) x3 = mma4(u4[st][j], dm4[st][j], x3);
+                }
+                // dA_qk Rk, dA_kk Rk, dA_qk^T Pq + (beta dA_kk)^T Pk over the chunk's rows
+                tile_nt<kC>(sDq + xr * LC, sRkT + yr * LC, lg, y1);
+                tile_nt<kC>(sDk + xr * LC, sRkT + yr * LC, lg, y2);
+                tile_nt<kC>(sDqT + xr * LC, sPqT + yr * LC, lg, y3);
+                tile_nt<kC>(sDkbT + xr * LC, sPkT + yr * LC, lg, y3);
+                const int c = ct * 16 + lr;
+                const float Gr = sG[kR * LK + c], Gl = sG[(kC - 1) * LK + c];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = rt * 16 + 4 * lg + j;
+                    const float Gi = sG[i * LK + c];
+                    const float gam = ex2(Gi), e1 = ex2(Gi - Gr), e2 = ex2(Gr - Gi), lam = ex2(Gl - Gi);
+                    const float bt = sB[i];
+                    const float dq = scale * gam * x1[j] + e1 * y1[j];
+                    const float dkr = bt * (e1 * y2[j] - gam * x2[j]);
+                    const float dkw = lam * x3[j] + e2 * y3[j];
+                    const float q = sQ[i * LK + c], k = sK[i * LK + c];
+                    if (i < nv) eg[static_cast<size_t>(i) * HV * K + c] = q * dq + k * (dkr - dkw);
+                    dqa[u][j] += dq;
+                    dka[u][j] += dkr + dkw;
+                }
+            }
+        }
+    }
+    // dq, dk (bf16) of the chunk's rows inside the sequence
+    uint16_t *dqg = static_cast<uint16_t *>(a.dq), *dkg = static_cast<uint16_t *>(a.dk);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int tile = wave + 8 * u;
+        if (tile < NT) {
+            const int rt = tile / KT, ct = tile % KT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = rt * 16 + 4 * lg + j;
+                if (i < nv) {
+                    const size_t o = ((tok + i) * a.H + h) * K + ct * 16 + lr;
+                    dqg[o] = float_to_bf16_bits(dqa[u][j]);
+                    dkg[o] = float_to_bf16_bits(dka[u][j]);
+                }
+            }
+        }
+    }
+}
+
+template <int K>
+constexpr int prep_lds() { return (Img<K>::floats + 4 * kC * (K + 4) + kThr + kC + 2 * 16 * 20) * 4; }
+template <int K, int VT>
+constexpr int chain_lds() { return 2 * (Img<K>::floats + (kC * (VT + 8) * 2 + 15) / 16 * 4) * 4; }
+template <int K>
+constexpr int grad_lds() { return (3 * kC * (K + 4) + 3 * K * (kC + 4) + 4 * kC * (kC + 4) + kThrG + kC + 4 * kC) * 4; }
+
+template <typename F>
+hipError_t launch_dyn(F kern, unsigned grid, int lds, hipStream_t stream, const SlabArgs &s, int threads = kThr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, stream, s);
+    return hipGetLastError();
+}
+
+template <int K, int V>
+hipError_t launch_slab_kernels(const SlabArgs &s, hipStream_t stream) {
+    static_assert(prep_lds<K>() <= 160 * 1024 && grad_lds<K>() <= 160 * 1024, "LDS plan exceeds 160 KB");
+    const ChunkBwdArgs &a = s.a;
+    hipError_t e = launch_dyn(cbwd_prep_kernel<K>, static_cast<unsigned>(a.B) * a.HV * s.NCs, prep_lds<K>(), stream, s);
+    if (e != hipSuccess) return e;
+    // V over two workgroups when there are few (b, hv) chains, as in the forward
+    const bool split = V >= 64 && static_cast<long>(a.B) * a.HV < 160;
+    constexpr int VS = V >= 64 ? V / 2 : V;
+    static_assert(chain_lds<K, V>() <= 160 * 1024 && chain_lds<K, VS>() <= 160 * 1024, "LDS plan exceeds 160 KB");
+    if (split)
+        e = launch_dyn(cbwd_chain_kernel<K, VS>, static_cast<unsigned>(a.B) * a.HV * (V / VS), chain_lds<K, VS>(), stream, s);
+    else
+        e = launch_dyn(cbwd_chain_kernel<K, V>, static_cast<unsigned>(a.B) * a.HV, chain_lds<K, V>(), stream, s);
+    if (e != hipSuccess) return e;
+    return launch_dyn(cbwd_grad_kernel<K, V>, static_cast<unsigned>(a.B) * a.H * s.NCs, grad_lds<K>(), stream, s,
+                      kThrG);
+}
+
+template <int K>
+hipError_t launch_slab_k(const SlabArgs &s, hipStream_t stream) {
+    switch (s.a.V) {
+    case 32: return launch_slab_kernels<K, 32>(s, stream);
+    case 64: return launch_slab_kernels<K, 64>(s, stream);
+    case 128: return launch_slab_kernels<K, 128>(s, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int chunk_bwd_image_floats(int K) {
+    return K == 32 ? Img<32>::floats : K == 64 ? Img<64>::floats : K == 128 ? Img<128>::floats : 0;
+}
+
+hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
+    if (a.B == 0) return hipSuccess;
+    const size_t sKV = static_cast<size_t>(a.HV) * a.K * a.V;
+    if (a.T == 0) {
+        // only dS0 = dL/dS_T (or zeros)
+        if (!a.dS0) return hipSuccess;
+        const size_t bytes = static_cast<size_t>(a.B) * sKV * 4;
+        return a.dST ? hipMemcpyAsync(a.dS0, a.dST, bytes, hipMemcpyDeviceToDevice, stream)
+                     : hipMemsetAsync(a.dS0, 0, bytes, stream);
+    }
+    const int ns = (a.T + a.Ls - 1) / a.Ls;
+    // 0. the whole sequence once: S_T and the states at the slab starts
+    {
+        PrefillArgs f{};
+        f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta; f.S0 = a.S0;
+        f.ST = a.ST;
+        f.snap = ns > 1 ? a.snap1 : nullptr;
+        f.snap_chunks = a.Ls / kC; f.NS = ns - 1;
+        f.B = a.B; f.T = a.T; f.H = a.H; f.HV = a.HV; f.K = a.K; f.V = a.V;
+        f.scale = a.scale; f.bf16 = true; f.bwd = true;
+        const hipError_t e = launch_prefill_bf16(f, stream);
+        if (e != hipSuccess) return e;
+    }
+    float *gc[2] = {a.gc, a.gc + static_cast<size_t>(a.B) * a.HV * a.K};
+    for (int si = ns - 1, j = 0; si >= 0; --si, ++j) {
+        SlabArgs s{};
+        s.a = a;
+        s.t_begin = si * a.Ls;
+        s.len = min(a.T, s.t_begin + a.Ls) - s.t_begin;
+        s.NCs = (s.len + kC - 1) / kC;
+        if (si == 0) {
+            s.Sstart = a.S0;
+            s.s_bstride = static_cast<long long>(sKV);
+        } else {
+            s.Sstart = a.snap1 + static_cast<size_t>(si - 1) * sKV;
+            s.s_bstride = static_cast<long long>(a.NS1) * sKV;
+        }
+        s.dm_in = si == ns - 1 ? a.dST : a.Dc;
+        s.dm_out = si == 0 ? a.dS0 : a.Dc;
+        // the slab's forward pass: states at its chunk starts, W and U
+        PrefillArgs f{};
+        f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
+        f.S0 = s.Sstart; f.s0_bstride = s.s_bstride;
+        f.snap = s.NCs > 1 ? a.snapc : nullptr;
+        f.snap_chunks = 1; f.NS = s.NCs - 1;
+        f.w_out = a.W; f.u_out = a.U; f.Lw = a.Ls;
+        f.t_off = s.t_begin; f.Tseq = a.T;
+        f.B = a.B; f.T = s.len; f.H = a.H; f.HV = a.HV; f.K = a.K; f.V = a.V;
+        f.scale = a.scale; f.bf16 = true; f.bwd = true;
+        hipError_t e = launch_prefill_bf16(f, stream);
+        if (e != hipSuccess) return e;
+        e = a.K == 32 ? launch_slab_k<32>(s, stream)
+          : a.K == 64 ? launch_slab_k<64>(s, stream)
+          : a.K == 128 ? launch_slab_k<128>(s, stream) : hipErrorInvalidValue;
+        if (e != hipSuccess) return e;
+        // dg over the slab, carried to the slab before
+        BwdArgs d{};
+        d.t_begin = s.t_begin; d.t_end = s.t_begin + s.len;
+        d.e = a.e; d.bs = a.bs; d.NB = a.NB; d.Ls = a.Ls;
+        d.gc_in = gc[j & 1]; d.gc_out = gc[(j + 1) & 1];
+        d.ST = a.ST; d.dST = a.dST; d.dg = a.dg;
+        d.B = a.B; d.T = a.T; d.H = a.H; d.HV = a.HV; d.K = a.K; d.V = a.V;
+        e = launch_dg_slab(d, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace kda

@@ -35,6 +35,18 @@ struct PrefillArgs {
     // per row of V values, o rounded to the output dtype first.
     const void *ogate;              // [B,T,HV,V] (dtype) or nullptr
     float og_eps;
+    // Sub-range of the sequences (bf16 chunk kernel): the call processes
+    // tokens [t_off, t_off + T) of sequences Tseq tokens long in memory
+    // (Tseq = 0 means T, t_off = 0: the whole sequence).
+    int t_off, Tseq;
+    // Chunked backward's forward pass (bf16 chunk kernel, with snap): when
+    // w_out is set, W = v - (k Gamma) M and U = (I + A_kk)^-1 diag(beta) W of
+    // every chunk go to w_out and u_out ([B, Lw, HV, V] fp32, token index
+    // relative to t_off) and no o is written.
+    float *w_out, *u_out;
+    int Lw;
+    bool bwd;                   // the backward's forward pass: no o; W, U where set
+    long long s0_bstride;       // elements between the sequences of S0 (0: HV K V)
 };
 
 // Arguments of one decode step.
@@ -120,6 +132,32 @@ struct BwdArgs {
     float scale;
     bool bf16;
 };
+// Arguments of the chunked backward (kda_chunk_bwd, bf16 inputs, bounded gate).
+struct ChunkBwdArgs {
+    const void *q, *k, *v;      // [B,T,H,K], [B,T,H,K], [B,T,HV,V] bf16
+    const float *g, *beta;      // [B,T,HV,K], [B,T,HV]
+    const float *S0;            // [B,HV,K,V] or nullptr
+    const void *dout;           // [B,T,HV,V] bf16
+    const float *dST;           // [B,HV,K,V] or nullptr
+    void *dq, *dk, *dv;         // [B,T,H,K], [B,T,H,K], [B,T,HV,V] bf16
+    float *dg, *dbeta;          // [B,T,HV,K], [B,T,HV]
+    float *dS0;                 // [B,HV,K,V] or nullptr
+    // workspace (fp32): see chunk_bwd_layout in kda_api.hip
+    float *ST, *snap1, *Dc, *snapc, *W, *U, *img, *dR, *dMs, *e, *bs, *gc;
+    int Ls;                     // tokens per slab (a multiple of 32)
+    int NS1;                    // slab starts kept by the first forward pass (slabs - 1)
+    int NB;                     // dg blocks per slab
+    int B, T, H, HV, K, V;
+    float scale;
+};
+hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream);
+// floats of one chunk's operand image (the chunked backward's pre-pass output)
+int chunk_bwd_image_floats(int K);
+// the dg reverse sum of one slab of the token-recurrent backward, shared with
+// the chunked backward (BwdArgs fields t_begin, t_end, e, bs, NB, Ls, gc_in,
+// gc_out, ST, dST, dg, B, T, HV, K, V)
+hipError_t launch_dg_slab(const BwdArgs &a, hipStream_t stream);
+
 constexpr int kBwdCols = 32;    // state columns per workgroup of the backward passes
 constexpr int kDgBlock = 64;    // tokens per block of the reverse sum that forms dg
 constexpr int kBwdSlab = 1024;  // tokens per slab of the backward passes (a multiple of kDgBlock)

@@ -246,9 +246,10 @@ struct Plan {
 
 // SNAP: the variant that also writes prefix snapshots of the state (a
 // separate instantiation, so that the plain path carries none of its code).
-template <int K, int VT, bool SNAP, bool GATED, bool OG>
+template <int K, int VT, bool SNAP, bool GATED, bool OG, bool BWD>
 __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     static_assert(!OG || !SNAP, "the output gate is built for the plain prefill only");
+    static_assert(!BWD || (SNAP && !GATED && !OG), "the backward's forward pass is a snapshot variant");
     using L = Plan<K>;
     static_assert(L::bytes + L::stage_bytes(VT) <= 160 * 1024, "LDS plan exceeds 160 KB");
     constexpr int LDO = VT + 8;   // bf16 rows of the o staging tile
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     // chunk past the end has an empty resource.  Prefetches are therefore issued
     // unconditionally, which keeps their registers out of loop-carried copies
     // that would wait for the loads.
-    const size_t tok_b = static_cast<size_t>(b) * T;
+    const size_t tok_b = static_cast<size_t>(b) * (a.Tseq ? a.Tseq : T) + a.t_off;
     const int g_stride = HV * K;             // elements per token
     const int qk_stride = a.H * K;
     const int v_stride = HV * V;
@@ -679,6 +680,24 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             (__attribute__((address_space(3))) bf16x4 *)(sV + row * LDO + col));
     };
 
+    // BWD: one 16-row tile of a chunk's [C][VT] fp32 result (accumulator
+    // layout, this carry wave's column block gi) to dst [B, Lw, HV, V], rows
+    // past the end dropped by the resource; nothing when dst is null
+    auto storeTile = [&](float *dst, int n, int rt, int gi, const f32x4 &x) {
+        if (!dst) return;
+        const int lane = opaque_tid() & 63, lr = lane & 15, lg = lane >> 4;
+        const int t0 = n * kC;
+        const auto rs = make_rsrc(dst + ((static_cast<size_t>(b) * a.Lw + t0) * HV + hv) * V + v0,
+                                  rows_bytes(t0, v_stride, VT, 4));
+        const int col = 16 * (wave * NG + gi) + lr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float xr = x[r];
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xr), rs,
+                                                  ((rt * 16 + lg * 4 + r) * v_stride + col) * 4, 0, 0);
+        }
+    };
+
     f32x4 m[NG][KT];
     f32x4 pq[NG][2], xq[NG][2];
     bf16x8 ubh[NG], ubl[NG];       // U of the chunk between its solve (P1) and the state update (P2)
@@ -773,6 +792,17 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                     rr[gi][rt][r] = bt[r] * (fl(vf[gi][rt][r]) - xq[gi][rt][r]);
                 }
         }
+        if constexpr (BWD) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    f32x4 w;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) w[r] = fl(vf[gi][rt][r]) - xq[gi][rt][r];
+                    storeTile(a.w_out, n, rt, gi, w);
+                }
+        }
         // U1 = T11 R1;  Y = R2 - A21 U1;  U2 = T22 Y   (16x16x16 MFMAs, 3 terms each)
         bf16x4 uh0[NG], ul0[NG], uh1[NG], ul1[NG];
         f32x4 acc[NG], acc2[NG];
@@ -787,6 +817,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             split4(acc[gi] + acc2[gi], uh0[gi], ul0[gi]);
+            if constexpr (BWD) storeTile(a.u_out, n, 0, gi, acc[gi] + acc2[gi]);
             acc[gi] = mfma16(a21h, uh0[gi], rr[gi][1]);
             acc2[gi] = mfma16(a21h, ul0[gi], f32x4{0.f, 0.f, 0.f, 0.f});
             acc2[gi] = mfma16(a21l, uh0[gi], acc2[gi]);
@@ -802,12 +833,14 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             split4(acc[gi] + acc2[gi], uh1[gi], ul1[gi]);
+            if constexpr (BWD) storeTile(a.u_out, n, 1, gi, acc[gi] + acc2[gi]);
             ubh[gi] = cat(uh0[gi], uh1[gi]);
             ubl[gi] = cat(ul0[gi], ul1[gi]);
         }
 
         // O = scale (P + A_qk U) -> the LDS staging tile (row-major); waves 4..7
         // store it to HBM in whole rows in the next phase
+        if constexpr (BWD) return;
         f32x4 o[2][NG];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -834,6 +867,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     // o of chunk n from the staging tile to HBM, 16 bytes per lane and whole
     // rows of the V tile per lane group (the helper waves, a third each)
     auto storeO = [&](int n) {
+        if constexpr (BWD) return;
         const int lane = opaque_tid() & 63;
         const int t0 = n * kC;
         const auto ro = make_rsrc(og + ((tok_b + t0) * HV + hv) * V + v0, rows_bytes(t0, v_stride, VT, 2));
@@ -962,7 +996,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     // Prefix snapshots (SNAP only): the state after chunks snap_chunks,
     // 2 snap_chunks, ..., NS snap_chunks; snap_ptr is the next one's [K][V]
     // slice, null when none is left.
-    float *snap_ptr = SNAP ? a.snap + ((static_cast<size_t>(b) * a.NS) * HV + hv) * K * V : nullptr;
+    float *snap_ptr = SNAP && a.snap ? a.snap + ((static_cast<size_t>(b) * a.NS) * HV + hv) * K * V : nullptr;
     int snap_at = a.snap_chunks;
     // Snapshot after chunk snap_at - 1.  exact: m holds M (after the last
     // chunk).  Otherwise m holds the next chunk's N (end of P2, off the carry's
@@ -987,7 +1021,8 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     if (carry) {
         const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
         if (a.S0) {
-            const float *S0 = a.S0 + (static_cast<size_t>(b) * HV + hv) * K * V;
+            const size_t s0b = a.s0_bstride ? static_cast<size_t>(a.s0_bstride) : static_cast<size_t>(HV) * K * V;
+            const float *S0 = a.S0 + b * s0b + static_cast<size_t>(hv) * K * V;
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const int vcol = v0 + 16 * (wave * NG + gi) + lr;
@@ -1084,10 +1119,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     if (a.ST && carry) carryStore(a.ST + (static_cast<size_t>(b) * HV + hv) * K * V);
 }
 
-template <int K, int VT, bool SNAP, bool GATED, bool OG>
+template <int K, int VT, bool SNAP, bool GATED, bool OG, bool BWD = false>
 hipError_t launch_kvt_s(const PrefillArgs &a, hipStream_t stream) {
     using L = Plan<K>;
-    auto kern = prefill_bf16_kernel<K, VT, SNAP, GATED, OG>;
+    auto kern = prefill_bf16_kernel<K, VT, SNAP, GATED, OG, BWD>;
     constexpr int lds = L::bytes + L::stage_bytes(VT);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1099,6 +1134,7 @@ hipError_t launch_kvt_s(const PrefillArgs &a, hipStream_t stream) {
 
 template <int K, int VT>
 hipError_t launch_kvt(const PrefillArgs &a, hipStream_t stream) {
+    if (a.bwd) return launch_kvt_s<K, VT, true, false, false, true>(a, stream);
     if (a.snap) return launch_kvt_s<K, VT, true, false, false>(a, stream);
     if (!a.A_log) return launch_kvt_s<K, VT, false, false, false>(a, stream);
     // the fused gate; the output gate in the o stores when the workgroup

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 enum kda_status { KDA_OK = 0, KDA_EINVAL = 1, KDA_EUNSUPPORTED = 2, KDA_EHIP = 3 };
 
@@ -208,6 +208,41 @@ int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *
                       float *dbeta, float *dinitial_state, int B, int T, int H, int HV, int K,
                       int V, float scale, int dtype, void *workspace, long long workspace_bytes,
                       void *stream);
+
+/*
+ * kda_chunk_bwd -- the same gradients as kda_recurrent_bwd for bf16 inputs in
+ * the bounded-gate range of kda_chunk_fwd (-5 <= g <= 0), computed in the
+ * chunk form on the matrix cores.
+ *
+ * The chunk form of delta_recurrence on the page
+ * "src/tinycenn_lm/research_layers.py" (as kda_chunk_fwd evaluates it),
+ * differentiated chunk by chunk in reverse: the backward of KDAFunction on
+ * the page "K3/kda/ops/reference/recurrent.py" restated for chunks of 32
+ * tokens.  Arguments, layouts, outputs and return codes as kda_recurrent_bwd,
+ * with dtype KDA_DTYPE_BF16 only (others: KDA_EUNSUPPORTED) and
+ *   workspace     device memory of at least
+ *                 kda_chunk_bwd_workspace_size(B, T, H, HV, K, V, dtype)
+ *                 bytes, 16-byte aligned, owned by the caller, scratch
+ *                 between calls; may be NULL when B * T == 0.
+ * With g outside [-5, 0] the result is not defined (use kda_recurrent_bwd).
+ * Runs the chunked forward once over the sequence (keeping the final state
+ * and the state every 1024 tokens), then, one slab of 1024 tokens at a time
+ * from the last: the forward over the slab again (the state at every chunk
+ * start and the in-chunk solve's input and result), a chunk-parallel pass
+ * forming the reverse chain's operands, the reverse chain of state gradients
+ * (one workgroup per value head and V tile), a chunk-parallel pass for
+ * dq, dk, dv, dbeta and the dg terms, and the reverse sum that forms dg; all
+ * asynchronous on `stream`.  Workspace about 0.85 GB at B = 1, T = 8192,
+ * HV = 96, K = V = 128.
+ * kda_chunk_bwd_workspace_size returns the workspace size in bytes, or -1
+ * (message in kda_last_error) for sizes or a dtype kda_chunk_bwd rejects.
+ */
+long long kda_chunk_bwd_workspace_size(int B, int T, int H, int HV, int K, int V, int dtype);
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  const float *initial_state, const void *dout, const float *dfinal_state, void *dq,
+                  void *dk, void *dv, float *dg, float *dbeta, float *dinitial_state, int B, int T,
+                  int H, int HV, int K, int V, float scale, int dtype, void *workspace,
+                  long long workspace_bytes, void *stream);
 
 /*
  * kda_recurrent_bwd_noalloc -- kda_recurrent_bwd for callers that cannot

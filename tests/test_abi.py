@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol():
                           "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_gated",
                           "kda_chunk_fwd_snapshots", "kda_recurrent_fwd", "kda_prefill_prologue",
                           "kda_output_gate", "kda_decode_step", "kda_recurrent_bwd",
-                          "kda_recurrent_bwd_workspace_size", "kda_recurrent_bwd_noalloc"}
+                          "kda_recurrent_bwd_workspace_size", "kda_recurrent_bwd_noalloc",
+                          "kda_chunk_bwd", "kda_chunk_bwd_workspace_size"}
     L = ctypes.CDLL(kda.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -462,3 +463,77 @@ def test_noalloc_backward_scratch_limit():
     assert rc == 1 and "dg is not 16-byte aligned" in err, err
     rc, err = call(1, 8, 2, 3, 32, 32)
     assert rc == 1 and "multiple" in err, err
+
+
+def chunk_bwd_call(**over):
+    """kda_chunk_bwd with fake, disjoint pointers (each BIG apart)."""
+    a = dict(q=BIG, k=2 * BIG, v=3 * BIG, g=4 * BIG, beta=5 * BIG, s0=None, do=6 * BIG, dst=None,
+             dq=7 * BIG, dk=8 * BIG, dv=9 * BIG, dg=10 * BIG, db=11 * BIG, ds0=None, ws=12 * BIG,
+             wsb=1 << 40, B=1, T=8, H=2, HV=4, K=32, V=32, scale=0.0, dtype=1)
+    a.update(over)
+    L = lib()
+    rc = L.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["do"], a["dst"],
+                         a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["ds0"], a["B"], a["T"],
+                         a["H"], a["HV"], a["K"], a["V"], a["scale"], a["dtype"], a["ws"], a["wsb"], None)
+    return rc, L.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(dtype=0), 2, "KDA_DTYPE_BF16"),
+    (dict(HV=3), 1, "kda_chunk_bwd: HV=3"),
+    (dict(K=16), 2, "32, 64 or 128"),
+    (dict(V=48), 2, "32, 64 or 128"),
+    (dict(do=None), 1, "dout must be non-NULL"),
+    (dict(db=None), 1, "dbeta must be non-NULL"),
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(wsb=1000), 1, "needed"),
+    (dict(dk=8 * BIG + 4), 1, "dk is not 16-byte aligned"),
+    (dict(dq=BIG + 64), 1, "dq overlaps q"),
+    (dict(ws=9 * BIG + 256), 1, "dv overlaps workspace"),
+    (dict(ds0=4 * BIG), 1, "dinitial_state overlaps g"),
+    (dict(scale=float("inf")), 1, "infinite"),
+    (dict(B=1 << 20, HV=64, H=64), 2, "launch grid"),
+])
+def test_chunk_bwd_rejects(over, code, msg):
+    rc, err = chunk_bwd_call(**over)
+    assert rc == code, err
+    assert msg in err, err
+
+
+def test_chunk_bwd_empty_batch_is_noop():
+    rc, err = chunk_bwd_call(B=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None, dk=None,
+                             dv=None, dg=None, db=None, ws=None)
+    assert rc == 0, err
+
+
+def test_chunk_bwd_workspace_size():
+    L = lib()
+    up = lambda floats: (floats * 4 + 255) // 256 * 256
+
+    def img(K):
+        # k Lambda' [32][K+4]; s (q Gamma)^T and -(beta k Gamma)^T [K][36];
+        # s A_qk^T [32][36]; T11^T, T22^T, -A21^T [16][20]; Gamma_last [K]
+        # (the whole padded to a multiple of 1024 floats)
+        return (32 * (K + 4) + 2 * K * 36 + 32 * 36 + 3 * 16 * 20 + K + 1023) // 1024 * 1024
+
+    def want(B, T, HV, K, V):
+        # slabs of Ls = 1024 tokens (T rounded up to 32 when shorter), NC = Ls/32
+        # chunks: S_T, carried dS [B,HV,K,V]; slab starts [B,slabs-1,HV,K,V];
+        # chunk-start states [B,NC-1,HV,K,V]; W, U, dR [B,Ls,HV,V]; operand
+        # images [B,NC,HV,img]; dS per chunk [B,NC,HV,K,V]; dg terms
+        # [B,Ls,HV,K]; block sums [B,HV,Ls/64,K]; dg carry [2,B,HV,K]
+        Ls = 1024 if T > 1024 else max(32, -(-T // 32) * 32)
+        NS1 = -(-T // Ls) - 1 if T > 0 else 0
+        NC = Ls // 32
+        return (2 * up(B * HV * K * V) + up(B * NS1 * HV * K * V) + up(B * (NC - 1) * HV * K * V)
+                + 3 * up(B * Ls * HV * V) + up(B * NC * HV * img(K)) + up(B * NC * HV * K * V)
+                + up(B * Ls * HV * K) + up(B * HV * -(-Ls // 64) * K) + up(2 * B * HV * K))
+    for args in [(2, 100, 2, 4, 64, 128), (1, 8192, 96, 96, 128, 128), (3, 2500, 1, 2, 32, 64),
+                 (1, 1024, 1, 1, 128, 128), (1, 1025, 1, 1, 128, 128), (1, 1, 1, 1, 32, 32)]:
+        B, T, H, HV, K, V = args
+        assert L.kda_chunk_bwd_workspace_size(*args, 1) == want(B, T, HV, K, V), args
+    # the HV96 workload: below the token-recurrent backward's 1.16 GB
+    assert L.kda_chunk_bwd_workspace_size(1, 8192, 96, 96, 128, 128, 1) < 0.9e9
+    assert L.kda_chunk_bwd_workspace_size(1, 8, 2, 4, 32, 32, 0) == -1
+    assert "KDA_DTYPE_BF16" in L.kda_last_error().decode()
+    assert L.kda_chunk_bwd_workspace_size(1, 8, 2, 3, 32, 32, 1) == -1
