@@ -485,18 +485,20 @@ __global__ __launch_bounds__(kThr, 1) void cbwd_chain_kernel(SlabArgs s) {
 
 // ---------------------------------------------------------------- 3. grad
 // One workgroup per (b, q/k head h, chunk of the slab); the value heads of h
-// one after another, dq and dk summed over them in registers.
+// one after another, dq and dk summed over them in registers.  The chunk's
+// dO, dR and U are staged in LDS once per head (every wave reads all of their
+// rows); each wave's [C x K] tiles share one 16-column block of K, so it loads
+// that block's 16 rows of M and dM' once for both, half of V at a time.
 template <int K, int V>
 __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
-    constexpr int LK = K + 4, LC = kC + 4;
+    constexpr int LK = K + 4, LC = kC + 4, LV = V + 4, LQ = K + 8, LO = V + 8;
     constexpr int KT = K / 16;
     constexpr int NT = 2 * KT;              // 16x16 tiles of a [C][K] result
-    constexpr int TPW = (NT + 7) / 8;       // tiles per wave
+    constexpr int TPW = (NT + 7) / 8;       // tiles per wave (all of one column block)
+    constexpr int VS = V / 16;              // reduction blocks over V
     const ChunkBwdArgs &a = s.a;
     extern __shared__ __attribute__((aligned(16))) float sm[];
-    float *sQ = sm;                         // [C][LK] q, k of the chunk (fp32)
-    float *sK = sQ + kC * LK;
-    float *sG = sK + kC * LK;               // [C][LK] base-2 cumulative sums
+    float *sG = sm;                         // [C][LK] base-2 cumulative sums
     float *sPqT = sG + kC * LK;             // [K][LC] (q e1)^T, (k e1)^T, (k e2)^T
     float *sPkT = sPqT + K * LC;
     float *sRkT = sPkT + K * LC;
@@ -504,9 +506,14 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
     float *sDqT = sDq + kC * LC;
     float *sDk = sDqT + kC * LC;
     float *sDkbT = sDk + kC * LC;
-    float *sTot = sDkbT + kC * LC;          // [kThrG] partial column sums
+    float *sdR = sDkbT + kC * LC;           // [C][LV] dR, U of the chunk and head
+    float *sU = sdR + kC * LV;
+    float *sTot = sU + kC * LV;             // [kThrG] partial column sums
     float *sB = sTot + kThrG;               // [C] beta
     float *sDb = sB + kC;                   // [4][C] partial dbeta
+    uint16_t *sQ = reinterpret_cast<uint16_t *>(sDb + 4 * kC);   // [C][LQ] bf16 q, k
+    uint16_t *sK = sQ + kC * LQ;
+    uint16_t *sdO = sK + kC * LQ;           // [C][LO] bf16 dO
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const int n = blockIdx.x % s.NCs;
@@ -521,8 +528,11 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
     const uint16_t *kg = static_cast<const uint16_t *>(a.k);
     const uint16_t *dog = static_cast<const uint16_t *>(a.dout);
     const float scale = a.scale;
+    const bool has_tiles = wave < NT;
+    const int ct = wave % KT;               // this wave's column block of K (every tile of the wave)
+    const int yr = ct * 16 + lr;
 
-    // q, k of the chunk: 8 bf16 (16 bytes) per thread and row piece
+    // q, k of the chunk as bf16 rows, 16 bytes per unit (rows past the end 0)
     for (int u = tid; u < kC * K / 8; u += kThrG) {
         const int i = u / (K / 8), c = (u % (K / 8)) * 8;
         uint4 wq = make_uint4(0u, 0u, 0u, 0u), wk = wq;
@@ -531,15 +541,15 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
             wq = *reinterpret_cast<const uint4 *>(qg + qi);
             wk = *reinterpret_cast<const uint4 *>(kg + qi);
         }
-        const uint32_t q8[4] = {wq.x, wq.y, wq.z, wq.w}, k8[4] = {wk.x, wk.y, wk.z, wk.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sQ[i * LK + c + 2 * e] = __uint_as_float(q8[e] << 16);
-            sQ[i * LK + c + 2 * e + 1] = __uint_as_float(q8[e] & 0xffff0000u);
-            sK[i * LK + c + 2 * e] = __uint_as_float(k8[e] << 16);
-            sK[i * LK + c + 2 * e + 1] = __uint_as_float(k8[e] & 0xffff0000u);
-        }
+        *reinterpret_cast<uint4 *>(sQ + i * LQ + c) = wq;
+        *reinterpret_cast<uint4 *>(sK + i * LQ + c) = wk;
     }
+    auto qk_at = [&](const uint16_t *base, int i, int c) { return bf2f(base[i * LQ + c]); };
+    auto dO4 = [&](int row, int col) -> f32x4 {
+        const uint2 w = *reinterpret_cast<const uint2 *>(sdO + row * LO + col);
+        return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+    };
 
     f32x4 dqa[TPW], dka[TPW];
 #pragma unroll
@@ -547,20 +557,6 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
 
     for (int gv = 0; gv < G; ++gv) {
         const int hv = h * G + gv;
-        __syncthreads();   // the previous head's LDS reads are done
-        chunk_cumsum<K, kThrG>(a.g + (tok * HV + hv) * K, nv, HV * K, sG, LK, sTot);
-        if (tid < kC) sB[tid] = tid < nv ? a.beta[(tok + tid) * HV + hv] : 0.f;
-        __syncthreads();
-        for (int e = tid; e < kC * K; e += kThrG) {
-            const int c = e / kC, i = e % kC;   // consecutive threads: consecutive rows of one column
-            const float Gi = sG[i * LK + c], Gr = sG[kR * LK + c];
-            const float e1 = ex2(Gi - Gr), e2 = ex2(Gr - Gi);
-            sPqT[c * LC + i] = sQ[i * LK + c] * e1;
-            sPkT[c * LC + i] = sK[i * LK + c] * e1;
-            sRkT[c * LC + i] = sK[i * LK + c] * e2;
-        }
-        __syncthreads();
-
         // slab-local rows of this chunk in the [B, Ls, HV, V] arrays
         const size_t lrow0 = static_cast<size_t>(b) * a.Ls + n * kC;
         const float *Ug = a.U + (lrow0 * HV + hv) * V;
@@ -568,45 +564,73 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
         const float *dRg = a.dR + (lrow0 * HV + hv) * V;
         const uint16_t *dOg = dog + (tok * HV + hv) * V;
         const size_t rs = static_cast<size_t>(HV) * V;   // row stride of those arrays
-        // A operand of an [C x C] or [C x K] product from a row of dO (bf16,
-        // rows past the end read as 0)
-        auto dO4 = [&](int row, int col) -> f32x4 {
-            if (row >= nv) return f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint2 w = *reinterpret_cast<const uint2 *>(dOg + row * rs + col);
-            return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                         __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
-        };
-        auto row4 = [&](const float *base, int row, int col) -> f32x4 {
-            if (row >= nv) return f32x4{0.f, 0.f, 0.f, 0.f};
-            return ld4(base + row * rs + col);
-        };
+        // dO (8 bf16 per unit), dR and U (4 floats per unit) of the chunk: every
+        // load in flight before the first wait (rows past the end are 0)
+        constexpr int NUO = kC * V / 8, NUF = kC * V / 4;
+        constexpr int JO = (NUO + kThrG - 1) / kThrG, JF = (NUF + kThrG - 1) / kThrG;
+        uint4 wo[JO];
+        f32x4 wr[JF], wu[JF];
+#pragma unroll
+        for (int j = 0; j < JO; ++j) {
+            const int u = tid + kThrG * j, i = u / (V / 8), c = (u % (V / 8)) * 8;
+            wo[j] = make_uint4(0u, 0u, 0u, 0u);
+            if (u < NUO && i < nv) wo[j] = *reinterpret_cast<const uint4 *>(dOg + i * rs + c);
+        }
+#pragma unroll
+        for (int j = 0; j < JF; ++j) {
+            const int u = tid + kThrG * j, i = u / (V / 4), c = (u % (V / 4)) * 4;
+            wr[j] = wu[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (u < NUF && i < nv) {
+                wr[j] = ld4(dRg + i * rs + c);
+                wu[j] = ld4(Ug + i * rs + c);
+            }
+        }
+        __syncthreads();   // the previous head's LDS reads are done
+        chunk_cumsum<K, kThrG>(a.g + (tok * HV + hv) * K, nv, HV * K, sG, LK, sTot);
+        if (tid < kC) sB[tid] = tid < nv ? a.beta[(tok + tid) * HV + hv] : 0.f;
+#pragma unroll
+        for (int j = 0; j < JO; ++j) {
+            const int u = tid + kThrG * j, i = u / (V / 8), c = (u % (V / 8)) * 8;
+            if (u < NUO) *reinterpret_cast<uint4 *>(sdO + i * LO + c) = wo[j];
+        }
+#pragma unroll
+        for (int j = 0; j < JF; ++j) {
+            const int u = tid + kThrG * j, i = u / (V / 4), c = (u % (V / 4)) * 4;
+            if (u < NUF) {
+                *reinterpret_cast<f32x4 *>(sdR + i * LV + c) = wr[j];
+                *reinterpret_cast<f32x4 *>(sU + i * LV + c) = wu[j];
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < kC * K; e += kThrG) {
+            const int c = e / kC, i = e % kC;   // consecutive threads: consecutive rows of one column
+            const float Gi = sG[i * LK + c], Gr = sG[kR * LK + c];
+            const float e1 = ex2(Gi - Gr), e2 = ex2(Gr - Gi);
+            const float qv = qk_at(sQ, i, c), kv = qk_at(sK, i, c);
+            sPqT[c * LC + i] = qv * e1;
+            sPkT[c * LC + i] = kv * e1;
+            sRkT[c * LC + i] = kv * e2;
+        }
+        __syncthreads();
 
         if (wave < 6) {
             // dA_qk = s L(dO U^T) (waves 0-2), dA_kk = -SL(dR U^T) and the
             // dbeta term with SL(Pk Rk^T) (waves 3-5); lower tiles (0,0), (1,0), (1,1)
-            const int t = wave % 3, rt = t == 0 ? 0 : 1, ct = t == 2 ? 1 : 0;
-            const int xr = rt * 16 + lr, yr = ct * 16 + lr;
+            const int t = wave % 3, rt = t == 0 ? 0 : 1, ctt = t == 2 ? 1 : 0;
+            const int xr = rt * 16 + lr, jr = ctt * 16 + lr;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            // the loads of four steps first, then their products
-            constexpr int SA = V / 16 > 4 ? 4 : V / 16;
 #pragma unroll
-            for (int s0 = 0; s0 < V / 16; s0 += SA) {
-                f32x4 xa[SA], yb[SA];
+            for (int st = 0; st < VS; ++st) {
+                const int c = st * 16 + 4 * lg;
+                const f32x4 xa = wave < 3 ? dO4(xr, c) : ld4(sdR + xr * LV + c);
+                const f32x4 yb = ld4(sU + jr * LV + c);
 #pragma unroll
-                for (int st = 0; st < SA; ++st) {
-                    const int c = (s0 + st) * 16 + 4 * lg;
-                    xa[st] = wave < 3 ? dO4(xr, c) : row4(dRg, xr, c);
-                    yb[st] = row4(Ug, yr, c);
-                }
-#pragma unroll
-                for (int st = 0; st < SA; ++st)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc = mma4(xa[st][j], yb[st][j], acc);
+                for (int j = 0; j < 4; ++j) acc = mma4(xa[j], yb[j], acc);
             }
             if (wave < 3) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int row = rt * 16 + 4 * lg + j, col = ct * 16 + lr;
+                    const int row = rt * 16 + 4 * lg + j, col = ctt * 16 + lr;
                     const float x = col <= row ? scale * acc[j] : 0.f;
                     sDq[row * LC + col] = x;
                     sDqT[col * LC + row] = x;
@@ -626,12 +650,12 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int kk = k0 + 4 * lg + j;
-                        ar = mma4(sPkT[kk * LC + xr], sRkT[kk * LC + yr], ar);
+                        ar = mma4(sPkT[kk * LC + xr], sRkT[kk * LC + jr], ar);
                     }
                 float part[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int row = rt * 16 + 4 * lg + j, col = ct * 16 + lr;
+                    const int row = rt * 16 + 4 * lg + j, col = ctt * 16 + lr;
                     const float x = col < row ? -acc[j] : 0.f;
                     sDk[row * LC + col] = x;
                     sDkbT[col * LC + row] = sB[row] * x;
@@ -659,25 +683,18 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
             if (row < nv) {
                 uint16_t *dvg = static_cast<uint16_t *>(a.dv) + ((tok + row) * HV + hv) * V;
                 const float bt = sB[row];
-                constexpr int SD = V / 16 > 4 ? 4 : V / 16;
+                f32x4 ww[VS];
 #pragma unroll
-                for (int s0 = 0; s0 < V / 16; s0 += SD) {
-                f32x4 dd[SD], ww[SD];
+                for (int st = 0; st < VS; ++st) ww[st] = ld4(Wg + row * rs + st * 16 + qv * 4);
 #pragma unroll
-                for (int st = 0; st < SD; ++st) {
-                    dd[st] = ld4(dRg + row * rs + (s0 + st) * 16 + qv * 4);
-                    ww[st] = ld4(Wg + row * rs + (s0 + st) * 16 + qv * 4);
-                }
-#pragma unroll
-                for (int st = 0; st < SD; ++st) {
-                    const int c = (s0 + st) * 16 + qv * 4;
-                    const f32x4 d = dd[st], w = ww[st];
+                for (int st = 0; st < VS; ++st) {
+                    const int c = st * 16 + qv * 4;
+                    const f32x4 d = ld4(sdR + row * LV + c), w = ww[st];
                     dot += d[0] * w[0] + d[1] * w[1] + d[2] * w[2] + d[3] * w[3];
                     uint2 o;
                     o.x = static_cast<uint32_t>(float_to_bf16_bits(bt * d[0])) | (static_cast<uint32_t>(float_to_bf16_bits(bt * d[1])) << 16);
                     o.y = static_cast<uint32_t>(float_to_bf16_bits(bt * d[2])) | (static_cast<uint32_t>(float_to_bf16_bits(bt * d[3])) << 16);
                     *reinterpret_cast<uint2 *>(dvg + c) = o;
-                }
                 }
             }
             dot += lanes::dpp<0xb1>(dot);
@@ -691,52 +708,57 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
             a.dbeta[(tok + tid) * HV + hv] = sDb[2 * kC + tid] + dA;
         }
 
-        // [C x K] results, tile (rt, ct) per wave
+        // [C x K] results: tiles (rt, ct) of this wave.  Its rows of M (the
+        // state at the chunk start) and dM' (the gradient at its end) are
+        // loaded once for both tiles, half of V at a time (all in flight together)
         const float *Mn = n == 0 ? (s.Sstart ? s.Sstart + b * s.s_bstride + static_cast<size_t>(hv) * K * V : nullptr)
                                  : a.snapc + ((static_cast<size_t>(b) * (s.NCs - 1) + n - 1) * HV + hv) * K * V;
         const float *dMn = a.dMs + ((static_cast<size_t>(b) * s.NCs + n) * HV + hv) * K * V;
+        constexpr int VH = VS > 4 ? 4 : VS;     // reduction blocks per half
+        f32x4 x1[TPW], x2[TPW], x3[TPW];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) x1[u] = x2[u] = x3[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (has_tiles) {
+#pragma unroll
+            for (int s0 = 0; s0 < VS; s0 += VH) {
+                f32x4 mrow[VH], dmrow[VH];
+#pragma unroll
+                for (int st = 0; st < VH; ++st) {
+                    const int c = (s0 + st) * 16 + 4 * lg;
+                    mrow[st] = Mn ? ld4(Mn + static_cast<size_t>(yr) * V + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    dmrow[st] = ld4(dMn + static_cast<size_t>(yr) * V + c);
+                }
+#pragma unroll
+                for (int u = 0; u < TPW; ++u) {
+                    const int tile = wave + 8 * u;
+                    if (tile < NT) {
+                        const int xr = (tile / KT) * 16 + lr;
+                        // dO M^T, dR M^T, U dM'^T over this half of V; dO, dR, U rows from LDS
+#pragma unroll
+                        for (int st = 0; st < VH; ++st) {
+                            const int c = (s0 + st) * 16 + 4 * lg;
+                            const f32x4 o4 = dO4(xr, c), r4 = ld4(sdR + xr * LV + c), u4 = ld4(sU + xr * LV + c);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                x1[u] = mma4(o4[j], mrow[st][j], x1[u]);
+                                x2[u] = mma4(r4[j], mrow[st][j], x2[u]);
+                                x3[u] = mma4(u4[j], dmrow[st][j], x3[u]);
+                            }
+                        }
+                    }
+                    // one tile at a time: both tiles' operand reads would not fit the registers
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
         float *eg = a.e + ((static_cast<size_t>(b) * a.Ls + n * kC) * HV + hv) * K;
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int tile = wave + 8 * u;
             if (tile < NT) {
-                const int rt = tile / KT, ct = tile % KT;
-                const int xr = rt * 16 + lr, yr = ct * 16 + lr;
-                f32x4 x1 = {0.f, 0.f, 0.f, 0.f}, x2 = x1, x3 = x1, y1 = x1, y2 = x1, y3 = x1;
-                // dO M^T and dR M^T over V (every step's loads first), then U dM'^T
-                constexpr int SB = V / 16 > 4 ? 4 : V / 16;   // steps per batch of loads
-#pragma unroll
-                for (int s0 = 0; s0 < V / 16; s0 += SB) {
-                    f32x4 o4[SB], r4[SB], m4[SB];
-#pragma unroll
-                    for (int st = 0; st < SB; ++st) {
-                        const int c = (s0 + st) * 16 + 4 * lg;
-                        o4[st] = dO4(xr, c);
-                        r4[st] = row4(dRg, xr, c);
-                        m4[st] = Mn ? ld4(Mn + static_cast<size_t>(yr) * V + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-                    }
-#pragma unroll
-                    for (int st = 0; st < SB; ++st)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            x1 = mma4(o4[st][j], m4[st][j], x1);
-                            x2 = mma4(r4[st][j], m4[st][j], x2);
-                        }
-                }
-#pragma unroll
-                for (int s0 = 0; s0 < V / 16; s0 += SB) {
-                    f32x4 u4[SB], dm4[SB];
-#pragma unroll
-                    for (int st = 0; st < SB; ++st) {
-                        const int c = (s0 + st) * 16 + 4 * lg;
-                        u4[st] = row4(Ug, xr, c);
-                        dm4[st] = ld4(dMn + static_cast<size_t>(yr) * V + c);
-                    }
-#pragma unroll
-                    for (int st = 0; st < SB; ++st)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) x3 = mma4(u4[st][j], dm4[st][j], x3);
-                }
+                const int rt = tile / KT;
+                const int xr = rt * 16 + lr;
+                f32x4 y1 = {0.f, 0.f, 0.f, 0.f}, y2 = y1, y3 = y1;
                 // dA_qk Rk, dA_kk Rk, dA_qk^T Pq + (beta dA_kk)^T Pk over the chunk's rows
                 tile_nt<kC>(sDq + xr * LC, sRkT + yr * LC, lg, y1);
                 tile_nt<kC>(sDk + xr * LC, sRkT + yr * LC, lg, y2);
@@ -750,10 +772,10 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
                     const float Gi = sG[i * LK + c];
                     const float gam = ex2(Gi), e1 = ex2(Gi - Gr), e2 = ex2(Gr - Gi), lam = ex2(Gl - Gi);
                     const float bt = sB[i];
-                    const float dq = scale * gam * x1[j] + e1 * y1[j];
-                    const float dkr = bt * (e1 * y2[j] - gam * x2[j]);
-                    const float dkw = lam * x3[j] + e2 * y3[j];
-                    const float q = sQ[i * LK + c], k = sK[i * LK + c];
+                    const float dq = scale * gam * x1[u][j] + e1 * y1[j];
+                    const float dkr = bt * (e1 * y2[j] - gam * x2[u][j]);
+                    const float dkw = lam * x3[u][j] + e2 * y3[j];
+                    const float q = qk_at(sQ, i, c), k = qk_at(sK, i, c);
                     if (i < nv) eg[static_cast<size_t>(i) * HV * K + c] = q * dq + k * (dkr - dkw);
                     dqa[u][j] += dq;
                     dka[u][j] += dkr + dkw;
@@ -767,7 +789,7 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
     for (int u = 0; u < TPW; ++u) {
         const int tile = wave + 8 * u;
         if (tile < NT) {
-            const int rt = tile / KT, ct = tile % KT;
+            const int rt = tile / KT;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int i = rt * 16 + 4 * lg + j;
@@ -785,8 +807,11 @@ template <int K>
 constexpr int prep_lds() { return (Img<K>::floats + 4 * kC * (K + 4) + kThr + kC + 2 * 16 * 20) * 4; }
 template <int K, int VT>
 constexpr int chain_lds() { return 2 * (Img<K>::floats + (kC * (VT + 8) * 2 + 15) / 16 * 4) * 4; }
-template <int K>
-constexpr int grad_lds() { return (3 * kC * (K + 4) + 3 * K * (kC + 4) + 4 * kC * (kC + 4) + kThrG + kC + 4 * kC) * 4; }
+template <int K, int V>
+constexpr int grad_lds() {
+    return (kC * (K + 4) + 3 * K * (kC + 4) + 4 * kC * (kC + 4) + 2 * kC * (V + 4) + kThrG + kC + 4 * kC) * 4
+         + (2 * kC * (K + 8) + kC * (V + 8)) * 2;
+}
 
 template <typename F>
 hipError_t launch_dyn(F kern, unsigned grid, int lds, hipStream_t stream, const SlabArgs &s, int threads = kThr) {
@@ -799,7 +824,7 @@ hipError_t launch_dyn(F kern, unsigned grid, int lds, hipStream_t stream, const 
 
 template <int K, int V>
 hipError_t launch_slab_kernels(const SlabArgs &s, hipStream_t stream) {
-    static_assert(prep_lds<K>() <= 160 * 1024 && grad_lds<K>() <= 160 * 1024, "LDS plan exceeds 160 KB");
+    static_assert(prep_lds<K>() <= 160 * 1024 && grad_lds<K, V>() <= 160 * 1024, "LDS plan exceeds 160 KB");
     const ChunkBwdArgs &a = s.a;
     hipError_t e = launch_dyn(cbwd_prep_kernel<K>, static_cast<unsigned>(a.B) * a.HV * s.NCs, prep_lds<K>(), stream, s);
     if (e != hipSuccess) return e;
@@ -812,7 +837,7 @@ hipError_t launch_slab_kernels(const SlabArgs &s, hipStream_t stream) {
     else
         e = launch_dyn(cbwd_chain_kernel<K, V>, static_cast<unsigned>(a.B) * a.HV, chain_lds<K, V>(), stream, s);
     if (e != hipSuccess) return e;
-    return launch_dyn(cbwd_grad_kernel<K, V>, static_cast<unsigned>(a.B) * a.H * s.NCs, grad_lds<K>(), stream, s,
+    return launch_dyn(cbwd_grad_kernel<K, V>, static_cast<unsigned>(a.B) * a.H * s.NCs, grad_lds<K, V>(), stream, s,
                       kThrG);
 }
 
