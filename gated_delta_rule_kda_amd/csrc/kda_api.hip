@@ -254,21 +254,20 @@ bool bwd_layout(BwdLayout &L, int B, int T, int HV, int K, int V) {
 // shorter); everything but the final state and the slab-start states holds one
 // slab.
 struct ChunkBwdLayout {
-    uint64_t st, snap1, Dc, snapc, W, U, img, dR, dMs, e, bs, gc, total;
-    int Ls, NS1, NCs, NB;
+    uint64_t st, snap1, Dc, snapc, W, U, img, dR, dMs, e, cs, gc, total;
+    int Ls, NS1, NCs;
 };
 
 bool chunk_bwd_layout(ChunkBwdLayout &L, int B, int T, int HV, int K, int V) {
     L.Ls = T > kda::kBwdSlab ? kda::kBwdSlab : (T > 0 ? (T + 31) / 32 * 32 : 32);
     L.NS1 = T > 0 ? (T + L.Ls - 1) / L.Ls - 1 : 0;
     L.NCs = L.Ls / 32;
-    L.NB = (L.Ls + kda::kDgBlock - 1) / kda::kDgBlock;
     const int imf = kda::chunk_bwd_image_floats(K);
-    uint64_t ns, nsn, nsc, nv, nimg, nms, ne, nbs, ngc;
+    uint64_t ns, nsn, nsc, nv, nimg, nms, ne, ncs, ngc;
     if (imf <= 0 || !count(ns, {B, HV, K, V}) || !count(nsn, {B, L.NS1, HV, K, V}) ||
         !count(nsc, {B, L.NCs - 1, HV, K, V}) || !count(nv, {B, L.Ls, HV, V}) ||
         !count(nimg, {B, L.NCs, HV, imf}) || !count(nms, {B, L.NCs, HV, K, V}) ||
-        !count(ne, {B, L.Ls, HV, K}) || !count(nbs, {B, HV, L.NB, K}) || !count(ngc, {2, B, HV, K}))
+        !count(ne, {B, L.Ls, HV, K}) || !count(ncs, {B, HV, L.NCs, K}) || !count(ngc, {2, B, HV, K}))
         return false;
     uint64_t off = 0;
     auto take = [&](uint64_t floats) {
@@ -278,7 +277,7 @@ bool chunk_bwd_layout(ChunkBwdLayout &L, int B, int T, int HV, int K, int V) {
     };
     L.st = take(ns); L.snap1 = take(nsn); L.Dc = take(ns); L.snapc = take(nsc);
     L.W = take(nv); L.U = take(nv); L.img = take(nimg); L.dR = take(nv); L.dMs = take(nms);
-    L.e = take(ne); L.bs = take(nbs); L.gc = take(ngc);
+    L.e = take(ne); L.cs = take(ncs); L.gc = take(ngc);
     L.total = off;
     return true;
 }
@@ -449,9 +448,9 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, c
         auto at = [&](uint64_t off) { return reinterpret_cast<float *>(ws + off); };
         a.ST = at(L.st); a.snap1 = at(L.snap1); a.Dc = at(L.Dc); a.snapc = at(L.snapc);
         a.W = at(L.W); a.U = at(L.U); a.img = at(L.img); a.dR = at(L.dR); a.dMs = at(L.dMs);
-        a.e = at(L.e); a.bs = at(L.bs); a.gc = at(L.gc);
+        a.e = at(L.e); a.cs = at(L.cs); a.gc = at(L.gc);
     }
-    a.Ls = L.Ls; a.NS1 = L.NS1; a.NB = L.NB;
+    a.Ls = L.Ls; a.NS1 = L.NS1;
     a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
     a.scale = scale;
     const hipError_t e = kda::launch_chunk_backward(a, static_cast<hipStream_t>(stream));

@@ -42,7 +42,8 @@
 //     the dM update, on the matrix cores; keeps dR and every chunk's dM';
 //  3. grad (chunk-parallel, one workgroup per (b, q/k head, chunk), summing
 //     over the head's value heads): the rest of the formulas above;
-//  4. dg: the blocked reverse sum of the token-recurrent backward.
+//  4. dg: a reverse sum over the chunks' sums of the dg terms (which the
+//     grad pass leaves), then over each chunk's tokens.
 // Every product is an fp32 MFMA (v_mfma_f32_16x16x4_f32): no operand is
 // rounded below fp32 in the backward itself.
 //
@@ -511,7 +512,8 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
     float *sTot = sU + kC * LV;             // [kThrG] partial column sums
     float *sB = sTot + kThrG;               // [C] beta
     float *sDb = sB + kC;                   // [4][C] partial dbeta
-    uint16_t *sQ = reinterpret_cast<uint16_t *>(sDb + 4 * kC);   // [C][LQ] bf16 q, k
+    float *sCs = sDb + 4 * kC;              // [8][K] partial column sums of the dg terms
+    uint16_t *sQ = reinterpret_cast<uint16_t *>(sCs + 8 * K);    // [C][LQ] bf16 q, k
     uint16_t *sK = sQ + kC * LQ;
     uint16_t *sdO = sK + kC * LQ;           // [C][LO] bf16 dO
 
@@ -766,6 +768,7 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
                 tile_nt<kC>(sDkbT + xr * LC, sPkT + yr * LC, lg, y3);
                 const int c = ct * 16 + lr;
                 const float Gr = sG[kR * LK + c], Gl = sG[(kC - 1) * LK + c];
+                float csum = 0.f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int i = rt * 16 + 4 * lg + j;
@@ -776,11 +779,22 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
                     const float dkr = bt * (e1 * y2[j] - gam * x2[u][j]);
                     const float dkw = lam * x3[u][j] + e2 * y3[j];
                     const float q = qk_at(sQ, i, c), k = qk_at(sK, i, c);
-                    if (i < nv) eg[static_cast<size_t>(i) * HV * K + c] = q * dq + k * (dkr - dkw);
+                    const float term = q * dq + k * (dkr - dkw);   // 0 on rows past the end (q = k = 0)
+                    if (i < nv) eg[static_cast<size_t>(i) * HV * K + c] = term;
+                    csum += term;
                     dqa[u][j] += dq;
                     dka[u][j] += dkr + dkw;
                 }
+                sCs[(rt * 4 + lg) * K + c] = csum;
             }
+        }
+        // the chunk's sum of the dg terms per column, for the reverse sum over chunks
+        __syncthreads();
+        if (tid < K) {
+            float cs = 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) cs += sCs[r * K + tid];
+            a.cs[((static_cast<size_t>(b) * HV + hv) * s.NCs + n) * K + tid] = cs;
         }
     }
     // dq, dk (bf16) of the chunk's rows inside the sequence
@@ -803,13 +817,64 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
     }
 }
 
+// ---------------------------------------------------------------- 4. dg
+// dg_u = sum over V of S_T (.) dL/dS_T + sum over t >= u of the dg terms e_t
+// (the identity in the header).  The final-state term starts the carry:
+// gc[b, hv, k] = sum_v S_T[k][v] dL/dS_T[k][v].
+__global__ __launch_bounds__(256) void cbwd_dg_final_kernel(ChunkBwdArgs a, float *gc) {
+    const long n = static_cast<long>(a.B) * a.HV * a.K;
+    const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    float c = 0.f;
+    if (a.dST) {
+        const f32x4 *st = reinterpret_cast<const f32x4 *>(a.ST + i * a.V);
+        const f32x4 *ds = reinterpret_cast<const f32x4 *>(a.dST + i * a.V);
+        for (int v = 0; v < a.V / 4; ++v) {
+            const f32x4 x = st[v], y = ds[v];
+            c += (x[0] * y[0] + x[1] * y[1]) + (x[2] * y[2] + x[3] * y[3]);
+        }
+    }
+    gc[i] = c;
+}
+
+// One slab: thread = (b, hv, chunk j, k).  The carry in (the final-state term
+// and every later slab's terms) plus the later chunks' sums, then the chunk's
+// 32 tokens from the last; the thread of chunk 0 leaves the carry for the
+// slab before.
+__global__ __launch_bounds__(256) void cbwd_dg_kernel(SlabArgs s, const float *gc_in, float *gc_out) {
+    const ChunkBwdArgs &a = s.a;
+    const long n = static_cast<long>(a.B) * a.HV * s.NCs * a.K;
+    const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int k = static_cast<int>(i % a.K);
+    const long r = i / a.K;
+    const int j = static_cast<int>(r % s.NCs);
+    const long bhv = r / s.NCs;
+    const int b = static_cast<int>(bhv / a.HV), hv = static_cast<int>(bhv % a.HV);
+    float acc = gc_in[bhv * a.K + k];
+    for (int jj = s.NCs - 1; jj > j; --jj) acc += a.cs[(bhv * s.NCs + jj) * a.K + k];
+    const int nv = min(kC, s.len - j * kC);
+    const size_t step = static_cast<size_t>(a.HV) * a.K;
+    const float *e = a.e + ((static_cast<size_t>(b) * a.Ls + j * kC) * a.HV + hv) * a.K + k;
+    float *dg = a.dg + ((static_cast<size_t>(b) * a.T + s.t_begin + j * kC) * a.HV + hv) * a.K + k;
+    float ev[kC];
+#pragma unroll
+    for (int t = 0; t < kC; ++t) ev[t] = t < nv ? e[t * step] : 0.f;
+#pragma unroll
+    for (int t = kC - 1; t >= 0; --t) {
+        acc += ev[t];
+        if (t < nv) dg[t * step] = acc;
+    }
+    if (j == 0) gc_out[bhv * a.K + k] = acc;
+}
+
 template <int K>
 constexpr int prep_lds() { return (Img<K>::floats + 4 * kC * (K + 4) + kThr + kC + 2 * 16 * 20) * 4; }
 template <int K, int VT>
 constexpr int chain_lds() { return 2 * (Img<K>::floats + (kC * (VT + 8) * 2 + 15) / 16 * 4) * 4; }
 template <int K, int V>
 constexpr int grad_lds() {
-    return (kC * (K + 4) + 3 * K * (kC + 4) + 4 * kC * (kC + 4) + 2 * kC * (V + 4) + kThrG + kC + 4 * kC) * 4
+    return (kC * (K + 4) + 3 * K * (kC + 4) + 4 * kC * (kC + 4) + 2 * kC * (V + 4) + kThrG + kC + 4 * kC + 8 * K) * 4
          + (2 * kC * (K + 8) + kC * (V + 8)) * 2;
 }
 
@@ -828,14 +893,12 @@ hipError_t launch_slab_kernels(const SlabArgs &s, hipStream_t stream) {
     const ChunkBwdArgs &a = s.a;
     hipError_t e = launch_dyn(cbwd_prep_kernel<K>, static_cast<unsigned>(a.B) * a.HV * s.NCs, prep_lds<K>(), stream, s);
     if (e != hipSuccess) return e;
-    // V over two workgroups when there are few (b, hv) chains, as in the forward
-    const bool split = V >= 64 && static_cast<long>(a.B) * a.HV < 160;
-    constexpr int VS = V >= 64 ? V / 2 : V;
-    static_assert(chain_lds<K, V>() <= 160 * 1024 && chain_lds<K, VS>() <= 160 * 1024, "LDS plan exceeds 160 KB");
-    if (split)
-        e = launch_dyn(cbwd_chain_kernel<K, VS>, static_cast<unsigned>(a.B) * a.HV * (V / VS), chain_lds<K, VS>(), stream, s);
-    else
-        e = launch_dyn(cbwd_chain_kernel<K, V>, static_cast<unsigned>(a.B) * a.HV, chain_lds<K, V>(), stream, s);
+    // One workgroup per (b, hv) with all of V: the chain is bound by bringing in
+    // each chunk's operand image, not by its matrix work, and a head split
+    // over two workgroups reads the image twice (measured 0.3 ms slower per
+    // call on the HV96 shape, where the forward does split V).
+    static_assert(chain_lds<K, V>() <= 160 * 1024, "LDS plan exceeds 160 KB");
+    e = launch_dyn(cbwd_chain_kernel<K, V>, static_cast<unsigned>(a.B) * a.HV, chain_lds<K, V>(), stream, s);
     if (e != hipSuccess) return e;
     return launch_dyn(cbwd_grad_kernel<K, V>, static_cast<unsigned>(a.B) * a.H * s.NCs, grad_lds<K, V>(), stream, s,
                       kThrG);
@@ -881,6 +944,13 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     float *gc[2] = {a.gc, a.gc + static_cast<size_t>(a.B) * a.HV * a.K};
+    {
+        const long nk = static_cast<long>(a.B) * a.HV * a.K;
+        hipLaunchKernelGGL(cbwd_dg_final_kernel, dim3(static_cast<unsigned>((nk + 255) / 256)), dim3(256), 0,
+                           stream, a, gc[0]);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     for (int si = ns - 1, j = 0; si >= 0; --si, ++j) {
         SlabArgs s{};
         s.a = a;
@@ -913,13 +983,10 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
           : a.K == 128 ? launch_slab_k<128>(s, stream) : hipErrorInvalidValue;
         if (e != hipSuccess) return e;
         // dg over the slab, carried to the slab before
-        BwdArgs d{};
-        d.t_begin = s.t_begin; d.t_end = s.t_begin + s.len;
-        d.e = a.e; d.bs = a.bs; d.NB = a.NB; d.Ls = a.Ls;
-        d.gc_in = gc[j & 1]; d.gc_out = gc[(j + 1) & 1];
-        d.ST = a.ST; d.dST = a.dST; d.dg = a.dg;
-        d.B = a.B; d.T = a.T; d.H = a.H; d.HV = a.HV; d.K = a.K; d.V = a.V;
-        e = launch_dg_slab(d, stream);
+        const long nd = static_cast<long>(a.B) * a.HV * s.NCs * a.K;
+        hipLaunchKernelGGL(cbwd_dg_kernel, dim3(static_cast<unsigned>((nd + 255) / 256)), dim3(256), 0, stream, s,
+                           gc[j & 1], gc[(j + 1) & 1]);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

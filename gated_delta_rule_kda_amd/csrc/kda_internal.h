@@ -143,20 +143,15 @@ struct ChunkBwdArgs {
     float *dg, *dbeta;          // [B,T,HV,K], [B,T,HV]
     float *dS0;                 // [B,HV,K,V] or nullptr
     // workspace (fp32): see chunk_bwd_layout in kda_api.hip
-    float *ST, *snap1, *Dc, *snapc, *W, *U, *img, *dR, *dMs, *e, *bs, *gc;
+    float *ST, *snap1, *Dc, *snapc, *W, *U, *img, *dR, *dMs, *e, *cs, *gc;
     int Ls;                     // tokens per slab (a multiple of 32)
     int NS1;                    // slab starts kept by the first forward pass (slabs - 1)
-    int NB;                     // dg blocks per slab
     int B, T, H, HV, K, V;
     float scale;
 };
 hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream);
 // floats of one chunk's operand image (the chunked backward's pre-pass output)
 int chunk_bwd_image_floats(int K);
-// the dg reverse sum of one slab of the token-recurrent backward, shared with
-// the chunked backward (BwdArgs fields t_begin, t_end, e, bs, NB, Ls, gc_in,
-// gc_out, ST, dST, dg, B, T, HV, K, V)
-hipError_t launch_dg_slab(const BwdArgs &a, hipStream_t stream);
 
 constexpr int kBwdCols = 32;    // state columns per workgroup of the backward passes
 constexpr int kDgBlock = 64;    // tokens per block of the reverse sum that forms dg

@@ -604,18 +604,13 @@ hipError_t launch_slab(const BwdArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL(bwd_sum_kernel<false>, dim3(blocks_of(rows, 256 / a.K)), dim3(256), 0, stream, a);
         if (a.H != a.HV) hipLaunchKernelGGL(bwd_qk_kernel<false>, dim3(qk_blocks), dim3(256), 0, stream, a);
     }
-    return launch_dg_slab(a, stream);
-}
-
-}  // namespace
-
-hipError_t launch_dg_slab(const BwdArgs &a, hipStream_t stream) {
-    const int len = a.t_end - a.t_begin;
     const long nb = static_cast<long>(a.B) * a.HV * ((len + kDgBlock - 1) / kDgBlock) * a.K;
     hipLaunchKernelGGL(bwd_dg_blocks_kernel, dim3(blocks_of(nb, 256)), dim3(256), 0, stream, a);
     hipLaunchKernelGGL(bwd_dg_kernel, dim3(blocks_of(nb, 256)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
+
+}  // namespace
 
 hipError_t launch_backward(const BwdArgs &a0, hipStream_t stream) {
     if (a0.B == 0) return hipSuccess;

@@ -521,13 +521,13 @@ def test_chunk_bwd_workspace_size():
         # chunks: S_T, carried dS [B,HV,K,V]; slab starts [B,slabs-1,HV,K,V];
         # chunk-start states [B,NC-1,HV,K,V]; W, U, dR [B,Ls,HV,V]; operand
         # images [B,NC,HV,img]; dS per chunk [B,NC,HV,K,V]; dg terms
-        # [B,Ls,HV,K]; block sums [B,HV,Ls/64,K]; dg carry [2,B,HV,K]
+        # [B,Ls,HV,K]; their chunk sums [B,HV,NC,K]; dg carry [2,B,HV,K]
         Ls = 1024 if T > 1024 else max(32, -(-T // 32) * 32)
         NS1 = -(-T // Ls) - 1 if T > 0 else 0
         NC = Ls // 32
         return (2 * up(B * HV * K * V) + up(B * NS1 * HV * K * V) + up(B * (NC - 1) * HV * K * V)
                 + 3 * up(B * Ls * HV * V) + up(B * NC * HV * img(K)) + up(B * NC * HV * K * V)
-                + up(B * Ls * HV * K) + up(B * HV * -(-Ls // 64) * K) + up(2 * B * HV * K))
+                + up(B * Ls * HV * K) + up(B * HV * NC * K) + up(2 * B * HV * K))
     for args in [(2, 100, 2, 4, 64, 128), (1, 8192, 96, 96, 128, 128), (3, 2500, 1, 2, 32, 64),
                  (1, 1024, 1, 1, 128, 128), (1, 1025, 1, 1, 128, 128), (1, 1, 1, 1, 32, 32)]:
         B, T, H, HV, K, V = args
