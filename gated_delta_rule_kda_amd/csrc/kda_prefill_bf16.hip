@@ -74,6 +74,10 @@
 //    the same page, y = sigmoid(gate) o / sqrt(mean(o^2) + eps), to the bf16
 //    rows of o as the helper waves store them: the 16 lanes holding a row of
 //    128 values sum its squares by DPP within their row of lanes.
+//  * The chunked backward's forward pass (BWD, a snapshot instantiation):
+//    no o; W = v - (k Gamma) M and U of every chunk go to the workspace from
+//    the carry's registers (fp32), and the call may cover a sub-range of the
+//    sequences (t_off, Tseq) starting from a state with its own batch stride.
 
 #include "kda_internal.h"
 
