@@ -56,6 +56,8 @@
 // used as the B operand of the next product (dm, dU, dR) is already in that
 // order: its element j is row 4 kq + j.
 
+#include <mutex>
+
 #include "kda_internal.h"
 #include "kda_lanes.h"
 
@@ -887,31 +889,83 @@ hipError_t launch_dyn(F kern, unsigned grid, int lds, hipStream_t stream, const 
     return hipGetLastError();
 }
 
+template <int K>
+hipError_t launch_prep_k(const SlabArgs &s, hipStream_t stream) {
+    static_assert(prep_lds<K>() <= 160 * 1024, "LDS plan exceeds 160 KB");
+    return launch_dyn(cbwd_prep_kernel<K>, static_cast<unsigned>(s.a.B) * s.a.HV * s.NCs, prep_lds<K>(), stream, s);
+}
+// One workgroup per (b, hv) with all of V: the chain is bound by bringing in
+// each chunk's operand image, not by its matrix work, and a head split over
+// two workgroups reads the image twice (measured 0.3 ms slower per call on the
+// HV96 shape, where the forward does split V).
 template <int K, int V>
-hipError_t launch_slab_kernels(const SlabArgs &s, hipStream_t stream) {
-    static_assert(prep_lds<K>() <= 160 * 1024 && grad_lds<K, V>() <= 160 * 1024, "LDS plan exceeds 160 KB");
-    const ChunkBwdArgs &a = s.a;
-    hipError_t e = launch_dyn(cbwd_prep_kernel<K>, static_cast<unsigned>(a.B) * a.HV * s.NCs, prep_lds<K>(), stream, s);
-    if (e != hipSuccess) return e;
-    // One workgroup per (b, hv) with all of V: the chain is bound by bringing in
-    // each chunk's operand image, not by its matrix work, and a head split
-    // over two workgroups reads the image twice (measured 0.3 ms slower per
-    // call on the HV96 shape, where the forward does split V).
+hipError_t launch_chain_kv(const SlabArgs &s, hipStream_t stream) {
     static_assert(chain_lds<K, V>() <= 160 * 1024, "LDS plan exceeds 160 KB");
-    e = launch_dyn(cbwd_chain_kernel<K, V>, static_cast<unsigned>(a.B) * a.HV, chain_lds<K, V>(), stream, s);
-    if (e != hipSuccess) return e;
-    return launch_dyn(cbwd_grad_kernel<K, V>, static_cast<unsigned>(a.B) * a.H * s.NCs, grad_lds<K, V>(), stream, s,
+    return launch_dyn(cbwd_chain_kernel<K, V>, static_cast<unsigned>(s.a.B) * s.a.HV, chain_lds<K, V>(), stream, s);
+}
+template <int K, int V>
+hipError_t launch_grad_kv(const SlabArgs &s, hipStream_t stream) {
+    static_assert(grad_lds<K, V>() <= 160 * 1024, "LDS plan exceeds 160 KB");
+    return launch_dyn(cbwd_grad_kernel<K, V>, static_cast<unsigned>(s.a.B) * s.a.H * s.NCs, grad_lds<K, V>(), stream, s,
                       kThrG);
 }
-
+enum class Pass { prep, chain, grad };
+template <int K, int V>
+hipError_t launch_pass_kv(Pass p, const SlabArgs &s, hipStream_t stream) {
+    switch (p) {
+    case Pass::prep: return launch_prep_k<K>(s, stream);
+    case Pass::chain: return launch_chain_kv<K, V>(s, stream);
+    default: return launch_grad_kv<K, V>(s, stream);
+    }
+}
 template <int K>
-hipError_t launch_slab_k(const SlabArgs &s, hipStream_t stream) {
+hipError_t launch_pass_k(Pass p, const SlabArgs &s, hipStream_t stream) {
     switch (s.a.V) {
-    case 32: return launch_slab_kernels<K, 32>(s, stream);
-    case 64: return launch_slab_kernels<K, 64>(s, stream);
-    case 128: return launch_slab_kernels<K, 128>(s, stream);
+    case 32: return launch_pass_kv<K, 32>(p, s, stream);
+    case 64: return launch_pass_kv<K, 64>(p, s, stream);
+    case 128: return launch_pass_kv<K, 128>(p, s, stream);
     default: return hipErrorInvalidValue;
     }
+}
+hipError_t launch_pass(Pass p, const SlabArgs &s, hipStream_t stream) {
+    switch (s.a.K) {
+    case 32: return launch_pass_k<32>(p, s, stream);
+    case 64: return launch_pass_k<64>(p, s, stream);
+    case 128: return launch_pass_k<128>(p, s, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// The second stream of the backward (one per device, default priority,
+// created on first use) and the events that order it against the caller's.
+// The mutex makes one call's enqueue sequence atomic, so calls from several
+// host threads on one device do not interleave their event records.
+struct SideStream {
+    std::mutex mu;
+    hipStream_t y = nullptr;
+    hipEvent_t start = nullptr, st = nullptr, p0[2] = {}, prep[2] = {}, chain[2] = {}, grad[2] = {};
+};
+constexpr int kMaxDev = 64;
+SideStream g_side[kMaxDev];
+
+hipError_t side_stream(hipStream_t stream, SideStream **out) {
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    SideStream &ss = g_side[dev];
+    *out = &ss;
+    if (ss.y) return hipSuccess;
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    e = hipStreamCreateWithFlags(&ss.y, hipStreamNonBlocking);
+    hipEvent_t *evs[] = {&ss.start, &ss.st, &ss.p0[0], &ss.p0[1], &ss.prep[0], &ss.prep[1],
+                         &ss.chain[0], &ss.chain[1], &ss.grad[0], &ss.grad[1]};
+    for (hipEvent_t *ev : evs)
+        if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    return e != hipSuccess ? e : e2;
 }
 
 }  // namespace
@@ -920,6 +974,14 @@ int chunk_bwd_image_floats(int K) {
     return K == 32 ? Img<32>::floats : K == 64 ? Img<64>::floats : K == 128 ? Img<128>::floats : 0;
 }
 
+// Slab by slab from the last.  The caller's stream X runs the chain of state
+// gradients, the gradient pass and the dg sums in order; a second stream Y
+// runs what they consume and does not depend on them -- the whole-sequence
+// forward pass, then per slab its forward pass and the operand images --
+// ahead of X, on the CUs the chain leaves idle (one workgroup per head).
+// Y's per-slab outputs (chunk-start states, W, U, images) are double-buffered
+// by slab parity; Y overwrites a buffer only after X's pass of the slab two
+// before has read it.
 hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
     const size_t sKV = static_cast<size_t>(a.HV) * a.K * a.V;
@@ -930,6 +992,14 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         return a.dST ? hipMemcpyAsync(a.dS0, a.dST, bytes, hipMemcpyDeviceToDevice, stream)
                      : hipMemsetAsync(a.dS0, 0, bytes, stream);
     }
+    SideStream *ss = nullptr;
+    hipError_t e = side_stream(stream, &ss);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(ss->mu);
+    hipStream_t X = stream, Y = ss->y;
+#define KDA_TRY(x) do { const hipError_t e_ = (x); if (e_ != hipSuccess) return e_; } while (0)
+    KDA_TRY(hipEventRecord(ss->start, X));
+    KDA_TRY(hipStreamWaitEvent(Y, ss->start, 0));
     const int ns = (a.T + a.Ls - 1) / a.Ls;
     // 0. the whole sequence once: S_T and the states at the slab starts
     {
@@ -940,20 +1010,24 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         f.snap_chunks = a.Ls / kC; f.NS = ns - 1;
         f.B = a.B; f.T = a.T; f.H = a.H; f.HV = a.HV; f.K = a.K; f.V = a.V;
         f.scale = a.scale; f.bf16 = true; f.bwd = true;
-        const hipError_t e = launch_prefill_bf16(f, stream);
-        if (e != hipSuccess) return e;
+        KDA_TRY(launch_prefill_bf16(f, Y));
+        KDA_TRY(hipEventRecord(ss->st, Y));
     }
     float *gc[2] = {a.gc, a.gc + static_cast<size_t>(a.B) * a.HV * a.K};
     {
+        KDA_TRY(hipStreamWaitEvent(X, ss->st, 0));
         const long nk = static_cast<long>(a.B) * a.HV * a.K;
         hipLaunchKernelGGL(cbwd_dg_final_kernel, dim3(static_cast<unsigned>((nk + 255) / 256)), dim3(256), 0,
-                           stream, a, gc[0]);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+                           X, a, gc[0]);
+        KDA_TRY(hipGetLastError());
     }
     for (int si = ns - 1, j = 0; si >= 0; --si, ++j) {
+        const int p = si & 1;
         SlabArgs s{};
         s.a = a;
+        if (p) {
+            s.a.snapc = a.snapc2; s.a.W = a.W2; s.a.U = a.U2; s.a.img = a.img2;
+        }
         s.t_begin = si * a.Ls;
         s.len = min(a.T, s.t_begin + a.Ls) - s.t_begin;
         s.NCs = (s.len + kC - 1) / kC;
@@ -966,29 +1040,37 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         }
         s.dm_in = si == ns - 1 ? a.dST : a.Dc;
         s.dm_out = si == 0 ? a.dS0 : a.Dc;
-        // the slab's forward pass: states at its chunk starts, W and U
+        // Y: the slab's forward pass (states at its chunk starts, W, U) once the
+        // gradient pass of slab si + 2 has read these buffers
+        if (j >= 2) KDA_TRY(hipStreamWaitEvent(Y, ss->grad[p], 0));
         PrefillArgs f{};
         f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
         f.S0 = s.Sstart; f.s0_bstride = s.s_bstride;
-        f.snap = s.NCs > 1 ? a.snapc : nullptr;
+        f.snap = s.NCs > 1 ? s.a.snapc : nullptr;
         f.snap_chunks = 1; f.NS = s.NCs - 1;
-        f.w_out = a.W; f.u_out = a.U; f.Lw = a.Ls;
+        f.w_out = s.a.W; f.u_out = s.a.U; f.Lw = a.Ls;
         f.t_off = s.t_begin; f.Tseq = a.T;
         f.B = a.B; f.T = s.len; f.H = a.H; f.HV = a.HV; f.K = a.K; f.V = a.V;
         f.scale = a.scale; f.bf16 = true; f.bwd = true;
-        hipError_t e = launch_prefill_bf16(f, stream);
-        if (e != hipSuccess) return e;
-        e = a.K == 32 ? launch_slab_k<32>(s, stream)
-          : a.K == 64 ? launch_slab_k<64>(s, stream)
-          : a.K == 128 ? launch_slab_k<128>(s, stream) : hipErrorInvalidValue;
-        if (e != hipSuccess) return e;
-        // dg over the slab, carried to the slab before
+        KDA_TRY(launch_prefill_bf16(f, Y));
+        KDA_TRY(hipEventRecord(ss->p0[p], Y));
+        // Y: the operand images, once the chain of slab si + 2 has read them
+        if (j >= 2) KDA_TRY(hipStreamWaitEvent(Y, ss->chain[p], 0));
+        KDA_TRY(launch_pass(Pass::prep, s, Y));
+        KDA_TRY(hipEventRecord(ss->prep[p], Y));
+        // X: the chain, the gradient pass, dg (carried to the slab before)
+        KDA_TRY(hipStreamWaitEvent(X, ss->prep[p], 0));
+        KDA_TRY(launch_pass(Pass::chain, s, X));
+        KDA_TRY(hipEventRecord(ss->chain[p], X));
+        KDA_TRY(hipStreamWaitEvent(X, ss->p0[p], 0));
+        KDA_TRY(launch_pass(Pass::grad, s, X));
+        KDA_TRY(hipEventRecord(ss->grad[p], X));
         const long nd = static_cast<long>(a.B) * a.HV * s.NCs * a.K;
-        hipLaunchKernelGGL(cbwd_dg_kernel, dim3(static_cast<unsigned>((nd + 255) / 256)), dim3(256), 0, stream, s,
+        hipLaunchKernelGGL(cbwd_dg_kernel, dim3(static_cast<unsigned>((nd + 255) / 256)), dim3(256), 0, X, s,
                            gc[j & 1], gc[(j + 1) & 1]);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        KDA_TRY(hipGetLastError());
     }
+#undef KDA_TRY
     return hipSuccess;
 }
 

@@ -230,10 +230,14 @@ int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *
  * from the last: the forward over the slab again (the state at every chunk
  * start and the in-chunk solve's input and result), a chunk-parallel pass
  * forming the reverse chain's operands, the reverse chain of state gradients
- * (one workgroup per value head and V tile), a chunk-parallel pass for
- * dq, dk, dv, dbeta and the dg terms, and the reverse sum that forms dg; all
- * asynchronous on `stream`.  Workspace about 0.85 GB at B = 1, T = 8192,
- * HV = 96, K = V = 128.
+ * (one workgroup per value head), a chunk-parallel pass for dq, dk, dv, dbeta
+ * and the dg terms, and the reverse sum that forms dg.  The forward passes and
+ * the operand pass run on a second stream of the library's (one per device,
+ * default priority, created on the first call), ordered against `stream` by
+ * events; the call returns when all is enqueued, and work enqueued on
+ * `stream` afterwards runs after all of it.  Calls from several host threads
+ * on one device are serialized while they enqueue.  Workspace about 1.35 GB
+ * at B = 1, T = 8192, HV = 96, K = V = 128.
  * kda_chunk_bwd_workspace_size returns the workspace size in bytes, or -1
  * (message in kda_last_error) for sizes or a dtype kda_chunk_bwd rejects.
  */
