@@ -35,7 +35,7 @@ _lib = None
 KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EHIP = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_DIRECT, GATE_BOUNDED, GATE_SOFTPLUS = 0, 1, 2
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class KDAError(RuntimeError):
@@ -89,6 +89,10 @@ def _load():
             lib.kda_chunk_fwd_gated.restype = I
             lib.kda_recurrent_fwd.argtypes = [P] * 8 + [I] * 6 + [F, I, P]
             lib.kda_recurrent_fwd.restype = I
+            lib.kda_chunk_fwd_unbounded_workspace_size.argtypes = [I] * 7
+            lib.kda_chunk_fwd_unbounded_workspace_size.restype = ctypes.c_longlong
+            lib.kda_chunk_fwd_unbounded.argtypes = [P] * 8 + [I] * 6 + [F, I, P, ctypes.c_longlong, P]
+            lib.kda_chunk_fwd_unbounded.restype = I
             lib.kda_recurrent_bwd_workspace_size.argtypes = [I] * 6
             lib.kda_recurrent_bwd_workspace_size.restype = ctypes.c_longlong
             lib.kda_recurrent_bwd.argtypes = ([P] * 14 + [I] * 6 + [F, I, P, ctypes.c_longlong, P])
@@ -237,6 +241,38 @@ def recurrent_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(out),
             _ptr(final_state), B, T, H, HV, K, V, float(scale) if scale else 0.0,
             _dtype_code(q.dtype), _stream_handle(dev)))
+    return out, final_state
+
+
+def chunk_fwd_unbounded_workspace_size(B, T, H, HV, K, V, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace ``kda_chunk_fwd_unbounded`` needs for these sizes
+    (bf16 only)."""
+    n = _load().kda_chunk_fwd_unbounded_workspace_size(B, T, H, HV, K, V, _dtype_code(dtype))
+    if n < 0:
+        raise KDAError(KDA_EINVAL, _load().kda_last_error().decode(errors="replace"))
+    return n
+
+
+def chunk_fwd_unbounded(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
+                        *, out=None, final_state=None, workspace=None):
+    """``kda_chunk_fwd_unbounded``: :func:`chunk_fwd` for gates with no lower
+    bound (any g <= 0; each token's g floored at -17), on the matrix cores.
+    bf16 inputs only.  ``workspace``: a uint8 GPU tensor of at least
+    :func:`chunk_fwd_unbounded_workspace_size` bytes, else one is allocated."""
+    (B, T, H, HV, K, V), out, final_state = _prefill_args(
+        q, k, v, g, beta, initial_state, output_final_state, out, final_state)
+    dev = q.device
+    if workspace is None:
+        n = chunk_fwd_unbounded_workspace_size(B, T, H, HV, K, V, q.dtype)
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n > 0 else None
+    else:
+        _need(workspace, "workspace", torch.uint8, None, dev)
+    with torch.cuda.device(dev):
+        _check(_load().kda_chunk_fwd_unbounded(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(out),
+            _ptr(final_state), B, T, H, HV, K, V, float(scale) if scale else 0.0,
+            _dtype_code(q.dtype), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+            _stream_handle(dev)))
     return out, final_state
 
 

@@ -96,6 +96,16 @@ int prefill_sizes_ok(const char *fn, int B, int T, int H, int HV, int K, int V, 
 // intermediate in registers and LDS, so none of the built paths needs any.
 uint64_t prefill_workspace_bytes(int, int, int, int, int, int, int, int) { return 0; }
 
+// Workspace bytes of kda_chunk_fwd_unbounded: every chunk's in-chunk matrices
+// (kUnbImgElems bf16), [B, HV, NC]; sizes already validated.
+uint64_t unbounded_workspace_bytes(int B, int T, int HV) {
+    const uint64_t nc = (static_cast<uint64_t>(T) + 31) / 32;
+    return static_cast<uint64_t>(B) * HV * nc * kda::kUnbImgElems * 2;
+}
+
+// Which kernels a prefill entry point runs.
+enum class Path { chunk, recurrent, unbounded };
+
 // The fused layer stages of kda_chunk_fwd_gated (none when A_log is NULL).
 struct FusedStages {
     bool on = false;
@@ -109,10 +119,12 @@ int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, 
                    const float *beta, const float *initial_state, void *out, float *final_state,
                    float *snapshots, int snapshot_every, int B, int T, int H, int HV, int K,
                    int V, float scale, int chunk, int dtype, void *workspace,
-                   long long workspace_bytes, void *stream, bool recurrent = false,
+                   long long workspace_bytes, void *stream, Path path = Path::chunk,
                    const FusedStages &fs = FusedStages()) {
     g_err[0] = '\0';
     if (const int rc = prefill_sizes_ok(fn, B, T, H, HV, K, V, chunk, dtype)) return rc;
+    if (path == Path::unbounded && dtype != KDA_DTYPE_BF16)
+        return fail(KDA_EUNSUPPORTED, "%s: built for KDA_DTYPE_BF16 only (fp32 inputs: kda_recurrent_fwd)", fn);
     const bool fused = fs.on;
     if (fused) {
         if (dtype != KDA_DTYPE_BF16)
@@ -137,7 +149,9 @@ int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, 
         !count(nb, {B, T, HV}) || !count(ns, {B, HV, K, V}) || !count(nsn, {B, NS, HV, K, V}))
         return fail(KDA_EINVAL, "%s: tensor sizes overflow", fn);
     const bool work = (static_cast<int64_t>(B) * T) > 0;
-    const uint64_t ws_need = recurrent ? 0 : prefill_workspace_bytes(B, T, H, HV, K, V, chunk, dtype);
+    const uint64_t ws_need = path == Path::recurrent ? 0
+                             : path == Path::unbounded ? unbounded_workspace_bytes(B, T, HV)
+                                                       : prefill_workspace_bytes(B, T, H, HV, K, V, chunk, dtype);
     if (work) {
         if (!q || !k || !v || !g || !beta || !out)
             return fail(KDA_EINVAL, "%s: q, k, v, %s, %s and out must be non-NULL", fn, fused ? "z" : "g",
@@ -207,7 +221,10 @@ int chunk_fwd_impl(const char *fn, const void *q, const void *k, const void *v, 
     a.bf16 = dtype == KDA_DTYPE_BF16;
     a.A_log = fs.A_log; a.dt_bias = fs.dt_bias; a.lower_bound = fs.lower_bound;
     a.ogate = fs.ogate; a.og_eps = fs.og_eps;
-    const hipError_t e = recurrent ? kda::launch_recurrent(a, st) : kda::launch_prefill(a, st);
+    const hipError_t e = path == Path::recurrent ? kda::launch_recurrent(a, st)
+                         : path == Path::unbounded
+                             ? kda::launch_unbounded_prefill(a, static_cast<uint16_t *>(workspace), st)
+                             : kda::launch_prefill(a, st);
     if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KDA_OK;
 }
@@ -335,7 +352,7 @@ int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const float
     fs.ogate = out_gate; fs.og_eps = out_gate_eps;
     return chunk_fwd_impl("kda_chunk_fwd_gated", q, k, v, z, beta_logit, initial_state, out, final_state,
                           nullptr, 0, B, T, H, HV, K, V, scale, chunk, dtype, workspace, workspace_bytes,
-                          stream, false, fs);
+                          stream, Path::chunk, fs);
 }
 
 int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *g,
@@ -343,7 +360,33 @@ int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *
                       float *final_state, int B, int T, int H, int HV, int K, int V,
                       float scale, int dtype, void *stream) {
     return chunk_fwd_impl("kda_recurrent_fwd", q, k, v, g, beta, initial_state, out, final_state,
-                          nullptr, 0, B, T, H, HV, K, V, scale, 0, dtype, nullptr, 0, stream, true);
+                          nullptr, 0, B, T, H, HV, K, V, scale, 0, dtype, nullptr, 0, stream, Path::recurrent);
+}
+
+long long kda_chunk_fwd_unbounded_workspace_size(int B, int T, int H, int HV, int K, int V, int dtype) {
+    g_err[0] = '\0';
+    const char *fn = "kda_chunk_fwd_unbounded_workspace_size";
+    if (prefill_sizes_ok(fn, B, T, H, HV, K, V, 0, dtype) != KDA_OK) return -1;
+    if (dtype != KDA_DTYPE_BF16) {
+        fail(KDA_EUNSUPPORTED, "%s: built for KDA_DTYPE_BF16 only", fn);
+        return -1;
+    }
+    uint64_t n;
+    if (!count(n, {B, T, HV, K}) || !count(n, {B, T, HV, V}) || !count(n, {B, T / 32 + 1, HV, kda::kUnbImgElems})) {
+        fail(KDA_EINVAL, "%s: tensor sizes overflow", fn);
+        return -1;
+    }
+    return static_cast<long long>(unbounded_workspace_bytes(B, T, HV));
+}
+
+int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *initial_state, void *out,
+                            float *final_state, int B, int T, int H, int HV, int K, int V,
+                            float scale, int dtype, void *workspace, long long workspace_bytes,
+                            void *stream) {
+    return chunk_fwd_impl("kda_chunk_fwd_unbounded", q, k, v, g, beta, initial_state, out, final_state,
+                          nullptr, 0, B, T, H, HV, K, V, scale, 0, dtype, workspace, workspace_bytes,
+                          stream, Path::unbounded);
 }
 
 long long kda_recurrent_bwd_workspace_size(int B, int T, int H, int HV, int K, int V) {

@@ -47,7 +47,21 @@ struct PrefillArgs {
     int Lw;
     bool bwd;                   // the backward's forward pass: no o; W, U where set
     long long s0_bstride;       // elements between the sequences of S0 (0: HV K V)
+    // Gates without a lower bound (bf16 chunk kernel): the in-chunk matrices
+    // come from img ([B,HV,NC,kUnbImgElems] bf16, written by the pass of
+    // kda_unb_prep.hip) and the state products use forward-only decay factors.
+    const uint16_t *img;
+    bool unb;
 };
+
+// Floor of each token's log-decay on the unbounded chunked path (natural log):
+// e^-17 ~ 4e-8 of the state is the least a token keeps there.  With it, the
+// in-chunk factors around a reference row at most 4 tokens away stay within
+// [2^-98, 2^98].
+constexpr float kUnbFloor = -17.0f;
+// bf16 elements of one chunk's in-chunk matrices on that path (A_qk, -A21,
+// T11, T22, each as hi/lo pairs)
+constexpr int kUnbImgElems = 3584;
 
 // Arguments of one decode step.
 struct DecodeArgs {
@@ -169,6 +183,9 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_output_gate(const OutputGateArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t stream);
+// kda_chunk_fwd_unbounded: the in-chunk matrix pass into img, then the bf16
+// chunk kernel's unbounded instantiation
+hipError_t launch_unbounded_prefill(const PrefillArgs &a, uint16_t *img, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers

@@ -78,6 +78,14 @@
 //    no o; W = v - (k Gamma) M and U of every chunk go to the workspace from
 //    the carry's registers (fp32), and the call may cover a sub-range of the
 //    sequences (t_off, Tseq) starting from a state with its own batch stride.
+//  * Gates without a lower bound (UNB, for kda_chunk_fwd_unbounded): A_qk,
+//    -A21, T11 and T22 come from the chunk-parallel pass of kda_unb_prep.hip
+//    (an image per chunk in HBM, the layouts of sAqk, sA21 and sTi), which
+//    waves 4..7 copy into LDS where the other instantiations form them.  The
+//    operand pass applies the same per-token floor to g (kUnbFloor) and uses
+//    forward-only factors, each <= 1: q Gamma and k Gamma with Gamma_i =
+//    2^{G_i}, and k Lambda with Lambda_i = 2^{G_last - G_i} for the update.
+//    The carry holds M itself: M' = Gamma_last (.) M + (k Lambda)^T U.
 
 #include "kda_internal.h"
 
@@ -250,10 +258,11 @@ struct Plan {
 
 // SNAP: the variant that also writes prefix snapshots of the state (a
 // separate instantiation, so that the plain path carries none of its code).
-template <int K, int VT, bool SNAP, bool GATED, bool OG, bool BWD>
+template <int K, int VT, bool SNAP, bool GATED, bool OG, bool BWD, bool UNB>
 __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     static_assert(!OG || !SNAP, "the output gate is built for the plain prefill only");
     static_assert(!BWD || (SNAP && !GATED && !OG), "the backward's forward pass is a snapshot variant");
+    static_assert(!UNB || (!SNAP && !GATED && !OG && !BWD), "the unbounded gate is built for the plain prefill");
     using L = Plan<K>;
     static_assert(L::bytes + L::stage_bytes(VT) <= 160 * 1024, "LDS plan exceeds 160 KB");
     constexpr int LDO = VT + 8;   // bf16 rows of the o staging tile
@@ -393,6 +402,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     float gl[RPG][2];
     uint32_t qw[RPG], kw[RPG];
     float pl[2], og2[2];
+    float gl2[2];   // UNB: G_last (base 2) of the lane's columns
     auto op1a = [&](int buf, int ch) {
         const int lane = opaque_tid() & 63;
 #pragma unroll
@@ -425,6 +435,13 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                                    ? a.lower_bound * inv1p_exp2(__builtin_fmaf(gl[r][c], gsl, gof[c]))
                                    : 0.f;
         }
+        if constexpr (UNB) {
+#pragma unroll
+            for (int r = 0; r < RPG; ++r) {
+                gl[r][0] = fmaxf(gl[r][0], kUnbFloor);
+                gl[r][1] = fmaxf(gl[r][1], kUnbFloor);
+            }
+        }
 #pragma unroll
         for (int r = 1; r < RPG; ++r) {
             gl[r][0] += gl[r - 1][0];
@@ -451,13 +468,20 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             const float Gl = Gr + (rt[1] + rt[3]);
             const float before = drow == 0 ? 0.f : drow == 2 ? rt[0] : drow == 1 ? Gr : Gr + rt[1];
             const float off = before + (sc - gl[RPG - 1][c]);    // rows before the group
-            pr[c] = ex2(Gr * kLog2e);              // 2^{G_r}         >= 2^-116
-            pl[c] = ex2((Gl - Gr) * kLog2e);       // 2^{G_last - G_r} in [2^-116, 1]
-            og2[c] = (off - Gr) * kLog2e;
+            if constexpr (UNB) {
+                pr[c] = 1.f;
+                pl[c] = ex2(Gl * kLog2e);          // Gamma_last
+                gl2[c] = Gl * kLog2e;
+                og2[c] = off * kLog2e;
+            } else {
+                pr[c] = ex2(Gr * kLog2e);          // 2^{G_r}         >= 2^-116
+                pl[c] = ex2((Gl - Gr) * kLog2e);   // 2^{G_last - G_r} in [2^-116, 1]
+                og2[c] = (off - Gr) * kLog2e;
+            }
         }
         if (rg == 0) {
             *reinterpret_cast<float2 *>(sPl + buf * K + f0) = make_float2(pl[0], pl[1]);
-            *reinterpret_cast<float2 *>(sPr + f0) = make_float2(pr[0], pr[1]);
+            if constexpr (!UNB) *reinterpret_cast<float2 *>(sPr + f0) = make_float2(pr[0], pr[1]);
         }
     };
 
@@ -474,8 +498,9 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             float xlk[2], xlq[2], xr[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const float d = __builtin_fmaf(gl[r][c], kLog2e, og2[c]);   // G_i - G_r
-                const float e1 = ex2(d), e2 = ex2(-d);
+                // G_i - G_r (UNB: G_i, and the factors Gamma_i, Lambda_i)
+                const float d = __builtin_fmaf(gl[r][c], kLog2e, og2[c]);
+                const float e1 = ex2(d), e2 = UNB ? ex2(gl2[c] - d) : ex2(-d);
                 xlk[c] = kf[c] * e1;
                 xlq[c] = qf[c] * e1;
                 xr[c] = kf[c] * e2;
@@ -487,8 +512,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             st_word(sLq + at, hi);
             st_word(sLq + kC * LDK + at, lo);
             split2(xr[0], xr[1], rh[r], rl[r]);
-            st_word(sR + at, rh[r]);
-            st_word(sR + kC * LDK + at, rl[r]);
+            if constexpr (!UNB) {
+                st_word(sR + at, rh[r]);
+                st_word(sR + kC * LDK + at, rl[r]);
+            }
         }
         // (k e2)^T for the state update: the same bf16 halves, regrouped by
         // column (tokens 2w, 2w + 1 of column f0 + c in one word)
@@ -615,6 +642,47 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 const __bf16 hi = bf(x);
                 sA21[i * L16 + lr] = hi;
                 sA21[16 * L16 + i * L16 + lr] = bf(x - fl(hi));
+            }
+        }
+    };
+
+    // UNB: the chunk's in-chunk matrices from the image in HBM, 16 bytes per
+    // lane, waves 4..7 a quarter each, loaded a phase ahead like v
+    constexpr int kImgUnits = kUnbImgElems / 8;
+    uint4 pfi[UNB ? 2 : 1];
+    auto loadImg = [&](int ch) {
+        if constexpr (UNB) {
+            const int lane = opaque_tid() & 63;
+            const auto ri = make_rsrc(a.img + ((static_cast<size_t>(b) * HV + hv) * NC + ch) * kUnbImgElems,
+                                      ch < NC ? kUnbImgElems * 2 : 0);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int u = (4 * j + wave - 4) * 64 + lane;   // past the image: read as 0, not stored
+                const auto w = __builtin_amdgcn_raw_buffer_load_b128(ri, u * 16, 0, 0);
+                pfi[j] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    };
+    auto writeImg = [&]() {
+        if constexpr (UNB) {
+            const int lane = opaque_tid() & 63;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int u = (4 * j + wave - 4) * 64 + lane;
+                if (u < kImgUnits) {
+                    const int e = 8 * u;
+                    __bf16 *dst;
+                    if (e < 2048) {
+                        dst = sAqk + (e >> 10) * kC * LDC + ((e >> 5) & 31) * LDC + (e & 31);
+                    } else if (e < 2560) {
+                        const int f = e - 2048;
+                        dst = sA21 + (f >> 8) * 16 * L16 + ((f >> 4) & 15) * L16 + (f & 15);
+                    } else {
+                        const int f = e - 2560;
+                        dst = sTi + (f >> 8) * 16 * L16 + ((f >> 4) & 15) * L16 + (f & 15);
+                    }
+                    *reinterpret_cast<uint4 *>(dst) = pfi[j];
+                }
             }
         }
     };
@@ -933,6 +1001,15 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
                 kf[u] = ld8(kb_buf + (k0 + u) * 16 * LDC);
                 kfl[u] = ld8(kb_buf + K * LDC + (k0 + u) * 16 * LDC);
             }
+            if constexpr (UNB) {
+                // M' = Gamma_last (.) M + (k Lambda)^T U: the decay first
+#pragma unroll
+                for (int u = 0; u < KB; ++u) {
+                    const f32x4 plv = *reinterpret_cast<const f32x4 *>(plp + (k0 + u) * 16);
+#pragma unroll
+                    for (int gi = 0; gi < NG; ++gi) m[gi][k0 + u] *= plv;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < KB; ++u)
 #pragma unroll
@@ -945,20 +1022,23 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
             for (int u = 0; u < KB; ++u)
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) m[gi][k0 + u] = mfma(kfl[u], ubh[gi], m[gi][k0 + u]);
+            if constexpr (!UNB) {
 #pragma unroll
-            for (int u = 0; u < KB; ++u) {
-                const f32x4 plv = *reinterpret_cast<const f32x4 *>(plp + (k0 + u) * 16);
-                const f32x4 prv = *reinterpret_cast<const f32x4 *>(prp + (k0 + u) * 16);
+                for (int u = 0; u < KB; ++u) {
+                    const f32x4 plv = *reinterpret_cast<const f32x4 *>(plp + (k0 + u) * 16);
+                    const f32x4 prv = *reinterpret_cast<const f32x4 *>(prp + (k0 + u) * 16);
 #pragma unroll
-                for (int gi = 0; gi < NG; ++gi) {
-                    m[gi][k0 + u] *= plv;
-                    if (!last) m[gi][k0 + u] *= prv;
+                    for (int gi = 0; gi < NG; ++gi) {
+                        m[gi][k0 + u] *= plv;
+                        if (!last) m[gi][k0 + u] *= prv;
+                    }
                 }
             }
         }
     };
     // N of the first chunk: S0 scaled by its 2^{G_r}
     auto carryScaleState = [&]() {
+        if constexpr (UNB) return;   // the carry holds M itself
         const int lane = opaque_tid() & 63, lg = (lane >> 4) & 3;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
@@ -1042,7 +1122,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) m[gi][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (wave == 0) {
+        if (!UNB && wave == 0) {
             // rows 0-15 x columns 16-31 of A_qk lie above the diagonal: zero for every chunk
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1058,6 +1138,11 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         loadV(1);
         loadOG(0);
     }
+    if (UNB && wave >= 4) {
+        loadImg(0);
+        writeImg();
+        loadImg(1);
+    }
     if (opw) {
         load_prep(0);
         op1a(0, 0);
@@ -1066,7 +1151,7 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         op2(0);
     }
     lds_barrier();
-    if (wave >= 4) phaseAT(0);
+    if (!UNB && wave >= 4) phaseAT(0);
     if (carry) {
         carryScaleState();
         carryPX();
@@ -1095,7 +1180,12 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
         lds_barrier();
         // P2
         if (wave >= 4) {
-            phaseAT(nb);
+            if constexpr (UNB) {
+                writeImg();      // the in-chunk matrices of chunk n+1
+                loadImg(n + 2);
+            } else {
+                phaseAT(nb);
+            }
             if (wave != 6) {
                 storeO(n);
                 writeV();        // v of chunk n+1 for the next phase's carry
@@ -1123,10 +1213,10 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
     if (a.ST && carry) carryStore(a.ST + (static_cast<size_t>(b) * HV + hv) * K * V);
 }
 
-template <int K, int VT, bool SNAP, bool GATED, bool OG, bool BWD = false>
+template <int K, int VT, bool SNAP, bool GATED, bool OG, bool BWD = false, bool UNB = false>
 hipError_t launch_kvt_s(const PrefillArgs &a, hipStream_t stream) {
     using L = Plan<K>;
-    auto kern = prefill_bf16_kernel<K, VT, SNAP, GATED, OG, BWD>;
+    auto kern = prefill_bf16_kernel<K, VT, SNAP, GATED, OG, BWD, UNB>;
     constexpr int lds = L::bytes + L::stage_bytes(VT);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1139,6 +1229,7 @@ hipError_t launch_kvt_s(const PrefillArgs &a, hipStream_t stream) {
 template <int K, int VT>
 hipError_t launch_kvt(const PrefillArgs &a, hipStream_t stream) {
     if (a.bwd) return launch_kvt_s<K, VT, true, false, false, true>(a, stream);
+    if (a.unb) return launch_kvt_s<K, VT, false, false, false, false, true>(a, stream);
     if (a.snap) return launch_kvt_s<K, VT, true, false, false>(a, stream);
     if (!a.A_log) return launch_kvt_s<K, VT, false, false, false>(a, stream);
     // the fused gate; the output gate in the o stores when the workgroup

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 enum kda_status { KDA_OK = 0, KDA_EINVAL = 1, KDA_EUNSUPPORTED = 2, KDA_EHIP = 3 };
 
@@ -162,6 +162,41 @@ int kda_recurrent_fwd(const void *q, const void *k, const void *v, const float *
                       const float *beta, const float *initial_state, void *out,
                       float *final_state, int B, int T, int H, int HV, int K, int V,
                       float scale, int dtype, void *stream);
+
+/*
+ * kda_chunk_fwd_unbounded -- kda_chunk_fwd for gates with no lower bound, on
+ * the matrix cores: the chunk form of kda_chunk_fwd with the in-chunk decay
+ * factors split around several reference rows (none more than 4 tokens from
+ * the rows it serves) instead of one, so that no factor leaves fp32 however
+ * strongly a token decays -- for instance under the unbounded gate
+ * -exp(A_log) * softplus(z + dt_bias) of bounded_gate on the page
+ * "metrale_model_weights/kimi_k3_host/kda.rs" (no lower bound).  The in-chunk
+ * matrices of every chunk are formed first by a chunk-parallel pass into the
+ * workspace, then the chunk kernel carries the state.
+ *
+ *   g  [B, T, HV, K]  fp32, log-space decay; PRECONDITION g <= 0 (finite or
+ *      -inf).  Each token's g is floored at -17 first: a token that would keep
+ *      less than e^-17 (about 4e-8) of the state keeps exactly that much,
+ *      a change of at most 4e-8 of the state's magnitude per such token.
+ *   workspace  device scratch of workspace_bytes bytes owned by the caller,
+ *      16-byte aligned, disjoint from every other argument, at least
+ *      kda_chunk_fwd_unbounded_workspace_size(...) bytes (B * HV * ceil(T/32)
+ *      * 7168: bf16 in-chunk matrices of every chunk); its contents carry
+ *      nothing between calls (else KDA_EINVAL).
+ * q, k, v, beta, initial_state, out, final_state, sizes, scale and the
+ * errors are those of kda_chunk_fwd (chunk 32).  Built for KDA_DTYPE_BF16
+ * only: KDA_EUNSUPPORTED for KDA_DTYPE_F32, whose unbounded gates go to
+ * kda_recurrent_fwd.
+ *
+ * kda_chunk_fwd_unbounded_workspace_size returns those bytes for these sizes,
+ * or -1 with a message in kda_last_error for arguments the call rejects.
+ */
+long long kda_chunk_fwd_unbounded_workspace_size(int B, int T, int H, int HV, int K, int V, int dtype);
+int kda_chunk_fwd_unbounded(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *initial_state, void *out,
+                            float *final_state, int B, int T, int H, int HV, int K, int V,
+                            float scale, int dtype, void *workspace, long long workspace_bytes,
+                            void *stream);
 
 /*
  * kda_recurrent_bwd -- gradients of the forward pass (kda_recurrent_fwd, or

@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol():
                           "kda_chunk_fwd_snapshots", "kda_recurrent_fwd", "kda_prefill_prologue",
                           "kda_output_gate", "kda_decode_step", "kda_recurrent_bwd",
                           "kda_recurrent_bwd_workspace_size", "kda_recurrent_bwd_noalloc",
-                          "kda_chunk_bwd", "kda_chunk_bwd_workspace_size"}
+                          "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd_unbounded",
+                          "kda_chunk_fwd_unbounded_workspace_size"}
     L = ctypes.CDLL(kda.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -538,3 +539,58 @@ def test_chunk_bwd_workspace_size():
     assert L.kda_chunk_bwd_workspace_size(1, 8, 2, 4, 32, 32, 0) == -1
     assert "KDA_DTYPE_BF16" in L.kda_last_error().decode()
     assert L.kda_chunk_bwd_workspace_size(1, 8, 2, 3, 32, 32, 1) == -1
+
+
+def unb_call(**over):
+    """kda_chunk_fwd_unbounded with fake, disjoint pointers (each BIG apart)."""
+    a = dict(q=BIG, k=2 * BIG, v=3 * BIG, g=4 * BIG, beta=5 * BIG, s0=None, out=6 * BIG, st=None,
+             B=1, T=8, H=2, HV=4, K=32, V=32, scale=0.0, dtype=1, ws=7 * BIG, wsb=1 << 30)
+    a.update(over)
+    L = lib()
+    rc = L.kda_chunk_fwd_unbounded(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["out"], a["st"],
+                                   a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["scale"], a["dtype"],
+                                   a["ws"], a["wsb"], None)
+    return rc, L.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(HV=3), 1, "kda_chunk_fwd_unbounded: HV=3"),
+    (dict(K=16), 2, "32, 64 or 128"),
+    (dict(dtype=0), 2, "KDA_DTYPE_BF16 only"),
+    (dict(dtype=7), 2, "dtype"),
+    (dict(q=None), 1, "non-NULL"),
+    (dict(ws=None), 1, "needed"),
+    (dict(wsb=1000), 1, "needed"),
+    (dict(wsb=-1), 1, "workspace_bytes=-1"),
+    (dict(ws=7 * BIG + 8), 1, "workspace is not 16-byte aligned"),
+    (dict(ws=BIG + 64), 1, "workspace overlaps q"),
+    (dict(ws=6 * BIG + 64), 1, "workspace overlaps an output"),
+    (dict(out=4 * BIG + 64), 1, "out overlaps g"),
+    (dict(scale=float("inf")), 1, "infinite"),
+])
+def test_chunk_fwd_unbounded_rejects(over, code, msg):
+    rc, err = unb_call(**over)
+    assert rc == code, err
+    assert msg in err, err
+
+
+def test_chunk_fwd_unbounded_empty_is_noop():
+    rc, err = unb_call(B=0, q=None, k=None, v=None, g=None, beta=None, out=None, ws=None, wsb=0)
+    assert rc == 0, err
+    rc, err = unb_call(T=0, q=None, k=None, v=None, g=None, beta=None, out=None, ws=None, wsb=0)
+    assert rc == 0, err
+
+
+def test_chunk_fwd_unbounded_workspace_size():
+    """B * HV * ceil(T / 32) chunk images of 3584 bf16 (A_qk, -A21, T11, T22
+    as hi/lo pairs)."""
+    L = lib()
+    for B, T, H, HV, K, V in [(1, 8, 2, 4, 32, 32), (2, 33, 1, 3, 64, 128), (1, 8192, 96, 96, 128, 128),
+                              (8, 4096, 16, 64, 128, 128), (3, 0, 1, 1, 32, 32), (0, 5, 1, 1, 32, 32)]:
+        want = B * HV * ((T + 31) // 32) * 3584 * 2
+        assert L.kda_chunk_fwd_unbounded_workspace_size(B, T, H, HV, K, V, 1) == want
+        assert kda.chunk_fwd_unbounded_workspace_size(B, T, H, HV, K, V) == want
+    assert L.kda_chunk_fwd_unbounded_workspace_size(1, 8192, 96, 96, 128, 128, 1) < 180e6
+    assert L.kda_chunk_fwd_unbounded_workspace_size(1, 8, 2, 4, 32, 32, 0) == -1
+    assert "BF16 only" in L.kda_last_error().decode()
+    assert L.kda_chunk_fwd_unbounded_workspace_size(1, 8, 2, 3, 32, 32, 1) == -1
