@@ -16,8 +16,9 @@ Headline workload (one JSON line on stdout):
     with prefix snapshots of the state every 1024 and every 32 tokens
     (kda_chunk_fwd_snapshots; the snapshot stores count in the bytes), and the
     layer's per-token stages on the HV96 shape (kda_prefill_prologue,
-    kda_output_gate) against the HBM peak, kda_recurrent_fwd on the HV96
-    workload with an unbounded gate (against the fp32 vector peak), and the
+    kda_output_gate) against the HBM peak, the HV96 workload with an
+    unbounded gate (kda_chunk_fwd_unbounded against the HBM peak, and
+    kda_recurrent_fwd against the fp32 vector peak), and the
     backward on the HV96 workload: kda_chunk_bwd (fp32 matrix cores) and
     kda_recurrent_bwd (fp32 vector ALUs).
 Inputs are seeded synthetic tensors (gated_delta_rule_kda_amd.synth) created on
@@ -216,7 +217,8 @@ def cpu_baseline(inp, shape, budget_heads=None):
             "seconds": dt}
 
 
-def bench_prefill(shape, steps, warmup, tag, snapshot_every=None, inp=None, recurrent=False):
+def bench_prefill(shape, steps, warmup, tag, snapshot_every=None, inp=None, recurrent=False,
+                  unbounded=False):
     import torch
     import gated_delta_rule_kda_amd as kda
     from gated_delta_rule_kda_amd import synth
@@ -239,6 +241,14 @@ def bench_prefill(shape, steps, warmup, tag, snapshot_every=None, inp=None, recu
         def call():
             kda.recurrent_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                               initial_state=inp["S0"], out=out, final_state=ST)
+    elif unbounded:
+        ws = torch.empty(kda.chunk_fwd_unbounded_workspace_size(shape.B, shape.T, shape.H, shape.HV,
+                                                                shape.K, shape.V),
+                         dtype=torch.uint8, device=dev)
+
+        def call():
+            kda.chunk_fwd_unbounded(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                    initial_state=inp["S0"], out=out, final_state=ST, workspace=ws)
     else:
         def call():
             kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
@@ -261,7 +271,8 @@ def bench_prefill(shape, steps, warmup, tag, snapshot_every=None, inp=None, recu
     log("[%s] prefill avg %.4f ms (min %.4f, max %.4f), span %.3f ms, wall %.3f s" % (
         tag, avg_ms, min(ev_ms), max(ev_ms), total_ms, wall))
     return dict(inp=inp, avg_ms=avg_ms, min_ms=min(ev_ms), span_ms=total_ms,
-                bytes=nbytes, flops=flops, tokens=shape.B * shape.T)
+                bytes=nbytes, flops=flops, tokens=shape.B * shape.T,
+                workspace=ws.numel() if unbounded else 0)
 
 
 def bench_decode(shape, steps, warmup):
@@ -506,8 +517,9 @@ def main():
         return
     if args.only == "unbounded":
         sh = synth.PREFILL_HV96_BF16
-        bench_prefill(sh, args.steps, args.warmup, "hv96 unbounded gate, recurrent",
-                      inp=synth.make_prefill_inputs(sh, "cuda:0", 0, g_heavy=True), recurrent=True)
+        uinp = synth.make_prefill_inputs(sh, "cuda:0", 0, g_heavy=True)
+        bench_prefill(sh, args.steps, args.warmup, "hv96 unbounded gate, chunked", inp=uinp, unbounded=True)
+        bench_prefill(sh, args.steps, args.warmup, "hv96 unbounded gate, recurrent", inp=uinp, recurrent=True)
         return
     if args.only == "stages":
         bench_layer_stages(args.steps, args.warmup)
@@ -585,20 +597,35 @@ def main():
     if not args.no_unbounded:
         uinp = dict(p["inp"])
         uinp["g"] = synth.make_prefill_inputs(shape, "cuda:0", 0, g_heavy=True)["g"]
+        uc = bench_prefill(shape, max(3, args.steps // 2), args.warmup, "hv96 unbounded gate, chunked",
+                           inp=uinp, unbounded=True)
         ub = bench_prefill(shape, max(3, args.steps // 4), min(args.warmup, 3), "hv96 unbounded gate, recurrent",
                            inp=uinp, recurrent=True)
         del uinp
+        gc = uc["bytes"] / (uc["avg_ms"] * 1e-3) / 1e9
         tf = ub["flops"] / (ub["avg_ms"] * 1e-3) / 1e12
         line["prefill_unbounded_gate"] = {
-            "workload": "kda_recurrent_fwd on the HV96 workload with g = -exp(1.5 N(0,1)) (no lower bound; "
-                        "outside kda_chunk_fwd's -5 <= g <= 0)",
-            "tokens_per_s": ub["tokens"] / (ub["avg_ms"] * 1e-3), "avg_launch_ms": ub["avg_ms"],
-            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
-                         "frac": tf * 1e12 / FP32_VALU_PEAK,
-                         "peak_nonpacked": FP32_VALU_PEAK_NONPACKED / 1e12,
-                         "frac_nonpacked": tf * 1e12 / FP32_VALU_PEAK_NONPACKED,
-                         "flops_per_launch": ub["flops"]}}
-        del ub
+            "workload": "kda_chunk_fwd_unbounded on the HV96 workload with g = -exp(1.5 N(0,1)) (no lower "
+                        "bound; outside kda_chunk_fwd's -5 <= g <= 0): the in-chunk matrix pass, then the "
+                        "bf16 chunk kernel",
+            "tokens_per_s": uc["tokens"] / (uc["avg_ms"] * 1e-3), "avg_call_ms": uc["avg_ms"],
+            "workspace_bytes": uc["workspace"],
+            "roofline": {"bound": "hbm", "achieved": gc, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gc / HBM_PEAK_GBS, "alg_bytes_per_call": uc["bytes"],
+                         "kernels": "unb_prep_kernel<128> + prefill_bf16_kernel<128,64> (unbounded)"},
+            "mfma": {"alg_flops_per_call": uc["flops"],
+                     "achieved_tflops": uc["flops"] / (uc["avg_ms"] * 1e-3) / 1e12,
+                     "peak_tflops": BF16_MFMA_PEAK / 1e12,
+                     "frac": uc["flops"] / (uc["avg_ms"] * 1e-3) / BF16_MFMA_PEAK},
+            "recurrent": {
+                "workload": "kda_recurrent_fwd (token recurrence on the vector ALUs) on the same inputs",
+                "tokens_per_s": ub["tokens"] / (ub["avg_ms"] * 1e-3), "avg_launch_ms": ub["avg_ms"],
+                "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
+                             "frac": tf * 1e12 / FP32_VALU_PEAK,
+                             "peak_nonpacked": FP32_VALU_PEAK_NONPACKED / 1e12,
+                             "frac_nonpacked": tf * 1e12 / FP32_VALU_PEAK_NONPACKED,
+                             "flops_per_launch": ub["flops"]}}}
+        del ub, uc
     if not args.no_backward:
         bw = bench_backward(shape, max(3, args.steps // 4), min(args.warmup, 3), inp=p["inp"], chunked=True)
         tf = bw["flops"] / (bw["avg_ms"] * 1e-3) / 1e12

@@ -23,7 +23,8 @@
 // less than e^-17 (4e-8) of the state: such a token then keeps 4e-8 of it.
 // The chunk kernel applies the same floor to its own cumulative sums.
 //
-// One workgroup of 4 waves per (b, hv, chunk).  q, k and G go to LDS as fp32;
+// Workgroups of 4 waves, each taking chunks in turn with the next chunk's
+// loads in flight.  q, k go to LDS as loaded, G as fp32;
 // wave w forms the fp32 MFMA products (v_mfma_f32_16x16x4_f32) of family
 // F1, F2 (both 16-blocks in one 16x16 tile), F3 of rows 0..15, F3 of rows
 // 16..31, for A_qk and the raw A_kk at once; the factors are formed per
@@ -79,6 +80,10 @@ __device__ __forceinline__ float quad_bcast(float x, int p) {
     default: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xff, 0xf, 0xf, false));
     }
 }
+// Workgroup barrier for LDS hand-offs that, unlike __syncthreads(), does not
+// wait for outstanding global loads: the next chunk's prefetch stays in flight
+// across it (each register is waited for at its first use).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes), 0x00020000);
 }
@@ -87,206 +92,275 @@ struct UnbPrepArgs {
     const uint16_t *q, *k;      // [B,T,H,K] bf16
     const float *g, *beta;      // [B,T,HV,K], [B,T,HV]
     uint16_t *img;              // [B,HV,NC,kUnbImgElems] bf16
-    int T, H, HV, NC;
+    int B, T, H, HV, NC;
 };
 
 template <int K>
 struct UPlan {
-    static constexpr int LK = K + 4;
-    static constexpr int oQ = 0;                    // fp32 [C][LK] q
-    static constexpr int oK = oQ + kC * LK;         // fp32 [C][LK] k
-    static constexpr int oG = oK + kC * LK;         // fp32 [C][LK] G (base 2, floored g)
-    static constexpr int oAq = oG + kC * LK;        // fp32 [C][kLA] A_qk
-    static constexpr int oAk = oAq + kC * kLA;      // fp32 [C][kLA] A_kk without beta
-    static constexpr int oB = oAk + kC * kLA;       // fp32 [C] beta
-    static constexpr int floats = oB + kC;
+    static constexpr int LK = K + 4;    // fp32 rows of G
+    static constexpr int LKB = K + 8;   // bf16 rows of q, k
+    static constexpr int oQ = 0;                    // bf16 [C][LKB] q (as loaded)
+    static constexpr int oK = oQ + kC * LKB / 2;    // bf16 [C][LKB] k
+    static constexpr int oG = oK + kC * LKB / 2 > 2 * kC * kLA ? oK + kC * LKB / 2 : 2 * kC * kLA;
+                                                    // fp32 [C][LK] G (base 2, floored g)
+    static constexpr int oB = oG + kC * LK;         // fp32 [C] beta
+    static constexpr int floats = oB + kC;          // (offsets in floats)
+    // A_qk and A_kk (without beta), fp32 [C][kLA] each, over q and k (and
+    // below G) once the products have read them
+    static constexpr int oAq = oQ;
+    static constexpr int oAk = oAq + kC * kLA;
+    static_assert(2 * kC * kLA <= oG, "A arrays must fit below G");
 };
+
+// x of lane l - D within the lane's row of 16 (DPP row_shr:D)
+template <int D>
+__device__ __forceinline__ float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xf, 0xf, false));
+}
 
 template <int K>
 __global__ __launch_bounds__(kThrU) void unb_prep_kernel(UnbPrepArgs a) {
     using P = UPlan<K>;
-    constexpr int LK = P::LK;
+    constexpr int LK = P::LK, LKB = P::LKB;
     __shared__ __attribute__((aligned(16))) float sm[P::floats];
-    float *sQ = sm + P::oQ, *sK = sm + P::oK, *sG = sm + P::oG;
+    uint16_t *sQ = reinterpret_cast<uint16_t *>(sm + P::oQ), *sK = reinterpret_cast<uint16_t *>(sm + P::oK);
+    float *sG = sm + P::oG;
     float *sAq = sm + P::oAq, *sAk = sm + P::oAk, *sB = sm + P::oB;
 
     const int tid = static_cast<int>(threadIdx.x);
-    const int ch = static_cast<int>(blockIdx.x) % a.NC;
-    const int bhv = static_cast<int>(blockIdx.x) / a.NC;
-    const int b = bhv / a.HV, hv = bhv % a.HV;
-    const int h = hv / (a.HV / a.H);
-    const int t0 = ch * kC;
-    const int nv = min(kC, a.T - t0);   // valid tokens (>= 1)
-    const size_t tb = static_cast<size_t>(b) * a.T + t0;
-
-    // ---- loads: rows past the sequence end read 0 (an exact no-op token)
-    {
-        const int gs = a.HV * K, qs = a.H * K;
-        const auto rg = make_rsrc(a.g + (tb * a.HV + hv) * K, static_cast<uint32_t>(((nv - 1) * gs + K) * 4));
-        const auto rq = make_rsrc(a.q + (tb * a.H + h) * K, static_cast<uint32_t>(((nv - 1) * qs + K) * 2));
-        const auto rk = make_rsrc(a.k + (tb * a.H + h) * K, static_cast<uint32_t>(((nv - 1) * qs + K) * 2));
-        constexpr int G4 = kC * K / 4;
+    const long total = static_cast<long>(a.B) * a.HV * a.NC;
+    const int gs = a.HV * K, qs = a.H * K;
+    // Items in the order (b, chunk, value head), so that the workgroups running
+    // at a time read whole token rows of every head (DRAM pages stay open).
+    // Each workgroup takes items blockIdx.x, + gridDim.x, ...; the next
+    // chunk's q, k, g and beta are loaded into registers while the current
+    // one is processed.  Rows past the sequence end read 0 (an exact no-op
+    // token), and so does everything of an item past the last.
+    // g: thread (channel c, part p) holds rows p R .. p R + R - 1 of column c,
+    // the NP parts of a column in consecutive lanes.
+    constexpr int NP = kThrU / K, R = kC / NP;
+    static_assert(NP * K == kThrU && (NP == 2 || NP == 4 || NP == 8), "g parts per column");
+    constexpr int Q8 = kC * K / 8, QPT = (Q8 + kThrU - 1) / kThrU;  // 16-byte units of q, k per thread
+    const int gc = tid / NP, gp = tid % NP;
+    float pg[R];
+    u32x4 pq[QPT], pk[QPT];
+    uint32_t pb = 0;
+    auto load = [&](long item) {
+        long it = item < total ? item : 0;
+        const int hv = static_cast<int>(it % a.HV), bch = static_cast<int>(it / a.HV);
+        const int ch = bch % a.NC, b = bch / a.NC, h = hv / (a.HV / a.H);
+        const int t0 = ch * kC;
+        const int nv = item < total ? min(kC, a.T - t0) : 0;
+        const size_t tb = static_cast<size_t>(b) * a.T + t0;
+        const auto rg = make_rsrc(a.g + (tb * a.HV + hv) * K, nv ? static_cast<uint32_t>(((nv - 1) * gs + K) * 4) : 0u);
+        const auto rq = make_rsrc(a.q + (tb * a.H + h) * K, nv ? static_cast<uint32_t>(((nv - 1) * qs + K) * 2) : 0u);
+        const auto rk = make_rsrc(a.k + (tb * a.H + h) * K, nv ? static_cast<uint32_t>(((nv - 1) * qs + K) * 2) : 0u);
 #pragma unroll
-        for (int u = tid; u < G4; u += kThrU) {
-            const int row = u / (K / 4), c = (u % (K / 4)) * 4;
-            const auto w = __builtin_amdgcn_raw_buffer_load_b128(rg, (row * gs + c) * 4, 0, 0);
-            f32x4 x;
+        for (int r = 0; r < R; ++r)
+            pg[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, ((gp * R + r) * gs + gc) * 4, 0, 0));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = fmaxf(__uint_as_float(w[e]), kUnbFloor) * kLog2e;
-            *reinterpret_cast<f32x4 *>(sG + row * LK + c) = x;
-        }
-        constexpr int Q8 = kC * K / 8;
-#pragma unroll
-        for (int u = tid; u < Q8; u += kThrU) {
-            const int row = u / (K / 8), c = (u % (K / 8)) * 8;
-            const auto wq = __builtin_amdgcn_raw_buffer_load_b128(rq, (row * qs + c) * 2, 0, 0);
-            const auto wk = __builtin_amdgcn_raw_buffer_load_b128(rk, (row * qs + c) * 2, 0, 0);
-            f32x4 q0, q1, k0, k1;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                q0[2 * e] = bf_lo(wq[e]); q0[2 * e + 1] = bf_hi(wq[e]);
-                q1[2 * e] = bf_lo(wq[e + 2]); q1[2 * e + 1] = bf_hi(wq[e + 2]);
-                k0[2 * e] = bf_lo(wk[e]); k0[2 * e + 1] = bf_hi(wk[e]);
-                k1[2 * e] = bf_lo(wk[e + 2]); k1[2 * e + 1] = bf_hi(wk[e + 2]);
-            }
-            *reinterpret_cast<f32x4 *>(sQ + row * LK + c) = q0;
-            *reinterpret_cast<f32x4 *>(sQ + row * LK + c + 4) = q1;
-            *reinterpret_cast<f32x4 *>(sK + row * LK + c) = k0;
-            *reinterpret_cast<f32x4 *>(sK + row * LK + c + 4) = k1;
+        for (int j = 0; j < QPT; ++j) {
+            const int u = tid + j * kThrU, row = u / (K / 8), c = (u % (K / 8)) * 8;   // u >= Q8: row >= C, reads 0
+            pq[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, (row * qs + c) * 2, 0, 0);
+            pk[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, (row * qs + c) * 2, 0, 0);
         }
         if (tid < kC) {
-            const auto rb = make_rsrc(a.beta + tb * a.HV + hv, static_cast<uint32_t>(((nv - 1) * a.HV + 1) * 4));
-            sB[tid] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, tid * a.HV * 4, 0, 0));
+            const auto rb = make_rsrc(a.beta + tb * a.HV + hv, nv ? static_cast<uint32_t>(((nv - 1) * a.HV + 1) * 4) : 0u);
+            pb = __builtin_amdgcn_raw_buffer_load_b32(rb, tid * a.HV * 4, 0, 0);
         }
-        for (int u = tid; u < 2 * kC * kLA; u += kThrU) sAq[u] = 0.f;   // sAq, sAk are adjacent
-    }
-    __syncthreads();
-    // ---- G: inclusive sums over the chunk's tokens, one key channel per thread
-    for (int c = tid; c < K; c += kThrU) {
-        float col[kC];
+    };
+    // The loaded registers to LDS: q, k as loaded; G = the inclusive sums of
+    // floored g (base 2) over the chunk's tokens (within the thread's rows,
+    // then over the parts before it by DPP).
+    auto stage = [&]() {
+        float run = 0.f;
 #pragma unroll
-        for (int i = 0; i < kC; ++i) col[i] = sG[i * LK + c];
-#pragma unroll
-        for (int i = 1; i < kC; ++i) col[i] += col[i - 1];
-#pragma unroll
-        for (int i = 0; i < kC; ++i) sG[i * LK + c] = col[i];
-    }
-    __syncthreads();
-
-    // ---- products.  Lane (x, kq): A operand row ri (reference rr), B operand
-    // row cj (reference rc); reduction steps k0 + 4 kq + j.
-    const int wave = tid >> 6, lane = tid & 63, x = lane & 15, kq = lane >> 4;
-    {
-        int ri, rr, cj, rc;
-        if (wave == 0) {
-            ri = 16 + x; rr = 15; cj = x; rc = 15;
-        } else if (wave == 1) {
-            ri = x < 8 ? 8 + x : 16 + x; rr = x < 8 ? 7 : 23;
-            cj = x < 8 ? x : 8 + x; rc = rr;
-        } else {
-            const int o = 16 * (wave - 2);
-            ri = o + x; rr = o + (x < 8 ? 3 : 11);
-            cj = ri; rc = rr;
+        for (int r = 0; r < R; ++r) {
+            run += fmaxf(pg[r], kUnbFloor) * kLog2e;
+            pg[r] = run;
         }
-        f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = aq;
-#pragma unroll 2
-        for (int k0 = 0; k0 < K; k0 += 16) {
-            const int c = k0 + 4 * kq;
-            const f32x4 q4 = ld4(sQ + ri * LK + c), k4 = ld4(sK + ri * LK + c);
-            const f32x4 g4 = ld4(sG + ri * LK + c), gr4 = ld4(sG + rr * LK + c);
-            const f32x4 kc4 = ld4(sK + cj * LK + c), gc4 = ld4(sG + cj * LK + c), gcr4 = ld4(sG + rc * LK + c);
+        float incl = run;
+        if constexpr (NP > 1) { const float y = row_shr<1>(incl); if (gp >= 1) incl += y; }
+        if constexpr (NP > 2) { const float y = row_shr<2>(incl); if (gp >= 2) incl += y; }
+        if constexpr (NP > 4) { const float y = row_shr<4>(incl); if (gp >= 4) incl += y; }
+        const float before = incl - run;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float er = ex2(g4[j] - gr4[j]), ec = ex2(gcr4[j] - gc4[j]);
-                const float bk = kc4[j] * ec;
-                aq = mma4(q4[j] * er, bk, aq);
-                ak = mma4(k4[j] * er, bk, ak);
+        for (int r = 0; r < R; ++r) sG[(gp * R + r) * LK + gc] = pg[r] + before;
+#pragma unroll
+        for (int j = 0; j < QPT; ++j) {
+            const int u = tid + j * kThrU, row = u / (K / 8), c = (u % (K / 8)) * 8;
+            if (u < Q8) {
+                *reinterpret_cast<u32x4 *>(sQ + row * LKB + c) = pq[j];
+                *reinterpret_cast<u32x4 *>(sK + row * LKB + c) = pk[j];
             }
         }
-        // element j: tile row r = 4 kq + j, tile column x
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * kq + j;
+        if (tid < kC) sB[tid] = __uint_as_float(pb);
+    };
+    // 4 bf16 of a row of q or k as fp32
+    auto ldb4 = [](const uint16_t *p) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(p);
+        return f32x4{bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y)};
+    };
+
+    load(blockIdx.x);
+    for (long item = blockIdx.x; item < total; item += gridDim.x) {
+        lds_barrier();   // the previous item's outputs have read the LDS
+        stage();
+        load(item + gridDim.x);
+        lds_barrier();
+
+        // ---- products.  Lane (x, kq): A operand row ri (reference rr), B operand
+        // row cj (reference rc); reduction steps k0 + 4 kq + j.
+        const int wave = tid >> 6, lane = tid & 63, x = lane & 15, kq = lane >> 4;
+        {
+            int ri, rr, cj, rc;
             if (wave == 0) {
-                sAq[(16 + r) * kLA + x] = aq[j];
-                sAk[(16 + r) * kLA + x] = ak[j];
-            } else if ((r < 8) == (x < 8)) {
-                if (wave == 1) {
-                    const int i = r < 8 ? 8 + r : 16 + r, jj = x < 8 ? x : 8 + x;
-                    sAq[i * kLA + jj] = aq[j];
-                    sAk[i * kLA + jj] = ak[j];
+                ri = 16 + x; rr = 15; cj = x; rc = 15;
+            } else if (wave == 1) {
+                ri = x < 8 ? 8 + x : 16 + x; rr = x < 8 ? 7 : 23;
+                cj = x < 8 ? x : 8 + x; rc = rr;
+            } else {
+                const int o = 16 * (wave - 2);
+                ri = o + x; rr = o + (x < 8 ? 3 : 11);
+                cj = ri; rc = rr;
+            }
+            f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = aq;
+            if (wave >= 2) {
+                // F3: both operands from the same rows and reference rows
+#pragma unroll 2
+                for (int k0 = 0; k0 < K; k0 += 16) {
+                    const int c = k0 + 4 * kq;
+                    const f32x4 q4 = ldb4(sQ + ri * LKB + c), k4 = ldb4(sK + ri * LKB + c);
+                    const f32x4 g4 = ld4(sG + ri * LK + c), gr4 = ld4(sG + rr * LK + c);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float er = ex2(g4[j] - gr4[j]), ec = ex2(gr4[j] - g4[j]);
+                        const float bk = k4[j] * ec;
+                        aq = mma4(q4[j] * er, bk, aq);
+                        ak = mma4(k4[j] * er, bk, ak);
+                    }
+                }
+            } else {
+#pragma unroll 2
+                for (int k0 = 0; k0 < K; k0 += 16) {
+                    const int c = k0 + 4 * kq;
+                    const f32x4 q4 = ldb4(sQ + ri * LKB + c), k4 = ldb4(sK + ri * LKB + c);
+                    const f32x4 g4 = ld4(sG + ri * LK + c), gr4 = ld4(sG + rr * LK + c);
+                    const f32x4 kc4 = ldb4(sK + cj * LKB + c), gc4 = ld4(sG + cj * LK + c);
+                    const f32x4 gcr4 = ld4(sG + rc * LK + c);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float er = ex2(g4[j] - gr4[j]), ec = ex2(gcr4[j] - gc4[j]);
+                        const float bk = kc4[j] * ec;
+                        aq = mma4(q4[j] * er, bk, aq);
+                        ak = mma4(k4[j] * er, bk, ak);
+                    }
+                }
+            }
+            // element j: tile row r = 4 kq + j, tile column x.  Every entry of
+            // A_qk and of the blocks of A_kk the outputs read is written, zeros
+            // included: A_qk's upper right tile by F1, the entries above the
+            // diagonal of each 16x16 diagonal block by F3.
+            lds_barrier();   // q and k are read: A goes over them
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * kq + j;
+                if (wave == 0) {
+                    sAq[(16 + r) * kLA + x] = aq[j];
+                    sAk[(16 + r) * kLA + x] = ak[j];
+                    sAq[r * kLA + 16 + x] = 0.f;
+                } else if (wave == 1) {
+                    if ((r < 8) == (x < 8)) {
+                        const int i = r < 8 ? 8 + r : 16 + r, jj = x < 8 ? x : 8 + x;
+                        sAq[i * kLA + jj] = aq[j];
+                        sAk[i * kLA + jj] = ak[j];
+                    }
                 } else {
-                    const int o = 16 * (wave - 2);
-                    if (x <= r) sAq[(o + r) * kLA + o + x] = aq[j];
-                    if (x < r) sAk[(o + r) * kLA + o + x] = ak[j];
+                    const int o = 16 * (wave - 2), at = (o + r) * kLA + o + x;
+                    if ((r < 8) == (x < 8)) {
+                        sAq[at] = x <= r ? aq[j] : 0.f;
+                        sAk[at] = x < r ? ak[j] : 0.f;
+                    } else if (r < 8) {
+                        sAq[at] = 0.f;
+                        sAk[at] = 0.f;
+                    }
                 }
             }
         }
-    }
-    __syncthreads();
+        lds_barrier();
 
-    // ---- outputs
-    uint16_t *img = a.img + (static_cast<size_t>(bhv) * a.NC + ch) * kUnbImgElems;
-    if (wave < 2) {
-        // T_blk = (I + diag(beta) A_blk)^-1, A_blk the strictly lower diagonal
-        // block `wave` of A_kk.  Row i of T solves x^T (I + A_blk) = e_i^T,
-        // swept k = 15 .. 1: once x_k is final it is removed from every earlier
-        // column.  Lane = (row i, quarter q) holds x_{4q..4q+3}; x_k comes from
-        // its row's lane k / 4.
-        const int o = 16 * wave, i = lane >> 2, q = lane & 3;
-        float xv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) xv[e] = (4 * q + e == i) ? 1.f : 0.f;
-#pragma unroll
-        for (int kk = 15; kk >= 1; --kk) {
-            const f32x4 av = ld4(sAk + (o + kk) * kLA + o + 4 * q);
-            const float xk = quad_bcast(xv[kk % 4], kk / 4) * sB[o + kk];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) xv[e] -= av[e] * xk;
+        // ---- outputs
+        uint16_t *img;
+        {
+            const int hv = static_cast<int>(item % a.HV), bch = static_cast<int>(item / a.HV);
+            img = a.img + ((static_cast<size_t>(bch / a.NC) * a.HV + hv) * a.NC + bch % a.NC) * kUnbImgElems;
         }
-        uint32_t hw[2], lw[2];
-        split2(xv[0], xv[1], hw[0], lw[0]);
-        split2(xv[2], xv[3], hw[1], lw[1]);
-        uint16_t *dst = img + 2560 + wave * 512 + i * 16 + 4 * q;
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(hw[0], hw[1]);
-        *reinterpret_cast<uint2 *>(dst + 256) = make_uint2(lw[0], lw[1]);
-    } else if (wave == 2) {
-        // -A21 = -diag(beta) A_kk(rows 16..31, columns 0..15)
-        const int i = lane >> 2, q = lane & 3;
-        const f32x4 av = ld4(sAk + (16 + i) * kLA + 4 * q);
-        const float nb = -sB[16 + i];
-        uint32_t hw[2], lw[2];
-        split2(nb * av[0], nb * av[1], hw[0], lw[0]);
-        split2(nb * av[2], nb * av[3], hw[1], lw[1]);
-        uint16_t *dst = img + 2048 + i * 16 + 4 * q;
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(hw[0], hw[1]);
-        *reinterpret_cast<uint2 *>(dst + 256) = make_uint2(lw[0], lw[1]);
-    } else {
-        // A_qk row i, positions 16 hh .. 16 hh + 15: position p = 8 g + 4 h' + e
-        // holds column 16 h' + 4 g + e
-        const int i = lane >> 1, hh = lane & 1;
-        uint32_t hw[8], lw[8];
+        if (wave < 2) {
+            // T_blk = (I + diag(beta) A_blk)^-1, A_blk the strictly lower diagonal
+            // block `wave` of A_kk.  Row i of T solves x^T (I + A_blk) = e_i^T,
+            // swept k = 15 .. 1: once x_k is final it is removed from every earlier
+            // column.  Lane = (row i, quarter q) holds x_{4q..4q+3}; x_k comes from
+            // its row's lane k / 4.
+            const int o = 16 * wave, i = lane >> 2, q = lane & 3;
+            float xv[4];
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            float v2[2];
+            for (int e = 0; e < 4; ++e) xv[e] = (4 * q + e == i) ? 1.f : 0.f;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int p = 16 * hh + 2 * w + s;
-                const int c = 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3);
-                v2[s] = sAq[i * kLA + c];
+            for (int kk = 15; kk >= 1; --kk) {
+                const f32x4 av = ld4(sAk + (o + kk) * kLA + o + 4 * q);
+                const float xk = quad_bcast(xv[kk % 4], kk / 4) * sB[o + kk];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xv[e] -= av[e] * xk;
             }
-            split2(v2[0], v2[1], hw[w], lw[w]);
+            uint32_t hw[2], lw[2];
+            split2(xv[0], xv[1], hw[0], lw[0]);
+            split2(xv[2], xv[3], hw[1], lw[1]);
+            uint16_t *dst = img + 2560 + wave * 512 + i * 16 + 4 * q;
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(hw[0], hw[1]);
+            *reinterpret_cast<uint2 *>(dst + 256) = make_uint2(lw[0], lw[1]);
+        } else if (wave == 2) {
+            // -A21 = -diag(beta) A_kk(rows 16..31, columns 0..15)
+            const int i = lane >> 2, q = lane & 3;
+            const f32x4 av = ld4(sAk + (16 + i) * kLA + 4 * q);
+            const float nb = -sB[16 + i];
+            uint32_t hw[2], lw[2];
+            split2(nb * av[0], nb * av[1], hw[0], lw[0]);
+            split2(nb * av[2], nb * av[3], hw[1], lw[1]);
+            uint16_t *dst = img + 2048 + i * 16 + 4 * q;
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(hw[0], hw[1]);
+            *reinterpret_cast<uint2 *>(dst + 256) = make_uint2(lw[0], lw[1]);
+        } else {
+            // A_qk row i, positions 16 hh .. 16 hh + 15: position p = 8 g + 4 h' + e
+            // holds column 16 h' + 4 g + e
+            // (runs of four: positions 16 hh + 4 m .. + 3 hold columns
+            // 8 hh + {0, 16, 4, 20}[m] .. + 3)
+            const int i = lane >> 1, hh = lane & 1;
+            f32x4 run[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) run[m] = ld4(sAq + i * kLA + 8 * hh + 16 * (m & 1) + 4 * (m >> 1));
+            uint32_t hw[8], lw[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) split2(run[w >> 1][2 * (w & 1)], run[w >> 1][2 * (w & 1) + 1], hw[w], lw[w]);
+            uint16_t *dst = img + i * 32 + 16 * hh;
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            *reinterpret_cast<uint4 *>(dst + 8) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+            *reinterpret_cast<uint4 *>(dst + 1024) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            *reinterpret_cast<uint4 *>(dst + 1032) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
         }
-        uint16_t *dst = img + i * 32 + 16 * hh;
-        *reinterpret_cast<uint4 *>(dst) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4 *>(dst + 8) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-        *reinterpret_cast<uint4 *>(dst + 1024) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        *reinterpret_cast<uint4 *>(dst + 1032) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
     }
 }
 
+// Workgroups: as many as are resident on the device at once, at most one per
+// chunk.
 template <int K>
-hipError_t launch_prep_k(const UnbPrepArgs &u, long blocks, hipStream_t stream) {
+hipError_t launch_prep_k(const UnbPrepArgs &u, long items, hipStream_t stream) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, unb_prep_kernel<K>, kThrU, 0);
+    if (e != hipSuccess) return e;
+    const long resident = static_cast<long>(cus) * (per_cu > 0 ? per_cu : 1);
+    const long blocks = items < resident ? items : resident;
     hipLaunchKernelGGL(unb_prep_kernel<K>, dim3(static_cast<unsigned>(blocks)), dim3(kThrU), 0, stream, u);
     return hipGetLastError();
 }
@@ -300,7 +374,7 @@ hipError_t launch_unbounded_prefill(const PrefillArgs &a, uint16_t *img, hipStre
     u.q = static_cast<const uint16_t *>(a.q);
     u.k = static_cast<const uint16_t *>(a.k);
     u.g = a.g; u.beta = a.beta; u.img = img;
-    u.T = a.T; u.H = a.H; u.HV = a.HV; u.NC = (a.T + kC - 1) / kC;
+    u.B = a.B; u.T = a.T; u.H = a.H; u.HV = a.HV; u.NC = (a.T + kC - 1) / kC;
     const long blocks = static_cast<long>(a.B) * a.HV * u.NC;
     hipError_t e = a.K == 32 ? launch_prep_k<32>(u, blocks, stream)
                  : a.K == 64 ? launch_prep_k<64>(u, blocks, stream)
