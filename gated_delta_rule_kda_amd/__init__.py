@@ -432,17 +432,19 @@ def chunk_fwd_gated(q, k, v, z, beta_logit, A_log, dt_bias, gate_lower_bound=-5.
 
 
 class _KDA(torch.autograd.Function):
-    """Forward by kda_chunk_fwd (chunked) or kda_recurrent_fwd, backward by
-    kda_chunk_bwd (chunked forward, bf16) or kda_recurrent_bwd: all compute
-    the same function and its gradients."""
+    """Forward by kda_chunk_fwd (chunked, bounded gate), kda_chunk_fwd_unbounded
+    (chunked, bf16, any g <= 0) or kda_recurrent_fwd; backward by kda_chunk_bwd
+    (after a chunked bf16 forward with the bounded gate) or kda_recurrent_bwd:
+    all compute the same function and its gradients."""
 
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, initial_state, scale, chunked):
-        fwd = chunk_fwd if chunked else recurrent_fwd
+    def forward(ctx, q, k, v, g, beta, initial_state, scale, chunked, bounded_gate):
+        unbounded = chunked and not bounded_gate and q.dtype == torch.bfloat16
+        fwd = chunk_fwd_unbounded if unbounded else chunk_fwd if chunked and bounded_gate else recurrent_fwd
         o, S = fwd(q, k, v, g, beta, scale=scale, initial_state=initial_state, output_final_state=True)
         ctx.save_for_backward(q, k, v, g, beta, initial_state)
         ctx.scale = scale
-        ctx.chunked = chunked and q.dtype == torch.bfloat16
+        ctx.chunked = chunked and bounded_gate and q.dtype == torch.bfloat16
         return o, S
 
     @staticmethod
@@ -453,17 +455,22 @@ class _KDA(torch.autograd.Function):
         bwd = chunk_bwd if ctx.chunked else recurrent_bwd
         dq, dk, dv, dg, db, dS0 = bwd(q, k, v, g, beta, do, dS, scale=ctx.scale, initial_state=S0,
                                       need_d_initial_state=S0 is not None)
-        return dq, dk, dv, dg, db, dS0, None, None
+        return dq, dk, dv, dg, db, dS0, None, None, None
 
 
-def kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False, *, chunked=True):
+def kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False, *, chunked=True,
+        bounded_gate=True):
     """KDA forward with autograd: the interface of naive_kda on the
     "K3/kda/ops/reference/recurrent.py" page.  Returns (o, final state or
-    None); gradients reach q, k, v, g, beta and initial_state.  ``chunked``
-    picks kda_chunk_fwd (needs -5 <= g <= 0) or kda_recurrent_fwd (any g)
-    for the forward; the backward is kda_chunk_bwd after a chunked bf16
-    forward, else kda_recurrent_bwd."""
-    o, S = _KDA.apply(q, k, v, g, beta, initial_state, scale, chunked)
+    None); gradients reach q, k, v, g, beta and initial_state.  The forward:
+    chunked with ``bounded_gate`` (-5 <= g <= 0), kda_chunk_fwd; chunked
+    without it, kda_chunk_fwd_unbounded for bf16 inputs (any g <= 0, each
+    token's g floored at -17) and kda_recurrent_fwd for fp32; not chunked,
+    kda_recurrent_fwd (any g).  The backward is kda_chunk_bwd after a chunked
+    bf16 forward with the bounded gate, else kda_recurrent_bwd (which takes g
+    as given: where the forward floored it, the two differ by the gradient of
+    less than e^-17 of the state)."""
+    o, S = _KDA.apply(q, k, v, g, beta, initial_state, scale, chunked, bounded_gate)
     return o, (S if output_final_state else None)
 
 

@@ -191,3 +191,27 @@ def test_full_size_hv96_unbounded_chunk_sampled():
         say("   head", hv, assert_close(o[:, :, hv:hv + 1], oref, torch.bfloat16, True,
                                        "HV96 unbounded chunked o head %d" % hv))
         assert_close(S[:, hv:hv + 1], Sref, torch.bfloat16, False, "HV96 unbounded chunked S head %d" % hv)
+
+
+def test_autograd_unbounded_gate():
+    """kda.kda(..., bounded_gate=False): the chunked unbounded forward under
+    torch.autograd with the token-recurrent backward; outputs and gradients
+    of L = sum(o * Wo) + sum(S_T * WS) against the oracle, with g = -exp(1.5 N(0,1))."""
+    shape = synth.PrefillShape(2, 45, 1, 2, 64, 64, torch.bfloat16, "normal", s0_std=0.3)
+    inp = synth.make_prefill_inputs(shape, DEV, 31)
+    inp["g"] = gates(shape, 31, "heavy")
+    gen = torch.Generator(device="cpu").manual_seed(32)
+    Wo = torch.randn(2, 45, 2, 64, generator=gen).to(torch.bfloat16).to(DEV)
+    WS = (torch.randn(2, 2, 64, 64, generator=gen) * 0.1).to(DEV)
+    leaves = {n: inp[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g", "beta", "S0")}
+    o, S = kda.kda(leaves["q"], leaves["k"], leaves["v"], leaves["g"], leaves["beta"],
+                   initial_state=leaves["S0"], output_final_state=True, bounded_gate=False)
+    ((o.float() * Wo.float()).sum() + (S * WS).sum()).backward()
+    torch.cuda.synchronize()
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    oref, Sref = oracle.kda_fwd(*args, initial_state=inp["S0"])
+    assert_close(o, oref, torch.bfloat16, True, "autograd unbounded o")
+    ref = oracle.kda_bwd(*args, Wo, WS, initial_state=inp["S0"])
+    for name, want, st in zip(("q", "k", "v", "g", "beta", "S0"), ref, (True, True, True, False, False, False)):
+        assert leaves[name].grad is not None, name
+        assert_close(leaves[name].grad, want, torch.bfloat16, st, "autograd unbounded d%s" % name)
