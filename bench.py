@@ -425,10 +425,12 @@ def backward_alg_flops(B, T, HV, K, V):
     return 15 * K * V * B * T * HV
 
 
-def bench_backward(shape, steps, warmup, inp=None, chunked=True):
+def bench_backward(shape, steps, warmup, inp=None, chunked=True, saved=False):
     """kda_chunk_bwd (chunked) or kda_recurrent_bwd on `shape` with dL/do ~
     N(0,1) and dL/dS_T ~ 0.1 N(0,1); workspace and outputs allocated before the
-    timed region."""
+    timed region.  saved: kda_chunk_bwd_saved, given the states every 1024
+    tokens and the final state of a kda_chunk_fwd_snapshots call made before
+    the timed region (the forward a training step has already run)."""
     import torch
     import gated_delta_rule_kda_amd as kda
     from gated_delta_rule_kda_amd import synth
@@ -449,9 +451,14 @@ def bench_backward(shape, steps, warmup, inp=None, chunked=True):
             torch.empty(B, T, HV, K, device=dev), torch.empty(B, T, HV, device=dev),
             torch.empty(B, HV, K, V, device=dev))
     args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], dout, dST)
+    kw = {}
+    if saved:
+        _, ST, snaps = kda.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], 1024,
+                                               initial_state=inp["S0"], output_final_state=True)
+        kw = dict(saved_states=snaps, final_state=ST)
 
     def call():
-        bwd(*args, initial_state=inp["S0"], workspace=ws, out=outs)
+        bwd(*args, initial_state=inp["S0"], workspace=ws, out=outs, **kw)
 
     for _ in range(warmup):
         call()
@@ -462,7 +469,8 @@ def bench_backward(shape, steps, warmup, inp=None, chunked=True):
     ms = sum(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)) / steps
     flops = backward_alg_flops(B, T, HV, K, V)
     log("[backward %s] avg %.3f ms, %.1f TFLOP/s (15KV per token-head), workspace %.2f GB"
-        % ("chunked" if chunked else "recurrent", ms, flops / (ms * 1e-3) / 1e12, ws.numel() / 1e9))
+        % (("chunked, saved states" if saved else "chunked") if chunked else "recurrent", ms,
+           flops / (ms * 1e-3) / 1e12, ws.numel() / 1e9))
     return dict(avg_ms=ms, flops=flops, tokens=B * T, workspace=ws.numel())
 
 
@@ -531,6 +539,7 @@ def main():
     if args.only == "backward":
         bench_backward(synth.PREFILL_HV96_BF16, args.steps, args.warmup, chunked=True)
         bench_backward(synth.PREFILL_HV96_BF16, args.steps, args.warmup, chunked=False)
+        bench_backward(synth.PREFILL_HV96_BF16, args.steps, args.warmup, chunked=True, saved=True)
         return
     if args.only == "snap":
         bench_prefill(synth.PREFILL_HV96_BF16, args.steps, args.warmup, "hv96 snapshots/1024", 1024)
@@ -631,6 +640,9 @@ def main():
         tf = bw["flops"] / (bw["avg_ms"] * 1e-3) / 1e12
         br = bench_backward(shape, max(3, args.steps // 4), min(args.warmup, 3), inp=p["inp"], chunked=False)
         tr = br["flops"] / (br["avg_ms"] * 1e-3) / 1e12
+        bs = bench_backward(shape, max(3, args.steps // 4), min(args.warmup, 3), inp=p["inp"], chunked=True,
+                            saved=True)
+        ts = bs["flops"] / (bs["avg_ms"] * 1e-3) / 1e12
         line["backward"] = {
             "workload": "kda_chunk_bwd on the HV96 workload (B1 T8192 H=HV=96 K=V=128 bf16, bounded "
                         "gate), dL/do ~ N(0,1), dL/dS_T ~ 0.1 N(0,1): dq, dk, dv, dg, dbeta, dS0",
@@ -640,6 +652,13 @@ def main():
                          "frac": tf * 1e12 / FP32_MFMA_PEAK, "flops_per_call": bw["flops"],
                          "what": "the gradient's own arithmetic (15KV per token and value head) against "
                                  "the fp32 matrix-core peak its products run on"},
+            "saved_states": {
+                "workload": "kda_chunk_bwd_saved on the same inputs, given the forward's states every 1024 "
+                            "tokens and its final state (kda_chunk_fwd_snapshots, run before the timed "
+                            "region, as a training step's forward has): no forward over the whole sequence",
+                "avg_call_ms": bs["avg_ms"], "tokens_per_s": bs["tokens"] / (bs["avg_ms"] * 1e-3),
+                "roofline": {"bound": "mfma", "achieved": ts, "peak": FP32_MFMA_PEAK / 1e12, "unit": "TFLOP/s",
+                             "frac": ts * 1e12 / FP32_MFMA_PEAK, "flops_per_call": bs["flops"]}},
             "recurrent": {
                 "workload": "kda_recurrent_bwd (token recurrence on the vector ALUs, any finite g) on the "
                             "same inputs",
@@ -649,7 +668,7 @@ def main():
                              "peak_nonpacked": FP32_VALU_PEAK_NONPACKED / 1e12,
                              "frac_nonpacked": tr * 1e12 / FP32_VALU_PEAK_NONPACKED,
                              "flops_per_call": br["flops"]}}}
-        del bw, br
+        del bw, br, bs
     if not args.no_layer_stages:
         st = bench_layer_stages(args.steps, args.warmup)
         line["layer_stages"] = {

@@ -35,7 +35,7 @@ _lib = None
 KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EHIP = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_DIRECT, GATE_BOUNDED, GATE_SOFTPLUS = 0, 1, 2
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class KDAError(RuntimeError):
@@ -103,6 +103,8 @@ def _load():
             lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_longlong
             lib.kda_chunk_bwd.argtypes = ([P] * 14 + [I] * 6 + [F, I, P, ctypes.c_longlong, P])
             lib.kda_chunk_bwd.restype = I
+            lib.kda_chunk_bwd_saved.argtypes = ([P] * 16 + [I] * 6 + [F, I, P, ctypes.c_longlong, P])
+            lib.kda_chunk_bwd_saved.restype = I
             lib.kda_chunk_fwd_snapshots.argtypes = [P] * 9 + [I] * 7 + [F, I, I, P, ctypes.c_longlong, P]
             lib.kda_chunk_fwd_snapshots.restype = I
             lib.kda_prefill_prologue.argtypes = ([P, P, P, ctypes.POINTER(DecodePrologue)] + [P] * 5
@@ -308,19 +310,25 @@ def chunk_bwd_workspace_size(B, T, H, HV, K, V, dtype=torch.bfloat16) -> int:
 
 
 def chunk_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initial_state=None,
-              *, workspace=None, need_d_initial_state=True, out=None):
+              *, workspace=None, need_d_initial_state=True, out=None, saved_states=None,
+              final_state=None):
     """``kda_chunk_bwd``: :func:`recurrent_bwd` in the chunk form on the
     matrix cores, for bf16 inputs with -5 <= g <= 0 (the inputs of
     :func:`chunk_fwd`).  Same arguments and results; ``workspace`` of at
-    least :func:`chunk_bwd_workspace_size` bytes."""
+    least :func:`chunk_bwd_workspace_size` bytes.  With ``saved_states``
+    (the snapshots of :func:`chunk_fwd_snapshots` at snapshot_every = 1024,
+    [B, T // 1024, HV, K, V]; None allowed when T <= 1024) and
+    ``final_state`` (the forward's final state, needed with d_final_state)
+    it calls ``kda_chunk_bwd_saved``, which does not run the forward again."""
+    saved = saved_states is not None or final_state is not None
     return recurrent_bwd(q, k, v, g, beta, dout, d_final_state, scale, initial_state,
                          workspace=workspace, need_d_initial_state=need_d_initial_state,
-                         out=out, _chunked=True)
+                         out=out, _chunked=True, _saved=(saved_states, final_state) if saved else None)
 
 
 def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initial_state=None,
                   *, workspace=None, need_d_initial_state=True, out=None, _noalloc=False,
-                  _chunked=False):
+                  _chunked=False, _saved=None):
     """``kda_recurrent_bwd``: gradients of the forward pass with the same
     inputs (any finite g).  dout [B,T,HV,V] is dL/do (v's dtype),
     d_final_state [B,HV,K,V] fp32 (or None) is dL/dS_T.  Returns (dq, dk
@@ -341,6 +349,11 @@ def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initia
     for t_, n_ in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
         if t_ is not None:
             _need(t_, n_, torch.float32, (B, HV, K, V), dev)
+    if _saved is not None:
+        if _saved[0] is not None:
+            _need(_saved[0], "saved_states", torch.float32, (B, T // 1024, HV, K, V), dev)
+        if _saved[1] is not None:
+            _need(_saved[1], "final_state", torch.float32, (B, HV, K, V), dev)
     if not _noalloc:
         nbytes = (chunk_bwd_workspace_size(B, T, H, HV, K, V, dt) if _chunked
                   else recurrent_bwd_workspace_size(B, T, H, HV, K, V))
@@ -369,6 +382,12 @@ def recurrent_bwd(q, k, v, g, beta, dout, d_final_state=None, scale=None, initia
                 _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dout),
                 _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dS0),
                 B, T, H, HV, K, V, float(scale) if scale else 0.0, _dtype_code(dt), _stream_handle(dev)))
+        elif _saved is not None:
+            _check(_load().kda_chunk_bwd_saved(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(_saved[0]),
+                _ptr(_saved[1]), _ptr(dout), _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                _ptr(db), _ptr(dS0), B, T, H, HV, K, V, float(scale) if scale else 0.0, _dtype_code(dt),
+                _ptr(workspace), workspace.numel(), _stream_handle(dev)))
         else:
             entry = _load().kda_chunk_bwd if _chunked else _load().kda_recurrent_bwd
             _check(entry(
@@ -440,21 +459,32 @@ class _KDA(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, g, beta, initial_state, scale, chunked, bounded_gate):
         unbounded = chunked and not bounded_gate and q.dtype == torch.bfloat16
-        fwd = chunk_fwd_unbounded if unbounded else chunk_fwd if chunked and bounded_gate else recurrent_fwd
-        o, S = fwd(q, k, v, g, beta, scale=scale, initial_state=initial_state, output_final_state=True)
-        ctx.save_for_backward(q, k, v, g, beta, initial_state)
-        ctx.scale = scale
         ctx.chunked = chunked and bounded_gate and q.dtype == torch.bfloat16
+        snaps = None
+        if ctx.chunked:
+            # the states every 1024 tokens, so that the backward does not run
+            # the forward again (kda_chunk_bwd_saved)
+            o, S, snaps = chunk_fwd_snapshots(q, k, v, g, beta, 1024, scale=scale, initial_state=initial_state,
+                                              output_final_state=True)
+        else:
+            fwd = chunk_fwd_unbounded if unbounded else chunk_fwd if chunked and bounded_gate else recurrent_fwd
+            o, S = fwd(q, k, v, g, beta, scale=scale, initial_state=initial_state, output_final_state=True)
+        ctx.save_for_backward(q, k, v, g, beta, initial_state, snaps, S)
+        ctx.scale = scale
         return o, S
 
     @staticmethod
     def backward(ctx, do, dS):
-        q, k, v, g, beta, S0 = ctx.saved_tensors
+        q, k, v, g, beta, S0, snaps, ST = ctx.saved_tensors
         do = torch.zeros_like(v) if do is None else do.contiguous()
         dS = None if dS is None else dS.contiguous()
-        bwd = chunk_bwd if ctx.chunked else recurrent_bwd
-        dq, dk, dv, dg, db, dS0 = bwd(q, k, v, g, beta, do, dS, scale=ctx.scale, initial_state=S0,
-                                      need_d_initial_state=S0 is not None)
+        if ctx.chunked:
+            dq, dk, dv, dg, db, dS0 = chunk_bwd(q, k, v, g, beta, do, dS, scale=ctx.scale, initial_state=S0,
+                                                need_d_initial_state=S0 is not None, saved_states=snaps,
+                                                final_state=ST)
+        else:
+            dq, dk, dv, dg, db, dS0 = recurrent_bwd(q, k, v, g, beta, do, dS, scale=ctx.scale, initial_state=S0,
+                                                    need_d_initial_state=S0 is not None)
         return dq, dk, dv, dg, db, dS0, None, None, None
 
 

@@ -431,13 +431,18 @@ long long kda_chunk_bwd_workspace_size(int B, int T, int H, int HV, int K, int V
     return static_cast<long long>(L.total);
 }
 
-int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                  const float *initial_state, const void *dout, const float *dfinal_state, void *dq,
-                  void *dk, void *dv, float *dg, float *dbeta, float *dinitial_state, int B, int T,
-                  int H, int HV, int K, int V, float scale, int dtype, void *workspace,
-                  long long workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of kda_chunk_bwd and kda_chunk_bwd_saved (saved: the forward's
+// states every kBwdSlab tokens and its final state come from the caller).
+int chunk_bwd_impl(const char *fn, bool saved, const void *q, const void *k, const void *v, const float *g,
+                   const float *beta, const float *initial_state, const float *saved_states,
+                   const float *final_state, const void *dout, const float *dfinal_state, void *dq, void *dk,
+                   void *dv, float *dg, float *dbeta, float *dinitial_state, int B, int T, int H, int HV, int K,
+                   int V, float scale, int dtype, void *workspace, long long workspace_bytes, void *stream) {
     g_err[0] = '\0';
-    const char *fn = "kda_chunk_bwd";
     if (dtype != KDA_DTYPE_BF16)
         return fail(KDA_EUNSUPPORTED, "%s: dtype %d; the chunked backward takes KDA_DTYPE_BF16 (use kda_recurrent_bwd)", fn, dtype);
     if (B < 0 || T < 0) return fail(KDA_EINVAL, "%s: B=%d and T=%d must be >= 0", fn, B, T);
@@ -450,9 +455,11 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, c
     if (isinf(scale)) return fail(KDA_EINVAL, "%s: scale is infinite", fn);
     if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(K));
     ChunkBwdLayout L;
-    uint64_t nq, nv, ng, nb, ns;
+    const int NSs = saved ? T / kda::kBwdSlab : 0;
+    uint64_t nq, nv, ng, nb, ns, nss;
     if (!chunk_bwd_layout(L, B, T, HV, K, V) || !count(nq, {B, T, H, K}) || !count(nv, {B, T, HV, V}) ||
-        !count(ng, {B, T, HV, K}) || !count(nb, {B, T, HV}) || !count(ns, {B, HV, K, V}))
+        !count(ng, {B, T, HV, K}) || !count(nb, {B, T, HV}) || !count(ns, {B, HV, K, V}) ||
+        !count(nss, {B, NSs, HV, K, V}))
         return fail(KDA_EINVAL, "%s: tensor sizes overflow", fn);
     const bool work = static_cast<int64_t>(B) * T > 0;
     if (work) {
@@ -460,28 +467,35 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, c
             return fail(KDA_EINVAL, "%s: q, k, v, g, beta and dout must be non-NULL", fn);
         if (!dq || !dk || !dv || !dg || !dbeta)
             return fail(KDA_EINVAL, "%s: dq, dk, dv, dg and dbeta must be non-NULL", fn);
+        if (saved && L.NS1 > 0 && !saved_states)
+            return fail(KDA_EINVAL, "%s: saved_states must be non-NULL when T > %d", fn, kda::kBwdSlab);
+        if (saved && dfinal_state && !final_state)
+            return fail(KDA_EINVAL, "%s: final_state must be non-NULL when dfinal_state is given", fn);
         if (!workspace) return fail(KDA_EINVAL, "%s: workspace is NULL", fn);
         if (workspace_bytes < 0 || static_cast<uint64_t>(workspace_bytes) < L.total)
             return fail(KDA_EINVAL, "%s: workspace of %lld bytes, %llu needed", fn, workspace_bytes,
                         static_cast<unsigned long long>(L.total));
     }
-    const void *ptrs[] = {q, k, v, g, beta, initial_state, dout, dfinal_state,
+    const void *ptrs[] = {q, k, v, g, beta, initial_state, dout, dfinal_state, saved_states, final_state,
                           dq, dk, dv, dg, dbeta, dinitial_state, workspace};
     const char *names[] = {"q", "k", "v", "g", "beta", "initial_state", "dout", "dfinal_state",
-                           "dq", "dk", "dv", "dg", "dbeta", "dinitial_state", "workspace"};
-    for (int i = 0; i < 15; ++i)
+                           "saved_states", "final_state", "dq", "dk", "dv", "dg", "dbeta", "dinitial_state",
+                           "workspace"};
+    for (int i = 0; i < 17; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(KDA_EINVAL, "%s: %s is not 16-byte aligned", fn, names[i]);
     const Range rs[] = {rng("q", q, nq * 2), rng("k", k, nq * 2), rng("v", v, nv * 2),
                         rng("g", g, ng * 4), rng("beta", beta, nb * 4),
                         rng("initial_state", initial_state, ns * 4), rng("dout", dout, nv * 2),
                         rng("dfinal_state", dfinal_state, ns * 4),
+                        rng("saved_states", saved ? saved_states : nullptr, nss * 4),
+                        rng("final_state", saved ? final_state : nullptr, ns * 4),
                         rng("dq", dq, nq * 2), rng("dk", dk, nq * 2), rng("dv", dv, nv * 2),
                         rng("dg", dg, ng * 4), rng("dbeta", dbeta, nb * 4),
                         rng("dinitial_state", dinitial_state, ns * 4),
                         rng("workspace", work ? workspace : nullptr, L.total)};
-    for (int o = 8; o < 15; ++o)
-        for (int i = 0; i < 15; ++i)
+    for (int o = 10; o < 17; ++o)
+        for (int i = 0; i < 17; ++i)
             if (i != o && overlap(rs[o], rs[i]))
                 return fail(KDA_EINVAL, "%s: %s overlaps %s", fn, rs[o].name, rs[i].name);
 
@@ -496,13 +510,44 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, c
         a.W = at(L.W); a.U = at(L.U); a.img = at(L.img); a.dR = at(L.dR); a.dMs = at(L.dMs);
         a.snapc2 = at(L.snapc2); a.W2 = at(L.W2); a.U2 = at(L.U2); a.img2 = at(L.img2);
         a.e = at(L.e); a.cs = at(L.cs); a.gc = at(L.gc);
+        if (saved) {
+            // read only: the kernels never write ST or snap1 in this variant
+            a.ST = const_cast<float *>(final_state);
+            a.snap1 = const_cast<float *>(saved_states);
+        }
     }
+    a.saved = saved;
+    a.NSsaved = NSs;
     a.Ls = L.Ls; a.NS1 = L.NS1;
     a.B = B; a.T = T; a.H = H; a.HV = HV; a.K = K; a.V = V;
     a.scale = scale;
     const hipError_t e = kda::launch_chunk_backward(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KDA_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  const float *initial_state, const void *dout, const float *dfinal_state, void *dq,
+                  void *dk, void *dv, float *dg, float *dbeta, float *dinitial_state, int B, int T,
+                  int H, int HV, int K, int V, float scale, int dtype, void *workspace,
+                  long long workspace_bytes, void *stream) {
+    return chunk_bwd_impl("kda_chunk_bwd", false, q, k, v, g, beta, initial_state, nullptr, nullptr, dout,
+                          dfinal_state, dq, dk, dv, dg, dbeta, dinitial_state, B, T, H, HV, K, V, scale, dtype,
+                          workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_bwd_saved(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                        const float *initial_state, const float *saved_states, const float *final_state,
+                        const void *dout, const float *dfinal_state, void *dq, void *dk, void *dv, float *dg,
+                        float *dbeta, float *dinitial_state, int B, int T, int H, int HV, int K, int V,
+                        float scale, int dtype, void *workspace, long long workspace_bytes, void *stream) {
+    return chunk_bwd_impl("kda_chunk_bwd_saved", true, q, k, v, g, beta, initial_state, saved_states,
+                          final_state, dout, dfinal_state, dq, dk, dv, dg, dbeta, dinitial_state, B, T, H, HV, K,
+                          V, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

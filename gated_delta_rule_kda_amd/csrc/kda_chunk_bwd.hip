@@ -1002,7 +1002,8 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
     KDA_TRY(hipStreamWaitEvent(Y, ss->start, 0));
     const int ns = (a.T + a.Ls - 1) / a.Ls;
     // 0. the whole sequence once: S_T and the states at the slab starts
-    {
+    // (given by the caller in the saved variant)
+    if (!a.saved) {
         PrefillArgs f{};
         f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta; f.S0 = a.S0;
         f.ST = a.ST;
@@ -1015,7 +1016,7 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
     }
     float *gc[2] = {a.gc, a.gc + static_cast<size_t>(a.B) * a.HV * a.K};
     {
-        KDA_TRY(hipStreamWaitEvent(X, ss->st, 0));
+        if (!a.saved) KDA_TRY(hipStreamWaitEvent(X, ss->st, 0));
         const long nk = static_cast<long>(a.B) * a.HV * a.K;
         hipLaunchKernelGGL(cbwd_dg_final_kernel, dim3(static_cast<unsigned>((nk + 255) / 256)), dim3(256), 0,
                            X, a, gc[0]);
@@ -1036,7 +1037,7 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
             s.s_bstride = static_cast<long long>(sKV);
         } else {
             s.Sstart = a.snap1 + static_cast<size_t>(si - 1) * sKV;
-            s.s_bstride = static_cast<long long>(a.NS1) * sKV;
+            s.s_bstride = static_cast<long long>(a.saved ? a.NSsaved : a.NS1) * sKV;
         }
         s.dm_in = si == ns - 1 ? a.dST : a.Dc;
         s.dm_out = si == 0 ? a.dS0 : a.Dc;

@@ -161,6 +161,11 @@ struct ChunkBwdArgs {
     float *snapc2, *W2, *U2, *img2;   // second copies for the slabs of odd index
     int Ls;                     // tokens per slab (a multiple of 32)
     int NS1;                    // slab starts kept by the first forward pass (slabs - 1)
+    // The forward's own states instead of the first forward pass: ST (S_T)
+    // and snap1 ([B, NSsaved, HV, K, V], the state after every Ls tokens)
+    // come from the caller and nothing recomputes them.
+    bool saved;
+    int NSsaved;
     int B, T, H, HV, K, V;
     float scale;
 };

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 enum kda_status { KDA_OK = 0, KDA_EINVAL = 1, KDA_EUNSUPPORTED = 2, KDA_EHIP = 3 };
 
@@ -282,6 +282,31 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, c
                   void *dk, void *dv, float *dg, float *dbeta, float *dinitial_state, int B, int T,
                   int H, int HV, int K, int V, float scale, int dtype, void *workspace,
                   long long workspace_bytes, void *stream);
+
+/*
+ * kda_chunk_bwd_saved -- kda_chunk_bwd given the forward pass's own states,
+ * so that it does not run the forward over the whole sequence again (its
+ * first step).  For training, where the forward has just run: the forward of
+ * the same inputs by kda_chunk_fwd_snapshots with snapshot_every = 1024
+ * provides both.
+ *   saved_states  [B, T / 1024, HV, K, V] fp32: the state after the first
+ *                 1024, 2048, ... tokens of each sequence (the snapshots of
+ *                 kda_chunk_fwd_snapshots at snapshot_every = 1024); may be
+ *                 NULL when T <= 1024 (else KDA_EINVAL)
+ *   final_state   [B, HV, K, V] fp32: the forward's final state; needed when
+ *                 dfinal_state is given (for dg's final-state term; else
+ *                 KDA_EINVAL), otherwise not read
+ * Both are inputs (not written; neither may overlap an output or the
+ * workspace).  Everything else -- arguments, layouts, the workspace and its
+ * size, the second stream, return codes -- as kda_chunk_bwd.  The gradients
+ * are those of the forward that produced the states: with states from
+ * different inputs they are not defined.
+ */
+int kda_chunk_bwd_saved(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                        const float *initial_state, const float *saved_states, const float *final_state,
+                        const void *dout, const float *dfinal_state, void *dq, void *dk, void *dv, float *dg,
+                        float *dbeta, float *dinitial_state, int B, int T, int H, int HV, int K, int V,
+                        float scale, int dtype, void *workspace, long long workspace_bytes, void *stream);
 
 /*
  * kda_recurrent_bwd_noalloc -- kda_recurrent_bwd for callers that cannot

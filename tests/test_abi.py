@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
                           "kda_output_gate", "kda_decode_step", "kda_recurrent_bwd",
                           "kda_recurrent_bwd_workspace_size", "kda_recurrent_bwd_noalloc",
                           "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd_unbounded",
-                          "kda_chunk_fwd_unbounded_workspace_size"}
+                          "kda_chunk_fwd_unbounded_workspace_size", "kda_chunk_bwd_saved"}
     L = ctypes.CDLL(kda.library_path())
     for n in names:
         assert hasattr(L, n), n
@@ -594,3 +594,38 @@ def test_chunk_fwd_unbounded_workspace_size():
     assert L.kda_chunk_fwd_unbounded_workspace_size(1, 8, 2, 4, 32, 32, 0) == -1
     assert "BF16 only" in L.kda_last_error().decode()
     assert L.kda_chunk_fwd_unbounded_workspace_size(1, 8, 2, 3, 32, 32, 1) == -1
+
+
+def saved_call(**over):
+    """kda_chunk_bwd_saved with fake, disjoint pointers (each BIG apart)."""
+    a = dict(q=BIG, k=2 * BIG, v=3 * BIG, g=4 * BIG, beta=5 * BIG, s0=None, sv=13 * BIG, fs=14 * BIG,
+             do=6 * BIG, dst=None, dq=7 * BIG, dk=8 * BIG, dv=9 * BIG, dg=10 * BIG, db=11 * BIG, ds0=None,
+             ws=12 * BIG, wsb=1 << 40, B=1, T=2100, H=2, HV=4, K=32, V=32, scale=0.0, dtype=1)
+    a.update(over)
+    L = lib()
+    rc = L.kda_chunk_bwd_saved(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sv"], a["fs"], a["do"],
+                               a["dst"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["ds0"], a["B"], a["T"],
+                               a["H"], a["HV"], a["K"], a["V"], a["scale"], a["dtype"], a["ws"], a["wsb"], None)
+    return rc, L.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(HV=3), 1, "kda_chunk_bwd_saved: HV=3"),
+    (dict(dtype=0), 2, "KDA_DTYPE_BF16"),
+    (dict(sv=None), 1, "saved_states must be non-NULL when T > 1024"),
+    (dict(dst=15 * BIG, fs=None), 1, "final_state must be non-NULL"),
+    (dict(sv=13 * BIG + 8), 1, "saved_states is not 16-byte aligned"),
+    (dict(sv=7 * BIG + 64), 1, "dq overlaps saved_states"),
+    (dict(fs=12 * BIG + 256), 1, "workspace overlaps final_state"),
+    (dict(ws=None), 1, "workspace is NULL"),
+])
+def test_chunk_bwd_saved_rejects(over, code, msg):
+    rc, err = saved_call(**over)
+    assert rc == code, err
+    assert msg in err, err
+
+
+def test_chunk_bwd_saved_empty_is_noop():
+    rc, err = saved_call(B=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None, dk=None, dv=None,
+                         dg=None, db=None, sv=None, fs=None, ws=None, wsb=0)
+    assert rc == 0, err

@@ -253,3 +253,35 @@ def test_full_size_gqa_chunk_bwd_sampled():
     for name, gpu, want, st in zip(NAMES, part, ref, STORED):
         m = assert_close(gpu, want, torch.bfloat16, st, "GQA %s" % name)
         say("   %-6s max_rel %.2e  excess/rms %.2e" % (name, m["max_rel"], m["excess_over_rms"]))
+
+
+SAVED = [
+    # B, T, H, HV, K, V: one slab, a ragged last slab, T a multiple of the slab, GQA
+    (1, 300, 1, 2, 64, 64),
+    (1, 2100, 1, 2, 64, 64),
+    (2, 2048, 1, 2, 32, 64),
+    (1, 1100, 2, 4, 128, 128),
+]
+
+
+@pytest.mark.parametrize("case", SAVED, ids=lambda c: "B%dT%dH%dHV%dK%dV%d" % c)
+@pytest.mark.parametrize("with_dst", [True, False])
+def test_chunk_bwd_saved_states(case, with_dst):
+    """kda_chunk_bwd_saved with the states kda_chunk_fwd_snapshots keeps every
+    1024 tokens and its final state: the gradients of kda_chunk_bwd (within
+    the tolerance of each other) and the oracle's."""
+    B, T, H, HV, K, V = case
+    shape = synth.PrefillShape(B, T, H, HV, K, V, torch.bfloat16, "normal", s0_std=0.3)
+    say("saved-states backward", case, "dS_T", with_dst)
+    inp = synth.make_prefill_inputs(shape, DEV, T + 5)
+    dout, dST = grads_in(shape, T + 5, with_dst)
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    _, ST, snaps = kda.chunk_fwd_snapshots(*args, 1024, initial_state=inp["S0"], output_final_state=True)
+    got = kda.chunk_bwd(*args, dout, dST, initial_state=inp["S0"], saved_states=snaps if T > 1024 else None,
+                        final_state=ST)
+    plain = kda.chunk_bwd(*args, dout, dST, initial_state=inp["S0"])
+    torch.cuda.synchronize()
+    ref = oracle.kda_bwd(*args, dout, dST, initial_state=inp["S0"])
+    for name, gpu, p, want, st in zip(NAMES, got, plain, ref, STORED):
+        assert_close(gpu, want, torch.bfloat16, st, "saved %s %s" % (name, case))
+        assert_close(gpu, p.double().cpu().numpy(), torch.bfloat16, st, "saved vs plain %s %s" % (name, case))
