@@ -936,14 +936,15 @@ hipError_t launch_pass(Pass p, const SlabArgs &s, hipStream_t stream) {
     }
 }
 
-// The second stream of the backward (one per device, default priority,
-// created on first use) and the events that order it against the caller's.
-// The mutex makes one call's enqueue sequence atomic, so calls from several
-// host threads on one device do not interleave their event records.
+// The two further streams of the backward (one pair per device, default
+// priority, created on first use) and the events that order them against the
+// caller's.  The mutex makes one call's enqueue sequence atomic, so calls from
+// several host threads on one device do not interleave their event records.
 struct SideStream {
     std::mutex mu;
-    hipStream_t y = nullptr;
+    hipStream_t y = nullptr, z = nullptr;
     hipEvent_t start = nullptr, st = nullptr, p0[2] = {}, prep[2] = {}, chain[2] = {}, grad[2] = {};
+    hipEvent_t zdone = nullptr;
 };
 constexpr int kMaxDev = 64;
 SideStream g_side[kMaxDev];
@@ -960,8 +961,9 @@ hipError_t side_stream(hipStream_t stream, SideStream **out) {
     if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
     if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
     e = hipStreamCreateWithFlags(&ss.y, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&ss.z, hipStreamNonBlocking);
     hipEvent_t *evs[] = {&ss.start, &ss.st, &ss.p0[0], &ss.p0[1], &ss.prep[0], &ss.prep[1],
-                         &ss.chain[0], &ss.chain[1], &ss.grad[0], &ss.grad[1]};
+                         &ss.chain[0], &ss.chain[1], &ss.grad[0], &ss.grad[1], &ss.zdone};
     for (hipEvent_t *ev : evs)
         if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
     const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
@@ -974,14 +976,19 @@ int chunk_bwd_image_floats(int K) {
     return K == 32 ? Img<32>::floats : K == 64 ? Img<64>::floats : K == 128 ? Img<128>::floats : 0;
 }
 
-// Slab by slab from the last.  The caller's stream X runs the chain of state
-// gradients, the gradient pass and the dg sums in order; a second stream Y
-// runs what they consume and does not depend on them -- the whole-sequence
-// forward pass, then per slab its forward pass and the operand images --
-// ahead of X, on the CUs the chain leaves idle (one workgroup per head).
-// Y's per-slab outputs (chunk-start states, W, U, images) are double-buffered
-// by slab parity; Y overwrites a buffer only after X's pass of the slab two
-// before has read it.
+// Slab by slab from the last, on three streams.  The caller's stream X runs
+// the chain of state gradients, slab after slab.  A second stream Y runs what
+// the chain and the gradient pass consume and does not depend on them -- the
+// whole-sequence forward pass, then per slab its forward pass and the operand
+// images -- ahead of X; a third, Z, runs each slab's gradient pass and dg sums
+// once its chain is done, beside the chain of the slab before.  Y and Z use
+// the CUs the chain leaves idle (one workgroup per head).  Per-slab buffers
+// that one stream writes while another may still read the previous slab's
+// (chunk-start states, W, U, images from Y; dR and every chunk's dM' from X)
+// are double-buffered by slab parity, and each is overwritten only after the
+// pass of the slab two before that reads it is done.  X waits for Z's last
+// work before the call's enqueue ends, so work enqueued on X afterwards runs
+// after all of it.
 hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
     const size_t sKV = static_cast<size_t>(a.HV) * a.K * a.V;
@@ -996,10 +1003,11 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
     hipError_t e = side_stream(stream, &ss);
     if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> lock(ss->mu);
-    hipStream_t X = stream, Y = ss->y;
+    hipStream_t X = stream, Y = ss->y, Z = ss->z;
 #define KDA_TRY(x) do { const hipError_t e_ = (x); if (e_ != hipSuccess) return e_; } while (0)
     KDA_TRY(hipEventRecord(ss->start, X));
     KDA_TRY(hipStreamWaitEvent(Y, ss->start, 0));
+    KDA_TRY(hipStreamWaitEvent(Z, ss->start, 0));
     const int ns = (a.T + a.Ls - 1) / a.Ls;
     // 0. the whole sequence once: S_T and the states at the slab starts
     // (given by the caller in the saved variant)
@@ -1016,10 +1024,10 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
     }
     float *gc[2] = {a.gc, a.gc + static_cast<size_t>(a.B) * a.HV * a.K};
     {
-        if (!a.saved) KDA_TRY(hipStreamWaitEvent(X, ss->st, 0));
+        if (!a.saved) KDA_TRY(hipStreamWaitEvent(Z, ss->st, 0));
         const long nk = static_cast<long>(a.B) * a.HV * a.K;
         hipLaunchKernelGGL(cbwd_dg_final_kernel, dim3(static_cast<unsigned>((nk + 255) / 256)), dim3(256), 0,
-                           X, a, gc[0]);
+                           Z, a, gc[0]);
         KDA_TRY(hipGetLastError());
     }
     for (int si = ns - 1, j = 0; si >= 0; --si, ++j) {
@@ -1028,6 +1036,7 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         s.a = a;
         if (p) {
             s.a.snapc = a.snapc2; s.a.W = a.W2; s.a.U = a.U2; s.a.img = a.img2;
+            s.a.dR = a.dR2; s.a.dMs = a.dMs2;
         }
         s.t_begin = si * a.Ls;
         s.len = min(a.T, s.t_begin + a.Ls) - s.t_begin;
@@ -1059,18 +1068,25 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         if (j >= 2) KDA_TRY(hipStreamWaitEvent(Y, ss->chain[p], 0));
         KDA_TRY(launch_pass(Pass::prep, s, Y));
         KDA_TRY(hipEventRecord(ss->prep[p], Y));
-        // X: the chain, the gradient pass, dg (carried to the slab before)
+        // X: the chain, once the images are there and the gradient pass of
+        // slab si + 2 has read this parity's dR and dM'
         KDA_TRY(hipStreamWaitEvent(X, ss->prep[p], 0));
+        if (j >= 2) KDA_TRY(hipStreamWaitEvent(X, ss->grad[p], 0));
         KDA_TRY(launch_pass(Pass::chain, s, X));
         KDA_TRY(hipEventRecord(ss->chain[p], X));
-        KDA_TRY(hipStreamWaitEvent(X, ss->p0[p], 0));
-        KDA_TRY(launch_pass(Pass::grad, s, X));
-        KDA_TRY(hipEventRecord(ss->grad[p], X));
+        // Z: the gradient pass and dg (carried to the slab before)
+        KDA_TRY(hipStreamWaitEvent(Z, ss->chain[p], 0));
+        KDA_TRY(hipStreamWaitEvent(Z, ss->p0[p], 0));
+        KDA_TRY(launch_pass(Pass::grad, s, Z));
+        KDA_TRY(hipEventRecord(ss->grad[p], Z));
         const long nd = static_cast<long>(a.B) * a.HV * s.NCs * a.K;
-        hipLaunchKernelGGL(cbwd_dg_kernel, dim3(static_cast<unsigned>((nd + 255) / 256)), dim3(256), 0, X, s,
+        hipLaunchKernelGGL(cbwd_dg_kernel, dim3(static_cast<unsigned>((nd + 255) / 256)), dim3(256), 0, Z, s,
                            gc[j & 1], gc[(j + 1) & 1]);
         KDA_TRY(hipGetLastError());
     }
+    // everything on Y ends in work X or Z waited for; Z's end joins X
+    KDA_TRY(hipEventRecord(ss->zdone, Z));
+    KDA_TRY(hipStreamWaitEvent(X, ss->zdone, 0));
 #undef KDA_TRY
     return hipSuccess;
 }

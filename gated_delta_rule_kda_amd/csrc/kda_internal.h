@@ -159,6 +159,7 @@ struct ChunkBwdArgs {
     // workspace (fp32): see chunk_bwd_layout in kda_api.hip
     float *ST, *snap1, *Dc, *snapc, *W, *U, *img, *dR, *dMs, *e, *cs, *gc;
     float *snapc2, *W2, *U2, *img2;   // second copies for the slabs of odd index
+    float *dR2, *dMs2;
     int Ls;                     // tokens per slab (a multiple of 32)
     int NS1;                    // slab starts kept by the first forward pass (slabs - 1)
     // The forward's own states instead of the first forward pass: ST (S_T)

@@ -266,13 +266,14 @@ int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *
  * start and the in-chunk solve's input and result), a chunk-parallel pass
  * forming the reverse chain's operands, the reverse chain of state gradients
  * (one workgroup per value head), a chunk-parallel pass for dq, dk, dv, dbeta
- * and the dg terms, and the reverse sum that forms dg.  The forward passes and
- * the operand pass run on a second stream of the library's (one per device,
- * default priority, created on the first call), ordered against `stream` by
- * events; the call returns when all is enqueued, and work enqueued on
- * `stream` afterwards runs after all of it.  Calls from several host threads
- * on one device are serialized while they enqueue.  Workspace about 1.35 GB
- * at B = 1, T = 8192, HV = 96, K = V = 128.
+ * and the dg terms, and the reverse sum that forms dg.  The chain runs on
+ * `stream`; the forward passes and the operand pass, and the gradient pass
+ * with the dg sum, run on two further streams of the library's (one pair per
+ * device, default priority, created on the first call), ordered against
+ * `stream` by events; the call returns when all is enqueued, and work
+ * enqueued on `stream` afterwards runs after all of it.  Calls from several
+ * host threads on one device are serialized while they enqueue.  Workspace
+ * about 1.6 GB at B = 1, T = 8192, HV = 96, K = V = 128.
  * kda_chunk_bwd_workspace_size returns the workspace size in bytes, or -1
  * (message in kda_last_error) for sizes or a dtype kda_chunk_bwd rejects.
  */
@@ -298,7 +299,7 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *g, c
  *                 KDA_EINVAL), otherwise not read
  * Both are inputs (not written; neither may overlap an output or the
  * workspace).  Everything else -- arguments, layouts, the workspace and its
- * size, the second stream, return codes -- as kda_chunk_bwd.  The gradients
+ * size, the streams, return codes -- as kda_chunk_bwd.  The gradients
  * are those of the forward that produced the states: with states from
  * different inputs they are not defined.
  */

@@ -526,16 +526,17 @@ def test_chunk_bwd_workspace_size():
         Ls = 1024 if T > 1024 else max(32, -(-T // 32) * 32)
         NS1 = -(-T // Ls) - 1 if T > 0 else 0
         NC = Ls // 32
-        # (the chunk-start states, W, U and the images twice: slabs of even and odd index)
+        # (the chunk-start states, W, U, the images, dR and dS per chunk twice:
+        # slabs of even and odd index)
         return (2 * up(B * HV * K * V) + up(B * NS1 * HV * K * V) + 2 * up(B * (NC - 1) * HV * K * V)
-                + 5 * up(B * Ls * HV * V) + 2 * up(B * NC * HV * img(K)) + up(B * NC * HV * K * V)
+                + 6 * up(B * Ls * HV * V) + 2 * up(B * NC * HV * img(K)) + 2 * up(B * NC * HV * K * V)
                 + up(B * Ls * HV * K) + up(B * HV * NC * K) + up(2 * B * HV * K))
     for args in [(2, 100, 2, 4, 64, 128), (1, 8192, 96, 96, 128, 128), (3, 2500, 1, 2, 32, 64),
                  (1, 1024, 1, 1, 128, 128), (1, 1025, 1, 1, 128, 128), (1, 1, 1, 1, 32, 32)]:
         B, T, H, HV, K, V = args
         assert L.kda_chunk_bwd_workspace_size(*args, 1) == want(B, T, HV, K, V), args
-    # the HV96 workload: about 1.36 GB
-    assert L.kda_chunk_bwd_workspace_size(1, 8192, 96, 96, 128, 128, 1) < 1.4e9
+    # the HV96 workload: about 1.6 GB
+    assert L.kda_chunk_bwd_workspace_size(1, 8192, 96, 96, 128, 128, 1) < 1.7e9
     assert L.kda_chunk_bwd_workspace_size(1, 8, 2, 4, 32, 32, 0) == -1
     assert "KDA_DTYPE_BF16" in L.kda_last_error().decode()
     assert L.kda_chunk_bwd_workspace_size(1, 8, 2, 3, 32, 32, 1) == -1
