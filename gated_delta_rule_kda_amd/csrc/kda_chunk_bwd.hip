@@ -945,6 +945,7 @@ struct SideStream {
     hipStream_t y = nullptr, z = nullptr;
     hipEvent_t start = nullptr, st = nullptr, p0[2] = {}, prep[2] = {}, chain[2] = {}, grad[2] = {};
     hipEvent_t zdone = nullptr;
+    bool ready = false;   // every stream and event above created
 };
 constexpr int kMaxDev = 64;
 SideStream g_side[kMaxDev];
@@ -956,7 +957,8 @@ hipError_t side_stream(hipStream_t stream, SideStream **out) {
     if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
     SideStream &ss = g_side[dev];
     *out = &ss;
-    if (ss.y) return hipSuccess;
+    std::lock_guard<std::mutex> lock(ss.mu);   // one creation per device, whichever thread comes first
+    if (ss.ready) return hipSuccess;
     int cur = -1;
     if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
     if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
@@ -966,6 +968,7 @@ hipError_t side_stream(hipStream_t stream, SideStream **out) {
                          &ss.chain[0], &ss.chain[1], &ss.grad[0], &ss.grad[1], &ss.zdone};
     for (hipEvent_t *ev : evs)
         if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+    ss.ready = e == hipSuccess;
     const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
     return e != hipSuccess ? e : e2;
 }

@@ -285,3 +285,38 @@ def test_chunk_bwd_saved_states(case, with_dst):
     for name, gpu, p, want, st in zip(NAMES, got, plain, ref, STORED):
         assert_close(gpu, want, torch.bfloat16, st, "saved %s %s" % (name, case))
         assert_close(gpu, p.double().cpu().numpy(), torch.bfloat16, st, "saved vs plain %s %s" % (name, case))
+
+
+def test_chunk_bwd_concurrent_host_threads():
+    """Two host threads, each with its own stream, call the chunked backward
+    at the same time (the library's side streams are shared per device and a
+    call's enqueue is serialized): each result has the bits of a call made
+    alone."""
+    import threading
+    shape = synth.PrefillShape(1, 1100, 1, 2, 64, 64, torch.bfloat16, "normal", s0_std=0.3, g_lower=-1.0)
+    inp = synth.make_prefill_inputs(shape, DEV, 41)
+    dout, dST = grads_in(shape, 41)
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    alone = kda.chunk_bwd(*args, dout, dST, initial_state=inp["S0"])
+    torch.cuda.synchronize()
+    results, errors = [None, None], []
+
+    def worker(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for _ in range(3):
+                    results[i] = kda.chunk_bwd(*args, dout, dST, initial_state=inp["S0"])
+            st.synchronize()
+        except Exception as e:   # reported below, on the main thread
+            errors.append(e)
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        for name, a, b in zip(NAMES, results[i], alone):
+            assert torch.equal(a, b), "thread %d: %s differs from the call made alone" % (i, name)
