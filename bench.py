@@ -474,6 +474,41 @@ def bench_backward(shape, steps, warmup, inp=None, chunked=True, saved=False):
     return dict(avg_ms=ms, flops=flops, tokens=B * T, workspace=ws.numel())
 
 
+def bench_train_step(shape, steps, warmup, inp=None):
+    """One layer's forward and backward as a training step runs them: kda.kda
+    under torch.autograd (chunked bf16: kda_chunk_fwd_snapshots keeping a
+    state every 1024 tokens, then kda_chunk_bwd_saved), the backward driven by
+    given dL/do ~ N(0,1) and dL/dS_T ~ 0.1 N(0,1)."""
+    import torch
+    import gated_delta_rule_kda_amd as kda
+    from gated_delta_rule_kda_amd import synth
+    dev = torch.device("cuda:0")
+    if inp is None:
+        inp = synth.make_prefill_inputs(shape, dev, 0)
+    B, T, H, HV, K, V = shape.B, shape.T, shape.H, shape.HV, shape.K, shape.V
+    gen = torch.Generator(device=dev).manual_seed(2)
+    dout = torch.randn(B, T, HV, V, generator=gen, device=dev).to(shape.dtype)
+    dST = torch.randn(B, HV, K, V, generator=gen, device=dev) * 0.1
+    leaves = {n: inp[n].detach().clone().requires_grad_(True) for n in ("q", "k", "v", "g", "beta", "S0")}
+
+    def call():
+        for t in leaves.values():
+            t.grad = None
+        o, S = kda.kda(leaves["q"], leaves["k"], leaves["v"], leaves["g"], leaves["beta"],
+                       initial_state=leaves["S0"], output_final_state=True)
+        torch.autograd.backward([o, S], [dout, dST])
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts, ends = time_calls(call, steps, stream)
+    torch.cuda.synchronize()
+    ms = sum(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)) / steps
+    log("[train step] forward + backward avg %.3f ms" % ms)
+    return dict(avg_ms=ms, tokens=B * T)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -540,6 +575,7 @@ def main():
         bench_backward(synth.PREFILL_HV96_BF16, args.steps, args.warmup, chunked=True)
         bench_backward(synth.PREFILL_HV96_BF16, args.steps, args.warmup, chunked=False)
         bench_backward(synth.PREFILL_HV96_BF16, args.steps, args.warmup, chunked=True, saved=True)
+        bench_train_step(synth.PREFILL_HV96_BF16, args.steps, args.warmup)
         return
     if args.only == "snap":
         bench_prefill(synth.PREFILL_HV96_BF16, args.steps, args.warmup, "hv96 snapshots/1024", 1024)
@@ -668,7 +704,13 @@ def main():
                              "peak_nonpacked": FP32_VALU_PEAK_NONPACKED / 1e12,
                              "frac_nonpacked": tr * 1e12 / FP32_VALU_PEAK_NONPACKED,
                              "flops_per_call": br["flops"]}}}
-        del bw, br, bs
+        ts_ = bench_train_step(shape, max(3, args.steps // 4), min(args.warmup, 3), inp=p["inp"])
+        line["backward"]["train_step"] = {
+            "workload": "one layer's forward and backward under torch.autograd (kda.kda, chunked bf16: "
+                        "kda_chunk_fwd_snapshots keeping a state every 1024 tokens, then kda_chunk_bwd_saved), "
+                        "driven by given dL/do and dL/dS_T",
+            "avg_step_ms": ts_["avg_ms"], "tokens_per_s": ts_["tokens"] / (ts_["avg_ms"] * 1e-3)}
+        del bw, br, bs, ts_
     if not args.no_layer_stages:
         st = bench_layer_stages(args.steps, args.warmup)
         line["layer_stages"] = {
