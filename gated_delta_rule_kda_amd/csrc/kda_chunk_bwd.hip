@@ -56,6 +56,7 @@
 // used as the B operand of the next product (dm, dU, dR) is already in that
 // order: its element j is row 4 kq + j.
 
+#include <algorithm>
 #include <mutex>
 
 #include "kda_internal.h"
@@ -839,6 +840,14 @@ __global__ __launch_bounds__(256) void cbwd_dg_final_kernel(ChunkBwdArgs a, floa
     gc[i] = c;
 }
 
+// T = 0: dS0 = dL/dS_T, or zeros without it (a kernel rather than a memset or
+// copy node, so that the call records only kernels when captured).
+__global__ __launch_bounds__(256) void cbwd_ds0_kernel(float *dS0, const float *dST, long n) {
+    const long stride = static_cast<long>(gridDim.x) * 256;
+    for (long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride)
+        dS0[i] = dST ? dST[i] : 0.f;
+}
+
 // One slab: thread = (b, hv, chunk j, k).  The carry in (the final-state term
 // and every later slab's terms) plus the later chunks' sums, then the chunk's
 // 32 tokens from the last; the thread of chunk 0 leaves the carry for the
@@ -992,25 +1001,43 @@ int chunk_bwd_image_floats(int K) {
 // pass of the slab two before that reads it is done.  X waits for Z's last
 // work before the call's enqueue ends, so work enqueued on X afterwards runs
 // after all of it.
+//
+// While the caller's stream is being captured into a graph, every pass runs
+// in the same order on that stream alone: no side streams, events or stream
+// queries are recorded (the enqueue order below satisfies every dependency
+// the events express, so the results are the same bits).
 hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
     const size_t sKV = static_cast<size_t>(a.HV) * a.K * a.V;
     if (a.T == 0) {
         // only dS0 = dL/dS_T (or zeros)
         if (!a.dS0) return hipSuccess;
-        const size_t bytes = static_cast<size_t>(a.B) * sKV * 4;
-        return a.dST ? hipMemcpyAsync(a.dS0, a.dST, bytes, hipMemcpyDeviceToDevice, stream)
-                     : hipMemsetAsync(a.dS0, 0, bytes, stream);
+        const long n = static_cast<long>(a.B) * static_cast<long>(sKV);
+        const long blocks = std::min<long>((n + 255) / 256, 4096);
+        hipLaunchKernelGGL(cbwd_ds0_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a.dS0,
+                           a.dST, n);
+        return hipGetLastError();
     }
-    SideStream *ss = nullptr;
-    hipError_t e = side_stream(stream, &ss);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cap);
     if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(ss->mu);
-    hipStream_t X = stream, Y = ss->y, Z = ss->z;
+    const bool serial = cap != hipStreamCaptureStatusNone;
+    SideStream none, *ss = &none;   // none: events never used (serial)
+    std::unique_lock<std::mutex> lock;
+    hipStream_t X = stream, Y = stream, Z = stream;
+    if (!serial) {
+        e = side_stream(stream, &ss);
+        if (e != hipSuccess) return e;
+        lock = std::unique_lock<std::mutex>(ss->mu);
+        Y = ss->y;
+        Z = ss->z;
+    }
+    auto rec = [&](hipEvent_t ev, hipStream_t s) { return serial ? hipSuccess : hipEventRecord(ev, s); };
+    auto wait = [&](hipStream_t s, hipEvent_t ev) { return serial ? hipSuccess : hipStreamWaitEvent(s, ev, 0); };
 #define KDA_TRY(x) do { const hipError_t e_ = (x); if (e_ != hipSuccess) return e_; } while (0)
-    KDA_TRY(hipEventRecord(ss->start, X));
-    KDA_TRY(hipStreamWaitEvent(Y, ss->start, 0));
-    KDA_TRY(hipStreamWaitEvent(Z, ss->start, 0));
+    KDA_TRY(rec(ss->start, X));
+    KDA_TRY(wait(Y, ss->start));
+    KDA_TRY(wait(Z, ss->start));
     const int ns = (a.T + a.Ls - 1) / a.Ls;
     // 0. the whole sequence once: S_T and the states at the slab starts
     // (given by the caller in the saved variant)
@@ -1023,11 +1050,11 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         f.B = a.B; f.T = a.T; f.H = a.H; f.HV = a.HV; f.K = a.K; f.V = a.V;
         f.scale = a.scale; f.bf16 = true; f.bwd = true;
         KDA_TRY(launch_prefill_bf16(f, Y));
-        KDA_TRY(hipEventRecord(ss->st, Y));
+        KDA_TRY(rec(ss->st, Y));
     }
     float *gc[2] = {a.gc, a.gc + static_cast<size_t>(a.B) * a.HV * a.K};
     {
-        if (!a.saved) KDA_TRY(hipStreamWaitEvent(Z, ss->st, 0));
+        if (!a.saved) KDA_TRY(wait(Z, ss->st));
         const long nk = static_cast<long>(a.B) * a.HV * a.K;
         hipLaunchKernelGGL(cbwd_dg_final_kernel, dim3(static_cast<unsigned>((nk + 255) / 256)), dim3(256), 0,
                            Z, a, gc[0]);
@@ -1055,7 +1082,7 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         s.dm_out = si == 0 ? a.dS0 : a.Dc;
         // Y: the slab's forward pass (states at its chunk starts, W, U) once the
         // gradient pass of slab si + 2 has read these buffers
-        if (j >= 2) KDA_TRY(hipStreamWaitEvent(Y, ss->grad[p], 0));
+        if (j >= 2) KDA_TRY(wait(Y, ss->grad[p]));
         PrefillArgs f{};
         f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta;
         f.S0 = s.Sstart; f.s0_bstride = s.s_bstride;
@@ -1066,30 +1093,30 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         f.B = a.B; f.T = s.len; f.H = a.H; f.HV = a.HV; f.K = a.K; f.V = a.V;
         f.scale = a.scale; f.bf16 = true; f.bwd = true;
         KDA_TRY(launch_prefill_bf16(f, Y));
-        KDA_TRY(hipEventRecord(ss->p0[p], Y));
+        KDA_TRY(rec(ss->p0[p], Y));
         // Y: the operand images, once the chain of slab si + 2 has read them
-        if (j >= 2) KDA_TRY(hipStreamWaitEvent(Y, ss->chain[p], 0));
+        if (j >= 2) KDA_TRY(wait(Y, ss->chain[p]));
         KDA_TRY(launch_pass(Pass::prep, s, Y));
-        KDA_TRY(hipEventRecord(ss->prep[p], Y));
+        KDA_TRY(rec(ss->prep[p], Y));
         // X: the chain, once the images are there and the gradient pass of
         // slab si + 2 has read this parity's dR and dM'
-        KDA_TRY(hipStreamWaitEvent(X, ss->prep[p], 0));
-        if (j >= 2) KDA_TRY(hipStreamWaitEvent(X, ss->grad[p], 0));
+        KDA_TRY(wait(X, ss->prep[p]));
+        if (j >= 2) KDA_TRY(wait(X, ss->grad[p]));
         KDA_TRY(launch_pass(Pass::chain, s, X));
-        KDA_TRY(hipEventRecord(ss->chain[p], X));
+        KDA_TRY(rec(ss->chain[p], X));
         // Z: the gradient pass and dg (carried to the slab before)
-        KDA_TRY(hipStreamWaitEvent(Z, ss->chain[p], 0));
-        KDA_TRY(hipStreamWaitEvent(Z, ss->p0[p], 0));
+        KDA_TRY(wait(Z, ss->chain[p]));
+        KDA_TRY(wait(Z, ss->p0[p]));
         KDA_TRY(launch_pass(Pass::grad, s, Z));
-        KDA_TRY(hipEventRecord(ss->grad[p], Z));
+        KDA_TRY(rec(ss->grad[p], Z));
         const long nd = static_cast<long>(a.B) * a.HV * s.NCs * a.K;
         hipLaunchKernelGGL(cbwd_dg_kernel, dim3(static_cast<unsigned>((nd + 255) / 256)), dim3(256), 0, Z, s,
                            gc[j & 1], gc[(j + 1) & 1]);
         KDA_TRY(hipGetLastError());
     }
     // everything on Y ends in work X or Z waited for; Z's end joins X
-    KDA_TRY(hipEventRecord(ss->zdone, Z));
-    KDA_TRY(hipStreamWaitEvent(X, ss->zdone, 0));
+    KDA_TRY(rec(ss->zdone, Z));
+    KDA_TRY(wait(X, ss->zdone));
 #undef KDA_TRY
     return hipSuccess;
 }

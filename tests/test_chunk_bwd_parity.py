@@ -169,10 +169,13 @@ def test_chunk_bwd_empty_sequence():
                         z(B, 0, HV, V), dST)
     torch.cuda.synchronize()
     assert torch.equal(got[5], dST)
+    # the zeros are written, over whatever dS0 held
+    outs = (z(B, 0, H, K), z(B, 0, H, K), z(B, 0, HV, V), zf(B, 0, HV, K), zf(B, 0, HV),
+            torch.full((B, HV, K, V), float("nan"), device=DEV))
     got = kda.chunk_bwd(z(B, 0, H, K), z(B, 0, H, K), z(B, 0, HV, V), zf(B, 0, HV, K), zf(B, 0, HV),
-                        z(B, 0, HV, V), None)
+                        z(B, 0, HV, V), None, out=outs)
     torch.cuda.synchronize()
-    assert torch.count_nonzero(got[5]) == 0
+    assert torch.count_nonzero(got[5]) == 0 and not torch.isnan(got[5]).any()
 
 
 def test_chunk_bwd_workspace_reuse_and_determinism():

@@ -1,7 +1,7 @@
 """HIP graph capture of the entry points a serving or training loop would
 capture: kda_chunk_fwd, kda_chunk_fwd_unbounded (its two kernels), and
-kda_chunk_bwd / kda_chunk_bwd_saved (kernels on three streams joined by
-events).  Each graph is replayed several times, with new input values written
+kda_chunk_bwd / kda_chunk_bwd_saved (eagerly on three streams joined by
+events; while captured, every pass in order on the captured stream).  Each graph is replayed several times, with new input values written
 in place and the program's own eager work and synchronizations between the
 replays, and every replay must give the eager call's bits on those inputs."""
 import sys
@@ -14,11 +14,7 @@ from gated_delta_rule_kda_amd import synth
 from kda_testutil import gpu_available
 
 pytestmark = [pytest.mark.gpu,
-              pytest.mark.skipif(not gpu_available(), reason="needs a GPU"),
-              pytest.mark.skip(reason="the first run of this file ended in a host segmentation fault "
-                                      "(exit 139, no GPU fault reported) before any test reported; its "
-                                      "cause is not identified, so graph capture stays untested and "
-                                      "these cases stay off the GPU")]
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 DEV = "cuda"
 
@@ -42,14 +38,17 @@ def replay_and_check(capture, eager, refill_fn, n=3):
     call (the reference), a replay, and a bitwise comparison."""
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
+    say("   capture")
     with torch.cuda.graph(g):
         outs = capture()
     torch.cuda.synchronize()
     for r in range(n):
+        say("   replay", r, ": new inputs, eager call")
         refill_fn(100 + r)
         torch.cuda.synchronize()
         want = [t.clone() for t in eager() if t is not None]
         torch.cuda.synchronize()
+        say("   replay", r, ": graph")
         g.replay()
         torch.cuda.synchronize()
         got = [t for t in outs if t is not None]
@@ -65,6 +64,7 @@ def test_graph_chunk_fwd():
     ST = torch.empty(2, 4, 64, 64, device=DEV)
     args = lambda: (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
     run = lambda o, s: kda.chunk_fwd(*args(), initial_state=inp["S0"], out=o, final_state=s)
+    say("chunk_fwd B2 T200 H2 HV4 K64 V64: eager")
     run(out, ST)   # eager first
     replay_and_check(lambda: run(out, ST), lambda: run(torch.empty_like(out), torch.empty_like(ST)),
                      lambda seed: refill(inp, shape, seed))
@@ -80,6 +80,7 @@ def test_graph_chunk_fwd_unbounded():
     args = lambda: (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
     run = lambda o, s, w: kda.chunk_fwd_unbounded(*args(), initial_state=inp["S0"], out=o, final_state=s,
                                                   workspace=w)
+    say("chunk_fwd_unbounded B1 T300 H1 HV2 K128 V64: eager")
     run(out, ST, ws)
     replay_and_check(lambda: run(out, ST, ws), lambda: run(torch.empty_like(out), torch.empty_like(ST), ws2),
                      lambda seed: refill(inp, shape, seed, heavy=True))
@@ -117,6 +118,7 @@ def test_graph_chunk_bwd(saved):
             return kda.chunk_bwd(*args(), dout, dST, initial_state=inp["S0"], workspace=w, out=o,
                                  saved_states=snaps, final_state=ST)
         return kda.chunk_bwd(*args(), dout, dST, initial_state=inp["S0"], workspace=w, out=o)
+    say("chunk_bwd saved=%s B1 T2100 H1 HV2 K64 V64: eager" % saved)
     run(outs, ws)
     replay_and_check(lambda: run(outs, ws), lambda: run(mk_outs(), ws2),
                      lambda seed: refill(inp, shape, seed))
