@@ -122,3 +122,139 @@ def test_graph_chunk_bwd(saved):
     run(outs, ws)
     replay_and_check(lambda: run(outs, ws), lambda: run(mk_outs(), ws2),
                      lambda seed: refill(inp, shape, seed))
+
+
+def test_graph_decode_steps():
+    """Two fused decode steps (conv width 4 + SiLU, L2 norm, bounded gate,
+    beta logits) in one graph; state and conv registers updated in place."""
+    B, H, HV, K, V, KW = 4, 2, 4, 64, 64, 4
+    C = 2 * H * K + HV * V
+    say("decode B4 H2 HV4 K64 V64 KW4, two steps: eager")
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    r = lambda *s_: torch.randn(*s_, generator=gen).to(DEV)
+    conv_w, A_log, dt_bias = r(C, KW), r(HV), r(HV * K)
+    xs = [torch.empty(B, C, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    zs = [torch.empty(B, HV, K, device=DEV) for _ in range(2)]
+    bls = [torch.empty(B, HV, device=DEV) for _ in range(2)]
+    state = torch.empty(B, HV, K, V, device=DEV)
+    conv = torch.empty(B, C, KW, device=DEV)
+    outs = [torch.empty(B, HV, V, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+
+    def refill_fn(seed):
+        g2 = torch.Generator(device="cpu").manual_seed(seed)
+        rr = lambda *s_: torch.randn(*s_, generator=g2).to(DEV)
+        for i in range(2):
+            xs[i].copy_(rr(B, C))
+            zs[i].copy_(rr(B, HV, K))
+            bls[i].copy_(rr(B, HV))
+        state.copy_(0.1 * rr(B, HV, K, V))
+        conv.copy_(rr(B, C, KW))
+
+    def steps(st, cv, o):
+        for i in range(2):
+            kda.decode_step(xs[i], zs[i], bls[i], st, H=H, HV=HV, K=K, V=V, out=o[i], conv_weight=conv_w,
+                            conv_state=cv, l2norm_qk=True, l2_eps=1e-6, gate_mode=kda.GATE_BOUNDED,
+                            A_log=A_log, dt_bias=dt_bias, gate_lower_bound=-5.0, beta_is_logit=True)
+        return list(o) + [st, cv]
+
+    def eager():
+        return steps(state.clone(), conv.clone(), [torch.empty_like(o) for o in outs])
+
+    refill_fn(1)
+    eager()
+    replay_and_check(lambda: steps(state, conv, outs), eager, refill_fn)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_graph_recurrent_fwd_bwd(dt):
+    """kda_recurrent_fwd, then kda_recurrent_bwd on its inputs, in one graph."""
+    B, T, H, HV, K, V = 1, 150, 1, 2, 64, 32
+    say("recurrent fwd + bwd B1 T150 H1 HV2 K64 V32 %s: eager" % dt)
+    shape = synth.PrefillShape(B, T, H, HV, K, V, dt, "normal", s0_std=0.3)
+    inp = synth.make_prefill_inputs(shape, DEV, 5, g_heavy=True)
+    dout = torch.empty(B, T, HV, V, dtype=dt, device=DEV)
+    dST = torch.empty(B, HV, K, V, device=DEV)
+    ws = torch.empty(kda.recurrent_bwd_workspace_size(B, T, H, HV, K, V), dtype=torch.uint8, device=DEV)
+    ws2 = torch.empty_like(ws)
+
+    def mk():
+        return (torch.empty(B, T, HV, V, dtype=dt, device=DEV), torch.empty(B, HV, K, V, device=DEV),
+                (torch.empty(B, T, H, K, dtype=dt, device=DEV), torch.empty(B, T, H, K, dtype=dt, device=DEV),
+                 torch.empty(B, T, HV, V, dtype=dt, device=DEV), torch.empty(B, T, HV, K, device=DEV),
+                 torch.empty(B, T, HV, device=DEV), torch.empty(B, HV, K, V, device=DEV)))
+    cap = mk()
+
+    def refill_fn(seed):
+        refill(inp, shape, seed, heavy=True)
+        g2 = torch.Generator(device="cpu").manual_seed(seed)
+        dout.copy_(torch.randn(B, T, HV, V, generator=g2).to(dt))
+        dST.copy_(0.1 * torch.randn(B, HV, K, V, generator=g2))
+
+    def run(o, w):
+        a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+        kda.recurrent_fwd(*a, initial_state=inp["S0"], out=o[0], final_state=o[1])
+        kda.recurrent_bwd(*a, dout, dST, initial_state=inp["S0"], workspace=w, out=o[2])
+        return [o[0], o[1]] + list(o[2])
+
+    refill_fn(6)
+    run(mk(), ws2)
+    replay_and_check(lambda: run(cap, ws), lambda: run(mk(), ws2), refill_fn)
+
+
+def test_graph_layer_paths():
+    """The layer's per-token stages around the chunk kernel, both ways:
+    kda_prefill_prologue (gate stage) -> kda_chunk_fwd_snapshots ->
+    kda_output_gate, and kda_prefill_prologue (no gate stage) ->
+    kda_chunk_fwd_gated with the output gate; conv registers in place."""
+    B, T, H, HV, K, V, KW = 1, 200, 2, 4, 128, 128, 4
+    C = 2 * H * K + HV * V
+    say("layer paths B1 T200 H2 HV4 K128 V128 KW4: eager")
+    gen = torch.Generator(device="cpu").manual_seed(21)
+    r = lambda *s_: torch.randn(*s_, generator=gen).to(DEV)
+    conv_w, A_log, dt_bias = 0.5 * r(C, KW), r(HV), r(HV * K)
+    x = torch.empty(B, T, C, dtype=torch.bfloat16, device=DEV)
+    z = torch.empty(B, T, HV, K, device=DEV)
+    bl = torch.empty(B, T, HV, device=DEV)
+    og = torch.empty(B, T, HV, V, dtype=torch.bfloat16, device=DEV)
+    cs = [torch.empty(B, C, KW, device=DEV) for _ in range(2)]
+    common = dict(H=H, HV=HV, K=K, V=V, conv_weight=conv_w, l2norm_qk=True, l2_eps=1e-6)
+
+    def refill_fn(seed):
+        g2 = torch.Generator(device="cpu").manual_seed(seed)
+        rr = lambda *s_: torch.randn(*s_, generator=g2).to(DEV)
+        x.copy_(rr(B, T, C))
+        z.copy_(2 * rr(B, T, HV, K))
+        bl.copy_(rr(B, T, HV))
+        og.copy_(rr(B, T, HV, V))
+        st = rr(B, C, KW)
+        for c in cs:
+            c.copy_(st)
+
+    def mk():
+        bf = dict(dtype=torch.bfloat16, device=DEV)
+        pro = lambda gate: (torch.empty(B, T, H, K, **bf), torch.empty(B, T, H, K, **bf),
+                            torch.empty(B, T, HV, V, **bf),
+                            torch.empty(B, T, HV, K, device=DEV) if gate else None,
+                            torch.empty(B, T, HV, device=DEV) if gate else None)
+        return dict(p1=pro(True), p2=pro(False), o1=torch.empty(B, T, HV, V, **bf),
+                    S1=torch.empty(B, HV, K, V, device=DEV), sn=torch.empty(B, T // 64, HV, K, V, device=DEV),
+                    y1=torch.empty(B, T, HV, V, **bf), y2=torch.empty(B, T, HV, V, **bf),
+                    S2=torch.empty(B, HV, K, V, device=DEV))
+
+    def run(o, c1, c2):
+        q, k, v, g, beta = kda.prefill_prologue(x, z, bl, conv_state=c1, gate_mode=kda.GATE_BOUNDED,
+                                                A_log=A_log, dt_bias=dt_bias, gate_lower_bound=-5.0,
+                                                beta_is_logit=True, out=o["p1"], **common)
+        kda.chunk_fwd_snapshots(q, k, v, g, beta, 64, out=o["o1"], final_state=o["S1"], snapshots=o["sn"])
+        kda.output_gate(o["o1"], og, 1e-6, out=o["y1"])
+        q2, k2, v2, _, _ = kda.prefill_prologue(x, None, None, conv_state=c2, out=o["p2"], **common)
+        kda.chunk_fwd_gated(q2, k2, v2, z, bl, A_log, dt_bias, -5.0, out_gate=og, out_gate_eps=1e-6,
+                            out=o["y2"], final_state=o["S2"])
+        return [o["o1"], o["S1"], o["sn"], o["y1"], o["y2"], o["S2"], c1, c2] + [t for t in o["p1"]] + \
+            [t for t in o["p2"] if t is not None]
+
+    cap = mk()
+    refill_fn(22)
+    run(mk(), cs[0].clone(), cs[1].clone())
+    replay_and_check(lambda: run(cap, cs[0], cs[1]), lambda: run(mk(), cs[0].clone(), cs[1].clone()),
+                     refill_fn)
