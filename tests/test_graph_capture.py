@@ -167,7 +167,9 @@ def test_graph_decode_steps():
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_graph_recurrent_fwd_bwd(dt):
-    """kda_recurrent_fwd, then kda_recurrent_bwd on its inputs, in one graph."""
+    """kda_recurrent_fwd, then kda_recurrent_bwd and kda_recurrent_bwd_noalloc
+    (the library's scratch array in place of a workspace) on its inputs, in
+    one graph."""
     B, T, H, HV, K, V = 1, 150, 1, 2, 64, 32
     say("recurrent fwd + bwd B1 T150 H1 HV2 K64 V32 %s: eager" % dt)
     shape = synth.PrefillShape(B, T, H, HV, K, V, dt, "normal", s0_std=0.3)
@@ -177,11 +179,14 @@ def test_graph_recurrent_fwd_bwd(dt):
     ws = torch.empty(kda.recurrent_bwd_workspace_size(B, T, H, HV, K, V), dtype=torch.uint8, device=DEV)
     ws2 = torch.empty_like(ws)
 
+    def grads():
+        return (torch.empty(B, T, H, K, dtype=dt, device=DEV), torch.empty(B, T, H, K, dtype=dt, device=DEV),
+                torch.empty(B, T, HV, V, dtype=dt, device=DEV), torch.empty(B, T, HV, K, device=DEV),
+                torch.empty(B, T, HV, device=DEV), torch.empty(B, HV, K, V, device=DEV))
+
     def mk():
         return (torch.empty(B, T, HV, V, dtype=dt, device=DEV), torch.empty(B, HV, K, V, device=DEV),
-                (torch.empty(B, T, H, K, dtype=dt, device=DEV), torch.empty(B, T, H, K, dtype=dt, device=DEV),
-                 torch.empty(B, T, HV, V, dtype=dt, device=DEV), torch.empty(B, T, HV, K, device=DEV),
-                 torch.empty(B, T, HV, device=DEV), torch.empty(B, HV, K, V, device=DEV)))
+                grads(), grads())
     cap = mk()
 
     def refill_fn(seed):
@@ -194,7 +199,8 @@ def test_graph_recurrent_fwd_bwd(dt):
         a = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
         kda.recurrent_fwd(*a, initial_state=inp["S0"], out=o[0], final_state=o[1])
         kda.recurrent_bwd(*a, dout, dST, initial_state=inp["S0"], workspace=w, out=o[2])
-        return [o[0], o[1]] + list(o[2])
+        kda.recurrent_bwd_noalloc(*a, dout, dST, initial_state=inp["S0"], out=o[3])
+        return [o[0], o[1]] + list(o[2]) + list(o[3])
 
     refill_fn(6)
     run(mk(), ws2)
