@@ -687,7 +687,8 @@ def main():
             "roofline": {"bound": "mfma", "achieved": tf, "peak": FP32_MFMA_PEAK / 1e12, "unit": "TFLOP/s",
                          "frac": tf * 1e12 / FP32_MFMA_PEAK, "flops_per_call": bw["flops"],
                          "what": "the gradient's own arithmetic (15KV per token and value head) against "
-                                 "the fp32 matrix-core peak its products run on"},
+                                 "the fp32 matrix-core peak (the gradient and operand passes multiply fp32 "
+                                 "operands; the reverse chain bf16 pairs)"},
             "saved_states": {
                 "workload": "kda_chunk_bwd_saved on the same inputs, given the forward's states every 1024 "
                             "tokens and its final state (kda_chunk_fwd_snapshots, run before the timed "

@@ -37,15 +37,19 @@
 //     start, W and U (kda_prefill_bf16.hip);
 //  1. prep (chunk-parallel): every chunk's operands of the reverse chain --
 //     k Lambda', s (q Gamma)^T, -(beta k Gamma)^T, s A_qk^T, T11^T, T22^T,
-//     -A21^T, Gamma_last -- as the exact LDS image the chain kernel reads;
+//     -A21^T, Gamma_last -- as the exact LDS image the chain kernel reads
+//     (bf16 hi/lo pairs);
 //  2. chain (one workgroup per (b, hv, V tile), chunks in reverse): dU, dR,
 //     the dM update, on the matrix cores; keeps dR and every chunk's dM';
 //  3. grad (chunk-parallel, one workgroup per (b, q/k head, chunk), summing
 //     over the head's value heads): the rest of the formulas above;
 //  4. dg: a reverse sum over the chunks' sums of the dg terms (which the
 //     grad pass leaves), then over each chunk's tokens.
-// Every product is an fp32 MFMA (v_mfma_f32_16x16x4_f32): no operand is
-// rounded below fp32 in the backward itself.
+// The chain's products take both operands as bf16 pairs x = hi + lo and sum
+// hi.hi + hi.lo + lo.hi (two terms where dO, exact in bf16, is one operand),
+// the forward's policy; the image holds its operands that way, and dM' and dR
+// are split from their fp32 accumulators each chunk.  Every other product is
+// an fp32 MFMA (v_mfma_f32_16x16x4_f32) on fp32 operands.
 //
 // fp32 16x16x4 MFMA lane layout (lane l, x = l % 16, kq = l / 16): A[x][kq],
 // B[kq][x]; the result holds D[4 kq + j][x] in element j.  Every product
@@ -76,10 +80,50 @@ constexpr int kThr = 512;  // threads per workgroup of the prep and chain kernel
 constexpr int kThrG = 512;  // of the grad kernel
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mma4(float a, float b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// bf16 products of the reverse chain: 16x16 tiles over 32 and 16 reduction
+// indices (A: row = lane % 16, 8 or 4 consecutive reduction indices of lane
+// group lane / 16; B: the same indices of column lane % 16)
+__device__ __forceinline__ f32x4 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x4 &a, const bf16x4 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                     0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 ld8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ bf16x4 ld4h(const __bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
+__device__ __forceinline__ bf16x8 cat(const bf16x4 &a, const bf16x4 &b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+// x = hi + lo with hi = bf16(x) (round to nearest even) and lo = bf16(x - hi)
+__device__ __forceinline__ void split1(float x, __bf16 &hi, __bf16 &lo) {
+    hi = static_cast<__bf16>(x);
+    lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
+    const bf16x2 h0 = __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2);
+    const bf16x2 h1 = __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2);
+    hi = bf16x4{h0[0], h0[1], h1[0], h1[1]};
+    const bf16x2 l0 = __builtin_convertvector(
+        f32x2{x[0] - static_cast<float>(h0[0]), x[1] - static_cast<float>(h0[1])}, bf16x2);
+    const bf16x2 l1 = __builtin_convertvector(
+        f32x2{x[2] - static_cast<float>(h1[0]), x[3] - static_cast<float>(h1[1])}, bf16x2);
+    lo = bf16x4{l0[0], l0[1], l1[0], l1[1]};
+}
+// Position of reduction index x within its block of 32: 16 h + 4 g + e goes to
+// 8 g + 4 h + e, so that lane group g's 8 indices (rows 4g..4g+3 of two
+// 16-row accumulator tiles) are contiguous.
+__device__ __forceinline__ int perm32(int x) {
+    return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
 }
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
@@ -109,25 +153,30 @@ __device__ __forceinline__ void tile_nt(const float *xrow, const float *yrow, in
 }
 
 // ---------------------------------------------------------------- operand image
-// Floats of one chunk's operands of the reverse chain, as the chain kernel's
-// LDS holds them (row pitches padded by 4 floats).
+// One chunk's operands of the reverse chain, as the chain kernel's LDS holds
+// them: bf16 hi/lo pairs (x = hi + lo), offsets and pitches in bf16 elements.
+// The reduction index of each product (K of k Lambda', the chunk's tokens of
+// the others) is stored in perm32 order within each block of 32, so that one
+// 16-byte read gives a lane its 8 indices; Gamma_last is fp32.
 template <int K>
 struct Img {
-    static constexpr int LK = K + 4;     // [C][K] rows
-    static constexpr int LC = kC + 4;    // [K][C], [C][C] rows
+    static constexpr int LK = K + 8;     // [C][K] rows
+    static constexpr int LC = kC + 8;    // [K][C], [C][C] rows
     static constexpr int L16 = 20;       // [16][16] rows
-    static constexpr int oKb = 0;                    // [C][LK]  k Lambda'
-    static constexpr int oA1 = oKb + kC * LK;         // [K][LC]  s (q Gamma)^T
-    static constexpr int oA2 = oA1 + K * LC;         // [K][LC]  -(beta k Gamma)^T
-    static constexpr int oAq = oA2 + K * LC;         // [C][LC]  s A_qk^T
-    static constexpr int oT1 = oAq + kC * LC;        // [16][L16] T11^T
-    static constexpr int oT2 = oT1 + 16 * L16;       // [16][L16] T22^T
-    static constexpr int oNA = oT2 + 16 * L16;       // [16][L16] -A21^T
-    static constexpr int oGl = oNA + 16 * L16;       // [K] Gamma_last
-    static constexpr int used = oGl + K;
-    // floats per chunk in HBM and per LDS buffer: whole rounds of the
-    // chain kernel's copy (256 lanes x 16 bytes)
-    static constexpr int floats = (used + 1023) / 1024 * 1024;
+    static constexpr int oKb = 0;                      // [2][C][LK]  k Lambda' (hi, lo)
+    static constexpr int oA1 = oKb + 2 * kC * LK;      // [2][K][LC]  s (q Gamma)^T
+    static constexpr int oA2 = oA1 + 2 * K * LC;       // [2][K][LC]  -(beta k Gamma)^T
+    static constexpr int oAq = oA2 + 2 * K * LC;       // [2][C][LC]  s A_qk^T
+    static constexpr int oT1 = oAq + 2 * kC * LC;      // [2][16][L16] T11^T (natural order)
+    static constexpr int oT2 = oT1 + 2 * 16 * L16;     // [2][16][L16] T22^T
+    static constexpr int oNA = oT2 + 2 * 16 * L16;     // [2][16][L16] -A21^T
+    static constexpr int oGl = (oNA + 2 * 16 * L16 + 7) / 8 * 8;   // [K] Gamma_last, fp32
+    static constexpr int used = oGl + 2 * K;           // bf16 elements
+    // floats per chunk in HBM and per LDS buffer: whole rounds of the chain
+    // kernel's copy (256 lanes x 16 bytes)
+    static constexpr int floats = (used / 2 + 1023) / 1024 * 1024;
+    static_assert(oKb % 8 == 0 && oA1 % 8 == 0 && oA2 % 8 == 0 && oAq % 8 == 0 && oT1 % 4 == 0,
+                  "16-byte fragment reads");
 };
 
 // Per-slab arguments of the three kernels.
@@ -169,7 +218,8 @@ __device__ __forceinline__ void chunk_cumsum(const float *g, int nv, int row_str
 template <int K>
 __global__ __launch_bounds__(kThr) void cbwd_prep_kernel(SlabArgs s) {
     using I = Img<K>;
-    constexpr int LK = I::LK, LC = I::LC, L16 = I::L16;
+    constexpr int LK = K + 4;                         // fp32 [C][K] working arrays
+    constexpr int IK = I::LK, IC = I::LC, L16 = I::L16;   // image pitches (bf16)
     const ChunkBwdArgs &a = s.a;
     extern __shared__ __attribute__((aligned(16))) float sm[];
     float *img = sm;                        // [I::floats]
@@ -190,6 +240,14 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_kernel(SlabArgs s) {
     const size_t tok = static_cast<size_t>(b) * a.T + t0;
     const uint16_t *qg = static_cast<const uint16_t *>(a.q);
     const uint16_t *kg = static_cast<const uint16_t *>(a.k);
+    __bf16 *im = reinterpret_cast<__bf16 *>(img);
+    // x as its bf16 pair: hi at element at, lo at + half (the array's lo half)
+    auto put = [&](int at, int half, float x) {
+        __bf16 h, l;
+        split1(x, h, l);
+        im[at] = h;
+        im[at + half] = l;
+    };
 
     chunk_cumsum<K, kThr>(a.g + (tok * a.HV + hv) * K, nv, a.HV * K, sG, LK, sTot);
     if (tid < kC) sB[tid] = tid < nv ? a.beta[(tok + tid) * a.HV + hv] : 0.f;
@@ -216,10 +274,10 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_kernel(SlabArgs s) {
             sPq[i * LK + c] = qv * e1;
             sPk[i * LK + c] = kv * e1;
             sRk[i * LK + c] = kv * e2;
-            img[I::oKb + i * LK + c] = kv * lam;
-            img[I::oA1 + c * LC + i] = a.scale * qv * gam;
-            img[I::oA2 + c * LC + i] = -bi * kv * gam;
-            if (i == kC - 1) img[I::oGl + c] = ex2(Gl);
+            put(I::oKb + i * IK + perm32(c), kC * IK, kv * lam);
+            put(I::oA1 + c * IC + perm32(i), K * IC, a.scale * qv * gam);
+            put(I::oA2 + c * IC + perm32(i), K * IC, -bi * kv * gam);
+            if (i == kC - 1) reinterpret_cast<float *>(im + I::oGl)[c] = ex2(Gl);
         }
     }
     __syncthreads();
@@ -235,12 +293,12 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_kernel(SlabArgs s) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = rt * 16 + 4 * lg + j, col = ct * 16 + lr;
-                img[I::oAq + col * LC + row] = col <= row ? a.scale * acc[j] : 0.f;
+                put(I::oAq + col * IC + perm32(row), kC * IC, col <= row ? a.scale * acc[j] : 0.f);
             }
             if (wave == 0) {
                 // rows 16-31 of A_qk^T, columns 0-15: above A_qk's diagonal
 #pragma unroll
-                for (int j = 0; j < 4; ++j) img[I::oAq + (16 + lr) * LC + 4 * lg + j] = 0.f;
+                for (int j = 0; j < 4; ++j) put(I::oAq + (16 + lr) * IC + perm32(4 * lg + j), kC * IC, 0.f);
             }
         } else if (t != 1) {
             // diagonal block of A_kk = diag(beta) SL(Pk Rk^T)
@@ -253,7 +311,7 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_kernel(SlabArgs s) {
         } else {
             // -A21^T: element (m, j) = -beta_{16+j} (Pk Rk^T)[16 + j][m]
 #pragma unroll
-            for (int j = 0; j < 4; ++j) img[I::oNA + lr * L16 + 4 * lg + j] = -sB[16 + 4 * lg + j] * acc[j];
+            for (int j = 0; j < 4; ++j) put(I::oNA + lr * L16 + 4 * lg + j, 16 * L16, -sB[16 + 4 * lg + j] * acc[j]);
         }
     }
     __syncthreads();
@@ -275,9 +333,9 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_kernel(SlabArgs s) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] -= av[e] * xk;
         }
-        float *TT = img + (blk == 0 ? I::oT1 : I::oT2);
+        const int oT = blk == 0 ? I::oT1 : I::oT2;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) TT[(4 * q + e) * L16 + i] = x[e];
+        for (int e = 0; e < 4; ++e) put(oT + (4 * q + e) * L16 + i, 16 * L16, x[e]);
     }
     __syncthreads();
     // the image to HBM, 16 bytes per thread
@@ -377,67 +435,88 @@ __global__ __launch_bounds__(kThr, 1) void cbwd_chain_kernel(SlabArgs s) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) dms[static_cast<size_t>(kb * 16 + 4 * lg + j) * V + col] = dm[gi][kb][j];
             }
-            // dO fragments: rows 16 b2 + 4 lg + j of the block's column lr
-            f32x4 dof[NG][2];
+            // dO fragments (bf16, exact): rows 4 lg + j and 16 + 4 lg + j of the
+            // block's column lr -- lane group lg's tokens in perm32 order
+            bf16x8 dob[NG];
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi)
+            for (int gi = 0; gi < NG; ++gi) {
+                bf16x4 f[2];
 #pragma unroll
                 for (int b2 = 0; b2 < 2; ++b2) {
                     const int row = b2 * 16 + 4 * (lane >> 4) + ((lane >> 2) & 3);
                     const int col = 16 * (wave * NG + gi) + 4 * (lane & 3);
-                    const bf16x4 f = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    f[b2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                         (__attribute__((address_space(3))) bf16x4 *)(sdo + row * LDO + col));
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) dof[gi][b2][j] = static_cast<float>(f[j]);
                 }
-            // dU = (k Lambda') dM' + s A_qk^T dO
+                dob[gi] = cat(f[0], f[1]);
+            }
+            const __bf16 *im = reinterpret_cast<const __bf16 *>(img);
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            // dU = (k Lambda') dM' + s A_qk^T dO.  dM' (accumulator rows 4 lg + j
+            // of two 16-row tiles: lane group lg's 8 rows of a block of 32) split
+            // into bf16 pairs is the B operand as it stands; three terms, two
+            // where dO (exact in bf16) is the B operand
             f32x4 du[NG][2];
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) du[gi][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int rt = 0; rt < 2; ++rt) du[gi][rt] = zero;
 #pragma unroll
-            for (int kb = 0; kb < KT; ++kb) {
-                f32x4 kk[2];
+            for (int ks = 0; ks < K / 32; ++ks) {
+                bf16x8 kh[2], kl[2];
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) kk[rt] = ld4(img + I::oKb + (rt * 16 + lr) * LK + kb * 16 + 4 * lg);
+                for (int rt = 0; rt < 2; ++rt) {
+                    const int at = I::oKb + (rt * 16 + lr) * LK + ks * 32 + 8 * lg;
+                    kh[rt] = ld8(im + at);
+                    kl[rt] = ld8(im + at + kC * LK);
+                }
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int gi = 0; gi < NG; ++gi) {
+                    bf16x4 h0, l0, h1, l1;
+                    split4(dm[gi][2 * ks], h0, l0);
+                    split4(dm[gi][2 * ks + 1], h1, l1);
+                    const bf16x8 mh = cat(h0, h1), ml = cat(l0, l1);
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                        for (int gi = 0; gi < NG; ++gi) du[gi][rt] = mma4(kk[rt][j], dm[gi][kb][j], du[gi][rt]);
+                    for (int rt = 0; rt < 2; ++rt) {
+                        du[gi][rt] = mfma32(kh[rt], mh, du[gi][rt]);
+                        du[gi][rt] = mfma32(kh[rt], ml, du[gi][rt]);
+                        du[gi][rt] = mfma32(kl[rt], mh, du[gi][rt]);
+                    }
+                }
             }
 #pragma unroll
-            for (int b2 = 0; b2 < 2; ++b2) {
-                f32x4 aq[2];
+            for (int rt = 0; rt < 2; ++rt) {
+                const int at = I::oAq + (rt * 16 + lr) * LC + 8 * lg;
+                const bf16x8 ah = ld8(im + at), al = ld8(im + at + kC * LC);
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) aq[rt] = ld4(img + I::oAq + (rt * 16 + lr) * LC + b2 * 16 + 4 * lg);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                        for (int gi = 0; gi < NG; ++gi) du[gi][rt] = mma4(aq[rt][j], dof[gi][b2][j], du[gi][rt]);
+                for (int gi = 0; gi < NG; ++gi) {
+                    du[gi][rt] = mfma32(ah, dob[gi], du[gi][rt]);
+                    du[gi][rt] = mfma32(al, dob[gi], du[gi][rt]);
+                }
             }
-            // dR2 = T22^T dU2;  Y = dU1 - A21^T dR2;  dR1 = T11^T Y
-            const f32x4 t1 = ld4(img + I::oT1 + lr * L16 + 4 * lg);
-            const f32x4 t2 = ld4(img + I::oT2 + lr * L16 + 4 * lg);
-            const f32x4 na = ld4(img + I::oNA + lr * L16 + 4 * lg);
+            // dR2 = T22^T dU2;  Y = dU1 - A21^T dR2;  dR1 = T11^T Y  (16x16x16,
+            // three terms; the accumulator rows 4 lg + j are the B operand's)
+            const int tq = lr * L16 + 4 * lg, th = 16 * L16;
+            const bf16x4 t1h = ld4h(im + I::oT1 + tq), t1l = ld4h(im + I::oT1 + th + tq);
+            const bf16x4 t2h = ld4h(im + I::oT2 + tq), t2l = ld4h(im + I::oT2 + th + tq);
+            const bf16x4 nah = ld4h(im + I::oNA + tq), nal = ld4h(im + I::oNA + th + tq);
             f32x4 dr[NG][2];
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
-                f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) x = mma4(t2[j], du[gi][1][j], x);
+                bf16x4 xh, xl;
+                split4(du[gi][1], xh, xl);
+                f32x4 x = mfma16(t2h, xh, zero), x2 = mfma16(t2h, xl, zero);
+                x2 = mfma16(t2l, xh, x2);
+                x += x2;
                 dr[gi][1] = x;
-                f32x4 y = du[gi][0];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) y = mma4(na[j], x[j], y);
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) z = mma4(t1[j], y[j], z);
-                dr[gi][0] = z;
+                split4(x, xh, xl);
+                f32x4 y = mfma16(nah, xh, du[gi][0]), y2 = mfma16(nah, xl, zero);
+                y2 = mfma16(nal, xh, y2);
+                y += y2;
+                split4(y, xh, xl);
+                f32x4 z = mfma16(t1h, xh, zero), z2 = mfma16(t1h, xl, zero);
+                z2 = mfma16(t1l, xh, z2);
+                dr[gi][0] = z + z2;
             }
             // dR (rows of the chunk inside the sequence) for the gradient kernel
 #pragma unroll
@@ -453,26 +532,35 @@ __global__ __launch_bounds__(kThr, 1) void cbwd_chain_kernel(SlabArgs s) {
                     }
             }
             // dM = Gamma_last (.) dM' + s (q Gamma)^T dO - (beta k Gamma)^T dR
+            // (dR split into bf16 pairs: three terms; dO two)
+            bf16x8 rbh[NG], rbl[NG];
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                bf16x4 h0, l0, h1, l1;
+                split4(dr[gi][0], h0, l0);
+                split4(dr[gi][1], h1, l1);
+                rbh[gi] = cat(h0, h1);
+                rbl[gi] = cat(l0, l1);
+            }
+            const float *glp = reinterpret_cast<const float *>(im + I::oGl);
 #pragma unroll
             for (int kb = 0; kb < KT; ++kb) {
-                const f32x4 gl = ld4(img + I::oGl + kb * 16 + 4 * lg);
+                const f32x4 gl = ld4(glp + kb * 16 + 4 * lg);
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) dm[gi][kb] *= gl;
+                const int at1 = I::oA1 + (kb * 16 + lr) * LC + 8 * lg, at2 = I::oA2 + (kb * 16 + lr) * LC + 8 * lg;
+                const bf16x8 a1h = ld8(im + at1), a1l = ld8(im + at1 + K * LC);
+                const bf16x8 a2h = ld8(im + at2), a2l = ld8(im + at2 + K * LC);
 #pragma unroll
-                for (int b2 = 0; b2 < 2; ++b2) {
-                    const f32x4 a1 = ld4(img + I::oA1 + (kb * 16 + lr) * LC + b2 * 16 + 4 * lg);
-                    const f32x4 a2 = ld4(img + I::oA2 + (kb * 16 + lr) * LC + b2 * 16 + 4 * lg);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int gi = 0; gi < NG; ++gi) {
-                            dm[gi][kb] = mma4(a1[j], dof[gi][b2][j], dm[gi][kb]);
-                            dm[gi][kb] = mma4(a2[j], dr[gi][b2][j], dm[gi][kb]);
-                        }
+                for (int gi = 0; gi < NG; ++gi) {
+                    dm[gi][kb] = mfma32(a1h, dob[gi], dm[gi][kb]);
+                    dm[gi][kb] = mfma32(a1l, dob[gi], dm[gi][kb]);
+                    dm[gi][kb] = mfma32(a2h, rbh[gi], dm[gi][kb]);
+                    dm[gi][kb] = mfma32(a2h, rbl[gi], dm[gi][kb]);
+                    dm[gi][kb] = mfma32(a2l, rbh[gi], dm[gi][kb]);
                 }
             }
-        }
-        __syncthreads();
+        }        __syncthreads();
     }
     if (carry && s.dm_out) {
         float *dst = s.dm_out + (static_cast<size_t>(b) * HV + hv) * K * V;

@@ -512,10 +512,13 @@ def test_chunk_bwd_workspace_size():
     up = lambda floats: (floats * 4 + 255) // 256 * 256
 
     def img(K):
-        # k Lambda' [32][K+4]; s (q Gamma)^T and -(beta k Gamma)^T [K][36];
-        # s A_qk^T [32][36]; T11^T, T22^T, -A21^T [16][20]; Gamma_last [K]
-        # (the whole padded to a multiple of 1024 floats)
-        return (32 * (K + 4) + 2 * K * 36 + 32 * 36 + 3 * 16 * 20 + K + 1023) // 1024 * 1024
+        # bf16 hi/lo pairs: k Lambda' [2][32][K+8]; s (q Gamma)^T and
+        # -(beta k Gamma)^T [2][K][40]; s A_qk^T [2][32][40]; T11^T, T22^T,
+        # -A21^T [2][16][20]; then (at a multiple of 8 elements) Gamma_last [K]
+        # fp32; the whole in floats, padded to a multiple of 1024
+        b16 = 2 * 32 * (K + 8) + 2 * 2 * K * 40 + 2 * 32 * 40 + 3 * 2 * 16 * 20
+        b16 = (b16 + 7) // 8 * 8 + 2 * K
+        return (b16 // 2 + 1023) // 1024 * 1024
 
     def want(B, T, HV, K, V):
         # slabs of Ls = 1024 tokens (T rounded up to 32 when shorter), NC = Ls/32
