@@ -19,7 +19,8 @@ Headline workload (one JSON line on stdout):
     kda_output_gate) against the HBM peak, the HV96 workload with an
     unbounded gate (kda_chunk_fwd_unbounded against the HBM peak, and
     kda_recurrent_fwd against the fp32 vector peak), and the
-    backward on the HV96 workload: kda_chunk_bwd (fp32 matrix cores) and
+    backward on the HV96 workload: kda_chunk_bwd (matrix cores: fp32, and bf16
+    pairs in its reverse chain) and
     kda_recurrent_bwd (fp32 vector ALUs).
 Inputs are seeded synthetic tensors (gated_delta_rule_kda_amd.synth) created on
 the GPU before the timed region.  Kernel durations come from HIP events
