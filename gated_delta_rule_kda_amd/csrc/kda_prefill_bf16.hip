@@ -1245,10 +1245,16 @@ hipError_t launch_kvt(const PrefillArgs &a, hipStream_t stream) {
 
 template <int K>
 hipError_t launch_k(const PrefillArgs &a, hipStream_t stream) {
-    // Split V across two workgroups when there are too few (b, hv) chains to
-    // occupy the GPU; each chain is otherwise one workgroup.
+    // Split V across two workgroups when the halves of every (b, hv) chain all
+    // fit on the GPU at once (one workgroup per CU): a chunk takes less time
+    // with half of V.  With more chains the split would queue a second round
+    // of workgroups behind the first, so each chain is then one workgroup.
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
     const long chains = static_cast<long>(a.B) * a.HV;
-    const bool split = a.V >= 64 && chains < 160;
+    const bool split = a.V >= 64 && 2 * chains <= cus;
     if (a.V == 128) return split ? launch_kvt<K, 64>(a, stream) : launch_kvt<K, 128>(a, stream);
     if (a.V == 64) return split ? launch_kvt<K, 32>(a, stream) : launch_kvt<K, 64>(a, stream);
     return launch_kvt<K, 32>(a, stream);
