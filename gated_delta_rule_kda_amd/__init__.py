@@ -493,13 +493,14 @@ def kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=Fal
     """KDA forward with autograd: the interface of naive_kda on the
     "K3/kda/ops/reference/recurrent.py" page.  Returns (o, final state or
     None); gradients reach q, k, v, g, beta and initial_state.  The forward:
-    chunked with ``bounded_gate`` (-5 <= g <= 0), kda_chunk_fwd; chunked
-    without it, kda_chunk_fwd_unbounded for bf16 inputs (any g <= 0, each
-    token's g floored at -17) and kda_recurrent_fwd for fp32; not chunked,
-    kda_recurrent_fwd (any g).  The backward is kda_chunk_bwd after a chunked
-    bf16 forward with the bounded gate, else kda_recurrent_bwd (which takes g
-    as given: where the forward floored it, the two differ by the gradient of
-    less than e^-17 of the state)."""
+    chunked with ``bounded_gate`` (-5 <= g <= 0), kda_chunk_fwd (for bf16 its
+    snapshot form, keeping the state every 1024 tokens for the backward);
+    chunked without it, kda_chunk_fwd_unbounded for bf16 inputs (any g <= 0,
+    each token's g floored at -17) and kda_recurrent_fwd for fp32; not
+    chunked, kda_recurrent_fwd (any g).  The backward is kda_chunk_bwd_saved
+    (given those states) after a chunked bf16 forward with the bounded gate,
+    else kda_recurrent_bwd (which takes g as given: where the forward floored
+    it, the two differ by the gradient of less than e^-17 of the state)."""
     o, S = _KDA.apply(q, k, v, g, beta, initial_state, scale, chunked, bounded_gate)
     return o, (S if output_final_state else None)
 
