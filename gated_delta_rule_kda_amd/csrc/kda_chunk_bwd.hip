@@ -1033,13 +1033,13 @@ hipError_t launch_pass(Pass p, const SlabArgs &s, hipStream_t stream) {
     }
 }
 
-// The two further streams of the backward (one pair per device, default
+// The three further streams of the backward (one set per device, default
 // priority, created on first use) and the events that order them against the
 // caller's.  The mutex makes one call's enqueue sequence atomic, so calls from
 // several host threads on one device do not interleave their event records.
 struct SideStream {
     std::mutex mu;
-    hipStream_t y = nullptr, z = nullptr;
+    hipStream_t y = nullptr, z = nullptr, w = nullptr;
     hipEvent_t start = nullptr, st = nullptr, p0[2] = {}, prep[2] = {}, chain[2] = {}, grad[2] = {};
     hipEvent_t zdone = nullptr;
     bool ready = false;   // every stream and event above created
@@ -1061,6 +1061,7 @@ hipError_t side_stream(hipStream_t stream, SideStream **out) {
     if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
     e = hipStreamCreateWithFlags(&ss.y, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&ss.z, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&ss.w, hipStreamNonBlocking);
     hipEvent_t *evs[] = {&ss.start, &ss.st, &ss.p0[0], &ss.p0[1], &ss.prep[0], &ss.prep[1],
                          &ss.chain[0], &ss.chain[1], &ss.grad[0], &ss.grad[1], &ss.zdone};
     for (hipEvent_t *ev : evs)
@@ -1076,19 +1077,19 @@ int chunk_bwd_image_floats(int K) {
     return K == 32 ? Img<32>::floats : K == 64 ? Img<64>::floats : K == 128 ? Img<128>::floats : 0;
 }
 
-// Slab by slab from the last, on three streams.  The caller's stream X runs
-// the chain of state gradients, slab after slab.  A second stream Y runs what
-// the chain and the gradient pass consume and does not depend on them -- the
-// whole-sequence forward pass, then per slab its forward pass and the operand
-// images -- ahead of X; a third, Z, runs each slab's gradient pass and dg sums
-// once its chain is done, beside the chain of the slab before.  Y and Z use
-// the CUs the chain leaves idle (one workgroup per head).  Per-slab buffers
-// that one stream writes while another may still read the previous slab's
-// (chunk-start states, W, U, images from Y; dR and every chunk's dM' from X)
-// are double-buffered by slab parity, and each is overwritten only after the
-// pass of the slab two before that reads it is done.  X waits for Z's last
-// work before the call's enqueue ends, so work enqueued on X afterwards runs
-// after all of it.
+// Slab by slab from the last, on four streams.  The caller's stream X runs
+// the chain of state gradients, slab after slab.  A second stream Y runs the
+// forward passes the chain's consumers need -- the whole sequence, then each
+// slab -- and a third, W, the operand images, which depend on the inputs
+// alone, both ahead of X; a fourth, Z, runs each slab's gradient pass and dg
+// sums once its chain is done, beside the chain of the slab before.  Y, W and
+// Z use the CUs the chain leaves idle (one workgroup per head).  Per-slab
+// buffers that one stream writes while another may still read the previous
+// slab's (chunk-start states, W, U from Y; images from W; dR and every
+// chunk's dM' from X) are double-buffered by slab parity, and each is
+// overwritten only after the pass of the slab two before that reads it is
+// done.  X waits for Z's last work before the call's enqueue ends, so work
+// enqueued on X afterwards runs after all of it.
 //
 // While the caller's stream is being captured into a graph, every pass runs
 // in the same order on that stream alone: no side streams, events or stream
@@ -1112,13 +1113,14 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
     const bool serial = cap != hipStreamCaptureStatusNone;
     SideStream none, *ss = &none;   // none: events never used (serial)
     std::unique_lock<std::mutex> lock;
-    hipStream_t X = stream, Y = stream, Z = stream;
+    hipStream_t X = stream, Y = stream, Z = stream, W = stream;
     if (!serial) {
         e = side_stream(stream, &ss);
         if (e != hipSuccess) return e;
         lock = std::unique_lock<std::mutex>(ss->mu);
         Y = ss->y;
         Z = ss->z;
+        W = ss->w;
     }
     auto rec = [&](hipEvent_t ev, hipStream_t s) { return serial ? hipSuccess : hipEventRecord(ev, s); };
     auto wait = [&](hipStream_t s, hipEvent_t ev) { return serial ? hipSuccess : hipStreamWaitEvent(s, ev, 0); };
@@ -1126,6 +1128,7 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
     KDA_TRY(rec(ss->start, X));
     KDA_TRY(wait(Y, ss->start));
     KDA_TRY(wait(Z, ss->start));
+    KDA_TRY(wait(W, ss->start));
     const int ns = (a.T + a.Ls - 1) / a.Ls;
     // 0. the whole sequence once: S_T and the states at the slab starts
     // (given by the caller in the saved variant)
@@ -1182,10 +1185,11 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         f.scale = a.scale; f.bf16 = true; f.bwd = true;
         KDA_TRY(launch_prefill_bf16(f, Y));
         KDA_TRY(rec(ss->p0[p], Y));
-        // Y: the operand images, once the chain of slab si + 2 has read them
-        if (j >= 2) KDA_TRY(wait(Y, ss->chain[p]));
-        KDA_TRY(launch_pass(Pass::prep, s, Y));
-        KDA_TRY(rec(ss->prep[p], Y));
+        // W: the operand images (from the inputs alone), once the chain of
+        // slab si + 2 has read this parity's
+        if (j >= 2) KDA_TRY(wait(W, ss->chain[p]));
+        KDA_TRY(launch_pass(Pass::prep, s, W));
+        KDA_TRY(rec(ss->prep[p], W));
         // X: the chain, once the images are there and the gradient pass of
         // slab si + 2 has read this parity's dR and dM'
         KDA_TRY(wait(X, ss->prep[p]));
@@ -1202,7 +1206,7 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
                            gc[j & 1], gc[(j + 1) & 1]);
         KDA_TRY(hipGetLastError());
     }
-    // everything on Y ends in work X or Z waited for; Z's end joins X
+    // everything on Y and W ends in work X or Z waited for; Z's end joins X
     KDA_TRY(rec(ss->zdone, Z));
     KDA_TRY(wait(X, ss->zdone));
 #undef KDA_TRY

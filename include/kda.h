@@ -267,8 +267,8 @@ int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *
  * forming the reverse chain's operands, the reverse chain of state gradients
  * (one workgroup per value head), a chunk-parallel pass for dq, dk, dv, dbeta
  * and the dg terms, and the reverse sum that forms dg.  The chain runs on
- * `stream`; the forward passes and the operand pass, and the gradient pass
- * with the dg sum, run on two further streams of the library's (one pair per
+ * `stream`; the forward passes, the operand pass, and the gradient pass
+ * with the dg sum run on three further streams of the library's (one set per
  * device, default priority, created on the first call), ordered against
  * `stream` by events; the call returns when all is enqueued, and work
  * enqueued on `stream` afterwards runs after all of it.  Calls from several

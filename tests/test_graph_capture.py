@@ -1,6 +1,6 @@
 """HIP graph capture of the entry points a serving or training loop would
 capture: kda_chunk_fwd, kda_chunk_fwd_unbounded (its two kernels), and
-kda_chunk_bwd / kda_chunk_bwd_saved (eagerly on three streams joined by
+kda_chunk_bwd / kda_chunk_bwd_saved (eagerly on four streams joined by
 events; while captured, every pass in order on the captured stream).  Each graph is replayed several times, with new input values written
 in place and the program's own eager work and synchronizations between the
 replays, and every replay must give the eager call's bits on those inputs."""
@@ -88,8 +88,9 @@ def test_graph_chunk_fwd_unbounded():
 
 @pytest.mark.parametrize("saved", [False, True])
 def test_graph_chunk_bwd(saved):
-    """Three slabs (T = 2100): the library's two side streams fork from and
-    join the captured stream through its events."""
+    """Three slabs (T = 2100): captured, the passes run in order on the
+    captured stream; each replay must give the eager call's bits, which runs
+    them on four streams joined by events."""
     B, T, H, HV, K, V = 1, 2100, 1, 2, 64, 64
     shape = synth.PrefillShape(B, T, H, HV, K, V, torch.bfloat16, "normal", s0_std=0.3, g_lower=-1.0)
     inp = synth.make_prefill_inputs(shape, DEV, 3)
