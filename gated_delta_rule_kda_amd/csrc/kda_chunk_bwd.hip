@@ -214,22 +214,41 @@ __device__ __forceinline__ void chunk_cumsum(const float *g, int nv, int row_str
 }
 
 // ---------------------------------------------------------------- 1. prep
-// One workgroup per (b, hv, chunk of the slab).
+// One workgroup per (b, hv, chunk of the slab).  The element-wise parts of
+// the image (k Lambda', s (q Gamma)^T, -(beta k Gamma)^T, Gamma_last) go
+// straight to HBM, each thread a 16-byte hi and lo piece of 8 reduction
+// indices that perm32 keeps together; the products (A_qk, Pk Rk^T) form
+// their scaled operands as the MFMAs read them, from q and k in LDS as bf16
+// and G.  Only the image's in-chunk matrices (s A_qk^T, T11^T, T22^T,
+// -A21^T) are staged in LDS and copied out: about 48 KB of LDS, so that
+// several workgroups share a CU and hide each other's latency.
 template <int K>
-__global__ __launch_bounds__(kThr) void cbwd_prep_kernel(SlabArgs s) {
+struct PrepPlan {
     using I = Img<K>;
-    constexpr int LK = K + 4;                         // fp32 [C][K] working arrays
+    static constexpr int LK = K + 4;           // fp32 [C][K] G
+    static constexpr int LQ = K + 8;           // bf16 [C][K] q, k
+    static constexpr int tail = I::oAq;        // image elements staged in LDS: [oAq, oGl)
+    static constexpr int ntail = I::oGl - I::oAq;
+    static constexpr int bytes = (kC * LK + kThr + kC + 2 * 16 * 20) * 4 + 2 * kC * LQ * 2 + ntail * 2;
+    static_assert(ntail % 8 == 0, "16-byte copy of the staged part");
+};
+
+// (at least 6 waves per SIMD: three workgroups per CU, 80 VGPRs at K = 128)
+template <int K>
+__global__ __launch_bounds__(kThr, 6) void cbwd_prep_kernel(SlabArgs s) {
+    using I = Img<K>;
+    using P = PrepPlan<K>;
+    constexpr int LK = P::LK, LQ = P::LQ;
     constexpr int IK = I::LK, IC = I::LC, L16 = I::L16;   // image pitches (bf16)
     const ChunkBwdArgs &a = s.a;
     extern __shared__ __attribute__((aligned(16))) float sm[];
-    float *img = sm;                        // [I::floats]
-    float *sPq = img + I::floats;           // [C][LK] q e1, k e1, k e2
-    float *sPk = sPq + kC * LK;
-    float *sRk = sPk + kC * LK;
-    float *sG = sRk + kC * LK;              // [C][LK]
+    float *sG = sm;                         // [C][LK] base-2 cumulative sums
     float *sTot = sG + kC * LK;             // [kThr] partial column sums
     float *sB = sTot + kThr;                // [C] beta
     float *sAb = sB + kC;                   // [2][16][L16] diagonal blocks of A_kk
+    uint16_t *sQ = reinterpret_cast<uint16_t *>(sAb + 2 * 16 * L16);   // [C][LQ] bf16 q, k
+    uint16_t *sK = sQ + kC * LQ;
+    __bf16 *st = reinterpret_cast<__bf16 *>(sK + kC * LQ);   // image elements [oAq, oGl)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const int n = blockIdx.x % s.NCs;
@@ -240,54 +259,92 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_kernel(SlabArgs s) {
     const size_t tok = static_cast<size_t>(b) * a.T + t0;
     const uint16_t *qg = static_cast<const uint16_t *>(a.q);
     const uint16_t *kg = static_cast<const uint16_t *>(a.k);
-    __bf16 *im = reinterpret_cast<__bf16 *>(img);
-    // x as its bf16 pair: hi at element at, lo at + half (the array's lo half)
+    // this chunk's image in HBM, as bf16 elements
+    __bf16 *gim = reinterpret_cast<__bf16 *>(a.img + ((static_cast<size_t>(b) * s.NCs + n) * a.HV + hv) * I::floats);
+    // x as its bf16 pair in the staged part: hi at image element at, lo at + half
     auto put = [&](int at, int half, float x) {
-        __bf16 h, l;
-        split1(x, h, l);
-        im[at] = h;
-        im[at + half] = l;
+        __bf16 hi, lo;
+        split1(x, hi, lo);
+        st[at - P::tail] = hi;
+        st[at - P::tail + half] = lo;
+    };
+    // 8 values as bf16 pairs, to image elements at (hi) and at + half (lo) in HBM
+    auto put8 = [&](int at, int half, const float (&x)[8]) {
+        bf16x4 h0, l0, h1, l1;
+        split4(f32x4{x[0], x[1], x[2], x[3]}, h0, l0);
+        split4(f32x4{x[4], x[5], x[6], x[7]}, h1, l1);
+        *reinterpret_cast<bf16x8 *>(gim + at) = cat(h0, h1);
+        *reinterpret_cast<bf16x8 *>(gim + at + half) = cat(l0, l1);
     };
 
-    chunk_cumsum<K, kThr>(a.g + (tok * a.HV + hv) * K, nv, a.HV * K, sG, LK, sTot);
-    if (tid < kC) sB[tid] = tid < nv ? a.beta[(tok + tid) * a.HV + hv] : 0.f;
-    __syncthreads();
-
-    // element-wise operands: 8 columns of one row per thread (16-byte loads of q, k)
+    // q, k of the chunk as bf16 rows, 16 bytes per unit (rows past the end 0)
     for (int u = tid; u < kC * K / 8; u += kThr) {
-        const int i = u / (K / 8), c0 = (u % (K / 8)) * 8;
+        const int i = u / (K / 8), c = (u % (K / 8)) * 8;
         uint4 wq = make_uint4(0u, 0u, 0u, 0u), wk = wq;
         if (i < nv) {
-            const size_t qi = ((tok + i) * a.H + h) * K + c0;
+            const size_t qi = ((tok + i) * a.H + h) * K + c;
             wq = *reinterpret_cast<const uint4 *>(qg + qi);
             wk = *reinterpret_cast<const uint4 *>(kg + qi);
         }
-        const uint32_t q8[4] = {wq.x, wq.y, wq.z, wq.w}, k8[4] = {wk.x, wk.y, wk.z, wk.w};
-        const float bi = sB[i];
+        *reinterpret_cast<uint4 *>(sQ + i * LQ + c) = wq;
+        *reinterpret_cast<uint4 *>(sK + i * LQ + c) = wk;
+    }
+    chunk_cumsum<K, kThr>(a.g + (tok * a.HV + hv) * K, nv, a.HV * K, sG, LK, sTot);
+    if (tid < kC) sB[tid] = tid < nv ? a.beta[(tok + tid) * a.HV + hv] : 0.f;
+    __syncthreads();
+    auto qat = [&](int i, int c) { return bf2f(sQ[i * LQ + c]); };
+    auto kat = [&](int i, int c) { return bf2f(sK[i * LQ + c]); };
+    // index e of the 8 that perm32 places at 8 g .. 8 g + 7 of a block of 32
+    auto pidx = [](int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); };
+
+    // k Lambda' [token i][channels of group m], 16 bytes per piece
+    for (int u = tid; u < kC * K / 8; u += kThr) {
+        const int i = u / (K / 8), m = u % (K / 8), c0 = (m / 4) * 32, g = m % 4;
+        float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int c = c0 + e;
-            const float qv = __uint_as_float(e & 1 ? q8[e >> 1] & 0xffff0000u : q8[e >> 1] << 16);
-            const float kv = __uint_as_float(e & 1 ? k8[e >> 1] & 0xffff0000u : k8[e >> 1] << 16);
-            const float Gi = sG[i * LK + c], Gr = sG[kR * LK + c], Gl = sG[(kC - 1) * LK + c];
-            const float e1 = ex2(Gi - Gr), e2 = ex2(Gr - Gi), gam = ex2(Gi), lam = ex2(Gl - Gi);
-            sPq[i * LK + c] = qv * e1;
-            sPk[i * LK + c] = kv * e1;
-            sRk[i * LK + c] = kv * e2;
-            put(I::oKb + i * IK + perm32(c), kC * IK, kv * lam);
-            put(I::oA1 + c * IC + perm32(i), K * IC, a.scale * qv * gam);
-            put(I::oA2 + c * IC + perm32(i), K * IC, -bi * kv * gam);
-            if (i == kC - 1) reinterpret_cast<float *>(im + I::oGl)[c] = ex2(Gl);
+            const int c = c0 + pidx(g, e);
+            x[e] = kat(i, c) * ex2(sG[(kC - 1) * LK + c] - sG[i * LK + c]);
         }
+        put8(I::oKb + i * IK + c0 + 8 * g, kC * IK, x);
     }
-    __syncthreads();
+    // s (q Gamma)^T and -(beta k Gamma)^T [channel c][tokens of group g]
+    for (int u = tid; u < K * 4; u += kThr) {
+        const int c = u / 4, g = u % 4;
+        float x1[8], x2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = pidx(g, e);
+            const float gam = ex2(sG[i * LK + c]);
+            x1[e] = a.scale * qat(i, c) * gam;
+            x2[e] = -sB[i] * kat(i, c) * gam;
+        }
+        put8(I::oA1 + c * IC + 8 * g, K * IC, x1);
+        put8(I::oA2 + c * IC + 8 * g, K * IC, x2);
+    }
+    // Gamma_last, fp32
+    for (int c = tid; c < K; c += kThr)
+        reinterpret_cast<float *>(gim + I::oGl)[c] = ex2(sG[(kC - 1) * LK + c]);
 
-    // A_qk (waves 0-2) and Pk Rk^T (waves 3-5), lower tiles (0,0), (1,0), (1,1)
+    // A_qk (waves 0-2) and Pk Rk^T (waves 3-5), lower tiles (0,0), (1,0), (1,1):
+    // rows X e1 (X = q or k) against columns k e2, e1 = 2^{G_i - G_r} and
+    // e2 = 2^{G_r - G_j} formed per operand element
     if (wave < 6) {
         const int t = wave % 3, rt = t == 0 ? 0 : 1, ct = t == 2 ? 1 : 0;
-        const float *X = wave < 3 ? sPq : sPk;
+        const uint16_t *X = wave < 3 ? sQ : sK;
+        const int xr = rt * 16 + lr, yr = ct * 16 + lr;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        tile_nt<K>(X + (rt * 16 + lr) * LK, sRk + (ct * 16 + lr) * LK, lg, acc);
+#pragma unroll 4
+        for (int k0 = 0; k0 < K; k0 += 16) {
+            const int c = k0 + 4 * lg;
+            const f32x4 gx = ld4(sG + xr * LK + c), gy = ld4(sG + yr * LK + c), gr = ld4(sG + kR * LK + c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float xa = bf2f(X[xr * LQ + c + j]) * ex2(gx[j] - gr[j]);
+                const float yb = kat(yr, c + j) * ex2(gr[j] - gy[j]);
+                acc = mma4(xa, yb, acc);
+            }
+        }
         if (wave < 3) {
             // s A_qk^T: element (col, row) of A_qk, lower including the diagonal
 #pragma unroll
@@ -338,10 +395,9 @@ __global__ __launch_bounds__(kThr) void cbwd_prep_kernel(SlabArgs s) {
         for (int e = 0; e < 4; ++e) put(oT + (4 * q + e) * L16 + i, 16 * L16, x[e]);
     }
     __syncthreads();
-    // the image to HBM, 16 bytes per thread
-    float4 *dst = reinterpret_cast<float4 *>(a.img + ((static_cast<size_t>(b) * s.NCs + n) * a.HV + hv) * I::floats);
-    const float4 *src = reinterpret_cast<const float4 *>(img);
-    for (int u = tid; u < I::floats / 4; u += kThr) dst[u] = src[u];
+    // the staged in-chunk matrices to HBM, 16 bytes per thread
+    for (int u = tid; u < P::ntail / 8; u += kThr)
+        *reinterpret_cast<bf16x8 *>(gim + P::tail + 8 * u) = *reinterpret_cast<const bf16x8 *>(st + 8 * u);
 }
 
 // ---------------------------------------------------------------- 2. chain
@@ -968,7 +1024,7 @@ __global__ __launch_bounds__(256) void cbwd_dg_kernel(SlabArgs s, const float *g
 }
 
 template <int K>
-constexpr int prep_lds() { return (Img<K>::floats + 4 * kC * (K + 4) + kThr + kC + 2 * 16 * 20) * 4; }
+constexpr int prep_lds() { return PrepPlan<K>::bytes; }
 template <int K, int VT>
 constexpr int chain_lds() { return 2 * (Img<K>::floats + (kC * (VT + 8) * 2 + 15) / 16 * 4) * 4; }
 template <int K, int V>
