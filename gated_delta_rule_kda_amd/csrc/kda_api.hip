@@ -270,10 +270,10 @@ bool bwd_layout(BwdLayout &L, int B, int T, int HV, int K, int V) {
 // bytes).  Slabs of Ls tokens (1024, or T rounded up to the chunk when
 // shorter); everything but the final state and the slab-start states holds one
 // slab, and what one stream produces while another still reads the previous
-// slab's (chunk-start states, W, U, operand images, dR, every chunk's dM') two,
+// slab's (chunk-start states, U, operand images, dR, every chunk's dM') two,
 // by slab parity.
 struct ChunkBwdLayout {
-    uint64_t st, snap1, Dc, snapc, W, U, img, snapc2, W2, U2, img2, dR, dMs, dR2, dMs2, e, cs, gc, total;
+    uint64_t st, snap1, Dc, snapc, U, img, snapc2, U2, img2, dR, dMs, dR2, dMs2, e, cs, gc, total;
     int Ls, NS1, NCs;
 };
 
@@ -295,8 +295,8 @@ bool chunk_bwd_layout(ChunkBwdLayout &L, int B, int T, int HV, int K, int V) {
         return at;
     };
     L.st = take(ns); L.snap1 = take(nsn); L.Dc = take(ns); L.snapc = take(nsc);
-    L.W = take(nv); L.U = take(nv); L.img = take(nimg);
-    L.snapc2 = take(nsc); L.W2 = take(nv); L.U2 = take(nv); L.img2 = take(nimg);
+    L.U = take(nv); L.img = take(nimg);
+    L.snapc2 = take(nsc); L.U2 = take(nv); L.img2 = take(nimg);
     L.dR = take(nv); L.dMs = take(nms);
     L.dR2 = take(nv); L.dMs2 = take(nms);
     L.e = take(ne); L.cs = take(ncs); L.gc = take(ngc);
@@ -509,8 +509,8 @@ int chunk_bwd_impl(const char *fn, bool saved, const void *q, const void *k, con
     if (work) {
         auto at = [&](uint64_t off) { return reinterpret_cast<float *>(ws + off); };
         a.ST = at(L.st); a.snap1 = at(L.snap1); a.Dc = at(L.Dc); a.snapc = at(L.snapc);
-        a.W = at(L.W); a.U = at(L.U); a.img = at(L.img); a.dR = at(L.dR); a.dMs = at(L.dMs);
-        a.snapc2 = at(L.snapc2); a.W2 = at(L.W2); a.U2 = at(L.U2); a.img2 = at(L.img2);
+        a.U = at(L.U); a.img = at(L.img); a.dR = at(L.dR); a.dMs = at(L.dMs);
+        a.snapc2 = at(L.snapc2); a.U2 = at(L.U2); a.img2 = at(L.img2);
         a.dR2 = at(L.dR2); a.dMs2 = at(L.dMs2);
         a.e = at(L.e); a.cs = at(L.cs); a.gc = at(L.gc);
         if (saved) {

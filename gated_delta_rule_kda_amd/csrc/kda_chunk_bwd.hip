@@ -19,7 +19,8 @@
 //     dk_read  = beta (.) (-Gamma (.) (dR M^T) + e1 (.) (dA_kk Rk))
 //     dk_write = Lambda' (.) (U dM'^T) + e2 (.) (dA_qk^T Pq + (beta dA_kk)^T Pk)
 //     dk = dk_read + dk_write,  dv = beta dR,
-//     dbeta = rowsum(dR (.) W) + rowsum(dA_kk (.) SL(Pk Rk^T))
+//     dbeta = rowsum(dR (.) W) + rowsum(dA_kk (.) SL(Pk Rk^T)), where
+//     rowsum(dR (.) W) = rowsum(dR (.) v) - rowsum((k Gamma) (.) dR M^T)
 // and dg from the same identity the token-recurrent backward uses: a change
 // of g_u scales every read at t >= u against every write before u, so
 //     dg_u = sum_{t >= u} (q (.) dq + k (.) dk_read - k (.) dk_write)_t
@@ -34,7 +35,7 @@
 //  0. a forward pass over the whole sequence keeps S_T and the states at the
 //     slab starts; per slab, the forward kernel's backward instantiation runs
 //     the slab again from its start state, keeping the state at every chunk
-//     start, W and U (kda_prefill_bf16.hip);
+//     start and U (kda_prefill_bf16.hip);
 //  1. prep (chunk-parallel): every chunk's operands of the reverse chain --
 //     k Lambda', s (q Gamma)^T, -(beta k Gamma)^T, s A_qk^T, T11^T, T22^T,
 //     -A21^T, Gamma_last -- as the exact LDS image the chain kernel reads
@@ -660,7 +661,8 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
     float *sB = sTot + kThrG;               // [C] beta
     float *sDb = sB + kC;                   // [4][C] partial dbeta
     float *sCs = sDb + 4 * kC;              // [8][K] partial column sums of the dg terms
-    uint16_t *sQ = reinterpret_cast<uint16_t *>(sCs + 8 * K);    // [C][LQ] bf16 q, k
+    float *sXw = sCs + 8 * K;               // [K/16][C] partial rowsum((k Gamma) (.) dR M^T)
+    uint16_t *sQ = reinterpret_cast<uint16_t *>(sXw + 8 * kC);   // [C][LQ] bf16 q, k
     uint16_t *sK = sQ + kC * LQ;
     uint16_t *sdO = sK + kC * LQ;           // [C][LO] bf16 dO
 
@@ -709,7 +711,7 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
         // slab-local rows of this chunk in the [B, Ls, HV, V] arrays
         const size_t lrow0 = static_cast<size_t>(b) * a.Ls + n * kC;
         const float *Ug = a.U + (lrow0 * HV + hv) * V;
-        const float *Wg = a.W + (lrow0 * HV + hv) * V;
+        const uint16_t *vg = static_cast<const uint16_t *>(a.v) + (tok * HV + hv) * V;
         const float *dRg = a.dR + (lrow0 * HV + hv) * V;
         const uint16_t *dOg = dog + (tok * HV + hv) * V;
         const size_t rs = static_cast<size_t>(HV) * V;   // row stride of those arrays
@@ -826,7 +828,7 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
                 }
             }
         } else if (wave < 8) {
-            // waves 6-7: dv = beta dR, and rowsum(dR (.) W); lane = (row, quarter of V)
+            // waves 6-7: dv = beta dR, and rowsum(dR (.) v); lane = (row, quarter of V)
             const int l = tid - 384, row = l >> 2, qv = l & 3;
             float dot = 0.f;
             if (row < nv) {
@@ -834,7 +836,11 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
                 const float bt = sB[row];
                 f32x4 ww[VS];
 #pragma unroll
-                for (int st = 0; st < VS; ++st) ww[st] = ld4(Wg + row * rs + st * 16 + qv * 4);
+                for (int st = 0; st < VS; ++st) {
+                    const uint2 w2 = *reinterpret_cast<const uint2 *>(vg + row * rs + st * 16 + qv * 4);
+                    ww[st] = f32x4{__uint_as_float(w2.x << 16), __uint_as_float(w2.x & 0xffff0000u),
+                                   __uint_as_float(w2.y << 16), __uint_as_float(w2.y & 0xffff0000u)};
+                }
 #pragma unroll
                 for (int st = 0; st < VS; ++st) {
                     const int c = st * 16 + qv * 4;
@@ -851,11 +857,6 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
             if (qv == 0) sDb[2 * kC + row] = dot;
         }
         __syncthreads();
-        if (tid < nv) {
-            // rows 0-15 have one A_kk tile term, rows 16-31 two
-            const float dA = sDb[tid] + (tid >= 16 ? sDb[kC + tid] : 0.f);
-            a.dbeta[(tok + tid) * HV + hv] = sDb[2 * kC + tid] + dA;
-        }
 
         // [C x K] results: tiles (rt, ct) of this wave.  Its rows of M (the
         // state at the chunk start) and dM' (the gradient at its end) are
@@ -915,7 +916,7 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
                 tile_nt<kC>(sDkbT + xr * LC, sPkT + yr * LC, lg, y3);
                 const int c = ct * 16 + lr;
                 const float Gr = sG[kR * LK + c], Gl = sG[(kC - 1) * LK + c];
-                float csum = 0.f;
+                float csum = 0.f, wx[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int i = rt * 16 + 4 * lg + j;
@@ -931,8 +932,16 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
                     csum += term;
                     dqa[u][j] += dq;
                     dka[u][j] += dkr + dkw;
+                    wx[j] = k * gam * x2[u][j];
                 }
                 sCs[(rt * 4 + lg) * K + c] = csum;
+                // this column block's part of rowsum((k Gamma) (.) dR M^T)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wx[j] = group_sum<16>(wx[j]);
+                if (lr == 0) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sXw[ct * kC + rt * 16 + 4 * lg + j] = wx[j];
+                }
             }
         }
         // the chunk's sum of the dg terms per column, for the reverse sum over chunks
@@ -942,6 +951,15 @@ __global__ __launch_bounds__(kThrG, 1) void cbwd_grad_kernel(SlabArgs s) {
 #pragma unroll
             for (int r = 0; r < 8; ++r) cs += sCs[r * K + tid];
             a.cs[((static_cast<size_t>(b) * HV + hv) * s.NCs + n) * K + tid] = cs;
+        }
+        if (tid < nv) {
+            // dbeta: rowsum(dR (.) v) - rowsum((k Gamma) (.) dR M^T) (= rowsum(dR (.) W))
+            // and the A_kk tile terms (rows 0-15 one, rows 16-31 two)
+            float wx = 0.f;
+#pragma unroll
+            for (int cb = 0; cb < KT; ++cb) wx += sXw[cb * kC + tid];
+            const float dA = sDb[tid] + (tid >= 16 ? sDb[kC + tid] : 0.f);
+            a.dbeta[(tok + tid) * HV + hv] = (sDb[2 * kC + tid] - wx) + dA;
         }
     }
     // dq, dk (bf16) of the chunk's rows inside the sequence
@@ -1029,7 +1047,7 @@ template <int K, int VT>
 constexpr int chain_lds() { return 2 * (Img<K>::floats + (kC * (VT + 8) * 2 + 15) / 16 * 4) * 4; }
 template <int K, int V>
 constexpr int grad_lds() {
-    return (kC * (K + 4) + 3 * K * (kC + 4) + 4 * kC * (kC + 4) + 2 * kC * (V + 4) + kThrG + kC + 4 * kC + 8 * K) * 4
+    return (kC * (K + 4) + 3 * K * (kC + 4) + 4 * kC * (kC + 4) + 2 * kC * (V + 4) + kThrG + kC + 4 * kC + 8 * K + 8 * kC) * 4
          + (2 * kC * (K + 8) + kC * (V + 8)) * 2;
 }
 
@@ -1136,12 +1154,12 @@ int chunk_bwd_image_floats(int K) {
 // Slab by slab from the last, on four streams.  The caller's stream X runs
 // the chain of state gradients, slab after slab.  A second stream Y runs the
 // forward passes the chain's consumers need -- the whole sequence, then each
-// slab -- and a third, W, the operand images, which depend on the inputs
+// slab -- and a third, P, the operand images, which depend on the inputs
 // alone, both ahead of X; a fourth, Z, runs each slab's gradient pass and dg
-// sums once its chain is done, beside the chain of the slab before.  Y, W and
+// sums once its chain is done, beside the chain of the slab before.  Y, P and
 // Z use the CUs the chain leaves idle (one workgroup per head).  Per-slab
 // buffers that one stream writes while another may still read the previous
-// slab's (chunk-start states, W, U from Y; images from W; dR and every
+// slab's (chunk-start states and U from Y; images from P; dR and every
 // chunk's dM' from X) are double-buffered by slab parity, and each is
 // overwritten only after the pass of the slab two before that reads it is
 // done.  X waits for Z's last work before the call's enqueue ends, so work
@@ -1169,14 +1187,14 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
     const bool serial = cap != hipStreamCaptureStatusNone;
     SideStream none, *ss = &none;   // none: events never used (serial)
     std::unique_lock<std::mutex> lock;
-    hipStream_t X = stream, Y = stream, Z = stream, W = stream;
+    hipStream_t X = stream, Y = stream, Z = stream, P = stream;
     if (!serial) {
         e = side_stream(stream, &ss);
         if (e != hipSuccess) return e;
         lock = std::unique_lock<std::mutex>(ss->mu);
         Y = ss->y;
         Z = ss->z;
-        W = ss->w;
+        P = ss->w;
     }
     auto rec = [&](hipEvent_t ev, hipStream_t s) { return serial ? hipSuccess : hipEventRecord(ev, s); };
     auto wait = [&](hipStream_t s, hipEvent_t ev) { return serial ? hipSuccess : hipStreamWaitEvent(s, ev, 0); };
@@ -1184,7 +1202,7 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
     KDA_TRY(rec(ss->start, X));
     KDA_TRY(wait(Y, ss->start));
     KDA_TRY(wait(Z, ss->start));
-    KDA_TRY(wait(W, ss->start));
+    KDA_TRY(wait(P, ss->start));
     const int ns = (a.T + a.Ls - 1) / a.Ls;
     // 0. the whole sequence once: S_T and the states at the slab starts
     // (given by the caller in the saved variant)
@@ -1212,7 +1230,7 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         SlabArgs s{};
         s.a = a;
         if (p) {
-            s.a.snapc = a.snapc2; s.a.W = a.W2; s.a.U = a.U2; s.a.img = a.img2;
+            s.a.snapc = a.snapc2; s.a.U = a.U2; s.a.img = a.img2;
             s.a.dR = a.dR2; s.a.dMs = a.dMs2;
         }
         s.t_begin = si * a.Ls;
@@ -1227,7 +1245,7 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         }
         s.dm_in = si == ns - 1 ? a.dST : a.Dc;
         s.dm_out = si == 0 ? a.dS0 : a.Dc;
-        // Y: the slab's forward pass (states at its chunk starts, W, U) once the
+        // Y: the slab's forward pass (states at its chunk starts, U) once the
         // gradient pass of slab si + 2 has read these buffers
         if (j >= 2) KDA_TRY(wait(Y, ss->grad[p]));
         PrefillArgs f{};
@@ -1235,17 +1253,17 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
         f.S0 = s.Sstart; f.s0_bstride = s.s_bstride;
         f.snap = s.NCs > 1 ? s.a.snapc : nullptr;
         f.snap_chunks = 1; f.NS = s.NCs - 1;
-        f.w_out = s.a.W; f.u_out = s.a.U; f.Lw = a.Ls;
+        f.u_out = s.a.U; f.Lw = a.Ls;
         f.t_off = s.t_begin; f.Tseq = a.T;
         f.B = a.B; f.T = s.len; f.H = a.H; f.HV = a.HV; f.K = a.K; f.V = a.V;
         f.scale = a.scale; f.bf16 = true; f.bwd = true;
         KDA_TRY(launch_prefill_bf16(f, Y));
         KDA_TRY(rec(ss->p0[p], Y));
-        // W: the operand images (from the inputs alone), once the chain of
+        // P: the operand images (from the inputs alone), once the chain of
         // slab si + 2 has read this parity's
-        if (j >= 2) KDA_TRY(wait(W, ss->chain[p]));
-        KDA_TRY(launch_pass(Pass::prep, s, W));
-        KDA_TRY(rec(ss->prep[p], W));
+        if (j >= 2) KDA_TRY(wait(P, ss->chain[p]));
+        KDA_TRY(launch_pass(Pass::prep, s, P));
+        KDA_TRY(rec(ss->prep[p], P));
         // X: the chain, once the images are there and the gradient pass of
         // slab si + 2 has read this parity's dR and dM'
         KDA_TRY(wait(X, ss->prep[p]));
@@ -1262,7 +1280,7 @@ hipError_t launch_chunk_backward(const ChunkBwdArgs &a, hipStream_t stream) {
                            gc[j & 1], gc[(j + 1) & 1]);
         KDA_TRY(hipGetLastError());
     }
-    // everything on Y and W ends in work X or Z waited for; Z's end joins X
+    // everything on Y and P ends in work X or Z waited for; Z's end joins X
     KDA_TRY(rec(ss->zdone, Z));
     KDA_TRY(wait(X, ss->zdone));
 #undef KDA_TRY

@@ -40,12 +40,12 @@ struct PrefillArgs {
     // (Tseq = 0 means T, t_off = 0: the whole sequence).
     int t_off, Tseq;
     // Chunked backward's forward pass (bf16 chunk kernel, with snap): when
-    // w_out is set, W = v - (k Gamma) M and U = (I + A_kk)^-1 diag(beta) W of
-    // every chunk go to w_out and u_out ([B, Lw, HV, V] fp32, token index
-    // relative to t_off) and no o is written.
-    float *w_out, *u_out;
+    // u_out is set, U = (I + A_kk)^-1 diag(beta) (v - (k Gamma) M) of every
+    // chunk goes to u_out ([B, Lw, HV, V] fp32, token index relative to
+    // t_off) and no o is written.
+    float *u_out;
     int Lw;
-    bool bwd;                   // the backward's forward pass: no o; W, U where set
+    bool bwd;                   // the backward's forward pass: no o; U where set
     long long s0_bstride;       // elements between the sequences of S0 (0: HV K V)
     // Gates without a lower bound (bf16 chunk kernel): the in-chunk matrices
     // come from img ([B,HV,NC,kUnbImgElems] bf16, written by the pass of
@@ -157,8 +157,8 @@ struct ChunkBwdArgs {
     float *dg, *dbeta;          // [B,T,HV,K], [B,T,HV]
     float *dS0;                 // [B,HV,K,V] or nullptr
     // workspace (fp32): see chunk_bwd_layout in kda_api.hip
-    float *ST, *snap1, *Dc, *snapc, *W, *U, *img, *dR, *dMs, *e, *cs, *gc;
-    float *snapc2, *W2, *U2, *img2;   // second copies for the slabs of odd index
+    float *ST, *snap1, *Dc, *snapc, *U, *img, *dR, *dMs, *e, *cs, *gc;
+    float *snapc2, *U2, *img2;   // second copies for the slabs of odd index
     float *dR2, *dMs2;
     int Ls;                     // tokens per slab (a multiple of 32)
     int NS1;                    // slab starts kept by the first forward pass (slabs - 1)

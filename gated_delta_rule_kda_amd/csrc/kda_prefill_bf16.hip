@@ -75,8 +75,8 @@
 //    rows of o as the helper waves store them: the 16 lanes holding a row of
 //    128 values sum its squares by DPP within their row of lanes.
 //  * The chunked backward's forward pass (BWD, a snapshot instantiation):
-//    no o; W = v - (k Gamma) M and U of every chunk go to the workspace from
-//    the carry's registers (fp32), and the call may cover a sub-range of the
+//    no o; U of every chunk goes to the workspace from the carry's registers
+//    (fp32), and the call may cover a sub-range of the
 //    sequences (t_off, Tseq) starting from a state with its own batch stride.
 //  * Gates without a lower bound (UNB, for kda_chunk_fwd_unbounded): A_qk,
 //    -A21, T11 and T22 come from the chunk-parallel pass of kda_unb_prep.hip
@@ -862,17 +862,6 @@ __global__ __launch_bounds__(kNT, 1) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     rr[gi][rt][r] = bt[r] * (fl(vf[gi][rt][r]) - xq[gi][rt][r]);
-                }
-        }
-        if constexpr (BWD) {
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int gi = 0; gi < NG; ++gi) {
-                    f32x4 w;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) w[r] = fl(vf[gi][rt][r]) - xq[gi][rt][r];
-                    storeTile(a.w_out, n, rt, gi, w);
                 }
         }
         // U1 = T11 R1;  Y = R2 - A21 U1;  U2 = T22 Y   (16x16x16 MFMAs, 3 terms each)

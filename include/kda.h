@@ -276,7 +276,7 @@ int kda_recurrent_bwd(const void *q, const void *k, const void *v, const float *
  * `stream` is being captured into a HIP graph, every pass is enqueued in the
  * same order on `stream` alone (no further streams or events: same results,
  * no overlap between the passes).  Workspace
- * about 1.6 GB at B = 1, T = 8192, HV = 96, K = V = 128.
+ * about 1.5 GB at B = 1, T = 8192, HV = 96, K = V = 128.
  * kda_chunk_bwd_workspace_size returns the workspace size in bytes, or -1
  * (message in kda_last_error) for sizes or a dtype kda_chunk_bwd rejects.
  */

@@ -523,16 +523,16 @@ def test_chunk_bwd_workspace_size():
     def want(B, T, HV, K, V):
         # slabs of Ls = 1024 tokens (T rounded up to 32 when shorter), NC = Ls/32
         # chunks: S_T, carried dS [B,HV,K,V]; slab starts [B,slabs-1,HV,K,V];
-        # chunk-start states [B,NC-1,HV,K,V]; W, U, dR [B,Ls,HV,V]; operand
+        # chunk-start states [B,NC-1,HV,K,V]; U, dR [B,Ls,HV,V]; operand
         # images [B,NC,HV,img]; dS per chunk [B,NC,HV,K,V]; dg terms
         # [B,Ls,HV,K]; their chunk sums [B,HV,NC,K]; dg carry [2,B,HV,K]
         Ls = 1024 if T > 1024 else max(32, -(-T // 32) * 32)
         NS1 = -(-T // Ls) - 1 if T > 0 else 0
         NC = Ls // 32
-        # (the chunk-start states, W, U, the images, dR and dS per chunk twice:
+        # (the chunk-start states, U, the images, dR and dS per chunk twice:
         # slabs of even and odd index)
         return (2 * up(B * HV * K * V) + up(B * NS1 * HV * K * V) + 2 * up(B * (NC - 1) * HV * K * V)
-                + 6 * up(B * Ls * HV * V) + 2 * up(B * NC * HV * img(K)) + 2 * up(B * NC * HV * K * V)
+                + 4 * up(B * Ls * HV * V) + 2 * up(B * NC * HV * img(K)) + 2 * up(B * NC * HV * K * V)
                 + up(B * Ls * HV * K) + up(B * HV * NC * K) + up(2 * B * HV * K))
     for args in [(2, 100, 2, 4, 64, 128), (1, 8192, 96, 96, 128, 128), (3, 2500, 1, 2, 32, 64),
                  (1, 1024, 1, 1, 128, 128), (1, 1025, 1, 1, 128, 128), (1, 1, 1, 1, 32, 32)]:
