@@ -8,7 +8,8 @@ Headline workload (one JSON line on stdout):
     g/beta, explicit zero fp32 initial state, final state returned, chunk 32.
     One timed step = one call over that batch.  value = tokens/s.
   * decode: 1000 kda_decode_step calls on B=256 sequences, H=HV=96, K=V=128,
-    fp32 everywhere, fused short conv (width 4) + SiLU, L2 norm of q/k
+    fp32 everywhere, fused short conv (width 4) + SiLU (its registers as a
+    ring of 4 slot arrays; the shifted [B, C, 4] rows timed beside), L2 norm of q/k
     (eps 1e-6), bounded gate -5*sigmoid(exp(A_log)(z+dt_bias)), beta logits;
     state resident in HBM and updated in place.  Reported as GB/s against the
     HBM peak.
@@ -63,6 +64,7 @@ KERNEL_SOURCES = {
     "prefill_hv96": ["kda_prefill_bf16.hip", "kda_internal.h"],
     "prefill_gqa": ["kda_prefill_bf16.hip", "kda_internal.h"],
     "decode_b256": ["kda_decode.hip", "kda_internal.h"],
+    "decode_b256_ring": ["kda_decode.hip", "kda_internal.h"],
 }
 
 
@@ -276,7 +278,10 @@ def bench_prefill(shape, steps, warmup, tag, snapshot_every=None, inp=None, recu
                 workspace=ws.numel() if unbounded else 0)
 
 
-def bench_decode(shape, steps, warmup):
+def bench_decode(shape, steps, warmup, ring=True):
+    """ring: the conv registers as the [KW, B, C] ring (each step reads the
+    KW - 1 newest slots and writes one); else the [B, C, KW] rows that each
+    step shifts and rewrites whole."""
     import torch
     import gated_delta_rule_kda_amd as kda
     from gated_delta_rule_kda_amd import synth
@@ -285,7 +290,7 @@ def bench_decode(shape, steps, warmup):
     C = 2 * H * K + HV * V
     prm = synth.make_decode_params(shape, dev, 0)
     state = torch.zeros(B, HV, K, V, device=dev)
-    conv = torch.zeros(B, C, KW, device=dev)
+    conv = torch.zeros(KW, B, C, device=dev) if ring else torch.zeros(B, C, KW, device=dev)
     out = torch.empty(B, HV, V, device=dev)
     pool = [(x, z.view(B, HV, K), bl) for (x, z, bl) in prm["pool"]]
 
@@ -294,7 +299,8 @@ def bench_decode(shape, steps, warmup):
         kda.decode_step(x, z, bl, state, H=H, HV=HV, K=K, V=V, out=out,
                         conv_weight=prm["conv_w"], conv_state=conv, l2norm_qk=True, l2_eps=1e-6,
                         gate_mode=kda.GATE_BOUNDED, A_log=prm["A_log"], dt_bias=prm["dt_bias"],
-                        gate_lower_bound=shape.lower_bound, beta_is_logit=True)
+                        gate_lower_bound=shape.lower_bound, beta_is_logit=True,
+                        conv_ring=ring, conv_pos=t % KW)
 
     for t in range(warmup):
         call(t)
@@ -311,7 +317,8 @@ def bench_decode(shape, steps, warmup):
     nbytes = decode_alg_bytes(B, H, HV, K, V, KW)
     per_ms = span_ms / steps
     gbs = nbytes / (per_ms * 1e-3) / 1e9
-    log("[decode] %d steps: %.3f ms total, %.4f ms/step, %.1f GB/s" % (steps, span_ms, per_ms, gbs))
+    log("[decode%s] %d steps: %.3f ms total, %.4f ms/step, %.1f GB/s"
+        % (" ring" if ring else " rows", steps, span_ms, per_ms, gbs))
     return dict(span_ms=span_ms, per_ms=per_ms, bytes=nbytes, gbs=gbs)
 
 
@@ -523,7 +530,7 @@ def main():
     ap.add_argument("--no-layer-stages", action="store_true")
     ap.add_argument("--no-unbounded", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "gqa", "decode", "copy", "snap", "stages", "unbounded",
+    ap.add_argument("--only", choices=["prefill", "gqa", "decode", "decode_rows", "copy", "snap", "stages", "unbounded",
                                        "backward", "bandwidth", "layer"],
                     default=None,
                     help="run one workload only (for profiler runs); prints no JSON line")
@@ -558,6 +565,9 @@ def main():
         return
     if args.only == "decode":
         bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup)
+        return
+    if args.only == "decode_rows":
+        bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup, ring=False)
         return
     if args.only == "unbounded":
         sh = synth.PREFILL_HV96_BF16
@@ -740,16 +750,22 @@ def main():
             **lp}
     if not args.no_decode:
         d = bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup)
+        dr = bench_decode(synth.DECODE_B256_HV96, args.decode_steps, args.warmup, ring=False)
         bw_meas = measure_copy_bandwidth()
         line["decode"] = {
-            "workload": "KDA recurrent decode, %d steps, B256 H=HV=96 K=V=128 fp32, fused conv4+SiLU, "
-                        "L2 norm, bounded gate -5, beta logits" % args.decode_steps,
+            "workload": "KDA recurrent decode, %d steps, B256 H=HV=96 K=V=128 fp32, fused conv4+SiLU "
+                        "(conv registers as a [4, B, C] ring), L2 norm, bounded gate -5, beta logits"
+                        % args.decode_steps,
             "value": d["gbs"], "unit": "GB/s", "ms_per_token_step": d["per_ms"],
             "steps": args.decode_steps, "seconds_total": d["span_ms"] * 1e-3, "dtype": "f32",
             "roofline": {"bound": "hbm", "achieved": d["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": d["gbs"] / HBM_PEAK_GBS, "traffic": load_counters("decode_b256"),
+                         "frac": d["gbs"] / HBM_PEAK_GBS, "traffic": load_counters("decode_b256_ring"),
                          "kernel": "decode_kernel<128,128>", "alg_bytes_per_launch": d["bytes"],
                          "avg_launch_ms": d["per_ms"]},
+            "rows_layout": {"what": "the same steps with the conv registers as [B, C, 4] rows, shifted "
+                                    "and rewritten whole each step",
+                            "ms_per_token_step": dr["per_ms"], "achieved_gbs": dr["gbs"],
+                            "frac_hbm": dr["gbs"] / HBM_PEAK_GBS, "traffic": load_counters("decode_b256")},
             "measured_ceilings": {"copy_gbs": bw_meas["copy"], "rmw_in_place_gbs": bw_meas["rmw_in_place"],
                                   "frac_of_copy": d["gbs"] / bw_meas["copy"],
                                   "frac_of_rmw_in_place": d["gbs"] / bw_meas["rmw_in_place"],

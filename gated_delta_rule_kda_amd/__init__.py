@@ -35,7 +35,7 @@ _lib = None
 KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EHIP = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_DIRECT, GATE_BOUNDED, GATE_SOFTPLUS = 0, 1, 2
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class KDAError(RuntimeError):
@@ -59,6 +59,8 @@ class DecodePrologue(ctypes.Structure):
         ("dt_bias", ctypes.c_void_p),
         ("gate_lower_bound", ctypes.c_float),
         ("beta_is_logit", ctypes.c_int),
+        ("conv_ring", ctypes.c_int),
+        ("conv_pos", ctypes.c_int),
     ]
 
 
@@ -505,18 +507,28 @@ def kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=Fal
     return o, (S if output_final_state else None)
 
 
+def _conv_fields(pro, C, B, dev, conv_weight, conv_state, conv_ring, conv_pos, need_state):
+    """The conv fields of the prologue struct: conv_state is [B, C, KW]
+    (oldest register first), or with ``conv_ring`` the [KW, B, C] ring whose
+    oldest register sits in slot ``conv_pos``."""
+    KW = conv_weight.shape[-1]
+    _need(conv_weight, "conv_weight", torch.float32, (C, KW), dev)
+    pro.conv_weight = conv_weight.data_ptr()
+    if conv_state is not None or need_state:
+        _need(conv_state, "conv_state", torch.float32, (KW, B, C) if conv_ring else (B, C, KW), dev)
+        pro.conv_state = conv_state.data_ptr()
+    pro.conv_kernel = KW
+    if conv_ring:
+        pro.conv_ring = 1
+        pro.conv_pos = int(conv_pos)
+
+
 def _prologue_struct(C, dev, conv_weight, conv_state, l2norm_qk, l2_eps, gate_mode, A_log,
-                     dt_bias, gate_lower_bound, beta_is_logit, HV, K, B):
+                     dt_bias, gate_lower_bound, beta_is_logit, HV, K, B, conv_ring=False, conv_pos=0):
     pro = DecodePrologue()
     use = False
     if conv_weight is not None:
-        KW = conv_weight.shape[-1]
-        _need(conv_weight, "conv_weight", torch.float32, (C, KW), dev)
-        pro.conv_weight = conv_weight.data_ptr()
-        if conv_state is not None:
-            _need(conv_state, "conv_state", torch.float32, (B, C, KW), dev)
-            pro.conv_state = conv_state.data_ptr()
-        pro.conv_kernel = KW
+        _conv_fields(pro, C, B, dev, conv_weight, conv_state, conv_ring, conv_pos, False)
         use = True
     if l2norm_qk:
         pro.l2norm_qk = 1
@@ -538,11 +550,14 @@ def _prologue_struct(C, dev, conv_weight, conv_state, l2norm_qk, l2_eps, gate_mo
 
 def prefill_prologue(x, gate, beta, *, H, HV, K, V, conv_weight=None, conv_state=None,
                      l2norm_qk=False, l2_eps=1e-6, gate_mode=GATE_DIRECT, A_log=None,
-                     dt_bias=None, gate_lower_bound=-5.0, beta_is_logit=False, out=None):
+                     dt_bias=None, gate_lower_bound=-5.0, beta_is_logit=False, out=None,
+                     conv_ring=False, conv_pos=0):
     """``kda_prefill_prologue``: the decode prologue's stages over all T tokens.
 
     x [B,T,2HK+HV*V] (bf16 or fp32), gate [B,T,HV,K] fp32 (g or z), beta
-    [B,T,HV] fp32 (or logits); ``conv_state`` [B,C,KW] fp32 is read and then
+    [B,T,HV] fp32 (or logits); ``conv_state`` [B,C,KW] fp32 (with
+    ``conv_ring``: the [KW,B,C] ring, oldest register in slot ``conv_pos``;
+    the caller then advances conv_pos by T mod KW) is read and then
     overwritten with the registers after the last token.  Returns
     (q [B,T,H,K], k, v [B,T,HV,V] in x's dtype, g [B,T,HV,K] fp32, beta [B,T,HV] fp32)
     -- the inputs of :func:`chunk_fwd`.  ``out`` may supply those five tensors.
@@ -576,7 +591,8 @@ def prefill_prologue(x, gate, beta, *, H, HV, K, V, conv_weight=None, conv_state
     else:
         g = bo = None
     pro, use = _prologue_struct(C, dev, conv_weight, conv_state, l2norm_qk, l2_eps, gate_mode,
-                                A_log, dt_bias, gate_lower_bound, beta_is_logit, HV, K, B)
+                                A_log, dt_bias, gate_lower_bound, beta_is_logit, HV, K, B,
+                                conv_ring, conv_pos)
     with torch.cuda.device(dev):
         _check(_load().kda_prefill_prologue(
             _ptr(x), _ptr(gate), _ptr(beta), ctypes.byref(pro) if use else None,
@@ -605,11 +621,13 @@ def output_gate(o, gate, eps=1e-6, *, out=None):
 def decode_step(qkv, gate, beta, state, *, H, HV, K, V, scale=None, out=None,
                 conv_weight=None, conv_state=None, l2norm_qk=False, l2_eps=1e-6,
                 gate_mode=GATE_DIRECT, A_log=None, dt_bias=None, gate_lower_bound=-5.0,
-                beta_is_logit=False):
+                beta_is_logit=False, conv_ring=False, conv_pos=0):
     """One decode token (``kda_decode_step``); ``state`` (and ``conv_state``)
     are updated in place.  qkv [B, 2HK+HV*V] (bf16 or fp32), gate [B,HV,K] fp32
     (g, or z for the BOUNDED/SOFTPLUS gate modes), beta [B,HV] fp32.
-    Returns out [B,HV,V] in qkv's dtype."""
+    ``conv_state`` is [B,C,KW], or with ``conv_ring`` the [KW,B,C] ring whose
+    oldest register sits in slot ``conv_pos`` (the caller then advances
+    conv_pos by 1 mod KW).  Returns out [B,HV,V] in qkv's dtype."""
     _need(qkv, "qkv")
     B = qkv.shape[0]
     C = 2 * H * K + HV * V
@@ -627,12 +645,7 @@ def decode_step(qkv, gate, beta, state, *, H, HV, K, V, scale=None, out=None,
     pro = DecodePrologue()
     use_pro = False
     if conv_weight is not None:
-        KW = conv_weight.shape[-1]
-        _need(conv_weight, "conv_weight", torch.float32, (C, KW), dev)
-        _need(conv_state, "conv_state", torch.float32, (B, C, KW), dev)
-        pro.conv_weight = conv_weight.data_ptr()
-        pro.conv_state = conv_state.data_ptr()
-        pro.conv_kernel = KW
+        _conv_fields(pro, C, B, dev, conv_weight, conv_state, conv_ring, conv_pos, True)
         use_pro = True
     if l2norm_qk:
         pro.l2norm_qk = 1

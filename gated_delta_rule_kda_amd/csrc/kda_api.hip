@@ -760,6 +760,9 @@ int kda_prefill_prologue(const void *x, const float *gate, const float *beta,
         if (p.conv_kernel < 1) return fail(KDA_EINVAL, "%s: conv_kernel=%d must be >= 1", fn, p.conv_kernel);
         if (p.conv_kernel > 8)
             return fail(KDA_EUNSUPPORTED, "%s: conv_kernel=%d; at most 8 is built", fn, p.conv_kernel);
+        if (p.conv_ring && (p.conv_pos < 0 || p.conv_pos >= p.conv_kernel))
+            return fail(KDA_EINVAL, "%s: conv_pos=%d must be in 0..conv_kernel-1=%d", fn, p.conv_pos,
+                        p.conv_kernel - 1);
     }
     if (p.gate_mode < 0 || p.gate_mode > 2)
         return fail(KDA_EINVAL, "%s: gate_mode=%d is not a kda_gate_mode", fn, p.gate_mode);
@@ -812,6 +815,7 @@ int kda_prefill_prologue(const void *x, const float *gate, const float *beta,
     a.conv_state = conv ? p.conv_state : nullptr;
     a.conv_state_out = conv ? p.conv_state : nullptr;
     a.KW = KW; a.l2norm = p.l2norm_qk ? 1 : 0; a.l2_eps = p.l2_eps;
+    a.conv_ring = conv && p.conv_ring ? 1 : 0; a.conv_pos = a.conv_ring ? p.conv_pos : 0;
     a.gate = gate; a.gate_mode = p.gate_mode; a.A_log = p.A_log; a.dt_bias = p.dt_bias;
     a.lower_bound = p.gate_lower_bound; a.beta_in = beta; a.beta_is_logit = p.beta_is_logit ? 1 : 0;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta_out = beta_out;
@@ -874,6 +878,9 @@ int kda_decode_step(const void *qkv, const float *gate, const float *beta, float
         if (p.conv_kernel < 1) return fail(KDA_EINVAL, "kda_decode_step: conv_kernel=%d must be >= 1", p.conv_kernel);
         if (p.conv_kernel > 8)
             return fail(KDA_EUNSUPPORTED, "kda_decode_step: conv_kernel=%d; at most 8 is built", p.conv_kernel);
+        if (p.conv_ring && (p.conv_pos < 0 || p.conv_pos >= p.conv_kernel))
+            return fail(KDA_EINVAL, "kda_decode_step: conv_pos=%d must be in 0..conv_kernel-1=%d", p.conv_pos,
+                        p.conv_kernel - 1);
     }
     if (p.gate_mode < 0 || p.gate_mode > 2)
         return fail(KDA_EINVAL, "kda_decode_step: gate_mode=%d is not a kda_gate_mode", p.gate_mode);
@@ -916,6 +923,7 @@ int kda_decode_step(const void *qkv, const float *gate, const float *beta, float
     a.qkv = qkv; a.gate = gate; a.beta = beta; a.state = state; a.out = out;
     a.conv_w = p.conv_weight; a.conv_state = conv ? p.conv_state : nullptr;
     a.conv_kernel = conv ? p.conv_kernel : 0;
+    a.conv_ring = conv && p.conv_ring ? 1 : 0; a.conv_pos = a.conv_ring ? p.conv_pos : 0;
     a.l2norm = p.l2norm_qk ? 1 : 0; a.l2_eps = p.l2_eps;
     a.gate_mode = p.gate_mode; a.A_log = p.A_log; a.dt_bias = p.dt_bias;
     a.lower_bound = p.gate_lower_bound; a.beta_is_logit = p.beta_is_logit ? 1 : 0;

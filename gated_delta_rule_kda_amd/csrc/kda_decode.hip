@@ -60,8 +60,36 @@ __device__ __forceinline__ float channel_value(const DecodeArgs &a, int b, int c
     const float x = load_io(a.qkv, static_cast<size_t>(b) * C + c, a.bf16);
     if (a.conv_w == nullptr) return x;
     const int KW = a.conv_kernel;
-    float *st = a.conv_state + (static_cast<size_t>(b) * C + c) * KW;
     const float *w = a.conv_w + static_cast<size_t>(c) * KW;
+    if (a.conv_ring) {
+        // slot arrays [KW][B][C]: register j (0 = oldest) in slot (conv_pos + j) % KW.
+        // The window is registers 1..KW-1 and the token; the token goes into
+        // the oldest register's slot, the only store.
+        const size_t slot = static_cast<size_t>(a.B) * C;
+        float *col = a.conv_state + static_cast<size_t>(b) * C + c;
+        if (KW == 4) {
+            // the common width: the weights in one 16-byte load, the slots of
+            // registers 1..3 by a mask
+            const float4 wv = *reinterpret_cast<const float4 *>(w);
+            const float r1 = col[((a.conv_pos + 1) & 3) * slot];
+            const float r2 = col[((a.conv_pos + 2) & 3) * slot];
+            const float r3 = col[((a.conv_pos + 3) & 3) * slot];
+            col[a.conv_pos * slot] = x;
+            const float acc = fmaf(wv.w, x, fmaf(wv.z, r3, fmaf(wv.y, r2, wv.x * r1)));
+            return acc * sigmoid_acc(acc);
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 1; j < kMaxConv; ++j)
+            if (j < KW) {
+                const int p = a.conv_pos + j < KW ? a.conv_pos + j : a.conv_pos + j - KW;
+                acc = fmaf(w[j - 1], col[p * slot], acc);
+            }
+        acc = fmaf(w[KW - 1], x, acc);
+        col[a.conv_pos * slot] = x;
+        return acc * sigmoid_acc(acc);
+    }
+    float *st = a.conv_state + (static_cast<size_t>(b) * C + c) * KW;
     if (KW == 4) {
         // the common width: one 16-byte load and store of the channel's register
         const float4 o = *reinterpret_cast<const float4 *>(st);

@@ -71,8 +71,9 @@ struct DecodeArgs {
     float *state;               // [B,HV,K,V]
     void *out;                  // [B,HV,V] (dtype)
     const float *conv_w;        // [C,KW] or nullptr
-    float *conv_state;          // [B,C,KW]
+    float *conv_state;          // [B,C,KW]; ring: [KW,B,C], oldest register in slot conv_pos
     int conv_kernel;
+    int conv_ring, conv_pos;
     int l2norm;
     float l2_eps;
     int gate_mode;
@@ -91,6 +92,7 @@ struct PrologueArgs {
     const float *conv_state;    // [B,C,KW] registers before token 0, or nullptr (zeros)
     float *conv_state_out;      // [B,C,KW] registers after token T-1, or nullptr
     int KW;
+    int conv_ring, conv_pos;    // ring: both [KW,B,C], oldest register in slot conv_pos
     int l2norm;
     float l2_eps;
     const float *gate;          // [B,T,HV,K]: g, or z for the gate modes

@@ -130,13 +130,19 @@ __global__ __launch_bounds__(kRowThreads) void prologue_rows_kernel(PrologueArgs
         for (int e = 0; e < 8; ++e)
 #pragma unroll
             for (int j = 0; j < KW; ++j) w[e][j] = a.conv_w[static_cast<size_t>(c + e) * KW + j];
-        // tokens before 0 come from the conv registers, whose slot KW + t holds
-        // x_t for t = -1 .. -(KW - 1)
+        // tokens before 0 come from the conv registers: register KW + t holds
+        // x_t for t = -1 .. -(KW - 1); in the ring layout ([KW][B][C], register
+        // j in slot (conv_pos + j) % KW) that is slot (conv_pos + KW + t) % KW
 #pragma unroll
         for (int i = 0; i < NH; ++i) {
             const int t = t0 - NH + i;
             if (t >= 0) {
                 load8<BF16>(a.x, (static_cast<size_t>(b) * a.T + t) * C + c, h[i]);
+            } else if (a.conv_ring && a.conv_state) {
+                const int p = (a.conv_pos + KW + t) % KW;
+                const float *col = a.conv_state + (static_cast<size_t>(p) * a.B + b) * C + c;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[i][e] = col[e];
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -210,14 +216,26 @@ __global__ __launch_bounds__(kRowThreads) void prologue_gate_kernel(PrologueArgs
     }
 }
 
-// Conv registers after the last token: slot j holds input T - KW + j, which
-// for T < KW reaches back into the registers the call started from.  Runs
-// after the row kernels, which read the old registers.
+// Conv registers after the last token: register j holds input T - KW + j,
+// which for T < KW reaches back into the registers the call started from.
+// Runs after the row kernels, which read the old registers.
 __global__ __launch_bounds__(kRowThreads) void prologue_conv_state_kernel(PrologueArgs a) {
     const int C = 2 * a.H * a.K + a.HV * a.V;
     const size_t i = static_cast<size_t>(blockIdx.x) * kRowThreads + threadIdx.x;
     if (i >= static_cast<size_t>(a.B) * C) return;
     const int b = static_cast<int>(i / C), c = static_cast<int>(i % C);
+    if (a.conv_ring) {
+        // [KW][B][C] ring: input t goes into slot (conv_pos + t) % KW, the slot
+        // of the register it replaces; only the last min(T, KW) inputs are
+        // stored, and the slots of older registers that stay are not touched
+        const size_t slot = static_cast<size_t>(a.B) * C;
+        for (int t = a.T > a.KW ? a.T - a.KW : 0; t < a.T; ++t) {
+            const float x = a.bf16 ? bf16_bits_to_float(static_cast<const uint16_t *>(a.x)[(static_cast<size_t>(b) * a.T + t) * C + c])
+                                   : static_cast<const float *>(a.x)[(static_cast<size_t>(b) * a.T + t) * C + c];
+            a.conv_state_out[static_cast<size_t>((a.conv_pos + t) % a.KW) * slot + i] = x;
+        }
+        return;
+    }
     float *st = a.conv_state_out + i * a.KW;
     float nw[kMaxConvKernel];
 #pragma unroll

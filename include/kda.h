@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 enum kda_status { KDA_OK = 0, KDA_EINVAL = 1, KDA_EUNSUPPORTED = 2, KDA_EHIP = 3 };
 
@@ -390,7 +390,27 @@ typedef struct kda_decode_prologue {
     const float *dt_bias;     /* [HV * K]  (BOUNDED, SOFTPLUS) */
     float gate_lower_bound;   /* BOUNDED: g = lb * sigmoid(exp(A_log) * (z + dt_bias)) */
     int beta_is_logit;        /* nonzero: beta = sigmoid(beta argument) */
+    int conv_ring;            /* nonzero: conv_state is a ring of slot arrays (below) */
+    int conv_pos;             /* ring: the slot of the oldest register, 0..conv_kernel-1 */
 } kda_decode_prologue;
+
+/*
+ * Two layouts of the conv registers, the last conv_kernel (W) inputs of each
+ * channel (the window of conv_update on the page
+ * "metrale_model_weights/kimi_k3_host/kda.rs"):
+ *   conv_ring == 0: [B, C, W], oldest first.  A decode step shifts each row
+ *     and appends the token, so it reads and rewrites all W values.
+ *   conv_ring != 0: [W, B, C], W slot arrays used as a ring.  Register j
+ *     (0 = oldest) of channel c of sequence b sits in slot (conv_pos + j) % W,
+ *     at conv_state[((conv_pos + j) % W) * B * C + b * C + c].  A decode step
+ *     reads the W - 1 newest registers and writes the token into slot
+ *     conv_pos alone (the oldest, which its window no longer uses); a
+ *     prefill of T tokens writes its last min(T, W) inputs into slots
+ *     (conv_pos + t) % W.  The library never changes conv_pos: after a call
+ *     the caller advances it, by 1 for a decode step and by T for a prefill
+ *     (mod W).  Both layouts give identical results; the ring moves W - 1
+ *     reads and one write per channel and token instead of W of each.
+ */
 
 /*
  * kda_prefill_prologue -- the stages of the decode prologue applied to all T

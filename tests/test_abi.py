@@ -219,6 +219,8 @@ def test_decode_rejects(over, code, msg):
     (dict(conv_weight=FAKE * 7, conv_kernel=4), 1, "conv_state"),
     (dict(conv_weight=FAKE * 7, conv_state=FAKE * 8, conv_kernel=0), 1, ">= 1"),
     (dict(conv_weight=FAKE * 7, conv_state=FAKE * 8, conv_kernel=9), 2, "at most 8"),
+    (dict(conv_weight=FAKE * 7, conv_state=FAKE * 8, conv_kernel=4, conv_ring=1, conv_pos=4), 1, "conv_pos=4"),
+    (dict(conv_weight=FAKE * 7, conv_state=FAKE * 8, conv_kernel=4, conv_ring=1, conv_pos=-1), 1, "conv_pos=-1"),
     (dict(gate_mode=1), 1, "A_log"),
     (dict(gate_mode=5), 1, "gate_mode"),
     (dict(l2norm_qk=1, l2_eps=-1.0), 1, "l2_eps"),
@@ -314,6 +316,7 @@ def test_chunk_fwd_gated_rejects(over, code, msg):
 @pytest.mark.parametrize("pro,code,msg", [
     (dict(conv_weight=FAKE * 9, conv_kernel=0), 1, "conv_kernel=0"),
     (dict(conv_weight=FAKE * 9, conv_kernel=9), 2, "at most 8"),
+    (dict(conv_weight=FAKE * 9, conv_kernel=3, conv_ring=1, conv_pos=3), 1, "conv_pos=3"),
     (dict(gate_mode=1), 1, "needs A_log"),
     (dict(gate_mode=4), 1, "kda_gate_mode"),
     (dict(l2norm_qk=1, l2_eps=-1.0), 1, "l2_eps"),
