@@ -118,8 +118,11 @@ __device__ __forceinline__ float row_shr(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xf, 0xf, false));
 }
 
+// At most 168 VGPRs (three waves per SIMD; the compiler takes 159): three
+// workgroups per CU instead of the two that 172 allowed, their LDS 103 KB
+// (the pass 3 % faster on the HV96 workload; a budget of 128 spills).
 template <int K>
-__global__ __launch_bounds__(kThrU) void unb_prep_kernel(UnbPrepArgs a) {
+__global__ __launch_bounds__(kThrU, 3) void unb_prep_kernel(UnbPrepArgs a) {
     using P = UPlan<K>;
     constexpr int LK = P::LK, LKB = P::LKB;
     __shared__ __attribute__((aligned(16))) float sm[P::floats];
