@@ -410,6 +410,8 @@ typedef struct kda_decode_prologue {
  *     the caller advances it, by 1 for a decode step and by T for a prefill
  *     (mod W).  Both layouts give identical results; the ring moves W - 1
  *     reads and one write per channel and token instead of W of each.
+ *     conv_pos is an argument of the call, so a decode loop under HIP graph
+ *     capture captures one graph per slot and replays them in turn.
  */
 
 /*

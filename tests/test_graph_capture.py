@@ -166,6 +166,51 @@ def test_graph_decode_steps():
     replay_and_check(lambda: steps(state, conv, outs), eager, refill_fn)
 
 
+def test_graph_decode_ring_rotation():
+    """The ring layout of the conv registers under capture: the slot of the
+    oldest register is an argument of the call, so a loop captures one graph
+    per slot (KW of them) and replays them in turn.  Nine steps through the
+    three graphs of a width-3 ring against the same steps eagerly, every step
+    bit for bit (outputs, state and the ring)."""
+    B, H, HV, K, V, KW = 2, 2, 2, 64, 64, 3
+    C = 2 * H * K + HV * V
+    say("decode ring B2 H2 HV2 K64 V64 KW3: one graph per slot")
+    gen = torch.Generator(device="cpu").manual_seed(13)
+    r = lambda *s_: torch.randn(*s_, generator=gen).to(DEV)
+    conv_w, A_log, dt_bias = r(C, KW), r(HV), r(HV * K)
+    x = torch.empty(B, C, device=DEV)
+    z = torch.empty(B, HV, K, device=DEV)
+    bl = torch.empty(B, HV, device=DEV)
+    out = torch.empty(B, HV, V, device=DEV)
+    state = 0.1 * r(B, HV, K, V)
+    ring = r(KW, B, C)
+    st_e, ring_e = state.clone(), ring.clone()
+    kw = dict(H=H, HV=HV, K=K, V=V, conv_weight=conv_w, l2norm_qk=True, l2_eps=1e-6,
+              gate_mode=kda.GATE_BOUNDED, A_log=A_log, dt_bias=dt_bias, gate_lower_bound=-5.0,
+              beta_is_logit=True, conv_ring=True)
+    torch.cuda.synchronize()
+    # capturing records the work without running it: state and ring stay as they are
+    graphs = []
+    for pos in range(KW):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            kda.decode_step(x, z, bl, state, out=out, conv_state=ring, conv_pos=pos, **kw)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for t in range(3 * KW):
+        x.copy_(r(B, C))
+        z.copy_(r(B, HV, K))
+        bl.copy_(r(B, HV))
+        want = kda.decode_step(x, z, bl, st_e, conv_state=ring_e, conv_pos=t % KW, **kw)
+        torch.cuda.synchronize()
+        graphs[t % KW].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), ("out", t)
+        assert torch.equal(state, st_e), ("state", t)
+        assert torch.equal(ring, ring_e), ("ring", t)
+        say("   step", t, "slot", t % KW, "ok")
+
+
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_graph_recurrent_fwd_bwd(dt):
     """kda_recurrent_fwd, then kda_recurrent_bwd and kda_recurrent_bwd_noalloc
