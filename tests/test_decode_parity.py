@@ -49,15 +49,16 @@ def test_plain_steps_equal_prefill_oracle(dt, H, HV, K, V):
     assert_close(state, Sref, torch.float32, False, "decode S")
 
 
-def _prologue_run(shape: synth.DecodeShape, steps, seed=0, dt=torch.float32, check_b=None):
+def _prologue_run(shape: synth.DecodeShape, steps, seed=0, dt=torch.float32, check_b=None, ring=False):
     """Run `steps` fused decode steps with the full prologue (conv + SiLU,
-    L2 norm, bounded gate, sigmoid beta) and compare against the oracle."""
+    L2 norm, bounded gate, sigmoid beta) and compare against the oracle.
+    ring: the conv registers as the [KW, B, C] ring (the oracle keeps rows)."""
     B, H, HV, K, V, KW = shape.B, shape.H, shape.HV, shape.K, shape.V, shape.KW
     C = 2 * H * K + HV * V
-    say("decode prologue", shape, "steps", steps, "dtype", dt)
+    say("decode prologue", shape, "steps", steps, "dtype", dt, "ring" if ring else "rows")
     prm = synth.make_decode_params(shape, DEV, seed)
     state = torch.zeros(B, HV, K, V, device=DEV)
-    conv = torch.zeros(B, C, KW, device=DEV)
+    conv = torch.zeros(KW, B, C, device=DEV) if ring else torch.zeros(B, C, KW, device=DEV)
     bs = list(range(B)) if check_b is None else check_b
     st_ref = np.zeros((len(bs), HV, K, V))
     cv_ref = np.zeros((len(bs), C, KW))
@@ -68,7 +69,7 @@ def _prologue_run(shape: synth.DecodeShape, steps, seed=0, dt=torch.float32, che
                               conv_weight=prm["conv_w"], conv_state=conv, l2norm_qk=True,
                               l2_eps=1e-6, gate_mode=kda.GATE_BOUNDED, A_log=prm["A_log"],
                               dt_bias=prm["dt_bias"], gate_lower_bound=shape.lower_bound,
-                              beta_is_logit=True)
+                              beta_is_logit=True, conv_ring=ring, conv_pos=t % KW)
         oref = oracle.kda_decode_step(x[bs], st_ref, H, HV, K, V, conv_w=prm["conv_w"],
                                       conv_state=cv_ref, l2norm_qk=True, eps=1e-6,
                                       gate_in=z[bs], A_log=prm["A_log"], dt_bias=prm["dt_bias"],
@@ -76,6 +77,9 @@ def _prologue_run(shape: synth.DecodeShape, steps, seed=0, dt=torch.float32, che
                                       beta=bl[bs], beta_is_logit=True)
         assert_close(out[bs], oref, dt, True, "step %d out" % t)
     assert_close(state[bs], st_ref, torch.float32, False, "final state")
+    if ring:
+        # register j (oldest first) of the ring after `steps` steps sits in slot (steps + j) % KW
+        conv = torch.stack([conv[(steps + j) % KW] for j in range(KW)], dim=-1)
     assert_close(conv[bs], cv_ref, torch.float32, False, "conv state")
 
 
@@ -95,6 +99,13 @@ def test_prologue_production_geometry_sampled():
     L2 norm eps 1e-6, beta logits) for 40 steps; all 256 sequences run on the
     GPU, four of them are followed by the oracle."""
     _prologue_run(synth.DECODE_B256_HV96, steps=40, check_b=[0, 77, 128, 255])
+
+
+def test_prologue_production_geometry_ring_sampled():
+    """The same workload with the conv registers as the [4, B, C] ring, as
+    the decode bench runs it: 41 steps (ten turns of the ring and one slot),
+    four sequences followed by the oracle."""
+    _prologue_run(synth.DECODE_B256_HV96, steps=41, check_b=[1, 64, 200, 254], ring=True)
 
 
 def test_softplus_gate_mode():
