@@ -147,7 +147,7 @@ def test_layer_path_and_decode_continuation(dtype):
     rq, rk, rv, rg, rb = oracle.prefill_prologue(x, H, HV, K, V, conv_state=cs_ref,
                                                  gate_in=p["z"][:, :T], beta=p["beta"][:, :T], **opt)
     # the chunk step of the oracle sees the GPU's own (rounded) prologue outputs,
-    # so each stage is judged on its own error
+    # so each stage is checked against its own error
     ro, rS = oracle.kda_fwd(q, k, v, gg, bb)
     assert_close(q, rq, dtype, True, "layer q")
     assert_close(o, ro, dtype, True, "layer o")
